@@ -1,0 +1,249 @@
+"""Seeded synthetic inputs for paged low-rank-compressed attention.
+
+This module only draws random numbers and lays them out in the library's
+paged cache format; it holds none of the attention arithmetic, so both the
+HIP path and the CPU checker can be fed from it.
+
+Workload shapes follow the Proxima README: 32-head MHA with head size 128
+and rank 64 ("Per-decode-step attention"), 16-token KV blocks ("KV-cache
+capacity"), and chunked prefill of N new tokens per request
+("Per-prefill-chunk attention").  Rank 64 is read as r_k = 64 per head for K
+and a joint r_v = 512 for V.
+
+Draw order for one case (numpy PCG64, ``default_rng(seed)``):
+  1. U_h for h = 0..H-1: reduced QR of N(0,1)^{d x r_k}, column signs fixed so
+     diag(R) > 0, cast to fp16;
+  2. W: the same from N(0,1)^{(H*d) x r_v};
+  3. sequence lengths, when the config draws them (inclusive uniform);
+  4. the physical block permutation ``rng.permutation(NB)``, handed out to
+     (sequence, logical block) in sequence-major order;
+  5. latents in logical (sequence, token) order, per sequence: c_k ~ N(0,1)
+     of shape [L, H, r_k] then c_v ~ N(0,1) of shape [L, r_v], drawn as
+     float32 and cast to fp16 (round to nearest even);
+  6. prefill only: new k, then v, then q ~ N(0,1) [sum C, H, d] fp16;
+     decode: q ~ N(0,1) [B, H, d] fp16.
+Cache slots that hold no token (ragged tails, the spare block) are fp16 NaN
+(0x7E00) so that any read of them shows up in the output.
+
+Cache layouts: k_cache [NB, H, bs, r_k] fp16, v_cache [NB, r_v, bs] fp16.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+FP16_NAN_BITS = 0x7E00
+
+
+@dataclass(frozen=True)
+class Shape:
+    H: int
+    d: int
+    r_k: int
+    r_v: int
+    bs: int = 16
+
+
+MAIN = Shape(H=32, d=128, r_k=64, r_v=512, bs=16)
+TINY = Shape(H=4, d=64, r_k=16, r_v=64, bs=16)
+
+# Named workloads.  "seq" is ("fixed", L) or ("uniform", lo, hi) inclusive.
+CONFIGS = {
+    "tiny": dict(kind="decode", shape=TINY, B=2, seq=("fixed", 256), seed=0),
+    "decode_b16": dict(kind="decode", shape=MAIN, B=16, seq=("fixed", 2048), seed=1),
+    "decode_b64": dict(kind="decode", shape=MAIN, B=64, seq=("uniform", 4096, 8192), seed=2),
+    "long_b20": dict(kind="decode", shape=MAIN, B=20, seq=("fixed", 32768), seed=3),
+    "prefill_b16": dict(kind="prefill", shape=MAIN, B=16, cached=4096, chunk=256, seed=4),
+}
+
+
+def _nan_f16(shape):
+    return np.full(shape, FP16_NAN_BITS, dtype=np.uint16).view(np.float16)
+
+
+def orthonormal_fp16(rng, rows, cols):
+    """Reduced QR of an N(0,1) matrix, sign-fixed, cast to fp16."""
+    a = rng.standard_normal((rows, cols))
+    qm, rm = np.linalg.qr(a)
+    sgn = np.sign(np.diag(rm))
+    sgn[sgn == 0] = 1.0
+    return (qm * sgn[None, :]).astype(np.float16)
+
+
+def draw_bases(rng, shape: Shape):
+    U = np.stack([orthonormal_fp16(rng, shape.d, shape.r_k) for _ in range(shape.H)])
+    W = orthonormal_fp16(rng, shape.H * shape.d, shape.r_v)
+    return U, W
+
+
+@dataclass
+class PagedCache:
+    """Block tables plus fp16 caches in the library layout."""
+    shape: Shape
+    seq_lens: np.ndarray          # [B] int32, tokens in the cache
+    block_tables: np.ndarray      # [B, max_blocks] int32, -1 = unused
+    k_cache: np.ndarray           # [NB, H, bs, r_k] fp16
+    v_cache: np.ndarray           # [NB, r_v, bs] fp16
+    logical_ck: Optional[List[np.ndarray]] = None  # per sequence [L, H, r_k]
+    logical_cv: Optional[List[np.ndarray]] = None  # per sequence [L, r_v]
+
+    @property
+    def num_blocks(self):
+        return self.k_cache.shape[0]
+
+
+def build_block_tables(rng, blocks_per_seq: Sequence[int], spare_blocks=1,
+                       shuffle=True, extra_cols=0):
+    nb = int(sum(blocks_per_seq)) + int(spare_blocks)
+    perm = rng.permutation(nb) if shuffle else np.arange(nb)
+    max_blocks = max([int(x) for x in blocks_per_seq] + [1]) + int(extra_cols)
+    bt = np.full((len(blocks_per_seq), max_blocks), -1, dtype=np.int32)
+    i = 0
+    for b, n in enumerate(blocks_per_seq):
+        bt[b, :n] = perm[i:i + n]
+        i += n
+    return bt, nb
+
+
+def scatter_tokens(k_cache, v_cache, table_row, t0, ck, cv, bs):
+    """Place logical tokens t0..t0+len-1 (ck [n,H,r_k], cv [n,r_v]) in their pages."""
+    n = ck.shape[0]
+    t = t0 + np.arange(n)
+    blk = table_row[t // bs]
+    off = t % bs
+    k_cache[blk, :, off, :] = ck
+    v_cache[blk, :, off] = cv
+
+
+def fill_cache(rng, shape: Shape, seq_lens, cache_lens=None, spare_blocks=1,
+               shuffle=True, keep_logical=False, extra_cols=0):
+    """Block tables for seq_lens tokens, latents drawn for the first cache_lens."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    cache_lens = seq_lens if cache_lens is None else np.asarray(cache_lens, dtype=np.int32)
+    bs = shape.bs
+    nblk = [(int(L) + bs - 1) // bs for L in seq_lens]
+    bt, nb = build_block_tables(rng, nblk, spare_blocks, shuffle, extra_cols)
+    kc = _nan_f16((nb, shape.H, bs, shape.r_k))
+    vc = _nan_f16((nb, shape.r_v, bs))
+    lck, lcv = [], []
+    for b, L in enumerate(cache_lens):
+        L = int(L)
+        ck = rng.standard_normal((L, shape.H, shape.r_k), dtype=np.float32).astype(np.float16)
+        cv = rng.standard_normal((L, shape.r_v), dtype=np.float32).astype(np.float16)
+        if L:
+            scatter_tokens(kc, vc, bt[b], 0, ck, cv, bs)
+        if keep_logical:
+            lck.append(ck)
+            lcv.append(cv)
+    return PagedCache(shape, seq_lens, bt, kc, vc,
+                      lck if keep_logical else None, lcv if keep_logical else None)
+
+
+@dataclass
+class DecodeCase:
+    shape: Shape
+    U: np.ndarray          # [H, d, r_k] fp16
+    W: np.ndarray          # [H*d, r_v] fp16
+    cache: PagedCache
+    q: np.ndarray          # [B, H, d] fp16
+    scale: float
+    seed: int = 0
+    name: str = ""
+
+    @property
+    def B(self):
+        return self.q.shape[0]
+
+
+@dataclass
+class PrefillCase:
+    shape: Shape
+    U: np.ndarray
+    W: np.ndarray
+    cache: PagedCache               # caches hold the first cached_lens tokens
+    cached_lens: np.ndarray         # [B] tokens already in the cache
+    k_new: np.ndarray               # [T, H, d] fp16, T = sum of chunk lengths
+    v_new: np.ndarray               # [T, H, d] fp16
+    q: np.ndarray                   # [T, H, d] fp16
+    slot_mapping: np.ndarray        # [T] int64 slot of each new token
+    query_start_loc: np.ndarray     # [B+1] int32
+    scale: float
+    seed: int = 0
+    name: str = ""
+
+    @property
+    def seq_lens(self):
+        return self.cache.seq_lens
+
+
+def draw_seq_lens(rng, B, seq):
+    if seq[0] == "fixed":
+        return np.full(B, int(seq[1]), dtype=np.int32)
+    if seq[0] == "uniform":
+        return rng.integers(int(seq[1]), int(seq[2]), size=B, endpoint=True).astype(np.int32)
+    raise ValueError(seq)
+
+
+def make_decode_case(shape: Shape, seq_lens=None, B=None, seq=None, seed=0,
+                     spare_blocks=1, shuffle=True, keep_logical=False,
+                     bases=None, extra_cols=0, name=""):
+    """One decode step: B sequences of seq_lens tokens, one query each."""
+    rng = np.random.default_rng(seed)
+    if bases is None:
+        U, W = draw_bases(rng, shape)
+    else:
+        U, W = (np.asarray(x, dtype=np.float16) for x in bases)
+    if seq_lens is None:
+        seq_lens = draw_seq_lens(rng, B, seq)
+    cache = fill_cache(rng, shape, seq_lens, spare_blocks=spare_blocks,
+                       shuffle=shuffle, keep_logical=keep_logical, extra_cols=extra_cols)
+    q = rng.standard_normal((len(cache.seq_lens), shape.H, shape.d),
+                            dtype=np.float32).astype(np.float16)
+    return DecodeCase(shape, U, W, cache, q, 1.0 / np.sqrt(shape.d), seed, name)
+
+
+def make_prefill_case(shape: Shape, cached_lens, chunk_lens, seed=0,
+                      spare_blocks=1, shuffle=True, keep_logical=False,
+                      bases=None, name=""):
+    """One chunked-prefill step: request b has cached_lens[b] latent tokens and
+    appends chunk_lens[b] new full-precision tokens, then attends causally."""
+    rng = np.random.default_rng(seed)
+    if bases is None:
+        U, W = draw_bases(rng, shape)
+    else:
+        U, W = (np.asarray(x, dtype=np.float16) for x in bases)
+    cached_lens = np.asarray(cached_lens, dtype=np.int32)
+    chunk_lens = np.asarray(chunk_lens, dtype=np.int32)
+    total = cached_lens + chunk_lens
+    cache = fill_cache(rng, shape, total, cache_lens=cached_lens,
+                       spare_blocks=spare_blocks, shuffle=shuffle,
+                       keep_logical=keep_logical)
+    T = int(chunk_lens.sum())
+    dims = (T, shape.H, shape.d)
+    k_new = rng.standard_normal(dims, dtype=np.float32).astype(np.float16)
+    v_new = rng.standard_normal(dims, dtype=np.float32).astype(np.float16)
+    q = rng.standard_normal(dims, dtype=np.float32).astype(np.float16)
+    qsl = np.zeros(len(chunk_lens) + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(chunk_lens)
+    slots = np.empty(T, dtype=np.int64)
+    bs = shape.bs
+    for b in range(len(chunk_lens)):
+        pos = cached_lens[b] + np.arange(chunk_lens[b])
+        slots[qsl[b]:qsl[b + 1]] = (cache.block_tables[b, pos // bs].astype(np.int64) * bs
+                                    + pos % bs)
+    return PrefillCase(shape, U, W, cache, cached_lens, k_new, v_new, q, slots, qsl,
+                       1.0 / np.sqrt(shape.d), seed, name)
+
+
+def make_config(name: str, keep_logical=False):
+    """Build a named workload with its own seed."""
+    cfg = CONFIGS[name]
+    shape = cfg["shape"]
+    if cfg["kind"] == "decode":
+        return make_decode_case(shape, B=cfg["B"], seq=cfg["seq"], seed=cfg["seed"],
+                                keep_logical=keep_logical, name=name)
+    B = cfg["B"]
+    return make_prefill_case(shape, [cfg["cached"]] * B, [cfg["chunk"]] * B,
+                             seed=cfg["seed"], keep_logical=keep_logical, name=name)
