@@ -1,0 +1,184 @@
+/*
+ * starkv.h -- C ABI of libstarkv, attention over a paged KV cache stored in
+ * low-rank compressed form, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (Proxima README, introduction): each layer keeps a low-rank
+ * projection of its KV cache -- head-wise for keys, joint across heads for
+ * values -- in a compressed paged format.  With U_h in R^{d x r_k} per head
+ * and one W in R^{(H*d) x r_v}:
+ *
+ *     key latent    c_k[t, h] = U_h^T k[t, h]           (r_k values per head)
+ *     value latent  c_v[t]    = W^T vec(v[t])           (r_v values per token)
+ *
+ * where vec() flattens [H, d] head-major (row h*d + i of W pairs with
+ * v[t, h, i]) and W_h denotes rows h*d .. h*d+d-1 of W.  Attention runs on the
+ * latents without rebuilding K or V:
+ *
+ *     q~_h = U_h^T q_h,  s_t = scale * q~_h . c_k[t, h],  p = softmax(s),
+ *     z_h = sum_t p_t c_v[t],  out_h = W_h z_h.
+ *
+ * This equals softmax attention over the rebuilt K^ = U c_k, V^ = W c_v for
+ * any U and W.  Pages hold 16 tokens (README, "KV-cache capacity": block
+ * size 16); token t of sequence b lives in block block_tables[b][t / 16] at
+ * offset t % 16.
+ *
+ * Layouts (all fp16 = IEEE binary16, little-endian, dense, row-major):
+ *   k_cache  [num_blocks][H][16][r_k]
+ *   v_cache  [num_blocks][r_v][16]      (feature-major within a page)
+ *   U        [H][d][r_k]
+ *   W        [H*d][r_v]
+ *   q, k, v, out   [tokens][H][d]
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns all
+ *     memory, including workspaces; the library allocates nothing and keeps
+ *     no per-call state.  `stream` is a hipStream_t (NULL = default stream).
+ *     Calls are asynchronous on `stream`; nothing synchronises the host.
+ *   - Arguments are validated on the host BEFORE any HIP call: on failure the
+ *     call returns a non-zero status and enqueues nothing.  Device pointers
+ *     must be 16-byte aligned.  A launch failure maps to STARKV_ERR_LAUNCH.
+ *   - Contents of device index arrays (block tables, seq_lens, slots,
+ *     query_start_loc) are trusted.  Block ids outside [0, num_blocks) and
+ *     slots outside the cache are skipped rather than dereferenced.
+ *   - Compiled shape instances: (H, d, r_k, r_v) = (32, 128, 64, 512) and
+ *     (4, 64, 16, 64), block size 16.  Other shapes return
+ *     STARKV_ERR_UNSUPPORTED.
+ */
+#ifndef STARKV_H_
+#define STARKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define STARKV_ABI_VERSION 1
+
+typedef enum {
+  STARKV_OK = 0,
+  STARKV_ERR_NULL = 1,        /* a required pointer is NULL */
+  STARKV_ERR_DIMS = 2,        /* a size is negative, zero where it must not be, or inconsistent */
+  STARKV_ERR_UNSUPPORTED = 3, /* no compiled kernel instance for this shape */
+  STARKV_ERR_WORKSPACE = 4,   /* workspace smaller than the size query returned */
+  STARKV_ERR_ALIGN = 5,       /* a device pointer is not 16-byte aligned */
+  STARKV_ERR_LAUNCH = 6,      /* a kernel launch failed (hipGetLastError) */
+  STARKV_ERR_ARG = 7          /* another invalid argument (scale, timing selector) */
+} starkv_status;
+
+/* Model and cache dimensions (host struct). */
+typedef struct {
+  int32_t num_heads;  /* H */
+  int32_t head_dim;   /* d */
+  int32_t rank_k;     /* r_k, key latent size per head (<= d) */
+  int32_t rank_v;     /* r_v, joint value latent size (<= H*d) */
+  int32_t block_size; /* tokens per page; must be 16 */
+  int32_t num_blocks; /* pages in k_cache / v_cache (> 0) */
+} starkv_dims;
+
+/* Version of this ABI (STARKV_ABI_VERSION). */
+int32_t starkv_abi_version(void);
+
+/* Static, NUL-terminated description of a status code; never NULL. */
+const char* starkv_status_string(int32_t status);
+
+/* 1 if a kernel instance exists for these dims, else 0 (dims may be NULL -> 0). */
+int32_t starkv_shape_supported(const starkv_dims* dims);
+
+/*
+ * Append (README, "Kernel profiling breakdown": the write kernel's low-rank
+ * projection and paged write).  For each n < num_tokens with
+ * slot_mapping[n] >= 0, writes
+ *     k_cache[slot / 16][h][slot % 16][:] = fp16(U_h^T k[n, h, :])   for all h
+ *     v_cache[slot / 16][:][slot % 16]    = fp16(W^T vec(v[n]))
+ * rounded to nearest even from an fp32 accumulation.  Negative slots are
+ * skipped (padding); slots at or beyond num_blocks*16 are skipped.  Slots
+ * must be distinct.  num_tokens == 0 is a no-op.
+ *   k, v          [num_tokens][H][d] fp16
+ *   U, W          fp16, layouts above
+ *   slot_mapping  [num_tokens] int64
+ *   k_cache, v_cache  updated in place
+ */
+starkv_status starkv_append(const starkv_dims* dims, const void* k, const void* v, const void* U,
+                            const void* W, const int64_t* slot_mapping, int32_t num_tokens,
+                            void* k_cache, void* v_cache, void* stream);
+
+/*
+ * Workspace bytes (host out-parameter *bytes) that starkv_decode_attn needs
+ * for `batch` sequences of at most max_seq_len tokens.  Returns a status.
+ */
+starkv_status starkv_decode_workspace_size(const starkv_dims* dims, int32_t batch,
+                                           int32_t max_seq_len, size_t* bytes /* (host) */);
+
+/*
+ * Decode attention (README, "Per-decode-step attention"): one query per
+ * sequence attends to all seq_lens[b] cached tokens (append the step's token
+ * first).  out[b, h, :] = W_h sum_t softmax_t(scale * q~_h . c_k[t, h]) c_v[t].
+ *   q             [batch][H][d] fp16
+ *   block_tables  [batch][max_blocks_per_seq] int32; entries past
+ *                 ceil(seq_lens[b] / 16) are never read
+ *   seq_lens      [batch] int32, each in [0, max_seq_len]; 0 gives zeros
+ *   max_seq_len   (host) upper bound used to plan the split-K work; requires
+ *                 max_blocks_per_seq >= ceil(max_seq_len / 16)
+ *   scale         (host) softmax scale, normally 1/sqrt(d); finite, > 0
+ *   out           [batch][H][d] fp16
+ *   workspace     >= starkv_decode_workspace_size(...) bytes, 256-byte aligned
+ *                 preferred; contents need no initialisation
+ * Four kernels run on `stream`: q projection, split-K latent attention,
+ * split combine, and the W_h up-projection.
+ */
+starkv_status starkv_decode_attn(const starkv_dims* dims, const void* q, const void* k_cache,
+                                 const void* v_cache, const void* U, const void* W,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                 float scale, void* out, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * Workspace bytes for starkv_prefill_attn with total_q chunk queries.
+ */
+starkv_status starkv_prefill_workspace_size(const starkv_dims* dims, int32_t batch,
+                                            int32_t total_q, int32_t max_seq_len,
+                                            size_t* bytes /* (host) */);
+
+/*
+ * Chunked-prefill attention (README, "Per-prefill-chunk attention").
+ * Request b owns query rows query_start_loc[b] .. query_start_loc[b+1]-1,
+ * the last C_b = query_start_loc[b+1] - query_start_loc[b] of its
+ * seq_lens[b] cached tokens (append the chunk first).  Chunk query j sits at
+ * position P0 + j, P0 = seq_lens[b] - C_b, and sees keys 0 .. P0 + j.
+ *   q                [total_q][H][d] fp16
+ *   query_start_loc  [batch + 1] int32, non-decreasing, [0] = 0, [batch] = total_q
+ *   max_query_len    (host) >= every C_b
+ *   block_tables, seq_lens, max_seq_len, scale: as for decode; C_b <= seq_lens[b]
+ *   out              [total_q][H][d] fp16
+ */
+starkv_status starkv_prefill_attn(const starkv_dims* dims, const void* q,
+                                  const int32_t* query_start_loc, int32_t total_q,
+                                  int32_t max_query_len, const void* k_cache, const void* v_cache,
+                                  const void* U, const void* W, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                  int32_t batch, int32_t max_seq_len, float scale, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Profiling aid: record hipEvent_t `start` / `stop` on the call's stream
+ * immediately before and after one kernel of later calls.
+ *   which = 0 none (clears), 1 decode split-K attention, 2 prefill attention,
+ *   3 append.  Events are owned by the caller and must outlive the calls.
+ * Process-wide setting; not for concurrent use from several threads.
+ */
+starkv_status starkv_set_timing_events(void* start, void* stop, int32_t which);
+
+/*
+ * Split plan the decode call will use (host out-parameters), for reports.
+ */
+starkv_status starkv_decode_plan(const starkv_dims* dims, int32_t batch, int32_t max_seq_len,
+                                 int32_t* pages_per_split, int32_t* num_splits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STARKV_H_ */

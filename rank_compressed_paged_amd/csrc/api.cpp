@@ -1,0 +1,262 @@
+// C ABI of libstarkv: host-side validation, split planning, workspace
+// layout and kernel launches.  Every check runs before the first HIP call,
+// so a rejected call enqueues nothing; no C++ exception crosses the ABI.
+#include <cmath>
+#include <initializer_list>
+#include <cstdlib>
+
+#include "../../include/starkv.h"
+#include "kernels.h"
+
+namespace starkv {
+
+TimingHook g_timing;
+
+bool shape_supported(const ShapeKey& s) {
+  return (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) ||
+         (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64);
+}
+
+static int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  const int x = std::atoi(v);
+  return x > 0 ? x : dflt;
+}
+
+static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
+
+// Split-K plan: aim for about kTarget work groups over the batch, but keep
+// at least kMinPages pages per split so the partial state (H*r_v fp32 per
+// split) stays small next to the latents read; at most 256 splits.
+DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int bs) {
+  (void)s;
+  const int pages = cdiv(max_seq_len, bs);
+  if (pages <= 0 || batch <= 0) return DecodePlan{1, 1};
+  const int target = env_int("STARKV_DECODE_TARGET_WGS", 512);
+  const int min_pps = env_int("STARKV_DECODE_MIN_PAGES", 4);
+  const int want_splits = cdiv(target, batch);
+  int pps = cdiv(pages, want_splits);
+  if (pps < min_pps) pps = min_pps;
+  int ns = cdiv(pages, pps);
+  while (ns > 256) {
+    pps *= 2;
+    ns = cdiv(pages, pps);
+  }
+  return DecodePlan{pps, ns};
+}
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+DecodeWorkspace decode_workspace_layout(const ShapeKey& s, int batch, const DecodePlan& p) {
+  const size_t r16 = (size_t)((s.H + 15) / 16) * 16;
+  DecodeWorkspace w;
+  size_t off = 0;
+  w.qt_off = off;
+  off = align256(off + (size_t)batch * s.H * s.rk * 2);
+  w.ml_off = off;
+  off = align256(off + (size_t)batch * p.num_splits * 2 * r16 * 4);
+  w.acc_off = off;
+  off = align256(off + (size_t)batch * p.num_splits * r16 * s.rv * 4);
+  w.z_off = off;
+  off = align256(off + (size_t)batch * s.H * s.rv * 4);
+  w.total = off;
+  return w;
+}
+
+PrefillWorkspace prefill_workspace_layout(const ShapeKey& s, int total_q) {
+  PrefillWorkspace w;
+  size_t off = 0;
+  w.qt_off = off;
+  off = align256(off + (size_t)total_q * s.H * s.rk * 2);
+  w.z_off = off;
+  off = align256(off + (size_t)total_q * s.H * s.rv * 4);
+  w.total = off;
+  return w;
+}
+
+}  // namespace starkv
+
+using namespace starkv;
+
+namespace {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+starkv_status check_dims(const starkv_dims* d, ShapeKey* key) {
+  if (!d) return STARKV_ERR_NULL;
+  if (d->num_heads <= 0 || d->head_dim <= 0 || d->rank_k <= 0 || d->rank_v <= 0 ||
+      d->block_size <= 0 || d->num_blocks <= 0)
+    return STARKV_ERR_DIMS;
+  if (d->rank_k > d->head_dim || (long)d->rank_v > (long)d->num_heads * d->head_dim)
+    return STARKV_ERR_DIMS;
+  const ShapeKey k{d->num_heads, d->head_dim, d->rank_k, d->rank_v};
+  if (d->block_size != 16 || !shape_supported(k)) return STARKV_ERR_UNSUPPORTED;
+  *key = k;
+  return STARKV_OK;
+}
+
+starkv_status check_ptrs(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (!p) return STARKV_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return STARKV_ERR_ALIGN;
+  return STARKV_OK;
+}
+
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+
+starkv_status check_paging(int32_t batch, int32_t max_seq_len, int32_t max_blocks, int bs) {
+  if (batch < 0 || max_seq_len < 0 || max_blocks < 0) return STARKV_ERR_DIMS;
+  if (batch > 65535) return STARKV_ERR_DIMS;
+  if ((long)max_blocks * bs < (long)max_seq_len) return STARKV_ERR_DIMS;
+  return STARKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t starkv_abi_version(void) { return STARKV_ABI_VERSION; }
+
+const char* starkv_status_string(int32_t status) {
+  switch (status) {
+    case STARKV_OK: return "ok";
+    case STARKV_ERR_NULL: return "required pointer is NULL";
+    case STARKV_ERR_DIMS: return "invalid or inconsistent sizes";
+    case STARKV_ERR_UNSUPPORTED: return "no kernel instance for this shape";
+    case STARKV_ERR_WORKSPACE: return "workspace too small";
+    case STARKV_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case STARKV_ERR_LAUNCH: return "kernel launch failed";
+    case STARKV_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+int32_t starkv_shape_supported(const starkv_dims* dims) {
+  ShapeKey k;
+  return check_dims(dims, &k) == STARKV_OK ? 1 : 0;
+}
+
+starkv_status starkv_append(const starkv_dims* dims, const void* k, const void* v, const void* U,
+                            const void* W, const int64_t* slot_mapping, int32_t num_tokens,
+                            void* k_cache, void* v_cache, void* stream) {
+  ShapeKey key;
+  starkv_status st = check_dims(dims, &key);
+  if (st != STARKV_OK) return st;
+  if (num_tokens < 0) return STARKV_ERR_DIMS;
+  if (num_tokens == 0) return STARKV_OK;
+  st = check_ptrs({k, v, U, W, slot_mapping, k_cache, v_cache});
+  if (st != STARKV_OK) return st;
+  const hipError_t e = launch_append(key, k, v, U, W, slot_mapping, num_tokens, dims->num_blocks,
+                                     k_cache, v_cache, (hipStream_t)stream);
+  return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
+}
+
+starkv_status starkv_decode_workspace_size(const starkv_dims* dims, int32_t batch,
+                                           int32_t max_seq_len, size_t* bytes) {
+  ShapeKey key;
+  starkv_status st = check_dims(dims, &key);
+  if (st != STARKV_OK) return st;
+  if (!bytes) return STARKV_ERR_NULL;
+  if (batch < 0 || max_seq_len < 0 || batch > 65535) return STARKV_ERR_DIMS;
+  const DecodePlan p = plan_decode(key, batch, max_seq_len, dims->block_size);
+  *bytes = decode_workspace_layout(key, batch, p).total;
+  return STARKV_OK;
+}
+
+starkv_status starkv_decode_plan(const starkv_dims* dims, int32_t batch, int32_t max_seq_len,
+                                 int32_t* pages_per_split, int32_t* num_splits) {
+  ShapeKey key;
+  starkv_status st = check_dims(dims, &key);
+  if (st != STARKV_OK) return st;
+  if (!pages_per_split || !num_splits) return STARKV_ERR_NULL;
+  if (batch < 0 || max_seq_len < 0) return STARKV_ERR_DIMS;
+  const DecodePlan p = plan_decode(key, batch, max_seq_len, dims->block_size);
+  *pages_per_split = p.pages_per_split;
+  *num_splits = p.num_splits;
+  return STARKV_OK;
+}
+
+starkv_status starkv_decode_attn(const starkv_dims* dims, const void* q, const void* k_cache,
+                                 const void* v_cache, const void* U, const void* W,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                 float scale, void* out, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  ShapeKey key;
+  starkv_status st = check_dims(dims, &key);
+  if (st != STARKV_OK) return st;
+  st = check_paging(batch, max_seq_len, max_blocks_per_seq, dims->block_size);
+  if (st != STARKV_OK) return st;
+  if (!scale_ok(scale)) return STARKV_ERR_ARG;
+  if (batch == 0) return STARKV_OK;
+  st = check_ptrs({q, k_cache, v_cache, U, W, block_tables, seq_lens, out, workspace});
+  if (st != STARKV_OK) return st;
+  const DecodePlan p = plan_decode(key, batch, max_seq_len, dims->block_size);
+  const DecodeWorkspace ws = decode_workspace_layout(key, batch, p);
+  if (workspace_bytes < ws.total) return STARKV_ERR_WORKSPACE;
+  char* wb = (char*)workspace;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_qproj(key, q, U, batch, scale, wb + ws.qt_off, s);
+  if (e != hipSuccess) return STARKV_ERR_LAUNCH;
+  e = launch_decode(key, p, wb + ws.qt_off, k_cache, v_cache, W, block_tables,
+                    max_blocks_per_seq, seq_lens, dims->num_blocks, batch,
+                    (float*)(wb + ws.ml_off), (float*)(wb + ws.acc_off), (float*)(wb + ws.z_off),
+                    out, s);
+  return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
+}
+
+starkv_status starkv_prefill_workspace_size(const starkv_dims* dims, int32_t batch,
+                                            int32_t total_q, int32_t max_seq_len, size_t* bytes) {
+  ShapeKey key;
+  starkv_status st = check_dims(dims, &key);
+  if (st != STARKV_OK) return st;
+  if (!bytes) return STARKV_ERR_NULL;
+  if (batch < 0 || total_q < 0 || max_seq_len < 0) return STARKV_ERR_DIMS;
+  *bytes = prefill_workspace_layout(key, total_q).total;
+  return STARKV_OK;
+}
+
+starkv_status starkv_prefill_attn(const starkv_dims* dims, const void* q,
+                                  const int32_t* query_start_loc, int32_t total_q,
+                                  int32_t max_query_len, const void* k_cache, const void* v_cache,
+                                  const void* U, const void* W, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                  int32_t batch, int32_t max_seq_len, float scale, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  ShapeKey key;
+  starkv_status st = check_dims(dims, &key);
+  if (st != STARKV_OK) return st;
+  st = check_paging(batch, max_seq_len, max_blocks_per_seq, dims->block_size);
+  if (st != STARKV_OK) return st;
+  if (total_q < 0 || max_query_len < 0) return STARKV_ERR_DIMS;
+  if (total_q > 0 && max_query_len == 0) return STARKV_ERR_DIMS;
+  if (max_query_len > max_seq_len) return STARKV_ERR_DIMS;
+  if (!scale_ok(scale)) return STARKV_ERR_ARG;
+  if (batch == 0 || total_q == 0) return STARKV_OK;
+  st = check_ptrs({q, query_start_loc, k_cache, v_cache, U, W, block_tables, seq_lens, out,
+                   workspace});
+  if (st != STARKV_OK) return st;
+  const PrefillWorkspace ws = prefill_workspace_layout(key, total_q);
+  if (workspace_bytes < ws.total) return STARKV_ERR_WORKSPACE;
+  char* wb = (char*)workspace;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_qproj(key, q, U, total_q, scale, wb + ws.qt_off, s);
+  if (e != hipSuccess) return STARKV_ERR_LAUNCH;
+  e = launch_prefill(key, wb + ws.qt_off, query_start_loc, total_q, max_query_len, k_cache,
+                     v_cache, W, block_tables, max_blocks_per_seq, seq_lens, dims->num_blocks,
+                     batch, (float*)(wb + ws.z_off), out, s);
+  return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
+}
+
+starkv_status starkv_set_timing_events(void* start, void* stop, int32_t which) {
+  if (which < 0 || which > 3) return STARKV_ERR_ARG;
+  if (which != 0 && (!start || !stop)) return STARKV_ERR_NULL;
+  g_timing.start = (hipEvent_t)start;
+  g_timing.stop = (hipEvent_t)stop;
+  g_timing.which = which;
+  return STARKV_OK;
+}
+
+}  // extern "C"

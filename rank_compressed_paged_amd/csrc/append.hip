@@ -1,0 +1,161 @@
+// Append: project new full-precision K/V into latents and scatter them into
+// their paged slots (the README's write kernel, "Kernel profiling
+// breakdown": low-rank projection plus the paged write).
+//
+//   c_k[n, h, :] = U_h^T k[n, h, :]       (a [N x d] x [d x r_k] product per head)
+//   c_v[n, :]    = W^T vec(v[n])           (one [N x H*d] x [H*d x r_v] product)
+//
+// Both products are C = A B with A row-major (contraction contiguous) and B
+// row-major (outputs contiguous), so one tiled matrix-core kernel serves both.
+// A 256-thread work group computes a 64 (tokens) x 64 (outputs) tile with
+// v_mfma_f32_16x16x32_f16; A operands come straight from memory (8
+// contiguous fp16 per lane), B is staged through LDS transposed so that each
+// lane again reads 8 contiguous values.  The epilogue rounds to fp16
+// (nearest even) and writes slot_mapping[n]; negative or out-of-range slots
+// are skipped.  Layouts: k_cache [NB, H, 16, r_k], v_cache [NB, r_v, 16].
+#include "common.h"
+#include "kernels.h"
+
+namespace starkv {
+
+struct AppendArgs {
+  const half_t* k;  // [N, H, d]
+  const half_t* v;  // [N, H, d]
+  const half_t* U;  // [H, d, r_k]
+  const half_t* W;  // [H*d, r_v]
+  const int64_t* slots;
+  half_t* k_cache;
+  half_t* v_cache;
+  int N, H, D, RK, RV, num_blocks;
+  int tiles_m, v_tiles_n, k_tiles_n;
+};
+
+constexpr int AT_M = 64, AT_N = 64, AT_K = 32, AT_LDS = AT_K + 8;
+
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  __shared__ __attribute__((aligned(16))) half_t sB[AT_N][AT_LDS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int col = lane & 15, quad = lane >> 4;
+
+  // ---- job decode: value tiles first, then key tiles (one head each)
+  int job = blockIdx.x;
+  const int n_vjobs = a.tiles_m * a.v_tiles_n;
+  bool is_v;
+  int mt_idx, nt_idx, h = 0;
+  if (job < n_vjobs) {
+    is_v = true;
+    mt_idx = job / a.v_tiles_n;
+    nt_idx = job % a.v_tiles_n;
+  } else {
+    is_v = false;
+    job -= n_vjobs;
+    mt_idx = job / (a.H * a.k_tiles_n);
+    const int rem = job % (a.H * a.k_tiles_n);
+    h = rem / a.k_tiles_n;
+    nt_idx = rem % a.k_tiles_n;
+  }
+  const int HD = a.H * a.D;
+  const half_t* A = is_v ? a.v : a.k + (size_t)h * a.D;
+  const int lda = HD;
+  const half_t* Bm = is_v ? a.W : a.U + (size_t)h * a.D * a.RK;
+  const int ldb = is_v ? a.RV : a.RK;
+  const int Kdim = is_v ? HD : a.D;
+  const int Ndim = is_v ? a.RV : a.RK;
+  const int m_base = mt_idx * AT_M, n_base = nt_idx * AT_N;
+
+  float4v acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = zero4();
+
+  // staging role: k row kk, outputs n0 .. n0+7
+  const int kk = tid >> 3, n0 = (tid & 7) * 8;
+  const bool b_ok = (n_base + n0 + 8 <= Ndim);
+  const half8 hz = {};
+
+  int arow[2];
+  bool arow_ok[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int m = m_base + wm * 32 + mt * 16 + col;
+    arow_ok[mt] = m < a.N;
+    arow[mt] = arow_ok[mt] ? m : 0;
+  }
+
+  for (int k0 = 0; k0 < Kdim; k0 += AT_K) {
+    const half8 bv = b_ok ? *(const half8*)(Bm + (size_t)(k0 + kk) * ldb + n_base + n0) : hz;
+    half8 av[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      av[mt] = arow_ok[mt] ? *(const half8*)(A + (size_t)arow[mt] * lda + k0 + quad * 8) : hz;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sB[n0 + e][kk] = bv[e];
+    __syncthreads();
+    half8 bq[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) bq[nt] = *(const half8*)&sB[wn * 32 + nt * 16 + col][quad * 8];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16x16x32(av[mt], bq[nt], acc[mt][nt]);
+  }
+
+  // ---- epilogue: D[token][output], lane holds rows 4*quad + r, column col
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = m_base + wm * 32 + mt * 16 + quad * 4 + r;
+      if (m >= a.N) continue;
+      const int64_t slot = a.slots[m];
+      if (slot < 0) continue;
+      const int64_t blk = slot / 16;
+      const int off = (int)(slot % 16);
+      if (blk >= a.num_blocks) continue;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int n = n_base + wn * 32 + nt * 16 + col;
+        if (n >= Ndim) continue;
+        const half_t val = (half_t)acc[mt][nt][r];
+        if (is_v)
+          a.v_cache[((size_t)blk * a.RV + n) * 16 + off] = val;
+        else
+          a.k_cache[(((size_t)blk * a.H + h) * 16 + off) * a.RK + n] = val;
+      }
+    }
+  }
+}
+
+hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const void* U,
+                         const void* W, const int64_t* slots, int n_tokens, int num_blocks,
+                         void* k_cache, void* v_cache, hipStream_t st) {
+  if (n_tokens <= 0) return hipSuccess;
+  AppendArgs a;
+  a.k = (const half_t*)k;
+  a.v = (const half_t*)v;
+  a.U = (const half_t*)U;
+  a.W = (const half_t*)W;
+  a.slots = slots;
+  a.k_cache = (half_t*)k_cache;
+  a.v_cache = (half_t*)v_cache;
+  a.N = n_tokens;
+  a.H = s.H;
+  a.D = s.d;
+  a.RK = s.rk;
+  a.RV = s.rv;
+  a.num_blocks = num_blocks;
+  a.tiles_m = (n_tokens + AT_M - 1) / AT_M;
+  a.v_tiles_n = (s.rv + AT_N - 1) / AT_N;
+  a.k_tiles_n = (s.rk + AT_N - 1) / AT_N;
+  const long jobs = (long)a.tiles_m * (a.v_tiles_n + (long)s.H * a.k_tiles_n);
+  if (g_timing.which == TIME_APPEND && g_timing.start) hipEventRecord(g_timing.start, st);
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)jobs), dim3(256), 0, st, a);
+  if (g_timing.which == TIME_APPEND && g_timing.stop) hipEventRecord(g_timing.stop, st);
+  return hipGetLastError();
+}
+
+}  // namespace starkv

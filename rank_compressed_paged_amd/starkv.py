@@ -1,0 +1,228 @@
+"""Thin ctypes binding over libstarkv (declared in include/starkv.h).
+
+Argument marshalling only: every step of the attention path runs in the HIP
+kernels behind the C ABI.  Tensors are torch tensors on the GPU; this module
+checks dtype, shape, contiguity and device, then passes ``data_ptr()`` and
+the current HIP stream.  Importing it raises if the library is missing, and
+nothing here falls back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("STARKV_LIB", os.path.join(_HERE, "libstarkv.so"))
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libstarkv.so not found at {LIB_PATH}; build it with "
+        "`python -m rank_compressed_paged_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+STATUS = {
+    0: "STARKV_OK", 1: "STARKV_ERR_NULL", 2: "STARKV_ERR_DIMS", 3: "STARKV_ERR_UNSUPPORTED",
+    4: "STARKV_ERR_WORKSPACE", 5: "STARKV_ERR_ALIGN", 6: "STARKV_ERR_LAUNCH", 7: "STARKV_ERR_ARG",
+}
+EXPORTED = [
+    "starkv_abi_version", "starkv_status_string", "starkv_shape_supported", "starkv_append",
+    "starkv_decode_workspace_size", "starkv_decode_attn", "starkv_prefill_workspace_size",
+    "starkv_prefill_attn", "starkv_set_timing_events", "starkv_decode_plan",
+]
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("rank_k", ctypes.c_int32), ("rank_v", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32)]
+
+
+class StarKVError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = int(status)
+        msg = _lib.starkv_status_string(int(status)).decode()
+        super().__init__(f"{where}: {STATUS.get(int(status), status)} ({msg})")
+
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+_lib.starkv_abi_version.restype = _i32
+_lib.starkv_abi_version.argtypes = []
+_lib.starkv_status_string.restype = ctypes.c_char_p
+_lib.starkv_status_string.argtypes = [_i32]
+_lib.starkv_shape_supported.restype = _i32
+_lib.starkv_shape_supported.argtypes = [ctypes.POINTER(Dims)]
+_lib.starkv_append.restype = _i32
+_lib.starkv_append.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]
+_lib.starkv_decode_workspace_size.restype = _i32
+_lib.starkv_decode_workspace_size.argtypes = [ctypes.POINTER(Dims), _i32, _i32, ctypes.POINTER(_sz)]
+_lib.starkv_decode_plan.restype = _i32
+_lib.starkv_decode_plan.argtypes = [ctypes.POINTER(Dims), _i32, _i32, ctypes.POINTER(_i32),
+                                    ctypes.POINTER(_i32)]
+_lib.starkv_decode_attn.restype = _i32
+_lib.starkv_decode_attn.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
+                                    _i32, _i32, ctypes.c_float, _vp, _vp, _sz, _vp]
+_lib.starkv_prefill_workspace_size.restype = _i32
+_lib.starkv_prefill_workspace_size.argtypes = [ctypes.POINTER(Dims), _i32, _i32, _i32,
+                                               ctypes.POINTER(_sz)]
+_lib.starkv_prefill_attn.restype = _i32
+_lib.starkv_prefill_attn.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _i32, _i32, _vp, _vp, _vp,
+                                     _vp, _vp, _i32, _vp, _i32, _i32, ctypes.c_float, _vp, _vp,
+                                     _sz, _vp]
+_lib.starkv_set_timing_events.restype = _i32
+_lib.starkv_set_timing_events.argtypes = [_vp, _vp, _i32]
+
+TIME_NONE, TIME_DECODE_SPLIT, TIME_PREFILL_ATTN, TIME_APPEND = 0, 1, 2, 3
+
+
+def lib():
+    return _lib
+
+
+def abi_version():
+    return _lib.starkv_abi_version()
+
+
+def _check(status, where):
+    if status != 0:
+        raise StarKVError(status, where)
+
+
+def make_dims(H, d, r_k, r_v, num_blocks, block_size=16):
+    return Dims(H, d, r_k, r_v, block_size, num_blocks)
+
+
+def dims_of(k_cache, v_cache, U, W):
+    NB, H, bs, r_k = k_cache.shape
+    d = U.shape[1]
+    r_v = v_cache.shape[1]
+    return make_dims(H, d, r_k, r_v, NB, bs)
+
+
+def shape_supported(dims):
+    return bool(_lib.starkv_shape_supported(ctypes.byref(dims)))
+
+
+def _dev(t, dtype, name, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return _vp(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return _vp(s.cuda_stream)
+
+
+def decode_workspace_size(dims, batch, max_seq_len):
+    out = _sz(0)
+    _check(_lib.starkv_decode_workspace_size(ctypes.byref(dims), int(batch), int(max_seq_len),
+                                             ctypes.byref(out)), "starkv_decode_workspace_size")
+    return int(out.value)
+
+
+def decode_plan(dims, batch, max_seq_len):
+    pps, ns = _i32(0), _i32(0)
+    _check(_lib.starkv_decode_plan(ctypes.byref(dims), int(batch), int(max_seq_len),
+                                   ctypes.byref(pps), ctypes.byref(ns)), "starkv_decode_plan")
+    return int(pps.value), int(ns.value)
+
+
+def prefill_workspace_size(dims, batch, total_q, max_seq_len):
+    out = _sz(0)
+    _check(_lib.starkv_prefill_workspace_size(ctypes.byref(dims), int(batch), int(total_q),
+                                              int(max_seq_len), ctypes.byref(out)),
+           "starkv_prefill_workspace_size")
+    return int(out.value)
+
+
+def alloc_workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def append(k, v, U, W, slot_mapping, k_cache, v_cache, stream=None):
+    """Project k, v [N, H, d] to latents and write them to slot_mapping [N] (int64)."""
+    dims = dims_of(k_cache, v_cache, U, W)
+    N = k.shape[0]
+    H, d = dims.num_heads, dims.head_dim
+    st = _lib.starkv_append(
+        ctypes.byref(dims), _dev(k, torch.float16, "k", (N, H, d)),
+        _dev(v, torch.float16, "v", (N, H, d)), _dev(U, torch.float16, "U"),
+        _dev(W, torch.float16, "W"), _dev(slot_mapping, torch.int64, "slot_mapping", (N,)),
+        int(N), _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"),
+        _stream(stream))
+    _check(st, "starkv_append")
+
+
+def decode_attn(q, k_cache, v_cache, U, W, block_tables, seq_lens, max_seq_len, scale=None,
+                out=None, workspace=None, stream=None):
+    """Decode attention for q [B, H, d]; returns out [B, H, d] fp16."""
+    dims = dims_of(k_cache, v_cache, U, W)
+    B = q.shape[0]
+    H, d = dims.num_heads, dims.head_dim
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.float16, device=q.device)
+    need = decode_workspace_size(dims, B, max_seq_len)
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    st = _lib.starkv_decode_attn(
+        ctypes.byref(dims), _dev(q, torch.float16, "q", (B, H, d)),
+        _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"),
+        _dev(U, torch.float16, "U"), _dev(W, torch.float16, "W"),
+        _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
+        _dev(seq_lens, torch.int32, "seq_lens", (B,)), int(B), int(max_seq_len), float(scale),
+        _dev(out, torch.float16, "out", (B, H, d)), _dev(workspace, torch.uint8, "workspace"),
+        int(workspace.numel()), _stream(stream))
+    _check(st, "starkv_decode_attn")
+    return out
+
+
+def prefill_attn(q, query_start_loc, max_query_len, k_cache, v_cache, U, W, block_tables,
+                 seq_lens, max_seq_len, scale=None, out=None, workspace=None, stream=None):
+    """Chunked-prefill attention for q [total_q, H, d]; returns out fp16."""
+    dims = dims_of(k_cache, v_cache, U, W)
+    T = q.shape[0]
+    B = seq_lens.shape[0]
+    H, d = dims.num_heads, dims.head_dim
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((T, H, d), dtype=torch.float16, device=q.device)
+    need = prefill_workspace_size(dims, B, T, max_seq_len)
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    st = _lib.starkv_prefill_attn(
+        ctypes.byref(dims), _dev(q, torch.float16, "q", (T, H, d)),
+        _dev(query_start_loc, torch.int32, "query_start_loc", (B + 1,)), int(T),
+        int(max_query_len), _dev(k_cache, torch.float16, "k_cache"),
+        _dev(v_cache, torch.float16, "v_cache"), _dev(U, torch.float16, "U"),
+        _dev(W, torch.float16, "W"), _dev(block_tables, torch.int32, "block_tables"),
+        int(block_tables.shape[1]), _dev(seq_lens, torch.int32, "seq_lens", (B,)), int(B),
+        int(max_seq_len), float(scale), _dev(out, torch.float16, "out", (T, H, d)),
+        _dev(workspace, torch.uint8, "workspace"), int(workspace.numel()), _stream(stream))
+    _check(st, "starkv_prefill_attn")
+    return out
+
+
+def set_timing_events(start_event, stop_event, which):
+    """Record torch.cuda.Event objects around one kernel of later calls."""
+    if which == TIME_NONE:
+        _check(_lib.starkv_set_timing_events(None, None, 0), "starkv_set_timing_events")
+        return
+    _check(_lib.starkv_set_timing_events(_vp(start_event.cuda_event), _vp(stop_event.cuda_event),
+                                         int(which)), "starkv_set_timing_events")

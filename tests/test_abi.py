@@ -1,0 +1,120 @@
+"""The C-ABI library loads, exports every symbol include/starkv.h declares,
+and rejects bad arguments on the host before any HIP call (no GPU needed:
+every call here fails validation, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rank_compressed_paged_amd import starkv as sk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "starkv.h")
+
+FAKE = 0x10000          # aligned, never dereferenced: validation fails first
+MISALIGNED = 0x10008
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(starkv_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_match_header():
+    decl = declared_symbols()
+    assert decl, "no declarations parsed"
+    for name in decl:
+        assert hasattr(sk.lib(), name), f"{name} declared but not exported"
+    assert sorted(sk.EXPORTED) == decl
+
+
+def test_version_and_status_strings():
+    assert sk.abi_version() == 1
+    for s in range(0, 8):
+        assert sk.lib().starkv_status_string(s)
+    assert sk.lib().starkv_status_string(99) == b"unknown status"
+
+
+def _main_dims(nb=8):
+    return sk.make_dims(32, 128, 64, 512, nb)
+
+
+def test_shape_support():
+    assert sk.shape_supported(_main_dims())
+    assert sk.shape_supported(sk.make_dims(4, 64, 16, 64, 3))
+    assert not sk.shape_supported(sk.make_dims(32, 128, 64, 256, 3))
+    assert not sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, block_size=32))
+    assert not sk.shape_supported(sk.make_dims(32, 128, 256, 512, 3))  # r_k > d
+    assert not sk.shape_supported(sk.make_dims(32, 128, 64, 512, 0))
+
+
+def _decode(dims, q=FAKE, kc=FAKE, vc=FAKE, U=FAKE, W=FAKE, bt=FAKE, mb=128, sl=FAKE, B=16,
+            msl=2048, scale=0.088, out=FAKE, ws=FAKE, wsb=0):
+    return sk.lib().starkv_decode_attn(ctypes.byref(dims), q, kc, vc, U, W, bt, mb, sl, B, msl,
+                                       scale, out, ws, wsb, None)
+
+
+def test_decode_validation():
+    d = _main_dims()
+    need = sk.decode_workspace_size(d, 16, 2048)
+    assert need > 16 * 32 * 512 * 4
+    assert _decode(d) == 4                                   # workspace too small
+    assert _decode(d, q=None, wsb=need) == 1                 # null pointer
+    assert _decode(d, q=MISALIGNED, wsb=need) == 5           # misaligned
+    assert _decode(d, mb=100, wsb=need) == 2                 # block table too narrow
+    assert _decode(d, B=-1) == 2
+    assert _decode(d, scale=0.0) == 7
+    assert _decode(d, scale=float("nan")) == 7
+    assert _decode(sk.make_dims(32, 128, 64, 256, 8)) == 3   # unsupported shape
+    assert sk.lib().starkv_decode_attn(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, 1, 1,
+                                       0.1, FAKE, FAKE, 0, None) == 1
+    assert _decode(d, B=0) == 0                              # empty batch: no-op
+
+
+def test_append_validation():
+    d = _main_dims()
+    f = sk.lib().starkv_append
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, FAKE, None) == 2
+    assert f(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None) == 1
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, MISALIGNED, FAKE, 4, FAKE, FAKE, None) == 5
+    assert f(ctypes.byref(d), None, None, None, None, None, 0, None, None, None) == 0
+
+
+def test_prefill_validation():
+    d = _main_dims()
+    f = sk.lib().starkv_prefill_attn
+    need = sk.prefill_workspace_size(d, 16, 4096, 4352)
+    assert need >= 4096 * 32 * (64 * 2 + 512 * 4)
+    args = lambda **kw: dict(dict(q=FAKE, qsl=FAKE, T=4096, mq=256, kc=FAKE, vc=FAKE, U=FAKE,
+                                  W=FAKE, bt=FAKE, mb=272, sl=FAKE, B=16, msl=4352, scale=0.088,
+                                  out=FAKE, ws=FAKE, wsb=0), **kw)
+
+    def call(a):
+        return f(ctypes.byref(d), a["q"], a["qsl"], a["T"], a["mq"], a["kc"], a["vc"], a["U"],
+                 a["W"], a["bt"], a["mb"], a["sl"], a["B"], a["msl"], a["scale"], a["out"],
+                 a["ws"], a["wsb"], None)
+    assert call(args()) == 4
+    assert call(args(qsl=None, wsb=need)) == 1
+    assert call(args(mq=0, wsb=need)) == 2
+    assert call(args(mq=5000, wsb=need)) == 2
+    assert call(args(mb=10, wsb=need)) == 2
+    assert call(args(scale=-1.0, wsb=need)) == 7
+    assert call(args(T=0)) == 0
+
+
+def test_timing_event_validation():
+    f = sk.lib().starkv_set_timing_events
+    assert f(None, None, 0) == 0
+    assert f(None, None, 1) == 1
+    assert f(FAKE, FAKE, 9) == 7
+
+
+def test_decode_plan_properties():
+    d = _main_dims()
+    for B, L in [(16, 2048), (64, 8192), (20, 32768), (1, 1), (2, 256), (1, 40000)]:
+        pps, ns = sk.decode_plan(d, B, L)
+        pages = -(-L // 16)
+        assert 1 <= ns <= 256 and pps >= 1
+        assert pps * ns >= pages and pps * (ns - 1) < pages

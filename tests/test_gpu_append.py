@@ -1,0 +1,107 @@
+"""GPU parity of the fused projection + paged scatter (append) against the
+oracle: written slots are bit-exact, values within one fp16 ulp."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import dev, note
+from rank_compressed_paged_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sk():
+    from rank_compressed_paged_amd import starkv
+    return starkv
+
+
+def _ulp_diff(a, b):
+    """Distance in fp16 units in the last place (same-sign ordering)."""
+    ai = a.view(np.int16).astype(np.int32)
+    bi = b.view(np.int16).astype(np.int32)
+    ai = np.where(ai < 0, -32768 - ai, ai)
+    bi = np.where(bi < 0, -32768 - bi, bi)
+    return np.abs(ai - bi)
+
+
+def _case(shape, n, seed, neg_every=0, nb_extra=3):
+    rng = np.random.default_rng(seed)
+    U, W = wl.draw_bases(rng, shape)
+    nb = (n + shape.bs - 1) // shape.bs + nb_extra
+    slots = rng.permutation(nb * shape.bs)[:n].astype(np.int64)
+    if neg_every:
+        slots[::neg_every] = -1
+    k = rng.standard_normal((n, shape.H, shape.d), dtype=np.float32).astype(np.float16)
+    v = rng.standard_normal((n, shape.H, shape.d), dtype=np.float32).astype(np.float16)
+    kc = wl._nan_f16((nb, shape.H, shape.bs, shape.r_k))
+    vc = wl._nan_f16((nb, shape.r_v, shape.bs))
+    return U, W, k, v, slots, kc, vc
+
+
+def _run(sk, U, W, k, v, slots, kc, vc):
+    tk, tv = dev(kc), dev(vc)
+    sk.append(dev(k), dev(v), dev(U), dev(W), dev(slots), tk, tv)
+    torch.cuda.synchronize()
+    return tk.cpu().numpy(), tv.cpu().numpy()
+
+
+def _check(gk, gv, rk, rv, what):
+    # identical NaN pattern: exactly the listed slots were written
+    assert np.array_equal(np.isnan(gk), np.isnan(rk)), f"{what}: k slot set differs"
+    assert np.array_equal(np.isnan(gv), np.isnan(rv)), f"{what}: v slot set differs"
+    m = ~np.isnan(rk)
+    uk = _ulp_diff(gk[m], rk[m])
+    mv = ~np.isnan(rv)
+    uv = _ulp_diff(gv[mv], rv[mv])
+    print(f"[parity] {what}: k max ulp {uk.max(initial=0)}, v max ulp {uv.max(initial=0)}", flush=True)
+    assert uk.max(initial=0) <= 1 and uv.max(initial=0) <= 1
+
+
+@pytest.mark.parametrize("shape,n,seed,neg", [(wl.MAIN, 16, 31, 0), (wl.MAIN, 300, 32, 7),
+                                              (wl.TINY, 5, 33, 2), (wl.TINY, 130, 34, 0)],
+                         ids=["main_decode_step", "main_ragged_300", "tiny_5", "tiny_130"])
+def test_append_matches_oracle(sk, shape, n, seed, neg):
+    U, W, k, v, slots, kc, vc = _case(shape, n, seed, neg)
+    note(f"append {shape} n={n}")
+    gk, gv = _run(sk, U, W, k, v, slots, kc, vc)
+    rk, rv = oracle.append(k, v, U, W, slots, kc, vc)
+    _check(gk, gv, rk, rv, f"append n={n}")
+
+
+def test_append_selection_bases_bit_exact(sk):
+    """Bases that pick coordinates (one 1.0 per column) make every latent an
+    exact copy of an input value, so the whole cache must match bit for bit."""
+    sh = wl.MAIN
+    rng = np.random.default_rng(35)
+    U = np.zeros((sh.H, sh.d, sh.r_k), np.float16)
+    for h in range(sh.H):
+        U[h, rng.permutation(sh.d)[:sh.r_k], np.arange(sh.r_k)] = 1.0
+    W = np.zeros((sh.H * sh.d, sh.r_v), np.float16)
+    W[rng.permutation(sh.H * sh.d)[:sh.r_v], np.arange(sh.r_v)] = 1.0
+    _, _, k, v, slots, kc, vc = _case(sh, 77, 36, 5)
+    note("append selection bases")
+    gk, gv = _run(sk, U, W, k, v, slots, kc, vc)
+    rk, rv = oracle.append(k, v, U, W, slots, kc, vc)
+    assert np.array_equal(gk.view(np.uint16), rk.view(np.uint16))
+    assert np.array_equal(gv.view(np.uint16), rv.view(np.uint16))
+
+
+def test_prefill_chunk_append_full_size(sk):
+    """The prefill workload's append (16 x 256 new tokens): slot set exact,
+    values within one ulp on a sample of tokens."""
+    case = wl.make_config("prefill_b16")
+    note("append prefill_b16 chunk")
+    gk, gv = _run(sk, case.U, case.W, case.k_new, case.v_new, case.slot_mapping,
+                  case.cache.k_cache, case.cache.v_cache)
+    assert not np.isnan(gk[case.slot_mapping // 16, :, case.slot_mapping % 16, :]).any()
+    sample = np.arange(0, case.slot_mapping.size, 97)
+    sl = case.slot_mapping[sample]
+    rk, rv = oracle.append(case.k_new[sample], case.v_new[sample], case.U, case.W, sl,
+                           case.cache.k_cache, case.cache.v_cache)
+    bk, ok = sl // 16, sl % 16
+    uk = _ulp_diff(gk[bk, :, ok, :], rk[bk, :, ok, :])
+    uv = _ulp_diff(gv[bk, :, ok], rv[bk, :, ok])
+    print(f"[parity] prefill_b16 append sample: k max ulp {uk.max()}, v max ulp {uv.max()}")
+    assert uk.max() <= 1 and uv.max() <= 1

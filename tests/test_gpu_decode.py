@@ -1,0 +1,108 @@
+"""GPU parity of decode attention (q projection, split-K latent attention,
+combine, up-projection) against the fp64 oracle, through the C ABI."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import assert_parity, decode_tensors, note, run_decode
+from rank_compressed_paged_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sk():
+    from rank_compressed_paged_amd import starkv
+    return starkv
+
+
+def _oracle(case, rows=None):
+    c = case.cache
+    return oracle.decode(case.q, c.k_cache, c.v_cache, case.U, case.W, c.block_tables,
+                         c.seq_lens, case.scale, batch_indices=rows)
+
+
+def test_tiny_config(sk):
+    case = wl.make_config("tiny")
+    note("decode tiny config")
+    out = run_decode(sk, case)
+    assert_parity(out, _oracle(case), "tiny")
+
+
+@pytest.mark.parametrize("lens", [[1, 17, 300], [16, 15, 33, 64, 2], [0, 1, 4097, 31]],
+                         ids=["short", "page_edges", "long_and_empty"])
+def test_main_shape_ragged(sk, lens):
+    case = wl.make_decode_case(wl.MAIN, seq_lens=lens, seed=21, extra_cols=3)
+    note(f"decode main shape lens={lens}")
+    out = run_decode(sk, case)
+    ref = _oracle(case)
+    assert_parity(out, ref, f"main {lens}")
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert torch.count_nonzero(out[b]).item() == 0
+
+
+def test_tiny_shape_ragged(sk):
+    case = wl.make_decode_case(wl.TINY, seq_lens=[3, 0, 16, 17, 250], seed=22)
+    note("decode tiny shape ragged")
+    assert_parity(run_decode(sk, case), _oracle(case), "tiny ragged")
+
+
+def test_block_table_permutation_is_bit_identical(sk):
+    """Same logical latents in shuffled and identity page orders."""
+    lens = [40, 513, 7]
+    a = wl.make_decode_case(wl.MAIN, seq_lens=lens, seed=23, shuffle=True)
+    b = wl.make_decode_case(wl.MAIN, seq_lens=lens, seed=23, shuffle=False)
+    assert not np.array_equal(a.cache.block_tables, b.cache.block_tables)
+    note("decode shuffled vs identity block table")
+    oa = run_decode(sk, a)
+    ob = run_decode(sk, b)
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+
+
+def test_repeatable(sk):
+    case = wl.make_decode_case(wl.MAIN, seq_lens=[100, 1000], seed=24)
+    t = decode_tensors(case)
+    note("decode repeatability")
+    o1 = run_decode(sk, case, t).clone()
+    o2 = run_decode(sk, case, t)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+@pytest.mark.parametrize("min_pages,target", [("1", "4096"), ("64", "16")])
+def test_split_plan_invariance(sk, min_pages, target, monkeypatch):
+    case = wl.make_decode_case(wl.MAIN, seq_lens=[1500, 700, 33], seed=25)
+    ref = _oracle(case)
+    monkeypatch.setenv("STARKV_DECODE_MIN_PAGES", min_pages)
+    monkeypatch.setenv("STARKV_DECODE_TARGET_WGS", target)
+    note(f"decode split plan min_pages={min_pages} target={target}")
+    out = run_decode(sk, case)
+    assert_parity(out, ref, f"plan {min_pages}/{target}")
+
+
+def test_max_seq_len_bound_larger_than_lengths(sk):
+    """The host bound only plans the split; a loose bound gives the same result."""
+    case = wl.make_decode_case(wl.MAIN, seq_lens=[90, 31], seed=26, extra_cols=40)
+    note("decode loose max_seq_len")
+    o1 = run_decode(sk, case)
+    o2 = run_decode(sk, case, max_seq_len=(case.cache.block_tables.shape[1]) * 16)
+    ref = _oracle(case)
+    assert_parity(o1, ref, "tight bound")
+    assert_parity(o2, ref, "loose bound")
+
+
+@pytest.mark.parametrize("name,rows", [("decode_b16", None), ("decode_b64", [0, 17, 63]),
+                                       ("long_b20", [0, 19])])
+def test_full_size_config_sampled(sk, name, rows):
+    """Full-size workload in the benchmark's launch configuration; the oracle
+    checks all sequences (b16) or a fixed sample of them."""
+    case = wl.make_config(name)
+    note(f"decode full config {name} rows={rows}")
+    out = run_decode(sk, case)
+    ref = _oracle(case, rows)
+    sel = list(range(case.B)) if rows is None else rows
+    assert torch.isfinite(out.float()).all()
+    assert_parity(out[sel], ref[sel], f"{name} rows={rows}")
