@@ -97,7 +97,9 @@ class PagedCache:
 def build_block_tables(rng, blocks_per_seq: Sequence[int], spare_blocks=1,
                        shuffle=True, extra_cols=0):
     nb = int(sum(blocks_per_seq)) + int(spare_blocks)
-    perm = rng.permutation(nb) if shuffle else np.arange(nb)
+    perm = rng.permutation(nb)          # drawn either way: the later draws stay the same
+    if not shuffle:
+        perm = np.arange(nb)
     max_blocks = max([int(x) for x in blocks_per_seq] + [1]) + int(extra_cols)
     bt = np.full((len(blocks_per_seq), max_blocks), -1, dtype=np.int32)
     i = 0

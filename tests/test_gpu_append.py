@@ -47,16 +47,33 @@ def _run(sk, U, W, k, v, slots, kc, vc):
     return tk.cpu().numpy(), tv.cpu().numpy()
 
 
+# The GPU accumulates the projections in fp32 on the matrix cores, so a value
+# may round to the other fp16 neighbour of the exact result (1 ulp), and
+# values near zero carry the fp32 summation error in absolute terms: about
+# sqrt(K) * 2^-24 per unit of partial-sum size for K products, K = d = 128
+# for keys and K = H*d = 4096 for values; 8x that is the allowance below.
+ATOL_K = 8 * np.sqrt(128) * 2.0**-24
+ATOL_V = 8 * np.sqrt(4096) * 2.0**-24
+
+
+def _within(g, r, atol):
+    u = _ulp_diff(g, r)
+    a = np.abs(g.astype(np.float64) - r.astype(np.float64))
+    return (u <= 1) | (a <= atol), u, a
+
+
 def _check(gk, gv, rk, rv, what):
     # identical NaN pattern: exactly the listed slots were written
     assert np.array_equal(np.isnan(gk), np.isnan(rk)), f"{what}: k slot set differs"
     assert np.array_equal(np.isnan(gv), np.isnan(rv)), f"{what}: v slot set differs"
     m = ~np.isnan(rk)
-    uk = _ulp_diff(gk[m], rk[m])
+    okk, uk, ak = _within(gk[m], rk[m], ATOL_K)
     mv = ~np.isnan(rv)
-    uv = _ulp_diff(gv[mv], rv[mv])
-    print(f"[parity] {what}: k max ulp {uk.max(initial=0)}, v max ulp {uv.max(initial=0)}", flush=True)
-    assert uk.max(initial=0) <= 1 and uv.max(initial=0) <= 1
+    okv, uv, av = _within(gv[mv], rv[mv], ATOL_V)
+    print(f"[parity] {what}: k max ulp {uk.max(initial=0)} max abs {ak.max(initial=0):.2e}; "
+          f"v max ulp {uv.max(initial=0)} max abs {av.max(initial=0):.2e}; "
+          f"v >1ulp {(uv > 1).sum()} of {uv.size}", flush=True)
+    assert okk.all() and okv.all()
 
 
 @pytest.mark.parametrize("shape,n,seed,neg", [(wl.MAIN, 16, 31, 0), (wl.MAIN, 300, 32, 7),
@@ -101,7 +118,7 @@ def test_prefill_chunk_append_full_size(sk):
     rk, rv = oracle.append(case.k_new[sample], case.v_new[sample], case.U, case.W, sl,
                            case.cache.k_cache, case.cache.v_cache)
     bk, ok = sl // 16, sl % 16
-    uk = _ulp_diff(gk[bk, :, ok, :], rk[bk, :, ok, :])
-    uv = _ulp_diff(gv[bk, :, ok], rv[bk, :, ok])
+    okk, uk, _ = _within(gk[bk, :, ok, :], rk[bk, :, ok, :], ATOL_K)
+    okv, uv, _ = _within(gv[bk, :, ok], rv[bk, :, ok], ATOL_V)
     print(f"[parity] prefill_b16 append sample: k max ulp {uk.max()}, v max ulp {uv.max()}")
-    assert uk.max() <= 1 and uv.max() <= 1
+    assert okk.all() and okv.all()

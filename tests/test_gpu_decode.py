@@ -54,12 +54,15 @@ def test_tiny_shape_ragged(sk):
 def test_block_table_permutation_is_bit_identical(sk):
     """Same logical latents in shuffled and identity page orders."""
     lens = [40, 513, 7]
-    a = wl.make_decode_case(wl.MAIN, seq_lens=lens, seed=23, shuffle=True)
-    b = wl.make_decode_case(wl.MAIN, seq_lens=lens, seed=23, shuffle=False)
+    a = wl.make_decode_case(wl.MAIN, seq_lens=lens, seed=23, shuffle=True, keep_logical=True)
+    b = wl.make_decode_case(wl.MAIN, seq_lens=lens, seed=23, shuffle=False, keep_logical=True)
     assert not np.array_equal(a.cache.block_tables, b.cache.block_tables)
     note("decode shuffled vs identity block table")
+    for x, y in zip(a.cache.logical_ck or [], b.cache.logical_ck or []):
+        assert np.array_equal(x, y)
     oa = run_decode(sk, a)
     ob = run_decode(sk, b)
+    assert_parity(oa, _oracle(a), "shuffled pages")
     assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
 
 
