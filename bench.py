@@ -80,6 +80,8 @@ def parse_args(argv=None):
                     choices=["decode_b16", "decode_b64", "long_b20", "tiny"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU sample budget")
+    ap.add_argument("--flush", choices=["read", "write"], default="read",
+                    help="evict the Infinity Cache by reading (default) or writing 512 MiB")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"))
     return ap.parse_args(argv)
@@ -140,8 +142,17 @@ def run_bench(args):
     dims = sk.dims_of(t["k_cache"], t["v_cache"], t["U"], t["W"])
     ws = sk.alloc_workspace(sk.decode_workspace_size(dims, B, msl), "cuda")
     out = torch.empty((B, sh.H, sh.d), dtype=torch.float16, device="cuda")
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    flush_sink = torch.empty((), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+
+    def do_flush(i):
+        # a read-only sweep leaves clean lines behind; a write sweep leaves
+        # dirty ones whose write-back competes with the next step's reads
+        if args.flush == "read":
+            torch.sum(flush, dim=0, out=flush_sink)
+        else:
+            flush.fill_(float(i & 0xFF))
     lat_bytes = metrics.decode_latent_bytes(case.cache.seq_lens, sh.H, sh.r_k, sh.r_v)
     pps, ns = sk.decode_plan(dims, B, msl)
 
@@ -163,7 +174,7 @@ def run_bench(args):
     def append_step():
         sk.append(k_new, v_new, t["U"], t["W"], slots, kc_app, vc_app)
 
-    def timed(fn, n, do_flush, kernel_sel=sk.TIME_NONE):
+    def timed(fn, n, flushed, kernel_sel=sk.TIME_NONE):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(n)]
         kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -174,8 +185,8 @@ def run_bench(args):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(n):
-            if do_flush:
-                flush.fill_(i & 0xFF)
+            if flushed:
+                do_flush(i)
             if kernel_sel:
                 sk.set_timing_events(kev[i][0], kev[i][1], kernel_sel)
             ev[i][0].record(stream)
@@ -189,14 +200,28 @@ def run_bench(args):
         return steps_ms, kern_ms, wall
 
     # warmup (untimed)
-    for _ in range(args.warmup):
-        flush.fill_(0)
+    for i in range(args.warmup):
+        do_flush(i)
         step()
     torch.cuda.synchronize()
 
-    step_ms, kern_ms, wall = timed(step, args.steps, True, sk.TIME_DECODE_SPLIT)
-    warm_ms, warm_kern_ms, _ = timed(step, args.steps, False, sk.TIME_DECODE_SPLIT)
-    app_ms, app_kern_ms, _ = timed(append_step, max(args.steps, 10), True, sk.TIME_APPEND)
+    # headline: whole steps, cache flushed before each, no events inside the step
+    step_ms, _, wall = timed(step, args.steps, True)
+    # the split-K kernel alone (events recorded around its launch), flushed
+    _, kern_ms, _ = timed(step, args.steps, True, sk.TIME_DECODE_SPLIT)
+    # warm (latents left in the Infinity Cache), for reference only
+    warm_ms, _, _ = timed(step, args.steps, False)
+    _, warm_kern_ms, _ = timed(step, args.steps, False, sk.TIME_DECODE_SPLIT)
+    app_ms, _, _ = timed(append_step, max(args.steps, 10), True)
+    _, app_kern_ms, _ = timed(append_step, max(args.steps, 10), True, sk.TIME_APPEND)
+
+    # measured streaming-read ceiling on this machine: a plain reduction reading
+    # as many bytes as one step's latents, after the same flush
+    ceil_buf = torch.ones(lat_bytes // 4, dtype=torch.float32, device="cuda")
+    ceil_sink = torch.empty((), dtype=torch.float32, device="cuda")
+    ceil_ms, _, _ = timed(lambda: torch.sum(ceil_buf, dim=0, out=ceil_sink), max(args.steps, 10), True)
+    ceiling_gbs = lat_bytes / (statistics.fmean(ceil_ms) * 1e-3) / 1e9
+    del ceil_buf
 
     ms = statistics.fmean(step_ms)
     kern = statistics.fmean(kern_ms)
@@ -231,6 +256,8 @@ def run_bench(args):
         "append_kernel_ms": round(statistics.fmean(app_kern_ms), 5),
         "wall_s_timed_loop_incl_flush": round(wall, 4),
         "split_plan": {"pages_per_split": pps, "num_splits": ns},
+        "flush": args.flush,
+        "stream_read_ceiling_gbs": round(ceiling_gbs, 1),
         "roofline": {
             "kernel": DECODE_KERNEL,
             "bound": "hbm",

@@ -33,8 +33,8 @@ DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int bs) {
   (void)s;
   const int pages = cdiv(max_seq_len, bs);
   if (pages <= 0 || batch <= 0) return DecodePlan{1, 1};
-  const int target = env_int("STARKV_DECODE_TARGET_WGS", 512);
-  const int min_pps = env_int("STARKV_DECODE_MIN_PAGES", 4);
+  const int target = env_int("STARKV_DECODE_TARGET_WGS", 256);
+  const int min_pps = env_int("STARKV_DECODE_MIN_PAGES", 8);
   const int want_splits = cdiv(target, batch);
   int pps = cdiv(pages, want_splits);
   if (pps < min_pps) pps = min_pps;

@@ -10,7 +10,8 @@
 // A 256-thread work group computes a 64 (tokens) x 64 (outputs) tile with
 // v_mfma_f32_16x16x32_f16; A operands come straight from memory (8
 // contiguous fp16 per lane), B is staged through LDS transposed so that each
-// lane again reads 8 contiguous values.  The epilogue rounds to fp16
+// lane again reads 8 contiguous values.  The next K step's loads are issued
+// before the current step's LDS barrier (which waits on LDS only).  The epilogue rounds to fp16
 // (nearest even) and writes slot_mapping[n]; negative or out-of-range slots
 // are skipped.  Layouts: k_cache [NB, H, 16, r_k], v_cache [NB, r_v, 16].
 #include "common.h"
@@ -33,7 +34,7 @@ struct AppendArgs {
 constexpr int AT_M = 64, AT_N = 64, AT_K = 32, AT_LDS = AT_K + 8;
 
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-  __shared__ __attribute__((aligned(16))) half_t sB[AT_N][AT_LDS];
+  __shared__ __attribute__((aligned(16))) half_t sB[2][AT_N][AT_LDS];
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -85,23 +86,37 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     arow[mt] = arow_ok[mt] ? m : 0;
   }
 
+  auto load_b = [&](int k0) {
+    return b_ok ? *(const half8*)(Bm + (size_t)(k0 + kk) * ldb + n_base + n0) : hz;
+  };
+  auto load_a = [&](int k0, int mt) {
+    return arow_ok[mt] ? *(const half8*)(A + (size_t)arow[mt] * lda + k0 + quad * 8) : hz;
+  };
+  // software pipeline: the next K step's global loads are in flight while
+  // the current step goes through LDS and the matrix cores; LDS is
+  // double-buffered so one LDS-only barrier per step suffices
+  half8 bv = load_b(0);
+  half8 av0 = load_a(0, 0), av1 = load_a(0, 1);
+  int buf = 0;
   for (int k0 = 0; k0 < Kdim; k0 += AT_K) {
-    const half8 bv = b_ok ? *(const half8*)(Bm + (size_t)(k0 + kk) * ldb + n_base + n0) : hz;
-    half8 av[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      av[mt] = arow_ok[mt] ? *(const half8*)(A + (size_t)arow[mt] * lda + k0 + quad * 8) : hz;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sB[n0 + e][kk] = bv[e];
-    __syncthreads();
+    for (int e = 0; e < 8; ++e) sB[buf][n0 + e][kk] = bv[e];
+    const half8 a0 = av0, a1 = av1;
+    if (k0 + AT_K < Kdim) {
+      bv = load_b(k0 + AT_K);
+      av0 = load_a(k0 + AT_K, 0);
+      av1 = load_a(k0 + AT_K, 1);
+    }
+    block_sync_lds();
     half8 bq[2];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) bq[nt] = *(const half8*)&sB[wn * 32 + nt * 16 + col][quad * 8];
+    for (int nt = 0; nt < 2; ++nt) bq[nt] = *(const half8*)&sB[buf][wn * 32 + nt * 16 + col][quad * 8];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16x16x32(av[mt], bq[nt], acc[mt][nt]);
+    for (int nt = 0; nt < 2; ++nt) {
+      acc[0][nt] = mfma16x16x32(a0, bq[nt], acc[0][nt]);
+      acc[1][nt] = mfma16x16x32(a1, bq[nt], acc[1][nt]);
+    }
+    buf ^= 1;
   }
 
   // ---- epilogue: D[token][output], lane holds rows 4*quad + r, column col

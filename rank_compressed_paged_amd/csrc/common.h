@@ -67,9 +67,18 @@ __device__ __forceinline__ void split_f16x4(float4v a, half4& hi, half4& lo) {
   }
 }
 
-template <typename T>
-__device__ __forceinline__ T ld_nt(const T* p) {
-  return __builtin_nontemporal_load(p);
+// Work-group barrier that orders LDS only: waits for this wave's LDS (and
+// scalar) operations, then s_barrier.  Unlike __syncthreads() it does not
+// wait for outstanding global loads, so register prefetches issued before
+// it stay in flight across the barrier.  Use only where the barrier guards
+// LDS data.
+__device__ __forceinline__ void block_sync_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Wait for this wave's own LDS operations (no barrier): enough when a wave
+// reads back what it wrote itself.
+__device__ __forceinline__ void wave_sync_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 }  // namespace starkv

@@ -9,7 +9,8 @@
 // README's "Per-decode-step attention" notes), W_h being rows h*d..h*d+d-1.
 //
 // One decode step is four launches on the caller's stream:
-//   1. qproj        q~ = U_h^T q, pre-scaled by scale*log2(e), fp16
+//   1. qproj        q~ = U_h^T q, pre-scaled by scale*log2(e), fp16, on the
+//                   matrix cores (U_h staged transposed in LDS)
 //   2. decode_split split-K pass over the pages (README, "Kernel profiling
 //                   breakdown": split-K attention plus a combine); one work
 //                   group owns all heads of a run of pages so the joint value
@@ -19,22 +20,26 @@
 //                   fp16 hi/lo pair so the product keeps fp32 accuracy
 //
 // decode_split per page (16 tokens) in a work group of NW waves:
-//   * scores: wave w owns heads [w*HPW, (w+1)*HPW).  For each head the 16x64
+//   * scores: wave w owns heads [w*HPW, (w+1)*HPW).  For each head the 16xr_k
 //     key page is the A operand of v_mfma_f32_16x16x32_f16 and q~_h sits in
 //     column (h - w*HPW) of B, zeros elsewhere, so one 16x16 accumulator
 //     collects the scores of all the wave's heads (tokens x heads).  The
 //     lane that holds column c then runs the online-softmax update of that
 //     head on its 4 tokens plus a 4-lane butterfly.
 //   * P (fp16) and the rescale factors go through LDS (double-buffered, one
-//     barrier per page).
+//     LDS-only barrier per page, so prefetched loads stay in flight).
 //   * values: wave w owns features [w*FPW, (w+1)*FPW).  Z^T[f, h] +=
 //     sum_t c_v[t, f] P[h, t] with v_mfma_f32_16x16x16_f16: the feature-major
 //     value page gives each lane 8 contiguous bytes, and the accumulator
-//     column is the head, so the rescale is one scalar per lane.
-//   * the next page's keys and values are loaded into registers before the
-//     current page is processed.
+//     column is the head, so the rescale is one scalar per lane; it is
+//     skipped for pages where no running max moved.
+//   * two register sets ping-pong: page p+1 is loaded while page p is used.
 #include "common.h"
 #include "kernels.h"
+
+#ifndef STARKV_DECODE_WAVES
+#define STARKV_DECODE_WAVES 8
+#endif
 
 namespace starkv {
 
@@ -55,51 +60,64 @@ struct DecodeCfg {
 constexpr int BS = 16;  // tokens per page
 
 // ---------------------------------------------------------------------------
-// 1. q~[n, h, :] = (scale*log2e) * U_h^T q[n, h, :]  (fp32 math, fp16 out)
-// grid (H, ceil(N / QT)), 256 threads
+// 1. q~[n, h, :] = (scale*log2e) * U_h^T q[n, h, :]  -> fp16
+// grid (H, ceil(N/64)), 4 waves; wave w owns tokens n0+16w .. n0+16w+15.
+// A = q (16 tokens x 32 of d, 16 contiguous bytes per lane), B = U_h staged in
+// LDS as [r][d] so each lane again reads 8 contiguous values.
 // ---------------------------------------------------------------------------
 template <int H, int D, int RK>
 __global__ __launch_bounds__(256) void qproj_kernel(const half_t* __restrict__ q,
                                                     const half_t* __restrict__ U, int n_tokens,
                                                     float qscale, half_t* __restrict__ qt) {
-  constexpr int QT = 16;
-  __shared__ float sU[D][RK + 1];
-  __shared__ float sQ[QT][D];
+  constexpr int LDU = D + 8;
+  __shared__ __attribute__((aligned(16))) half_t sUt[RK][LDU];
   const int h = blockIdx.x;
-  const int n0 = blockIdx.y * QT;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, quad = lane >> 4;
   const half_t* Uh = U + (size_t)h * D * RK;
-  for (int i = tid; i < D * RK; i += 256) sU[i / RK][i % RK] = (float)Uh[i];
-  for (int i = tid; i < QT * D; i += 256) {
-    const int n = n0 + i / D;
-    sQ[i / D][i % D] = (n < n_tokens) ? (float)q[((size_t)n * H + h) * D + (i % D)] : 0.f;
+  constexpr int CHUNKS = D * RK / 8;
+  for (int c = tid; c < CHUNKS; c += 256) {
+    const int i = c / (RK / 8), r0 = (c % (RK / 8)) * 8;
+    const half8 u = *(const half8*)(Uh + (size_t)i * RK + r0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sUt[r0 + e][i] = u[e];
   }
   __syncthreads();
-  constexpr int STEP = 256 / RK;
-  const int r = tid % RK;
-  for (int qi = tid / RK; qi < QT; qi += STEP) {
-    const int n = n0 + qi;
-    if (n >= n_tokens) break;
-    float accv = 0.f;
-#pragma unroll 8
-    for (int i = 0; i < D; ++i) accv = fmaf(sU[i][r], sQ[qi][i], accv);
-    qt[((size_t)n * H + h) * RK + r] = (half_t)(accv * qscale);
+  const int nb = blockIdx.y * 64 + w * 16;
+  if (nb >= n_tokens) return;  // wave-uniform; no barrier follows
+  const int n = nb + col;
+  const bool nv = n < n_tokens;
+  const half_t* qrow = q + ((size_t)(nv ? n : nb) * H + h) * D + quad * 8;
+  half8 a[D / 32];
+#pragma unroll
+  for (int k = 0; k < D / 32; ++k) a[k] = nv ? *(const half8*)(qrow + k * 32) : half8{};
+#pragma unroll
+  for (int rt = 0; rt < RK / 16; ++rt) {
+    float4v acc = zero4();
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) {
+      const half8 bq = *(const half8*)&sUt[rt * 16 + col][k * 32 + quad * 8];
+      acc = mfma16x16x32(a[k], bq, acc);
+    }
+    // D[token 4*quad + r][output col]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int nt = nb + quad * 4 + r;
+      if (nt < n_tokens) qt[((size_t)nt * H + h) * RK + rt * 16 + col] = (half_t)(acc[r] * qscale);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // 2. split-K latent attention
 // ---------------------------------------------------------------------------
-struct SplitArgs {
-  const half_t* qt;
-  const half_t* k_cache;
-  const half_t* v_cache;
-  const int32_t* block_tables;
-  const int32_t* seq_lens;
-  float* ml;   // [B][S][2][R16]
-  float* acc;  // [B][S][NW][RT][FT][64][4]
-  int max_blocks, num_blocks, pages_per_split, num_splits;
-};
+// Arguments are separate __restrict__ pointers (not a struct) so the
+// compiler can prove the block table is never written in the kernel and
+// reads it with scalar loads: a vector load of a block id would need a
+// vmcnt wait that also drains the page prefetch.
+//   ml  [B][S][2][R16]: running max (log2 domain) then sum
+//   acc [B][S][R16][RV]: unnormalised z rows
 
 template <int H, int RK, int RV, int NW>
 struct PageRegs {
@@ -129,7 +147,100 @@ __device__ __forceinline__ void load_page(PageRegs<H, RK, RV, NW>& pr, const hal
 }
 
 template <int H, int RK, int RV, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_split_kernel(SplitArgs a) {
+struct SplitState {
+  using C = DecodeCfg<H, RK, RV, NW>;
+  float m_run, l_run;
+  float4v acc[C::RT][C::FT];
+};
+
+// One page: scores, online softmax, P through LDS, P.c_v.  Branch-free in
+// `valid` (tokens of the page that belong to the sequence; 0 for a page past
+// the split or with an invalid block id): masked tokens get score -inf,
+// weight 0 and a zeroed value operand, so a fully masked page changes
+// nothing.  Keeping every page on the same path lets the compiler count the
+// prefetched loads exactly instead of draining them.
+template <int H, int RK, int RV, int NW>
+__device__ __forceinline__ void process_page(
+    SplitState<H, RK, RV, NW>& st, PageRegs<H, RK, RV, NW>& cur,
+    const typename PageRegs<H, RK, RV, NW>::kvec (&qv)[DecodeCfg<H, RK, RV, NW>::NKC],
+    half_t (*sP)[DecodeCfg<H, RK, RV, NW>::R16][BS], float (*sAlpha)[DecodeCfg<H, RK, RV, NW>::R16],
+    int* sFlag, int p, int buf, int valid, int w, int col, int quad) {
+  using C = DecodeCfg<H, RK, RV, NW>;
+  using kvec = typename PageRegs<H, RK, RV, NW>::kvec;
+  const kvec kzero = {};
+  float4v sacc = zero4();
+#pragma unroll
+  for (int hl = 0; hl < C::HPW; ++hl) {
+#pragma unroll
+    for (int c = 0; c < C::NKC; ++c) {
+      const kvec bq = (col == hl) ? qv[c] : kzero;
+      if constexpr (C::KC == 32)
+        sacc = mfma16x16x32(cur.k[hl][c], bq, sacc);
+      else
+        sacc = mfma16x16x16(cur.k[hl][c], bq, sacc);
+    }
+  }
+  float sv[4];
+  float pm = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    sv[r] = (quad * 4 + r < valid) ? sacc[r] : -INFINITY;
+    pm = fmaxf(pm, sv[r]);
+  }
+  pm = max_over_quads(pm);
+  const float m_new = fmaxf(st.m_run, pm);
+  const float alpha = (m_new == st.m_run) ? 1.f : exp2f(st.m_run - m_new);
+  float ps = 0.f;
+  half4 ph;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float pr = (sv[r] == -INFINITY) ? 0.f : exp2f(sv[r] - m_new);
+    ps += pr;
+    ph[r] = (half_t)pr;
+  }
+  ps = sum_over_quads(ps);
+  st.l_run = st.l_run * alpha + ps;
+  st.m_run = m_new;
+  if (col < C::HPW) {
+    const int row = w * C::HPW + col;
+    *(half4*)&sP[buf][row][quad * 4] = ph;
+    if (quad == 0) sAlpha[buf][row] = alpha;
+    if (alpha != 1.f) sFlag[buf] = p;
+  }
+  block_sync_lds();
+  const bool rescale = sFlag[buf] == p;  // uniform: skip when no max moved
+  half4 pb[C::RT];
+#pragma unroll
+  for (int rt = 0; rt < C::RT; ++rt) {
+    pb[rt] = *(const half4*)&sP[buf][rt * 16 + col][quad * 4];
+    if (rescale) {
+      const float al = sAlpha[buf][rt * 16 + col];
+#pragma unroll
+      for (int ft = 0; ft < C::FT; ++ft) st.acc[rt][ft] *= al;
+    }
+  }
+  // value slots past the sequence may hold anything (NaN): zero them
+  const int t0 = quad * 4;
+  const uint32_t m01 = (t0 < valid ? 0x0000FFFFu : 0u) | (t0 + 1 < valid ? 0xFFFF0000u : 0u);
+  const uint32_t m23 = (t0 + 2 < valid ? 0x0000FFFFu : 0u) | (t0 + 3 < valid ? 0xFFFF0000u : 0u);
+#pragma unroll
+  for (int ft = 0; ft < C::FT; ++ft) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 bits = __builtin_bit_cast(u32x2, cur.v[ft]);
+    bits[0] &= m01;
+    bits[1] &= m23;
+    const half4 av = __builtin_bit_cast(half4, bits);
+#pragma unroll
+    for (int rt = 0; rt < C::RT; ++rt) st.acc[rt][ft] = mfma16x16x16(av, pb[rt], st.acc[rt][ft]);
+  }
+}
+
+template <int H, int RK, int RV, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_split_kernel(
+    const half_t* __restrict__ qt, const half_t* __restrict__ k_cache,
+    const half_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ seq_lens, float* __restrict__ ml, float* __restrict__ acc,
+    int max_blocks, int num_blocks, int pages_per_split, int num_splits) {
   using C = DecodeCfg<H, RK, RV, NW>;
   using kvec = typename PageRegs<H, RK, RV, NW>::kvec;
   __shared__ __attribute__((aligned(16))) half_t sP[2][C::R16][BS];
@@ -137,11 +248,11 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(SplitArgs a) {
   __shared__ int sFlag[2];  // page index whose softmax step moved a running max
 
   const int s = blockIdx.x, b = blockIdx.y;
-  const int L = a.seq_lens[b];
-  const int n_pages = min(min((L + BS - 1) / BS, a.max_blocks), a.num_splits * a.pages_per_split);
-  const int p0 = s * a.pages_per_split;
+  const int L = seq_lens[b];
+  const int n_pages = min(min((L + BS - 1) / BS, max_blocks), num_splits * pages_per_split);
+  const int p0 = s * pages_per_split;
   if (p0 >= n_pages) return;
-  const int p1 = min(p0 + a.pages_per_split, n_pages);
+  const int p1 = min(p0 + pages_per_split, n_pages);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -156,175 +267,103 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(SplitArgs a) {
   kvec qv[C::NKC];
   {
     const int hq = w * C::HPW + (col < C::HPW ? col : 0);
-    const half_t* qp = a.qt + ((size_t)b * H + hq) * RK + quad * (C::KC / 4);
+    const half_t* qp = qt + ((size_t)b * H + hq) * RK + quad * (C::KC / 4);
 #pragma unroll
     for (int c = 0; c < C::NKC; ++c) qv[c] = *(const kvec*)(qp + c * C::KC);
   }
-  const kvec kzero = {};
 
-  float m_run = -INFINITY, l_run = 0.f;
-  float4v acc[C::RT][C::FT];
+  SplitState<H, RK, RV, NW> st;
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
 #pragma unroll
   for (int rt = 0; rt < C::RT; ++rt)
 #pragma unroll
-    for (int ft = 0; ft < C::FT; ++ft) acc[rt][ft] = zero4();
+    for (int ft = 0; ft < C::FT; ++ft) st.acc[rt][ft] = zero4();
 
-  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
-  auto safe_block = [&](int p) {
+  // page p of this split: its block id (clamped to a loadable one past the
+  // split or when invalid) and how many of its tokens count
+  const int32_t* bt = block_tables + (size_t)b * max_blocks;
+  auto page_block = [&](int p) {
+    const int blk = bt[min(p, p1 - 1)];
+    return ((unsigned)blk < (unsigned)num_blocks) ? blk : 0;
+  };
+  auto page_valid = [&](int p) {
+    if (p >= p1) return 0;
     const int blk = bt[p];
-    return ((unsigned)blk < (unsigned)a.num_blocks) ? blk : -1;
+    return ((unsigned)blk < (unsigned)num_blocks) ? min(BS, L - p * BS) : 0;
   };
 
-  PageRegs<H, RK, RV, NW> cur, nxt;
-  int blk_cur = safe_block(p0);
-  if (blk_cur >= 0) load_page<H, RK, RV, NW>(cur, a.k_cache, a.v_cache, blk_cur, w, col, quad);
-  __syncthreads();  // LDS init visible
+  PageRegs<H, RK, RV, NW> ra, rb;
+  load_page<H, RK, RV, NW>(ra, k_cache, v_cache, page_block(p0), w, col, quad);
+  __syncthreads();  // LDS initialisation visible
 
-  for (int p = p0; p < p1; ++p) {
-    const int buf = (p - p0) & 1;
-    int blk_nxt = -1;
-    if (p + 1 < p1) {
-      blk_nxt = safe_block(p + 1);
-      if (blk_nxt >= 0) load_page<H, RK, RV, NW>(nxt, a.k_cache, a.v_cache, blk_nxt, w, col, quad);
-    }
-    const int valid = (blk_cur >= 0) ? min(BS, L - p * BS) : 0;  // uniform in the group
-
-    if (valid > 0) {
-      // ---- scores: tokens (rows) x wave heads (columns)
-      float4v sacc = zero4();
-#pragma unroll
-      for (int hl = 0; hl < C::HPW; ++hl) {
-#pragma unroll
-        for (int c = 0; c < C::NKC; ++c) {
-          const kvec bq = (col == hl) ? qv[c] : kzero;
-          if constexpr (C::KC == 32)
-            sacc = mfma16x16x32(cur.k[hl][c], bq, sacc);
-          else
-            sacc = mfma16x16x16(cur.k[hl][c], bq, sacc);
-        }
-      }
-      // ---- online softmax of head (w*HPW + col) over this page
-      float sv[4];
-      float pm = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sv[r] = (quad * 4 + r < valid) ? sacc[r] : -INFINITY;
-        pm = fmaxf(pm, sv[r]);
-      }
-      pm = max_over_quads(pm);
-      const float m_new = fmaxf(m_run, pm);
-      const float alpha = exp2f(m_run - m_new);
-      float ps = 0.f;
-      half4 ph;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pr = exp2f(sv[r] - m_new);
-        ps += pr;
-        ph[r] = (half_t)pr;
-      }
-      ps = sum_over_quads(ps);
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-      if (col < C::HPW) {
-        const int row = w * C::HPW + col;
-        *(half4*)&sP[buf][row][quad * 4] = ph;
-        if (quad == 0) sAlpha[buf][row] = alpha;
-        if (alpha != 1.f) sFlag[buf] = p;
-      }
-    }
-    __syncthreads();
-    if (valid > 0) {
-      const bool rescale = sFlag[buf] == p;  // uniform: skip when no max moved
-      // ---- values: Z^T[f, h] = alpha_h Z^T[f, h] + sum_t c_v[t, f] P[h, t]
-      half4 pb[C::RT];
-#pragma unroll
-      for (int rt = 0; rt < C::RT; ++rt) {
-        pb[rt] = *(const half4*)&sP[buf][rt * 16 + col][quad * 4];
-        if (rescale) {
-          const float al = sAlpha[buf][rt * 16 + col];
-#pragma unroll
-          for (int ft = 0; ft < C::FT; ++ft) acc[rt][ft] *= al;
-        }
-      }
-#pragma unroll
-      for (int ft = 0; ft < C::FT; ++ft) {
-        half4 av = cur.v[ft];
-        if (valid < BS) {  // tail page: unused slots may hold anything (NaN)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (quad * 4 + e >= valid) av[e] = (half_t)0.f;
-        }
-#pragma unroll
-        for (int rt = 0; rt < C::RT; ++rt) acc[rt][ft] = mfma16x16x16(av, pb[rt], acc[rt][ft]);
-      }
-    }
-    if (p + 1 < p1) {
-      cur = nxt;
-      blk_cur = blk_nxt;
-    }
+  // sched_barrier(0) keeps the scheduler from hoisting the current page's
+  // matrix ops (and the waits they need) above the next page's load issue
+  for (int p = p0; p < p1; p += 2) {
+    load_page<H, RK, RV, NW>(rb, k_cache, v_cache, page_block(p + 1), w, col, quad);
+    __builtin_amdgcn_sched_barrier(0);
+    process_page<H, RK, RV, NW>(st, ra, qv, sP, sAlpha, sFlag, p, 0, page_valid(p), w, col, quad);
+    load_page<H, RK, RV, NW>(ra, k_cache, v_cache, page_block(p + 2), w, col, quad);
+    __builtin_amdgcn_sched_barrier(0);
+    process_page<H, RK, RV, NW>(st, rb, qv, sP, sAlpha, sFlag, p + 1, 1, page_valid(p + 1), w, col,
+                                quad);
   }
 
-  // ---- partial state of this split
-  const size_t ws = (size_t)b * a.num_splits + s;
+  // ---- partial state of this split: rows are heads, contiguous features
+  const size_t ws = (size_t)b * num_splits + s;
   if (col < C::HPW && quad == 0) {
-    a.ml[ws * 2 * C::R16 + w * C::HPW + col] = m_run;
-    a.ml[ws * 2 * C::R16 + C::R16 + w * C::HPW + col] = l_run;
+    ml[ws * 2 * C::R16 + w * C::HPW + col] = st.m_run;
+    ml[ws * 2 * C::R16 + C::R16 + w * C::HPW + col] = st.l_run;
   }
-  float4v* pa = (float4v*)(a.acc + (ws * NW + w) * (size_t)(C::RT * C::FT * 256));
+  float* pa = acc + ws * C::R16 * RV + w * C::FPW + quad * 4;
 #pragma unroll
   for (int rt = 0; rt < C::RT; ++rt)
 #pragma unroll
-    for (int ft = 0; ft < C::FT; ++ft) pa[(rt * C::FT + ft) * 64 + lane] = acc[rt][ft];
+    for (int ft = 0; ft < C::FT; ++ft)
+      *(float4v*)(pa + (size_t)(rt * 16 + col) * RV + ft * 16) = st.acc[rt][ft];
 }
 
 // ---------------------------------------------------------------------------
 // 3. combine: z[b,h,:] = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
-// grid (H, B), 256 threads
+// One thread per (sequence, head, 4 features); a single online pass over the
+// splits keeps (M, num, den) so every split's loads are independent of the
+// running state and many can be in flight.  grid ceil(B*H*RV/4 / 256).
 // ---------------------------------------------------------------------------
-template <int H, int RK, int RV, int NW>
+template <int H, int RV>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ml,
                                                       const float* __restrict__ acc,
                                                       const int32_t* __restrict__ seq_lens,
-                                                      int max_blocks, int pages_per_split,
-                                                      int num_splits, float* __restrict__ z) {
-  using C = DecodeCfg<H, RK, RV, NW>;
-  __shared__ float sW[256];
-  __shared__ float sInv;
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
+                                                      int batch, int max_blocks,
+                                                      int pages_per_split, int num_splits,
+                                                      float* __restrict__ z) {
+  constexpr int R16 = ((H + 15) / 16) * 16;
+  constexpr int F4 = RV / 4;
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  if (gid >= batch * H * F4) return;  // no barrier in this kernel
+  const int f4 = gid % F4;
+  const int h = (gid / F4) % H;
+  const int b = gid / (F4 * H);
   const int n_pages =
       min(min((seq_lens[b] + BS - 1) / BS, max_blocks), num_splits * pages_per_split);
   const int ns = (n_pages + pages_per_split - 1) / pages_per_split;
-  float* zo = z + ((size_t)b * H + h) * RV;
-  if (ns == 0) {
-    for (int f = tid; f < RV; f += 256) zo[f] = 0.f;
-    return;
+  const float* mlb = ml + (size_t)b * num_splits * 2 * R16 + h;
+  const float4v* ab = (const float4v*)(acc + ((size_t)b * num_splits * R16 + h) * RV) + f4;
+  float M = -INFINITY, den = 0.f;
+  float4v num = zero4();
+#pragma unroll 8
+  for (int s = 0; s < ns; ++s) {
+    const float ms = mlb[(size_t)s * 2 * R16];
+    const float ls = mlb[(size_t)s * 2 * R16 + R16];
+    const float4v as = ab[(size_t)s * R16 * F4];
+    const float Mn = fmaxf(M, ms);
+    const float sc = (Mn == M) ? 1.f : exp2f(M - Mn);
+    const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - Mn);
+    num = num * sc + as * wgt;
+    den = den * sc + ls * wgt;
+    M = Mn;
   }
-  // split weights (ns <= 256 is enforced by the planner)
-  const float* mlb = ml + (size_t)b * num_splits * 2 * C::R16;
-  float m = -INFINITY;
-  for (int s = 0; s < ns; ++s) m = fmaxf(m, mlb[(size_t)s * 2 * C::R16 + h]);
-  if (tid < ns) {
-    const float ms = mlb[(size_t)tid * 2 * C::R16 + h];
-    sW[tid] = (ms == -INFINITY) ? 0.f : exp2f(ms - m);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float den = 0.f;
-    for (int s = 0; s < ns; ++s) den += sW[s] * mlb[(size_t)s * 2 * C::R16 + C::R16 + h];
-    sInv = (den > 0.f) ? 1.f / den : 0.f;
-  }
-  __syncthreads();
-  const float inv = sInv;
-  const int rt = h / 16, c = h % 16;
-  for (int f = tid; f < RV; f += 256) {
-    const int w = f / C::FPW, ft = (f % C::FPW) / 16, fi = f % 16;
-    const size_t off = ((size_t)((w * C::RT + rt) * C::FT + ft) * 64 + c + 16 * (fi / 4)) * 4 + (fi % 4);
-    float num = 0.f;
-    const float* ab = acc + (size_t)b * num_splits * NW * (C::RT * C::FT * 256);
-    for (int s = 0; s < ns; ++s) num += sW[s] * ab[(size_t)s * NW * (C::RT * C::FT * 256) + off];
-    zo[f] = num * inv;
-  }
+  float4v* zo = (float4v*)(z + ((size_t)b * H + h) * RV) + f4;
+  *zo = (den > 0.f) ? num * (1.f / den) : zero4();
 }
 
 // ---------------------------------------------------------------------------
@@ -342,15 +381,16 @@ __global__ __launch_bounds__(256) void upproj_kernel(const half_t* __restrict__ 
   const int h = blockIdx.x, i0 = blockIdx.y * DR;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, quad = lane >> 4;
-  const int n = blockIdx.z * 64 + w * 16 + col;
-  if (blockIdx.z * 64 + w * 16 >= n_tokens) return;  // wave-uniform
+  const int nb = blockIdx.z * 64 + w * 16;
+  if (nb >= n_tokens) return;  // wave-uniform
+  const int n = nb + col;
   const bool nv = n < n_tokens;
-  const float* zr = z + ((size_t)(nv ? n : 0) * H + h) * RV + quad * 8;
+  const float* zr = z + ((size_t)(nv ? n : nb) * H + h) * RV + quad * 8;
   const half_t* wrow = W + ((size_t)h * D + i0 + col) * RV + quad * 8;
   float4v accv[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) accv[it] = zero4();
-#pragma unroll 2
+#pragma unroll
   for (int j0 = 0; j0 < RV; j0 += 32) {
     half8 hi, lo;
     const float4v z0 = nv ? *(const float4v*)(zr + j0) : zero4();
@@ -374,6 +414,67 @@ __global__ __launch_bounds__(256) void upproj_kernel(const half_t* __restrict__ 
   }
 }
 
+// Decode variant: grid (H, D/16); the 4 waves split the r_v contraction
+// (RV/4 features each) for every 16-token tile of the batch, and the four
+// partial tiles are summed through LDS.  More loads in flight per work group
+// than one wave walking all of r_v.
+template <int H, int D, int RV>
+__global__ __launch_bounds__(256) void upproj_small_kernel(const half_t* __restrict__ W,
+                                                           const float* __restrict__ z,
+                                                           int n_tokens,
+                                                           half_t* __restrict__ out) {
+  constexpr int KW = RV / 4;     // features per wave
+  constexpr int KS = KW / 32;    // 32-wide steps per wave
+  constexpr int TT = 4;          // token tiles per pass (64 tokens)
+  __shared__ float sRed[4][TT][16][17];
+  const int h = blockIdx.x, i0 = blockIdx.y * 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 15, quad = lane >> 4;
+  const half_t* wrow = W + ((size_t)h * D + i0 + col) * RV + w * KW + quad * 8;
+  half8 av[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) av[k] = *(const half8*)(wrow + k * 32);
+  for (int n0 = 0; n0 < n_tokens; n0 += 16 * TT) {
+    float4v acc[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      acc[t] = zero4();
+      const int n = n0 + t * 16 + col;
+      const bool nv = n < n_tokens;
+      const float* zr = z + ((size_t)(nv ? n : 0) * H + h) * RV + w * KW + quad * 8;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const float4v z0 = nv ? *(const float4v*)(zr + k * 32) : zero4();
+        const float4v z1 = nv ? *(const float4v*)(zr + k * 32 + 4) : zero4();
+        half8 hi, lo;
+        split_f16x8(z0, z1, hi, lo);
+        acc[t] = mfma16x16x32(av[k], hi, acc[t]);
+        acc[t] = mfma16x16x32(av[k], lo, acc[t]);
+      }
+    }
+    // D[row 4*quad + r][token col] of each tile -> LDS, then sum the waves
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sRed[w][t][quad * 4 + r][col] = acc[t][r];
+    __syncthreads();
+    {
+      const int t = threadIdx.x >> 6, e = threadIdx.x & 63;  // tile t, 4 outputs per thread
+      const int tok = e >> 2, r0 = (e & 3) * 4;
+      const int n = n0 + t * 16 + tok;
+      if (n < n_tokens) {
+        half4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          o[r] = (half_t)(sRed[0][t][r0 + r][tok] + sRed[1][t][r0 + r][tok] +
+                          sRed[2][t][r0 + r][tok] + sRed[3][t][r0 + r][tok]);
+        *(half4*)(out + ((size_t)n * H + h) * D + i0 + r0) = o;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <int H, int D, int RV, int DR>
 static void launch_upproj_t(const void* W, const float* z, int n_tokens, void* out, hipStream_t st) {
   hipLaunchKernelGGL((upproj_kernel<H, D, RV, DR>), dim3(H, D / DR, (n_tokens + 63) / 64), dim3(256),
@@ -385,10 +486,11 @@ hipError_t launch_upproj(const ShapeKey& s, const void* W, const float* z, int n
   if (n_tokens <= 0) return hipSuccess;
   if (s.H == 32 && s.d == 128 && s.rv == 512) {
     if (wide_rows) launch_upproj_t<32, 128, 512, 128>(W, z, n_tokens, out, st);
-    else launch_upproj_t<32, 128, 512, 16>(W, z, n_tokens, out, st);
+    else hipLaunchKernelGGL((upproj_small_kernel<32, 128, 512>), dim3(32, 128 / 16), dim3(256), 0,
+                            st, (const half_t*)W, z, n_tokens, (half_t*)out);
   } else if (s.H == 4 && s.d == 64 && s.rv == 64) {
     if (wide_rows) launch_upproj_t<4, 64, 64, 64>(W, z, n_tokens, out, st);
-    else launch_upproj_t<4, 64, 64, 16>(W, z, n_tokens, out, st);
+    else launch_upproj_t<4, 64, 64, 16>(W, z, n_tokens, out, st);  // r_v/4 < 32: one wave per tile
   } else {
     return hipErrorInvalidValue;
   }
@@ -404,24 +506,15 @@ static hipError_t decode_instance(const DecodePlan& p, const void* qt, const voi
                                   int max_blocks, const int32_t* seq_lens, int num_blocks,
                                   int batch, float* ml, float* acc, float* z, void* out,
                                   hipStream_t st) {
-  SplitArgs a;
-  a.qt = (const half_t*)qt;
-  a.k_cache = (const half_t*)k_cache;
-  a.v_cache = (const half_t*)v_cache;
-  a.block_tables = block_tables;
-  a.seq_lens = seq_lens;
-  a.ml = ml;
-  a.acc = acc;
-  a.max_blocks = max_blocks;
-  a.num_blocks = num_blocks;
-  a.pages_per_split = p.pages_per_split;
-  a.num_splits = p.num_splits;
   if (g_timing.which == TIME_DECODE_SPLIT && g_timing.start) hipEventRecord(g_timing.start, st);
   hipLaunchKernelGGL((decode_split_kernel<H, RK, RV, NW>), dim3(p.num_splits, batch), dim3(NW * 64),
-                     0, st, a);
+                     0, st, (const half_t*)qt, (const half_t*)k_cache, (const half_t*)v_cache,
+                     block_tables, seq_lens, ml, acc, max_blocks, num_blocks, p.pages_per_split,
+                     p.num_splits);
   if (g_timing.which == TIME_DECODE_SPLIT && g_timing.stop) hipEventRecord(g_timing.stop, st);
-  hipLaunchKernelGGL((combine_kernel<H, RK, RV, NW>), dim3(H, batch), dim3(256), 0, st,
-                     (const float*)ml, (const float*)acc, seq_lens, max_blocks,
+  const long threads = (long)batch * H * (RV / 4);
+  hipLaunchKernelGGL((combine_kernel<H, RV>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     st, (const float*)ml, (const float*)acc, seq_lens, batch, max_blocks,
                      p.pages_per_split, p.num_splits, z);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -431,7 +524,7 @@ static hipError_t decode_instance(const DecodePlan& p, const void* qt, const voi
 template <int H, int D, int RK>
 static hipError_t qproj_instance(const void* q, const void* U, int n, float scale, void* qt,
                                  hipStream_t st) {
-  hipLaunchKernelGGL((qproj_kernel<H, D, RK>), dim3(H, (n + 15) / 16), dim3(256), 0, st,
+  hipLaunchKernelGGL((qproj_kernel<H, D, RK>), dim3(H, (n + 63) / 64), dim3(256), 0, st,
                      (const half_t*)q, (const half_t*)U, n, scale * kLog2e, (half_t*)qt);
   return hipGetLastError();
 }
@@ -449,8 +542,9 @@ hipError_t launch_decode(const ShapeKey& s, const DecodePlan& p, const void* qt,
                          int max_blocks, const int32_t* seq_lens, int num_blocks, int batch,
                          float* ml, float* acc, float* z, void* out, hipStream_t st) {
   if (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512)
-    return decode_instance<32, 128, 64, 512, 4>(p, qt, k_cache, v_cache, W, block_tables, max_blocks,
-                                                seq_lens, num_blocks, batch, ml, acc, z, out, st);
+    return decode_instance<32, 128, 64, 512, STARKV_DECODE_WAVES>(
+        p, qt, k_cache, v_cache, W, block_tables, max_blocks, seq_lens, num_blocks, batch, ml, acc,
+        z, out, st);
   if (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64)
     return decode_instance<4, 64, 16, 64, 4>(p, qt, k_cache, v_cache, W, block_tables, max_blocks,
                                              seq_lens, num_blocks, batch, ml, acc, z, out, st);

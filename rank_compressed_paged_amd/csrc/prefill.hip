@@ -114,51 +114,53 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
   const half_t* kbase = a.k_cache + ((size_t)h * PBS + col) * RK + quad * (C::KC / 4);
   const half_t* vbase = a.v_cache + (size_t)(w * C::FPW + col) * PBS + quad * 4;
-  __syncthreads();
-
-  for (int p = 0; p < n_pages; ++p) {
-    const int buf = p & 1;
+  struct Regs {
+    kvec k[C::NKC];
+    half4 v[C::FT];
+  };
+  auto safe_block = [&](int p) {
     const int blk = bt[p];
-    const bool ok = (unsigned)blk < (unsigned)a.num_blocks;
-    // loads for this page (keys for the score unit, values for the feature slice)
-    kvec kr[C::NKC];
-    half4 vr[C::FT];
-    if (ok) {
-      const half_t* kp = kbase + (size_t)blk * H * PBS * RK;
+    return ((unsigned)blk < (unsigned)a.num_blocks) ? blk : -1;
+  };
+  auto load = [&](Regs& r, int blk) {
+    const half_t* kp = kbase + (size_t)blk * H * PBS * RK;
 #pragma unroll
-      for (int c = 0; c < C::NKC; ++c) kr[c] = *(const kvec*)(kp + c * C::KC);
-      const half_t* vp = vbase + (size_t)blk * RV * PBS;
+    for (int c = 0; c < C::NKC; ++c) r.k[c] = *(const kvec*)(kp + c * C::KC);
+    const half_t* vp = vbase + (size_t)blk * RV * PBS;
 #pragma unroll
-      for (int ft = 0; ft < C::FT; ++ft) vr[ft] = *(const half4*)(vp + (size_t)ft * 16 * PBS);
-    }
+    for (int ft = 0; ft < C::FT; ++ft) r.v[ft] = *(const half4*)(vp + (size_t)ft * 16 * PBS);
+  };
+  // one page: scores of this wave's (head, 16 queries), online softmax, P via
+  // LDS, then every wave's value slice for all rows
+  auto process = [&](Regs& r, int p, int buf, bool ok) {
     if (ok) {
       float4v sacc = zero4();
 #pragma unroll
       for (int c = 0; c < C::NKC; ++c) {
         if constexpr (C::KC == 32)
-          sacc = mfma16x16x32(kr[c], qv[c], sacc);
+          sacc = mfma16x16x32(r.k[c], qv[c], sacc);
         else
-          sacc = mfma16x16x16(kr[c], qv[c], sacc);
+          sacc = mfma16x16x16(r.k[c], qv[c], sacc);
       }
       float sv[4];
       float pm = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = p * PBS + quad * 4 + r;
-        sv[r] = (t < L && t <= qpos) ? sacc[r] : -INFINITY;
-        pm = fmaxf(pm, sv[r]);
+      for (int e = 0; e < 4; ++e) {
+        const int t = p * PBS + quad * 4 + e;
+        sv[e] = (t < L && t <= qpos) ? sacc[e] : -INFINITY;
+        pm = fmaxf(pm, sv[e]);
       }
       pm = max_over_quads(pm);
-      const float m_new = fmaxf(m_run, pm);
       // m_new is finite from the first page on: key 0 is visible to every query
+      const float m_new = fmaxf(m_run, pm);
       const float alpha = exp2f(m_run - m_new);
       float ps = 0.f;
       half4 ph;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pr = exp2f(sv[r] - m_new);
+      for (int e = 0; e < 4; ++e) {
+        const float pr = exp2f(sv[e] - m_new);
         ps += pr;
-        ph[r] = (half_t)pr;
+        ph[e] = (half_t)pr;
       }
       ps = sum_over_quads(ps);
       l_run = l_run * alpha + ps;
@@ -167,17 +169,16 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
       if (quad == 0) sAlpha[buf][row] = alpha;
       if (alpha != 1.f) sFlag[buf] = p;
     }
-    __syncthreads();
+    block_sync_lds();
     if (ok) {
       const bool rescale = sFlag[buf] == p;
       const int valid = min(PBS, L - p * PBS);
+      if (valid < PBS) {  // slots past the sequence may hold anything (NaN)
 #pragma unroll
-      for (int ft = 0; ft < C::FT; ++ft) {
-        if (valid < PBS) {
+        for (int ft = 0; ft < C::FT; ++ft)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (quad * 4 + e >= valid) vr[ft][e] = (half_t)0.f;
-        }
+            if (quad * 4 + e >= valid) r.v[ft][e] = (half_t)0.f;
       }
 #pragma unroll
       for (int rt = 0; rt < C::RT; ++rt) {
@@ -188,14 +189,34 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
           for (int ft = 0; ft < C::FT; ++ft) acc[rt][ft] *= al;
         }
 #pragma unroll
-        for (int ft = 0; ft < C::FT; ++ft) acc[rt][ft] = mfma16x16x16(vr[ft], pb, acc[rt][ft]);
+        for (int ft = 0; ft < C::FT; ++ft) acc[rt][ft] = mfma16x16x16(r.v[ft], pb, acc[rt][ft]);
       }
+    }
+  };
+
+  Regs ra, rb;
+  int blk_a = safe_block(0);
+  if (blk_a >= 0) load(ra, blk_a);
+  __syncthreads();
+  for (int p = 0; p < n_pages; p += 2) {
+    int blk_b = -1;
+    if (p + 1 < n_pages) {
+      blk_b = safe_block(p + 1);
+      if (blk_b >= 0) load(rb, blk_b);
+    }
+    process(ra, p, 0, blk_a >= 0);
+    if (p + 1 < n_pages) {
+      if (p + 2 < n_pages) {
+        blk_a = safe_block(p + 2);
+        if (blk_a >= 0) load(ra, blk_a);
+      }
+      process(rb, p + 1, 1, blk_b >= 0);
     }
   }
 
   // ---- normalise and write z rows of this tile
   if (quad == 0) sL[row] = l_run;
-  __syncthreads();
+  block_sync_lds();
 #pragma unroll
   for (int rt = 0; rt < C::RT; ++rt) {
     const int r_row = rt * 16 + col;
