@@ -215,11 +215,12 @@ def run_bench(args):
     app_ms, _, _ = timed(append_step, max(args.steps, 10), True)
     _, app_kern_ms, _ = timed(append_step, max(args.steps, 10), True, sk.TIME_APPEND)
 
-    # measured streaming-read ceiling on this machine: a plain reduction reading
-    # as many bytes as one step's latents, after the same flush
-    ceil_buf = torch.ones(lat_bytes // 4, dtype=torch.float32, device="cuda")
-    ceil_sink = torch.empty((), dtype=torch.float32, device="cuda")
-    ceil_ms, _, _ = timed(lambda: torch.sum(ceil_buf, dim=0, out=ceil_sink), max(args.steps, 10), True)
+    # measured streaming-read ceiling on this machine: the library's plain
+    # 16-byte streaming read over as many bytes as one step's latents, after
+    # the same flush
+    ceil_buf = torch.ones(lat_bytes, dtype=torch.uint8, device="cuda")
+    ceil_sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    ceil_ms, _, _ = timed(lambda: sk.stream_read(ceil_buf, ceil_sink), max(args.steps, 10), True)
     ceiling_gbs = lat_bytes / (statistics.fmean(ceil_ms) * 1e-3) / 1e9
     del ceil_buf
 

@@ -177,6 +177,14 @@ starkv_status starkv_set_timing_events(void* start, void* stop, int32_t which);
 starkv_status starkv_decode_plan(const starkv_dims* dims, int32_t batch, int32_t max_seq_len,
                                  int32_t* pages_per_split, int32_t* num_splits);
 
+/*
+ * Measurement utility (not part of the attention path): read `bytes` bytes
+ * at `src` (16-byte aligned, bytes a multiple of 16) with 16-byte loads, as a
+ * streaming-read ceiling for the HBM rate.  `sink` is a device buffer of at
+ * least 1024 uint32 that may be written.  Asynchronous on `stream`.
+ */
+starkv_status starkv_util_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

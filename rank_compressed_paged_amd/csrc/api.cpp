@@ -26,24 +26,60 @@ static int env_int(const char* name, int dflt) {
 
 static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
-// Split-K plan: aim for about kTarget work groups over the batch, but keep
-// at least kMinPages pages per split so the partial state (H*r_v fp32 per
-// split) stays small next to the latents read; at most 256 splits.
+// Number of compute units of the current device (queried once per device;
+// 256, the MI355X count, when no device answers).
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Split-K plan.  The split-K kernel runs one work group per compute unit,
+// so B*S groups execute in ceil(B*S / CUs) rounds, each as long as its
+// pages plus a start-up of about three page times (first-page latency),
+// and every split adds a partial that the combine reads back.  Pick the
+// number of splits S that minimises
+//     rounds * (3 + pages_per_split) + 0.5 * B * S / CUs,
+// preferring fewer splits on ties; pages_per_split <= 256 (block ids are
+// staged in LDS).  Environment overrides (tuning aids):
+// STARKV_DECODE_TARGET_WGS / STARKV_DECODE_MIN_PAGES switch to a fixed
+// target of work groups with a minimum split length.
 DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int bs) {
   (void)s;
   const int pages = cdiv(max_seq_len, bs);
-  if (pages <= 0 || batch <= 0) return DecodePlan{1, 1};
-  const int target = env_int("STARKV_DECODE_TARGET_WGS", 256);
-  const int min_pps = env_int("STARKV_DECODE_MIN_PAGES", 8);
-  const int want_splits = cdiv(target, batch);
-  int pps = cdiv(pages, want_splits);
-  if (pps < min_pps) pps = min_pps;
-  int ns = cdiv(pages, pps);
-  while (ns > 256) {
-    pps *= 2;
-    ns = cdiv(pages, pps);
+  const int variant = env_int("STARKV_DECODE_VARIANT", 0);
+  if (pages <= 0 || batch <= 0) return DecodePlan{1, 1, variant};
+  const int target = env_int("STARKV_DECODE_TARGET_WGS", 0);
+  if (target > 0) {
+    const int min_pps = env_int("STARKV_DECODE_MIN_PAGES", 1);
+    int pps = cdiv(pages, cdiv(target, batch));
+    if (pps < min_pps) pps = min_pps;
+    if (pps > 256) pps = 256;
+    return DecodePlan{pps, cdiv(pages, pps), variant};
   }
-  return DecodePlan{pps, ns};
+  const int cus = device_cus();
+  double best = 1e300;
+  int best_pps = pages < 256 ? pages : 256;
+  for (int ns = cdiv(pages, 256); ns <= pages; ++ns) {
+    const int pps = cdiv(pages, ns);
+    const int nsr = cdiv(pages, pps);  // splits actually used at this length
+    if (nsr != ns) continue;
+    const double rounds = (double)cdiv((long)batch * ns, cus);
+    const double cost = rounds * (3.0 + pps) + 0.5 * (double)batch * ns / cus;
+    if (cost < best - 1e-9) {
+      best = cost;
+      best_pps = pps;
+    }
+    if (ns > 4 * cus) break;
+  }
+  return DecodePlan{best_pps, cdiv(pages, best_pps), variant};
 }
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -248,6 +284,14 @@ starkv_status starkv_prefill_attn(const starkv_dims* dims, const void* q,
                      v_cache, W, block_tables, max_blocks_per_seq, seq_lens, dims->num_blocks,
                      batch, (float*)(wb + ws.z_off), out, s);
   return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
+}
+
+starkv_status starkv_util_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (bytes == 0) return STARKV_OK;
+  if (!src || !sink) return STARKV_ERR_NULL;
+  if (!aligned16(src) || (bytes & 15) != 0) return STARKV_ERR_ALIGN;
+  return launch_stream_read(src, bytes, sink, (hipStream_t)stream) == hipSuccess ? STARKV_OK
+                                                                                 : STARKV_ERR_LAUNCH;
 }
 
 starkv_status starkv_set_timing_events(void* start, void* stop, int32_t which) {

@@ -37,10 +37,6 @@
 #include "common.h"
 #include "kernels.h"
 
-#ifndef STARKV_DECODE_WAVES
-#define STARKV_DECODE_WAVES 8
-#endif
-
 namespace starkv {
 
 template <int H, int RK, int RV, int NW>
@@ -58,6 +54,7 @@ struct DecodeCfg {
 };
 
 constexpr int BS = 16;  // tokens per page
+constexpr int kMaxSplitPages = 256;  // planner bound on pages per split
 
 // ---------------------------------------------------------------------------
 // 1. q~[n, h, :] = (scale*log2e) * U_h^T q[n, h, :]  -> fp16
@@ -127,7 +124,15 @@ struct PageRegs {
   half4 v[C::FT];
 };
 
-template <int H, int RK, int RV, int NW>
+template <bool NT, typename T>
+__device__ __forceinline__ T ld_page(const T* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
+template <int H, int RK, int RV, int NW, bool NT>
 __device__ __forceinline__ void load_page(PageRegs<H, RK, RV, NW>& pr, const half_t* __restrict__ kc,
                                           const half_t* __restrict__ vc, int blk, int w, int col,
                                           int quad) {
@@ -139,11 +144,11 @@ __device__ __forceinline__ void load_page(PageRegs<H, RK, RV, NW>& pr, const hal
   for (int hl = 0; hl < C::HPW; ++hl)
 #pragma unroll
     for (int c = 0; c < C::NKC; ++c)
-      pr.k[hl][c] = *(const kvec*)(kb + (size_t)hl * BS * RK + c * C::KC);
+      pr.k[hl][c] = ld_page<NT>((const kvec*)(kb + (size_t)hl * BS * RK + c * C::KC));
   // values: feature (w*FPW + ft*16 + col), tokens 4*quad .. 4*quad+3
   const half_t* vb = vc + ((size_t)blk * RV + w * C::FPW + col) * BS + quad * 4;
 #pragma unroll
-  for (int ft = 0; ft < C::FT; ++ft) pr.v[ft] = *(const half4*)(vb + (size_t)ft * 16 * BS);
+  for (int ft = 0; ft < C::FT; ++ft) pr.v[ft] = ld_page<NT>((const half4*)(vb + (size_t)ft * 16 * BS));
 }
 
 template <int H, int RK, int RV, int NW>
@@ -235,7 +240,7 @@ __device__ __forceinline__ void process_page(
   }
 }
 
-template <int H, int RK, int RV, int NW>
+template <int H, int RK, int RV, int NW, int DEPTH, bool NT>
 __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     const half_t* __restrict__ qt, const half_t* __restrict__ k_cache,
     const half_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
@@ -246,6 +251,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
   __shared__ __attribute__((aligned(16))) half_t sP[2][C::R16][BS];
   __shared__ float sAlpha[2][C::R16];
   __shared__ int sFlag[2];  // page index whose softmax step moved a running max
+  __shared__ int sBlk[kMaxSplitPages];  // block ids of this split, loadable
 
   const int s = blockIdx.x, b = blockIdx.y;
   const int L = seq_lens[b];
@@ -258,10 +264,24 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
   const int lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
 
+  // Block ids of the split's pages are staged in LDS once: a per-page
+  // scalar load from the block table would stall the next page's load issue
+  // for a full memory latency under load.  Their loads are issued first, the
+  // first page's right after, and only the former is waited for before the
+  // (LDS-only) start barrier.  Invalid ids become -1 (masked page).
+  static_assert(kMaxSplitPages <= NW * 64, "one block id per thread");
+  const int32_t* bt = block_tables + (size_t)b * max_blocks;
+  const int bid = (tid < p1 - p0) ? bt[p0 + tid] : 0;
+  const int blk0 = bt[p0];
+  PageRegs<H, RK, RV, NW> ring[DEPTH];
+  load_page<H, RK, RV, NW, NT>(ring[0], k_cache, v_cache,
+                               ((unsigned)blk0 < (unsigned)num_blocks) ? blk0 : 0, w, col, quad);
+
   // rows >= H are padding: P stays zero there, alpha one
   for (int i = tid; i < 2 * C::R16 * BS; i += NW * 64) (&sP[0][0][0])[i] = (half_t)0.f;
   for (int i = tid; i < 2 * C::R16; i += NW * 64) (&sAlpha[0][0])[i] = 1.f;
   if (tid < 2) sFlag[tid] = -1;
+  if (tid < p1 - p0) sBlk[tid] = ((unsigned)bid < (unsigned)num_blocks) ? bid : -1;
 
   // q~ of head (w*HPW + col) for this lane's k chunks; B column col
   kvec qv[C::NKC];
@@ -280,33 +300,35 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
 #pragma unroll
     for (int ft = 0; ft < C::FT; ++ft) st.acc[rt][ft] = zero4();
 
+  block_sync_lds();  // block ids and LDS initialisation visible
+
   // page p of this split: its block id (clamped to a loadable one past the
   // split or when invalid) and how many of its tokens count
-  const int32_t* bt = block_tables + (size_t)b * max_blocks;
   auto page_block = [&](int p) {
-    const int blk = bt[min(p, p1 - 1)];
-    return ((unsigned)blk < (unsigned)num_blocks) ? blk : 0;
+    const int blk = __builtin_amdgcn_readfirstlane(sBlk[min(p, p1 - 1) - p0]);
+    return blk >= 0 ? blk : 0;
   };
   auto page_valid = [&](int p) {
     if (p >= p1) return 0;
-    const int blk = bt[p];
-    return ((unsigned)blk < (unsigned)num_blocks) ? min(BS, L - p * BS) : 0;
+    return __builtin_amdgcn_readfirstlane(sBlk[p - p0]) >= 0 ? min(BS, L - p * BS) : 0;
   };
 
-  PageRegs<H, RK, RV, NW> ra, rb;
-  load_page<H, RK, RV, NW>(ra, k_cache, v_cache, page_block(p0), w, col, quad);
-  __syncthreads();  // LDS initialisation visible
+  // DEPTH register sets form a ring: page p+DEPTH-1 is requested while page
+  // p is processed.  sched_barrier(0) keeps the scheduler from hoisting the
+  // current page's matrix ops (and the waits they need) above that request.
+#pragma unroll
+  for (int j = 1; j < DEPTH - 1; ++j)
+    load_page<H, RK, RV, NW, NT>(ring[j], k_cache, v_cache, page_block(p0 + j), w, col, quad);
 
-  // sched_barrier(0) keeps the scheduler from hoisting the current page's
-  // matrix ops (and the waits they need) above the next page's load issue
-  for (int p = p0; p < p1; p += 2) {
-    load_page<H, RK, RV, NW>(rb, k_cache, v_cache, page_block(p + 1), w, col, quad);
-    __builtin_amdgcn_sched_barrier(0);
-    process_page<H, RK, RV, NW>(st, ra, qv, sP, sAlpha, sFlag, p, 0, page_valid(p), w, col, quad);
-    load_page<H, RK, RV, NW>(ra, k_cache, v_cache, page_block(p + 2), w, col, quad);
-    __builtin_amdgcn_sched_barrier(0);
-    process_page<H, RK, RV, NW>(st, rb, qv, sP, sAlpha, sFlag, p + 1, 1, page_valid(p + 1), w, col,
-                                quad);
+  for (int p = p0; p < p1; p += DEPTH) {
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) {
+      load_page<H, RK, RV, NW, NT>(ring[(j + DEPTH - 1) % DEPTH], k_cache, v_cache,
+                                   page_block(p + j + DEPTH - 1), w, col, quad);
+      __builtin_amdgcn_sched_barrier(0);
+      process_page<H, RK, RV, NW>(st, ring[j], qv, sP, sAlpha, sFlag, p + j, (p + j - p0) & 1,
+                                  page_valid(p + j), w, col, quad);
+    }
   }
 
   // ---- partial state of this split: rows are heads, contiguous features
@@ -325,9 +347,11 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
 
 // ---------------------------------------------------------------------------
 // 3. combine: z[b,h,:] = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
-// One thread per (sequence, head, 4 features); a single online pass over the
-// splits keeps (M, num, den) so every split's loads are independent of the
-// running state and many can be in flight.  grid ceil(B*H*RV/4 / 256).
+// One thread per (sequence, head, 4 features), grid ceil(B*H*RV/4 / 256).
+// The statistics and partials of CB splits are requested together
+// (indices clamped to the last split, weight 0 past it), so a sequence with
+// up to CB splits costs one memory round trip; within a batch the new
+// running max is taken first, then the weighted sums.
 // ---------------------------------------------------------------------------
 template <int H, int RV>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ml,
@@ -338,6 +362,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       float* __restrict__ z) {
   constexpr int R16 = ((H + 15) / 16) * 16;
   constexpr int F4 = RV / 4;
+  constexpr int CB = 16;
   const int gid = blockIdx.x * 256 + threadIdx.x;
   if (gid >= batch * H * F4) return;  // no barrier in this kernel
   const int f4 = gid % F4;
@@ -350,17 +375,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const float4v* ab = (const float4v*)(acc + ((size_t)b * num_splits * R16 + h) * RV) + f4;
   float M = -INFINITY, den = 0.f;
   float4v num = zero4();
-#pragma unroll 8
-  for (int s = 0; s < ns; ++s) {
-    const float ms = mlb[(size_t)s * 2 * R16];
-    const float ls = mlb[(size_t)s * 2 * R16 + R16];
-    const float4v as = ab[(size_t)s * R16 * F4];
-    const float Mn = fmaxf(M, ms);
-    const float sc = (Mn == M) ? 1.f : exp2f(M - Mn);
-    const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - Mn);
-    num = num * sc + as * wgt;
-    den = den * sc + ls * wgt;
-    M = Mn;
+  for (int s0 = 0; s0 < ns; s0 += CB) {
+    float m[CB], l[CB];
+    float4v a[CB];
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const int sj = min(s0 + j, ns - 1);
+      m[j] = mlb[(size_t)sj * 2 * R16];
+      l[j] = mlb[(size_t)sj * 2 * R16 + R16];
+      a[j] = ab[(size_t)sj * R16 * F4];
+    }
+    float mx = M;
+#pragma unroll
+    for (int j = 0; j < CB; ++j) mx = (s0 + j < ns) ? fmaxf(mx, m[j]) : mx;
+    const float sc = (mx == M) ? 1.f : exp2f(M - mx);
+    num *= sc;
+    den *= sc;
+    M = mx;
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const bool live = s0 + j < ns && m[j] != -INFINITY;
+      const float wgt = live ? exp2f(m[j] - M) : 0.f;
+      num = live ? num + a[j] * wgt : num;
+      den = live ? den + l[j] * wgt : den;
+    }
   }
   float4v* zo = (float4v*)(z + ((size_t)b * H + h) * RV) + f4;
   *zo = (den > 0.f) ? num * (1.f / den) : zero4();
@@ -415,9 +453,9 @@ __global__ __launch_bounds__(256) void upproj_kernel(const half_t* __restrict__ 
 }
 
 // Decode variant: grid (H, D/16); the 4 waves split the r_v contraction
-// (RV/4 features each) for every 16-token tile of the batch, and the four
-// partial tiles are summed through LDS.  More loads in flight per work group
-// than one wave walking all of r_v.
+// (RV/4 features each) for up to 64 tokens per pass, and the four partial
+// tiles are summed through LDS.  Every W_h and z operand of a pass is
+// requested before the first matrix op, so a pass costs one round trip.
 template <int H, int D, int RV>
 __global__ __launch_bounds__(256) void upproj_small_kernel(const half_t* __restrict__ W,
                                                            const float* __restrict__ z,
@@ -426,6 +464,7 @@ __global__ __launch_bounds__(256) void upproj_small_kernel(const half_t* __restr
   constexpr int KW = RV / 4;     // features per wave
   constexpr int KS = KW / 32;    // 32-wide steps per wave
   constexpr int TT = 4;          // token tiles per pass (64 tokens)
+  static_assert(KS >= 1, "each wave needs at least one 32-wide step");
   __shared__ float sRed[4][TT][16][17];
   const int h = blockIdx.x, i0 = blockIdx.y * 16;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -435,19 +474,28 @@ __global__ __launch_bounds__(256) void upproj_small_kernel(const half_t* __restr
 #pragma unroll
   for (int k = 0; k < KS; ++k) av[k] = *(const half8*)(wrow + k * 32);
   for (int n0 = 0; n0 < n_tokens; n0 += 16 * TT) {
+    const int tiles = min(TT, (n_tokens - n0 + 15) / 16);  // uniform
+    float4v zr4[TT][KS][2];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      const int n = min(n0 + t * 16 + col, n_tokens - 1);  // in range; masked below
+      const float* zr = z + ((size_t)n * H + h) * RV + w * KW + quad * 8;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        zr4[t][k][0] = (t < tiles) ? *(const float4v*)(zr + k * 32) : zero4();
+        zr4[t][k][1] = (t < tiles) ? *(const float4v*)(zr + k * 32 + 4) : zero4();
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float4v acc[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       acc[t] = zero4();
-      const int n = n0 + t * 16 + col;
-      const bool nv = n < n_tokens;
-      const float* zr = z + ((size_t)(nv ? n : 0) * H + h) * RV + w * KW + quad * 8;
+      const bool nv = n0 + t * 16 + col < n_tokens;
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
-        const float4v z0 = nv ? *(const float4v*)(zr + k * 32) : zero4();
-        const float4v z1 = nv ? *(const float4v*)(zr + k * 32 + 4) : zero4();
         half8 hi, lo;
-        split_f16x8(z0, z1, hi, lo);
+        split_f16x8(nv ? zr4[t][k][0] : zero4(), nv ? zr4[t][k][1] : zero4(), hi, lo);
         acc[t] = mfma16x16x32(av[k], hi, acc[t]);
         acc[t] = mfma16x16x32(av[k], lo, acc[t]);
       }
@@ -490,7 +538,7 @@ hipError_t launch_upproj(const ShapeKey& s, const void* W, const float* z, int n
                             st, (const half_t*)W, z, n_tokens, (half_t*)out);
   } else if (s.H == 4 && s.d == 64 && s.rv == 64) {
     if (wide_rows) launch_upproj_t<4, 64, 64, 64>(W, z, n_tokens, out, st);
-    else launch_upproj_t<4, 64, 64, 16>(W, z, n_tokens, out, st);  // r_v/4 < 32: one wave per tile
+    else launch_upproj_t<4, 64, 64, 16>(W, z, n_tokens, out, st);
   } else {
     return hipErrorInvalidValue;
   }
@@ -500,14 +548,15 @@ hipError_t launch_upproj(const ShapeKey& s, const void* W, const float* z, int n
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-template <int H, int D, int RK, int RV, int NW>
+template <int H, int D, int RK, int RV, int NW, int DEPTH, bool NT>
 static hipError_t decode_instance(const DecodePlan& p, const void* qt, const void* k_cache,
                                   const void* v_cache, const void* W, const int32_t* block_tables,
                                   int max_blocks, const int32_t* seq_lens, int num_blocks,
                                   int batch, float* ml, float* acc, float* z, void* out,
                                   hipStream_t st) {
   if (g_timing.which == TIME_DECODE_SPLIT && g_timing.start) hipEventRecord(g_timing.start, st);
-  hipLaunchKernelGGL((decode_split_kernel<H, RK, RV, NW>), dim3(p.num_splits, batch), dim3(NW * 64),
+  hipLaunchKernelGGL((decode_split_kernel<H, RK, RV, NW, DEPTH, NT>), dim3(p.num_splits, batch),
+                     dim3(NW * 64),
                      0, st, (const half_t*)qt, (const half_t*)k_cache, (const half_t*)v_cache,
                      block_tables, seq_lens, ml, acc, max_blocks, num_blocks, p.pages_per_split,
                      p.num_splits);
@@ -541,13 +590,22 @@ hipError_t launch_decode(const ShapeKey& s, const DecodePlan& p, const void* qt,
                          const void* v_cache, const void* W, const int32_t* block_tables,
                          int max_blocks, const int32_t* seq_lens, int num_blocks, int batch,
                          float* ml, float* acc, float* z, void* out, hipStream_t st) {
-  if (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512)
-    return decode_instance<32, 128, 64, 512, STARKV_DECODE_WAVES>(
-        p, qt, k_cache, v_cache, W, block_tables, max_blocks, seq_lens, num_blocks, batch, ml, acc,
-        z, out, st);
+#define STARKV_DECODE_ARGS \
+  p, qt, k_cache, v_cache, W, block_tables, max_blocks, seq_lens, num_blocks, batch, ml, acc, z, out, st
+  if (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) {
+    // kernel variant (tuning aid): waves per group, prefetch depth, non-temporal loads
+    switch (p.variant) {
+      case 1: return decode_instance<32, 128, 64, 512, 4, 2, false>(STARKV_DECODE_ARGS);
+      case 2: return decode_instance<32, 128, 64, 512, 8, 3, false>(STARKV_DECODE_ARGS);
+      case 3: return decode_instance<32, 128, 64, 512, 8, 2, true>(STARKV_DECODE_ARGS);
+      case 4: return decode_instance<32, 128, 64, 512, 16, 2, false>(STARKV_DECODE_ARGS);
+      case 5: return decode_instance<32, 128, 64, 512, 8, 4, false>(STARKV_DECODE_ARGS);
+      default: return decode_instance<32, 128, 64, 512, 8, 2, false>(STARKV_DECODE_ARGS);
+    }
+  }
   if (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64)
-    return decode_instance<4, 64, 16, 64, 4>(p, qt, k_cache, v_cache, W, block_tables, max_blocks,
-                                             seq_lens, num_blocks, batch, ml, acc, z, out, st);
+    return decode_instance<4, 64, 16, 64, 4, 2, false>(STARKV_DECODE_ARGS);
+#undef STARKV_DECODE_ARGS
   return hipErrorInvalidValue;
 }
 

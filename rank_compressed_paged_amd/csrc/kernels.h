@@ -18,6 +18,7 @@ struct ShapeKey {
 struct DecodePlan {
   int pages_per_split;
   int num_splits;
+  int variant;  // split-kernel variant (0 = default)
 };
 
 // Byte offsets of the decode workspace regions.
@@ -55,6 +56,10 @@ hipError_t launch_decode(const ShapeKey& s, const DecodePlan& p, const void* qt,
 // work group per head and 64 tokens) over the decode tiling (16 rows).
 hipError_t launch_upproj(const ShapeKey& s, const void* W, const float* z, int n_tokens,
                          bool wide_rows, void* out, hipStream_t st);
+
+// Measurement aid: read `bytes` (a multiple of 16) with 16-byte loads and
+// fold them into one word per work group, so nothing is optimised away.
+hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t st);
 
 hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const void* U,
                          const void* W, const int64_t* slots, int n_tokens, int num_blocks,

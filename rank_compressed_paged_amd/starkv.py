@@ -32,6 +32,7 @@ EXPORTED = [
     "starkv_abi_version", "starkv_status_string", "starkv_shape_supported", "starkv_append",
     "starkv_decode_workspace_size", "starkv_decode_attn", "starkv_prefill_workspace_size",
     "starkv_prefill_attn", "starkv_set_timing_events", "starkv_decode_plan",
+    "starkv_util_stream_read",
 ]
 
 
@@ -74,6 +75,8 @@ _lib.starkv_prefill_attn.restype = _i32
 _lib.starkv_prefill_attn.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _i32, _i32, _vp, _vp, _vp,
                                      _vp, _vp, _i32, _vp, _i32, _i32, ctypes.c_float, _vp, _vp,
                                      _sz, _vp]
+_lib.starkv_util_stream_read.restype = _i32
+_lib.starkv_util_stream_read.argtypes = [_vp, _sz, _vp, _vp]
 _lib.starkv_set_timing_events.restype = _i32
 _lib.starkv_set_timing_events.argtypes = [_vp, _vp, _i32]
 
@@ -217,6 +220,13 @@ def prefill_attn(q, query_start_loc, max_query_len, k_cache, v_cache, U, W, bloc
         _dev(workspace, torch.uint8, "workspace"), int(workspace.numel()), _stream(stream))
     _check(st, "starkv_prefill_attn")
     return out
+
+
+def stream_read(buf, sink, stream=None):
+    """Measurement utility: stream-read a uint8 buffer (HBM ceiling)."""
+    _check(_lib.starkv_util_stream_read(_dev(buf, torch.uint8, "buf"), int(buf.numel()),
+                                        _dev(sink, torch.int32, "sink"), _stream(stream)),
+           "starkv_util_stream_read")
 
 
 def set_timing_events(start_event, stop_event, which):

@@ -116,5 +116,5 @@ def test_decode_plan_properties():
     for B, L in [(16, 2048), (64, 8192), (20, 32768), (1, 1), (2, 256), (1, 40000)]:
         pps, ns = sk.decode_plan(d, B, L)
         pages = -(-L // 16)
-        assert 1 <= ns <= 256 and pps >= 1
+        assert ns >= 1 and 1 <= pps <= 256
         assert pps * ns >= pages and pps * (ns - 1) < pages
