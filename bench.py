@@ -7,12 +7,15 @@ d = 128, r_k = 64 per head, joint r_v = 512, 16-token pages, fp16 storage.
     python bench.py [--steps K] [--warmup W] [--workload decode_b16] [--no-cpu]
 
 Prints ONE JSON line.  Timing: every step is preceded (outside the timed
-events) by a 512 MiB fill that evicts the 256 MB Infinity Cache, so each step
-reads its latents from HBM; each step is bracketed by HIP events on the
-stream the library launches on, and the split-K kernel alone by events the
-library records around its launch.  `value` is latent-KV bytes per step /
-mean step time.  The CPU leg times the fp64 oracle on a bounded sample of
-the same workload on the host cores.
+events) by a 512 MiB read sweep that evicts the 256 MB Infinity Cache, so
+each step reads its latents from HBM; each step is bracketed by HIP events on
+the stream the library launches on.  The split-K kernel alone is timed by
+events that take its dispatch's own begin and end timestamps.  `value` is
+latent-KV bytes per step / mean step time.  Beside the headline the line
+carries the step with its append, a streaming-read ceiling, the chunked
+prefill workload (16 requests x 4096 cached + 256 new tokens: attention and
+append, as TFLOP/s against the fp16 MFMA peak), and the CPU leg, which times
+the fp64 oracle on a bounded sample of the decode workload on the host cores.
 
 Other modes:
     --profile-run             a few steps plus a 256 MiB copy, for rocprofv3
@@ -37,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-step attn ms + latent-KV HBM GB/s (% peak), 32h d128 r_k64 r_v512 fp16"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD public specification
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, AMD public specification
 FLUSH_BYTES = 512 << 20        # > 2x the 256 MB Infinity Cache
 COPY_BYTES = 256 << 20         # plain copy used to calibrate the HBM counters
 DECODE_KERNEL = "decode_split_kernel"
@@ -79,6 +83,7 @@ def parse_args(argv=None):
     ap.add_argument("--workload", default="decode_b16",
                     choices=["decode_b16", "decode_b64", "long_b20", "tiny"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill_b16 leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU sample budget")
     ap.add_argument("--flush", choices=["read", "write"], default="read",
                     help="evict the Infinity Cache by reading (default) or writing 512 MiB")
@@ -114,19 +119,130 @@ def cpu_baseline(case, budget_s):
     c = case.cache
     sh = case.shape
     done, spent, tokens = 0, 0.0, 0
-    while done < case.B and spent < budget_s:
+    # whole sequences, cycling over the batch, until the budget is spent
+    while spent < budget_s or done < 1:
+        b = done % case.B
         t0 = time.perf_counter()
         oracle.decode(case.q, c.k_cache, c.v_cache, case.U, case.W, c.block_tables,
-                      c.seq_lens, case.scale, batch_indices=[done])
+                      c.seq_lens, case.scale, batch_indices=[b])
         spent += time.perf_counter() - t0
-        tokens += int(c.seq_lens[done])
+        tokens += int(c.seq_lens[b])
         done += 1
     lat = tokens * metrics.latent_bytes_per_token(sh.H, sh.r_k, sh.r_v)
     return {"value": round(lat / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{done} of {case.B} sequences of one {case.name} step "
-                      f"({tokens} cached tokens), {spent:.1f} s, fp64 numpy rebuild-then-attend",
-            "ms_per_step_extrapolated": round(spent / done * case.B * 1e3, 1)}
+            "sample": f"{done} sequence decodes cycling over the {case.B} sequences of one "
+                      f"{case.name} step ({tokens} cached tokens, {done / case.B:.1f} steps' "
+                      f"worth), {spent:.1f} s, fp64 numpy rebuild-then-attend",
+            "ms_per_step_extrapolated": round(spent / tokens * int(c.seq_lens.sum()) * 1e3, 1)}
+
+
+def timed(fn, n, flush_fn=None, kernel_sel=0):
+    """Run fn n times, each optionally after flush_fn (outside the events).
+    Returns per-call ms from events around the call on the current stream,
+    per-call ms of one kernel through the library's timing hook (when
+    kernel_sel selects one: the library's timing events, bound to that
+    dispatch and recorded without a system-scope fence), and the wall time of
+    the loop."""
+    import torch
+    from rank_compressed_paged_amd import starkv as sk
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    kev = [(sk.TimingEvent(), sk.TimingEvent()) for _ in range(n)] if kernel_sel else []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        if flush_fn is not None:
+            flush_fn(i)
+        if kernel_sel:
+            sk.set_timing_events(kev[i][0], kev[i][1], kernel_sel)
+        ev[i][0].record(stream)
+        fn()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sk.set_timing_events(None, None, sk.TIME_NONE)
+    steps_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_ms = [a.elapsed_ms(b) for a, b in kev]
+    return steps_ms, kern_ms, wall
+
+
+def device_info():
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count,
+            "hbm_gib": round(p.total_memory / 2**30, 1)}
+
+
+def prefill_leg(flush_fn, steps):
+    """Chunked prefill at 16 requests x (4096 cached + 256 new) tokens: the
+    chunk's append (4096 tokens), then causal attention for the 4096 chunk
+    queries.  Reports time, algorithmic TFLOP/s and the fraction of the
+    dense fp16 MFMA peak for the attention kernel and for the append."""
+    import numpy as np
+    import torch
+    from rank_compressed_paged_amd import metrics
+    from rank_compressed_paged_amd import starkv as sk
+    from rank_compressed_paged_amd import workloads as wl
+    pc = wl.make_config("prefill_b16")
+    sh, c = pc.shape, pc.cache
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    q, k_new, v_new = dev(pc.q), dev(pc.k_new), dev(pc.v_new)
+    U, W = dev(pc.U), dev(pc.W)
+    kc, vc = dev(c.k_cache), dev(c.v_cache)
+    bt, sl = dev(c.block_tables), dev(c.seq_lens)
+    qsl, slots = dev(pc.query_start_loc), dev(pc.slot_mapping)
+    chunk = np.diff(pc.query_start_loc)
+    T, B = int(chunk.sum()), len(chunk)
+    mql, msl = int(chunk.max()), int(c.seq_lens.max())
+    dims = sk.dims_of(kc, vc, U, W)
+    ws = sk.alloc_workspace(sk.prefill_workspace_size(dims, B, T, msl), "cuda")
+    out = torch.empty((T, sh.H, sh.d), dtype=torch.float16, device="cuda")
+
+    def app():
+        sk.append(k_new, v_new, U, W, slots, kc, vc)   # same slots each time: idempotent
+
+    def attn():
+        sk.prefill_attn(q, qsl, mql, kc, vc, U, W, bt, sl, msl, pc.scale, out=out, workspace=ws)
+
+    app()
+    for i in range(3):
+        flush_fn(i)
+        attn()
+    torch.cuda.synchronize()
+    n = max(steps // 2, 10)
+    attn_ms, _, _ = timed(attn, n, flush_fn)
+    _, attn_kern_ms, _ = timed(attn, n, flush_fn, sk.TIME_PREFILL_ATTN)
+    app_ms, _, _ = timed(app, n, flush_fn)
+    _, app_kern_ms, _ = timed(app, n, flush_fn, sk.TIME_APPEND)
+    flops = metrics.prefill_flops(pc.cached_lens, chunk, sh.H, sh.d, sh.r_k, sh.r_v)
+    pairs = metrics.prefill_pairs(pc.cached_lens, chunk)
+    kern_flops = 2 * sh.H * pairs * (sh.r_k + sh.r_v)     # scores + P.c_v, the kernel's share
+    app_flops = metrics.append_flops(T, sh.H, sh.d, sh.r_k, sh.r_v)
+    app_bytes = (2 * T * sh.H * sh.d * 2 + T * 8 + metrics.basis_bytes(sh.H, sh.d, sh.r_k, sh.r_v)
+                 + T * metrics.latent_bytes_per_token(sh.H, sh.r_k, sh.r_v))
+    m = statistics.fmean
+    tf = lambda f, ms: f / (ms * 1e-3) / 1e12
+    return {
+        "workload": "prefill_b16", "requests": B, "cached": int(pc.cached_lens[0]),
+        "chunk": int(chunk[0]), "steps": n,
+        "attn_call_ms": round(m(attn_ms), 4),
+        "attn_call_tflops": round(tf(flops, m(attn_ms)), 1),
+        "attn_call_mfma_frac": round(tf(flops, m(attn_ms)) / MFMA_F16_PEAK_TFLOPS, 4),
+        "attn_kernel_ms": round(m(attn_kern_ms), 4),
+        "attn_kernel_tflops": round(tf(kern_flops, m(attn_kern_ms)), 1),
+        "attn_kernel_mfma_frac": round(tf(kern_flops, m(attn_kern_ms)) / MFMA_F16_PEAK_TFLOPS, 4),
+        "algorithmic_gflop_call": round(flops / 1e9, 1),
+        "algorithmic_gflop_kernel": round(kern_flops / 1e9, 1),
+        "append_tokens": T,
+        "append_call_ms": round(m(app_ms), 4),
+        "append_kernel_ms": round(m(app_kern_ms), 4),
+        "append_kernel_tflops": round(tf(app_flops, m(app_kern_ms)), 1),
+        "append_kernel_mfma_frac": round(tf(app_flops, m(app_kern_ms)) / MFMA_F16_PEAK_TFLOPS, 4),
+        "append_kernel_gbs": round(app_bytes / (m(app_kern_ms) * 1e-3) / 1e9, 1),
+    }
 
 
 def run_bench(args):
@@ -144,7 +260,6 @@ def run_bench(args):
     out = torch.empty((B, sh.H, sh.d), dtype=torch.float16, device="cuda")
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     flush_sink = torch.empty((), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
 
     def do_flush(i):
         # a read-only sweep leaves clean lines behind; a write sweep leaves
@@ -174,31 +289,6 @@ def run_bench(args):
     def append_step():
         sk.append(k_new, v_new, t["U"], t["W"], slots, kc_app, vc_app)
 
-    def timed(fn, n, flushed, kernel_sel=sk.TIME_NONE):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n)]
-        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n)]
-        for a, b in kev:   # materialise the HIP events before handing them over
-            a.record()
-            b.record()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(n):
-            if flushed:
-                do_flush(i)
-            if kernel_sel:
-                sk.set_timing_events(kev[i][0], kev[i][1], kernel_sel)
-            ev[i][0].record(stream)
-            fn()
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        sk.set_timing_events(None, None, sk.TIME_NONE)
-        steps_ms = [a.elapsed_time(b) for a, b in ev]
-        kern_ms = [a.elapsed_time(b) for a, b in kev] if kernel_sel else []
-        return steps_ms, kern_ms, wall
-
     # warmup (untimed)
     for i in range(args.warmup):
         do_flush(i)
@@ -206,21 +296,24 @@ def run_bench(args):
     torch.cuda.synchronize()
 
     # headline: whole steps, cache flushed before each, no events inside the step
-    step_ms, _, wall = timed(step, args.steps, True)
-    # the split-K kernel alone (events recorded around its launch), flushed
-    _, kern_ms, _ = timed(step, args.steps, True, sk.TIME_DECODE_SPLIT)
+    step_ms, _, wall = timed(step, args.steps, do_flush)
+    # the split-K kernel alone (the dispatch's own timestamps), flushed
+    _, kern_ms, _ = timed(step, args.steps, do_flush, sk.TIME_DECODE_SPLIT)
     # warm (latents left in the Infinity Cache), for reference only
-    warm_ms, _, _ = timed(step, args.steps, False)
-    _, warm_kern_ms, _ = timed(step, args.steps, False, sk.TIME_DECODE_SPLIT)
-    app_ms, _, _ = timed(append_step, max(args.steps, 10), True)
-    _, app_kern_ms, _ = timed(append_step, max(args.steps, 10), True, sk.TIME_APPEND)
+    warm_ms, _, _ = timed(step, args.steps)
+    _, warm_kern_ms, _ = timed(step, args.steps, None, sk.TIME_DECODE_SPLIT)
+    app_ms, _, _ = timed(append_step, max(args.steps, 10), do_flush)
+    _, app_kern_ms, _ = timed(append_step, max(args.steps, 10), do_flush, sk.TIME_APPEND)
+    # the step with its append in front (second row)
+    both_ms, _, _ = timed(lambda: (append_step(), step()), args.steps, do_flush)
 
     # measured streaming-read ceiling on this machine: the library's plain
     # 16-byte streaming read over as many bytes as one step's latents, after
     # the same flush
     ceil_buf = torch.ones(lat_bytes, dtype=torch.uint8, device="cuda")
     ceil_sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
-    ceil_ms, _, _ = timed(lambda: sk.stream_read(ceil_buf, ceil_sink), max(args.steps, 10), True)
+    ceil_ms, _, _ = timed(lambda: sk.stream_read(ceil_buf, ceil_sink), max(args.steps, 10),
+                          do_flush)
     ceiling_gbs = lat_bytes / (statistics.fmean(ceil_ms) * 1e-3) / 1e9
     del ceil_buf
 
@@ -255,6 +348,7 @@ def run_bench(args):
         "warm_split_kernel_ms": round(statistics.fmean(warm_kern_ms), 5),
         "append_step_ms": round(statistics.fmean(app_ms), 5),
         "append_kernel_ms": round(statistics.fmean(app_kern_ms), 5),
+        "step_with_append_ms": round(statistics.fmean(both_ms), 5),
         "wall_s_timed_loop_incl_flush": round(wall, 4),
         "split_plan": {"pages_per_split": pps, "num_splits": ns},
         "flush": args.flush,
@@ -271,6 +365,16 @@ def run_bench(args):
             "algorithmic_bytes_per_launch": int(lat_bytes),
         },
     }
+    if not args.no_prefill:
+        del ceil_sink
+        res["prefill"] = prefill_leg(do_flush, args.steps)
+    res["device"] = device_info()
+    if case.name == "decode_b16":
+        # the pages' own decode-step figures for this shape (NVIDIA L4, other
+        # hardware): context only, not a target
+        res["context_l4"] = {"source": "Proxima README, Per-decode-step attention table",
+                             "seq_len": 2048, "batch": 16, "star_kv_ms": 1.735,
+                             "flash_attn2_ms": 2.314, "hardware": "NVIDIA L4"}
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     else:
@@ -287,15 +391,16 @@ def profile_run(args):
     msl = int(case.cache.seq_lens.max())
     dims = sk.dims_of(t["k_cache"], t["v_cache"], t["U"], t["W"])
     ws = sk.alloc_workspace(sk.decode_workspace_size(dims, case.B, msl), "cuda")
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
     for _ in range(max(args.steps, 1)):
-        flush.fill_(1)
+        torch.sum(flush, dim=0, out=sink)   # the benchmark's read flush
         sk.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["U"], t["W"], t["block_tables"],
                        t["seq_lens"], msl, case.scale, workspace=ws)
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(3)
     dst = torch.empty_like(src)
     for _ in range(3):
-        flush.fill_(2)
+        torch.sum(flush, dim=0, out=sink)
         dst.copy_(src)
     torch.cuda.synchronize()
     print(f"profile-run done: {args.steps} steps of {case.name}, 3 copies of {COPY_BYTES} B",
@@ -308,36 +413,54 @@ def _pmc_rows(path):
 
 
 def summarize_pmc(fetch_csv, write_csv, out_path):
-    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the split-K
-    kernel and of the plain copy; scale each by the copy's bytes-per-KiB."""
-    from rank_compressed_paged_amd import metrics, workloads as wl
-    def avg(rows, counter, match):
+    """Average FETCH_SIZE / WRITE_SIZE per dispatch of the split-K kernel and
+    of the COPY_BYTES device copies, and scale the kernel's counts by the
+    bytes each counted unit represents on the copy."""
+    from rank_compressed_paged_amd import metrics
+
+    def per_dispatch(rows, counter, match):
         vals = [float(r["Counter_Value"]) for r in rows
                 if match(r["Kernel_Name"]) and r["Counter_Name"] == counter]
-        return sum(vals) / len(vals) if vals else float("nan"), len(vals)
+        return vals
+
+    def big_copy(rows, counter):
+        vals = per_dispatch(rows, counter, lambda n: "copyBuffer" in n)
+        top = max(vals)
+        big = [v for v in vals if v > 0.5 * top]      # the COPY_BYTES copies
+        return sum(big) / len(big), len(big)
+
     is_split = lambda n: DECODE_KERNEL in n
-    is_copy = lambda n: ("copy" in n.lower() or "elementwise" in n.lower()) and "fill" not in n.lower()
     fr, wr = _pmc_rows(fetch_csv), _pmc_rows(write_csv)
-    f_split, nf = avg(fr, "FETCH_SIZE", is_split)
-    w_split, nw = avg(wr, "WRITE_SIZE", is_split)
-    f_copy, _ = avg(fr, "FETCH_SIZE", is_copy)
-    w_copy, _ = avg(wr, "WRITE_SIZE", is_copy)
-    f_scale = COPY_BYTES / f_copy          # bytes per counted KiB, reads
-    w_scale = COPY_BYTES / w_copy          # bytes per counted KiB, writes
-    case = wl.CONFIGS["decode_b16"]
+    fv = per_dispatch(fr, "FETCH_SIZE", is_split)
+    wv = per_dispatch(wr, "WRITE_SIZE", is_split)
+    f_split, w_split = sum(fv) / len(fv), sum(wv) / len(wv)
+    f_copy, nfc = big_copy(fr, "FETCH_SIZE")
+    w_copy, nwc = big_copy(wr, "WRITE_SIZE")
+    f_scale = COPY_BYTES / f_copy          # bytes per counted unit, reads
+    w_scale = COPY_BYTES / w_copy          # bytes per counted unit, writes
     lat = 16 * 2048 * metrics.latent_bytes_per_token(32, 64, 512)
-    hbm = f_split * f_scale + w_split * w_scale
+    rd, wb = f_split * f_scale, w_split * w_scale
     with open(out_path, "w") as f:
-        f.write("# HBM traffic of the split-K decode kernel, decode_b16 (batch 16 x 2048, H32 d128 r_k64 r_v512)\n")
-        f.write("# FETCH_SIZE and WRITE_SIZE from two rocprofv3 --pmc runs of `bench.py --profile-run`,\n")
-        f.write("# each scaled by the same counter on a plain copy of COPY_BYTES bytes.\n")
+        f.write("# HBM traffic of the split-K decode kernel, decode_b16 "
+                "(batch 16 x 2048 tokens, H32 d128 r_k64 r_v512, 16-token pages)\n")
+        f.write("# FETCH_SIZE and WRITE_SIZE from two rocprofv3 --pmc passes over\n")
+        f.write("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o fetch -- "
+                "python3 bench.py --profile-run --steps 5\n")
+        f.write("#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o write -- "
+                "python3 bench.py --profile-run --steps 5\n")
+        f.write("# each kernel count is scaled by the bytes per counted unit measured on a\n")
+        f.write("# plain device copy of copy_bytes bytes in the same run; written with\n")
+        f.write("#   python3 bench.py --summarize-pmc <fetch csv> <write csv> <this file>\n")
         f.write(f"kernel_source_sha={kernel_source_hash()}\n")
-        f.write(f"dispatches_fetch={nf}\ndispatches_write={nw}\n")
-        f.write(f"fetch_kib_per_dispatch={f_split:.1f}\nwrite_kib_per_dispatch={w_split:.1f}\n")
-        f.write(f"copy_bytes={COPY_BYTES}\ncopy_fetch_kib={f_copy:.1f}\ncopy_write_kib={w_copy:.1f}\n")
-        f.write(f"fetch_scale_bytes_per_kib={f_scale:.2f}\nwrite_scale_bytes_per_kib={w_scale:.2f}\n")
-        f.write(f"hbm_bytes_per_launch={hbm:.0f}\nalgorithmic_bytes_per_launch={lat}\n")
-        f.write(f"traffic_over_algorithmic={hbm / lat:.3f}\n")
+        f.write(f"dispatches_fetch={len(fv)}\ndispatches_write={len(wv)}\n")
+        f.write(f"fetch_units_per_dispatch={f_split:.1f}\nwrite_units_per_dispatch={w_split:.1f}\n")
+        f.write(f"copy_bytes={COPY_BYTES}\ncopy_fetch_units={f_copy:.1f} (over {nfc} copies)\n")
+        f.write(f"copy_write_units={w_copy:.1f} (over {nwc} copies)\n")
+        f.write(f"fetch_bytes_per_unit={f_scale:.2f}\nwrite_bytes_per_unit={w_scale:.2f}\n")
+        f.write(f"hbm_read_bytes_per_launch={rd:.0f}\nhbm_write_bytes_per_launch={wb:.0f}\n")
+        f.write(f"hbm_bytes_per_launch={rd + wb:.0f}\nalgorithmic_bytes_per_launch={lat}\n")
+        f.write(f"read_over_algorithmic={rd / lat:.4f}\n")
+        f.write(f"traffic_over_algorithmic={(rd + wb) / lat:.4f}\n")
     print(open(out_path).read())
 
 

@@ -163,8 +163,9 @@ starkv_status starkv_prefill_attn(const starkv_dims* dims, const void* q,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Profiling aid: record hipEvent_t `start` / `stop` on the call's stream
- * immediately before and after one kernel of later calls.
+ * Profiling aid: time one kernel of later calls with the hipEvent_t pair
+ * `start` / `stop`.  The kernel is launched with hipExtLaunchKernelGGL, which
+ * binds the two events to that dispatch.
  *   which = 0 none (clears), 1 decode split-K attention, 2 prefill attention,
  *   3 append.  Events are owned by the caller and must outlive the calls.
  * Process-wide setting; not for concurrent use from several threads.
@@ -184,6 +185,22 @@ starkv_status starkv_decode_plan(const starkv_dims* dims, int32_t batch, int32_t
  * least 1024 uint32 that may be written.  Asynchronous on `stream`.
  */
 starkv_status starkv_util_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+
+/*
+ * Measurement utilities (not part of the attention path): a timing event
+ * created with hipEventDisableSystemFence, so recording it adds no
+ * system-scope cache write-back to the timed work and its timestamps match a
+ * kernel trace; for use with starkv_set_timing_events.  Such an event does
+ * not make device writes visible to the host: synchronise the device before
+ * reading results or elapsed times.
+ *   starkv_util_event_create      *event (host out) receives a hipEvent_t
+ *   starkv_util_event_destroy     NULL is a no-op
+ *   starkv_util_event_elapsed_ms  *ms (host out) = stop - start, both recorded
+ *                                 and complete (hipEventElapsedTime)
+ */
+starkv_status starkv_util_event_create(void** event /* (host) */);
+starkv_status starkv_util_event_destroy(void* event);
+starkv_status starkv_util_event_elapsed_ms(void* start, void* stop, float* ms /* (host) */);
 
 #ifdef __cplusplus
 }

@@ -303,4 +303,25 @@ starkv_status starkv_set_timing_events(void* start, void* stop, int32_t which) {
   return STARKV_OK;
 }
 
+starkv_status starkv_util_event_create(void** event) {
+  if (!event) return STARKV_ERR_NULL;
+  *event = nullptr;
+  hipEvent_t e = nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return STARKV_ERR_LAUNCH;
+  *event = (void*)e;
+  return STARKV_OK;
+}
+
+starkv_status starkv_util_event_destroy(void* event) {
+  if (!event) return STARKV_OK;
+  return hipEventDestroy((hipEvent_t)event) == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
+}
+
+starkv_status starkv_util_event_elapsed_ms(void* start, void* stop, float* ms) {
+  if (!start || !stop || !ms) return STARKV_ERR_NULL;
+  return hipEventElapsedTime(ms, (hipEvent_t)start, (hipEvent_t)stop) == hipSuccess
+             ? STARKV_OK
+             : STARKV_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -167,9 +167,7 @@ hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const 
   a.v_tiles_n = (s.rv + AT_N - 1) / AT_N;
   a.k_tiles_n = (s.rk + AT_N - 1) / AT_N;
   const long jobs = (long)a.tiles_m * (a.v_tiles_n + (long)s.H * a.k_tiles_n);
-  if (g_timing.which == TIME_APPEND && g_timing.start) hipEventRecord(g_timing.start, st);
-  hipLaunchKernelGGL(append_kernel, dim3((unsigned)jobs), dim3(256), 0, st, a);
-  if (g_timing.which == TIME_APPEND && g_timing.stop) hipEventRecord(g_timing.stop, st);
+  launch_hooked(TIME_APPEND, append_kernel, dim3((unsigned)jobs), dim3(256), st, a);
   return hipGetLastError();
 }
 

@@ -554,13 +554,10 @@ static hipError_t decode_instance(const DecodePlan& p, const void* qt, const voi
                                   int max_blocks, const int32_t* seq_lens, int num_blocks,
                                   int batch, float* ml, float* acc, float* z, void* out,
                                   hipStream_t st) {
-  if (g_timing.which == TIME_DECODE_SPLIT && g_timing.start) hipEventRecord(g_timing.start, st);
-  hipLaunchKernelGGL((decode_split_kernel<H, RK, RV, NW, DEPTH, NT>), dim3(p.num_splits, batch),
-                     dim3(NW * 64),
-                     0, st, (const half_t*)qt, (const half_t*)k_cache, (const half_t*)v_cache,
-                     block_tables, seq_lens, ml, acc, max_blocks, num_blocks, p.pages_per_split,
-                     p.num_splits);
-  if (g_timing.which == TIME_DECODE_SPLIT && g_timing.stop) hipEventRecord(g_timing.stop, st);
+  launch_hooked(TIME_DECODE_SPLIT, decode_split_kernel<H, RK, RV, NW, DEPTH, NT>,
+                dim3(p.num_splits, batch), dim3(NW * 64), st, (const half_t*)qt,
+                (const half_t*)k_cache, (const half_t*)v_cache, block_tables, seq_lens, ml, acc,
+                max_blocks, num_blocks, p.pages_per_split, p.num_splits);
   const long threads = (long)batch * H * (RV / 4);
   hipLaunchKernelGGL((combine_kernel<H, RV>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                      st, (const float*)ml, (const float*)acc, seq_lens, batch, max_blocks,

@@ -2,6 +2,7 @@
 // Nothing here is exported from the shared library.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -42,6 +43,18 @@ struct TimingHook {
 };
 extern TimingHook g_timing;
 enum { TIME_NONE = 0, TIME_DECODE_SPLIT = 1, TIME_PREFILL_ATTN = 2, TIME_APPEND = 3 };
+
+// Launch `kernel` on `st`.  When the timing hook selects `which`, the launch
+// goes through hipExtLaunchKernelGGL so that the hook's two events carry the
+// dispatch's own begin and end timestamps (no event packets around it).
+template <typename... KArgs, typename... Args>
+inline void launch_hooked(int which, void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                          hipStream_t st, Args... args) {
+  if (g_timing.which == which && g_timing.start && g_timing.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, g_timing.start, g_timing.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
 
 hipError_t launch_qproj(const ShapeKey& s, const void* q, const void* U, int n_tokens,
                         float scale, void* qt, hipStream_t st);

@@ -251,10 +251,8 @@ static hipError_t prefill_instance(const void* qt, const int32_t* qsl, int max_q
   a.n_qtiles = (max_query_len + MQ - 1) / MQ;
   a.n_groups = H / G;
   const long wgs = (long)batch * a.n_qtiles * a.n_groups;
-  if (g_timing.which == TIME_PREFILL_ATTN && g_timing.start) hipEventRecord(g_timing.start, st);
-  hipLaunchKernelGGL((prefill_attn_kernel<H, RK, RV, G, MQ, NW>), dim3((unsigned)wgs),
-                     dim3(NW * 64), 0, st, a);
-  if (g_timing.which == TIME_PREFILL_ATTN && g_timing.stop) hipEventRecord(g_timing.stop, st);
+  launch_hooked(TIME_PREFILL_ATTN, prefill_attn_kernel<H, RK, RV, G, MQ, NW>, dim3((unsigned)wgs),
+                dim3(NW * 64), st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_upproj(ShapeKey{H, D, RK, RV}, W, z, total_q, true, out, st);

@@ -32,7 +32,8 @@ EXPORTED = [
     "starkv_abi_version", "starkv_status_string", "starkv_shape_supported", "starkv_append",
     "starkv_decode_workspace_size", "starkv_decode_attn", "starkv_prefill_workspace_size",
     "starkv_prefill_attn", "starkv_set_timing_events", "starkv_decode_plan",
-    "starkv_util_stream_read",
+    "starkv_util_stream_read", "starkv_util_event_create", "starkv_util_event_destroy",
+    "starkv_util_event_elapsed_ms",
 ]
 
 
@@ -77,6 +78,12 @@ _lib.starkv_prefill_attn.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _i32, _i32,
                                      _sz, _vp]
 _lib.starkv_util_stream_read.restype = _i32
 _lib.starkv_util_stream_read.argtypes = [_vp, _sz, _vp, _vp]
+_lib.starkv_util_event_create.restype = _i32
+_lib.starkv_util_event_create.argtypes = [ctypes.POINTER(_vp)]
+_lib.starkv_util_event_destroy.restype = _i32
+_lib.starkv_util_event_destroy.argtypes = [_vp]
+_lib.starkv_util_event_elapsed_ms.restype = _i32
+_lib.starkv_util_event_elapsed_ms.argtypes = [_vp, _vp, ctypes.POINTER(ctypes.c_float)]
 _lib.starkv_set_timing_events.restype = _i32
 _lib.starkv_set_timing_events.argtypes = [_vp, _vp, _i32]
 
@@ -229,10 +236,37 @@ def stream_read(buf, sink, stream=None):
            "starkv_util_stream_read")
 
 
+class TimingEvent:
+    """A library timing event (no system-scope fence when recorded)."""
+
+    def __init__(self):
+        h = _vp(None)
+        _check(_lib.starkv_util_event_create(ctypes.byref(h)), "starkv_util_event_create")
+        self.handle = h
+
+    def elapsed_ms(self, stop):
+        """Milliseconds from this event to `stop`; synchronise the device first."""
+        ms = ctypes.c_float(0.0)
+        _check(_lib.starkv_util_event_elapsed_ms(self.handle, stop.handle, ctypes.byref(ms)),
+               "starkv_util_event_elapsed_ms")
+        return float(ms.value)
+
+    def __del__(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            _lib.starkv_util_event_destroy(self.handle)
+            self.handle = None
+
+
+def _event_handle(ev):
+    if isinstance(ev, TimingEvent):
+        return ev.handle
+    return _vp(ev.cuda_event)      # a torch.cuda.Event
+
+
 def set_timing_events(start_event, stop_event, which):
-    """Record torch.cuda.Event objects around one kernel of later calls."""
+    """Time one kernel of later calls with two TimingEvent (or torch.cuda.Event)."""
     if which == TIME_NONE:
         _check(_lib.starkv_set_timing_events(None, None, 0), "starkv_set_timing_events")
         return
-    _check(_lib.starkv_set_timing_events(_vp(start_event.cuda_event), _vp(stop_event.cuda_event),
+    _check(_lib.starkv_set_timing_events(_event_handle(start_event), _event_handle(stop_event),
                                          int(which)), "starkv_set_timing_events")
