@@ -45,14 +45,22 @@ FLUSH_BYTES = 512 << 20        # > 2x the 256 MB Infinity Cache
 COPY_BYTES = 256 << 20         # plain copy used to calibrate the HBM counters
 DECODE_KERNEL = "decode_split_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_decode_b16_traffic.txt")
-KERNEL_SOURCES = ["rank_compressed_paged_amd/csrc/decode.hip", "rank_compressed_paged_amd/csrc/common.h"]
+TRAFFIC_WORKLOAD = "decode_b16"
+SPLIT_SECTION = ("// 2. split-K latent attention", "// 3. combine")
 
 
 def kernel_source_hash():
+    """Hash of the split-K kernel's device code (its section of decode.hip)
+    and of the shared device helpers: the traffic summary is only used while
+    this matches the code the counters were taken on."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    csrc = os.path.join(ROOT, "rank_compressed_paged_amd", "csrc")
+    with open(os.path.join(csrc, "decode.hip")) as f:
+        text = f.read()
+    a, b = text.index(SPLIT_SECTION[0]), text.index(SPLIT_SECTION[1])
+    h.update(text[a:b].encode())
+    with open(os.path.join(csrc, "common.h"), "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -321,7 +329,8 @@ def run_bench(args):
     kern = statistics.fmean(kern_ms)
     value = lat_bytes / (ms * 1e-3) / 1e9
     achieved = lat_bytes / (kern * 1e-3) / 1e9
-    traffic = read_traffic(lat_bytes)
+    # the counter summary covers the decode_b16 launch only
+    traffic = read_traffic(lat_bytes) if case.name == TRAFFIC_WORKLOAD else None
     q = lambda xs, p: sorted(xs)[min(len(xs) - 1, int(round(p * (len(xs) - 1))))]
     res = {
         "metric": METRIC,

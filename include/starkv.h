@@ -164,8 +164,12 @@ starkv_status starkv_prefill_attn(const starkv_dims* dims, const void* q,
 
 /*
  * Profiling aid: time one kernel of later calls with the hipEvent_t pair
- * `start` / `stop`.  The kernel is launched with hipExtLaunchKernelGGL, which
- * binds the two events to that dispatch.
+ * `start` / `stop`.  `stop` is bound to the selected kernel's dispatch and
+ * `start` to the dispatch just before it in the same call (the q projection),
+ * both through hipExtLaunchKernelGGL, so the elapsed time runs from the end
+ * of that predecessor to the end of the selected kernel with nothing
+ * enqueued between them.  Append has no predecessor: `start` is recorded on
+ * the stream just before its launch.
  *   which = 0 none (clears), 1 decode split-K attention, 2 prefill attention,
  *   3 append.  Events are owned by the caller and must outlive the calls.
  * Process-wide setting; not for concurrent use from several threads.

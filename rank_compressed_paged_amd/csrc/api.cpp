@@ -234,7 +234,7 @@ starkv_status starkv_decode_attn(const starkv_dims* dims, const void* q, const v
   if (workspace_bytes < ws.total) return STARKV_ERR_WORKSPACE;
   char* wb = (char*)workspace;
   const hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_qproj(key, q, U, batch, scale, wb + ws.qt_off, s);
+  hipError_t e = launch_qproj(key, q, U, batch, scale, wb + ws.qt_off, TIME_DECODE_SPLIT, s);
   if (e != hipSuccess) return STARKV_ERR_LAUNCH;
   e = launch_decode(key, p, wb + ws.qt_off, k_cache, v_cache, W, block_tables,
                     max_blocks_per_seq, seq_lens, dims->num_blocks, batch,
@@ -278,7 +278,7 @@ starkv_status starkv_prefill_attn(const starkv_dims* dims, const void* q,
   if (workspace_bytes < ws.total) return STARKV_ERR_WORKSPACE;
   char* wb = (char*)workspace;
   const hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_qproj(key, q, U, total_q, scale, wb + ws.qt_off, s);
+  hipError_t e = launch_qproj(key, q, U, total_q, scale, wb + ws.qt_off, TIME_PREFILL_ATTN, s);
   if (e != hipSuccess) return STARKV_ERR_LAUNCH;
   e = launch_prefill(key, wb + ws.qt_off, query_start_loc, total_q, max_query_len, k_cache,
                      v_cache, W, block_tables, max_blocks_per_seq, seq_lens, dims->num_blocks,

@@ -167,7 +167,9 @@ hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const 
   a.v_tiles_n = (s.rv + AT_N - 1) / AT_N;
   a.k_tiles_n = (s.rk + AT_N - 1) / AT_N;
   const long jobs = (long)a.tiles_m * (a.v_tiles_n + (long)s.H * a.k_tiles_n);
-  launch_hooked(TIME_APPEND, append_kernel, dim3((unsigned)jobs), dim3(256), st, a);
+  // a single launch: the start event is recorded on the stream just before it
+  if (g_timing.which == TIME_APPEND && g_timing.start) hipEventRecord(g_timing.start, st);
+  launch_hooked(TIME_APPEND, TIME_NONE, append_kernel, dim3((unsigned)jobs), dim3(256), st, a);
   return hipGetLastError();
 }
 

@@ -554,7 +554,7 @@ static hipError_t decode_instance(const DecodePlan& p, const void* qt, const voi
                                   int max_blocks, const int32_t* seq_lens, int num_blocks,
                                   int batch, float* ml, float* acc, float* z, void* out,
                                   hipStream_t st) {
-  launch_hooked(TIME_DECODE_SPLIT, decode_split_kernel<H, RK, RV, NW, DEPTH, NT>,
+  launch_hooked(TIME_DECODE_SPLIT, TIME_NONE, decode_split_kernel<H, RK, RV, NW, DEPTH, NT>,
                 dim3(p.num_splits, batch), dim3(NW * 64), st, (const half_t*)qt,
                 (const half_t*)k_cache, (const half_t*)v_cache, block_tables, seq_lens, ml, acc,
                 max_blocks, num_blocks, p.pages_per_split, p.num_splits);
@@ -569,17 +569,19 @@ static hipError_t decode_instance(const DecodePlan& p, const void* qt, const voi
 
 template <int H, int D, int RK>
 static hipError_t qproj_instance(const void* q, const void* U, int n, float scale, void* qt,
-                                 hipStream_t st) {
-  hipLaunchKernelGGL((qproj_kernel<H, D, RK>), dim3(H, (n + 63) / 64), dim3(256), 0, st,
-                     (const half_t*)q, (const half_t*)U, n, scale * kLog2e, (half_t*)qt);
+                                 int precedes, hipStream_t st) {
+  launch_hooked(TIME_NONE, precedes, qproj_kernel<H, D, RK>, dim3(H, (n + 63) / 64), dim3(256), st,
+                (const half_t*)q, (const half_t*)U, n, scale * kLog2e, (half_t*)qt);
   return hipGetLastError();
 }
 
 hipError_t launch_qproj(const ShapeKey& s, const void* q, const void* U, int n_tokens, float scale,
-                        void* qt, hipStream_t st) {
+                        void* qt, int precedes, hipStream_t st) {
   if (n_tokens <= 0) return hipSuccess;
-  if (s.H == 32 && s.d == 128 && s.rk == 64) return qproj_instance<32, 128, 64>(q, U, n_tokens, scale, qt, st);
-  if (s.H == 4 && s.d == 64 && s.rk == 16) return qproj_instance<4, 64, 16>(q, U, n_tokens, scale, qt, st);
+  if (s.H == 32 && s.d == 128 && s.rk == 64)
+    return qproj_instance<32, 128, 64>(q, U, n_tokens, scale, qt, precedes, st);
+  if (s.H == 4 && s.d == 64 && s.rk == 16)
+    return qproj_instance<4, 64, 16>(q, U, n_tokens, scale, qt, precedes, st);
   return hipErrorInvalidValue;
 }
 

@@ -44,20 +44,31 @@ struct TimingHook {
 extern TimingHook g_timing;
 enum { TIME_NONE = 0, TIME_DECODE_SPLIT = 1, TIME_PREFILL_ATTN = 2, TIME_APPEND = 3 };
 
-// Launch `kernel` on `st`.  When the timing hook selects `which`, the launch
-// goes through hipExtLaunchKernelGGL so that the hook's two events carry the
-// dispatch's own begin and end timestamps (no event packets around it).
+// Launch `kernel` on `st`.  Timing hook: when the hook selects `which`, its
+// stop event is bound to this dispatch (hipExtLaunchKernelGGL), so it takes
+// the dispatch's end timestamp; when it selects `precedes` (the kernel this
+// launch comes immediately before in the same call), its start event is bound
+// to this dispatch instead.  The timed span is then end-of-predecessor to
+// end-of-kernel with no event packets between the two dispatches.
 template <typename... KArgs, typename... Args>
-inline void launch_hooked(int which, void (*kernel)(KArgs...), dim3 grid, dim3 block,
-                          hipStream_t st, Args... args) {
-  if (g_timing.which == which && g_timing.start && g_timing.stop)
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, g_timing.start, g_timing.stop, 0, args...);
+inline void launch_hooked(int which, int precedes, void (*kernel)(KArgs...), dim3 grid,
+                          dim3 block, hipStream_t st, Args... args) {
+  hipEvent_t ev = nullptr;
+  if (g_timing.start && g_timing.stop) {
+    if (g_timing.which == which)
+      ev = g_timing.stop;
+    else if (precedes != TIME_NONE && g_timing.which == precedes)
+      ev = g_timing.start;
+  }
+  if (ev)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, nullptr, ev, 0, args...);
   else
     hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
 }
 
+// `precedes`: the hooked kernel that follows this launch in the call.
 hipError_t launch_qproj(const ShapeKey& s, const void* q, const void* U, int n_tokens,
-                        float scale, void* qt, hipStream_t st);
+                        float scale, void* qt, int precedes, hipStream_t st);
 
 hipError_t launch_decode(const ShapeKey& s, const DecodePlan& p, const void* qt,
                          const void* k_cache, const void* v_cache, const void* W,

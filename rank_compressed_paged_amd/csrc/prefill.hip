@@ -251,7 +251,7 @@ static hipError_t prefill_instance(const void* qt, const int32_t* qsl, int max_q
   a.n_qtiles = (max_query_len + MQ - 1) / MQ;
   a.n_groups = H / G;
   const long wgs = (long)batch * a.n_qtiles * a.n_groups;
-  launch_hooked(TIME_PREFILL_ATTN, prefill_attn_kernel<H, RK, RV, G, MQ, NW>, dim3((unsigned)wgs),
+  launch_hooked(TIME_PREFILL_ATTN, TIME_NONE, prefill_attn_kernel<H, RK, RV, G, MQ, NW>, dim3((unsigned)wgs),
                 dim3(NW * 64), st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
