@@ -10,35 +10,82 @@
 // and writes z [total_q, H, r_v] fp32; the up-projection out_h = W_h z_h
 // runs afterwards on the matrix cores (decode.hip, wide tiling).
 //
-// Work group = (request, tile of MQ queries, group of G heads), NW waves.
-// Rows of the attention tile are (head, query) pairs, R = G*MQ of them.
-//   * scores: wave w owns one (head, 16-query block); per page it runs
-//     v_mfma_f32_16x16x32_f16 with the 16x64 key page as A and the queries'
-//     q~ as B, giving tokens x queries, then the online-softmax update of its
-//     16 queries (lane = query, 4 tokens per lane, 4-lane butterfly).
-//   * P and the rescale factors pass through LDS (double-buffered).
-//   * values: wave w owns RV/NW features for all R rows,
-//     Z^T[f, row] += c_v[t, f] P[row, t] with v_mfma_f32_16x16x16_f16; the
-//     accumulator column is the row, so rescaling is per lane and is skipped
-//     for pages where no running max moved.
+// Work group = (request, tile of MQ queries, group of G heads), NW waves;
+// the main shape runs G = 2 heads x MQ = 64 queries = 128 (head, query) rows
+// with 8 waves, two 16-token pages per step.
+//   * scores: a score unit is one (head, 16-query block); per page it is
+//     v_mfma_f32_16x16x32_f16 with the 16 x r_k key page as A and the
+//     queries' q~ as B (tokens x queries), then the online-softmax update of
+//     its 16 queries (lane = query, 4 tokens per page per lane; the max and
+//     sum across the four lanes of a query use the cross-row lane swaps).
+//   * values: wave w owns RV/NW features for all rows.  Per page,
+//     Z^T[f, row] += c_v[t, f] P[row, t] is v_mfma_f32_32x32x16_f16 with the
+//     feature-major value page as A (16 contiguous bytes per lane) and P as B
+//     (read from LDS, where it is stored in exactly that operand order); the
+//     accumulator column is the row, so rescaling is per lane.
+//   * lazy rescaling: a row's reference max only moves when a step's max
+//     exceeds it by more than 2^kRaise (log2 domain), so P <= 2^kRaise stays
+//     well inside fp16 and the accumulators are rescaled on few steps.  The
+//     softmax is invariant to the reference, so this is exact math.
+//   * software pipeline: step s runs the scores and softmax of step s+1
+//     beside the P.c_v products of step s (the softmax's vector instructions
+//     interleaved between the products), while the keys of step s+2 and the
+//     values of step s+1 load into a register ring; one LDS-only barrier per
+//     step.
+//   * masks (causal limit, sequence end, invalid block ids) only on the
+//     steps that need them.
+//   * block ids stream through a 2*kChunk-entry LDS ring, a few new entries
+//     per step, so no block-table load sits on the critical path.
 //   * work groups of one request are placed on one XCD when the batch is a
 //     multiple of 8, so the request's latents are shared through that L2.
+#include <stdlib.h>
+
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace starkv {
 
+// v_mfma_f32_32x32x16_f16: lane l holds A[l%32][8*(l/32) + 0..7] and
+// B[8*(l/32) + 0..7][l%32]; the 32x32 fp32 result has
+// D[8*(i/4) + 4*(l/32) + i%4][l%32] in register i (i = 0..15).
+typedef float float16v __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ float16v mfma32x32x16(half8 a, half8 b, float16v c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Reductions over the four lanes l, l^16, l^32, l^48 (the four 4-token
+// slices of one query's scores) with the cross-row lane swaps, which stay in
+// the vector ALU instead of going through LDS.  With both operands equal,
+// permlane16_swap leaves lane l of one result and lane l^16 of the other
+// holding x[l] and x[l^16]; permlane32_swap does the same for l^32.
+__device__ __forceinline__ float quad_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int H, int RK, int RV, int G, int MQ, int NW>
 struct PrefillCfg {
-  static constexpr int R = G * MQ;
-  static constexpr int RT = R / 16;
-  static constexpr int QB = MQ / 16;
-  static constexpr int FPW = RV / NW;
-  static constexpr int FT = FPW / 16;
+  static constexpr int R = G * MQ;           // (head, query) rows
+  static constexpr int RT = R / 32;          // 32-row tiles
+  static constexpr int QB = MQ / 16;         // 16-query blocks per head
+  static constexpr int SU = G * QB;          // score units
+  static constexpr int SUW = SU / NW;        // score units per wave
+  static constexpr int FTW = RV / 32 / NW;   // 32-feature tiles per wave
   static constexpr int KC = (RK % 32 == 0) ? 32 : 16;
   static constexpr int NKC = RK / KC;
-  static_assert(MQ % 16 == 0 && G * QB == NW, "one (head, 16-query) score unit per wave");
-  static_assert(RV % (16 * NW) == 0, "value rank must split into 16-wide tiles per wave");
+  static_assert(R % 32 == 0 && MQ % 16 == 0, "rows must tile by 32, queries by 16");
+  static_assert(SU % NW == 0 && SUW >= 1, "score units must spread evenly over the waves");
+  static_assert(RV % (32 * NW) == 0 && FTW >= 1, "value rank must split into 32-wide tiles");
   static_assert(H % G == 0, "head groups must tile the heads");
 };
 
@@ -53,16 +100,32 @@ struct PrefillArgs {
   int max_blocks, num_blocks, batch, n_qtiles, n_groups;
 };
 
-constexpr int PBS = 16;
+constexpr int PBS = 16;                 // tokens per page
+constexpr int kChunk = 64;              // block-id ring: 2 * kChunk entries
+constexpr float kRaise = 8.f;           // lazy-rescale threshold (log2 units)
 
-template <int H, int RK, int RV, int G, int MQ, int NW>
+// Template knobs (tuning aids):
+//   PPS    pages per step: one LDS barrier, one block-id read and one
+//          rescale check per PPS pages
+//   DEPTH  steps of page operands held in the register ring (2 or 3)
+//   SCHED  instruction order inside a step: 0 left to the compiler, 1 score
+//          products, then the P.c_v products, then the softmax, 2 as 1 with
+//          the softmax's vector instructions interleaved between the products
+template <int H, int RK, int RV, int G, int MQ, int NW, int PPS, int DEPTH, int SCHED>
 __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
+  static_assert(DEPTH >= 2 && DEPTH <= 3, "register ring of 2 or 3 steps");
+  static_assert(PPS == 1 || PPS == 2, "one or two pages per step");
   using C = PrefillCfg<H, RK, RV, G, MQ, NW>;
   typedef _Float16 kvec __attribute__((ext_vector_type(C::KC / 4)));
-  __shared__ __attribute__((aligned(16))) half_t sP[2][C::R][PBS];
-  __shared__ float sAlpha[2][C::R];
+  constexpr int RING = 2 * kChunk;
+  constexpr int TPS = PPS * PBS;  // tokens per step
+  // P in the B-operand order of the 32x32x16 product:
+  // [buffer][page of the step][row tile][token half][row % 32][8 tokens]
+  __shared__ __attribute__((aligned(16))) half_t sP[2][PPS][C::RT][2][32][8];
+  // rescale factor of row rt*32 + r at sAlpha[buffer][r][rt]
+  __shared__ __attribute__((aligned(16))) float sAlpha[2][32][C::RT];
   __shared__ float sL[C::R];
-  __shared__ int sFlag[2];
+  __shared__ __attribute__((aligned(16))) int sBlk[RING];
 
   // ---- work decode (XCD-aware when the batch allows it)
   const int units = a.n_qtiles * a.n_groups;
@@ -80,158 +143,336 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   const int q_begin = a.qsl[b];
   const int Cn = a.qsl[b + 1] - q_begin;
   const int j0 = qtile * MQ;
-  if (j0 >= Cn) return;
+  if (j0 >= Cn) return;  // whole work group, before any barrier
   const int L = a.seq_lens[b];
   const int P0 = L - Cn;
   const int last_key = min(L - 1, P0 + min(j0 + MQ, Cn) - 1);
   const int n_pages = min(last_key / PBS + 1, a.max_blocks);
+  const int n_steps = (n_pages + PPS - 1) / PPS;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
-  const int col = lane & 15, quad = lane >> 4;
-  const int hl = w / C::QB, qb = w % C::QB;
-  const int h = g * G + hl;
-  const int jq = min(j0 + qb * 16 + col, Cn - 1);  // rows past the chunk mirror its last query
-  const int qpos = P0 + jq;
-  const int row = hl * MQ + qb * 16 + col;
+  const int col = lane & 15, quad = lane >> 4;   // 16x16 layouts
+  const int c32 = lane & 31, hf = lane >> 5;     // 32x32 layouts
+  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
 
-  if (tid < 2) sFlag[tid] = -1;
+  // block id of a page (pages past the tile's range repeat its last page;
+  // ids outside the cache read as -1)
+  auto fetch_block = [&](int page) {
+    const int v = bt[min(page, n_pages - 1)];
+    return ((unsigned)v < (unsigned)a.num_blocks) ? v : -1;
+  };
+  if (tid < RING) sBlk[tid] = fetch_block(tid);
 
-  kvec qv[C::NKC];
-  {
-    const half_t* qp = a.qt + ((size_t)(q_begin + jq) * H + h) * RK + quad * (C::KC / 4);
+  // ---- this wave's score units: (head, 16 queries); lane column = query
+  int su_h[C::SUW], su_row[C::SUW], su_lim[C::SUW];
+  kvec qv[C::SUW][C::NKC];
 #pragma unroll
-    for (int c = 0; c < C::NKC; ++c) qv[c] = *(const kvec*)(qp + c * C::KC);
+  for (int i = 0; i < C::SUW; ++i) {
+    const int unit = w * C::SUW + i;
+    const int hl = unit / C::QB, qb = unit % C::QB;
+    const int jq = min(j0 + qb * 16 + col, Cn - 1);  // rows past the chunk mirror its last query
+    su_h[i] = g * G + hl;
+    su_row[i] = hl * MQ + qb * 16 + col;
+    su_lim[i] = min(L - 1, P0 + jq);                 // last visible key
+    const half_t* qp = a.qt + ((size_t)(q_begin + jq) * H + su_h[i]) * RK + quad * (C::KC / 4);
+#pragma unroll
+    for (int c = 0; c < C::NKC; ++c) qv[i][c] = *(const kvec*)(qp + c * C::KC);
   }
+  float m_run[C::SUW], l_run[C::SUW];
+#pragma unroll
+  for (int i = 0; i < C::SUW; ++i) {
+    m_run[i] = -INFINITY;
+    l_run[i] = 0.f;
+  }
+  const int lim_min = min(L - 1, P0 + j0);  // last key the tile's first query sees
 
-  float m_run = -INFINITY, l_run = 0.f;
-  float4v acc[C::RT][C::FT];
+  float16v acc[C::RT][C::FTW];
 #pragma unroll
   for (int rt = 0; rt < C::RT; ++rt)
 #pragma unroll
-    for (int ft = 0; ft < C::FT; ++ft) acc[rt][ft] = zero4();
+    for (int ft = 0; ft < C::FTW; ++ft)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[rt][ft][e] = 0.f;
 
-  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
-  const half_t* kbase = a.k_cache + ((size_t)h * PBS + col) * RK + quad * (C::KC / 4);
-  const half_t* vbase = a.v_cache + (size_t)(w * C::FPW + col) * PBS + quad * 4;
-  struct Regs {
-    kvec k[C::NKC];
-    half4 v[C::FT];
+  typedef kvec KSet[PPS][C::SUW][C::NKC];
+  typedef half8 VSet[PPS][C::FTW];
+  KSet kr[DEPTH];  // ring of page operands in registers
+  VSet vr[DEPTH];
+  const int f_base = w * C::FTW * 32 + c32;  // feature of this lane in tile 0
+  // per-lane element offsets inside one page (the page base is uniform, so
+  // the loads take a scalar base plus a 32-bit vector offset)
+  int k_off[C::SUW];
+#pragma unroll
+  for (int i = 0; i < C::SUW; ++i) k_off[i] = (su_h[i] * PBS + col) * RK + quad * (C::KC / 4);
+  const int v_off = f_base * PBS + hf * 8;
+
+  auto block_of = [&](int page) {
+    return __builtin_amdgcn_readfirstlane(sBlk[page & (RING - 1)]);
   };
-  auto safe_block = [&](int p) {
-    const int blk = bt[p];
-    return ((unsigned)blk < (unsigned)a.num_blocks) ? blk : -1;
-  };
-  auto load = [&](Regs& r, int blk) {
-    const half_t* kp = kbase + (size_t)blk * H * PBS * RK;
+  auto load_k = [&](KSet& dst, int step) {
 #pragma unroll
-    for (int c = 0; c < C::NKC; ++c) r.k[c] = *(const kvec*)(kp + c * C::KC);
-    const half_t* vp = vbase + (size_t)blk * RV * PBS;
+    for (int pg = 0; pg < PPS; ++pg) {
+      const int blk = block_of(step * PPS + pg);
+      const half_t* kp = a.k_cache + (size_t)(blk < 0 ? 0 : blk) * (H * PBS * RK);
 #pragma unroll
-    for (int ft = 0; ft < C::FT; ++ft) r.v[ft] = *(const half4*)(vp + (size_t)ft * 16 * PBS);
-  };
-  // one page: scores of this wave's (head, 16 queries), online softmax, P via
-  // LDS, then every wave's value slice for all rows
-  auto process = [&](Regs& r, int p, int buf, bool ok) {
-    if (ok) {
-      float4v sacc = zero4();
+      for (int i = 0; i < C::SUW; ++i)
 #pragma unroll
-      for (int c = 0; c < C::NKC; ++c) {
-        if constexpr (C::KC == 32)
-          sacc = mfma16x16x32(r.k[c], qv[c], sacc);
-        else
-          sacc = mfma16x16x16(r.k[c], qv[c], sacc);
-      }
-      float sv[4];
-      float pm = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = p * PBS + quad * 4 + e;
-        sv[e] = (t < L && t <= qpos) ? sacc[e] : -INFINITY;
-        pm = fmaxf(pm, sv[e]);
-      }
-      pm = max_over_quads(pm);
-      // m_new is finite from the first page on: key 0 is visible to every query
-      const float m_new = fmaxf(m_run, pm);
-      const float alpha = exp2f(m_run - m_new);
-      float ps = 0.f;
-      half4 ph;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float pr = exp2f(sv[e] - m_new);
-        ps += pr;
-        ph[e] = (half_t)pr;
-      }
-      ps = sum_over_quads(ps);
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-      *(half4*)&sP[buf][row][quad * 4] = ph;
-      if (quad == 0) sAlpha[buf][row] = alpha;
-      if (alpha != 1.f) sFlag[buf] = p;
+        for (int c = 0; c < C::NKC; ++c) dst[pg][i][c] = *(const kvec*)(kp + k_off[i] + c * C::KC);
     }
-    block_sync_lds();
-    if (ok) {
-      const bool rescale = sFlag[buf] == p;
-      const int valid = min(PBS, L - p * PBS);
-      if (valid < PBS) {  // slots past the sequence may hold anything (NaN)
+  };
+  auto load_v = [&](VSet& dst, int step) {
 #pragma unroll
-        for (int ft = 0; ft < C::FT; ++ft)
+    for (int pg = 0; pg < PPS; ++pg) {
+      const int blk = block_of(step * PPS + pg);
+      const half_t* vp = a.v_cache + (size_t)(blk < 0 ? 0 : blk) * (RV * PBS);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (quad * 4 + e >= valid) r.v[ft][e] = (half_t)0.f;
+      for (int ft = 0; ft < C::FTW; ++ft)
+        dst[pg][ft] = *(const half8*)(vp + v_off + ft * 32 * PBS);
+    }
+  };
+
+  auto score_products = [&](const KSet& kk, float4v (&sacc)[PPS][C::SUW]) {
+#pragma unroll
+    for (int pg = 0; pg < PPS; ++pg)
+#pragma unroll
+      for (int i = 0; i < C::SUW; ++i) {
+        sacc[pg][i] = zero4();
+#pragma unroll
+        for (int c = 0; c < C::NKC; ++c) {
+          if constexpr (C::KC == 32)
+            sacc[pg][i] = mfma16x16x32(kk[pg][i][c], qv[i][c], sacc[pg][i]);
+          else
+            sacc[pg][i] = mfma16x16x16(kk[pg][i][c], qv[i][c], sacc[pg][i]);
+        }
       }
+  };
+  // online softmax of step s's tokens; P and the rescale factors go to LDS
+  // buffer `buf`.  A row's reference max moves only when the step's max
+  // exceeds it by more than kRaise.  `mask`: some token of the step is not
+  // visible to some row of the tile, or a page of the step is invalid.
+  // BRANCHFREE applies the masks with selects on every step (blk_ok: the
+  // step's pages have valid block ids), so the softmax forms one basic block
+  // with the products it is interleaved with.
+  auto softmax = [&](auto branchfree, bool mask, const bool (&blk_ok)[PPS],
+                     const float4v (&sacc)[PPS][C::SUW], int s, int buf) {
+    constexpr bool BRANCHFREE = decltype(branchfree)::value;
+#pragma unroll
+    for (int i = 0; i < C::SUW; ++i) {
+      float sv[PPS][4];
+#pragma unroll
+      for (int pg = 0; pg < PPS; ++pg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[pg][e] = sacc[pg][i][e];
+      auto apply_masks = [&]() {
+#pragma unroll
+        for (int pg = 0; pg < PPS; ++pg) {
+          const int page = s * PPS + pg;
+          const int d = (blk_ok[pg] ? su_lim[i] : -1) - (page * PBS + quad * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sv[pg][e] = (e <= d) ? sv[pg][e] : -INFINITY;
+        }
+      };
+      if constexpr (BRANCHFREE)
+        apply_masks();
+      else if (mask)  // uniform
+        apply_masks();
+      float mx = -INFINITY;
+#pragma unroll
+      for (int pg = 0; pg < PPS; ++pg)
+        mx = fmaxf(mx, fmaxf(fmaxf(sv[pg][0], sv[pg][1]), fmaxf(sv[pg][2], sv[pg][3])));
+      const float pm = quad_max(mx);
+      const bool raise = pm > m_run[i] + kRaise;  // false while pm is -inf
+      const float m_use = raise ? pm : m_run[i];
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run[i] - pm) : 1.f;  // 0 on the first raise
+      // m_use is -inf only while no key has been visible; every sv is then -inf
+      const float m_sub = (m_use == -INFINITY) ? 0.f : m_use;
+      float ps = 0.f;
+      const int row = su_row[i];
+#pragma unroll
+      for (int pg = 0; pg < PPS; ++pg) {
+        half4 ph;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pr = __builtin_amdgcn_exp2f(sv[pg][e] - m_sub);  // exp2(-inf) = 0
+          ps += pr;
+          ph[e] = (half_t)pr;
+        }
+        *(half4*)&sP[buf][pg][row >> 5][quad >> 1][row & 31][(quad & 1) * 4] = ph;
+      }
+      ps = quad_sum(ps);
+      l_run[i] = l_run[i] * alpha + ps;
+      m_run[i] = m_use;
+      sAlpha[buf][row & 31][row >> 5] = alpha;  // the four quads agree
+    }
+  };
+  // rescale before step s's products when any row's reference moved
+  auto rescale = [&](int buf) {
+    float al[C::RT];
+    float amin = 1.f;
+#pragma unroll
+    for (int rt = 0; rt < C::RT; ++rt) {
+      al[rt] = sAlpha[buf][c32][rt];
+      amin = fminf(amin, al[rt]);  // factors are 1 (unchanged) or below 1
+    }
+    if (__builtin_amdgcn_ballot_w64(amin < 1.f) != 0) {  // uniform
+#pragma unroll
+      for (int rt = 0; rt < C::RT; ++rt)
+#pragma unroll
+        for (int ft = 0; ft < C::FTW; ++ft) acc[rt][ft] *= al[rt];
+    }
+  };
+  // P.c_v of step s (values in vv, P in LDS buffer `buf`)
+  // zero the value columns of tokens past the sequence (they may hold
+  // anything, NaN included) and of pages with an invalid block id
+  auto mask_values = [&](VSet& vv, int s) {
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int pg = 0; pg < PPS; ++pg) {
+      const int page = s * PPS + pg;
+      const int nv = (block_of(page) >= 0) ? min(max(L - (page * PBS + hf * 8), 0), 8) : 0;
+#pragma unroll
+      for (int ft = 0; ft < C::FTW; ++ft) {
+        u4 bits = __builtin_bit_cast(u4, vv[pg][ft]);
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          bits[d] &= (2 * d + 1 < nv) ? 0xFFFFFFFFu : ((2 * d < nv) ? 0x0000FFFFu : 0u);
+        vv[pg][ft] = __builtin_bit_cast(half8, bits);
+      }
+    }
+  };
+  auto value_products = [&](bool mask, VSet& vv, int s, int buf) {
+    if (mask) mask_values(vv, s);  // uniform
+#pragma unroll
+    for (int pg = 0; pg < PPS; ++pg)
 #pragma unroll
       for (int rt = 0; rt < C::RT; ++rt) {
-        const half4 pb = *(const half4*)&sP[buf][rt * 16 + col][quad * 4];
-        if (rescale) {
-          const float al = sAlpha[buf][rt * 16 + col];
+        const half8 pb = *(const half8*)&sP[buf][pg][rt][hf][c32][0];
 #pragma unroll
-          for (int ft = 0; ft < C::FT; ++ft) acc[rt][ft] *= al;
-        }
-#pragma unroll
-        for (int ft = 0; ft < C::FT; ++ft) acc[rt][ft] = mfma16x16x16(r.v[ft], pb, acc[rt][ft]);
+        for (int ft = 0; ft < C::FTW; ++ft) acc[rt][ft] = mfma32x32x16(vv[pg][ft], pb, acc[rt][ft]);
       }
-    }
+  };
+  // every token of step s visible to every row, and every page valid
+  auto step_plain_scores = [&](int s) {
+    bool ok = (s * PPS + PPS) * PBS - 1 <= lim_min;
+#pragma unroll
+    for (int pg = 0; pg < PPS; ++pg) ok = ok && block_of(s * PPS + pg) >= 0;
+    return ok;
+  };
+  auto step_plain_values = [&](int s) {
+    bool ok = (s * PPS + PPS) * PBS <= L;
+#pragma unroll
+    for (int pg = 0; pg < PPS; ++pg) ok = ok && block_of(s * PPS + pg) >= 0;
+    return ok;
   };
 
-  Regs ra, rb;
-  int blk_a = safe_block(0);
-  if (blk_a >= 0) load(ra, blk_a);
-  __syncthreads();
-  for (int p = 0; p < n_pages; p += 2) {
-    int blk_b = -1;
-    if (p + 1 < n_pages) {
-      blk_b = safe_block(p + 1);
-      if (blk_b >= 0) load(rb, blk_b);
-    }
-    process(ra, p, 0, blk_a >= 0);
-    if (p + 1 < n_pages) {
-      if (p + 2 < n_pages) {
-        blk_a = safe_block(p + 2);
-        if (blk_a >= 0) load(ra, blk_a);
-      }
-      process(rb, p + 1, 1, blk_b >= 0);
-    }
+  // ---- prologue: block ids staged, keys of steps 0..DEPTH-1 and values of
+  // steps 0..DEPTH-2 in flight, step 0 scored
+  block_sync_lds();
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j) load_k(kr[j], j);
+#pragma unroll
+  for (int j = 0; j + 1 < DEPTH; ++j) load_v(vr[j], j);
+  {
+    float4v sacc[PPS][C::SUW];
+    score_products(kr[0], sacc);
+    bool ok0[PPS];
+#pragma unroll
+    for (int pg = 0; pg < PPS; ++pg) ok0[pg] = block_of(pg) >= 0;
+    softmax(std::false_type{}, true, ok0, sacc, 0, 0);
   }
+  // nothing of the prologue stays in flight into the loop, so the loop's
+  // wait counts depend on its own loads only
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  block_sync_lds();
+
+  // step s (register-ring phase PH = s % DEPTH): loads for the keys of step
+  // s+DEPTH and the values of step s+DEPTH-1, scores of step s+1, products of
+  // step s.  P and the rescale factors alternate between two LDS buffers.
+  auto step = [&](auto phase, int s) {
+    constexpr int PH = decltype(phase)::value;
+    int staged[PPS];
+#pragma unroll
+    for (int pg = 0; pg < PPS; ++pg)  // issued before the page loads
+      staged[pg] = fetch_block((s - 1) * PPS + pg + RING);
+    load_k(kr[PH], s + DEPTH);                      // keys of step s were scored last step
+    load_v(vr[(PH + DEPTH - 1) % DEPTH], s + DEPTH - 1);  // values of step s-1 were used last step
+    float4v sacc[PPS][C::SUW];
+    score_products(kr[(PH + 1) % DEPTH], sacc);
+    const int buf = s & 1;
+    rescale(buf);
+    const bool vmask = !step_plain_values(s);
+    const bool smask = !step_plain_scores(s + 1);
+    if constexpr (SCHED >= 1) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SCHED == 2) {  // masks ahead of the interleaved region
+      if (vmask) mask_values(vr[PH], s);
+      value_products(false, vr[PH], s, buf);
+    } else {
+      value_products(vmask, vr[PH], s, buf);
+    }
+    if constexpr (SCHED == 1) __builtin_amdgcn_sched_barrier(0);
+    bool ok_s[PPS];
+#pragma unroll
+    for (int pg = 0; pg < PPS; ++pg) ok_s[pg] = block_of((s + 1) * PPS + pg) >= 0;
+    if constexpr (SCHED == 2)
+      softmax(std::true_type{}, smask, ok_s, sacc, s + 1, buf ^ 1);
+    else
+      softmax(std::false_type{}, smask, ok_s, sacc, s + 1, buf ^ 1);
+    if constexpr (SCHED == 2) {
+      // one P.c_v product, then a few vector instructions, repeated, so the
+      // softmax runs in the shadow of the products
+#pragma unroll
+      for (int i = 0; i < PPS * C::RT * C::FTW; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // pages of step s-1 (+RING) into their slots, which no wave reads any more
+    if (tid == 0) {
+#pragma unroll
+      for (int pg = 0; pg < PPS; ++pg) sBlk[((s - 1) * PPS + pg) & (RING - 1)] = staged[pg];
+    }
+    block_sync_lds();
+  };
+  // DEPTH steps per loop trip (a single path through its body, so the wait
+  // counts at its head see only the previous trip's loads); the tail after
+  int s = 0;
+  for (; s + DEPTH <= n_steps; s += DEPTH) {
+    step(std::integral_constant<int, 0>{}, s);
+    step(std::integral_constant<int, 1>{}, s + 1);
+    if constexpr (DEPTH > 2) step(std::integral_constant<int, 2 % DEPTH>{}, s + 2);
+  }
+  if (s < n_steps) step(std::integral_constant<int, 0>{}, s);
+  if constexpr (DEPTH > 2)
+    if (s + 1 < n_steps) step(std::integral_constant<int, 1>{}, s + 1);
 
   // ---- normalise and write z rows of this tile
-  if (quad == 0) sL[row] = l_run;
+#pragma unroll
+  for (int i = 0; i < C::SUW; ++i) sL[su_row[i]] = l_run[i];  // the four quads agree
   block_sync_lds();
 #pragma unroll
   for (int rt = 0; rt < C::RT; ++rt) {
-    const int r_row = rt * 16 + col;
-    const int r_h = g * G + r_row / MQ;
-    const int r_j = j0 + r_row % MQ;
+    const int row = rt * 32 + c32;
+    const int r_h = g * G + row / MQ;
+    const int r_j = j0 + row % MQ;
     if (r_j >= Cn) continue;
-    const float lr = sL[r_row];
+    const float lr = sL[row];
     const float inv = lr > 0.f ? 1.f / lr : 0.f;
-    float* zr = a.z + ((size_t)(q_begin + r_j) * H + r_h) * RV + w * C::FPW + quad * 4;
+    float* zr = a.z + ((size_t)(q_begin + r_j) * H + r_h) * RV + f_base - c32 + 4 * hf;
 #pragma unroll
-    for (int ft = 0; ft < C::FT; ++ft) *(float4v*)(zr + ft * 16) = acc[rt][ft] * inv;
+    for (int ft = 0; ft < C::FTW; ++ft)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float4v o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = acc[rt][ft][4 * jj + r] * inv;
+        *(float4v*)(zr + ft * 32 + 8 * jj) = o;
+      }
   }
 }
 
-template <int H, int D, int RK, int RV, int G, int MQ, int NW>
+template <int H, int D, int RK, int RV, int G, int MQ, int NW, int PPS, int DEPTH, int SCHED>
 static hipError_t prefill_instance(const void* qt, const int32_t* qsl, int max_query_len,
                                    const void* k_cache, const void* v_cache, const void* W,
                                    const int32_t* block_tables, int max_blocks,
@@ -251,11 +492,21 @@ static hipError_t prefill_instance(const void* qt, const int32_t* qsl, int max_q
   a.n_qtiles = (max_query_len + MQ - 1) / MQ;
   a.n_groups = H / G;
   const long wgs = (long)batch * a.n_qtiles * a.n_groups;
-  launch_hooked(TIME_PREFILL_ATTN, TIME_NONE, prefill_attn_kernel<H, RK, RV, G, MQ, NW>, dim3((unsigned)wgs),
-                dim3(NW * 64), st, a);
+  launch_hooked(TIME_PREFILL_ATTN, TIME_NONE, prefill_attn_kernel<H, RK, RV, G, MQ, NW, PPS, DEPTH, SCHED>,
+                dim3((unsigned)wgs), dim3(NW * 64), st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_upproj(ShapeKey{H, D, RK, RV}, W, z, total_q, true, out, st);
+}
+
+// Kernel variant (tuning aid, STARKV_PREFILL_VARIANT): head group, query
+// tile and instruction schedule of the main shape.
+static int prefill_variant() {
+  static const int v = [] {
+    const char* e = getenv("STARKV_PREFILL_VARIANT");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
 }
 
 hipError_t launch_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl, int total_q,
@@ -264,14 +515,21 @@ hipError_t launch_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl,
                           const int32_t* seq_lens, int num_blocks, int batch, float* z, void* out,
                           hipStream_t st) {
   if (batch <= 0 || total_q <= 0) return hipSuccess;
-  if (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512)
-    return prefill_instance<32, 128, 64, 512, 4, 32, 8>(qt, qsl, max_query_len, k_cache, v_cache,
-                                                        W, block_tables, max_blocks, seq_lens,
-                                                        num_blocks, batch, total_q, z, out, st);
+#define STARKV_PREFILL_ARGS                                                                    \
+  qt, qsl, max_query_len, k_cache, v_cache, W, block_tables, max_blocks, seq_lens, num_blocks, \
+      batch, total_q, z, out, st
+  if (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) {
+    switch (prefill_variant()) {
+      case 1: return prefill_instance<32, 128, 64, 512, 4, 32, 8, 2, 2, 1>(STARKV_PREFILL_ARGS);
+      case 2: return prefill_instance<32, 128, 64, 512, 4, 32, 8, 2, 2, 2>(STARKV_PREFILL_ARGS);
+      case 3: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 2, 1>(STARKV_PREFILL_ARGS);
+      case 4: return prefill_instance<32, 128, 64, 512, 4, 32, 8, 1, 2, 1>(STARKV_PREFILL_ARGS);
+      default: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 2, 2>(STARKV_PREFILL_ARGS);
+    }
+  }
   if (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64)
-    return prefill_instance<4, 64, 16, 64, 4, 16, 4>(qt, qsl, max_query_len, k_cache, v_cache, W,
-                                                     block_tables, max_blocks, seq_lens,
-                                                     num_blocks, batch, total_q, z, out, st);
+    return prefill_instance<4, 64, 16, 64, 4, 16, 2, 2, 2, 1>(STARKV_PREFILL_ARGS);
+#undef STARKV_PREFILL_ARGS
   return hipErrorInvalidValue;
 }
 
