@@ -145,6 +145,124 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Few tokens (a decode step's append): the work is reading the bases, and a
+// contraction as long as H*d must not run as one serial chain.  One work
+// group per job:
+//   value job: 16 outputs f0..f0+15 of c_v over the whole K = H*d,
+//   key job:   one head, all r_k outputs over K = d.
+// The job's slice of W (or U_h) is staged once in LDS transposed to
+// [output][k], so a lane's 8 consecutive k of one output are one 16-byte
+// LDS read, the B operand of v_mfma_f32_16x16x32_f16; A is 8 consecutive
+// features of one token straight from memory.  The K range is split over
+// the waves, and the partial 16x16 tiles are summed through LDS (reusing
+// the staging area) before the fp16 rounding and the paged scatter.
+// ---------------------------------------------------------------------------
+constexpr int kSmallN = 64;            // tokens handled by the few-token kernel
+constexpr int kSmallWaves = 16;
+
+template <int K, int OUT>
+struct SmallJob {
+  static constexpr int OT = OUT / 16;                      // output tiles
+  static constexpr int KS0 = kSmallWaves / OT;             // wanted K splits
+  static constexpr int KS = (K / 32 < KS0) ? K / 32 : KS0;  // K splits (>= 32 each)
+  static constexpr int KPW = K / KS;                       // K per wave
+  static constexpr int LDK = K + 8;                        // halves per LDS row
+  static constexpr size_t lds_bytes(int nt) {
+    const size_t stage = (size_t)OUT * LDK * 2;
+    const size_t red = (size_t)OT * KS * nt * 256 * 4;
+    return stage > red ? stage : red;
+  }
+  static_assert(OUT % 16 == 0 && K % 32 == 0 && K % KS == 0 && KPW % 32 == 0, "job shape");
+};
+
+template <int H, int D, int RK, int RV>
+__global__ __launch_bounds__(kSmallWaves * 64) void append_small_kernel(AppendArgs a) {
+  using VJ = SmallJob<H * D, 16>;
+  using KJ = SmallJob<D, RK>;
+  constexpr size_t kLds = VJ::lds_bytes(kSmallN / 16) > KJ::lds_bytes(kSmallN / 16)
+                              ? VJ::lds_bytes(kSmallN / 16)
+                              : KJ::lds_bytes(kSmallN / 16);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, quad = lane >> 4;
+  const int n_tiles = (a.N + 15) / 16;  // <= kSmallN / 16
+
+  auto run = [&](auto job, const half_t* A, int lda, const half_t* B, int ldb, int o0,
+                 auto store) {
+    using J = decltype(job);
+    constexpr int K = J::KPW * J::KS, OUT = J::OT * 16;
+    half_t* sT = (half_t*)smem;  // [OUT][LDK]
+    // stage B[k][o0 .. o0+OUT) transposed: a thread takes 8 outputs of one k
+    for (int c = tid; c < K * (OUT / 8); c += kSmallWaves * 64) {
+      const int k = c / (OUT / 8), o = (c % (OUT / 8)) * 8;
+      const half8 bv = *(const half8*)(B + (size_t)k * ldb + o0 + o);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sT[(o + e) * J::LDK + k] = bv[e];
+    }
+    __syncthreads();
+    const bool active = w < J::OT * J::KS;
+    const int ot = w % J::OT, ks = w / J::OT;
+    float4v acc[kSmallN / 16];
+#pragma unroll
+    for (int t = 0; t < kSmallN / 16; ++t) acc[t] = zero4();
+    if (active) {
+#pragma unroll
+      for (int c = 0; c < J::KPW / 32; ++c) {
+        const int k0 = ks * J::KPW + c * 32 + quad * 8;
+        const half8 bq = *(const half8*)&sT[(ot * 16 + col) * J::LDK + k0];
+#pragma unroll
+        for (int t = 0; t < kSmallN / 16; ++t) {
+          if (t < n_tiles) {  // uniform
+            const int m = min(t * 16 + col, a.N - 1);
+            const half8 av = *(const half8*)(A + (size_t)m * lda + k0);
+            acc[t] = mfma16x16x32(av, bq, acc[t]);
+          }
+        }
+      }
+    }
+    __syncthreads();  // staging area becomes the reduction area
+    float* sR = (float*)smem;  // [OT][KS][tile][16 tokens][16 outputs]
+    if (active) {
+#pragma unroll
+      for (int t = 0; t < kSmallN / 16; ++t)
+        if (t < n_tiles)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sR[(((ot * J::KS + ks) * (kSmallN / 16) + t) * 16 + quad * 4 + r) * 16 + col] = acc[t][r];
+    }
+    __syncthreads();
+    for (int e = tid; e < a.N * OUT; e += kSmallWaves * 64) {
+      const int m = e / OUT, o = e % OUT;
+      const int t = m / 16, tok = m % 16, ot2 = o / 16, oc = o % 16;
+      float sum = 0.f;
+#pragma unroll
+      for (int k2 = 0; k2 < J::KS; ++k2)
+        sum += sR[(((ot2 * J::KS + k2) * (kSmallN / 16) + t) * 16 + tok) * 16 + oc];
+      const int64_t slot = a.slots[m];
+      if (slot < 0) continue;
+      const int64_t blk = slot / 16;
+      if (blk >= a.num_blocks) continue;
+      store(blk, (int)(slot % 16), o0 + o, (half_t)sum);
+    }
+  };
+
+  const int HD = H * D;
+  if (blockIdx.x < RV / 16) {
+    const int f0 = blockIdx.x * 16;
+    run(VJ{}, a.v, HD, a.W, RV, f0, [&](int64_t blk, int off, int f, half_t val) {
+      a.v_cache[((size_t)blk * RV + f) * 16 + off] = val;
+    });
+  } else {
+    const int h = blockIdx.x - RV / 16;
+    run(KJ{}, a.k + (size_t)h * D, HD, a.U + (size_t)h * D * RK, RK, 0,
+        [&](int64_t blk, int off, int r, half_t val) {
+          a.k_cache[(((size_t)blk * H + h) * 16 + off) * RK + r] = val;
+        });
+  }
+}
+
 hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const void* U,
                          const void* W, const int64_t* slots, int n_tokens, int num_blocks,
                          void* k_cache, void* v_cache, hipStream_t st) {
@@ -169,6 +287,18 @@ hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const 
   const long jobs = (long)a.tiles_m * (a.v_tiles_n + (long)s.H * a.k_tiles_n);
   // a single launch: the start event is recorded on the stream just before it
   if (g_timing.which == TIME_APPEND && g_timing.start) hipEventRecord(g_timing.start, st);
+  if (n_tokens <= kSmallN) {
+    if (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) {
+      launch_hooked(TIME_APPEND, TIME_NONE, append_small_kernel<32, 128, 64, 512>,
+                    dim3(512 / 16 + 32), dim3(kSmallWaves * 64), st, a);
+      return hipGetLastError();
+    }
+    if (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64) {
+      launch_hooked(TIME_APPEND, TIME_NONE, append_small_kernel<4, 64, 16, 64>,
+                    dim3(64 / 16 + 4), dim3(kSmallWaves * 64), st, a);
+      return hipGetLastError();
+    }
+  }
   launch_hooked(TIME_APPEND, TIME_NONE, append_kernel, dim3((unsigned)jobs), dim3(256), st, a);
   return hipGetLastError();
 }

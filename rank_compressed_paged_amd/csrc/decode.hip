@@ -58,11 +58,13 @@ constexpr int kMaxSplitPages = 256;  // planner bound on pages per split
 
 // ---------------------------------------------------------------------------
 // 1. q~[n, h, :] = (scale*log2e) * U_h^T q[n, h, :]  -> fp16
-// grid (H, ceil(N/64)), 4 waves; wave w owns tokens n0+16w .. n0+16w+15.
-// A = q (16 tokens x 32 of d, 16 contiguous bytes per lane), B = U_h staged in
-// LDS as [r][d] so each lane again reads 8 contiguous values.
+// grid (H, ceil(N/(64*TPW))), 4 waves; in token tile tt the wave w owns
+// tokens n0+16w .. n0+16w+15 of that tile's 64.  A = q (16 tokens x 32 of
+// d, 16 contiguous bytes per lane), B = U_h staged in LDS as [r][d] so each
+// lane again reads 8 contiguous values; TPW tiles per work group amortise
+// the staging over many tokens.
 // ---------------------------------------------------------------------------
-template <int H, int D, int RK>
+template <int H, int D, int RK, int TPW>
 __global__ __launch_bounds__(256) void qproj_kernel(const half_t* __restrict__ q,
                                                     const half_t* __restrict__ U, int n_tokens,
                                                     float qscale, half_t* __restrict__ qt) {
@@ -81,8 +83,9 @@ __global__ __launch_bounds__(256) void qproj_kernel(const half_t* __restrict__ q
     for (int e = 0; e < 8; ++e) sUt[r0 + e][i] = u[e];
   }
   __syncthreads();
-  const int nb = blockIdx.y * 64 + w * 16;
-  if (nb >= n_tokens) return;  // wave-uniform; no barrier follows
+  for (int tt = 0; tt < TPW; ++tt) {
+  const int nb = (blockIdx.y * TPW + tt) * 64 + w * 16;
+  if (nb >= n_tokens) break;  // wave-uniform; no barrier follows
   const int n = nb + col;
   const bool nv = n < n_tokens;
   const half_t* qrow = q + ((size_t)(nv ? n : nb) * H + h) * D + quad * 8;
@@ -103,6 +106,7 @@ __global__ __launch_bounds__(256) void qproj_kernel(const half_t* __restrict__ q
       const int nt = nb + quad * 4 + r;
       if (nt < n_tokens) qt[((size_t)nt * H + h) * RK + rt * 16 + col] = (half_t)(acc[r] * qscale);
     }
+  }
   }
 }
 
@@ -523,6 +527,89 @@ __global__ __launch_bounds__(256) void upproj_small_kernel(const half_t* __restr
   }
 }
 
+// Many-token variant (prefill): grid (H, ceil(N / (32*NW))).  W_h (D x RV
+// fp16) is staged once per work group in LDS, padded so that each 16-lane
+// group of a 16-byte read hits distinct banks; then every wave streams 32
+// tokens of z through v_mfma_f32_32x32x16_f16 with no further barrier:
+// A = z rows (32 tokens x 16 features, split into fp16 hi/lo, 32 contiguous
+// bytes of fp32 per lane), B = W_h^T (16 features x 32 outputs, from LDS),
+// D[token][output].  The z loads run up to 16 chunks ahead of their
+// products: z rows come from HBM, and the LDS footprint already limits the
+// kernel to two waves per SIMD, which leaves the registers for the ring.
+template <int H, int D, int RV, int NW>
+__global__ __launch_bounds__(NW * 64) void upproj_wide_kernel(const half_t* __restrict__ W,
+                                                              const float* __restrict__ z,
+                                                              int n_tokens,
+                                                              half_t* __restrict__ out) {
+  constexpr int LDW = RV + 8;  // halves per LDS row
+  constexpr int DT = D / 32;   // 32-wide output tiles
+  constexpr int KC = RV / 16;  // 16-feature chunks
+  constexpr int ZP = KC < 16 ? KC : 16;  // z chunks in flight (LDS limits occupancy anyway)
+  static_assert(D % 32 == 0 && RV % 16 == 0 && KC >= ZP, "tile shape");
+  typedef float float16v __attribute__((ext_vector_type(16)));
+  __shared__ __attribute__((aligned(16))) half_t sW[D][LDW];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c32 = lane & 31, hf = lane >> 5;
+  const half_t* Wh = W + (size_t)h * D * RV;
+  for (int c = tid; c < D * RV / 8; c += NW * 64) {
+    const int r = c / (RV / 8), k = (c % (RV / 8)) * 8;
+    *(half8*)&sW[r][k] = *(const half8*)(Wh + (size_t)r * RV + k);
+  }
+  __syncthreads();
+  const int t0 = blockIdx.y * (NW * 32) + w * 32;
+  if (t0 >= n_tokens) return;  // no barrier follows
+  const int tok = min(t0 + c32, n_tokens - 1);  // rows past the end repeat the last token
+  const float* zr = z + ((size_t)tok * H + h) * RV + 8 * hf;
+  float16v acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
+  float4v zq[ZP][2];
+#pragma unroll
+  for (int j = 0; j < ZP; ++j) {
+    zq[j][0] = *(const float4v*)(zr + j * 16);
+    zq[j][1] = *(const float4v*)(zr + j * 16 + 4);
+  }
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    half8 hi, lo;
+    split_f16x8(zq[kc % ZP][0], zq[kc % ZP][1], hi, lo);
+    if (kc + ZP < KC) {
+      zq[kc % ZP][0] = *(const float4v*)(zr + (kc + ZP) * 16);
+      zq[kc % ZP][1] = *(const float4v*)(zr + (kc + ZP) * 16 + 4);
+    }
+    // keep the refill issued here, ZP chunks ahead of its use, instead of
+    // letting the scheduler sink it next to the products that consume it
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const half8 b = *(const half8*)&sW[dt * 32 + c32][kc * 16 + 8 * hf];
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi, b, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lo, b, acc[dt], 0, 0, 0);
+    }
+  }
+  // register i of tile dt holds token 8*(i/4) + 4*hf + i%4, output dt*32 + c32
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int n = t0 + 8 * (i / 4) + 4 * hf + (i % 4);
+    if (n < n_tokens) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        out[((size_t)n * H + h) * D + dt * 32 + c32] = (half_t)acc[dt][i];
+    }
+  }
+}
+
+template <int H, int D, int RV, int NW>
+static void launch_upproj_wide(const void* W, const float* z, int n_tokens, void* out,
+                               hipStream_t st) {
+  hipLaunchKernelGGL((upproj_wide_kernel<H, D, RV, NW>),
+                     dim3(H, (n_tokens + NW * 32 - 1) / (NW * 32)), dim3(NW * 64), 0, st,
+                     (const half_t*)W, z, n_tokens, (half_t*)out);
+}
+
 template <int H, int D, int RV, int DR>
 static void launch_upproj_t(const void* W, const float* z, int n_tokens, void* out, hipStream_t st) {
   hipLaunchKernelGGL((upproj_kernel<H, D, RV, DR>), dim3(H, D / DR, (n_tokens + 63) / 64), dim3(256),
@@ -533,11 +620,11 @@ hipError_t launch_upproj(const ShapeKey& s, const void* W, const float* z, int n
                          bool wide_rows, void* out, hipStream_t st) {
   if (n_tokens <= 0) return hipSuccess;
   if (s.H == 32 && s.d == 128 && s.rv == 512) {
-    if (wide_rows) launch_upproj_t<32, 128, 512, 128>(W, z, n_tokens, out, st);
+    if (wide_rows) launch_upproj_wide<32, 128, 512, 8>(W, z, n_tokens, out, st);
     else hipLaunchKernelGGL((upproj_small_kernel<32, 128, 512>), dim3(32, 128 / 16), dim3(256), 0,
                             st, (const half_t*)W, z, n_tokens, (half_t*)out);
   } else if (s.H == 4 && s.d == 64 && s.rv == 64) {
-    if (wide_rows) launch_upproj_t<4, 64, 64, 64>(W, z, n_tokens, out, st);
+    if (wide_rows) launch_upproj_wide<4, 64, 64, 4>(W, z, n_tokens, out, st);
     else launch_upproj_t<4, 64, 64, 16>(W, z, n_tokens, out, st);
   } else {
     return hipErrorInvalidValue;
@@ -570,8 +657,14 @@ static hipError_t decode_instance(const DecodePlan& p, const void* qt, const voi
 template <int H, int D, int RK>
 static hipError_t qproj_instance(const void* q, const void* U, int n, float scale, void* qt,
                                  int precedes, hipStream_t st) {
-  launch_hooked(TIME_NONE, precedes, qproj_kernel<H, D, RK>, dim3(H, (n + 63) / 64), dim3(256), st,
-                (const half_t*)q, (const half_t*)U, n, scale * kLog2e, (half_t*)qt);
+  if (n >= 1024)  // many tokens: four 64-token tiles per work group
+    launch_hooked(TIME_NONE, precedes, qproj_kernel<H, D, RK, 4>, dim3(H, (n + 255) / 256),
+                  dim3(256), st, (const half_t*)q, (const half_t*)U, n, scale * kLog2e,
+                  (half_t*)qt);
+  else
+    launch_hooked(TIME_NONE, precedes, qproj_kernel<H, D, RK, 1>, dim3(H, (n + 63) / 64),
+                  dim3(256), st, (const half_t*)q, (const half_t*)U, n, scale * kLog2e,
+                  (half_t*)qt);
   return hipGetLastError();
 }
 

@@ -76,9 +76,13 @@ def _check(gk, gv, rk, rv, what):
     assert okk.all() and okv.all()
 
 
+# token counts on both sides of the few-token kernel's limit (64 tokens)
 @pytest.mark.parametrize("shape,n,seed,neg", [(wl.MAIN, 16, 31, 0), (wl.MAIN, 300, 32, 7),
-                                              (wl.TINY, 5, 33, 2), (wl.TINY, 130, 34, 0)],
-                         ids=["main_decode_step", "main_ragged_300", "tiny_5", "tiny_130"])
+                                              (wl.TINY, 5, 33, 2), (wl.TINY, 130, 34, 0),
+                                              (wl.MAIN, 1, 37, 0), (wl.MAIN, 64, 38, 5),
+                                              (wl.MAIN, 65, 39, 0), (wl.TINY, 64, 40, 3)],
+                         ids=["main_decode_step", "main_ragged_300", "tiny_5", "tiny_130",
+                              "main_1", "main_64", "main_65", "tiny_64"])
 def test_append_matches_oracle(sk, shape, n, seed, neg):
     U, W, k, v, slots, kc, vc = _case(shape, n, seed, neg)
     note(f"append {shape} n={n}")
@@ -87,7 +91,8 @@ def test_append_matches_oracle(sk, shape, n, seed, neg):
     _check(gk, gv, rk, rv, f"append n={n}")
 
 
-def test_append_selection_bases_bit_exact(sk):
+@pytest.mark.parametrize("n", [77, 40], ids=["many_tokens", "few_tokens"])
+def test_append_selection_bases_bit_exact(sk, n):
     """Bases that pick coordinates (one 1.0 per column) make every latent an
     exact copy of an input value, so the whole cache must match bit for bit."""
     sh = wl.MAIN
@@ -97,7 +102,7 @@ def test_append_selection_bases_bit_exact(sk):
         U[h, rng.permutation(sh.d)[:sh.r_k], np.arange(sh.r_k)] = 1.0
     W = np.zeros((sh.H * sh.d, sh.r_v), np.float16)
     W[rng.permutation(sh.H * sh.d)[:sh.r_v], np.arange(sh.r_v)] = 1.0
-    _, _, k, v, slots, kc, vc = _case(sh, 77, 36, 5)
+    _, _, k, v, slots, kc, vc = _case(sh, n, 36, 5)
     note("append selection bases")
     gk, gv = _run(sk, U, W, k, v, slots, kc, vc)
     rk, rv = oracle.append(k, v, U, W, slots, kc, vc)
