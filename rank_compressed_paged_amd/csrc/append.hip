@@ -14,6 +14,10 @@
 // before the current step's LDS barrier (which waits on LDS only).  The epilogue rounds to fp16
 // (nearest even) and writes slot_mapping[n]; negative or out-of-range slots
 // are skipped.  Layouts: k_cache [NB, H, 16, r_k], v_cache [NB, r_v, 16].
+#include <stdlib.h>
+
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -152,13 +156,26 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 // group per job:
 //   value job: 16 outputs f0..f0+15 of c_v over the whole K = H*d,
 //   key job:   one head, all r_k outputs over K = d.
-// The job's slice of W (or U_h) is staged once in LDS transposed to
-// [output][k], so a lane's 8 consecutive k of one output are one 16-byte
-// LDS read, the B operand of v_mfma_f32_16x16x32_f16; A is 8 consecutive
-// features of one token straight from memory.  The K range is split over
+// The job's slice of W (or U_h) is staged once in LDS as it is in memory,
+// [k][output], and the B operand of v_mfma_f32_16x16x32_f16 (8 consecutive
+// k of one output per lane) comes through the transposing LDS read; A is 8
+// consecutive features of one token straight from memory.  The K range is split over
 // the waves, and the partial 16x16 tiles are summed through LDS (reusing
 // the staging area) before the fp16 rounding and the paged scatter.
 // ---------------------------------------------------------------------------
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane i
+// receives element i%4 of the 4-element (8-byte) chunk addressed by lane
+// 4e + i/4, for e = 0..3.  So if lane q of a group addresses row k0 + q/4,
+// columns o0 + 4*(q%4) .. +3 of a row-major [k][output] tile, lane i gets
+// the 4 consecutive k of output o0 + i: an MFMA B-operand fragment read from
+// a tile stored untransposed.
+typedef short short4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ half4 lds_read_tr16(const half_t* p) {
+  typedef __attribute__((address_space(3))) short4v lds_short4v;
+  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)p);
+  return __builtin_bit_cast(half4, r);
+}
+
 constexpr int kSmallN = 64;            // tokens handled by the few-token kernel
 constexpr int kSmallWaves = 16;
 
@@ -168,9 +185,11 @@ struct SmallJob {
   static constexpr int KS0 = kSmallWaves / OT;             // wanted K splits
   static constexpr int KS = (K / 32 < KS0) ? K / 32 : KS0;  // K splits (>= 32 each)
   static constexpr int KPW = K / KS;                       // K per wave
-  static constexpr int LDK = K + 8;                        // halves per LDS row
+  // staged [k][output] as in memory; rows of 16 outputs are read without
+  // bank conflicts unpadded, wider rows get 8 halves of padding
+  static constexpr int LDB = (OUT == 16) ? 16 : OUT + 8;
   static constexpr size_t lds_bytes(int nt) {
-    const size_t stage = (size_t)OUT * LDK * 2;
+    const size_t stage = (size_t)K * LDB * 2;
     const size_t red = (size_t)OT * KS * nt * 256 * 4;
     return stage > red ? stage : red;
   }
@@ -193,33 +212,50 @@ __global__ __launch_bounds__(kSmallWaves * 64) void append_small_kernel(AppendAr
                  auto store) {
     using J = decltype(job);
     constexpr int K = J::KPW * J::KS, OUT = J::OT * 16;
-    half_t* sT = (half_t*)smem;  // [OUT][LDK]
-    // stage B[k][o0 .. o0+OUT) transposed: a thread takes 8 outputs of one k
-    for (int c = tid; c < K * (OUT / 8); c += kSmallWaves * 64) {
-      const int k = c / (OUT / 8), o = (c % (OUT / 8)) * 8;
-      const half8 bv = *(const half8*)(B + (size_t)k * ldb + o0 + o);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sT[(o + e) * J::LDK + k] = bv[e];
-    }
-    __syncthreads();
+    half_t* sT = (half_t*)smem;  // [K][LDB]
     const bool active = w < J::OT * J::KS;
     const int ot = w % J::OT, ks = w / J::OT;
+    // A fragments of a token tile (8 consecutive features of one token per
+    // chunk); tile 0's are requested before the staging so the two memory
+    // round trips overlap
+    auto load_a = [&](half8 (&av)[J::KPW / 32], int t) {
+      const int m = min(t * 16 + col, a.N - 1);
+#pragma unroll
+      for (int c = 0; c < J::KPW / 32; ++c)
+        av[c] = *(const half8*)(A + (size_t)m * lda + ks * J::KPW + c * 32 + quad * 8);
+    };
+    half8 av[J::KPW / 32];
+    if (active) load_a(av, 0);
+    // stage B[k][o0 .. o0+OUT): a thread takes 8 outputs of one k
+    for (int c = tid; c < K * (OUT / 8); c += kSmallWaves * 64) {
+      const int k = c / (OUT / 8), o = (c % (OUT / 8)) * 8;
+      *(half8*)&sT[k * J::LDB + o] = *(const half8*)(B + (size_t)k * ldb + o0 + o);
+    }
+    __syncthreads();
     float4v acc[kSmallN / 16];
 #pragma unroll
     for (int t = 0; t < kSmallN / 16; ++t) acc[t] = zero4();
     if (active) {
+      // token tiles outermost; all A fragments of a tile are requested
+      // before its first product, so a tile costs one memory round trip
+      for (int t = 0; t < n_tiles; ++t) {  // uniform
+        if (t > 0) load_a(av, t);
+        float4v acc_t = zero4();
 #pragma unroll
-      for (int c = 0; c < J::KPW / 32; ++c) {
-        const int k0 = ks * J::KPW + c * 32 + quad * 8;
-        const half8 bq = *(const half8*)&sT[(ot * 16 + col) * J::LDK + k0];
-#pragma unroll
-        for (int t = 0; t < kSmallN / 16; ++t) {
-          if (t < n_tiles) {  // uniform
-            const int m = min(t * 16 + col, a.N - 1);
-            const half8 av = *(const half8*)(A + (size_t)m * lda + k0);
-            acc[t] = mfma16x16x32(av, bq, acc[t]);
-          }
+        for (int c = 0; c < J::KPW / 32; ++c) {
+          const int k0 = ks * J::KPW + c * 32 + quad * 8;
+          // B fragment (k0 .. k0+7 of output ot*16 + col) through the
+          // transposing read: lane col of the group addresses row col/4,
+          // outputs 4*(col%4) .. +3
+          const half_t* bp = &sT[(k0 + (col >> 2)) * J::LDB + ot * 16 + 4 * (col & 3)];
+          const half4 b0 = lds_read_tr16(bp);
+          const half4 b1 = lds_read_tr16(bp + 4 * J::LDB);
+          const half8 bq = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+          acc_t = mfma16x16x32(av[c], bq, acc_t);
         }
+#pragma unroll
+        for (int t2 = 0; t2 < kSmallN / 16; ++t2)
+          if (t2 == t) acc[t2] = acc_t;
       }
     }
     __syncthreads();  // staging area becomes the reduction area
@@ -263,6 +299,180 @@ __global__ __launch_bounds__(kSmallWaves * 64) void append_small_kernel(AppendAr
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Many tokens (a prefill chunk's append): C = A B with A the token rows (v, or
+// one head of k) and B the bases (W, or U_h), as tiles of 128 tokens x 64
+// outputs.  Both operand tiles of a TK-wide K step pass through
+// double-buffered LDS as they are in memory (16-byte stores, no bank
+// conflicts); a wave reads its v_mfma_f32_32x32x16_f16 A operand as 16-byte
+// rows and its B operand through the transposing LDS read, and each token
+// row and basis row is fetched from memory once per work group.  The global
+// loads run RING steps ahead through a ring of registers, since one step's
+// products take far less time than a load's round trip.  Eight waves: wave
+// w owns tokens 32*(w%4).. and outputs 32*(w/4).. of the tile.
+// ---------------------------------------------------------------------------
+constexpr int TT_M = 128, TT_N = 64;
+
+
+template <int H, int D, int RK, int RV, int TK, int RING>
+__global__ __launch_bounds__(512) void append_tiled_kernel(AppendArgs a) {
+  static_assert(RV % TT_N == 0 && RK == TT_N && D % TK == 0, "tile shape");
+  static_assert(RING >= 1 && RING <= 4, "register ring of 1 to 4 steps");
+  typedef float float16v __attribute__((ext_vector_type(16)));
+  constexpr int LD = TK + 8;              // halves per LDS row of A
+  constexpr int LDB = TT_N + 8;           // halves per LDS row of B ([k][output])
+  constexpr int AC = TT_M * TK / 8 / 512;  // 16-byte A chunks per thread per step
+  constexpr int BC = TK * TT_N / 8 / 512;  // 16-byte B chunks per thread per step
+  static_assert(AC >= 1 && BC >= 1, "at least one chunk per thread");
+  __shared__ __attribute__((aligned(16))) half_t sA[2][TT_M][LD];
+  __shared__ __attribute__((aligned(16))) half_t sB[2][TK][LDB];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c32 = lane & 31, hf = lane >> 5;
+  const int wm = w & 3, wn = w >> 2;
+
+  // job decode: value tiles first, then key tiles (one head each).  Work
+  // groups are dealt to the XCDs round-robin, so consecutive value jobs take
+  // consecutive token tiles: the VT output tiles of one token tile then sit
+  // on one XCD (when the tile count is a multiple of 8) and share its L2
+  // copy of those token rows instead of fetching them once per XCD.
+  constexpr int VT = RV / TT_N;
+  const int tiles_m = (a.N + TT_M - 1) / TT_M;
+  int job = blockIdx.x;
+  bool is_v;
+  int mt, nt = 0, h = 0;
+  if (job < tiles_m * VT) {
+    is_v = true;
+    mt = job % tiles_m;
+    nt = job / tiles_m;
+  } else {
+    is_v = false;
+    job -= tiles_m * VT;
+    mt = job / H;
+    h = job % H;
+  }
+  constexpr int HD = H * D;
+  const half_t* A = is_v ? a.v : a.k + (size_t)h * D;
+  const half_t* B = is_v ? a.W + nt * TT_N : a.U + (size_t)h * D * RK;
+  const int ldb = is_v ? RV : RK;
+  const int n_steps = (is_v ? HD : D) / TK;
+  const int m_base = mt * TT_M;
+
+  // staging roles: A chunk i is row a_row[i], k offset a_k[i]; B chunk j is
+  // k row b_k[j], outputs b_o[j] .. +7
+  int a_row[AC], a_k[AC], b_k[BC], b_o[BC];
+  const half_t* a_src[AC];
+  const half_t* b_src[BC];
+#pragma unroll
+  for (int i = 0; i < AC; ++i) {
+    const int c = tid + i * 512;
+    a_row[i] = c / (TK / 8);
+    a_k[i] = (c % (TK / 8)) * 8;
+    a_src[i] = A + (size_t)min(m_base + a_row[i], a.N - 1) * HD + a_k[i];
+  }
+#pragma unroll
+  for (int j = 0; j < BC; ++j) {
+    const int c = tid + j * 512;
+    b_k[j] = c / (TT_N / 8);
+    b_o[j] = (c % (TT_N / 8)) * 8;
+    b_src[j] = B + (size_t)b_k[j] * ldb + b_o[j];
+  }
+
+  half8 ra[RING][AC], rb[RING][BC];
+  auto fetch = [&](auto slot, int step) {
+    constexpr int S = decltype(slot)::value;
+    const int k0 = step * TK;
+#pragma unroll
+    for (int i = 0; i < AC; ++i) ra[S][i] = *(const half8*)(a_src[i] + k0);
+#pragma unroll
+    for (int j = 0; j < BC; ++j) rb[S][j] = *(const half8*)(b_src[j] + (size_t)k0 * ldb);
+  };
+  auto stage = [&](auto slot, int buf) {
+    constexpr int S = decltype(slot)::value;
+#pragma unroll
+    for (int i = 0; i < AC; ++i) *(half8*)&sA[buf][a_row[i]][a_k[i]] = ra[S][i];
+#pragma unroll
+    for (int j = 0; j < BC; ++j) *(half8*)&sB[buf][b_k[j]][b_o[j]] = rb[S][j];
+  };
+  // B fragment of chunk c: lane group g = lane/16 covers outputs
+  // 16*(g%2) .. +15 of the wave's 32 and k 8*(g/2) .. +7 of the chunk
+  const int grp = lane >> 4, q = lane & 15;
+  const int b_row = 8 * (grp >> 1) + (q >> 2);
+  const int b_col = wn * 32 + 16 * (grp & 1) + 4 * (q & 3);
+  auto compute = [&](float16v& acc, int buf) {
+#pragma unroll
+    for (int c = 0; c < TK / 16; ++c) {
+      const half8 av = *(const half8*)&sA[buf][wm * 32 + c32][c * 16 + 8 * hf];
+      const half4 b0 = lds_read_tr16(&sB[buf][c * 16 + b_row][b_col]);
+      const half4 b1 = lds_read_tr16(&sB[buf][c * 16 + b_row + 4][b_col]);
+      const half8 bv = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc, 0, 0, 0);
+    }
+  };
+
+  float16v acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  // prologue: step 0 staged, steps 1..RING in the ring (slot = step % RING)
+  fetch(std::integral_constant<int, 0>{}, 0);
+  stage(std::integral_constant<int, 0>{}, 0);
+  fetch(std::integral_constant<int, 1 % RING>{}, min(1, n_steps - 1));
+  if constexpr (RING > 1) fetch(std::integral_constant<int, 2 % RING>{}, min(2, n_steps - 1));
+  if constexpr (RING > 2) fetch(std::integral_constant<int, 3 % RING>{}, min(3, n_steps - 1));
+  if constexpr (RING > 3) fetch(std::integral_constant<int, 4 % RING>{}, min(4, n_steps - 1));
+  __syncthreads();
+  // step s: products of step s from LDS buffer s&1, step s+1 from the ring
+  // into the other buffer, step s+1+RING into the freed ring slot
+  auto iter = [&](auto phase, int s) {
+    constexpr int P = decltype(phase)::value;  // (s + 1) % RING
+    compute(acc, s & 1);
+    if (s + 1 < n_steps) {  // uniform
+      stage(std::integral_constant<int, P>{}, (s + 1) & 1);
+      fetch(std::integral_constant<int, P>{}, min(s + 1 + RING, n_steps - 1));
+    }
+    __syncthreads();
+  };
+  int s = 0;
+  for (; s + RING <= n_steps; s += RING) {
+    iter(std::integral_constant<int, 1 % RING>{}, s);
+    if constexpr (RING > 1) iter(std::integral_constant<int, 2 % RING>{}, s + 1);
+    if constexpr (RING > 2) iter(std::integral_constant<int, 3 % RING>{}, s + 2);
+    if constexpr (RING > 3) iter(std::integral_constant<int, 4 % RING>{}, s + 3);
+  }
+  if (s < n_steps) iter(std::integral_constant<int, 1 % RING>{}, s);
+  if constexpr (RING > 1)
+    if (s + 1 < n_steps) iter(std::integral_constant<int, 2 % RING>{}, s + 1);
+  if constexpr (RING > 2)
+    if (s + 2 < n_steps) iter(std::integral_constant<int, 3 % RING>{}, s + 2);
+
+  // epilogue: register i holds token 8*(i/4) + 4*hf + i%4, output c32
+  const int n = wn * 32 + c32;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int m = m_base + wm * 32 + 8 * (i / 4) + 4 * hf + (i % 4);
+    if (m >= a.N) continue;
+    const int64_t slot = a.slots[m];
+    if (slot < 0) continue;
+    const int64_t blk = slot / 16;
+    const int off = (int)(slot % 16);
+    if (blk >= a.num_blocks) continue;
+    const half_t val = (half_t)acc[i];
+    if (is_v)
+      a.v_cache[((size_t)blk * RV + nt * TT_N + n) * 16 + off] = val;
+    else
+      a.k_cache[(((size_t)blk * H + h) * 16 + off) * RK + n] = val;
+  }
+}
+
+// Kernel variant of the many-token path (tuning aid, STARKV_APPEND_VARIANT).
+static int append_variant() {
+  static const int v = [] {
+    const char* e = getenv("STARKV_APPEND_VARIANT");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
 hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const void* U,
                          const void* W, const int64_t* slots, int n_tokens, int num_blocks,
                          void* k_cache, void* v_cache, hipStream_t st) {
@@ -298,6 +508,28 @@ hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const 
                     dim3(64 / 16 + 4), dim3(kSmallWaves * 64), st, a);
       return hipGetLastError();
     }
+  }
+  if (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) {
+    const long tiles_m = (n_tokens + TT_M - 1) / TT_M;
+    const dim3 grid((unsigned)(tiles_m * (512 / TT_N + 32)));
+    switch (append_variant()) {
+      case 1:
+        launch_hooked(TIME_APPEND, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 64, 4>, grid,
+                      dim3(512), st, a);
+        break;
+      case 2:
+        launch_hooked(TIME_APPEND, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 128, 2>, grid,
+                      dim3(512), st, a);
+        break;
+      case 3:
+        launch_hooked(TIME_APPEND, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 128, 3>, grid,
+                      dim3(512), st, a);
+        break;
+      default:
+        launch_hooked(TIME_APPEND, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 64, 1>, grid,
+                      dim3(512), st, a);
+    }
+    return hipGetLastError();
   }
   launch_hooked(TIME_APPEND, TIME_NONE, append_kernel, dim3((unsigned)jobs), dim3(256), st, a);
   return hipGetLastError();
