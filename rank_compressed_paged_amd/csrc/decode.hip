@@ -60,53 +60,69 @@ constexpr int kMaxSplitPages = 256;  // planner bound on pages per split
 // 1. q~[n, h, :] = (scale*log2e) * U_h^T q[n, h, :]  -> fp16
 // grid (H, ceil(N/(64*TPW))), 4 waves; in token tile tt the wave w owns
 // tokens n0+16w .. n0+16w+15 of that tile's 64.  A = q (16 tokens x 32 of
-// d, 16 contiguous bytes per lane), B = U_h staged in LDS as [r][d] so each
-// lane again reads 8 contiguous values; TPW tiles per work group amortise
-// the staging over many tokens.
+// d, 16 contiguous bytes per lane).  B = U_h, staged in LDS as it is in
+// memory ([d][r], 16-byte stores) and read through the transposing LDS read
+// (ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives
+// element i%4 of the 8-byte chunk addressed by lane 4e + i/4, e = 0..3), so
+// that each lane gets 8 consecutive d of one r.  The first tile's q rows are
+// requested before the staging, so the two memory round trips overlap; TPW
+// tiles per work group amortise the staging over many tokens.
 // ---------------------------------------------------------------------------
+typedef short short4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ half4 lds_read_tr16(const half_t* p) {
+  typedef __attribute__((address_space(3))) short4v lds_short4v;
+  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)p);
+  return __builtin_bit_cast(half4, r);
+}
+
 template <int H, int D, int RK, int TPW>
 __global__ __launch_bounds__(256) void qproj_kernel(const half_t* __restrict__ q,
                                                     const half_t* __restrict__ U, int n_tokens,
                                                     float qscale, half_t* __restrict__ qt) {
-  constexpr int LDU = D + 8;
-  __shared__ __attribute__((aligned(16))) half_t sUt[RK][LDU];
+  constexpr int LDU = RK + 8;  // halves per LDS row: 4 rows of a read group hit distinct banks
+  __shared__ __attribute__((aligned(16))) half_t sU[D][LDU];
   const int h = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
-  const half_t* Uh = U + (size_t)h * D * RK;
-  constexpr int CHUNKS = D * RK / 8;
-  for (int c = tid; c < CHUNKS; c += 256) {
-    const int i = c / (RK / 8), r0 = (c % (RK / 8)) * 8;
-    const half8 u = *(const half8*)(Uh + (size_t)i * RK + r0);
+  auto load_q = [&](half8 (&a)[D / 32], int nb) {
+    const int n = min(nb + col, n_tokens - 1);  // rows past the end are not stored
+    const half_t* qrow = q + ((size_t)n * H + h) * D + quad * 8;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sUt[r0 + e][i] = u[e];
+    for (int k = 0; k < D / 32; ++k) a[k] = *(const half8*)(qrow + k * 32);
+  };
+  half8 a[D / 32];
+  const int nb0 = blockIdx.y * TPW * 64 + w * 16;
+  if (nb0 < n_tokens) load_q(a, nb0);
+  const half_t* Uh = U + (size_t)h * D * RK;
+  for (int c = tid; c < D * RK / 8; c += 256) {
+    const int i = c / (RK / 8), r0 = (c % (RK / 8)) * 8;
+    *(half8*)&sU[i][r0] = *(const half8*)(Uh + (size_t)i * RK + r0);
   }
   __syncthreads();
   for (int tt = 0; tt < TPW; ++tt) {
-  const int nb = (blockIdx.y * TPW + tt) * 64 + w * 16;
-  if (nb >= n_tokens) break;  // wave-uniform; no barrier follows
-  const int n = nb + col;
-  const bool nv = n < n_tokens;
-  const half_t* qrow = q + ((size_t)(nv ? n : nb) * H + h) * D + quad * 8;
-  half8 a[D / 32];
+    const int nb = nb0 + tt * 64;
+    if (nb >= n_tokens) break;  // wave-uniform; no barrier follows
+    if (tt > 0) load_q(a, nb);
 #pragma unroll
-  for (int k = 0; k < D / 32; ++k) a[k] = nv ? *(const half8*)(qrow + k * 32) : half8{};
+    for (int rt = 0; rt < RK / 16; ++rt) {
+      float4v acc = zero4();
 #pragma unroll
-  for (int rt = 0; rt < RK / 16; ++rt) {
-    float4v acc = zero4();
+      for (int k = 0; k < D / 32; ++k) {
+        // B fragment: d = 32k + 8*quad .. +7 of output r = 16*rt + col
+        const half_t* bp = &sU[k * 32 + quad * 8 + (col >> 2)][rt * 16 + 4 * (col & 3)];
+        const half4 b0 = lds_read_tr16(bp);
+        const half4 b1 = lds_read_tr16(bp + 4 * LDU);
+        const half8 bq = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        acc = mfma16x16x32(a[k], bq, acc);
+      }
+      // D[token 4*quad + r][output col]
 #pragma unroll
-    for (int k = 0; k < D / 32; ++k) {
-      const half8 bq = *(const half8*)&sUt[rt * 16 + col][k * 32 + quad * 8];
-      acc = mfma16x16x32(a[k], bq, acc);
+      for (int r = 0; r < 4; ++r) {
+        const int nt = nb + quad * 4 + r;
+        if (nt < n_tokens) qt[((size_t)nt * H + h) * RK + rt * 16 + col] = (half_t)(acc[r] * qscale);
+      }
     }
-    // D[token 4*quad + r][output col]
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int nt = nb + quad * 4 + r;
-      if (nt < n_tokens) qt[((size_t)nt * H + h) * RK + rt * 16 + col] = (half_t)(acc[r] * qscale);
-    }
-  }
   }
 }
 

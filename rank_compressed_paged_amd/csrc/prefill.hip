@@ -18,6 +18,10 @@
 //     queries' q~ as B (tokens x queries), then the online-softmax update of
 //     its 16 queries (lane = query, 4 tokens per page per lane; the max and
 //     sum across the four lanes of a query use the cross-row lane swaps).
+//     The key pages go through LDS (a three-step ring, each thread copying
+//     one 16-byte chunk per step), so each is fetched once per work group
+//     rather than once per query block: the per-CU load path, not the
+//     matrix cores, is the scarcest resource of this kernel.
 //   * values: wave w owns RV/NW features for all rows.  Per page,
 //     Z^T[f, row] += c_v[t, f] P[row, t] is v_mfma_f32_32x32x16_f16 with the
 //     feature-major value page as A (16 contiguous bytes per lane) and P as B
@@ -110,8 +114,9 @@ constexpr float kRaise = 8.f;           // lazy-rescale threshold (log2 units)
 //   DEPTH  steps of page operands held in the register ring (2 or 3)
 //   SCHED  instruction order inside a step: 0 left to the compiler, 1 score
 //          products, then the P.c_v products, then the softmax, 2 as 1 with
-//          the softmax's vector instructions interleaved between the products
-template <int H, int RK, int RV, int G, int MQ, int NW, int PPS, int DEPTH, int SCHED>
+//          the softmax's vector instructions interleaved between the products,
+//          3 as 1 with the step's loads issued after the products
+template <int H, int RK, int RV, int G, int MQ, int NW, int PPS, int DEPTH, int SCHED, bool KLDS>
 __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   static_assert(DEPTH >= 2 && DEPTH <= 3, "register ring of 2 or 3 steps");
   static_assert(PPS == 1 || PPS == 2, "one or two pages per step");
@@ -126,6 +131,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) float sAlpha[2][32][C::RT];
   __shared__ float sL[C::R];
   __shared__ __attribute__((aligned(16))) int sBlk[RING];
+  // KLDS: key pages of three steps, [step % 3][head][page][token][r_k + pad],
+  // each loaded once per work group and shared by the head's score waves
+  constexpr int LDKV = RK + 8;
+  __shared__ __attribute__((aligned(16))) half_t sK[KLDS ? 3 : 1][G][PPS][PBS][LDKV];
 
   // ---- work decode (XCD-aware when the batch allows it)
   const int units = a.n_qtiles * a.n_groups;
@@ -197,7 +206,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
 
   typedef kvec KSet[PPS][C::SUW][C::NKC];
   typedef half8 VSet[PPS][C::FTW];
-  KSet kr[DEPTH];  // ring of page operands in registers
+  KSet kr[KLDS ? 1 : DEPTH];  // ring of page operands in registers
   VSet vr[DEPTH];
   const int f_base = w * C::FTW * 32 + c32;  // feature of this lane in tile 0
   // per-lane element offsets inside one page (the page base is uniform, so
@@ -210,10 +219,16 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   auto block_of = [&](int page) {
     return __builtin_amdgcn_readfirstlane(sBlk[page & (RING - 1)]);
   };
-  auto load_k = [&](KSet& dst, int step) {
+  // block ids of the PPS pages of a step, read together (one LDS round trip)
+  typedef int StepIds[PPS];
+  auto ids_of = [&](StepIds& ids, int step) {
+#pragma unroll
+    for (int pg = 0; pg < PPS; ++pg) ids[pg] = block_of(step * PPS + pg);
+  };
+  auto load_k = [&](KSet& dst, const StepIds& ids) {
 #pragma unroll
     for (int pg = 0; pg < PPS; ++pg) {
-      const int blk = block_of(step * PPS + pg);
+      const int blk = ids[pg];
       const half_t* kp = a.k_cache + (size_t)(blk < 0 ? 0 : blk) * (H * PBS * RK);
 #pragma unroll
       for (int i = 0; i < C::SUW; ++i)
@@ -221,15 +236,57 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
         for (int c = 0; c < C::NKC; ++c) dst[pg][i][c] = *(const kvec*)(kp + k_off[i] + c * C::KC);
     }
   };
-  auto load_v = [&](VSet& dst, int step) {
+  auto load_v = [&](VSet& dst, const StepIds& ids) {
 #pragma unroll
     for (int pg = 0; pg < PPS; ++pg) {
-      const int blk = block_of(step * PPS + pg);
+      const int blk = ids[pg];
       const half_t* vp = a.v_cache + (size_t)(blk < 0 ? 0 : blk) * (RV * PBS);
 #pragma unroll
       for (int ft = 0; ft < C::FTW; ++ft)
         dst[pg][ft] = *(const half8*)(vp + v_off + ft * 32 * PBS);
     }
+  };
+
+  // KLDS staging: thread t copies 16-byte chunks of the step's key pages
+  constexpr int KCH = G * PPS * PBS * RK / 8 / (NW * 64);  // chunks per thread
+  static_assert(!KLDS || (KCH >= 1 && KCH * NW * 64 * 8 == G * PPS * PBS * RK), "key chunks");
+  half8 kst[KLDS ? KCH : 1];
+  auto kst_load = [&](const StepIds& ids) {
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      const int c = tid + j * NW * 64;
+      const int rc = c % (RK / 8), tok = (c / (RK / 8)) % PBS;
+      const int pg = (c / (RK / 8 * PBS)) % PPS, hl = c / (RK / 8 * PBS * PPS);
+      const int blk = ids[pg] < 0 ? 0 : ids[pg];
+      kst[j] = *(const half8*)(a.k_cache + (((size_t)blk * H + g * G + hl) * PBS + tok) * RK + rc * 8);
+    }
+  };
+  auto kst_store = [&](int kb) {
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) {
+      const int c = tid + j * NW * 64;
+      const int rc = c % (RK / 8), tok = (c / (RK / 8)) % PBS;
+      const int pg = (c / (RK / 8 * PBS)) % PPS, hl = c / (RK / 8 * PBS * PPS);
+      *(half8*)&sK[kb][hl][pg][tok][rc * 8] = kst[j];
+    }
+  };
+  // score products of the step whose keys are in LDS buffer kb
+  auto score_products_lds = [&](int kb, float4v (&sacc)[PPS][C::SUW]) {
+#pragma unroll
+    for (int pg = 0; pg < PPS; ++pg)
+#pragma unroll
+      for (int i = 0; i < C::SUW; ++i) {
+        const int hl = su_h[i] - g * G;
+        sacc[pg][i] = zero4();
+#pragma unroll
+        for (int c = 0; c < C::NKC; ++c) {
+          const kvec kk = *(const kvec*)&sK[kb][hl][pg][col][c * C::KC + quad * (C::KC / 4)];
+          if constexpr (C::KC == 32)
+            sacc[pg][i] = mfma16x16x32(kk, qv[i][c], sacc[pg][i]);
+          else
+            sacc[pg][i] = mfma16x16x16(kk, qv[i][c], sacc[pg][i]);
+        }
+      }
   };
 
   auto score_products = [&](const KSet& kk, float4v (&sacc)[PPS][C::SUW]) {
@@ -325,12 +382,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   // P.c_v of step s (values in vv, P in LDS buffer `buf`)
   // zero the value columns of tokens past the sequence (they may hold
   // anything, NaN included) and of pages with an invalid block id
-  auto mask_values = [&](VSet& vv, int s) {
+  auto mask_values = [&](VSet& vv, const StepIds& ids, int s) {
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int pg = 0; pg < PPS; ++pg) {
       const int page = s * PPS + pg;
-      const int nv = (block_of(page) >= 0) ? min(max(L - (page * PBS + hf * 8), 0), 8) : 0;
+      const int nv = (ids[pg] >= 0) ? min(max(L - (page * PBS + hf * 8), 0), 8) : 0;
 #pragma unroll
       for (int ft = 0; ft < C::FTW; ++ft) {
         u4 bits = __builtin_bit_cast(u4, vv[pg][ft]);
@@ -341,44 +398,78 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
       }
     }
   };
-  auto value_products = [&](bool mask, VSet& vv, int s, int buf) {
-    if (mask) mask_values(vv, s);  // uniform
+  auto value_products = [&](bool mask, VSet& vv, const StepIds& ids, int s, int buf) {
+    if (mask) mask_values(vv, ids, s);  // uniform
 #pragma unroll
-    for (int pg = 0; pg < PPS; ++pg)
+    for (int pg = 0; pg < PPS; ++pg) {
+      // all row tiles' P fragments of the page are requested before its
+      // first product, so the page waits for LDS once
+      half8 pb[C::RT];
 #pragma unroll
-      for (int rt = 0; rt < C::RT; ++rt) {
-        const half8 pb = *(const half8*)&sP[buf][pg][rt][hf][c32][0];
+      for (int rt = 0; rt < C::RT; ++rt) pb[rt] = *(const half8*)&sP[buf][pg][rt][hf][c32][0];
+      if constexpr (SCHED != 2) __builtin_amdgcn_sched_barrier(0);  // keep the reads together
 #pragma unroll
-        for (int ft = 0; ft < C::FTW; ++ft) acc[rt][ft] = mfma32x32x16(vv[pg][ft], pb, acc[rt][ft]);
-      }
+      for (int rt = 0; rt < C::RT; ++rt)
+#pragma unroll
+        for (int ft = 0; ft < C::FTW; ++ft) acc[rt][ft] = mfma32x32x16(vv[pg][ft], pb[rt], acc[rt][ft]);
+    }
   };
   // every token of step s visible to every row, and every page valid
-  auto step_plain_scores = [&](int s) {
+  auto step_plain_scores = [&](const StepIds& ids, int s) {
     bool ok = (s * PPS + PPS) * PBS - 1 <= lim_min;
 #pragma unroll
-    for (int pg = 0; pg < PPS; ++pg) ok = ok && block_of(s * PPS + pg) >= 0;
+    for (int pg = 0; pg < PPS; ++pg) ok = ok && ids[pg] >= 0;
     return ok;
   };
-  auto step_plain_values = [&](int s) {
+  auto step_plain_values = [&](const StepIds& ids, int s) {
     bool ok = (s * PPS + PPS) * PBS <= L;
 #pragma unroll
-    for (int pg = 0; pg < PPS; ++pg) ok = ok && block_of(s * PPS + pg) >= 0;
+    for (int pg = 0; pg < PPS; ++pg) ok = ok && ids[pg] >= 0;
     return ok;
   };
 
   // ---- prologue: block ids staged, keys of steps 0..DEPTH-1 and values of
   // steps 0..DEPTH-2 in flight, step 0 scored
   block_sync_lds();
+  if constexpr (KLDS) {
+    // keys of steps 0 and 1 into LDS buffers 0 and 1, step 2's in flight
 #pragma unroll
-  for (int j = 0; j < DEPTH; ++j) load_k(kr[j], j);
+    for (int j = 0; j < 2; ++j) {
+      StepIds ids;
+      ids_of(ids, j);
+      kst_load(ids);
+      kst_store(j);
+    }
+    StepIds ids2;
+    ids_of(ids2, 2);
+    kst_load(ids2);
 #pragma unroll
-  for (int j = 0; j + 1 < DEPTH; ++j) load_v(vr[j], j);
+    for (int j = 0; j + 1 < DEPTH; ++j) {
+      StepIds ids;
+      ids_of(ids, j);
+      load_v(vr[j], ids);
+    }
+    block_sync_lds();
+  } else {
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) {
+      StepIds ids;
+      ids_of(ids, j);
+      load_k(kr[j], ids);
+      if (j + 1 < DEPTH) load_v(vr[j], ids);
+    }
+  }
   {
     float4v sacc[PPS][C::SUW];
-    score_products(kr[0], sacc);
+    if constexpr (KLDS)
+      score_products_lds(0, sacc);
+    else
+      score_products(kr[0], sacc);
+    StepIds ids0;
+    ids_of(ids0, 0);
     bool ok0[PPS];
 #pragma unroll
-    for (int pg = 0; pg < PPS; ++pg) ok0[pg] = block_of(pg) >= 0;
+    for (int pg = 0; pg < PPS; ++pg) ok0[pg] = ids0[pg] >= 0;
     softmax(std::false_type{}, true, ok0, sacc, 0, 0);
   }
   // nothing of the prologue stays in flight into the loop, so the loop's
@@ -392,28 +483,53 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   auto step = [&](auto phase, int s) {
     constexpr int PH = decltype(phase)::value;
     int staged[PPS];
+    // block ids of every step this one touches, read together up front
+    StepIds id_c, id_s, id_v, id_k;  // steps s, s+1, s+DEPTH-1, s+DEPTH (KLDS: s+3)
+    ids_of(id_c, s);
+    ids_of(id_s, s + 1);
+    ids_of(id_v, s + DEPTH - 1);
+    ids_of(id_k, KLDS ? s + 3 : s + DEPTH);
+    // loads for the keys of step s+DEPTH and the values of step s+DEPTH-1
+    // (their ring slots were consumed last step)
+    auto issue_loads = [&]() {
 #pragma unroll
-    for (int pg = 0; pg < PPS; ++pg)  // issued before the page loads
-      staged[pg] = fetch_block((s - 1) * PPS + pg + RING);
-    load_k(kr[PH], s + DEPTH);                      // keys of step s were scored last step
-    load_v(vr[(PH + DEPTH - 1) % DEPTH], s + DEPTH - 1);  // values of step s-1 were used last step
+      for (int pg = 0; pg < PPS; ++pg) staged[pg] = fetch_block((s - 1) * PPS + pg + RING);
+      if constexpr (KLDS) {
+        kst_store((s + 2) % 3);  // keys of step s+2 (loaded last step) into LDS
+        kst_load(id_k);          // keys of step s+3
+      } else {
+        load_k(kr[PH], id_k);
+      }
+      load_v(vr[(PH + DEPTH - 1) % DEPTH], id_v);
+    };
+    if constexpr (SCHED != 3) issue_loads();
     float4v sacc[PPS][C::SUW];
-    score_products(kr[(PH + 1) % DEPTH], sacc);
+    if constexpr (KLDS)
+      score_products_lds((s + 1) % 3, sacc);
+    else
+      score_products(kr[(PH + 1) % DEPTH], sacc);
     const int buf = s & 1;
     rescale(buf);
-    const bool vmask = !step_plain_values(s);
-    const bool smask = !step_plain_scores(s + 1);
+    const bool vmask = !step_plain_values(id_c, s);
+    const bool smask = !step_plain_scores(id_s, s + 1);
     if constexpr (SCHED >= 1) __builtin_amdgcn_sched_barrier(0);
     if constexpr (SCHED == 2) {  // masks ahead of the interleaved region
-      if (vmask) mask_values(vr[PH], s);
-      value_products(false, vr[PH], s, buf);
+      if (vmask) mask_values(vr[PH], id_c, s);
+      value_products(false, vr[PH], id_c, s, buf);
     } else {
-      value_products(vmask, vr[PH], s, buf);
+      value_products(vmask, vr[PH], id_c, s, buf);
     }
-    if constexpr (SCHED == 1) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SCHED == 3) {
+      // the loads go out behind the products: the per-CU load path is the
+      // busiest resource, and its back-pressure then stalls the wave while
+      // the matrix cores are busy rather than before they start
+      __builtin_amdgcn_sched_barrier(0);
+      issue_loads();
+    }
+    if constexpr (SCHED == 1 || SCHED == 3) __builtin_amdgcn_sched_barrier(0);
     bool ok_s[PPS];
 #pragma unroll
-    for (int pg = 0; pg < PPS; ++pg) ok_s[pg] = block_of((s + 1) * PPS + pg) >= 0;
+    for (int pg = 0; pg < PPS; ++pg) ok_s[pg] = id_s[pg] >= 0;
     if constexpr (SCHED == 2)
       softmax(std::true_type{}, smask, ok_s, sacc, s + 1, buf ^ 1);
     else
@@ -472,7 +588,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   }
 }
 
-template <int H, int D, int RK, int RV, int G, int MQ, int NW, int PPS, int DEPTH, int SCHED>
+template <int H, int D, int RK, int RV, int G, int MQ, int NW, int PPS, int DEPTH, int SCHED,
+          bool KLDS = false>
 static hipError_t prefill_instance(const void* qt, const int32_t* qsl, int max_query_len,
                                    const void* k_cache, const void* v_cache, const void* W,
                                    const int32_t* block_tables, int max_blocks,
@@ -492,7 +609,7 @@ static hipError_t prefill_instance(const void* qt, const int32_t* qsl, int max_q
   a.n_qtiles = (max_query_len + MQ - 1) / MQ;
   a.n_groups = H / G;
   const long wgs = (long)batch * a.n_qtiles * a.n_groups;
-  launch_hooked(TIME_PREFILL_ATTN, TIME_NONE, prefill_attn_kernel<H, RK, RV, G, MQ, NW, PPS, DEPTH, SCHED>,
+  launch_hooked(TIME_PREFILL_ATTN, TIME_NONE, prefill_attn_kernel<H, RK, RV, G, MQ, NW, PPS, DEPTH, SCHED, KLDS>,
                 dim3((unsigned)wgs), dim3(NW * 64), st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -520,15 +637,14 @@ hipError_t launch_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl,
       batch, total_q, z, out, st
   if (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) {
     switch (prefill_variant()) {
-      case 1: return prefill_instance<32, 128, 64, 512, 4, 32, 8, 2, 2, 1>(STARKV_PREFILL_ARGS);
-      case 2: return prefill_instance<32, 128, 64, 512, 4, 32, 8, 2, 2, 2>(STARKV_PREFILL_ARGS);
-      case 3: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 2, 1>(STARKV_PREFILL_ARGS);
-      case 4: return prefill_instance<32, 128, 64, 512, 4, 32, 8, 1, 2, 1>(STARKV_PREFILL_ARGS);
-      default: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 2, 2>(STARKV_PREFILL_ARGS);
+      case 1: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 2, 1, true>(STARKV_PREFILL_ARGS);
+      case 2: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 2, 2, false>(STARKV_PREFILL_ARGS);
+      case 3: return prefill_instance<32, 128, 64, 512, 4, 32, 8, 2, 2, 2, true>(STARKV_PREFILL_ARGS);
+      default: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 2, 2, true>(STARKV_PREFILL_ARGS);
     }
   }
   if (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64)
-    return prefill_instance<4, 64, 16, 64, 4, 16, 2, 2, 2, 1>(STARKV_PREFILL_ARGS);
+    return prefill_instance<4, 64, 16, 64, 4, 16, 2, 2, 2, 1, true>(STARKV_PREFILL_ARGS);
 #undef STARKV_PREFILL_ARGS
   return hipErrorInvalidValue;
 }
