@@ -105,8 +105,8 @@ PrefillWorkspace prefill_workspace_layout(const ShapeKey& s, int total_q) {
   size_t off = 0;
   w.qt_off = off;
   off = align256(off + (size_t)total_q * s.H * s.rk * 2);
-  w.z_off = off;
-  off = align256(off + (size_t)total_q * s.H * s.rv * 4);
+  w.z_off = off;  // fp16 z tiled by 32-token blocks, see launch_upproj
+  off = align256(off + (size_t)((total_q + 31) / 32) * 32 * s.H * s.rv * 2);
   w.total = off;
   return w;
 }
@@ -282,7 +282,7 @@ starkv_status starkv_prefill_attn(const starkv_dims* dims, const void* q,
   if (e != hipSuccess) return STARKV_ERR_LAUNCH;
   e = launch_prefill(key, wb + ws.qt_off, query_start_loc, total_q, max_query_len, k_cache,
                      v_cache, W, block_tables, max_blocks_per_seq, seq_lens, dims->num_blocks,
-                     batch, (float*)(wb + ws.z_off), out, s);
+                     batch, (void*)(wb + ws.z_off), out, s);
   return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
 }
 

@@ -547,20 +547,21 @@ __global__ __launch_bounds__(256) void upproj_small_kernel(const half_t* __restr
 // fp16) is staged once per work group in LDS, padded so that each 16-lane
 // group of a 16-byte read hits distinct banks; then every wave streams 32
 // tokens of z through v_mfma_f32_32x32x16_f16 with no further barrier:
-// A = z rows (32 tokens x 16 features, split into fp16 hi/lo, 32 contiguous
-// bytes of fp32 per lane), B = W_h^T (16 features x 32 outputs, from LDS),
+// A = z (32 tokens x 16 features, fp16; z arrives tiled in exactly this
+// operand order, so each lane's 16 bytes and each wave's KiB are
+// contiguous), B = W_h^T (16 features x 32 outputs, from LDS),
 // D[token][output].  The z loads run up to 16 chunks ahead of their
-// products: z rows come from HBM, and the LDS footprint already limits the
+// products: z comes from HBM, and the LDS footprint already limits the
 // kernel to two waves per SIMD, which leaves the registers for the ring.
 template <int H, int D, int RV, int NW>
-__global__ __launch_bounds__(NW * 64) void upproj_wide_kernel(const half_t* __restrict__ W,
-                                                              const float* __restrict__ z,
-                                                              int n_tokens,
-                                                              half_t* __restrict__ out) {
+__global__ __launch_bounds__(NW * 64) void upproj_tiled_kernel(const half_t* __restrict__ W,
+                                                               const half_t* __restrict__ z,
+                                                               int n_tokens,
+                                                               half_t* __restrict__ out) {
   constexpr int LDW = RV + 8;  // halves per LDS row
   constexpr int DT = D / 32;   // 32-wide output tiles
   constexpr int KC = RV / 16;  // 16-feature chunks
-  constexpr int ZP = KC < 16 ? KC : 16;  // z chunks in flight (LDS limits occupancy anyway)
+  constexpr int ZP = KC < 16 ? KC : 16;  // z chunks in flight
   static_assert(D % 32 == 0 && RV % 16 == 0 && KC >= ZP, "tile shape");
   typedef float float16v __attribute__((ext_vector_type(16)));
   __shared__ __attribute__((aligned(16))) half_t sW[D][LDW];
@@ -575,35 +576,29 @@ __global__ __launch_bounds__(NW * 64) void upproj_wide_kernel(const half_t* __re
   __syncthreads();
   const int t0 = blockIdx.y * (NW * 32) + w * 32;
   if (t0 >= n_tokens) return;  // no barrier follows
-  const int tok = min(t0 + c32, n_tokens - 1);  // rows past the end repeat the last token
-  const float* zr = z + ((size_t)tok * H + h) * RV + 8 * hf;
+  // tiled z: block t0/32 of head h, chunk kc at +kc*512, this lane's 8
+  // halves at +lane*8 (rows past n_tokens in the last block hold stale
+  // values and are never stored)
+  const half_t* zr = z + ((size_t)h * ((n_tokens + 31) / 32) + t0 / 32) * KC * 512 + lane * 8;
   float16v acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
-  float4v zq[ZP][2];
+  half8 zq[ZP];
 #pragma unroll
-  for (int j = 0; j < ZP; ++j) {
-    zq[j][0] = *(const float4v*)(zr + j * 16);
-    zq[j][1] = *(const float4v*)(zr + j * 16 + 4);
-  }
+  for (int j = 0; j < ZP; ++j) zq[j] = *(const half8*)(zr + j * 512);
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
-    half8 hi, lo;
-    split_f16x8(zq[kc % ZP][0], zq[kc % ZP][1], hi, lo);
-    if (kc + ZP < KC) {
-      zq[kc % ZP][0] = *(const float4v*)(zr + (kc + ZP) * 16);
-      zq[kc % ZP][1] = *(const float4v*)(zr + (kc + ZP) * 16 + 4);
-    }
+    const half8 av = zq[kc % ZP];
+    if (kc + ZP < KC) zq[kc % ZP] = *(const half8*)(zr + (kc + ZP) * 512);
     // keep the refill issued here, ZP chunks ahead of its use, instead of
     // letting the scheduler sink it next to the products that consume it
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const half8 b = *(const half8*)&sW[dt * 32 + c32][kc * 16 + 8 * hf];
-      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi, b, acc[dt], 0, 0, 0);
-      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lo, b, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, b, acc[dt], 0, 0, 0);
     }
   }
   // register i of tile dt holds token 8*(i/4) + 4*hf + i%4, output dt*32 + c32
@@ -619,11 +614,23 @@ __global__ __launch_bounds__(NW * 64) void upproj_wide_kernel(const half_t* __re
 }
 
 template <int H, int D, int RV, int NW>
-static void launch_upproj_wide(const void* W, const float* z, int n_tokens, void* out,
-                               hipStream_t st) {
-  hipLaunchKernelGGL((upproj_wide_kernel<H, D, RV, NW>),
+static void launch_upproj_tiled_t(const void* W, const void* z, int n_tokens, void* out,
+                                  hipStream_t st) {
+  hipLaunchKernelGGL((upproj_tiled_kernel<H, D, RV, NW>),
                      dim3(H, (n_tokens + NW * 32 - 1) / (NW * 32)), dim3(NW * 64), 0, st,
-                     (const half_t*)W, z, n_tokens, (half_t*)out);
+                     (const half_t*)W, (const half_t*)z, n_tokens, (half_t*)out);
+}
+
+hipError_t launch_upproj_tiled(const ShapeKey& s, const void* W, const void* z_tiled,
+                               int n_tokens, void* out, hipStream_t st) {
+  if (n_tokens <= 0) return hipSuccess;
+  if (s.H == 32 && s.d == 128 && s.rv == 512)
+    launch_upproj_tiled_t<32, 128, 512, 8>(W, z_tiled, n_tokens, out, st);
+  else if (s.H == 4 && s.d == 64 && s.rv == 64)
+    launch_upproj_tiled_t<4, 64, 64, 4>(W, z_tiled, n_tokens, out, st);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 template <int H, int D, int RV, int DR>
@@ -633,15 +640,13 @@ static void launch_upproj_t(const void* W, const float* z, int n_tokens, void* o
 }
 
 hipError_t launch_upproj(const ShapeKey& s, const void* W, const float* z, int n_tokens,
-                         bool wide_rows, void* out, hipStream_t st) {
+                         void* out, hipStream_t st) {
   if (n_tokens <= 0) return hipSuccess;
   if (s.H == 32 && s.d == 128 && s.rv == 512) {
-    if (wide_rows) launch_upproj_wide<32, 128, 512, 8>(W, z, n_tokens, out, st);
-    else hipLaunchKernelGGL((upproj_small_kernel<32, 128, 512>), dim3(32, 128 / 16), dim3(256), 0,
-                            st, (const half_t*)W, z, n_tokens, (half_t*)out);
+    hipLaunchKernelGGL((upproj_small_kernel<32, 128, 512>), dim3(32, 128 / 16), dim3(256), 0, st,
+                       (const half_t*)W, z, n_tokens, (half_t*)out);
   } else if (s.H == 4 && s.d == 64 && s.rv == 64) {
-    if (wide_rows) launch_upproj_wide<4, 64, 64, 4>(W, z, n_tokens, out, st);
-    else launch_upproj_t<4, 64, 64, 16>(W, z, n_tokens, out, st);
+    launch_upproj_t<4, 64, 64, 16>(W, z, n_tokens, out, st);
   } else {
     return hipErrorInvalidValue;
   }
@@ -667,7 +672,7 @@ static hipError_t decode_instance(const DecodePlan& p, const void* qt, const voi
                      p.pages_per_split, p.num_splits, z);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_upproj(ShapeKey{H, D, RK, RV}, W, z, batch, false, out, st);
+  return launch_upproj(ShapeKey{H, D, RK, RV}, W, z, batch, out, st);
 }
 
 template <int H, int D, int RK>

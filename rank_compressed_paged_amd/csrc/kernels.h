@@ -78,8 +78,16 @@ hipError_t launch_decode(const ShapeKey& s, const DecodePlan& p, const void* qt,
 
 // out[n, h, :] = W_h z[n, h, :]; wide_rows picks the prefill tiling (one
 // work group per head and 64 tokens) over the decode tiling (16 rows).
+// out[n, h, :] = W_h z[n, h, :].  Few tokens (launch_upproj): z is
+// [n][H][RV] fp32, split into an fp16 hi/lo pair at the products.  Many
+// tokens (launch_upproj_tiled, prefill): z is fp16, tiled in the A-operand
+// order of the up-projection's 32x32x16 products, [H][ceil(n/32)][RV/16][64][8],
+// where lane l of 16-feature chunk kc of a 32-token block holds token l%32,
+// features 16*kc + 8*(l/32) .. +7 (prefill writes it that way).
 hipError_t launch_upproj(const ShapeKey& s, const void* W, const float* z, int n_tokens,
-                         bool wide_rows, void* out, hipStream_t st);
+                         void* out, hipStream_t st);
+hipError_t launch_upproj_tiled(const ShapeKey& s, const void* W, const void* z_tiled,
+                               int n_tokens, void* out, hipStream_t st);
 
 // Measurement aid: read `bytes` (a multiple of 16) with 16-byte loads and
 // fold them into one word per work group, so nothing is optimised away.
@@ -92,7 +100,7 @@ hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const 
 hipError_t launch_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl, int total_q,
                           int max_query_len, const void* k_cache, const void* v_cache,
                           const void* W, const int32_t* block_tables, int max_blocks,
-                          const int32_t* seq_lens, int num_blocks, int batch, float* z,
+                          const int32_t* seq_lens, int num_blocks, int batch, void* z,
                           void* out, hipStream_t st);
 
 }  // namespace starkv

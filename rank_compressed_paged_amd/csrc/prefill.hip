@@ -7,8 +7,9 @@
 //   S^T[t, j] = c_k[t, h] . q~[j, h]          (q~ pre-scaled by scale*log2 e)
 //   P = causal softmax over t <= P0 + j, P0 = seq_len - chunk_len
 //   Z^T[f, j] = sum_t c_v[t, f] P[j, t]        (normalised at the end)
-// and writes z [total_q, H, r_v] fp32; the up-projection out_h = W_h z_h
-// runs afterwards on the matrix cores (decode.hip, wide tiling).
+// and writes z as fp16 (tiled by 32-token blocks in the operand order of the
+// up-projection); the up-projection out_h = W_h z_h runs afterwards on the
+// matrix cores (decode.hip, many-token variant).
 //
 // Work group = (request, tile of MQ queries, group of G heads), NW waves;
 // the main shape runs G = 2 heads x MQ = 64 queries = 128 (head, query) rows
@@ -100,8 +101,8 @@ struct PrefillArgs {
   const half_t* v_cache;
   const int32_t* block_tables;
   const int32_t* seq_lens;
-  float* z;  // [total_q, H, RV]
-  int max_blocks, num_blocks, batch, n_qtiles, n_groups;
+  half_t* z;  // fp16, tiled [H][n_tb][RV/16][64][8], see launch_upproj_tiled
+  int max_blocks, num_blocks, batch, n_qtiles, n_groups, n_tb;
 };
 
 constexpr int PBS = 16;                 // tokens per page
@@ -575,15 +576,20 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
     if (r_j >= Cn) continue;
     const float lr = sL[row];
     const float inv = lr > 0.f ? 1.f / lr : 0.f;
-    float* zr = a.z + ((size_t)(q_begin + r_j) * H + r_h) * RV + f_base - c32 + 4 * hf;
+    // z tiled for the up-projection: [head][token / 32][feature / 16][lane][8]
+    // with lane = token % 32 + 32 * ((feature / 8) % 2)
+    const int tok = q_begin + r_j;
+    half_t* zb = a.z + ((size_t)r_h * a.n_tb + tok / 32) * (RV / 16) * 512;
 #pragma unroll
     for (int ft = 0; ft < C::FTW; ++ft)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        float4v o;
+        // features f_base - c32 + 32*ft + 8*jj + 4*hf + 0..3
+        const int f0 = f_base - c32 + ft * 32 + 8 * jj;
+        half4 o;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = acc[rt][ft][4 * jj + r] * inv;
-        *(float4v*)(zr + ft * 32 + 8 * jj) = o;
+        for (int r = 0; r < 4; ++r) o[r] = (half_t)(acc[rt][ft][4 * jj + r] * inv);
+        *(half4*)(zb + (f0 / 16) * 512 + (tok % 32 + 32 * ((f0 / 8) % 2)) * 8 + 4 * hf) = o;
       }
   }
 }
@@ -594,7 +600,7 @@ static hipError_t prefill_instance(const void* qt, const int32_t* qsl, int max_q
                                    const void* k_cache, const void* v_cache, const void* W,
                                    const int32_t* block_tables, int max_blocks,
                                    const int32_t* seq_lens, int num_blocks, int batch,
-                                   int total_q, float* z, void* out, hipStream_t st) {
+                                   int total_q, void* z, void* out, hipStream_t st) {
   PrefillArgs a;
   a.qt = (const half_t*)qt;
   a.qsl = qsl;
@@ -602,18 +608,19 @@ static hipError_t prefill_instance(const void* qt, const int32_t* qsl, int max_q
   a.v_cache = (const half_t*)v_cache;
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
-  a.z = z;
+  a.z = (half_t*)z;
   a.max_blocks = max_blocks;
   a.num_blocks = num_blocks;
   a.batch = batch;
   a.n_qtiles = (max_query_len + MQ - 1) / MQ;
   a.n_groups = H / G;
+  a.n_tb = (total_q + 31) / 32;
   const long wgs = (long)batch * a.n_qtiles * a.n_groups;
   launch_hooked(TIME_PREFILL_ATTN, TIME_NONE, prefill_attn_kernel<H, RK, RV, G, MQ, NW, PPS, DEPTH, SCHED, KLDS>,
                 dim3((unsigned)wgs), dim3(NW * 64), st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_upproj(ShapeKey{H, D, RK, RV}, W, z, total_q, true, out, st);
+  return launch_upproj_tiled(ShapeKey{H, D, RK, RV}, W, z, total_q, out, st);
 }
 
 // Kernel variant (tuning aid, STARKV_PREFILL_VARIANT): head group, query
@@ -629,7 +636,7 @@ static int prefill_variant() {
 hipError_t launch_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl, int total_q,
                           int max_query_len, const void* k_cache, const void* v_cache,
                           const void* W, const int32_t* block_tables, int max_blocks,
-                          const int32_t* seq_lens, int num_blocks, int batch, float* z, void* out,
+                          const int32_t* seq_lens, int num_blocks, int batch, void* z, void* out,
                           hipStream_t st) {
   if (batch <= 0 || total_q <= 0) return hipSuccess;
 #define STARKV_PREFILL_ARGS                                                                    \

@@ -86,7 +86,8 @@ def test_prefill_validation():
     d = _main_dims()
     f = sk.lib().starkv_prefill_attn
     need = sk.prefill_workspace_size(d, 16, 4096, 4352)
-    assert need >= 4096 * 32 * (64 * 2 + 512 * 4)
+    # q~ (fp16, r_k per head) and z (fp16, r_v per head) of every chunk query
+    assert need >= 4096 * 32 * (64 * 2 + 512 * 2)
     args = lambda **kw: dict(dict(q=FAKE, qsl=FAKE, T=4096, mq=256, kc=FAKE, vc=FAKE, U=FAKE,
                                   W=FAKE, bt=FAKE, mb=272, sl=FAKE, B=16, msl=4352, scale=0.088,
                                   out=FAKE, ws=FAKE, wsb=0), **kw)
