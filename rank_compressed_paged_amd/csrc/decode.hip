@@ -59,14 +59,16 @@ constexpr int kMaxSplitPages = 256;  // planner bound on pages per split
 // ---------------------------------------------------------------------------
 // 1. q~[n, h, :] = (scale*log2e) * U_h^T q[n, h, :]  -> fp16
 // grid (H, ceil(N/(64*TPW))), 4 waves; in token tile tt the wave w owns
-// tokens n0+16w .. n0+16w+15 of that tile's 64.  A = q (16 tokens x 32 of
-// d, 16 contiguous bytes per lane).  B = U_h, staged in LDS as it is in
-// memory ([d][r], 16-byte stores) and read through the transposing LDS read
-// (ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives
-// element i%4 of the 8-byte chunk addressed by lane 4e + i/4, e = 0..3), so
-// that each lane gets 8 consecutive d of one r.  The first tile's q rows are
-// requested before the staging, so the two memory round trips overlap; TPW
-// tiles per work group amortise the staging over many tokens.
+// tokens n0+16w .. n0+16w+15 of that tile's 64.  The product is taken as
+// q~^T = U_h^T q^T, so that each lane ends with 4 consecutive outputs of one
+// token (one 8-byte store): A = U_h^T (16 outputs x 32 of d), read from
+// U_h staged in LDS as it is in memory ([d][r], 16-byte stores) through the
+// transposing LDS read (ds_read_b64_tr_b16: within each group of 16 lanes,
+// lane i receives element i%4 of the 8-byte chunk addressed by lane
+// 4e + i/4, e = 0..3, so lane i gets 4 consecutive d of output r0 + i);
+// B = q^T (32 of d x 16 tokens, 16 contiguous bytes per lane).  The first
+// tile's q rows are requested before the staging, so the two memory round
+// trips overlap; TPW tiles per work group amortise the staging.
 // ---------------------------------------------------------------------------
 typedef short short4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ half4 lds_read_tr16(const half_t* p) {
@@ -85,15 +87,15 @@ __global__ __launch_bounds__(256) void qproj_kernel(const half_t* __restrict__ q
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
-  auto load_q = [&](half8 (&a)[D / 32], int nb) {
+  auto load_q = [&](half8 (&b)[D / 32], int nb) {
     const int n = min(nb + col, n_tokens - 1);  // rows past the end are not stored
     const half_t* qrow = q + ((size_t)n * H + h) * D + quad * 8;
 #pragma unroll
-    for (int k = 0; k < D / 32; ++k) a[k] = *(const half8*)(qrow + k * 32);
+    for (int k = 0; k < D / 32; ++k) b[k] = *(const half8*)(qrow + k * 32);
   };
-  half8 a[D / 32];
+  half8 bq[D / 32];
   const int nb0 = blockIdx.y * TPW * 64 + w * 16;
-  if (nb0 < n_tokens) load_q(a, nb0);
+  if (nb0 < n_tokens) load_q(bq, nb0);
   const half_t* Uh = U + (size_t)h * D * RK;
   for (int c = tid; c < D * RK / 8; c += 256) {
     const int i = c / (RK / 8), r0 = (c % (RK / 8)) * 8;
@@ -103,24 +105,26 @@ __global__ __launch_bounds__(256) void qproj_kernel(const half_t* __restrict__ q
   for (int tt = 0; tt < TPW; ++tt) {
     const int nb = nb0 + tt * 64;
     if (nb >= n_tokens) break;  // wave-uniform; no barrier follows
-    if (tt > 0) load_q(a, nb);
+    if (tt > 0) load_q(bq, nb);
 #pragma unroll
     for (int rt = 0; rt < RK / 16; ++rt) {
       float4v acc = zero4();
 #pragma unroll
       for (int k = 0; k < D / 32; ++k) {
-        // B fragment: d = 32k + 8*quad .. +7 of output r = 16*rt + col
-        const half_t* bp = &sU[k * 32 + quad * 8 + (col >> 2)][rt * 16 + 4 * (col & 3)];
-        const half4 b0 = lds_read_tr16(bp);
-        const half4 b1 = lds_read_tr16(bp + 4 * LDU);
-        const half8 bq = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-        acc = mfma16x16x32(a[k], bq, acc);
+        // A fragment: outputs 16*rt + col, d = 32k + 8*quad .. +7
+        const half_t* ap = &sU[k * 32 + quad * 8 + (col >> 2)][rt * 16 + 4 * (col & 3)];
+        const half4 a0 = lds_read_tr16(ap);
+        const half4 a1 = lds_read_tr16(ap + 4 * LDU);
+        const half8 au = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        acc = mfma16x16x32(au, bq[k], acc);
       }
-      // D[token 4*quad + r][output col]
+      // D[output 4*quad + r][token col]: four consecutive outputs of one token
+      const int nt = nb + col;
+      if (nt < n_tokens) {
+        half4 o;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int nt = nb + quad * 4 + r;
-        if (nt < n_tokens) qt[((size_t)nt * H + h) * RK + rt * 16 + col] = (half_t)(acc[r] * qscale);
+        for (int r = 0; r < 4; ++r) o[r] = (half_t)(acc[r] * qscale);
+        *(half4*)(qt + ((size_t)nt * H + h) * RK + rt * 16 + quad * 4) = o;
       }
     }
   }
