@@ -46,7 +46,7 @@ COPY_BYTES = 256 << 20         # plain copy used to calibrate the HBM counters
 DECODE_KERNEL = "decode_split_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_decode_b16_traffic.txt")
 TRAFFIC_WORKLOAD = "decode_b16"
-SPLIT_SECTION = ("// 2. split-K latent attention", "// 3. combine")
+SPLIT_SECTION = ("// 2. split-K latent attention", "// 3. finish")
 
 
 def kernel_source_hash():

@@ -51,18 +51,25 @@ static int device_cus() {
 // staged in LDS).  Environment overrides (tuning aids):
 // STARKV_DECODE_TARGET_WGS / STARKV_DECODE_MIN_PAGES switch to a fixed
 // target of work groups with a minimum split length.
+static DecodePlan with_stride(DecodePlan p) {
+  const int cb = p.num_splits <= 4 ? 4 : 16;
+  p.split_stride = cdiv(p.num_splits, cb) * cb;
+  return p;
+}
+
 DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int bs) {
   (void)s;
   const int pages = cdiv(max_seq_len, bs);
   const int variant = env_int("STARKV_DECODE_VARIANT", 0);
-  if (pages <= 0 || batch <= 0) return DecodePlan{1, 1, variant};
+  const int ftb = env_int("STARKV_DECODE_FINISH_TB", 2);  // merge + up-projection tile
+  if (pages <= 0 || batch <= 0) return with_stride(DecodePlan{1, 1, variant, ftb, 0});
   const int target = env_int("STARKV_DECODE_TARGET_WGS", 0);
   if (target > 0) {
     const int min_pps = env_int("STARKV_DECODE_MIN_PAGES", 1);
     int pps = cdiv(pages, cdiv(target, batch));
     if (pps < min_pps) pps = min_pps;
     if (pps > 256) pps = 256;
-    return DecodePlan{pps, cdiv(pages, pps), variant};
+    return with_stride(DecodePlan{pps, cdiv(pages, pps), variant, ftb, 0});
   }
   const int cus = device_cus();
   double best = 1e300;
@@ -79,7 +86,7 @@ DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int bs) {
     }
     if (ns > 4 * cus) break;
   }
-  return DecodePlan{best_pps, cdiv(pages, best_pps), variant};
+  return with_stride(DecodePlan{best_pps, cdiv(pages, best_pps), variant, ftb, 0});
 }
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -91,11 +98,9 @@ DecodeWorkspace decode_workspace_layout(const ShapeKey& s, int batch, const Deco
   w.qt_off = off;
   off = align256(off + (size_t)batch * s.H * s.rk * 2);
   w.ml_off = off;
-  off = align256(off + (size_t)batch * p.num_splits * 2 * r16 * 4);
-  w.acc_off = off;
-  off = align256(off + (size_t)batch * p.num_splits * r16 * s.rv * 4);
-  w.z_off = off;
-  off = align256(off + (size_t)batch * s.H * s.rv * 4);
+  off = align256(off + (size_t)batch * p.split_stride * 2 * r16 * 4);
+  w.zp_off = off;  // per-split z rows, fp16
+  off = align256(off + (size_t)batch * p.split_stride * r16 * s.rv * 2);
   w.total = off;
   return w;
 }
@@ -238,8 +243,7 @@ starkv_status starkv_decode_attn(const starkv_dims* dims, const void* q, const v
   if (e != hipSuccess) return STARKV_ERR_LAUNCH;
   e = launch_decode(key, p, wb + ws.qt_off, k_cache, v_cache, W, block_tables,
                     max_blocks_per_seq, seq_lens, dims->num_blocks, batch,
-                    (float*)(wb + ws.ml_off), (float*)(wb + ws.acc_off), (float*)(wb + ws.z_off),
-                    out, s);
+                    (float*)(wb + ws.ml_off), wb + ws.zp_off, out, s);
   return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
 }
 

@@ -8,16 +8,16 @@
 // output is the matmul out_h = W_h z_h (the "matmul per step" of the
 // README's "Per-decode-step attention" notes), W_h being rows h*d..h*d+d-1.
 //
-// One decode step is four launches on the caller's stream:
+// One decode step is three launches on the caller's stream:
 //   1. qproj        q~ = U_h^T q, pre-scaled by scale*log2(e), fp16, on the
-//                   matrix cores (U_h staged transposed in LDS)
+//                   matrix cores (U_h read through the transposing LDS read)
 //   2. decode_split split-K pass over the pages (README, "Kernel profiling
 //                   breakdown": split-K attention plus a combine); one work
 //                   group owns all heads of a run of pages so the joint value
 //                   latent of each token is read from HBM exactly once
-//   3. combine      log-sum-exp merge of the splits -> z [B, H, r_v] fp32
-//   4. upproj       out_h = W_h z_h on the matrix cores, z split into an
-//                   fp16 hi/lo pair so the product keeps fp32 accuracy
+//   3. finish       log-sum-exp merge of the splits, then out_h = W_h z_h on
+//                   the matrix cores, z split into an fp16 hi/lo pair so the
+//                   product keeps fp32 accuracy
 //
 // decode_split per page (16 tokens) in a work group of NW waves:
 //   * scores: wave w owns heads [w*HPW, (w+1)*HPW).  For each head the 16xr_k
@@ -137,8 +137,11 @@ __global__ __launch_bounds__(256) void qproj_kernel(const half_t* __restrict__ q
 // compiler can prove the block table is never written in the kernel and
 // reads it with scalar loads: a vector load of a block id would need a
 // vmcnt wait that also drains the page prefetch.
-//   ml  [B][S][2][R16]: running max (log2 domain) then sum
-//   acc [B][S][R16][RV]: unnormalised z rows
+//   ml    [B][R16][2][SS] fp32: running max (log2 domain) of every split,
+//         then its sum
+//   zpart [B][R16][SS][RV] fp16: the split's z rows, normalised by its sum
+// SS (split_stride) is the split count rounded up to the merge's request
+// batch; slots past a sequence's last split are never written.
 
 template <int H, int RK, int RV, int NW>
 struct PageRegs {
@@ -268,35 +271,39 @@ template <int H, int RK, int RV, int NW, int DEPTH, bool NT>
 __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     const half_t* __restrict__ qt, const half_t* __restrict__ k_cache,
     const half_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ seq_lens, float* __restrict__ ml, float* __restrict__ acc,
-    int max_blocks, int num_blocks, int pages_per_split, int num_splits) {
+    const int32_t* __restrict__ seq_lens, float* __restrict__ ml, half_t* __restrict__ zpart,
+    int max_blocks, int num_blocks, int pages_per_split, int num_splits, int split_stride) {
   using C = DecodeCfg<H, RK, RV, NW>;
   using kvec = typename PageRegs<H, RK, RV, NW>::kvec;
   __shared__ __attribute__((aligned(16))) half_t sP[2][C::R16][BS];
   __shared__ float sAlpha[2][C::R16];
   __shared__ int sFlag[2];  // page index whose softmax step moved a running max
   __shared__ int sBlk[kMaxSplitPages];  // block ids of this split, loadable
+  __shared__ float sL[C::R16];          // final softmax sums, by head
 
   const int s = blockIdx.x, b = blockIdx.y;
-  const int L = seq_lens[b];
-  const int n_pages = min(min((L + BS - 1) / BS, max_blocks), num_splits * pages_per_split);
-  const int p0 = s * pages_per_split;
-  if (p0 >= n_pages) return;
-  const int p1 = min(p0 + pages_per_split, n_pages);
-
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
+  const int p0 = s * pages_per_split;
 
   // Block ids of the split's pages are staged in LDS once: a per-page
   // scalar load from the block table would stall the next page's load issue
-  // for a full memory latency under load.  Their loads are issued first, the
-  // first page's right after, and only the former is waited for before the
-  // (LDS-only) start barrier.  Invalid ids become -1 (masked page).
+  // for a full memory latency under load.  They are requested together with
+  // the sequence length (clamped to the table row: a split past the
+  // sequence exits below), and the empty asm keeps the compiler from moving
+  // them after the exit test, so the first page's request follows after one
+  // memory round trip instead of two.  Invalid ids become -1 (masked page).
   static_assert(kMaxSplitPages <= NW * 64, "one block id per thread");
   const int32_t* bt = block_tables + (size_t)b * max_blocks;
-  const int bid = (tid < p1 - p0) ? bt[p0 + tid] : 0;
-  const int blk0 = bt[p0];
+  const int blk0 = bt[min(p0, max_blocks - 1)];
+  const int bid = (tid < pages_per_split && p0 + tid < max_blocks) ? bt[p0 + tid] : 0;
+  const int L = seq_lens[b];
+  asm volatile("" ::"s"(L), "s"(blk0), "v"(bid));
+  const int n_pages = min(min((L + BS - 1) / BS, max_blocks), num_splits * pages_per_split);
+  if (p0 >= n_pages) return;
+  const int p1 = min(p0 + pages_per_split, n_pages);
+
   PageRegs<H, RK, RV, NW> ring[DEPTH];
   load_page<H, RK, RV, NW, NT>(ring[0], k_cache, v_cache,
                                ((unsigned)blk0 < (unsigned)num_blocks) ? blk0 : 0, w, col, quad);
@@ -355,199 +362,190 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     }
   }
 
-  // ---- partial state of this split: rows are heads, contiguous features
-  const size_t ws = (size_t)b * num_splits + s;
+  // ---- partial state of this split: running max and sum (fp32) per head,
+  // and the split's normalised z = acc / l (fp16, a convex combination of
+  // value latents, so it stays within their range), rows are heads with
+  // contiguous features.  The sums move to the value layout through LDS.
   if (col < C::HPW && quad == 0) {
-    ml[ws * 2 * C::R16 + w * C::HPW + col] = st.m_run;
-    ml[ws * 2 * C::R16 + C::R16 + w * C::HPW + col] = st.l_run;
+    float* mp = ml + ((size_t)b * C::R16 + w * C::HPW + col) * 2 * split_stride + s;
+    mp[0] = st.m_run;
+    mp[split_stride] = st.l_run;
+    sL[w * C::HPW + col] = st.l_run;
   }
-  float* pa = acc + ws * C::R16 * RV + w * C::FPW + quad * 4;
+  block_sync_lds();
+  half_t* pz = zpart + ((size_t)b * C::R16 * split_stride + s) * RV + w * C::FPW + quad * 4;
 #pragma unroll
-  for (int rt = 0; rt < C::RT; ++rt)
+  for (int rt = 0; rt < C::RT; ++rt) {
+    const int hr = rt * 16 + col;
+    if (hr < H) {  // rows past H are padding
+      const float lh = sL[hr];
+      const float inv = lh > 0.f ? 1.f / lh : 0.f;
 #pragma unroll
-    for (int ft = 0; ft < C::FT; ++ft)
-      *(float4v*)(pa + (size_t)(rt * 16 + col) * RV + ft * 16) = st.acc[rt][ft];
+      for (int ft = 0; ft < C::FT; ++ft) {
+        half4 zh;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) zh[r] = (half_t)(st.acc[rt][ft][r] * inv);
+        *(half4*)(pz + (size_t)hr * split_stride * RV + ft * 16) = zh;
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
-// 3. combine: z[b,h,:] = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
-// One thread per (sequence, head, 4 features), grid ceil(B*H*RV/4 / 256).
-// The statistics and partials of CB splits are requested together
-// (indices clamped to the last split, weight 0 past it), so a sequence with
-// up to CB splits costs one memory round trip; within a batch the new
-// running max is taken first, then the weighted sums.
+// 3. finish: the log-sum-exp merge of the splits and the up-projection,
+//    z[b,h,:] = sum_s w_s z_s / sum_s w_s with w_s = l_s 2^(m_s - M),
+//    M = max_s m_s, then out[b,h,:] = W_h z[b,h,:], in one launch.
+// One work group of 4 waves per head h and TB consecutive sequences.
+//   * W_h (D x RV fp16) goes straight from memory into the A operands of
+//     v_mfma_f32_16x16x32_f16, wave w owning output rows w*D/4 .. +D/4-1;
+//     those loads are issued first and stay in flight through the merge;
+//   * partials: thread u of the TB*RV/4 four-feature units merges its
+//     features of one sequence over the splits, CB splits per round of
+//     requests (weight 0 past the sequence's last split); the rounds run
+//     over the padded split count, so the first requests do not wait for
+//     the sequence length and their addresses are affine in the split.  z
+//     is split into an fp16 hi/lo pair as it goes to LDS;
+//   * B = z^T with column 2t+e holding part e of sequence t's z, read with
+//     one 16-byte LDS read per product (columns past TB read a zero row);
+//     the two parts share one product and are summed by a neighbour-lane add;
+//   * work groups are dealt to the 8 XCDs round robin (blockIdx % 8), so the
+//     ids are arranged to put every sequence group of one head on one XCD:
+//     W_h then reaches that XCD's L2 once instead of once per group.
+// An instruction cache that starts cold at every launch makes each
+// straight-line instruction of a short kernel cost a fetch, so the merge and
+// the products avoid per-element conversions in their unrolled bodies.
 // ---------------------------------------------------------------------------
-template <int H, int RV>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ml,
-                                                      const float* __restrict__ acc,
-                                                      const int32_t* __restrict__ seq_lens,
-                                                      int batch, int max_blocks,
-                                                      int pages_per_split, int num_splits,
-                                                      float* __restrict__ z) {
+template <int H, int D, int RV, int TB, int CB>
+__global__ __launch_bounds__(256) void finish_kernel(const float* __restrict__ ml,
+                                                     const half_t* __restrict__ zpart,
+                                                     const int32_t* __restrict__ seq_lens,
+                                                     const half_t* __restrict__ W, int batch,
+                                                     int max_blocks, int pages_per_split,
+                                                     int num_splits, int split_stride,
+                                                     half_t* __restrict__ out) {
   constexpr int R16 = ((H + 15) / 16) * 16;
   constexpr int F4 = RV / 4;
-  constexpr int CB = 16;
-  const int gid = blockIdx.x * 256 + threadIdx.x;
-  if (gid >= batch * H * F4) return;  // no barrier in this kernel
-  const int f4 = gid % F4;
-  const int h = (gid / F4) % H;
-  const int b = gid / (F4 * H);
-  const int n_pages =
-      min(min((seq_lens[b] + BS - 1) / BS, max_blocks), num_splits * pages_per_split);
-  const int ns = (n_pages + pages_per_split - 1) / pages_per_split;
-  const float* mlb = ml + (size_t)b * num_splits * 2 * R16 + h;
-  const float4v* ab = (const float4v*)(acc + ((size_t)b * num_splits * R16 + h) * RV) + f4;
-  float M = -INFINITY, den = 0.f;
-  float4v num = zero4();
-  for (int s0 = 0; s0 < ns; s0 += CB) {
-    float m[CB], l[CB];
-    float4v a[CB];
+  constexpr int NU = (TB * F4 + 255) / 256;  // four-feature units per thread
+  constexpr int RTW = D / 64;                // 16-row tiles of W_h per wave
+  constexpr int KS = RV / 32;                // 32-feature steps
+  constexpr int LDZ = RV + 8;                // halves per LDS row
+  constexpr bool UNIFORM_SEQ = F4 % 64 == 0; // a wave's units share one sequence
+  static_assert(D % 64 == 0 && RV % 32 == 0 && TB >= 1 && TB <= 8, "finish tile shape");
+  // hi and lo parts of z by sequence; row TB stays zero
+  __shared__ __attribute__((aligned(16))) half_t sZ[2][TB + 1][LDZ];
+
+  const int groups = (batch + TB - 1) / TB;
+  int h, g;
+  if constexpr (H % 8 == 0) {
+    const int x = blockIdx.x % 8, y = blockIdx.x / 8;
+    h = x + 8 * (y / groups);
+    g = y % groups;
+  } else {
+    h = blockIdx.x / groups;
+    g = blockIdx.x % groups;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, quad = lane >> 4;
+
+  // W_h operands: rows w*D/4 + 16*rt + col, features 32*k + 8*quad .. +7
+  half8 wa[RTW][KS];
+  {
+    const half_t* wrow = W + ((size_t)h * D + w * (D / 4) + col) * RV + quad * 8;
 #pragma unroll
-    for (int j = 0; j < CB; ++j) {
-      const int sj = min(s0 + j, ns - 1);
-      m[j] = mlb[(size_t)sj * 2 * R16];
-      l[j] = mlb[(size_t)sj * 2 * R16 + R16];
-      a[j] = ab[(size_t)sj * R16 * F4];
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int k = 0; k < KS; ++k) wa[rt][k] = *(const half8*)(wrow + (size_t)rt * 16 * RV + k * 32);
+  }
+  for (int i = tid; i < 2 * RV / 4; i += 256) {  // the zero row
+    const half4 hz = {};
+    *(half4*)&sZ[i / (RV / 4)][TB][(i % (RV / 4)) * 4] = hz;
+  }
+
+#pragma unroll
+  for (int j = 0; j < NU; ++j) {
+    const int u = tid + j * 256;
+    int t = min(u / F4, TB - 1);
+    if constexpr (UNIFORM_SEQ) t = __builtin_amdgcn_readfirstlane(t);
+    const int f4 = u % F4;
+    const int b = min(g * TB + t, batch - 1);
+    const bool live_u = u < TB * F4 && g * TB + t < batch;
+    const float* mp = ml + ((size_t)b * R16 + h) * 2 * split_stride;  // m of every split, then l
+    const half_t* zp = zpart + ((size_t)b * R16 + h) * split_stride * RV + f4 * 4;
+    const int n_pages =
+        min(min((seq_lens[b] + BS - 1) / BS, max_blocks), num_splits * pages_per_split);
+    const int ns = (n_pages + pages_per_split - 1) / pages_per_split;
+    float M = -INFINITY, den = 0.f;
+    float4v num = zero4();
+    for (int s0 = 0; s0 < split_stride; s0 += CB) {
+      float m[CB], l[CB];
+      half4 a[CB];
+#pragma unroll
+      for (int i = 0; i < CB; ++i) {
+        m[i] = mp[s0 + i];
+        l[i] = mp[split_stride + s0 + i];
+        a[i] = *(const half4*)(zp + (size_t)(s0 + i) * RV);
+      }
+      float mx = M;
+#pragma unroll
+      for (int i = 0; i < CB; ++i) mx = (s0 + i < ns) ? fmaxf(mx, m[i]) : mx;
+      const float sc = (mx == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(M - mx);
+      num *= sc;
+      den *= sc;
+      M = mx;
+#pragma unroll
+      for (int i = 0; i < CB; ++i) {
+        const bool live = s0 + i < ns && m[i] != -INFINITY;
+        const float wgt = live ? l[i] * __builtin_amdgcn_exp2f(m[i] - M) : 0.f;
+        const half4 hz = {};
+        const half4 av = live ? a[i] : hz;  // slots never written may hold NaN
+#pragma unroll
+        for (int e = 0; e < 4; ++e) num[e] = __builtin_fmaf((float)av[e], wgt, num[e]);
+        den += wgt;
+      }
     }
-    float mx = M;
+    if (u < TB * F4) {
+      const float inv = (live_u && den > 0.f) ? 1.f / den : 0.f;
+      half4 zh, zl;
 #pragma unroll
-    for (int j = 0; j < CB; ++j) mx = (s0 + j < ns) ? fmaxf(mx, m[j]) : mx;
-    const float sc = (mx == M) ? 1.f : exp2f(M - mx);
-    num *= sc;
-    den *= sc;
-    M = mx;
-#pragma unroll
-    for (int j = 0; j < CB; ++j) {
-      const bool live = s0 + j < ns && m[j] != -INFINITY;
-      const float wgt = live ? exp2f(m[j] - M) : 0.f;
-      num = live ? num + a[j] * wgt : num;
-      den = live ? den + l[j] * wgt : den;
+      for (int e = 0; e < 4; ++e) {
+        const float zv = num[e] * inv;
+        zh[e] = (half_t)zv;
+        zl[e] = (half_t)(zv - (float)zh[e]);
+      }
+      *(half4*)&sZ[0][u / F4][f4 * 4] = zh;
+      *(half4*)&sZ[1][u / F4][f4 * 4] = zl;
     }
   }
-  float4v* zo = (float4v*)(z + ((size_t)b * H + h) * RV) + f4;
-  *zo = (den > 0.f) ? num * (1.f / den) : zero4();
+  block_sync_lds();  // LDS only: the W_h loads stay in flight
+
+  // B column col: sequence col/2, part col%2
+  const int tc = col >> 1;
+  const half_t* zr = &sZ[col & 1][tc < TB ? tc : TB][quad * 8];
+  float4v o[RTW];
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) o[rt] = zero4();
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    const half8 bop = *(const half8*)(zr + k * 32);
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) o[rt] = mfma16x16x32(wa[rt][k], bop, o[rt]);
+  }
+  // D[row 4*quad + r][column col]; the even column of each pair adds its
+  // neighbour (the lo part) and stores four consecutive outputs
+  const int b = g * TB + tc;
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt) {
+    half4 ov;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ov[r] = (half_t)(o[rt][r] + __shfl_xor(o[rt][r], 1));
+    if (tc < TB && (col & 1) == 0 && b < batch)
+      *(half4*)(out + ((size_t)b * H + h) * D + w * (D / 4) + rt * 16 + quad * 4) = ov;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// 4. up-projection out[n, h, :] = W_h z[n, h, :] on the matrix cores.
-// grid (H, D/DR, ceil(N/64)); 4 waves, wave w owns tokens 16w..16w+15 of the
-// chunk and all DR output rows of the work group.  A = W_h (16 rows x 32
-// features, 16 contiguous bytes per lane), B = z (32 features x 16 tokens)
-// split into an fp16 hi/lo pair so the product keeps fp32 accuracy.
-// ---------------------------------------------------------------------------
-template <int H, int D, int RV, int DR>
-__global__ __launch_bounds__(256) void upproj_kernel(const half_t* __restrict__ W,
-                                                     const float* __restrict__ z, int n_tokens,
-                                                     half_t* __restrict__ out) {
-  constexpr int IT = DR / 16;
-  const int h = blockIdx.x, i0 = blockIdx.y * DR;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int col = lane & 15, quad = lane >> 4;
-  const int nb = blockIdx.z * 64 + w * 16;
-  if (nb >= n_tokens) return;  // wave-uniform
-  const int n = nb + col;
-  const bool nv = n < n_tokens;
-  const float* zr = z + ((size_t)(nv ? n : nb) * H + h) * RV + quad * 8;
-  const half_t* wrow = W + ((size_t)h * D + i0 + col) * RV + quad * 8;
-  float4v accv[IT];
-#pragma unroll
-  for (int it = 0; it < IT; ++it) accv[it] = zero4();
-#pragma unroll
-  for (int j0 = 0; j0 < RV; j0 += 32) {
-    half8 hi, lo;
-    const float4v z0 = nv ? *(const float4v*)(zr + j0) : zero4();
-    const float4v z1 = nv ? *(const float4v*)(zr + j0 + 4) : zero4();
-    split_f16x8(z0, z1, hi, lo);
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const half8 av = *(const half8*)(wrow + (size_t)it * 16 * RV + j0);
-      accv[it] = mfma16x16x32(av, hi, accv[it]);
-      accv[it] = mfma16x16x32(av, lo, accv[it]);
-    }
-  }
-  if (nv) {
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      half4 o;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = (half_t)accv[it][r];
-      *(half4*)(out + ((size_t)n * H + h) * D + i0 + it * 16 + quad * 4) = o;
-    }
-  }
-}
-
-// Decode variant: grid (H, D/16); the 4 waves split the r_v contraction
-// (RV/4 features each) for up to 64 tokens per pass, and the four partial
-// tiles are summed through LDS.  Every W_h and z operand of a pass is
-// requested before the first matrix op, so a pass costs one round trip.
-template <int H, int D, int RV>
-__global__ __launch_bounds__(256) void upproj_small_kernel(const half_t* __restrict__ W,
-                                                           const float* __restrict__ z,
-                                                           int n_tokens,
-                                                           half_t* __restrict__ out) {
-  constexpr int KW = RV / 4;     // features per wave
-  constexpr int KS = KW / 32;    // 32-wide steps per wave
-  constexpr int TT = 4;          // token tiles per pass (64 tokens)
-  static_assert(KS >= 1, "each wave needs at least one 32-wide step");
-  __shared__ float sRed[4][TT][16][17];
-  const int h = blockIdx.x, i0 = blockIdx.y * 16;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int col = lane & 15, quad = lane >> 4;
-  const half_t* wrow = W + ((size_t)h * D + i0 + col) * RV + w * KW + quad * 8;
-  half8 av[KS];
-#pragma unroll
-  for (int k = 0; k < KS; ++k) av[k] = *(const half8*)(wrow + k * 32);
-  for (int n0 = 0; n0 < n_tokens; n0 += 16 * TT) {
-    const int tiles = min(TT, (n_tokens - n0 + 15) / 16);  // uniform
-    float4v zr4[TT][KS][2];
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      const int n = min(n0 + t * 16 + col, n_tokens - 1);  // in range; masked below
-      const float* zr = z + ((size_t)n * H + h) * RV + w * KW + quad * 8;
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        zr4[t][k][0] = (t < tiles) ? *(const float4v*)(zr + k * 32) : zero4();
-        zr4[t][k][1] = (t < tiles) ? *(const float4v*)(zr + k * 32 + 4) : zero4();
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    float4v acc[TT];
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      acc[t] = zero4();
-      const bool nv = n0 + t * 16 + col < n_tokens;
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        half8 hi, lo;
-        split_f16x8(nv ? zr4[t][k][0] : zero4(), nv ? zr4[t][k][1] : zero4(), hi, lo);
-        acc[t] = mfma16x16x32(av[k], hi, acc[t]);
-        acc[t] = mfma16x16x32(av[k], lo, acc[t]);
-      }
-    }
-    // D[row 4*quad + r][token col] of each tile -> LDS, then sum the waves
-#pragma unroll
-    for (int t = 0; t < TT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sRed[w][t][quad * 4 + r][col] = acc[t][r];
-    __syncthreads();
-    {
-      const int t = threadIdx.x >> 6, e = threadIdx.x & 63;  // tile t, 4 outputs per thread
-      const int tok = e >> 2, r0 = (e & 3) * 4;
-      const int n = n0 + t * 16 + tok;
-      if (n < n_tokens) {
-        half4 o;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          o[r] = (half_t)(sRed[0][t][r0 + r][tok] + sRed[1][t][r0 + r][tok] +
-                          sRed[2][t][r0 + r][tok] + sRed[3][t][r0 + r][tok]);
-        *(half4*)(out + ((size_t)n * H + h) * D + i0 + r0) = o;
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// Many-token variant (prefill): grid (H, ceil(N / (32*NW))).  W_h (D x RV
+// 4. up-projection of many tokens (prefill), out[n, h, :] = W_h z[n, h, :]:
+// grid (H, ceil(N / (32*NW))).  W_h (D x RV
 // fp16) is staged once per work group in LDS, padded so that each 16-lane
 // group of a 16-byte read hits distinct banks; then every wave streams 32
 // tokens of z through v_mfma_f32_32x32x16_f16 with no further barrier:
@@ -637,26 +635,6 @@ hipError_t launch_upproj_tiled(const ShapeKey& s, const void* W, const void* z_t
   return hipGetLastError();
 }
 
-template <int H, int D, int RV, int DR>
-static void launch_upproj_t(const void* W, const float* z, int n_tokens, void* out, hipStream_t st) {
-  hipLaunchKernelGGL((upproj_kernel<H, D, RV, DR>), dim3(H, D / DR, (n_tokens + 63) / 64), dim3(256),
-                     0, st, (const half_t*)W, z, n_tokens, (half_t*)out);
-}
-
-hipError_t launch_upproj(const ShapeKey& s, const void* W, const float* z, int n_tokens,
-                         void* out, hipStream_t st) {
-  if (n_tokens <= 0) return hipSuccess;
-  if (s.H == 32 && s.d == 128 && s.rv == 512) {
-    hipLaunchKernelGGL((upproj_small_kernel<32, 128, 512>), dim3(32, 128 / 16), dim3(256), 0, st,
-                       (const half_t*)W, z, n_tokens, (half_t*)out);
-  } else if (s.H == 4 && s.d == 64 && s.rv == 64) {
-    launch_upproj_t<4, 64, 64, 16>(W, z, n_tokens, out, st);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
@@ -664,19 +642,29 @@ template <int H, int D, int RK, int RV, int NW, int DEPTH, bool NT>
 static hipError_t decode_instance(const DecodePlan& p, const void* qt, const void* k_cache,
                                   const void* v_cache, const void* W, const int32_t* block_tables,
                                   int max_blocks, const int32_t* seq_lens, int num_blocks,
-                                  int batch, float* ml, float* acc, float* z, void* out,
-                                  hipStream_t st) {
+                                  int batch, float* ml, void* zpart, void* out, hipStream_t st) {
   launch_hooked(TIME_DECODE_SPLIT, TIME_NONE, decode_split_kernel<H, RK, RV, NW, DEPTH, NT>,
                 dim3(p.num_splits, batch), dim3(NW * 64), st, (const half_t*)qt,
-                (const half_t*)k_cache, (const half_t*)v_cache, block_tables, seq_lens, ml, acc,
-                max_blocks, num_blocks, p.pages_per_split, p.num_splits);
-  const long threads = (long)batch * H * (RV / 4);
-  hipLaunchKernelGGL((combine_kernel<H, RV>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                     st, (const float*)ml, (const float*)acc, seq_lens, batch, max_blocks,
-                     p.pages_per_split, p.num_splits, z);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_upproj(ShapeKey{H, D, RK, RV}, W, z, batch, out, st);
+                (const half_t*)k_cache, (const half_t*)v_cache, block_tables, seq_lens, ml,
+                (half_t*)zpart, max_blocks, num_blocks, p.pages_per_split, p.num_splits,
+                p.split_stride);
+  // merge + up-projection: TB sequences per work group, CB splits per request round
+  const unsigned wgs2 = (unsigned)(H * ((batch + 1) / 2)), wgs4 = (unsigned)(H * ((batch + 3) / 4));
+  const bool tb4 = p.finish_tb >= 4, cb16 = p.split_stride % 16 == 0;
+#define STARKV_FINISH(TB_, CB_, WGS)                                                           \
+  hipLaunchKernelGGL((finish_kernel<H, D, RV, TB_, CB_>), dim3(WGS), dim3(256), 0, st,        \
+                     (const float*)ml, (const half_t*)zpart, seq_lens, (const half_t*)W, batch, \
+                     max_blocks, p.pages_per_split, p.num_splits, p.split_stride, (half_t*)out)
+  if (tb4 && cb16)
+    STARKV_FINISH(4, 16, wgs4);
+  else if (tb4)
+    STARKV_FINISH(4, 4, wgs4);
+  else if (cb16)
+    STARKV_FINISH(2, 16, wgs2);
+  else
+    STARKV_FINISH(2, 4, wgs2);
+#undef STARKV_FINISH
+  return hipGetLastError();
 }
 
 template <int H, int D, int RK>
@@ -706,9 +694,9 @@ hipError_t launch_qproj(const ShapeKey& s, const void* q, const void* U, int n_t
 hipError_t launch_decode(const ShapeKey& s, const DecodePlan& p, const void* qt, const void* k_cache,
                          const void* v_cache, const void* W, const int32_t* block_tables,
                          int max_blocks, const int32_t* seq_lens, int num_blocks, int batch,
-                         float* ml, float* acc, float* z, void* out, hipStream_t st) {
+                         float* ml, void* zpart, void* out, hipStream_t st) {
 #define STARKV_DECODE_ARGS \
-  p, qt, k_cache, v_cache, W, block_tables, max_blocks, seq_lens, num_blocks, batch, ml, acc, z, out, st
+  p, qt, k_cache, v_cache, W, block_tables, max_blocks, seq_lens, num_blocks, batch, ml, zpart, out, st
   if (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) {
     // kernel variant (tuning aid): waves per group, prefetch depth, non-temporal loads
     switch (p.variant) {

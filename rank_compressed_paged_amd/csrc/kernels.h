@@ -19,12 +19,15 @@ struct ShapeKey {
 struct DecodePlan {
   int pages_per_split;
   int num_splits;
-  int variant;  // split-kernel variant (0 = default)
+  int variant;    // split-kernel variant (0 = default)
+  int finish_tb;     // sequences per work group of the merge + up-projection (2 or 4)
+  int split_stride;  // split slots per sequence and head in the workspace: num_splits
+                     // rounded up to the merge's request batch (4 or 16)
 };
 
 // Byte offsets of the decode workspace regions.
 struct DecodeWorkspace {
-  size_t qt_off, ml_off, acc_off, z_off, total;
+  size_t qt_off, ml_off, zp_off, total;
 };
 
 struct PrefillWorkspace {
@@ -73,19 +76,14 @@ hipError_t launch_qproj(const ShapeKey& s, const void* q, const void* U, int n_t
 hipError_t launch_decode(const ShapeKey& s, const DecodePlan& p, const void* qt,
                          const void* k_cache, const void* v_cache, const void* W,
                          const int32_t* block_tables, int max_blocks, const int32_t* seq_lens,
-                         int num_blocks, int batch, float* ml, float* acc, float* z, void* out,
+                         int num_blocks, int batch, float* ml, void* zpart, void* out,
                          hipStream_t st);
 
-// out[n, h, :] = W_h z[n, h, :]; wide_rows picks the prefill tiling (one
-// work group per head and 64 tokens) over the decode tiling (16 rows).
-// out[n, h, :] = W_h z[n, h, :].  Few tokens (launch_upproj): z is
-// [n][H][RV] fp32, split into an fp16 hi/lo pair at the products.  Many
-// tokens (launch_upproj_tiled, prefill): z is fp16, tiled in the A-operand
-// order of the up-projection's 32x32x16 products, [H][ceil(n/32)][RV/16][64][8],
-// where lane l of 16-feature chunk kc of a 32-token block holds token l%32,
-// features 16*kc + 8*(l/32) .. +7 (prefill writes it that way).
-hipError_t launch_upproj(const ShapeKey& s, const void* W, const float* z, int n_tokens,
-                         void* out, hipStream_t st);
+// out[n, h, :] = W_h z[n, h, :] for the many tokens of a prefill call: z is
+// fp16, tiled in the A-operand order of the up-projection's 32x32x16
+// products, [H][ceil(n/32)][RV/16][64][8], where lane l of 16-feature chunk
+// kc of a 32-token block holds token l%32, features 16*kc + 8*(l/32) .. +7
+// (prefill writes it that way).
 hipError_t launch_upproj_tiled(const ShapeKey& s, const void* W, const void* z_tiled,
                                int n_tokens, void* out, hipStream_t st);
 

@@ -1,5 +1,5 @@
 """GPU parity of decode attention (q projection, split-K latent attention,
-combine, up-projection) against the fp64 oracle, through the C ABI."""
+combine and up-projection) against the fp64 oracle, through the C ABI."""
 import os
 
 import numpy as np
@@ -84,6 +84,22 @@ def test_split_plan_invariance(sk, min_pages, target, monkeypatch):
     note(f"decode split plan min_pages={min_pages} target={target}")
     out = run_decode(sk, case)
     assert_parity(out, ref, f"plan {min_pages}/{target}")
+
+
+@pytest.mark.parametrize("tb", ["2", "4"])
+@pytest.mark.parametrize("shape", ["main", "tiny"])
+def test_finish_tiles(sk, tb, shape, monkeypatch):
+    """The merge of the splits and the up-projection with two or four
+    sequences per work group, on a batch that leaves the last sequence group
+    partly empty and holds an empty sequence."""
+    cfg = wl.MAIN if shape == "main" else wl.TINY
+    case = wl.make_decode_case(cfg, seq_lens=[1500, 0, 33, 700, 5], seed=27)
+    ref = _oracle(case)
+    monkeypatch.setenv("STARKV_DECODE_FINISH_TB", tb)
+    note(f"decode finish tile tb={tb} shape={shape}")
+    out = run_decode(sk, case)
+    assert_parity(out, ref, f"finish tb={tb} {shape}")
+    assert torch.count_nonzero(out[1]).item() == 0
 
 
 def test_max_seq_len_bound_larger_than_lengths(sk):
