@@ -398,7 +398,8 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
 // One work group of 4 waves per head h and TB consecutive sequences.
 //   * W_h (D x RV fp16) goes straight from memory into the A operands of
 //     v_mfma_f32_16x16x32_f16, wave w owning output rows w*D/4 .. +D/4-1;
-//     those loads are issued first and stay in flight through the merge;
+//     those loads are issued right after the partials' first round and stay
+//     in flight through the merge, which waits for the partials only;
 //   * partials: thread u of the TB*RV/4 four-feature units merges its
 //     features of one sequence over the splits, CB splits per round of
 //     requests (weight 0 past the sequence's last split); the rounds run
@@ -447,15 +448,16 @@ __global__ __launch_bounds__(256) void finish_kernel(const float* __restrict__ m
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
 
-  // W_h operands: rows w*D/4 + 16*rt + col, features 32*k + 8*quad .. +7
+  // W_h operands: rows w*D/4 + 16*rt + col, features 32*k + 8*quad .. +7,
+  // requested after the partials' first round (below)
   half8 wa[RTW][KS];
-  {
+  auto load_w = [&]() {
     const half_t* wrow = W + ((size_t)h * D + w * (D / 4) + col) * RV + quad * 8;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
       for (int k = 0; k < KS; ++k) wa[rt][k] = *(const half8*)(wrow + (size_t)rt * 16 * RV + k * 32);
-  }
+  };
   for (int i = tid; i < 2 * RV / 4; i += 256) {  // the zero row
     const half4 hz = {};
     *(half4*)&sZ[i / (RV / 4)][TB][(i % (RV / 4)) * 4] = hz;
@@ -471,20 +473,29 @@ __global__ __launch_bounds__(256) void finish_kernel(const float* __restrict__ m
     const bool live_u = u < TB * F4 && g * TB + t < batch;
     const float* mp = ml + ((size_t)b * R16 + h) * 2 * split_stride;  // m of every split, then l
     const half_t* zp = zpart + ((size_t)b * R16 + h) * split_stride * RV + f4 * 4;
-    const int n_pages =
-        min(min((seq_lens[b] + BS - 1) / BS, max_blocks), num_splits * pages_per_split);
-    const int ns = (n_pages + pages_per_split - 1) / pages_per_split;
     float M = -INFINITY, den = 0.f;
     float4v num = zero4();
-    for (int s0 = 0; s0 < split_stride; s0 += CB) {
-      float m[CB], l[CB];
-      half4 a[CB];
+    float m[CB], l[CB];
+    half4 a[CB];
+    auto request = [&](int s0) {
 #pragma unroll
       for (int i = 0; i < CB; ++i) {
         m[i] = mp[s0 + i];
         l[i] = mp[split_stride + s0 + i];
         a[i] = *(const half4*)(zp + (size_t)(s0 + i) * RV);
       }
+    };
+    request(0);
+    if (j == 0) load_w();
+    __builtin_amdgcn_sched_barrier(0);  // the sequence length is read after these requests
+    const int n_pages =
+        min(min((seq_lens[b] + BS - 1) / BS, max_blocks), num_splits * pages_per_split);
+    const int ns = (n_pages + pages_per_split - 1) / pages_per_split;
+    // do-while: no guard between the first requests and their use, which
+    // would let the compiler sink them below a test of the split count
+    int s0 = 0;
+    do {
+      if (s0 > 0) request(s0);
       float mx = M;
 #pragma unroll
       for (int i = 0; i < CB; ++i) mx = (s0 + i < ns) ? fmaxf(mx, m[i]) : mx;
@@ -502,7 +513,8 @@ __global__ __launch_bounds__(256) void finish_kernel(const float* __restrict__ m
         for (int e = 0; e < 4; ++e) num[e] = __builtin_fmaf((float)av[e], wgt, num[e]);
         den += wgt;
       }
-    }
+      s0 += CB;
+    } while (s0 < split_stride);
     if (u < TB * F4) {
       const float inv = (live_u && den > 0.f) ? 1.f / den : 0.f;
       half4 zh, zl;
