@@ -51,25 +51,38 @@ static int device_cus() {
 // staged in LDS).  Environment overrides (tuning aids):
 // STARKV_DECODE_TARGET_WGS / STARKV_DECODE_MIN_PAGES switch to a fixed
 // target of work groups with a minimum split length.
-static DecodePlan with_stride(DecodePlan p) {
-  const int cb = p.num_splits <= 4 ? 4 : 16;
+// The merge + up-projection tile: TB sequences per work group, the largest
+// of 2, 4, 8 that still gives a work group per CU (each reads all of W_h,
+// so fewer, wider groups cut that traffic), or STARKV_DECODE_FINISH_TB; CB
+// splits per request round, the smallest power of two >= the split count
+// within 4 .. 32/TB (a thread holds TB/2 * CB partial rows in registers, and
+// the round's m and l in scalar registers).
+static DecodePlan with_finish(DecodePlan p, const ShapeKey& s, int batch) {
+  int tb = env_int("STARKV_DECODE_FINISH_TB", 0);
+  if (tb != 2 && tb != 4 && tb != 8) {
+    const int cus = device_cus();
+    tb = 2;
+    while (tb < 8 && (long)s.H * cdiv(batch, 2 * tb) >= cus) tb *= 2;
+  }
+  int cb = 4;
+  while (cb < 32 / tb && cb < p.num_splits) cb *= 2;
+  p.finish_tb = tb;
+  p.finish_cb = cb;
   p.split_stride = cdiv(p.num_splits, cb) * cb;
   return p;
 }
 
 DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int bs) {
-  (void)s;
   const int pages = cdiv(max_seq_len, bs);
   const int variant = env_int("STARKV_DECODE_VARIANT", 0);
-  const int ftb = env_int("STARKV_DECODE_FINISH_TB", 2);  // merge + up-projection tile
-  if (pages <= 0 || batch <= 0) return with_stride(DecodePlan{1, 1, variant, ftb, 0});
+  if (pages <= 0 || batch <= 0) return with_finish(DecodePlan{1, 1, variant, 0, 0, 0}, s, batch);
   const int target = env_int("STARKV_DECODE_TARGET_WGS", 0);
   if (target > 0) {
     const int min_pps = env_int("STARKV_DECODE_MIN_PAGES", 1);
     int pps = cdiv(pages, cdiv(target, batch));
     if (pps < min_pps) pps = min_pps;
     if (pps > 256) pps = 256;
-    return with_stride(DecodePlan{pps, cdiv(pages, pps), variant, ftb, 0});
+    return with_finish(DecodePlan{pps, cdiv(pages, pps), variant, 0, 0, 0}, s, batch);
   }
   const int cus = device_cus();
   double best = 1e300;
@@ -86,7 +99,7 @@ DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int bs) {
     }
     if (ns > 4 * cus) break;
   }
-  return with_stride(DecodePlan{best_pps, cdiv(pages, best_pps), variant, ftb, 0});
+  return with_finish(DecodePlan{best_pps, cdiv(pages, best_pps), variant, 0, 0, 0}, s, batch);
 }
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

@@ -661,20 +661,21 @@ static hipError_t decode_instance(const DecodePlan& p, const void* qt, const voi
                 (half_t*)zpart, max_blocks, num_blocks, p.pages_per_split, p.num_splits,
                 p.split_stride);
   // merge + up-projection: TB sequences per work group, CB splits per request round
-  const unsigned wgs2 = (unsigned)(H * ((batch + 1) / 2)), wgs4 = (unsigned)(H * ((batch + 3) / 4));
-  const bool tb4 = p.finish_tb >= 4, cb16 = p.split_stride % 16 == 0;
-#define STARKV_FINISH(TB_, CB_, WGS)                                                           \
-  hipLaunchKernelGGL((finish_kernel<H, D, RV, TB_, CB_>), dim3(WGS), dim3(256), 0, st,        \
+  // (the planner picks both; CB divides the split stride)
+  const unsigned wgs = (unsigned)(H * ((batch + p.finish_tb - 1) / p.finish_tb));
+#define STARKV_FINISH(TB_, CB_)                                                                \
+  hipLaunchKernelGGL((finish_kernel<H, D, RV, TB_, CB_>), dim3(wgs), dim3(256), 0, st,         \
                      (const float*)ml, (const half_t*)zpart, seq_lens, (const half_t*)W, batch, \
                      max_blocks, p.pages_per_split, p.num_splits, p.split_stride, (half_t*)out)
-  if (tb4 && cb16)
-    STARKV_FINISH(4, 16, wgs4);
-  else if (tb4)
-    STARKV_FINISH(4, 4, wgs4);
-  else if (cb16)
-    STARKV_FINISH(2, 16, wgs2);
-  else
-    STARKV_FINISH(2, 4, wgs2);
+  switch (p.finish_tb * 100 + p.finish_cb) {
+    case 204: STARKV_FINISH(2, 4); break;
+    case 208: STARKV_FINISH(2, 8); break;
+    case 216: STARKV_FINISH(2, 16); break;
+    case 404: STARKV_FINISH(4, 4); break;
+    case 408: STARKV_FINISH(4, 8); break;
+    case 804: STARKV_FINISH(8, 4); break;
+    default: return hipErrorInvalidValue;
+  }
 #undef STARKV_FINISH
   return hipGetLastError();
 }

@@ -20,9 +20,11 @@ struct DecodePlan {
   int pages_per_split;
   int num_splits;
   int variant;    // split-kernel variant (0 = default)
-  int finish_tb;     // sequences per work group of the merge + up-projection (2 or 4)
+  int finish_tb;     // sequences per work group of the merge + up-projection (2, 4, 8)
+  int finish_cb;     // splits per request round of the merge (4, 8, 16; finish_tb *
+                     // finish_cb <= 32)
   int split_stride;  // split slots per sequence and head in the workspace: num_splits
-                     // rounded up to the merge's request batch (4 or 16)
+                     // rounded up to a multiple of finish_cb
 };
 
 // Byte offsets of the decode workspace regions.

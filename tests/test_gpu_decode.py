@@ -86,12 +86,13 @@ def test_split_plan_invariance(sk, min_pages, target, monkeypatch):
     assert_parity(out, ref, f"plan {min_pages}/{target}")
 
 
-@pytest.mark.parametrize("tb", ["2", "4"])
+@pytest.mark.parametrize("tb", ["2", "4", "8"])
 @pytest.mark.parametrize("shape", ["main", "tiny"])
 def test_finish_tiles(sk, tb, shape, monkeypatch):
-    """The merge of the splits and the up-projection with two or four
-    sequences per work group, on a batch that leaves the last sequence group
-    partly empty and holds an empty sequence."""
+    """The merge of the splits and the up-projection with 2, 4 or 8
+    sequences per work group (and so 16, 8 or 4 splits per request round, in
+    several rounds where the plan has more splits), on a batch that leaves
+    the last sequence group partly empty and holds an empty sequence."""
     cfg = wl.MAIN if shape == "main" else wl.TINY
     case = wl.make_decode_case(cfg, seq_lens=[1500, 0, 33, 700, 5], seed=27)
     ref = _oracle(case)
