@@ -41,48 +41,68 @@ static int device_cus() {
   return cached[dev];
 }
 
-// Split-K plan.  The split-K kernel runs one work group per compute unit,
-// so B*S groups execute in ceil(B*S / CUs) rounds, each as long as its
-// pages plus a start-up of about three page times (first-page latency),
-// and every split adds a partial that the combine reads back.  Pick the
-// number of splits S that minimises
-//     rounds * (3 + pages_per_split) + 0.5 * B * S / CUs,
-// preferring fewer splits on ties; pages_per_split <= 256 (block ids are
-// staged in LDS).  Environment overrides (tuning aids):
-// STARKV_DECODE_TARGET_WGS / STARKV_DECODE_MIN_PAGES switch to a fixed
-// target of work groups with a minimum split length.
-// The merge + up-projection tile: TB sequences per work group, the largest
-// of 2, 4, 8 that still gives a work group per CU (each reads all of W_h,
-// so fewer, wider groups cut that traffic), or STARKV_DECODE_FINISH_TB; CB
-// splits per request round, the smallest power of two >= the split count
-// within 4 .. 32/TB (a thread holds TB/2 * CB partial rows in registers, and
-// the round's m and l in scalar registers).
+// The merge + up-projection tile.  TB sequences per work group: 1 when the
+// batch is too small to give every CU a (head, sequence) pair, else the
+// widest of 2, 4, 8 that still gives a work group per CU (each work group
+// reads all of W_h, so wide groups cut that traffic at large batch), or
+// STARKV_DECODE_FINISH_TB.  The merge requests CB splits per round and
+// thread; with many splits (small batch, long sequences) the work group
+// grows to 512 threads whose split groups take disjoint sets of splits, so
+// the partials are requested in fewer rounds (1024 threads would leave 128
+// registers per thread, too few for the operands in flight).
 static DecodePlan with_finish(DecodePlan p, const ShapeKey& s, int batch) {
+  const int cus = device_cus();
   int tb = env_int("STARKV_DECODE_FINISH_TB", 0);
-  if (tb != 2 && tb != 4 && tb != 8) {
-    const int cus = device_cus();
-    tb = 2;
-    while (tb < 8 && (long)s.H * cdiv(batch, 2 * tb) >= cus) tb *= 2;
+  if (tb != 1 && tb != 2 && tb != 4 && tb != 8) {
+    tb = (long)s.H * batch < cus ? 1 : 2;
+    while (tb >= 2 && tb < 8 && (long)s.H * cdiv(batch, 2 * tb) >= cus) tb *= 2;
   }
-  int cb = 4;
-  while (cb < 32 / tb && cb < p.num_splits) cb *= 2;
+  int nt = 256, cb = 4;
+  if (tb >= 4) {
+    cb = 32 / tb;  // a thread holds TB/2 units of CB partial rows
+  } else {
+    while (nt < 512 && finish_split_groups(nt, tb, s.rv) * 16 < p.num_splits) nt *= 2;
+    const int sg = finish_split_groups(nt, tb, s.rv);
+    while (cb < 16 && cb * sg < p.num_splits) cb *= 2;
+  }
   p.finish_tb = tb;
   p.finish_cb = cb;
-  p.split_stride = cdiv(p.num_splits, cb) * cb;
+  p.finish_nt = nt;
+  const int per_round = cb * finish_split_groups(nt, tb, s.rv);
+  p.split_stride = cdiv(p.num_splits, per_round) * per_round;
   return p;
 }
 
+// Split-K plan.  The split-K kernel runs one work group per compute unit,
+// so B*S groups execute in ceil(B*S / CUs) rounds, each as long as its
+// pages plus a start-up of about three page times (first-page latency),
+// and every split adds partials that are written and merged back.  Pick the
+// number of splits S that minimises
+//     rounds * (3 + pages_per_split) + 6 * B * S / CUs,
+// preferring fewer splits on ties; pages_per_split <= 256 (block ids are
+// staged in LDS).  The weight 6 of the per-split term comes from sweeps at
+// batch 1-64 (2K-32K tokens), where it picks the fastest plan or one within
+// a few percent of it.  Environment overrides (tuning aids):
+// STARKV_DECODE_TARGET_WGS / STARKV_DECODE_MIN_PAGES switch to a fixed
+// target of work groups with a minimum split length, and
+// STARKV_DECODE_SPLIT_COST (in tenths) replaces the weight 6.
+static double split_cost_weight() {
+  const int tenths = env_int("STARKV_DECODE_SPLIT_COST", 0);
+  return tenths > 0 ? tenths / 10.0 : 6.0;
+}
+
 DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int bs) {
+  const double kSplitCost = split_cost_weight();
   const int pages = cdiv(max_seq_len, bs);
   const int variant = env_int("STARKV_DECODE_VARIANT", 0);
-  if (pages <= 0 || batch <= 0) return with_finish(DecodePlan{1, 1, variant, 0, 0, 0}, s, batch);
+  if (pages <= 0 || batch <= 0) return with_finish(DecodePlan{1, 1, variant, 0, 0, 0, 0}, s, batch);
   const int target = env_int("STARKV_DECODE_TARGET_WGS", 0);
   if (target > 0) {
     const int min_pps = env_int("STARKV_DECODE_MIN_PAGES", 1);
     int pps = cdiv(pages, cdiv(target, batch));
     if (pps < min_pps) pps = min_pps;
     if (pps > 256) pps = 256;
-    return with_finish(DecodePlan{pps, cdiv(pages, pps), variant, 0, 0, 0}, s, batch);
+    return with_finish(DecodePlan{pps, cdiv(pages, pps), variant, 0, 0, 0, 0}, s, batch);
   }
   const int cus = device_cus();
   double best = 1e300;
@@ -92,14 +112,14 @@ DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int bs) {
     const int nsr = cdiv(pages, pps);  // splits actually used at this length
     if (nsr != ns) continue;
     const double rounds = (double)cdiv((long)batch * ns, cus);
-    const double cost = rounds * (3.0 + pps) + 0.5 * (double)batch * ns / cus;
+    const double cost = rounds * (3.0 + pps) + kSplitCost * (double)batch * ns / cus;
     if (cost < best - 1e-9) {
       best = cost;
       best_pps = pps;
     }
     if (ns > 4 * cus) break;
   }
-  return with_finish(DecodePlan{best_pps, cdiv(pages, best_pps), variant, 0, 0, 0}, s, batch);
+  return with_finish(DecodePlan{best_pps, cdiv(pages, best_pps), variant, 0, 0, 0, 0}, s, batch);
 }
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

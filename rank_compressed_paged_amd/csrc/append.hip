@@ -286,7 +286,13 @@ __global__ __launch_bounds__(kSmallWaves * 64) void append_small_kernel(AppendAr
 
   const int HD = H * D;
   if (blockIdx.x < RV / 16) {
-    const int f0 = blockIdx.x * 16;
+    // A value job reads 32 bytes of every 1 KiB row of W, so the four jobs
+    // of one 64-output group share each cache line.  Work groups are dealt
+    // to the 8 XCDs round robin (blockIdx % 8): give each XCD whole groups,
+    // so every line is fetched into one L2 once instead of into four.
+    int job = blockIdx.x;
+    if constexpr ((RV / 16) % 32 == 0) job = (blockIdx.x % 8) * (RV / 128) + blockIdx.x / 8;
+    const int f0 = job * 16;
     run(VJ{}, a.v, HD, a.W, RV, f0, [&](int64_t blk, int off, int f, half_t val) {
       a.v_cache[((size_t)blk * RV + f) * 16 + off] = val;
     });

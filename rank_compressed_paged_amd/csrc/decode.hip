@@ -416,24 +416,31 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
 // straight-line instruction of a short kernel cost a fetch, so the merge and
 // the products avoid per-element conversions in their unrolled bodies.
 // ---------------------------------------------------------------------------
-template <int H, int D, int RV, int TB, int CB>
-__global__ __launch_bounds__(256) void finish_kernel(const float* __restrict__ ml,
-                                                     const half_t* __restrict__ zpart,
-                                                     const int32_t* __restrict__ seq_lens,
-                                                     const half_t* __restrict__ W, int batch,
-                                                     int max_blocks, int pages_per_split,
-                                                     int num_splits, int split_stride,
-                                                     half_t* __restrict__ out) {
+template <int H, int D, int RV, int TB, int CB, int NT>
+__global__ __launch_bounds__(NT) void finish_kernel(const float* __restrict__ ml,
+                                                    const half_t* __restrict__ zpart,
+                                                    const int32_t* __restrict__ seq_lens,
+                                                    const half_t* __restrict__ W, int batch,
+                                                    int max_blocks, int pages_per_split,
+                                                    int num_splits, int split_stride,
+                                                    half_t* __restrict__ out) {
   constexpr int R16 = ((H + 15) / 16) * 16;
   constexpr int F4 = RV / 4;
-  constexpr int NU = (TB * F4 + 255) / 256;  // four-feature units per thread
-  constexpr int RTW = D / 64;                // 16-row tiles of W_h per wave
-  constexpr int KS = RV / 32;                // 32-feature steps
-  constexpr int LDZ = RV + 8;                // halves per LDS row
-  constexpr bool UNIFORM_SEQ = F4 % 64 == 0; // a wave's units share one sequence
-  static_assert(D % 64 == 0 && RV % 32 == 0 && TB >= 1 && TB <= 8, "finish tile shape");
+  constexpr int UG = TB * F4;                  // four-feature units of the work group
+  constexpr int SG = finish_split_groups(NT, TB, RV);  // split groups (1: one)
+  constexpr int NU = SG > 1 ? 1 : (UG + NT - 1) / NT;  // units per thread
+  constexpr int NWV = NT / 64;
+  constexpr int MW = NWV < D / 16 ? NWV : D / 16;  // waves on the products
+  constexpr int RTW = D / (16 * MW);           // 16-row tiles of W_h per product wave
+  constexpr int KS = RV / 32;                  // 32-feature steps
+  constexpr int LDZ = RV + 8;                  // halves per LDS row
+  constexpr bool UNIFORM_SEQ = F4 % 64 == 0;   // a wave's units share one sequence
+  static_assert(D % (16 * MW) == 0 && RV % 32 == 0 && TB >= 1 && TB <= 8, "finish tile shape");
+  static_assert(SG == 1 || SG * UG <= NT, "split groups must fit the work group");
   // hi and lo parts of z by sequence; row TB stays zero
   __shared__ __attribute__((aligned(16))) half_t sZ[2][TB + 1][LDZ];
+  // per split group: running max, sum and four weighted features of a unit
+  __shared__ float sMerge[SG > 1 ? SG : 1][SG > 1 ? UG : 1][6];
 
   const int groups = (batch + TB - 1) / TB;
   int h, g;
@@ -447,75 +454,107 @@ __global__ __launch_bounds__(256) void finish_kernel(const float* __restrict__ m
   }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
+  // split group of this thread: splits sg, sg + SG, sg + 2 SG, ...
+  const int sg = SG > 1 ? tid / UG : 0;
+  const bool merger = SG == 1 || tid < SG * UG;
 
-  // W_h operands: rows w*D/4 + 16*rt + col, features 32*k + 8*quad .. +7,
-  // requested after the partials' first round (below)
+  // W_h operands (product waves): rows w*D/MW + 16*rt + col, features
+  // 32*k + 8*quad .. +7, requested after the partials' first round (below)
   half8 wa[RTW][KS];
   auto load_w = [&]() {
-    const half_t* wrow = W + ((size_t)h * D + w * (D / 4) + col) * RV + quad * 8;
+    const half_t* wrow = W + ((size_t)h * D + w * (D / MW) + col) * RV + quad * 8;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
       for (int k = 0; k < KS; ++k) wa[rt][k] = *(const half8*)(wrow + (size_t)rt * 16 * RV + k * 32);
   };
-  for (int i = tid; i < 2 * RV / 4; i += 256) {  // the zero row
+  for (int i = tid; i < 2 * RV / 4; i += NT) {  // the zero row
     const half4 hz = {};
     *(half4*)&sZ[i / (RV / 4)][TB][(i % (RV / 4)) * 4] = hz;
   }
 
 #pragma unroll
   for (int j = 0; j < NU; ++j) {
-    const int u = tid + j * 256;
+    const int u = SG > 1 ? tid % UG : tid + j * NT;
     int t = min(u / F4, TB - 1);
     if constexpr (UNIFORM_SEQ) t = __builtin_amdgcn_readfirstlane(t);
     const int f4 = u % F4;
     const int b = min(g * TB + t, batch - 1);
-    const bool live_u = u < TB * F4 && g * TB + t < batch;
-    const float* mp = ml + ((size_t)b * R16 + h) * 2 * split_stride;  // m of every split, then l
-    const half_t* zp = zpart + ((size_t)b * R16 + h) * split_stride * RV + f4 * 4;
+    const bool live_u = u < UG && g * TB + t < batch;
+    // m of every split, then l; this group's first split
+    const float* mp = ml + ((size_t)b * R16 + h) * 2 * split_stride + sg;
+    const half_t* zp = zpart + (((size_t)b * R16 + h) * split_stride + sg) * RV + f4 * 4;
     float M = -INFINITY, den = 0.f;
     float4v num = zero4();
     float m[CB], l[CB];
     half4 a[CB];
-    auto request = [&](int s0) {
+    auto request = [&](int q0) {
 #pragma unroll
       for (int i = 0; i < CB; ++i) {
-        m[i] = mp[s0 + i];
-        l[i] = mp[split_stride + s0 + i];
-        a[i] = *(const half4*)(zp + (size_t)(s0 + i) * RV);
+        m[i] = mp[(q0 + i) * SG];
+        l[i] = mp[split_stride + (q0 + i) * SG];
+        a[i] = *(const half4*)(zp + (size_t)(q0 + i) * SG * RV);
       }
     };
-    request(0);
-    if (j == 0) load_w();
+    if (merger) request(0);
+    if (j == 0 && w < MW) load_w();
     __builtin_amdgcn_sched_barrier(0);  // the sequence length is read after these requests
     const int n_pages =
         min(min((seq_lens[b] + BS - 1) / BS, max_blocks), num_splits * pages_per_split);
     const int ns = (n_pages + pages_per_split - 1) / pages_per_split;
-    // do-while: no guard between the first requests and their use, which
-    // would let the compiler sink them below a test of the split count
-    int s0 = 0;
-    do {
-      if (s0 > 0) request(s0);
-      float mx = M;
+    if (merger) {
+      // do-while: no guard between the first requests and their use, which
+      // would let the compiler sink them below a test of the split count
+      int q0 = 0;
+      do {
+        if (q0 > 0) request(q0);
+        float mx = M;
 #pragma unroll
-      for (int i = 0; i < CB; ++i) mx = (s0 + i < ns) ? fmaxf(mx, m[i]) : mx;
-      const float sc = (mx == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(M - mx);
-      num *= sc;
-      den *= sc;
-      M = mx;
+        for (int i = 0; i < CB; ++i) mx = ((q0 + i) * SG + sg < ns) ? fmaxf(mx, m[i]) : mx;
+        const float sc = (mx == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(M - mx);
+        num *= sc;
+        den *= sc;
+        M = mx;
 #pragma unroll
-      for (int i = 0; i < CB; ++i) {
-        const bool live = s0 + i < ns && m[i] != -INFINITY;
-        const float wgt = live ? l[i] * __builtin_amdgcn_exp2f(m[i] - M) : 0.f;
-        const half4 hz = {};
-        const half4 av = live ? a[i] : hz;  // slots never written may hold NaN
+        for (int i = 0; i < CB; ++i) {
+          const bool live = (q0 + i) * SG + sg < ns && m[i] != -INFINITY;
+          const float wgt = live ? l[i] * __builtin_amdgcn_exp2f(m[i] - M) : 0.f;
+          const half4 hz = {};
+          const half4 av = live ? a[i] : hz;  // slots never written may hold NaN
 #pragma unroll
-        for (int e = 0; e < 4; ++e) num[e] = __builtin_fmaf((float)av[e], wgt, num[e]);
-        den += wgt;
+          for (int e = 0; e < 4; ++e) num[e] = __builtin_fmaf((float)av[e], wgt, num[e]);
+          den += wgt;
+        }
+        q0 += CB;
+      } while (q0 * SG < split_stride);
+    }
+    if constexpr (SG > 1) {  // merge the groups' states of each unit
+      if (merger) {
+        float* sm = sMerge[sg][u];
+        sm[0] = M;
+        sm[1] = den;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm[2 + e] = num[e];
       }
-      s0 += CB;
-    } while (s0 < split_stride);
-    if (u < TB * F4) {
+      block_sync_lds();
+      if (sg == 0 && merger) {
+        float mx = M;
+#pragma unroll
+        for (int k = 1; k < SG; ++k) mx = fmaxf(mx, sMerge[k][u][0]);
+        const float sc = (mx == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(M - mx);
+        num *= sc;
+        den *= sc;
+#pragma unroll
+        for (int k = 1; k < SG; ++k) {
+          const float mk = sMerge[k][u][0];
+          const float sk = (mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - mx);
+          den += sMerge[k][u][1] * sk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) num[e] += sMerge[k][u][2 + e] * sk;
+        }
+      }
+    }
+    if (u < UG && sg == 0 && merger) {
       const float inv = (live_u && den > 0.f) ? 1.f / den : 0.f;
       half4 zh, zl;
 #pragma unroll
@@ -529,6 +568,7 @@ __global__ __launch_bounds__(256) void finish_kernel(const float* __restrict__ m
     }
   }
   block_sync_lds();  // LDS only: the W_h loads stay in flight
+  if (w >= MW) return;  // no barrier follows
 
   // B column col: sequence col/2, part col%2
   const int tc = col >> 1;
@@ -551,7 +591,7 @@ __global__ __launch_bounds__(256) void finish_kernel(const float* __restrict__ m
 #pragma unroll
     for (int r = 0; r < 4; ++r) ov[r] = (half_t)(o[rt][r] + __shfl_xor(o[rt][r], 1));
     if (tc < TB && (col & 1) == 0 && b < batch)
-      *(half4*)(out + ((size_t)b * H + h) * D + w * (D / 4) + rt * 16 + quad * 4) = ov;
+      *(half4*)(out + ((size_t)b * H + h) * D + w * (D / MW) + rt * 16 + quad * 4) = ov;
   }
 }
 
@@ -660,20 +700,26 @@ static hipError_t decode_instance(const DecodePlan& p, const void* qt, const voi
                 (const half_t*)k_cache, (const half_t*)v_cache, block_tables, seq_lens, ml,
                 (half_t*)zpart, max_blocks, num_blocks, p.pages_per_split, p.num_splits,
                 p.split_stride);
-  // merge + up-projection: TB sequences per work group, CB splits per request round
-  // (the planner picks both; CB divides the split stride)
+  // merge + up-projection: TB sequences and NT threads per work group, CB
+  // splits per request round (the planner picks all three; the split stride
+  // is a multiple of CB times the split groups)
   const unsigned wgs = (unsigned)(H * ((batch + p.finish_tb - 1) / p.finish_tb));
-#define STARKV_FINISH(TB_, CB_)                                                                \
-  hipLaunchKernelGGL((finish_kernel<H, D, RV, TB_, CB_>), dim3(wgs), dim3(256), 0, st,         \
+#define STARKV_FINISH(TB_, CB_, NT_)                                                           \
+  hipLaunchKernelGGL((finish_kernel<H, D, RV, TB_, CB_, NT_>), dim3(wgs), dim3(NT_), 0, st,    \
                      (const float*)ml, (const half_t*)zpart, seq_lens, (const half_t*)W, batch, \
                      max_blocks, p.pages_per_split, p.num_splits, p.split_stride, (half_t*)out)
-  switch (p.finish_tb * 100 + p.finish_cb) {
-    case 204: STARKV_FINISH(2, 4); break;
-    case 208: STARKV_FINISH(2, 8); break;
-    case 216: STARKV_FINISH(2, 16); break;
-    case 404: STARKV_FINISH(4, 4); break;
-    case 408: STARKV_FINISH(4, 8); break;
-    case 804: STARKV_FINISH(8, 4); break;
+  switch (p.finish_tb * 1000000 + p.finish_cb * 10000 + p.finish_nt) {
+    case 1040256: STARKV_FINISH(1, 4, 256); break;
+    case 1080256: STARKV_FINISH(1, 8, 256); break;
+    case 1160256: STARKV_FINISH(1, 16, 256); break;
+    case 1160512: STARKV_FINISH(1, 16, 512); break;
+    case 2040256: STARKV_FINISH(2, 4, 256); break;
+    case 2080256: STARKV_FINISH(2, 8, 256); break;
+    case 2160256: STARKV_FINISH(2, 16, 256); break;
+    case 2160512: STARKV_FINISH(2, 16, 512); break;
+    case 4040256: STARKV_FINISH(4, 4, 256); break;
+    case 4080256: STARKV_FINISH(4, 8, 256); break;
+    case 8040256: STARKV_FINISH(8, 4, 256); break;
     default: return hipErrorInvalidValue;
   }
 #undef STARKV_FINISH

@@ -20,12 +20,19 @@ struct DecodePlan {
   int pages_per_split;
   int num_splits;
   int variant;    // split-kernel variant (0 = default)
-  int finish_tb;     // sequences per work group of the merge + up-projection (2, 4, 8)
-  int finish_cb;     // splits per request round of the merge (4, 8, 16; finish_tb *
-                     // finish_cb <= 32)
+  int finish_tb;     // sequences per work group of the merge + up-projection (1, 2, 4, 8)
+  int finish_cb;     // splits per request round of each merging thread (4, 8, 16)
+  int finish_nt;     // threads per work group of the merge (256, 512)
   int split_stride;  // split slots per sequence and head in the workspace: num_splits
-                     // rounded up to a multiple of finish_cb
+                     // rounded up to a multiple of finish_cb times the split groups
 };
+
+// Split groups of the merge: when a work group has more threads than
+// four-feature units (TB * RV / 4), the threads form up to 8 groups that
+// merge disjoint, interleaved sets of splits, combined through LDS.
+constexpr int finish_split_groups(int nt, int tb, int rv) {
+  return (tb * rv / 4 >= nt) ? 1 : (nt / (tb * rv / 4) > 8 ? 8 : nt / (tb * rv / 4));
+}
 
 // Byte offsets of the decode workspace regions.
 struct DecodeWorkspace {

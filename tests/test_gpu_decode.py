@@ -86,13 +86,14 @@ def test_split_plan_invariance(sk, min_pages, target, monkeypatch):
     assert_parity(out, ref, f"plan {min_pages}/{target}")
 
 
-@pytest.mark.parametrize("tb", ["2", "4", "8"])
+@pytest.mark.parametrize("tb", ["1", "2", "4", "8"])
 @pytest.mark.parametrize("shape", ["main", "tiny"])
 def test_finish_tiles(sk, tb, shape, monkeypatch):
-    """The merge of the splits and the up-projection with 2, 4 or 8
-    sequences per work group (and so 16, 8 or 4 splits per request round, in
-    several rounds where the plan has more splits), on a batch that leaves
-    the last sequence group partly empty and holds an empty sequence."""
+    """The merge of the splits and the up-projection with 1, 2, 4 or 8
+    sequences per work group (and so split groups, 16, 8 or 4 splits per
+    request round, several rounds where the plan has more splits), on a batch
+    that leaves the last sequence group partly empty and holds an empty
+    sequence."""
     cfg = wl.MAIN if shape == "main" else wl.TINY
     case = wl.make_decode_case(cfg, seq_lens=[1500, 0, 33, 700, 5], seed=27)
     ref = _oracle(case)
@@ -101,6 +102,16 @@ def test_finish_tiles(sk, tb, shape, monkeypatch):
     out = run_decode(sk, case)
     assert_parity(out, ref, f"finish tb={tb} {shape}")
     assert torch.count_nonzero(out[1]).item() == 0
+
+
+@pytest.mark.parametrize("lens", [[8192], [2048, 2048], [16384, 3, 9000, 600]],
+                         ids=["b1_long", "b2", "b4_ragged"])
+def test_small_batch_many_splits(sk, lens):
+    """Small batches split each sequence into many work groups (up to 256
+    splits), which the merge takes in split groups and several rounds."""
+    case = wl.make_decode_case(wl.MAIN, seq_lens=lens, seed=28)
+    note(f"decode small batch lens={lens}")
+    assert_parity(run_decode(sk, case), _oracle(case), f"small batch {lens}")
 
 
 def test_max_seq_len_bound_larger_than_lengths(sk):
