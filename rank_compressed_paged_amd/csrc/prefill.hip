@@ -33,10 +33,10 @@
 //     well inside fp16 and the accumulators are rescaled on few steps.  The
 //     softmax is invariant to the reference, so this is exact math.
 //   * software pipeline: step s runs the scores and softmax of step s+1
-//     beside the P.c_v products of step s (the softmax's vector instructions
-//     interleaved between the products), while the keys of step s+2 and the
-//     values of step s+1 load into a register ring; one LDS-only barrier per
-//     step.
+//     beside the P.c_v products of step s, with the softmax's vector
+//     instructions and the step's loads (keys of step s+3 for the LDS ring,
+//     values of step s+2 into a three-step register ring) interleaved
+//     between the products; one LDS-only barrier per step.
 //   * masks (causal limit, sequence end, invalid block ids) only on the
 //     steps that need them.
 //   * block ids stream through a 2*kChunk-entry LDS ring, a few new entries
@@ -116,7 +116,8 @@ constexpr float kRaise = 8.f;           // lazy-rescale threshold (log2 units)
 //   SCHED  instruction order inside a step: 0 left to the compiler, 1 score
 //          products, then the P.c_v products, then the softmax, 2 as 1 with
 //          the softmax's vector instructions interleaved between the products,
-//          3 as 1 with the step's loads issued after the products
+//          3 as 1 with the step's loads issued after the products, 4 as 2
+//          with the step's loads interleaved between the products too
 template <int H, int RK, int RV, int G, int MQ, int NW, int PPS, int DEPTH, int SCHED, bool KLDS>
 __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   static_assert(DEPTH >= 2 && DEPTH <= 3, "register ring of 2 or 3 steps");
@@ -503,7 +504,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
       }
       load_v(vr[(PH + DEPTH - 1) % DEPTH], id_v);
     };
-    if constexpr (SCHED != 3) issue_loads();
+    if constexpr (SCHED != 3 && SCHED != 4) issue_loads();
     float4v sacc[PPS][C::SUW];
     if constexpr (KLDS)
       score_products_lds((s + 1) % 3, sacc);
@@ -514,7 +515,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
     const bool vmask = !step_plain_values(id_c, s);
     const bool smask = !step_plain_scores(id_s, s + 1);
     if constexpr (SCHED >= 1) __builtin_amdgcn_sched_barrier(0);
-    if constexpr (SCHED == 2) {  // masks ahead of the interleaved region
+    if constexpr (SCHED == 4) {  // masks ahead of the interleaved region
+      if (vmask) mask_values(vr[PH], id_c, s);
+      value_products(false, vr[PH], id_c, s, buf);
+      issue_loads();
+    } else if constexpr (SCHED == 2) {  // masks ahead of the interleaved region
       if (vmask) mask_values(vr[PH], id_c, s);
       value_products(false, vr[PH], id_c, s, buf);
     } else {
@@ -531,10 +536,23 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
     bool ok_s[PPS];
 #pragma unroll
     for (int pg = 0; pg < PPS; ++pg) ok_s[pg] = id_s[pg] >= 0;
-    if constexpr (SCHED == 2)
+    if constexpr (SCHED == 2 || SCHED == 4)
       softmax(std::true_type{}, smask, ok_s, sacc, s + 1, buf ^ 1);
     else
       softmax(std::false_type{}, smask, ok_s, sacc, s + 1, buf ^ 1);
+    if constexpr (SCHED == 4) {
+      // one P.c_v product, a few vector instructions and, every other
+      // product, one of the step's loads: the loads drain through the
+      // per-CU load path while the matrix cores run instead of stalling the
+      // wave at the start of the step
+#pragma unroll
+      for (int i = 0; i < PPS * C::RT * C::FTW; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);                   // VALU
+        if (i % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if constexpr (SCHED == 2) {
       // one P.c_v product, then a few vector instructions, repeated, so the
       // softmax runs in the shadow of the products
@@ -647,7 +665,8 @@ hipError_t launch_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl,
       case 1: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 2, 1, true>(STARKV_PREFILL_ARGS);
       case 2: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 2, 2, false>(STARKV_PREFILL_ARGS);
       case 3: return prefill_instance<32, 128, 64, 512, 4, 32, 8, 2, 2, 2, true>(STARKV_PREFILL_ARGS);
-      default: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 2, 2, true>(STARKV_PREFILL_ARGS);
+      case 4: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 2, 2, true>(STARKV_PREFILL_ARGS);
+      default: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 3, 4, true>(STARKV_PREFILL_ARGS);
     }
   }
   if (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64)
