@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of one decode step of paged low-rank-compressed attention on
-one MI355X (q projection, split-K latent attention, combine, W_h
-up-projection), the workload being batch 16 x 2048 cached tokens, 32 heads,
+one MI355X (q projection, split-K latent attention, the merge of the
+splits with the W_h up-projection), the workload being batch 16 x 2048 cached tokens, 32 heads,
 d = 128, r_k = 64 per head, joint r_v = 512, 16-token pages, fp16 storage.
 
     python bench.py [--steps K] [--warmup W] [--workload decode_b16] [--no-cpu]

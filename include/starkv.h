@@ -125,8 +125,8 @@ starkv_status starkv_decode_workspace_size(const starkv_dims* dims, int32_t batc
  *   out           [batch][H][d] fp16
  *   workspace     >= starkv_decode_workspace_size(...) bytes, 256-byte aligned
  *                 preferred; contents need no initialisation
- * Four kernels run on `stream`: q projection, split-K latent attention,
- * split combine, and the W_h up-projection.
+ * Three kernels run on `stream`: q projection, split-K latent attention,
+ * and the merge of the splits fused with the W_h up-projection.
  */
 starkv_status starkv_decode_attn(const starkv_dims* dims, const void* q, const void* k_cache,
                                  const void* v_cache, const void* U, const void* W,

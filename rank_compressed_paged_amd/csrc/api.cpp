@@ -143,7 +143,7 @@ PrefillWorkspace prefill_workspace_layout(const ShapeKey& s, int total_q) {
   size_t off = 0;
   w.qt_off = off;
   off = align256(off + (size_t)total_q * s.H * s.rk * 2);
-  w.z_off = off;  // fp16 z tiled by 32-token blocks, see launch_upproj
+  w.z_off = off;  // fp16 z tiled by 32-token blocks, see launch_upproj_tiled
   off = align256(off + (size_t)((total_q + 31) / 32) * 32 * s.H * s.rv * 2);
   w.total = off;
   return w;

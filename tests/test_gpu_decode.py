@@ -1,5 +1,6 @@
 """GPU parity of decode attention (q projection, split-K latent attention,
-combine and up-projection) against the fp64 oracle, through the C ABI."""
+merge of the splits with the up-projection) against the fp64 oracle,
+through the C ABI."""
 import os
 
 import numpy as np
