@@ -396,10 +396,11 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
 //    z[b,h,:] = sum_s w_s z_s / sum_s w_s with w_s = l_s 2^(m_s - M),
 //    M = max_s m_s, then out[b,h,:] = W_h z[b,h,:], in one launch.
 // One work group of 4 waves per head h and TB consecutive sequences.
-//   * W_h (D x RV fp16) goes straight from memory into the A operands of
-//     v_mfma_f32_16x16x32_f16, wave w owning output rows w*D/4 .. +D/4-1;
-//     those loads are issued right after the partials' first round and stay
-//     in flight through the merge, which waits for the partials only;
+//   * W_h (D x RV fp16) is requested right after the partials' first round
+//     and stays in flight through the merge, which waits for the partials
+//     only; it reaches the A operands of v_mfma_f32_16x16x32_f16 through LDS
+//     (256-thread tiles: whole rows per load instruction) or straight from
+//     memory (512-thread tiles), a product wave owning D/MW output rows;
 //   * partials: thread u of the TB*RV/4 four-feature units merges its
 //     features of one sequence over the splits, CB splits per round of
 //     requests (weight 0 past the sequence's last split); the rounds run
@@ -439,6 +440,14 @@ __global__ __launch_bounds__(NT) void finish_kernel(const float* __restrict__ ml
   static_assert(SG == 1 || SG * UG <= NT, "split groups must fit the work group");
   // hi and lo parts of z by sequence; row TB stays zero
   __shared__ __attribute__((aligned(16))) half_t sZ[2][TB + 1][LDZ];
+  // 256-thread tiles stage W_h in LDS by whole rows (each load instruction
+  // covers one contiguous 1 KiB row), which moves it faster than loading the
+  // product operands directly (16 rows x 64 bytes per instruction); the
+  // 512-thread tiles have no LDS left for it.
+  constexpr bool WL = NT == 256;
+  constexpr int WCH = WL ? D * RV / 8 / NT : 1;  // 16-byte chunks per thread
+  __shared__ __attribute__((aligned(16))) half_t sW[WL ? D : 1][WL ? RV + 8 : 8];
+  half8 wst[WCH];
   // per split group: running max, sum and four weighted features of a unit
   __shared__ float sMerge[SG > 1 ? SG : 1][SG > 1 ? UG : 1][6];
 
@@ -462,6 +471,14 @@ __global__ __launch_bounds__(NT) void finish_kernel(const float* __restrict__ ml
   // 32*k + 8*quad .. +7, requested after the partials' first round (below)
   half8 wa[RTW][KS];
   auto load_w = [&]() {
+    if constexpr (WL) {
+#pragma unroll
+      for (int j = 0; j < WCH; ++j) {
+        const int c = tid + j * NT;  // chunk c: row c / (RV/8), 8 features
+        wst[j] = *(const half8*)(W + ((size_t)h * D + c / (RV / 8)) * RV + (c % (RV / 8)) * 8);
+      }
+      return;
+    }
     const half_t* wrow = W + ((size_t)h * D + w * (D / MW) + col) * RV + quad * 8;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
@@ -497,7 +514,7 @@ __global__ __launch_bounds__(NT) void finish_kernel(const float* __restrict__ ml
       }
     };
     if (merger) request(0);
-    if (j == 0 && w < MW) load_w();
+    if (j == 0 && (WL || w < MW)) load_w();
     __builtin_amdgcn_sched_barrier(0);  // the sequence length is read after these requests
     const int n_pages =
         min(min((seq_lens[b] + BS - 1) / BS, max_blocks), num_splits * pages_per_split);
@@ -567,8 +584,22 @@ __global__ __launch_bounds__(NT) void finish_kernel(const float* __restrict__ ml
       *(half4*)&sZ[1][u / F4][f4 * 4] = zl;
     }
   }
-  block_sync_lds();  // LDS only: the W_h loads stay in flight
+  if constexpr (WL) {
+#pragma unroll
+    for (int j = 0; j < WCH; ++j) {
+      const int c = tid + j * NT;
+      *(half8*)&sW[c / (RV / 8)][(c % (RV / 8)) * 8] = wst[j];
+    }
+  }
+  block_sync_lds();  // LDS only: (without staging) the W_h loads stay in flight
   if (w >= MW) return;  // no barrier follows
+  if constexpr (WL) {
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+        wa[rt][k] = *(const half8*)&sW[w * (D / MW) + rt * 16 + col][k * 32 + quad * 8];
+  }
 
   // B column col: sequence col/2, part col%2
   const int tc = col >> 1;
