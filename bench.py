@@ -47,18 +47,21 @@ DECODE_KERNEL = "decode_split_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_kernel_decode_b16_traffic.txt")
 TRAFFIC_WORKLOAD = "decode_b16"
 SPLIT_SECTION = ("// 2. split-K latent attention", "// 3. finish")
+LAUNCH_DECODE = "hipError_t launch_decode("
 
 
 def kernel_source_hash():
-    """Hash of the split-K kernel's device code (its section of decode.hip)
-    and of the shared device helpers: the traffic summary is only used while
-    this matches the code the counters were taken on."""
+    """Hash of the split-K kernel's device code (its section of decode.hip),
+    of the launcher that picks its instance, and of the shared device
+    helpers: the traffic summary is only used while this matches the code
+    the counters were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rank_compressed_paged_amd", "csrc")
     with open(os.path.join(csrc, "decode.hip")) as f:
         text = f.read()
     a, b = text.index(SPLIT_SECTION[0]), text.index(SPLIT_SECTION[1])
     h.update(text[a:b].encode())
+    h.update(text[text.index(LAUNCH_DECODE):].encode())
     with open(os.path.join(csrc, "common.h"), "rb") as f:
         h.update(f.read())
     return h.hexdigest()[:16]
