@@ -43,6 +43,8 @@ __all__ = [
     "softmax_rows",
     "decode",
     "prefill",
+    "fit_bases",
+    "projector",
 ]
 
 
@@ -202,3 +204,52 @@ def prefill(q, query_start_loc, k_cache, v_cache, U, W, block_tables,
             o, _ = _attend(qf[q0:q1, h], K[:, h, :], V[:, h, :], scale, visible)
             out[q0:q1, h] = o
     return out
+
+
+# ---------------------------------------------------------------------------
+# Bases from samples.  The pages calibrate U_h and W offline by short
+# knowledge distillation (README, introduction), which needs a trained model
+# and stays out of scope.  The unlearned stand-in: the rank-r linear
+# compression c = B^T x, x^ = B c with orthonormal B that loses the least
+# squared error over the samples (Eckart-Young), i.e. B spans the top-r
+# eigenspace of the uncentred second moment X^T X (X = samples as rows; no
+# mean is subtracted because the reconstruction B c has no offset term).
+# Keys: one basis per head from that head's keys; values: one joint basis
+# from vec(v[n]) flattened head-major (row h*d + i), as in append().
+# ---------------------------------------------------------------------------
+def _top_eigvecs(G, r):
+    """Orthonormal eigenvectors of the symmetric G for its r largest
+    eigenvalues (columns, largest first), and all eigenvalues descending."""
+    w, Q = np.linalg.eigh(G)  # ascending
+    order = np.argsort(w)[::-1]
+    return Q[:, order[:r]], w[order]
+
+
+def fit_bases(k, v, r_k, r_v):
+    """Least-squares bases of the samples k, v [N, H, d] (fp16).
+
+    Returns U [H, d, r_k] and W [H*d, r_v] fp64 with orthonormal columns
+    spanning the top eigenspaces of K_h^T K_h (per head) and V^T V, plus
+    their descending eigenvalues (lists: per head for keys, one for values).
+    The subspaces are unique when the r-th and (r+1)-th eigenvalues differ;
+    the bases themselves only up to a rotation inside them.
+    """
+    kf = _f64(k)
+    vf = _f64(v)
+    N, H, d = kf.shape
+    U = np.empty((H, d, r_k))
+    ev_k = []
+    for h in range(H):
+        Kh = kf[:, h, :]
+        U[h], w = _top_eigvecs(Kh.T @ Kh, r_k)
+        ev_k.append(w)
+    Vm = vf.reshape(N, H * d)
+    W, ev_v = _top_eigvecs(Vm.T @ Vm, r_v)
+    return U, W, ev_k, ev_v
+
+
+def projector(B):
+    """Orthogonal projector B (B^T B)^-1 B^T onto the column space of B: the
+    rotation-free quantity two bases of one subspace share."""
+    Bf = _f64(B)
+    return Bf @ np.linalg.solve(Bf.T @ Bf, Bf.T)

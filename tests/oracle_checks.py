@@ -344,7 +344,130 @@ def check_paging_fixture(orc, fixture):
         assert np.array_equal(cv[:, 0], -(100 * b + np.arange(L)))
 
 
+# ---------------------------------------------------------------------------
+# Bases from samples (fit_bases): planted subspaces with exact small-integer
+# data, optimality against independent candidate bases, agreement with an
+# SVD of the sample matrix, and invariances.
+# ---------------------------------------------------------------------------
+def _planted(rng, N, H, d, rk, rv, mean_dir=False):
+    """Integer samples exact in fp16: keys of head h in span(A_h) (plus,
+    with mean_dir, a constant offset along a direction outside it), values
+    vec(v[n]) (head-major) in span(B)."""
+    A = rng.integers(-2, 3, size=(H, d, rk)).astype(np.float64)
+    B = rng.integers(-2, 3, size=(H * d, rv)).astype(np.float64)
+    zk = rng.integers(-3, 4, size=(N, H, rk)).astype(np.float64)
+    zv = rng.integers(-3, 4, size=(N, rv)).astype(np.float64)
+    k = np.einsum("hdr,nhr->nhd", A, zk)
+    v = (zv @ B.T).reshape(N, H, d)
+    return k, v, A, B
+
+
+def _residual(X, B):
+    """Sum of squared reconstruction errors of the rows of X through the
+    orthonormal columns of B."""
+    R = X - (X @ B) @ B.T
+    return float(np.sum(R * R))
+
+
+def check_fit_planted_subspace(orc):
+    rng = np.random.default_rng(40)
+    N, H, d, rk, rv = 48, 3, 8, 3, 5
+    k, v, A, B = _planted(rng, N, H, d, rk, rv)
+    assert np.array_equal(k.astype(np.float16).astype(np.float64), k)  # exact in fp16
+    U, W, ek, ev = orc.fit_bases(k.astype(np.float16), v.astype(np.float16), rk, rv)
+    for h in range(H):
+        assert np.abs(orc.projector(U[h]) - orc.projector(A[h])).max() < 1e-9
+        assert ek[h][rk] < 1e-9 * ek[h][0]  # nothing outside the planted span
+    assert np.abs(orc.projector(W) - orc.projector(B)).max() < 1e-9
+    assert ev[rv] < 1e-9 * ev[0]
+
+
+def check_fit_uncentred(orc):
+    """Samples with a constant offset outside span(A): the uncentred
+    second moment keeps the offset's direction, so rank(A)+1 columns
+    reconstruct every sample exactly (a mean-centred fit would not)."""
+    rng = np.random.default_rng(41)
+    N, d, r = 40, 8, 2
+    A = rng.integers(-2, 3, size=(d, r)).astype(np.float64)
+    mu = None
+    for i in range(d):  # an integer offset 4 e_i outside span(A)
+        e = np.zeros(d)
+        e[i] = 1.0
+        if np.linalg.matrix_rank(np.column_stack([A, e])) == r + 1:
+            mu = 4.0 * e
+            break
+    assert mu is not None
+    z = rng.integers(-3, 4, size=(N, r)).astype(np.float64)
+    k = (mu[None, :] + z @ A.T)[:, None, :]
+    v = k.copy()
+    U, W, _, _ = orc.fit_bases(k.astype(np.float16), v.astype(np.float16), r + 1, r + 1)
+    X = k[:, 0, :]
+    assert _residual(X, U[0]) < 1e-18 * np.sum(X * X) + 1e-20
+    assert _residual(X, W) < 1e-18 * np.sum(X * X) + 1e-20
+
+
+def check_fit_optimal_against_candidates(orc):
+    """Eckart-Young: no other orthonormal rank-r basis reconstructs the
+    samples better (random bases, and bases of r of the samples)."""
+    rng = np.random.default_rng(42)
+    N, H, d, rk, rv = 64, 2, 12, 4, 6
+    scale = np.linspace(3.0, 0.2, d)
+    k = (rng.standard_normal((N, H, d)) * scale).astype(np.float16)
+    v = (rng.standard_normal((N, H, d)) * scale).astype(np.float16)
+    U, W, _, _ = orc.fit_bases(k, v, rk, rv)
+    kf, vf = k.astype(np.float64), v.astype(np.float64).reshape(N, H * d)
+    for h in range(H):
+        best = _residual(kf[:, h, :], U[h])
+        for _ in range(20):
+            Q = np.linalg.qr(rng.standard_normal((d, rk)))[0]
+            assert best <= _residual(kf[:, h, :], Q) * (1 + 1e-12)
+        Q = np.linalg.qr(kf[rng.choice(N, rk, replace=False), h, :].T)[0]
+        assert best <= _residual(kf[:, h, :], Q) * (1 + 1e-12)
+    best = _residual(vf, W)
+    for _ in range(20):
+        Q = np.linalg.qr(rng.standard_normal((H * d, rv)))[0]
+        assert best <= _residual(vf, Q) * (1 + 1e-12)
+
+
+def check_fit_matches_svd_of_samples(orc):
+    """The top right singular vectors of the sample matrix (a different
+    LAPACK path) span the same subspaces; the bases are orthonormal."""
+    rng = np.random.default_rng(43)
+    N, H, d, rk, rv = 80, 2, 10, 3, 7
+    scale = np.geomspace(4.0, 0.1, d)
+    k = (rng.standard_normal((N, H, d)) * scale).astype(np.float16)
+    v = (rng.standard_normal((N, H, d)) * scale).astype(np.float16)
+    U, W, _, _ = orc.fit_bases(k, v, rk, rv)
+    for h in range(H):
+        Vt = np.linalg.svd(k[:, h, :].astype(np.float64), full_matrices=False)[2]
+        assert np.abs(orc.projector(U[h]) - orc.projector(Vt[:rk].T)).max() < 1e-9
+        assert np.abs(U[h].T @ U[h] - np.eye(rk)).max() < 1e-12
+    Vt = np.linalg.svd(v.astype(np.float64).reshape(N, H * d), full_matrices=False)[2]
+    assert np.abs(orc.projector(W) - orc.projector(Vt[:rv].T)).max() < 1e-9
+    assert np.abs(W.T @ W - np.eye(rv)).max() < 1e-12
+
+
+def check_fit_invariances(orc):
+    """Sample order and a common power-of-two scale leave the subspaces."""
+    rng = np.random.default_rng(44)
+    N, H, d, rk, rv = 50, 2, 8, 3, 4
+    scale = np.linspace(2.0, 0.3, d)
+    k = (rng.standard_normal((N, H, d)) * scale).astype(np.float16)
+    v = (rng.standard_normal((N, H, d)) * scale).astype(np.float16)
+    U, W, _, _ = orc.fit_bases(k, v, rk, rv)
+    perm = rng.permutation(N)
+    U2, W2, _, _ = orc.fit_bases(k[perm] * np.float16(2), v[perm] * np.float16(2), rk, rv)
+    for h in range(H):
+        assert np.abs(orc.projector(U[h]) - orc.projector(U2[h])).max() < 1e-9
+    assert np.abs(orc.projector(W) - orc.projector(W2)).max() < 1e-9
+
+
 ALL_CHECKS = [
+    check_fit_planted_subspace,
+    check_fit_uncentred,
+    check_fit_optimal_against_candidates,
+    check_fit_matches_svd_of_samples,
+    check_fit_invariances,
     check_full_rank_decode_matches_sdpa,
     check_full_rank_prefill_matches_sdpa,
     check_subspace_lossless,

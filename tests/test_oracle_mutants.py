@@ -40,6 +40,11 @@ MUTANTS = {
     "append_truncates": ("kc[blk, h, off, :] = (Uf[h].T @ kf[n, h]).astype(np.float16)",
                          "kc[blk, h, off, :] = np.trunc((Uf[h].T @ kf[n, h]) * 64) / 64"),
     "empty_sequence_nan": ("out[b] = 0.0", "out[b] = np.nan"),
+    "fit_bottom_eigvecs": ("order = np.argsort(w)[::-1]", "order = np.argsort(w)"),
+    "fit_mean_centred": ("        Kh = kf[:, h, :]\n", "        Kh = kf[:, h, :] - kf[:, h, :].mean(axis=0)\n"),
+    "fit_v_feature_major": ("Vm = vf.reshape(N, H * d)", "Vm = vf.transpose(0, 2, 1).reshape(N, H * d)"),
+    "fit_wrong_head": ("        Kh = kf[:, h, :]\n", "        Kh = kf[:, (h + 1) % H, :]\n"),
+    "fit_values_from_keys": ("Vm = vf.reshape(N, H * d)", "Vm = kf.reshape(N, H * d)"),
     "decode_drops_last_token": ("ck, cv = gather_sequence_latents(k_cache, v_cache, block_tables[b], L)\n        K, V = reconstruct_sequence(ck, cv, U, W)\n        ph",
                                 "ck, cv = gather_sequence_latents(k_cache, v_cache, block_tables[b], max(L - 1, 1))\n        K, V = reconstruct_sequence(ck, cv, U, W)\n        L = K.shape[0]\n        ph"),
 }
