@@ -40,9 +40,10 @@
  *   - Contents of device index arrays (block tables, seq_lens, slots,
  *     query_start_loc) are trusted.  Block ids outside [0, num_blocks) and
  *     slots outside the cache are skipped rather than dereferenced.
- *   - Compiled shape instances: (H, d, r_k, r_v) = (32, 128, 64, 512) and
- *     (4, 64, 16, 64), block size 16.  Other shapes return
- *     STARKV_ERR_UNSUPPORTED.
+ *   - Compiled shape instances of the attention and append calls:
+ *     (H, d, r_k, r_v) = (32, 128, 64, 512) and (4, 64, 16, 64), block size
+ *     16.  Other shapes return STARKV_ERR_UNSUPPORTED.  The bases fit takes
+ *     any shape within the limits stated at its declaration.
  */
 #ifndef STARKV_H_
 #define STARKV_H_
@@ -181,6 +182,44 @@ starkv_status starkv_set_timing_events(void* start, void* stop, int32_t which);
  */
 starkv_status starkv_decode_plan(const starkv_dims* dims, int32_t batch, int32_t max_seq_len,
                                  int32_t* pages_per_split, int32_t* num_splits);
+
+/*
+ * Bases from samples (the step before the path).  The pages calibrate U_h
+ * and W offline by a short knowledge distillation (README, introduction and
+ * "Quick start"); this is an unlearned stand-in that returns the
+ * least-squares optimal bases of K/V samples:
+ *     U_h spans the top-r_k eigenspace of K_h^T K_h   (head-wise for keys)
+ *     W   spans the top-r_v eigenspace of V^T V       (joint for values)
+ * where row n of K_h is k[n, h, :] and row n of V is vec(v[n]) (head-major,
+ * as in the append).  The second moments are uncentred, as the compression
+ * is linear with no offset.  Columns come out orthonormal (to fp16
+ * rounding); within the subspace the basis is arbitrary.
+ * Method: subspace iteration from u0 / w0, `iters` products with the Gram
+ * matrix, each followed by a Cholesky QR orthonormalisation (fp64 normal
+ * equations), two on the last.  The result is the top eigenspace when the
+ * start is not deficient in it and the r-th and (r+1)-th eigenvalues are
+ * apart: the error falls as (lambda_{r+1} / lambda_r)^iters.
+ *   dims          head_dim a multiple of 64; rank_k, rank_v <= 512;
+ *                 H * head_dim <= 65536; block_size and num_blocks unused
+ *   k, v          [num_samples][H][d] fp16; num_samples >= rank_k, rank_v
+ *   u0            [H][d][r_k] fp32 starting matrices (e.g. Gaussian)
+ *   w0            [H*d][r_v] fp32
+ *   iters         1 .. 1000
+ *   U             [H][d][r_k] fp16 out (the layout append/decode take)
+ *   W             [H*d][r_v] fp16 out
+ *   workspace     >= starkv_fit_workspace_size(...) bytes; no initialisation
+ *                 (about (H*d)^2 * 4 bytes: the value Gram matrix in fp32)
+ *   info          optional (NULL = not reported), int32 device word: set to
+ *                 the number of non-positive pivots the Cholesky steps met
+ *                 (0 on success; > 0 means rank-deficient samples or start,
+ *                 and the output is then not orthonormal)
+ * Asynchronous on `stream`; about 20 kernels per iteration.
+ */
+starkv_status starkv_fit_workspace_size(const starkv_dims* dims, size_t* bytes /* (host) */);
+starkv_status starkv_fit_bases(const starkv_dims* dims, const void* k, const void* v,
+                               int32_t num_samples, const float* u0, const float* w0,
+                               int32_t iters, void* U, void* W, void* workspace,
+                               size_t workspace_bytes, int32_t* info, void* stream);
 
 /*
  * Measurement utility (not part of the attention path): read `bytes` bytes

@@ -180,6 +180,22 @@ starkv_status check_ptrs(std::initializer_list<const void*> ptrs) {
 
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
+// The bases fit has its own limits: d a multiple of 64 (Gram tiles), ranks
+// up to 512 (the triangular solve keeps a row block of Q in LDS); the page
+// size and page count do not enter.
+starkv_status check_fit_dims(const starkv_dims* d, ShapeKey* key) {
+  if (!d) return STARKV_ERR_NULL;
+  if (d->num_heads <= 0 || d->head_dim <= 0 || d->rank_k <= 0 || d->rank_v <= 0)
+    return STARKV_ERR_DIMS;
+  if (d->rank_k > d->head_dim || (long)d->rank_v > (long)d->num_heads * d->head_dim)
+    return STARKV_ERR_DIMS;
+  if (d->head_dim % 64 != 0 || d->rank_k > 512 || d->rank_v > 512 || d->num_heads > 65535 ||
+      (long)d->num_heads * d->head_dim > 65536)
+    return STARKV_ERR_UNSUPPORTED;
+  *key = ShapeKey{d->num_heads, d->head_dim, d->rank_k, d->rank_v};
+  return STARKV_OK;
+}
+
 starkv_status check_paging(int32_t batch, int32_t max_seq_len, int32_t max_blocks, int bs) {
   if (batch < 0 || max_seq_len < 0 || max_blocks < 0) return STARKV_ERR_DIMS;
   if (batch > 65535) return STARKV_ERR_DIMS;
@@ -320,6 +336,33 @@ starkv_status starkv_prefill_attn(const starkv_dims* dims, const void* q,
   e = launch_prefill(key, wb + ws.qt_off, query_start_loc, total_q, max_query_len, k_cache,
                      v_cache, W, block_tables, max_blocks_per_seq, seq_lens, dims->num_blocks,
                      batch, (void*)(wb + ws.z_off), out, s);
+  return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
+}
+
+starkv_status starkv_fit_workspace_size(const starkv_dims* dims, size_t* bytes) {
+  ShapeKey key;
+  const starkv_status st = check_fit_dims(dims, &key);
+  if (st != STARKV_OK) return st;
+  if (!bytes) return STARKV_ERR_NULL;
+  *bytes = fit_workspace_layout(key).total;
+  return STARKV_OK;
+}
+
+starkv_status starkv_fit_bases(const starkv_dims* dims, const void* k, const void* v,
+                               int32_t num_samples, const float* u0, const float* w0,
+                               int32_t iters, void* U, void* W, void* workspace,
+                               size_t workspace_bytes, int32_t* info, void* stream) {
+  ShapeKey key;
+  starkv_status st = check_fit_dims(dims, &key);
+  if (st != STARKV_OK) return st;
+  if (num_samples < key.rk || num_samples < key.rv) return STARKV_ERR_DIMS;
+  if (iters < 1 || iters > 1000) return STARKV_ERR_ARG;
+  st = check_ptrs({k, v, u0, w0, U, W, workspace});
+  if (st != STARKV_OK) return st;
+  if (info && ((uintptr_t)info & 3u) != 0) return STARKV_ERR_ALIGN;
+  if (workspace_bytes < fit_workspace_layout(key).total) return STARKV_ERR_WORKSPACE;
+  const hipError_t e = launch_fit(key, k, v, num_samples, u0, w0, iters, U, W, workspace,
+                                  (int*)info, (hipStream_t)stream);
   return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
 }
 

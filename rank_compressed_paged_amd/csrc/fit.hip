@@ -1,0 +1,750 @@
+// Bases from samples: the step before the attention path.  The pages
+// calibrate U_h and W offline by a short knowledge distillation (Proxima
+// README, introduction and "Quick start"), which needs a trained model and
+// stays out of scope.  This is the unlearned stand-in: the least-squares
+// optimal rank-r linear compressions of K/V samples (Eckart-Young).  U_h
+// spans the top-r_k eigenspace of G_h = K_h^T K_h (the keys of head h as
+// rows, head-wise as the pages decompose keys); W spans the top-r_v
+// eigenspace of G_v = V^T V (rows vec(v[n]), head-major, joint across heads as
+// the pages decompose values).
+//
+// Method: subspace iteration from the caller's starting matrices,
+//     Y = G Q,  Q = orth(Y)       (iters times)
+// with orth one Cholesky QR (S = Y^T Y in fp64, S = L L^T, Q = Y L^-T) and,
+// on the last iteration, a second one (Cholesky QR2), which leaves Q
+// orthonormal to fp32 rounding.  Any orthonormal basis of the subspace
+// serves the compression (attention only sees B B^T), so no small
+// eigenproblem is solved at the end.
+//
+// Kernels (all batched over problems: H key problems of size d, one value
+// problem of size H*d):
+//   gram_kernel        lower TMxTM tiles of X^T X for fp16 samples, fp32
+//                      sums, v_mfma_f32_32x32x16_f16 with operands read
+//                      through the transposing LDS read
+//   symm_f32_kernel    Y = G Q, G stored as its lower tiles (fp32 VALU)
+//   syrk_f64_kernel    row slices of S = Y^T Y, lower 64x64 tiles, fp64 sums
+//   sum_slices_kernel  S = sum of the slices
+//   chol_panel_kernel  one work group per problem: factor the 64x64 diagonal
+//                      block of the current panel and invert it
+//   chol_update_kernel panel rows L_I = A_Ip D^T and the trailing update
+//                      A_IJ -= L_I L_J^T over the lower tiles
+//   trsm_kernel        Q = Y L^-T, a work group per 16 rows
+//   to_f16_kernel      the result, rounded to fp16
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace starkv {
+
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane q addresses row
+// r0 + q/4, columns c0 + 4*(q%4); lane i then receives rows r0 .. r0+3 of
+// column c0 + i.
+__device__ __forceinline__ half4 fit_tr16(const half_t* p) {
+  typedef __attribute__((address_space(3))) short4v lds_short4v;
+  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)p);
+  return __builtin_bit_cast(half4, r);
+}
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Row I and column J <= I of lower-triangle tile t (row-major order).
+__device__ __forceinline__ void tri_index(int t, int& I, int& J) {
+  int i = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
+  while ((i + 1) * (i + 2) / 2 <= t) ++i;
+  while (i * (i + 1) / 2 > t) --i;
+  I = i;
+  J = t - i * (i + 1) / 2;
+}
+
+// ---------------------------------------------------------------------------
+// Gram matrices.  Tasks 0 .. tiles_v-1 are the lower tiles of G_v (X = v
+// samples, n = H*d); the next H * tiles_k are the lower tiles of each G_h
+// (X = the d columns of head h of the k samples).  Task order is row-major
+// over each triangle, so neighbouring tasks share a strip; block b runs task
+// (b % 8) * ceil(T / 8) + b / 8, which keeps neighbours on one XCD (its L2).
+// Work group: 4 waves, wave w owning the (TM/2)^2 quadrant (w/2, w%2) as
+// (TM/64)^2 32x32 accumulators.  Per 32-sample chunk the two TM-column
+// strips are staged in LDS as they lie in memory (whole rows, 16-byte
+// pieces), double-buffered; samples past N load as zero.  Diagonal tiles are
+// computed whole, so G[i][j] is valid whenever j/TM <= i/TM.
+// ---------------------------------------------------------------------------
+constexpr int kGramK = 32;
+
+template <int TM>
+__global__ __launch_bounds__(256) void gram_kernel(const half_t* __restrict__ kx,
+                                                   const half_t* __restrict__ vx, int N, int H,
+                                                   int d, float* __restrict__ Gk,
+                                                   float* __restrict__ Gv, int tiles_v,
+                                                   int tiles_k, int* __restrict__ info) {
+  constexpr int LS = TM + 16;          // LDS row stride (halves): 8-bank row shift
+  constexpr int CPR = TM / 8;          // 16-byte pieces per strip row
+  constexpr int NCH = kGramK * CPR / 256;
+  constexpr int WT = TM / 2, MB = WT / 32;
+  __shared__ __attribute__((aligned(16))) half_t sI[2][kGramK][LS];
+  __shared__ __attribute__((aligned(16))) half_t sJ[2][kGramK][LS];
+
+  const int total = tiles_v + H * tiles_k;
+  const int per = ceil_div(total, 8);
+  const int t = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && info) info[0] = 0;
+  if (t >= total) return;
+  const int ld = H * d;
+  const half_t* X;
+  float* G;
+  int n, I, J;
+  if (t < tiles_v) {
+    X = vx;
+    G = Gv;
+    n = ld;
+    tri_index(t, I, J);
+  } else {
+    const int u = t - tiles_v, h = u / tiles_k;
+    X = kx + (size_t)h * d;
+    G = Gk + (size_t)h * d * d;
+    n = d;
+    tri_index(u - h * tiles_k, I, J);
+  }
+  const int ci = I * TM, cj = J * TM;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wi = w >> 1, wj = w & 1;
+  const int grp = lane >> 4, q = lane & 15;
+  const int f_row = 8 * (grp >> 1) + (q >> 2);
+  const int f_col = 16 * (grp & 1) + 4 * (q & 3);
+
+  half8 ra[NCH], rb[NCH];
+  auto load = [&](int s0) {
+#pragma unroll
+    for (int e = 0; e < NCH; ++e) {
+      const int pc = tid + 256 * e, row = pc / CPR, col = (pc % CPR) * 8;
+      const bool ok = s0 + row < N;
+      const size_t off = (size_t)(ok ? s0 + row : 0) * ld + col;
+      const half8 z = {};
+      ra[e] = ok ? *(const half8*)(X + off + ci) : z;
+      rb[e] = ok ? *(const half8*)(X + off + cj) : z;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < NCH; ++e) {
+      const int pc = tid + 256 * e, row = pc / CPR, col = (pc % CPR) * 8;
+      *(half8*)&sI[buf][row][col] = ra[e];
+      *(half8*)&sJ[buf][row][col] = rb[e];
+    }
+  };
+
+  float16v acc[MB][MB];
+#pragma unroll
+  for (int a = 0; a < MB; ++a)
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  load(0);
+  store(0);
+  __syncthreads();
+  int buf = 0;
+  for (int s0 = 0; s0 < N; s0 += kGramK) {
+    const bool more = s0 + kGramK < N;  // uniform
+    if (more) load(s0 + kGramK);
+#pragma unroll
+    for (int c = 0; c < kGramK / 16; ++c) {
+      half8 av[MB], bv[MB];
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const half_t* ap = &sI[buf][16 * c + f_row][wi * WT + 32 * m + f_col];
+        const half_t* bp = &sJ[buf][16 * c + f_row][wj * WT + 32 * m + f_col];
+        const half4 a0 = fit_tr16(ap), a1 = fit_tr16(ap + 4 * LS);
+        const half4 b0 = fit_tr16(bp), b1 = fit_tr16(bp + 4 * LS);
+        av[m] = half8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        bv[m] = half8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      }
+#pragma unroll
+      for (int a = 0; a < MB; ++a)
+#pragma unroll
+        for (int b = 0; b < MB; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[a], bv[b], acc[a][b], 0, 0, 0);
+    }
+    if (more) store(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+  // register e of a 32x32 accumulator: row 8*(e/4) + 4*(lane/32) + e%4,
+  // column lane%32
+  const int c32 = lane & 31, hf = lane >> 5;
+#pragma unroll
+  for (int a = 0; a < MB; ++a)
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = ci + wi * WT + 32 * a + 8 * (e / 4) + 4 * hf + (e % 4);
+        const int col = cj + wj * WT + 32 * b + c32;
+        G[(size_t)row * n + col] = acc[a][b][e];
+      }
+}
+
+// ---------------------------------------------------------------------------
+// Y_p = G_p Q_p: G_p n x n holding only its lower TM-tiles (element [i][k]
+// is read from [k][i] when k/TM > i/TM), Q_p and Y_p n x r row-major fp32.
+// grid (ceil(r/64), n/64, problems); 256 threads, 4x4 outputs each; 16-deep
+// k chunks through LDS.  n is a multiple of 64 and of 16.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void symm_f32_kernel(const float* __restrict__ G, size_t sg,
+                                                       int n, int tm, const float* __restrict__ Q,
+                                                       size_t sq, float* __restrict__ Y, size_t sy,
+                                                       int r) {
+  __shared__ __attribute__((aligned(16))) float sA[16][64 + 4];  // [k][row]
+  __shared__ __attribute__((aligned(16))) float sB[16][64 + 4];  // [k][column]
+  const int p = blockIdx.z;
+  const float* Gp = G + (size_t)p * sg;
+  const float* Qp = Q + (size_t)p * sq;
+  float* Yp = Y + (size_t)p * sy;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
+  for (int k0 = 0; k0 < n; k0 += 16) {
+    const bool mirror = (k0 / tm) > (r0 / tm);  // uniform
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + e * 256;
+      if (mirror) {
+        const int ra = idx & 63, ka = idx >> 6;
+        sA[ka][ra] = Gp[(size_t)(k0 + ka) * n + r0 + ra];
+      } else {
+        const int ra = idx >> 4, ka = idx & 15;
+        sA[ka][ra] = Gp[(size_t)(r0 + ra) * n + k0 + ka];
+      }
+      const int kb = idx >> 6, cb = idx & 63;
+      sB[kb][cb] = (c0 + cb < r) ? Qp[(size_t)(k0 + kb) * r + c0 + cb] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const float4v av = *(const float4v*)&sA[kk][ty * 4];
+      const float4v bv = *(const float4v*)&sB[kk][tx * 4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fmaf(av[a], bv[b], acc[a][b]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int c = c0 + tx * 4 + b;
+      if (c < r) Yp[(size_t)(r0 + ty * 4 + a) * r + c] = acc[a][b];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Slice s of S_p = Y_p^T Y_p: sum over rows [s*rows, (s+1)*rows) of Y_p
+// (n x r fp32) of the exact fp64 products, lower 64x64 tiles only.
+// grid (tiles, problems * slices); 256 threads, 4x4 outputs each.
+// Output: S + (p * slices + s) * r * r.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void syrk_f64_kernel(const float* __restrict__ Y, size_t sy,
+                                                       int n, int r, int slices, int rows,
+                                                       double* __restrict__ S) {
+  __shared__ __attribute__((aligned(16))) float sa[32][64 + 4];
+  __shared__ __attribute__((aligned(16))) float sb[32][64 + 4];
+  const int p = blockIdx.y / slices, s = blockIdx.y % slices;
+  int I, J;
+  tri_index(blockIdx.x, I, J);
+  const float* Yp = Y + (size_t)p * sy;
+  const int a0 = I * 64, b0 = J * 64;
+  const int i_beg = s * rows, i_end = min(n, i_beg + rows);
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  double acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+  for (int i0 = i_beg; i0 < i_end; i0 += 32) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int idx = tid + e * 256, ii = idx >> 6, c = idx & 63;
+      const bool rok = i0 + ii < i_end;
+      sa[ii][c] = (rok && a0 + c < r) ? Yp[(size_t)(i0 + ii) * r + a0 + c] : 0.f;
+      sb[ii][c] = (rok && b0 + c < r) ? Yp[(size_t)(i0 + ii) * r + b0 + c] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int ii = 0; ii < 32; ++ii) {
+      const float4v av = *(const float4v*)&sa[ii][ty * 4];
+      const float4v bv = *(const float4v*)&sb[ii][tx * 4];
+      double bd[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) bd[b] = (double)bv[b];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const double ad = (double)av[a];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fma(ad, bd[b], acc[a][b]);
+      }
+    }
+    __syncthreads();
+  }
+  double* Sp = S + ((size_t)p * slices + s) * r * r;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int ra = a0 + ty * 4 + a, cb = b0 + tx * 4 + b;
+      if (ra < r && cb < r) Sp[(size_t)ra * r + cb] = acc[a][b];
+    }
+}
+
+// A_p = sum over s of S_(p*slices + s), entries in the lower 64-tiles only.
+__global__ __launch_bounds__(256) void sum_slices_kernel(const double* __restrict__ S, int r,
+                                                         int slices, int problems,
+                                                         double* __restrict__ A) {
+  const size_t rr = (size_t)r * r;
+  const size_t total = rr * problems;
+  for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < total; x += (size_t)gridDim.x * 256) {
+    const size_t p = x / rr, e = x % rr;
+    const int i = (int)(e / r), j = (int)(e % r);
+    if (j / 64 > i / 64) continue;
+    double s = 0.0;
+    for (int k = 0; k < slices; ++k) s += S[(p * slices + k) * rr + e];
+    A[x] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Blocked Cholesky, panel p (columns 64p .. 64p+nb-1, nb = min(64, r-64p)).
+// One work group of 1024 threads per problem.  Thread t holds column t%64
+// of rows t/64 + 16u (u = 0..3) of the diagonal block in registers.
+// Right-looking steps k = 0..nb-1: the owner of (k, k) takes the square root
+// of the pivot; column k below it is divided by the pivot and published in
+// LDS; the rest of the lower triangle takes the rank-one update.  A pivot
+// that is not positive (rank-deficient samples) is replaced by 1 and counted
+// in *info.  Then D = L11^-1 (lower) by the same sweep on the identity:
+// row k is divided by L_kk and published, the rows below subtract L_ik
+// times it.  Writes L11 into L (upper part zero) and D into Dinv[p].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void chol_panel_kernel(const double* __restrict__ A,
+                                                          double* __restrict__ L,
+                                                          double* __restrict__ Dinv, int r, int p,
+                                                          int* __restrict__ info) {
+  __shared__ double sCol[2][64];
+  __shared__ double sPiv[2];
+  __shared__ double sL[64][65];
+  const int prob = blockIdx.x;
+  const int nbk = ceil_div(r, 64);
+  const double* Ap = A + (size_t)prob * r * r;
+  double* Lp = L + (size_t)prob * r * r;
+  double* Dp = Dinv + ((size_t)prob * nbk + p) * 64 * 64;
+  const int j0 = 64 * p, nb = min(64, r - j0);
+  const int tid = threadIdx.x, j = tid & 63, i_base = tid >> 6;
+  double a[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = i_base + 16 * u;
+    a[u] = (i < nb && j <= i) ? Ap[(size_t)(j0 + i) * r + j0 + j] : 0.0;
+  }
+  for (int k = 0; k < nb; ++k) {
+    const int kb = k & 1;
+    // owner of (k, k): j == k, i_base == k % 16, u == k / 16
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (j == k && i_base + 16 * u == k) {
+        double dk = a[u];
+        if (!(dk > 0.0)) {
+          if (info) atomicAdd(info, 1);
+          dk = 1.0;
+        }
+        dk = sqrt(dk);
+        a[u] = dk;
+        sPiv[kb] = dk;
+      }
+    }
+    __syncthreads();
+    const double piv = sPiv[kb];
+    if (j == k) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i_base + 16 * u;
+        if (i > k && i < nb) {
+          a[u] /= piv;
+          sCol[kb][i] = a[u];
+        }
+      }
+    }
+    __syncthreads();
+    if (j > k) {
+      const double lj = sCol[kb][j];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i_base + 16 * u;
+        if (i >= j && i < nb) a[u] -= sCol[kb][i] * lj;
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = i_base + 16 * u;
+    sL[i][j] = (i < nb && j <= i) ? a[u] : 0.0;
+    if (i < nb && j < nb) Lp[(size_t)(j0 + i) * r + j0 + j] = (j <= i) ? a[u] : 0.0;
+  }
+  __syncthreads();
+  // D = L11^-1: x starts as the identity (rows past nb stay zero)
+  double x[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = i_base + 16 * u;
+    x[u] = (i == j && i < nb) ? 1.0 : 0.0;
+  }
+  for (int k = 0; k < nb; ++k) {
+    const int kb = k & 1;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i_base + 16 * u == k && j <= k) {  // row k: divide by L_kk, publish
+        x[u] /= sL[k][k];
+        sCol[kb][j] = x[u];
+      }
+    }
+    __syncthreads();
+    if (j <= k) {
+      const double xk = sCol[kb][j];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i_base + 16 * u;
+        if (i > k && i < nb) x[u] -= sL[i][k] * xk;
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = i_base + 16 * u;
+    Dp[i * 64 + j] = (i < nb && j <= i) ? x[u] : 0.0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// After panel p: for every lower tile (I, J), p < J <= I < ceil(r/64), with
+// P_X = A[X-rows, panel p] D_p^T (the panel rows of L):
+//     A[I-rows, J-cols] -= P_I P_J^T,   and, for I == J, L[I-rows, panel p] = P_I.
+// grid (tiles, problems), 256 threads, each 4x4 of the 64x64 products.  The
+// panel columns of A are only read, each tile of A is owned by one work
+// group, and L[I, p] is written by the diagonal tile of row I alone.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void chol_update_kernel(double* __restrict__ A,
+                                                          double* __restrict__ L,
+                                                          const double* __restrict__ Dinv, int r,
+                                                          int p) {
+  __shared__ double sD[64][65];
+  __shared__ double sPI[64][65];
+  __shared__ double sPJ[64][65];
+  const int prob = blockIdx.y;
+  const int nbk = ceil_div(r, 64);
+  int It, Jt;
+  tri_index(blockIdx.x, It, Jt);
+  const int I = p + 1 + It, J = p + 1 + Jt;
+  double* Ap = A + (size_t)prob * r * r;
+  double* Lp = L + (size_t)prob * r * r;
+  const double* Dp = Dinv + ((size_t)prob * nbk + p) * 64 * 64;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int pc = 64 * p, ri = 64 * I, rj = 64 * J;
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int row = e >> 6, col = e & 63;
+    sD[row][col] = Dp[e];
+    sPI[row][col] = (ri + row < r) ? Ap[(size_t)(ri + row) * r + pc + col] : 0.0;
+    sPJ[row][col] = (rj + row < r) ? Ap[(size_t)(rj + row) * r + pc + col] : 0.0;
+  }
+  __syncthreads();
+  // P = A_panel D^T for both row blocks: P[i][c] = sum_m A[i][m] D[c][m]
+  double pi[4][4], pj[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) pi[a][b] = pj[a][b] = 0.0;
+  for (int m = 0; m < 64; ++m) {
+    double dc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) dc[b] = sD[tx * 4 + b][m];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const double ai = sPI[ty * 4 + a][m], aj = sPJ[ty * 4 + a][m];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        pi[a][b] = __builtin_fma(ai, dc[b], pi[a][b]);
+        pj[a][b] = __builtin_fma(aj, dc[b], pj[a][b]);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      sPI[ty * 4 + a][tx * 4 + b] = pi[a][b];
+      sPJ[ty * 4 + a][tx * 4 + b] = pj[a][b];
+    }
+  __syncthreads();
+  if (I == J) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int row = ri + ty * 4 + a;
+        if (row < r) Lp[(size_t)row * r + pc + tx * 4 + b] = pi[a][b];
+      }
+  }
+  double c[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) c[a][b] = 0.0;
+  for (int m = 0; m < 64; ++m) {
+    double bj[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) bj[b] = sPJ[tx * 4 + b][m];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const double ai = sPI[ty * 4 + a][m];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) c[a][b] = __builtin_fma(ai, bj[b], c[a][b]);
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int row = ri + ty * 4 + a, col = rj + tx * 4 + b;
+      if (row < r && col < r) Ap[(size_t)row * r + col] -= c[a][b];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Q_p = Y_p L_p^-T (n x r, fp32), row by row: for column block J
+//     R = Y[:, J] - Q[:, <J] L[J, <J]^T,   Q[:, J] = R D_J^T.
+// grid (ceil(n/16), problems), 256 threads; the work group's 16 rows of Q
+// stay in LDS; L is read in fp64 and used in fp32 (the second Cholesky QR
+// round restores orthogonality to fp32 rounding).
+// ---------------------------------------------------------------------------
+constexpr int kTrsmRows = 16;
+constexpr int kFitMaxRank = 512;
+
+__global__ __launch_bounds__(256) void trsm_kernel(const float* __restrict__ Y, size_t sy,
+                                                   const double* __restrict__ L,
+                                                   const double* __restrict__ Dinv, int n, int r,
+                                                   float* __restrict__ Q) {
+  __shared__ __attribute__((aligned(16))) float sQ[kTrsmRows][kFitMaxRank + 4];
+  __shared__ __attribute__((aligned(16))) float sLc[32][64 + 4];  // [m][c] = L[c0+c][m0+m]
+  __shared__ __attribute__((aligned(16))) float sDt[64][64 + 4];  // [m][c] = D[c][m]
+  __shared__ float sR[kTrsmRows][64 + 1];
+  const int prob = blockIdx.y;
+  const int nbk = ceil_div(r, 64);
+  const float* Yp = Y + (size_t)prob * sy;
+  float* Qp = Q + (size_t)prob * sy;
+  const double* Lp = L + (size_t)prob * r * r;
+  const int row0 = blockIdx.x * kTrsmRows;
+  const int tid = threadIdx.x, rr = tid >> 4, cq = (tid & 15) * 4;
+  const int row = row0 + rr;
+  const bool rok = row < n;
+  for (int J = 0; J < nbk; ++J) {
+    const int c0 = 64 * J;
+    const double* Dp = Dinv + ((size_t)prob * nbk + J) * 64 * 64;
+    for (int e = tid; e < 64 * 64; e += 256) sDt[e & 63][e >> 6] = (float)Dp[e];
+    float acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int c = c0 + cq + b;
+      acc[b] = (rok && c < r) ? Yp[(size_t)row * r + c] : 0.f;
+    }
+    for (int m0 = 0; m0 < c0; m0 += 32) {
+      __syncthreads();
+      for (int e = tid; e < 64 * 32; e += 256) {
+        const int c = e >> 5, m = e & 31;
+        sLc[m][c] = (c0 + c < r) ? (float)Lp[(size_t)(c0 + c) * r + m0 + m] : 0.f;
+      }
+      __syncthreads();
+#pragma unroll 8
+      for (int m = 0; m < 32; ++m) {
+        const float qv = sQ[rr][m0 + m];
+        const float4v lv = *(const float4v*)&sLc[m][cq];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[b] = __builtin_fmaf(-qv, lv[b], acc[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) sR[rr][cq + b] = acc[b];
+    __syncthreads();
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < 64; ++m) {
+      const float rv = sR[rr][m];
+      const float4v dv = *(const float4v*)&sDt[m][cq];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) o[b] = __builtin_fmaf(rv, dv[b], o[b]);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int c = c0 + cq + b;
+      if (c < r) {
+        sQ[rr][c] = o[b];
+        if (rok) Qp[(size_t)row * r + c] = o[b];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void to_f16_kernel(const float* __restrict__ src, size_t n,
+                                                     half_t* __restrict__ dst) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    dst[i] = (half_t)src[i];
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+static int fit_tile(int d) { return d % 128 == 0 ? 128 : 64; }
+static int syrk_slices(int n) { return (n + 511) / 512; }
+static size_t align256_(size_t x) { return (x + 255) & ~(size_t)255; }
+
+FitWorkspace fit_workspace_layout(const ShapeKey& s) {
+  const size_t nv = (size_t)s.H * s.d, nk = s.d;
+  const size_t rk = s.rk, rv = s.rv;
+  const size_t nbk_k = (rk + 63) / 64, nbk_v = (rv + 63) / 64;
+  FitWorkspace w;
+  size_t off = 0;
+  w.gv_off = off;
+  off = align256_(off + nv * nv * 4);
+  w.gk_off = off;
+  off = align256_(off + (size_t)s.H * nk * nk * 4);
+  w.qv_off[0] = off;
+  off = align256_(off + nv * rv * 4);
+  w.qv_off[1] = off;
+  off = align256_(off + nv * rv * 4);
+  w.qk_off[0] = off;
+  off = align256_(off + (size_t)s.H * nk * rk * 4);
+  w.qk_off[1] = off;
+  off = align256_(off + (size_t)s.H * nk * rk * 4);
+  w.sv_off = off;  // slices of S_v (unused when one slice)
+  off = align256_(off + (size_t)syrk_slices((int)nv) * rv * rv * 8);
+  w.sk_off = off;
+  off = align256_(off + (size_t)s.H * syrk_slices((int)nk) * rk * rk * 8);
+  w.av_off = off;
+  off = align256_(off + rv * rv * 8);
+  w.ak_off = off;
+  off = align256_(off + (size_t)s.H * rk * rk * 8);
+  w.lv_off = off;
+  off = align256_(off + rv * rv * 8);
+  w.lk_off = off;
+  off = align256_(off + (size_t)s.H * rk * rk * 8);
+  w.dv_off = off;
+  off = align256_(off + nbk_v * 64 * 64 * 8);
+  w.dk_off = off;
+  off = align256_(off + (size_t)s.H * nbk_k * 64 * 64 * 8);
+  w.total = off;
+  return w;
+}
+
+namespace {
+
+struct OrthProblem {
+  int P, n, r;
+  double *S, *A, *L, *D;
+};
+
+// Q = Y L^-T with S = Y^T Y = L L^T, for P problems of n x r (Y, Q at stride n*r).
+hipError_t orth(const OrthProblem& o, const float* Y, float* Q, int* info, hipStream_t st) {
+  const int slices = syrk_slices(o.n), rows = ceil_div(o.n, slices);
+  const int nbk = ceil_div(o.r, 64);
+  const int tiles = nbk * (nbk + 1) / 2;
+  const size_t sy = (size_t)o.n * o.r;
+  double* dst = slices > 1 ? o.S : o.A;
+  hipLaunchKernelGGL(syrk_f64_kernel, dim3(tiles, o.P * slices), dim3(256), 0, st, Y, sy, o.n,
+                     o.r, slices, rows, dst);
+  if (slices > 1) {
+    const size_t total = (size_t)o.P * o.r * o.r;
+    const int blocks = (int)std::min<size_t>((total + 255) / 256, 2048);
+    hipLaunchKernelGGL(sum_slices_kernel, dim3(blocks), dim3(256), 0, st, o.S, o.r, slices, o.P,
+                       o.A);
+  }
+  for (int p = 0; p < nbk; ++p) {
+    hipLaunchKernelGGL(chol_panel_kernel, dim3(o.P), dim3(1024), 0, st, o.A, o.L, o.D, o.r, p,
+                       info);
+    const int m = nbk - p - 1;
+    if (m > 0)
+      hipLaunchKernelGGL(chol_update_kernel, dim3(m * (m + 1) / 2, o.P), dim3(256), 0, st, o.A,
+                         o.L, o.D, o.r, p);
+  }
+  hipLaunchKernelGGL(trsm_kernel, dim3(ceil_div(o.n, kTrsmRows), o.P), dim3(256), 0, st, Y, sy,
+                     o.L, o.D, o.n, o.r, Q);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fit(const ShapeKey& s, const void* k, const void* v, int n_samples,
+                      const float* u0, const float* w0, int iters, void* U, void* W,
+                      void* workspace, int* info, hipStream_t st) {
+  const FitWorkspace ws = fit_workspace_layout(s);
+  char* wb = (char*)workspace;
+  float* Gv = (float*)(wb + ws.gv_off);
+  float* Gk = (float*)(wb + ws.gk_off);
+  const int tm = fit_tile(s.d);
+  const int nbv = s.H * s.d / tm, nbk = s.d / tm;
+  const int tiles_v = nbv * (nbv + 1) / 2, tiles_k = nbk * (nbk + 1) / 2;
+  const int total = tiles_v + s.H * tiles_k;
+  const dim3 ggrid(8 * ceil_div(total, 8));
+  if (tm == 128)
+    hipLaunchKernelGGL(gram_kernel<128>, ggrid, dim3(256), 0, st, (const half_t*)k,
+                       (const half_t*)v, n_samples, s.H, s.d, Gk, Gv, tiles_v, tiles_k, info);
+  else
+    hipLaunchKernelGGL(gram_kernel<64>, ggrid, dim3(256), 0, st, (const half_t*)k,
+                       (const half_t*)v, n_samples, s.H, s.d, Gk, Gv, tiles_v, tiles_k, info);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  struct Side {
+    int P, n, r;
+    const float* G;
+    const float* q0;
+    float* buf[2];
+    OrthProblem o;
+    half_t* out;
+  };
+  Side sides[2] = {
+      {1, s.H * s.d, s.rv, Gv, w0, {(float*)(wb + ws.qv_off[0]), (float*)(wb + ws.qv_off[1])},
+       {1, s.H * s.d, s.rv, (double*)(wb + ws.sv_off), (double*)(wb + ws.av_off),
+        (double*)(wb + ws.lv_off), (double*)(wb + ws.dv_off)},
+       (half_t*)W},
+      {s.H, s.d, s.rk, Gk, u0, {(float*)(wb + ws.qk_off[0]), (float*)(wb + ws.qk_off[1])},
+       {s.H, s.d, s.rk, (double*)(wb + ws.sk_off), (double*)(wb + ws.ak_off),
+        (double*)(wb + ws.lk_off), (double*)(wb + ws.dk_off)},
+       (half_t*)U}};
+  for (Side& sd : sides) {
+    const size_t sg = (size_t)sd.n * sd.n, sq = (size_t)sd.n * sd.r;
+    const dim3 mgrid(ceil_div(sd.r, 64), sd.n / 64, sd.P);
+    const float* q = sd.q0;
+    // buf[1] takes Y = G Q, buf[0] the orthonormalised Q
+    for (int it = 0; it < iters; ++it) {
+      hipLaunchKernelGGL(symm_f32_kernel, mgrid, dim3(256), 0, st, sd.G, sg, sd.n, tm, q, sq,
+                         sd.buf[1], sq, sd.r);
+      e = orth(sd.o, sd.buf[1], sd.buf[0], info, st);
+      if (e != hipSuccess) return e;
+      q = sd.buf[0];
+    }
+    e = orth(sd.o, sd.buf[0], sd.buf[1], info, st);  // second round of the last QR
+    if (e != hipSuccess) return e;
+    const size_t cnt = (size_t)sd.P * sq;
+    const int blocks = (int)std::min<size_t>((cnt + 255) / 256, 4096);
+    hipLaunchKernelGGL(to_f16_kernel, dim3(blocks), dim3(256), 0, st, sd.buf[1], cnt, sd.out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace starkv

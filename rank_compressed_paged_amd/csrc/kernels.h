@@ -43,6 +43,16 @@ struct PrefillWorkspace {
   size_t qt_off, z_off, total;
 };
 
+// Byte offsets of the workspace of the bases fit: the Gram matrices (fp32),
+// two n x r fp32 buffers per side (Y = G Q and the orthonormalised Q), the
+// fp64 row-slice partials of S = Y^T Y, the Schur-complement matrix A that
+// the Cholesky factorisation updates in place, its factor L and the inverses
+// of L's 64x64 diagonal blocks.
+struct FitWorkspace {
+  size_t gv_off, gk_off, qv_off[2], qk_off[2], sv_off, sk_off, av_off, ak_off, lv_off, lk_off,
+      dv_off, dk_off, total;
+};
+
 bool shape_supported(const ShapeKey& s);
 DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int block_size);
 DecodeWorkspace decode_workspace_layout(const ShapeKey& s, int batch, const DecodePlan& p);
@@ -103,6 +113,14 @@ hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStre
 hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const void* U,
                          const void* W, const int64_t* slots, int n_tokens, int num_blocks,
                          void* k_cache, void* v_cache, hipStream_t st);
+
+FitWorkspace fit_workspace_layout(const ShapeKey& s);
+
+// Top-r_k eigenspaces of each head's key second-moment matrix and the top-r_v
+// eigenspace of the joint value one, by subspace iteration from u0 / w0.
+hipError_t launch_fit(const ShapeKey& s, const void* k, const void* v, int n_samples,
+                      const float* u0, const float* w0, int iters, void* U, void* W,
+                      void* workspace, int* info, hipStream_t st);
 
 hipError_t launch_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl, int total_q,
                           int max_query_len, const void* k_cache, const void* v_cache,

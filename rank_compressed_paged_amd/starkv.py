@@ -33,7 +33,7 @@ EXPORTED = [
     "starkv_decode_workspace_size", "starkv_decode_attn", "starkv_prefill_workspace_size",
     "starkv_prefill_attn", "starkv_set_timing_events", "starkv_decode_plan",
     "starkv_util_stream_read", "starkv_util_event_create", "starkv_util_event_destroy",
-    "starkv_util_event_elapsed_ms",
+    "starkv_util_event_elapsed_ms", "starkv_fit_workspace_size", "starkv_fit_bases",
 ]
 
 
@@ -84,6 +84,11 @@ _lib.starkv_util_event_destroy.restype = _i32
 _lib.starkv_util_event_destroy.argtypes = [_vp]
 _lib.starkv_util_event_elapsed_ms.restype = _i32
 _lib.starkv_util_event_elapsed_ms.argtypes = [_vp, _vp, ctypes.POINTER(ctypes.c_float)]
+_lib.starkv_fit_workspace_size.restype = _i32
+_lib.starkv_fit_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(_sz)]
+_lib.starkv_fit_bases.restype = _i32
+_lib.starkv_fit_bases.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp,
+                                  _vp, _sz, _vp, _vp]
 _lib.starkv_set_timing_events.restype = _i32
 _lib.starkv_set_timing_events.argtypes = [_vp, _vp, _i32]
 
@@ -227,6 +232,39 @@ def prefill_attn(q, query_start_loc, max_query_len, k_cache, v_cache, U, W, bloc
         _dev(workspace, torch.uint8, "workspace"), int(workspace.numel()), _stream(stream))
     _check(st, "starkv_prefill_attn")
     return out
+
+
+def fit_workspace_size(dims):
+    out = _sz(0)
+    _check(_lib.starkv_fit_workspace_size(ctypes.byref(dims), ctypes.byref(out)),
+           "starkv_fit_workspace_size")
+    return int(out.value)
+
+
+def fit_bases(k, v, r_k, r_v, u0, w0, iters, U=None, W=None, workspace=None, info=None,
+              stream=None):
+    """Bases U [H, d, r_k], W [H*d, r_v] (fp16) from samples k, v [N, H, d]
+    (fp16), by subspace iteration from u0, w0 (fp32, same shapes).  `info`
+    (int32 [1], optional) receives the count of non-positive pivots."""
+    N, H, d = k.shape
+    dims = make_dims(H, d, r_k, r_v, 1)
+    if U is None:
+        U = torch.empty((H, d, r_k), dtype=torch.float16, device=k.device)
+    if W is None:
+        W = torch.empty((H * d, r_v), dtype=torch.float16, device=k.device)
+    need = fit_workspace_size(dims)
+    if workspace is None:
+        workspace = alloc_workspace(need, k.device)
+    st = _lib.starkv_fit_bases(
+        ctypes.byref(dims), _dev(k, torch.float16, "k", (N, H, d)),
+        _dev(v, torch.float16, "v", (N, H, d)), int(N),
+        _dev(u0, torch.float32, "u0", (H, d, r_k)), _dev(w0, torch.float32, "w0", (H * d, r_v)),
+        int(iters), _dev(U, torch.float16, "U", (H, d, r_k)),
+        _dev(W, torch.float16, "W", (H * d, r_v)), _dev(workspace, torch.uint8, "workspace"),
+        int(workspace.numel()), None if info is None else _dev(info, torch.int32, "info", (1,)),
+        _stream(stream))
+    _check(st, "starkv_fit_bases")
+    return U, W
 
 
 def stream_read(buf, sink, stream=None):

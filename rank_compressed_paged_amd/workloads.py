@@ -56,6 +56,7 @@ CONFIGS = {
     "decode_b64": dict(kind="decode", shape=MAIN, B=64, seq=("uniform", 4096, 8192), seed=2),
     "long_b20": dict(kind="decode", shape=MAIN, B=20, seq=("fixed", 32768), seed=3),
     "prefill_b16": dict(kind="prefill", shape=MAIN, B=16, cached=4096, chunk=256, seed=4),
+    "fit_n16384": dict(kind="fit", shape=MAIN, N=16384, seed=5),
 }
 
 
@@ -239,10 +240,66 @@ def make_prefill_case(shape: Shape, cached_lens, chunk_lens, seed=0,
                        1.0 / np.sqrt(shape.d), seed, name)
 
 
+@dataclass
+class FitCase:
+    """K/V samples for fitting the bases, plus the starting matrices."""
+    shape: Shape
+    k: np.ndarray      # [N, H, d] fp16
+    v: np.ndarray      # [N, H, d] fp16
+    u0: np.ndarray     # [H, d, r_k] fp32
+    w0: np.ndarray     # [H*d, r_v] fp32
+    seed: int
+    name: str = ""
+
+
+def make_fit_case(shape: Shape, N, seed=0, noise=0.05, name=""):
+    """Samples with a planted low-rank structure plus isotropic noise.
+
+    Draw order (numpy PCG64, ``default_rng(seed)``):
+      1. per head h: an orthonormal d x r_k frame A_h (reduced QR of N(0,1),
+         sign-fixed, fp64); then the value frame B, (H*d) x r_v, the same way;
+      2. key coefficients z_k ~ N(0,1) [N, H, r_k], key noise e_k ~ N(0,1)
+         [N, H, d]; value coefficients z_v ~ N(0,1) [N, r_v], value noise
+         e_v ~ N(0,1) [N, H*d];
+      3. u0 ~ N(0,1) [H, d, r_k], w0 ~ N(0,1) [H*d, r_v] (fp32).
+    k[n, h] = A_h (s_k * z_k[n, h]) + noise * e_k[n, h] and
+    vec(v[n]) = B (s_v * z_v[n]) + noise * e_v[n], with per-direction scales
+    s falling linearly from 3 to 1, cast to fp16.  The r-th eigenvalue of the
+    second moment then sits near N (1 + noise^2) and the (r+1)-th near
+    N noise^2, a wide gap.
+    """
+    rng = np.random.default_rng(seed)
+
+    def frame(rows, cols):
+        a = rng.standard_normal((rows, cols))
+        qm, rm = np.linalg.qr(a)
+        sgn = np.sign(np.diag(rm))
+        sgn[sgn == 0] = 1.0
+        return qm * sgn[None, :]
+
+    H, d, rk, rv = shape.H, shape.d, shape.r_k, shape.r_v
+    A = np.stack([frame(d, rk) for _ in range(H)])          # [H, d, rk]
+    B = frame(H * d, rv)                                     # [H*d, rv]
+    zk = rng.standard_normal((N, H, rk))
+    ek = rng.standard_normal((N, H, d))
+    zv = rng.standard_normal((N, rv))
+    ev = rng.standard_normal((N, H * d))
+    sk = np.linspace(3.0, 1.0, rk)
+    sv = np.linspace(3.0, 1.0, rv)
+    k = np.einsum("hdr,nhr->nhd", A, zk * sk) + noise * ek
+    v = (zv * sv) @ B.T + noise * ev
+    u0 = rng.standard_normal((H, d, rk), dtype=np.float32)
+    w0 = rng.standard_normal((H * d, rv), dtype=np.float32)
+    return FitCase(shape, k.astype(np.float16), v.reshape(N, H, d).astype(np.float16),
+                   u0, w0, seed, name)
+
+
 def make_config(name: str, keep_logical=False):
     """Build a named workload with its own seed."""
     cfg = CONFIGS[name]
     shape = cfg["shape"]
+    if cfg["kind"] == "fit":
+        return make_fit_case(shape, cfg["N"], seed=cfg["seed"], name=name)
     if cfg["kind"] == "decode":
         return make_decode_case(shape, B=cfg["B"], seq=cfg["seq"], seed=cfg["seed"],
                                 keep_logical=keep_logical, name=name)
