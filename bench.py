@@ -14,8 +14,10 @@ events that take its dispatch's own begin and end timestamps.  `value` is
 latent-KV bytes per step / mean step time.  Beside the headline the line
 carries the step with its append, a streaming-read ceiling, the chunked
 prefill workload (16 requests x 4096 cached + 256 new tokens: attention and
-append, as TFLOP/s against the fp16 MFMA peak), and the CPU leg, which times
-the fp64 oracle on a bounded sample of the decode workload on the host cores.
+append, as TFLOP/s against the fp16 MFMA peak), the bases fit from 16384 K/V
+samples (its Gram kernel against the same peak), and the CPU leg, which
+times the fp64 oracle on a bounded sample of the decode workload on the host
+cores.
 
 Other modes:
     --profile-run             a few steps plus a 256 MiB copy, for rocprofv3
@@ -95,10 +97,13 @@ def parse_args(argv=None):
                     choices=["decode_b16", "decode_b64", "long_b20", "tiny"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill_b16 leg")
+    ap.add_argument("--no-fit", action="store_true", help="skip the bases-fit leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU sample budget")
     ap.add_argument("--flush", choices=["read", "write"], default="read",
                     help="evict the Infinity Cache by reading (default) or writing 512 MiB")
     ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--profile-fit", action="store_true",
+                    help="a few bases fits (fit_n16384, 8 iterations), for rocprofv3")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"))
     return ap.parse_args(argv)
 
@@ -256,6 +261,52 @@ def prefill_leg(flush_fn, steps):
     }
 
 
+def fit_leg(steps):
+    """The bases fit at 16384 K/V samples of the main shape, 8 iterations:
+    the whole call, and its Gram-matrix kernel (algorithmic TFLOP/s of the
+    distinct second-moment entries against the fp16 MFMA peak)."""
+    import numpy as np
+    import torch
+    from rank_compressed_paged_amd import metrics
+    from rank_compressed_paged_amd import starkv as sk
+    from rank_compressed_paged_amd import workloads as wl
+    iters = 8
+    fc = wl.make_config("fit_n16384")
+    sh = fc.shape
+    N = fc.k.shape[0]
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    k, v, u0, w0 = dev(fc.k), dev(fc.v), dev(fc.u0), dev(fc.w0)
+    U = torch.empty((sh.H, sh.d, sh.r_k), dtype=torch.float16, device="cuda")
+    W = torch.empty((sh.H * sh.d, sh.r_v), dtype=torch.float16, device="cuda")
+    ws = sk.alloc_workspace(sk.fit_workspace_size(sk.make_dims(sh.H, sh.d, sh.r_k, sh.r_v, 1)),
+                            "cuda")
+
+    def fit():
+        sk.fit_bases(k, v, sh.r_k, sh.r_v, u0, w0, iters, U=U, W=W, workspace=ws)
+
+    fit()
+    torch.cuda.synchronize()
+    n = max(min(steps // 5, 10), 3)
+    call_ms, _, _ = timed(fit, n)
+    _, gram_ms, _ = timed(fit, n, None, sk.TIME_FIT_GRAM)
+    m = statistics.fmean
+    gf = metrics.gram_flops(N, sh.H, sh.d)
+    itf = metrics.fit_iteration_flops(sh.H, sh.d, sh.r_k, sh.r_v)
+    gram_tf = gf / (m(gram_ms) * 1e-3) / 1e12
+    sample_bytes = 2 * N * sh.H * sh.d * 2
+    return {
+        "workload": "fit_n16384", "samples": N, "iters": iters, "steps": n,
+        "call_ms": round(m(call_ms), 4),
+        "gram_kernel_ms": round(m(gram_ms), 4),
+        "gram_kernel_tflops": round(gram_tf, 1),
+        "gram_kernel_mfma_frac": round(gram_tf / MFMA_F16_PEAK_TFLOPS, 4),
+        "gram_algorithmic_gflop": round(gf / 1e9, 1),
+        "gram_sample_bytes": int(sample_bytes),
+        "after_gram_ms": round(m(call_ms) - m(gram_ms), 4),
+        "iteration_algorithmic_gflop": round(itf / 1e9, 2),
+    }
+
+
 def run_bench(args):
     import numpy as np
     import torch
@@ -380,6 +431,8 @@ def run_bench(args):
     if not args.no_prefill:
         del ceil_sink
         res["prefill"] = prefill_leg(do_flush, args.steps)
+    if not args.no_fit:
+        res["fit"] = fit_leg(args.steps)
     res["device"] = device_info()
     if case.name == "decode_b16":
         # the pages' own decode-step figures for this shape (NVIDIA L4, other
@@ -392,6 +445,24 @@ def run_bench(args):
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
+
+
+def profile_fit(args):
+    """A short run for rocprofv3: bases fits of the fit_n16384 workload."""
+    import numpy as np
+    import torch
+    from rank_compressed_paged_amd import starkv as sk
+    from rank_compressed_paged_amd import workloads as wl
+    fc = wl.make_config("fit_n16384")
+    sh = fc.shape
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    k, v, u0, w0 = dev(fc.k), dev(fc.v), dev(fc.u0), dev(fc.w0)
+    ws = sk.alloc_workspace(sk.fit_workspace_size(sk.make_dims(sh.H, sh.d, sh.r_k, sh.r_v, 1)),
+                            "cuda")
+    for _ in range(max(args.steps, 1)):
+        sk.fit_bases(k, v, sh.r_k, sh.r_v, u0, w0, 8, workspace=ws)
+    torch.cuda.synchronize()
+    print(f"profile-fit done: {args.steps} fits of fit_n16384", flush=True)
 
 
 def profile_run(args):
@@ -488,6 +559,9 @@ def main():
         return 2
     if args.profile_run:
         profile_run(args)
+        return 0
+    if args.profile_fit:
+        profile_fit(args)
         return 0
     run_bench(args)
     return 0

@@ -169,10 +169,11 @@ starkv_status starkv_prefill_attn(const starkv_dims* dims, const void* q,
  * `start` to the dispatch just before it in the same call (the q projection),
  * both through hipExtLaunchKernelGGL, so the elapsed time runs from the end
  * of that predecessor to the end of the selected kernel with nothing
- * enqueued between them.  Append has no predecessor: `start` is recorded on
- * the stream just before its launch.
+ * enqueued between them.  Append and the Gram kernel have no predecessor:
+ * `start` is recorded on the stream just before their launch.
  *   which = 0 none (clears), 1 decode split-K attention, 2 prefill attention,
- *   3 append.  Events are owned by the caller and must outlive the calls.
+ *   3 append, 4 the Gram-matrix kernel of the bases fit (no predecessor
+ *   either).  Events are owned by the caller and must outlive the calls.
  * Process-wide setting; not for concurrent use from several threads.
  */
 starkv_status starkv_set_timing_events(void* start, void* stop, int32_t which);

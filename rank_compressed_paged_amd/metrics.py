@@ -54,3 +54,21 @@ def prefill_flops(cached_lens, chunk_lens, H, d, r_k, r_v):
 
 def append_flops(n_tokens, H, d, r_k, r_v):
     return 2 * n_tokens * (H * d * r_k + H * d * r_v)
+
+
+def gram_flops(n_samples, H, d):
+    """The bases fit's second moments: the n(n+1)/2 distinct entries of
+    V^T V (n = H*d) and of each K_h^T K_h (n = d), one MAC per sample each,
+    2 flops per MAC."""
+    nv = H * d
+    return int(n_samples) * (nv * (nv + 1) + H * d * (d + 1))
+
+
+def fit_iteration_flops(H, d, r_k, r_v):
+    """One subspace-iteration step of the bases fit, 2 flops per MAC: Y = G Q
+    (n^2 r), S = Y^T Y (n r(r+1)/2 distinct), Q = Y L^-T (n r(r+1)/2), for the
+    value problem (n = H*d) and the H key problems (n = d); the r^3/3 of the
+    Cholesky factorisation is left out."""
+    def one(n, r):
+        return 2 * (n * n * r + n * r * (r + 1))
+    return one(H * d, r_v) + H * one(d, r_k)

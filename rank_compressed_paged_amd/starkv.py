@@ -92,7 +92,7 @@ _lib.starkv_fit_bases.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _i32, _vp, _vp
 _lib.starkv_set_timing_events.restype = _i32
 _lib.starkv_set_timing_events.argtypes = [_vp, _vp, _i32]
 
-TIME_NONE, TIME_DECODE_SPLIT, TIME_PREFILL_ATTN, TIME_APPEND = 0, 1, 2, 3
+TIME_NONE, TIME_DECODE_SPLIT, TIME_PREFILL_ATTN, TIME_APPEND, TIME_FIT_GRAM = 0, 1, 2, 3, 4
 
 
 def lib():

@@ -110,6 +110,7 @@ def test_timing_event_validation():
     assert f(None, None, 0) == 0
     assert f(None, None, 1) == 1
     assert f(FAKE, FAKE, 9) == 7
+    assert f(FAKE, FAKE, 5) == 7
 
 
 def test_decode_plan_properties():
