@@ -13,6 +13,10 @@ capacity" table):
 * key latents    c_k[t, h] = U_h^T k[t, h],   U_h in R^{d x r_k}, one per head
 * value latents  c_v[t]    = W^T vec(v[t]),   W in R^{(H*d) x r_v}, shared
                  by all heads; vec() flattens [H, d] head-major (row h*d + i)
+* grouped-query layouts: H query heads share Hkv key/value heads, query head
+  h reading key/value head h // (H / Hkv) (consecutive groups); U, the key
+  latents and W's rows are per key/value head.  Hkv = H is multi-head
+  attention.
 * attention reads the latents through block tables.  The oracle takes the
   plain definition: rebuild K^[t,h] = U_h c_k[t,h] and V^[t] = W c_v[t]
   explicitly, then run textbook two-pass softmax attention in fp64 with the
@@ -21,7 +25,7 @@ capacity" table):
   rounding order, for any U and W.
 
 Readings taken where the pages are silent (each listed in the design notes):
-* layouts: k_cache [NB, H, bs, r_k], v_cache [NB, r_v, bs], fp16;
+* layouts: k_cache [NB, Hkv, bs, r_k], v_cache [NB, r_v, bs], fp16;
 * the write kernel's "normalization" (README, "Kernel profiling breakdown")
   is read as none: the stored latent is exactly fp16(U_h^T k), fp16(W^T v);
 * a decode query attends to all seq_lens[b] cached tokens (append first);
@@ -61,7 +65,8 @@ def gather_sequence_latents(k_cache, v_cache, block_table_row, seq_len):
     """Return the logical-order latents of one sequence.
 
     k_cache [NB, H, bs, r_k], v_cache [NB, r_v, bs]; block_table_row [>= ceil(L/bs)].
-    Returns (ck [L, H, r_k] fp64, cv [L, r_v] fp64).
+    Returns (ck [L, H, r_k] fp64, cv [L, r_v] fp64); H here (and in the
+    rebuild and the append) counts the key/value heads.
     """
     NB, H, bs, r_k = k_cache.shape
     r_v = v_cache.shape[1]
@@ -124,6 +129,14 @@ def append(k, v, U, W, slot_mapping, k_cache, v_cache):
     return kc, vc
 
 
+def _group_size(H, U):
+    """Query heads per key/value head: H over the heads of U."""
+    Hkv = U.shape[0]
+    if H % Hkv:
+        raise ValueError("query heads must be a multiple of key/value heads")
+    return H // Hkv
+
+
 def softmax_rows(s):
     """Textbook two-pass softmax along the last axis (max-subtracted)."""
     m = np.max(s, axis=-1, keepdims=True)
@@ -150,6 +163,7 @@ def decode(q, k_cache, v_cache, U, W, block_tables, seq_lens, scale,
     """
     qf = _f64(q)
     B, H, d = qf.shape
+    G = _group_size(H, U)
     out = np.full((B, H, d), np.nan)
     probs = [None] * B
     rows = range(B) if batch_indices is None else batch_indices
@@ -163,7 +177,8 @@ def decode(q, k_cache, v_cache, U, W, block_tables, seq_lens, scale,
         K, V = reconstruct_sequence(ck, cv, U, W)
         ph = np.empty((H, L))
         for h in range(H):
-            o, p = _attend(qf[b, h][None, :], K[:, h, :], V[:, h, :], scale)
+            g = h // G
+            o, p = _attend(qf[b, h][None, :], K[:, g, :], V[:, g, :], scale)
             out[b, h] = o[0]
             ph[h] = p[0]
         probs[b] = ph
@@ -183,6 +198,7 @@ def prefill(q, query_start_loc, k_cache, v_cache, U, W, block_tables,
     """
     qf = _f64(q)
     T, H, d = qf.shape
+    G = _group_size(H, U)
     out = np.full((T, H, d), np.nan)
     B = len(seq_lens)
     rows = range(B) if request_indices is None else request_indices
@@ -201,7 +217,8 @@ def prefill(q, query_start_loc, k_cache, v_cache, U, W, block_tables,
         qry_pos = P0 + np.arange(C)[:, None]
         visible = key_pos <= qry_pos
         for h in range(H):
-            o, _ = _attend(qf[q0:q1, h], K[:, h, :], V[:, h, :], scale, visible)
+            g = h // G
+            o, _ = _attend(qf[q0:q1, h], K[:, g, :], V[:, g, :], scale, visible)
             out[q0:q1, h] = o
     return out
 

@@ -8,24 +8,28 @@ Workload shapes follow the Proxima README: 32-head MHA with head size 128
 and rank 64 ("Per-decode-step attention"), 16-token KV blocks ("KV-cache
 capacity"), and chunked prefill of N new tokens per request
 ("Per-prefill-chunk attention").  Rank 64 is read as r_k = 64 per head for K
-and a joint r_v = 512 for V.
+and a joint r_v = 512 for V.  Grouped-query shapes (the next step the
+pages' multi-model support points to) keep H query heads and Hkv key/value
+heads: U, the key latents and W's rows are per key/value head.
 
 Draw order for one case (numpy PCG64, ``default_rng(seed)``):
-  1. U_h for h = 0..H-1: reduced QR of N(0,1)^{d x r_k}, column signs fixed so
+  1. U_h for h = 0..Hkv-1: reduced QR of N(0,1)^{d x r_k}, column signs fixed so
      diag(R) > 0, cast to fp16;
-  2. W: the same from N(0,1)^{(H*d) x r_v};
+  2. W: the same from N(0,1)^{(Hkv*d) x r_v};
   3. sequence lengths, when the config draws them (inclusive uniform);
   4. the physical block permutation ``rng.permutation(NB)``, handed out to
      (sequence, logical block) in sequence-major order;
   5. latents in logical (sequence, token) order, per sequence: c_k ~ N(0,1)
-     of shape [L, H, r_k] then c_v ~ N(0,1) of shape [L, r_v], drawn as
+     of shape [L, Hkv, r_k] then c_v ~ N(0,1) of shape [L, r_v], drawn as
      float32 and cast to fp16 (round to nearest even);
-  6. prefill only: new k, then v, then q ~ N(0,1) [sum C, H, d] fp16;
+  6. prefill only: new k, then v ([sum C, Hkv, d]), then q ~ N(0,1)
+     [sum C, H, d] fp16;
      decode: q ~ N(0,1) [B, H, d] fp16.
 Cache slots that hold no token (ragged tails, the spare block) are fp16 NaN
 (0x7E00) so that any read of them shows up in the output.
 
-Cache layouts: k_cache [NB, H, bs, r_k] fp16, v_cache [NB, r_v, bs] fp16.
+Cache layouts: k_cache [NB, Hkv, bs, r_k] fp16, v_cache [NB, r_v, bs] fp16
+(Hkv = H for multi-head attention).
 """
 from __future__ import annotations
 
@@ -39,15 +43,25 @@ FP16_NAN_BITS = 0x7E00
 
 @dataclass(frozen=True)
 class Shape:
-    H: int
+    H: int          # query heads
     d: int
     r_k: int
     r_v: int
     bs: int = 16
+    Hkv: int = 0    # key/value heads (grouped-query attention); 0 means H
+
+    @property
+    def kv(self):
+        """Key/value heads: the heads of U, of the key latents and of W's rows."""
+        return self.Hkv or self.H
 
 
 MAIN = Shape(H=32, d=128, r_k=64, r_v=512, bs=16)
 TINY = Shape(H=4, d=64, r_k=16, r_v=64, bs=16)
+# grouped-query layouts: 8 key/value heads for 32 query heads (groups of 4),
+# and a tiny one with groups of 2
+GQA8 = Shape(H=32, d=128, r_k=64, r_v=512, bs=16, Hkv=8)
+TINY_GQA = Shape(H=4, d=64, r_k=16, r_v=64, bs=16, Hkv=2)
 
 # Named workloads.  "seq" is ("fixed", L) or ("uniform", lo, hi) inclusive.
 CONFIGS = {
@@ -57,6 +71,10 @@ CONFIGS = {
     "long_b20": dict(kind="decode", shape=MAIN, B=20, seq=("fixed", 32768), seed=3),
     "prefill_b16": dict(kind="prefill", shape=MAIN, B=16, cached=4096, chunk=256, seed=4),
     "fit_n16384": dict(kind="fit", shape=MAIN, N=16384, seed=5),
+    "gqa8_b16": dict(kind="decode", shape=GQA8, B=16, seq=("fixed", 2048), seed=6),
+    "gqa8_b64": dict(kind="decode", shape=GQA8, B=64, seq=("uniform", 4096, 8192), seed=7),
+    "gqa8_prefill_b16": dict(kind="prefill", shape=GQA8, B=16, cached=4096, chunk=256, seed=8),
+    "tiny_gqa": dict(kind="decode", shape=TINY_GQA, B=2, seq=("fixed", 256), seed=9),
 }
 
 
@@ -74,8 +92,8 @@ def orthonormal_fp16(rng, rows, cols):
 
 
 def draw_bases(rng, shape: Shape):
-    U = np.stack([orthonormal_fp16(rng, shape.d, shape.r_k) for _ in range(shape.H)])
-    W = orthonormal_fp16(rng, shape.H * shape.d, shape.r_v)
+    U = np.stack([orthonormal_fp16(rng, shape.d, shape.r_k) for _ in range(shape.kv)])
+    W = orthonormal_fp16(rng, shape.kv * shape.d, shape.r_v)
     return U, W
 
 
@@ -85,7 +103,7 @@ class PagedCache:
     shape: Shape
     seq_lens: np.ndarray          # [B] int32, tokens in the cache
     block_tables: np.ndarray      # [B, max_blocks] int32, -1 = unused
-    k_cache: np.ndarray           # [NB, H, bs, r_k] fp16
+    k_cache: np.ndarray           # [NB, Hkv, bs, r_k] fp16
     v_cache: np.ndarray           # [NB, r_v, bs] fp16
     logical_ck: Optional[List[np.ndarray]] = None  # per sequence [L, H, r_k]
     logical_cv: Optional[List[np.ndarray]] = None  # per sequence [L, r_v]
@@ -128,12 +146,12 @@ def fill_cache(rng, shape: Shape, seq_lens, cache_lens=None, spare_blocks=1,
     bs = shape.bs
     nblk = [(int(L) + bs - 1) // bs for L in seq_lens]
     bt, nb = build_block_tables(rng, nblk, spare_blocks, shuffle, extra_cols)
-    kc = _nan_f16((nb, shape.H, bs, shape.r_k))
+    kc = _nan_f16((nb, shape.kv, bs, shape.r_k))
     vc = _nan_f16((nb, shape.r_v, bs))
     lck, lcv = [], []
     for b, L in enumerate(cache_lens):
         L = int(L)
-        ck = rng.standard_normal((L, shape.H, shape.r_k), dtype=np.float32).astype(np.float16)
+        ck = rng.standard_normal((L, shape.kv, shape.r_k), dtype=np.float32).astype(np.float16)
         cv = rng.standard_normal((L, shape.r_v), dtype=np.float32).astype(np.float16)
         if L:
             scatter_tokens(kc, vc, bt[b], 0, ck, cv, bs)
@@ -147,8 +165,8 @@ def fill_cache(rng, shape: Shape, seq_lens, cache_lens=None, spare_blocks=1,
 @dataclass
 class DecodeCase:
     shape: Shape
-    U: np.ndarray          # [H, d, r_k] fp16
-    W: np.ndarray          # [H*d, r_v] fp16
+    U: np.ndarray          # [Hkv, d, r_k] fp16
+    W: np.ndarray          # [Hkv*d, r_v] fp16
     cache: PagedCache
     q: np.ndarray          # [B, H, d] fp16
     scale: float
@@ -167,8 +185,8 @@ class PrefillCase:
     W: np.ndarray
     cache: PagedCache               # caches hold the first cached_lens tokens
     cached_lens: np.ndarray         # [B] tokens already in the cache
-    k_new: np.ndarray               # [T, H, d] fp16, T = sum of chunk lengths
-    v_new: np.ndarray               # [T, H, d] fp16
+    k_new: np.ndarray               # [T, Hkv, d] fp16, T = sum of chunk lengths
+    v_new: np.ndarray               # [T, Hkv, d] fp16
     q: np.ndarray                   # [T, H, d] fp16
     slot_mapping: np.ndarray        # [T] int64 slot of each new token
     query_start_loc: np.ndarray     # [B+1] int32
@@ -225,8 +243,9 @@ def make_prefill_case(shape: Shape, cached_lens, chunk_lens, seed=0,
                        keep_logical=keep_logical)
     T = int(chunk_lens.sum())
     dims = (T, shape.H, shape.d)
-    k_new = rng.standard_normal(dims, dtype=np.float32).astype(np.float16)
-    v_new = rng.standard_normal(dims, dtype=np.float32).astype(np.float16)
+    kv_dims = (T, shape.kv, shape.d)
+    k_new = rng.standard_normal(kv_dims, dtype=np.float32).astype(np.float16)
+    v_new = rng.standard_normal(kv_dims, dtype=np.float32).astype(np.float16)
     q = rng.standard_normal(dims, dtype=np.float32).astype(np.float16)
     qsl = np.zeros(len(chunk_lens) + 1, dtype=np.int32)
     qsl[1:] = np.cumsum(chunk_lens)

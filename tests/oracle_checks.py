@@ -52,6 +52,18 @@ def _sdpa(q, K, V, scale, mask=None):
     return np.transpose(o[0].numpy(), (1, 0, 2))
 
 
+def _sdpa_gqa(q, K, V, scale, mask=None):
+    """q [Q, H, d], K/V [L, Hkv, d] -> [Q, H, d] via torch's grouped-query
+    mode (its own head mapping), fp64 CPU."""
+    qt = torch.from_numpy(np.ascontiguousarray(np.transpose(q, (1, 0, 2)))).double()[None]
+    kt = torch.from_numpy(np.ascontiguousarray(np.transpose(K, (1, 0, 2)))).double()[None]
+    vt = torch.from_numpy(np.ascontiguousarray(np.transpose(V, (1, 0, 2)))).double()[None]
+    mt = None if mask is None else torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mt, scale=scale,
+                                                         enable_gqa=True)
+    return np.transpose(o[0].numpy(), (1, 0, 2))
+
+
 def _dense_from_latents(ck, cv, U, W):
     """Test-side rebuild for exact bases only (signed permutations)."""
     U = U.astype(np.float64)
@@ -106,6 +118,52 @@ def check_full_rank_prefill_matches_sdpa(orc):
         mask = np.arange(P0 + C)[None, :] <= (P0 + np.arange(C))[:, None]
         ref = _sdpa(case.q[q0:q1].astype(np.float64), K, V, case.scale,
                     mask=np.broadcast_to(mask, (sh.H, C, P0 + C)).copy())
+        assert _max_rel(out[q0:q1], ref) < TIGHT, b
+
+
+def check_gqa_decode_matches_sdpa(orc):
+    """Grouped-query layout (6 query heads on 2 key/value heads) with exact
+    bases: the oracle must equal torch's grouped-query attention on the
+    uncompressed K and V."""
+    rng = np.random.default_rng(21)
+    sh = Shape(H=6, d=8, r_k=8, r_v=16, bs=4, Hkv=2)
+    U = np.stack([signed_permutation(rng, 8) for _ in range(2)])
+    W = signed_permutation(rng, 16)
+    case = make_decode_case(sh, seq_lens=[1, 9, 16, 5], seed=7, keep_logical=True,
+                            bases=(U, W))
+    out = orc.decode(case.q, case.cache.k_cache, case.cache.v_cache, case.U, case.W,
+                     case.cache.block_tables, case.cache.seq_lens, case.scale)
+    for b, L in enumerate(case.cache.seq_lens):
+        K, V = _dense_from_latents(case.cache.logical_ck[b], case.cache.logical_cv[b], case.U, case.W)
+        ref = _sdpa_gqa(case.q[b:b + 1].astype(np.float64), K, V, case.scale)[0]
+        assert _max_rel(out[b], ref) < TIGHT, (b, _max_rel(out[b], ref))
+
+
+def check_gqa_prefill_matches_sdpa(orc):
+    """Grouped-query chunked prefill (4 query heads on 2) with exact bases and
+    the causal offset mask, against torch's grouped-query attention."""
+    rng = np.random.default_rng(22)
+    sh = Shape(H=4, d=8, r_k=8, r_v=16, bs=4, Hkv=2)
+    U = np.stack([signed_permutation(rng, 8) for _ in range(2)])
+    W = signed_permutation(rng, 16)
+    cached = [6, 0, 3]
+    chunk = [2, 5, 4]
+    case = make_prefill_case(sh, cached, chunk, seed=8, keep_logical=True, bases=(U, W))
+    kc, vc = orc.append(case.k_new, case.v_new, case.U, case.W, case.slot_mapping,
+                        case.cache.k_cache, case.cache.v_cache)
+    out = orc.prefill(case.q, case.query_start_loc, kc, vc, case.U, case.W,
+                      case.cache.block_tables, case.seq_lens, case.scale)
+    for b in range(3):
+        P0, C = cached[b], chunk[b]
+        q0, q1 = case.query_start_loc[b], case.query_start_loc[b + 1]
+        K_old, V_old = _dense_from_latents(case.cache.logical_ck[b].astype(np.float64),
+                                           case.cache.logical_cv[b].astype(np.float64),
+                                           case.U, case.W)
+        K = np.concatenate([K_old, case.k_new[q0:q1].astype(np.float64)])
+        V = np.concatenate([V_old, case.v_new[q0:q1].astype(np.float64)])
+        mask = np.arange(P0 + C)[None, :] <= (P0 + np.arange(C))[:, None]
+        ref = _sdpa_gqa(case.q[q0:q1].astype(np.float64), K, V, case.scale,
+                        mask=np.broadcast_to(mask, (sh.H, C, P0 + C)).copy())
         assert _max_rel(out[q0:q1], ref) < TIGHT, b
 
 
@@ -470,6 +528,8 @@ ALL_CHECKS = [
     check_fit_invariances,
     check_full_rank_decode_matches_sdpa,
     check_full_rank_prefill_matches_sdpa,
+    check_gqa_decode_matches_sdpa,
+    check_gqa_prefill_matches_sdpa,
     check_subspace_lossless,
     check_random_orthonormal_roundtrip,
     check_latent_identity,

@@ -28,8 +28,8 @@ MUTANTS = {
                            "return e / np.sum(e, axis=0, keepdims=True)"),
     "causal_excludes_diagonal": ("visible = key_pos <= qry_pos", "visible = key_pos < qry_pos"),
     "causal_ignores_prefix": ("qry_pos = P0 + np.arange(C)[:, None]", "qry_pos = np.arange(C)[:, None]"),
-    "no_causal_mask": ("o, _ = _attend(qf[q0:q1, h], K[:, h, :], V[:, h, :], scale, visible)",
-                       "o, _ = _attend(qf[q0:q1, h], K[:, h, :], V[:, h, :], scale)"),
+    "no_causal_mask": ("o, _ = _attend(qf[q0:q1, h], K[:, g, :], V[:, g, :], scale, visible)",
+                       "o, _ = _attend(qf[q0:q1, h], K[:, g, :], V[:, g, :], scale)"),
     "append_wrong_head_basis": ("kc[blk, h, off, :] = (Uf[h].T @ kf[n, h])",
                                 "kc[blk, h, off, :] = (Uf[(h + 1) % H].T @ kf[n, h])"),
     "append_v_flatten_feature_major": ("vc[blk, :, off] = (Wf.T @ vf[n].reshape(-1))",
@@ -40,6 +40,10 @@ MUTANTS = {
     "append_truncates": ("kc[blk, h, off, :] = (Uf[h].T @ kf[n, h]).astype(np.float16)",
                          "kc[blk, h, off, :] = np.trunc((Uf[h].T @ kf[n, h]) * 64) / 64"),
     "empty_sequence_nan": ("out[b] = 0.0", "out[b] = np.nan"),
+    "gqa_interleaved_groups": ("        for h in range(H):\n            g = h // G\n            o, p = _attend(",
+                               "        for h in range(H):\n            g = h % (H // G)\n            o, p = _attend("),
+    "gqa_prefill_first_head_only": ("            g = h // G\n            o, _ = _attend(",
+                                    "            g = 0\n            o, _ = _attend("),
     "fit_bottom_eigvecs": ("order = np.argsort(w)[::-1]", "order = np.argsort(w)"),
     "fit_mean_centred": ("        Kh = kf[:, h, :]\n", "        Kh = kf[:, h, :] - kf[:, h, :].mean(axis=0)\n"),
     "fit_v_feature_major": ("Vm = vf.reshape(N, H * d)", "Vm = vf.transpose(0, 2, 1).reshape(N, H * d)"),
