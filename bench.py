@@ -14,8 +14,9 @@ events that take its dispatch's own begin and end timestamps.  `value` is
 latent-KV bytes per step / mean step time.  Beside the headline the line
 carries the step with its append, a streaming-read ceiling, the chunked
 prefill workload (16 requests x 4096 cached + 256 new tokens: attention and
-append, as TFLOP/s against the fp16 MFMA peak), the bases fit from 16384 K/V
-samples (its Gram kernel against the same peak), and the CPU leg, which
+append, as TFLOP/s against the fp16 MFMA peak), grouped-query decode
+(gqa8_b16: 32 query heads on 8 key/value heads), the bases fit from 16384
+K/V samples (its Gram kernel against the same peak), and the CPU leg, which
 times the fp64 oracle on a bounded sample of the decode workload on the host
 cores.
 
@@ -98,6 +99,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill_b16 leg")
     ap.add_argument("--no-fit", action="store_true", help="skip the bases-fit leg")
+    ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query decode leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU sample budget")
     ap.add_argument("--flush", choices=["read", "write"], default="read",
                     help="evict the Infinity Cache by reading (default) or writing 512 MiB")
@@ -258,6 +260,48 @@ def prefill_leg(flush_fn, steps):
         "append_kernel_tflops": round(tf(app_flops, m(app_kern_ms)), 1),
         "append_kernel_mfma_frac": round(tf(app_flops, m(app_kern_ms)) / MFMA_F16_PEAK_TFLOPS, 4),
         "append_kernel_gbs": round(app_bytes / (m(app_kern_ms) * 1e-3) / 1e9, 1),
+    }
+
+
+def gqa_leg(flush_fn, steps):
+    """Decode at gqa8_b16: 16 sequences x 2048 tokens, 32 query heads on 8
+    key/value heads (H d128 r_k64 r_v512), 2048 latent bytes per token.
+    Flushed steps (events around the call) and the split-K kernel (the
+    library's timing events), as latent GB/s against the 8 TB/s peak."""
+    import numpy as np
+    import torch
+    from rank_compressed_paged_amd import metrics
+    from rank_compressed_paged_amd import starkv as sk
+    from rank_compressed_paged_amd import workloads as wl
+    case = wl.make_config("gqa8_b16")
+    sh, c = case.shape, case.cache
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    q, kc, vc, U, W = dev(case.q), dev(c.k_cache), dev(c.v_cache), dev(case.U), dev(case.W)
+    bt, sl = dev(c.block_tables), dev(c.seq_lens)
+    B, msl = case.B, int(c.seq_lens.max())
+    dims = sk.dims_of(kc, vc, U, W, num_heads=sh.H)
+    ws = sk.alloc_workspace(sk.decode_workspace_size(dims, B, msl), "cuda")
+    out = torch.empty((B, sh.H, sh.d), dtype=torch.float16, device="cuda")
+
+    def step():
+        sk.decode_attn(q, kc, vc, U, W, bt, sl, msl, case.scale, out=out, workspace=ws)
+
+    for i in range(5):
+        flush_fn(i)
+        step()
+    torch.cuda.synchronize()
+    step_ms, _, _ = timed(step, steps, flush_fn)
+    _, kern_ms, _ = timed(step, steps, flush_fn, sk.TIME_DECODE_SPLIT)
+    lat = metrics.decode_latent_bytes(c.seq_lens, sh.kv, sh.r_k, sh.r_v)
+    m = statistics.fmean
+    gbs = lambda ms: lat / (ms * 1e-3) / 1e9
+    return {
+        "workload": "gqa8_b16", "batch": B, "seq_len": msl, "heads": sh.H, "kv_heads": sh.kv,
+        "latent_bytes_per_step": int(lat), "steps": steps,
+        "step_ms": round(m(step_ms), 5), "step_gbs": round(gbs(m(step_ms)), 1),
+        "split_kernel_ms": round(m(kern_ms), 5),
+        "split_kernel_gbs": round(gbs(m(kern_ms)), 1),
+        "split_kernel_hbm_frac": round(gbs(m(kern_ms)) / HBM_PEAK_GBS, 4),
     }
 
 
@@ -431,6 +475,8 @@ def run_bench(args):
     if not args.no_prefill:
         del ceil_sink
         res["prefill"] = prefill_leg(do_flush, args.steps)
+    if not args.no_gqa:
+        res["gqa"] = gqa_leg(do_flush, args.steps)
     if not args.no_fit:
         res["fit"] = fit_leg(args.steps)
     res["device"] = device_info()

@@ -22,12 +22,20 @@
  * size 16); token t of sequence b lives in block block_tables[b][t / 16] at
  * offset t % 16.
  *
+ * Grouped-query attention (Hkv key/value heads shared by groups of H / Hkv
+ * query heads) keeps the same scheme per key/value head g: U_g and the key
+ * latents are per key/value head, W has Hkv*d rows and vec() flattens the
+ * [Hkv, d] values, and query head h reads key/value head g = h / (H / Hkv):
+ * q~_h = U_g^T q_h, scores on c_k[t, g], out_h = W_g z_h.
+ *
  * Layouts (all fp16 = IEEE binary16, little-endian, dense, row-major):
- *   k_cache  [num_blocks][H][16][r_k]
+ *   k_cache  [num_blocks][Hkv][16][r_k]
  *   v_cache  [num_blocks][r_v][16]      (feature-major within a page)
- *   U        [H][d][r_k]
- *   W        [H*d][r_v]
- *   q, k, v, out   [tokens][H][d]
+ *   U        [Hkv][d][r_k]
+ *   W        [Hkv*d][r_v]
+ *   q, out   [tokens][H][d]
+ *   k, v     [tokens][Hkv][d]
+ * (Hkv = H for multi-head attention.)
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless marked (host).  The caller owns all
@@ -41,9 +49,10 @@
  *     query_start_loc) are trusted.  Block ids outside [0, num_blocks) and
  *     slots outside the cache are skipped rather than dereferenced.
  *   - Compiled shape instances of the attention and append calls:
- *     (H, d, r_k, r_v) = (32, 128, 64, 512) and (4, 64, 16, 64), block size
- *     16.  Other shapes return STARKV_ERR_UNSUPPORTED.  The bases fit takes
- *     any shape within the limits stated at its declaration.
+ *     (H, d, r_k, r_v) = (32, 128, 64, 512) with Hkv 32 or 8, and
+ *     (4, 64, 16, 64) with Hkv 4 or 2; block size 16.  Other shapes return
+ *     STARKV_ERR_UNSUPPORTED.  The bases fit takes any shape within the
+ *     limits stated at its declaration.
  */
 #ifndef STARKV_H_
 #define STARKV_H_
@@ -55,7 +64,7 @@
 extern "C" {
 #endif
 
-#define STARKV_ABI_VERSION 1
+#define STARKV_ABI_VERSION 2
 
 typedef enum {
   STARKV_OK = 0,
@@ -73,9 +82,12 @@ typedef struct {
   int32_t num_heads;  /* H */
   int32_t head_dim;   /* d */
   int32_t rank_k;     /* r_k, key latent size per head (<= d) */
-  int32_t rank_v;     /* r_v, joint value latent size (<= H*d) */
+  int32_t rank_v;     /* r_v, joint value latent size (<= Hkv*d) */
   int32_t block_size; /* tokens per page; must be 16 */
   int32_t num_blocks; /* pages in k_cache / v_cache (> 0) */
+  int32_t num_kv_heads; /* Hkv, key/value heads; 0 means H (multi-head attention);
+                           must divide H.  Query head h uses key/value head
+                           h / (H / Hkv) (grouped-query attention). */
 } starkv_dims;
 
 /* Version of this ABI (STARKV_ABI_VERSION). */
@@ -96,8 +108,10 @@ int32_t starkv_shape_supported(const starkv_dims* dims);
  * rounded to nearest even from an fp32 accumulation.  Negative slots are
  * skipped (padding); slots at or beyond num_blocks*16 are skipped.  Slots
  * must be distinct.  num_tokens == 0 is a no-op.
- *   k, v          [num_tokens][H][d] fp16
+ *   k, v          [num_tokens][Hkv][d] fp16
  *   U, W          fp16, layouts above
+ * Only the key/value heads enter: num_heads may be any multiple of Hkv
+ * (dims with num_heads = Hkv and num_kv_heads 0 describe the same append).
  *   slot_mapping  [num_tokens] int64
  *   k_cache, v_cache  updated in place
  */
@@ -201,15 +215,15 @@ starkv_status starkv_decode_plan(const starkv_dims* dims, int32_t batch, int32_t
  * start is not deficient in it and the r-th and (r+1)-th eigenvalues are
  * apart: the error falls as (lambda_{r+1} / lambda_r)^iters.
  *   dims          head_dim a multiple of 64; rank_k, rank_v <= 512;
- *                 H * head_dim <= 65536; block_size and num_blocks unused
- *   k, v          [num_samples][H][d] fp16; num_samples >= rank_k, rank_v
- *   u0            [H][d][r_k] fp32 starting matrices (e.g. Gaussian)
- *   w0            [H*d][r_v] fp32
+ *                 Hkv * head_dim <= 65536; block_size and num_blocks unused
+ *   k, v          [num_samples][Hkv][d] fp16; num_samples >= rank_k, rank_v
+ *   u0            [Hkv][d][r_k] fp32 starting matrices (e.g. Gaussian)
+ *   w0            [Hkv*d][r_v] fp32
  *   iters         1 .. 1000
- *   U             [H][d][r_k] fp16 out (the layout append/decode take)
- *   W             [H*d][r_v] fp16 out
+ *   U             [Hkv][d][r_k] fp16 out (the layout append/decode take)
+ *   W             [Hkv*d][r_v] fp16 out
  *   workspace     >= starkv_fit_workspace_size(...) bytes; no initialisation
- *                 (about (H*d)^2 * 4 bytes: the value Gram matrix in fp32)
+ *                 (about (Hkv*d)^2 * 4 bytes: the value Gram matrix in fp32)
  *   info          optional (NULL = not reported), int32 device word: set to
  *                 the number of non-positive pivots the Cholesky steps met
  *                 (0 on success; > 0 means rank-deficient samples or start,

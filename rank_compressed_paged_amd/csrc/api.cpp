@@ -13,8 +13,15 @@ namespace starkv {
 TimingHook g_timing;
 
 bool shape_supported(const ShapeKey& s) {
-  return (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) ||
-         (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64);
+  return (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512 && (s.Hkv == 32 || s.Hkv == 8)) ||
+         (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64 && (s.Hkv == 4 || s.Hkv == 2));
+}
+
+// The append sees only the key/value heads: it supports the key/value view
+// (Hkv, d, r_k, r_v) of every supported shape, whatever the query heads.
+static bool kv_shape_supported(const ShapeKey& s) {
+  return (s.d == 128 && s.rk == 64 && s.rv == 512 && (s.Hkv == 32 || s.Hkv == 8)) ||
+         (s.d == 64 && s.rk == 16 && s.rv == 64 && (s.Hkv == 4 || s.Hkv == 2));
 }
 
 static int env_int(const char* name, int dflt) {
@@ -157,15 +164,26 @@ namespace {
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-starkv_status check_dims(const starkv_dims* d, ShapeKey* key) {
+// Key/value heads: num_kv_heads, or num_heads when it is 0; it must divide
+// num_heads.  Returns 0 when invalid.
+int kv_heads(const starkv_dims* d) {
+  const int hkv = d->num_kv_heads == 0 ? d->num_heads : d->num_kv_heads;
+  if (hkv <= 0 || d->num_heads <= 0 || d->num_heads % hkv != 0) return 0;
+  return hkv;
+}
+
+starkv_status check_dims(const starkv_dims* d, ShapeKey* key, bool kv_view = false) {
   if (!d) return STARKV_ERR_NULL;
   if (d->num_heads <= 0 || d->head_dim <= 0 || d->rank_k <= 0 || d->rank_v <= 0 ||
-      d->block_size <= 0 || d->num_blocks <= 0)
+      d->block_size <= 0 || d->num_blocks <= 0 || d->num_kv_heads < 0)
     return STARKV_ERR_DIMS;
-  if (d->rank_k > d->head_dim || (long)d->rank_v > (long)d->num_heads * d->head_dim)
+  const int hkv = kv_heads(d);
+  if (hkv == 0) return STARKV_ERR_DIMS;
+  if (d->rank_k > d->head_dim || (long)d->rank_v > (long)hkv * d->head_dim)
     return STARKV_ERR_DIMS;
-  const ShapeKey k{d->num_heads, d->head_dim, d->rank_k, d->rank_v};
-  if (d->block_size != 16 || !shape_supported(k)) return STARKV_ERR_UNSUPPORTED;
+  const ShapeKey k{d->num_heads, d->head_dim, d->rank_k, d->rank_v, hkv};
+  if (d->block_size != 16 || !(kv_view ? kv_shape_supported(k) : shape_supported(k)))
+    return STARKV_ERR_UNSUPPORTED;
   *key = k;
   return STARKV_OK;
 }
@@ -182,17 +200,21 @@ bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
 // The bases fit has its own limits: d a multiple of 64 (Gram tiles), ranks
 // up to 512 (the triangular solve keeps a row block of Q in LDS); the page
-// size and page count do not enter.
+// size and page count do not enter.  The samples carry the key/value heads,
+// so the fit's head count is Hkv.
 starkv_status check_fit_dims(const starkv_dims* d, ShapeKey* key) {
   if (!d) return STARKV_ERR_NULL;
-  if (d->num_heads <= 0 || d->head_dim <= 0 || d->rank_k <= 0 || d->rank_v <= 0)
+  if (d->num_heads <= 0 || d->head_dim <= 0 || d->rank_k <= 0 || d->rank_v <= 0 ||
+      d->num_kv_heads < 0)
     return STARKV_ERR_DIMS;
-  if (d->rank_k > d->head_dim || (long)d->rank_v > (long)d->num_heads * d->head_dim)
+  const int hkv = kv_heads(d);
+  if (hkv == 0) return STARKV_ERR_DIMS;
+  if (d->rank_k > d->head_dim || (long)d->rank_v > (long)hkv * d->head_dim)
     return STARKV_ERR_DIMS;
-  if (d->head_dim % 64 != 0 || d->rank_k > 512 || d->rank_v > 512 || d->num_heads > 65535 ||
-      (long)d->num_heads * d->head_dim > 65536)
+  if (d->head_dim % 64 != 0 || d->rank_k > 512 || d->rank_v > 512 || hkv > 65535 ||
+      (long)hkv * d->head_dim > 65536)
     return STARKV_ERR_UNSUPPORTED;
-  *key = ShapeKey{d->num_heads, d->head_dim, d->rank_k, d->rank_v};
+  *key = ShapeKey{hkv, d->head_dim, d->rank_k, d->rank_v, hkv};
   return STARKV_OK;
 }
 
@@ -232,14 +254,16 @@ starkv_status starkv_append(const starkv_dims* dims, const void* k, const void* 
                             const void* W, const int64_t* slot_mapping, int32_t num_tokens,
                             void* k_cache, void* v_cache, void* stream) {
   ShapeKey key;
-  starkv_status st = check_dims(dims, &key);
+  starkv_status st = check_dims(dims, &key, /*kv_view=*/true);
   if (st != STARKV_OK) return st;
   if (num_tokens < 0) return STARKV_ERR_DIMS;
   if (num_tokens == 0) return STARKV_OK;
   st = check_ptrs({k, v, U, W, slot_mapping, k_cache, v_cache});
   if (st != STARKV_OK) return st;
-  const hipError_t e = launch_append(key, k, v, U, W, slot_mapping, num_tokens, dims->num_blocks,
-                                     k_cache, v_cache, (hipStream_t)stream);
+  // the append only sees key/value heads
+  const ShapeKey kv_key{key.Hkv, key.d, key.rk, key.rv, key.Hkv};
+  const hipError_t e = launch_append(kv_key, k, v, U, W, slot_mapping, num_tokens,
+                                     dims->num_blocks, k_cache, v_cache, (hipStream_t)stream);
   return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
 }
 

@@ -514,6 +514,17 @@ hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const 
                     dim3(64 / 16 + 4), dim3(kSmallWaves * 64), st, a);
       return hipGetLastError();
     }
+    if (s.H == 8 && s.d == 128 && s.rk == 64 && s.rv == 512) {
+      launch_hooked(TIME_APPEND, TIME_NONE, append_small_kernel<8, 128, 64, 512>,
+                    dim3(512 / 16 + 8), dim3(kSmallWaves * 64), st, a);
+      return hipGetLastError();
+    }
+  }
+  if (s.H == 8 && s.d == 128 && s.rk == 64 && s.rv == 512) {
+    const long tiles_m = (n_tokens + TT_M - 1) / TT_M;
+    launch_hooked(TIME_APPEND, TIME_NONE, append_tiled_kernel<8, 128, 64, 512, 64, 1>,
+                  dim3((unsigned)(tiles_m * (512 / TT_N + 8))), dim3(512), st, a);
+    return hipGetLastError();
   }
   if (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) {
     const long tiles_m = (n_tokens + TT_M - 1) / TT_M;

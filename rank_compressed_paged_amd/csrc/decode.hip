@@ -59,7 +59,8 @@ constexpr int BS = 16;  // tokens per page
 constexpr int kMaxSplitPages = 256;  // planner bound on pages per split
 
 // ---------------------------------------------------------------------------
-// 1. q~[n, h, :] = (scale*log2e) * U_h^T q[n, h, :]  -> fp16
+// 1. q~[n, h, :] = (scale*log2e) * U_g^T q[n, h, :]  -> fp16, g = h / QG the
+//    key/value head of query head h (QG = 1: multi-head attention)
 // grid (H, ceil(N/(64*TPW))), 4 waves; in token tile tt the wave w owns
 // tokens n0+16w .. n0+16w+15 of that tile's 64.  The product is taken as
 // q~^T = U_h^T q^T, so that each lane ends with 4 consecutive outputs of one
@@ -79,7 +80,7 @@ __device__ __forceinline__ half4 lds_read_tr16(const half_t* p) {
   return __builtin_bit_cast(half4, r);
 }
 
-template <int H, int D, int RK, int TPW>
+template <int H, int D, int RK, int TPW, int QG>
 __global__ __launch_bounds__(256) void qproj_kernel(const half_t* __restrict__ q,
                                                     const half_t* __restrict__ U, int n_tokens,
                                                     float qscale, half_t* __restrict__ qt) {
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(256) void qproj_kernel(const half_t* __restrict__ q
   half8 bq[D / 32];
   const int nb0 = blockIdx.y * TPW * 64 + w * 16;
   if (nb0 < n_tokens) load_q(bq, nb0);
-  const half_t* Uh = U + (size_t)h * D * RK;
+  const half_t* Uh = U + (size_t)(h / QG) * D * RK;  // the head's key/value head
   for (int c = tid; c < D * RK / 8; c += 256) {
     const int i = c / (RK / 8), r0 = (c % (RK / 8)) * 8;
     *(half8*)&sU[i][r0] = *(const half8*)(Uh + (size_t)i * RK + r0);
@@ -145,11 +146,23 @@ __global__ __launch_bounds__(256) void qproj_kernel(const half_t* __restrict__ q
 // SS (split_stride) is the split count rounded up to the merge's request
 // batch; slots past a sequence's last split are never written.
 
-template <int H, int RK, int RV, int NW>
+// Key pages per wave under grouped-query attention (QG query heads per
+// key/value head): the wave's HPW query heads span KPW key/value heads, from
+// kv0 = w*HPW/QG on; each of them is loaded once and feeds the score
+// products of all its query heads.
+template <int H, int RK, int RV, int NW, int QG>
+struct KeyCfg {
+  static constexpr int HPW = DecodeCfg<H, RK, RV, NW>::HPW;
+  static constexpr int KPW = HPW >= QG ? HPW / QG : 1;
+  static constexpr int HKV = H / QG;
+  static_assert(H % QG == 0 && (HPW % QG == 0 || QG % HPW == 0), "query groups must align with waves");
+};
+
+template <int H, int RK, int RV, int NW, int QG>
 struct PageRegs {
   using C = DecodeCfg<H, RK, RV, NW>;
   typedef _Float16 kvec __attribute__((ext_vector_type(C::KC / 4)));
-  kvec k[C::HPW][C::NKC];
+  kvec k[KeyCfg<H, RK, RV, NW, QG>::KPW][C::NKC];
   half4 v[C::FT];
 };
 
@@ -161,19 +174,23 @@ __device__ __forceinline__ T ld_page(const T* p) {
     return *p;
 }
 
-template <int H, int RK, int RV, int NW, bool NT>
-__device__ __forceinline__ void load_page(PageRegs<H, RK, RV, NW>& pr, const half_t* __restrict__ kc,
+template <int H, int RK, int RV, int NW, int QG, bool NT>
+__device__ __forceinline__ void load_page(PageRegs<H, RK, RV, NW, QG>& pr,
+                                          const half_t* __restrict__ kc,
                                           const half_t* __restrict__ vc, int blk, int w, int col,
                                           int quad) {
   using C = DecodeCfg<H, RK, RV, NW>;
-  using kvec = typename PageRegs<H, RK, RV, NW>::kvec;
-  // keys: head (w*HPW + hl), token row `col`, k chunk `quad`
-  const half_t* kb = kc + (((size_t)blk * H + w * C::HPW) * BS + col) * RK + quad * (C::KC / 4);
+  using K = KeyCfg<H, RK, RV, NW, QG>;
+  using kvec = typename PageRegs<H, RK, RV, NW, QG>::kvec;
+  // keys: key/value head (kv0 + kk), token row `col`, k chunk `quad`
+  const int kv0 = w * C::HPW / QG;
+  const half_t* kb =
+      kc + (((size_t)blk * K::HKV + kv0) * BS + col) * RK + quad * (C::KC / 4);
 #pragma unroll
-  for (int hl = 0; hl < C::HPW; ++hl)
+  for (int kk = 0; kk < K::KPW; ++kk)
 #pragma unroll
     for (int c = 0; c < C::NKC; ++c)
-      pr.k[hl][c] = ld_page<NT>((const kvec*)(kb + (size_t)hl * BS * RK + c * C::KC));
+      pr.k[kk][c] = ld_page<NT>((const kvec*)(kb + (size_t)kk * BS * RK + c * C::KC));
   // values: feature (w*FPW + ft*16 + col), tokens 4*quad .. 4*quad+3
   const half_t* vb = vc + ((size_t)blk * RV + w * C::FPW + col) * BS + quad * 4;
 #pragma unroll
@@ -193,25 +210,29 @@ struct SplitState {
 // weight 0 and a zeroed value operand, so a fully masked page changes
 // nothing.  Keeping every page on the same path lets the compiler count the
 // prefetched loads exactly instead of draining them.
-template <int H, int RK, int RV, int NW>
+template <int H, int RK, int RV, int NW, int QG>
 __device__ __forceinline__ void process_page(
-    SplitState<H, RK, RV, NW>& st, PageRegs<H, RK, RV, NW>& cur,
-    const typename PageRegs<H, RK, RV, NW>::kvec (&qv)[DecodeCfg<H, RK, RV, NW>::NKC],
+    SplitState<H, RK, RV, NW>& st, PageRegs<H, RK, RV, NW, QG>& cur,
+    const typename PageRegs<H, RK, RV, NW, QG>::kvec (&qv)[DecodeCfg<H, RK, RV, NW>::NKC],
     half_t (*sP)[DecodeCfg<H, RK, RV, NW>::R16][BS], float (*sAlpha)[DecodeCfg<H, RK, RV, NW>::R16],
     int* sFlag, int p, int buf, int valid, int w, int col, int quad) {
   using C = DecodeCfg<H, RK, RV, NW>;
-  using kvec = typename PageRegs<H, RK, RV, NW>::kvec;
+  using K = KeyCfg<H, RK, RV, NW, QG>;
+  using kvec = typename PageRegs<H, RK, RV, NW, QG>::kvec;
   const kvec kzero = {};
+  // B column col holds q~ of query head w*HPW + col, whose key/value head is
+  // the wave's kk-th: the products for key page kk take only those columns
+  const int my_kk = col < C::HPW ? (w * C::HPW + col) / QG - w * C::HPW / QG : -1;
   float4v sacc = zero4();
 #pragma unroll
-  for (int hl = 0; hl < C::HPW; ++hl) {
+  for (int kk = 0; kk < K::KPW; ++kk) {
 #pragma unroll
     for (int c = 0; c < C::NKC; ++c) {
-      const kvec bq = (col == hl) ? qv[c] : kzero;
+      const kvec bq = (my_kk == kk) ? qv[c] : kzero;
       if constexpr (C::KC == 32)
-        sacc = mfma16x16x32(cur.k[hl][c], bq, sacc);
+        sacc = mfma16x16x32(cur.k[kk][c], bq, sacc);
       else
-        sacc = mfma16x16x16(cur.k[hl][c], bq, sacc);
+        sacc = mfma16x16x16(cur.k[kk][c], bq, sacc);
     }
   }
   float sv[4];
@@ -269,14 +290,14 @@ __device__ __forceinline__ void process_page(
   }
 }
 
-template <int H, int RK, int RV, int NW, int DEPTH, bool NT>
+template <int H, int RK, int RV, int NW, int DEPTH, bool NT, int QG>
 __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     const half_t* __restrict__ qt, const half_t* __restrict__ k_cache,
     const half_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ seq_lens, float* __restrict__ ml, half_t* __restrict__ zpart,
     int max_blocks, int num_blocks, int pages_per_split, int num_splits, int split_stride) {
   using C = DecodeCfg<H, RK, RV, NW>;
-  using kvec = typename PageRegs<H, RK, RV, NW>::kvec;
+  using kvec = typename PageRegs<H, RK, RV, NW, QG>::kvec;
   __shared__ __attribute__((aligned(16))) half_t sP[2][C::R16][BS];
   __shared__ float sAlpha[2][C::R16];
   __shared__ int sFlag[2];  // page index whose softmax step moved a running max
@@ -306,8 +327,8 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
   if (p0 >= n_pages) return;
   const int p1 = min(p0 + pages_per_split, n_pages);
 
-  PageRegs<H, RK, RV, NW> ring[DEPTH];
-  load_page<H, RK, RV, NW, NT>(ring[0], k_cache, v_cache,
+  PageRegs<H, RK, RV, NW, QG> ring[DEPTH];
+  load_page<H, RK, RV, NW, QG, NT>(ring[0], k_cache, v_cache,
                                ((unsigned)blk0 < (unsigned)num_blocks) ? blk0 : 0, w, col, quad);
 
   // rows >= H are padding: P stays zero there, alpha one
@@ -351,16 +372,16 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
   // current page's matrix ops (and the waits they need) above that request.
 #pragma unroll
   for (int j = 1; j < DEPTH - 1; ++j)
-    load_page<H, RK, RV, NW, NT>(ring[j], k_cache, v_cache, page_block(p0 + j), w, col, quad);
+    load_page<H, RK, RV, NW, QG, NT>(ring[j], k_cache, v_cache, page_block(p0 + j), w, col, quad);
 
   for (int p = p0; p < p1; p += DEPTH) {
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {
-      load_page<H, RK, RV, NW, NT>(ring[(j + DEPTH - 1) % DEPTH], k_cache, v_cache,
-                                   page_block(p + j + DEPTH - 1), w, col, quad);
+      load_page<H, RK, RV, NW, QG, NT>(ring[(j + DEPTH - 1) % DEPTH], k_cache, v_cache,
+                                       page_block(p + j + DEPTH - 1), w, col, quad);
       __builtin_amdgcn_sched_barrier(0);
-      process_page<H, RK, RV, NW>(st, ring[j], qv, sP, sAlpha, sFlag, p + j, (p + j - p0) & 1,
-                                  page_valid(p + j), w, col, quad);
+      process_page<H, RK, RV, NW, QG>(st, ring[j], qv, sP, sAlpha, sFlag, p + j,
+                                      (p + j - p0) & 1, page_valid(p + j), w, col, quad);
     }
   }
 
@@ -419,7 +440,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
 // straight-line instruction of a short kernel cost a fetch, so the merge and
 // the products avoid per-element conversions in their unrolled bodies.
 // ---------------------------------------------------------------------------
-template <int H, int D, int RV, int TB, int CB, int NT>
+template <int H, int D, int RV, int TB, int CB, int NT, int QG>
 __global__ __launch_bounds__(NT) void finish_kernel(const float* __restrict__ ml,
                                                     const half_t* __restrict__ zpart,
                                                     const int32_t* __restrict__ seq_lens,
@@ -477,11 +498,11 @@ __global__ __launch_bounds__(NT) void finish_kernel(const float* __restrict__ ml
 #pragma unroll
       for (int j = 0; j < WCH; ++j) {
         const int c = tid + j * NT;  // chunk c: row c / (RV/8), 8 features
-        wst[j] = *(const half8*)(W + ((size_t)h * D + c / (RV / 8)) * RV + (c % (RV / 8)) * 8);
+        wst[j] = *(const half8*)(W + ((size_t)(h / QG) * D + c / (RV / 8)) * RV + (c % (RV / 8)) * 8);
       }
       return;
     }
-    const half_t* wrow = W + ((size_t)h * D + w * (D / MW) + col) * RV + quad * 8;
+    const half_t* wrow = W + ((size_t)(h / QG) * D + w * (D / MW) + col) * RV + quad * 8;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
@@ -640,7 +661,7 @@ __global__ __launch_bounds__(NT) void finish_kernel(const float* __restrict__ ml
 // D[token][output].  The z loads run up to 16 chunks ahead of their
 // products: z comes from HBM, and the LDS footprint already limits the
 // kernel to two waves per SIMD, which leaves the registers for the ring.
-template <int H, int D, int RV, int NW>
+template <int H, int D, int RV, int NW, int QG>
 __global__ __launch_bounds__(NW * 64) void upproj_tiled_kernel(const half_t* __restrict__ W,
                                                                const half_t* __restrict__ z,
                                                                int n_tokens,
@@ -655,7 +676,7 @@ __global__ __launch_bounds__(NW * 64) void upproj_tiled_kernel(const half_t* __r
   const int h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c32 = lane & 31, hf = lane >> 5;
-  const half_t* Wh = W + (size_t)h * D * RV;
+  const half_t* Wh = W + (size_t)(h / QG) * D * RV;  // the head's key/value head
   for (int c = tid; c < D * RV / 8; c += NW * 64) {
     const int r = c / (RV / 8), k = (c % (RV / 8)) * 8;
     *(half8*)&sW[r][k] = *(const half8*)(Wh + (size_t)r * RV + k);
@@ -700,10 +721,10 @@ __global__ __launch_bounds__(NW * 64) void upproj_tiled_kernel(const half_t* __r
   }
 }
 
-template <int H, int D, int RV, int NW>
+template <int H, int D, int RV, int NW, int QG>
 static void launch_upproj_tiled_t(const void* W, const void* z, int n_tokens, void* out,
                                   hipStream_t st) {
-  hipLaunchKernelGGL((upproj_tiled_kernel<H, D, RV, NW>),
+  hipLaunchKernelGGL((upproj_tiled_kernel<H, D, RV, NW, QG>),
                      dim3(H, (n_tokens + NW * 32 - 1) / (NW * 32)), dim3(NW * 64), 0, st,
                      (const half_t*)W, (const half_t*)z, n_tokens, (half_t*)out);
 }
@@ -711,10 +732,14 @@ static void launch_upproj_tiled_t(const void* W, const void* z, int n_tokens, vo
 hipError_t launch_upproj_tiled(const ShapeKey& s, const void* W, const void* z_tiled,
                                int n_tokens, void* out, hipStream_t st) {
   if (n_tokens <= 0) return hipSuccess;
-  if (s.H == 32 && s.d == 128 && s.rv == 512)
-    launch_upproj_tiled_t<32, 128, 512, 8>(W, z_tiled, n_tokens, out, st);
-  else if (s.H == 4 && s.d == 64 && s.rv == 64)
-    launch_upproj_tiled_t<4, 64, 64, 4>(W, z_tiled, n_tokens, out, st);
+  if (s.H == 32 && s.Hkv == 32 && s.d == 128 && s.rv == 512)
+    launch_upproj_tiled_t<32, 128, 512, 8, 1>(W, z_tiled, n_tokens, out, st);
+  else if (s.H == 32 && s.Hkv == 8 && s.d == 128 && s.rv == 512)
+    launch_upproj_tiled_t<32, 128, 512, 8, 4>(W, z_tiled, n_tokens, out, st);
+  else if (s.H == 4 && s.Hkv == 4 && s.d == 64 && s.rv == 64)
+    launch_upproj_tiled_t<4, 64, 64, 4, 1>(W, z_tiled, n_tokens, out, st);
+  else if (s.H == 4 && s.Hkv == 2 && s.d == 64 && s.rv == 64)
+    launch_upproj_tiled_t<4, 64, 64, 4, 2>(W, z_tiled, n_tokens, out, st);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -723,12 +748,12 @@ hipError_t launch_upproj_tiled(const ShapeKey& s, const void* W, const void* z_t
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-template <int H, int D, int RK, int RV, int NW, int DEPTH, bool NT>
+template <int H, int D, int RK, int RV, int NW, int DEPTH, bool NT, int QG = 1>
 static hipError_t decode_instance(const DecodePlan& p, const void* qt, const void* k_cache,
                                   const void* v_cache, const void* W, const int32_t* block_tables,
                                   int max_blocks, const int32_t* seq_lens, int num_blocks,
                                   int batch, float* ml, void* zpart, void* out, hipStream_t st) {
-  launch_hooked(TIME_DECODE_SPLIT, TIME_NONE, decode_split_kernel<H, RK, RV, NW, DEPTH, NT>,
+  launch_hooked(TIME_DECODE_SPLIT, TIME_NONE, decode_split_kernel<H, RK, RV, NW, DEPTH, NT, QG>,
                 dim3(p.num_splits, batch), dim3(NW * 64), st, (const half_t*)qt,
                 (const half_t*)k_cache, (const half_t*)v_cache, block_tables, seq_lens, ml,
                 (half_t*)zpart, max_blocks, num_blocks, p.pages_per_split, p.num_splits,
@@ -738,7 +763,7 @@ static hipError_t decode_instance(const DecodePlan& p, const void* qt, const voi
   // is a multiple of CB times the split groups)
   const unsigned wgs = (unsigned)(H * ((batch + p.finish_tb - 1) / p.finish_tb));
 #define STARKV_FINISH(TB_, CB_, NT_)                                                           \
-  hipLaunchKernelGGL((finish_kernel<H, D, RV, TB_, CB_, NT_>), dim3(wgs), dim3(NT_), 0, st,    \
+  hipLaunchKernelGGL((finish_kernel<H, D, RV, TB_, CB_, NT_, QG>), dim3(wgs), dim3(NT_), 0, st, \
                      (const float*)ml, (const half_t*)zpart, seq_lens, (const half_t*)W, batch, \
                      max_blocks, p.pages_per_split, p.num_splits, p.split_stride, (half_t*)out)
   switch (p.finish_tb * 1000000 + p.finish_cb * 10000 + p.finish_nt) {
@@ -759,15 +784,15 @@ static hipError_t decode_instance(const DecodePlan& p, const void* qt, const voi
   return hipGetLastError();
 }
 
-template <int H, int D, int RK>
+template <int H, int D, int RK, int QG>
 static hipError_t qproj_instance(const void* q, const void* U, int n, float scale, void* qt,
                                  int precedes, hipStream_t st) {
   if (n >= 1024)  // many tokens: four 64-token tiles per work group
-    launch_hooked(TIME_NONE, precedes, qproj_kernel<H, D, RK, 4>, dim3(H, (n + 255) / 256),
+    launch_hooked(TIME_NONE, precedes, qproj_kernel<H, D, RK, 4, QG>, dim3(H, (n + 255) / 256),
                   dim3(256), st, (const half_t*)q, (const half_t*)U, n, scale * kLog2e,
                   (half_t*)qt);
   else
-    launch_hooked(TIME_NONE, precedes, qproj_kernel<H, D, RK, 1>, dim3(H, (n + 63) / 64),
+    launch_hooked(TIME_NONE, precedes, qproj_kernel<H, D, RK, 1, QG>, dim3(H, (n + 63) / 64),
                   dim3(256), st, (const half_t*)q, (const half_t*)U, n, scale * kLog2e,
                   (half_t*)qt);
   return hipGetLastError();
@@ -776,10 +801,14 @@ static hipError_t qproj_instance(const void* q, const void* U, int n, float scal
 hipError_t launch_qproj(const ShapeKey& s, const void* q, const void* U, int n_tokens, float scale,
                         void* qt, int precedes, hipStream_t st) {
   if (n_tokens <= 0) return hipSuccess;
-  if (s.H == 32 && s.d == 128 && s.rk == 64)
-    return qproj_instance<32, 128, 64>(q, U, n_tokens, scale, qt, precedes, st);
-  if (s.H == 4 && s.d == 64 && s.rk == 16)
-    return qproj_instance<4, 64, 16>(q, U, n_tokens, scale, qt, precedes, st);
+  if (s.H == 32 && s.d == 128 && s.rk == 64) {
+    if (s.Hkv == 32) return qproj_instance<32, 128, 64, 1>(q, U, n_tokens, scale, qt, precedes, st);
+    if (s.Hkv == 8) return qproj_instance<32, 128, 64, 4>(q, U, n_tokens, scale, qt, precedes, st);
+  }
+  if (s.H == 4 && s.d == 64 && s.rk == 16) {
+    if (s.Hkv == 4) return qproj_instance<4, 64, 16, 1>(q, U, n_tokens, scale, qt, precedes, st);
+    if (s.Hkv == 2) return qproj_instance<4, 64, 16, 2>(q, U, n_tokens, scale, qt, precedes, st);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -789,7 +818,11 @@ hipError_t launch_decode(const ShapeKey& s, const DecodePlan& p, const void* qt,
                          float* ml, void* zpart, void* out, hipStream_t st) {
 #define STARKV_DECODE_ARGS \
   p, qt, k_cache, v_cache, W, block_tables, max_blocks, seq_lens, num_blocks, batch, ml, zpart, out, st
-  if (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) {
+  if (s.H == 32 && s.Hkv == 8 && s.d == 128 && s.rk == 64 && s.rv == 512)
+    return decode_instance<32, 128, 64, 512, 16, 2, false, 4>(STARKV_DECODE_ARGS);
+  if (s.H == 4 && s.Hkv == 2 && s.d == 64 && s.rk == 16 && s.rv == 64)
+    return decode_instance<4, 64, 16, 64, 4, 2, false, 2>(STARKV_DECODE_ARGS);
+  if (s.H == 32 && s.Hkv == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) {
     // kernel variant (tuning aid): waves per group, prefetch depth, non-temporal loads
     switch (p.variant) {
       case 1: return decode_instance<32, 128, 64, 512, 4, 2, false>(STARKV_DECODE_ARGS);
@@ -801,7 +834,7 @@ hipError_t launch_decode(const ShapeKey& s, const DecodePlan& p, const void* qt,
       default: return decode_instance<32, 128, 64, 512, 16, 2, false>(STARKV_DECODE_ARGS);
     }
   }
-  if (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64)
+  if (s.H == 4 && s.Hkv == 4 && s.d == 64 && s.rk == 16 && s.rv == 64)
     return decode_instance<4, 64, 16, 64, 4, 2, false>(STARKV_DECODE_ARGS);
 #undef STARKV_DECODE_ARGS
   return hipErrorInvalidValue;

@@ -9,9 +9,11 @@
 
 namespace starkv {
 
-// One compiled shape instance: heads, head size, key rank, value rank.
+// One compiled shape instance: query heads, head size, key rank, value rank,
+// key/value heads (H for multi-head attention; H / Hkv query heads share one
+// key/value head under grouped-query attention).
 struct ShapeKey {
-  int H, d, rk, rv;
+  int H, d, rk, rv, Hkv;
 };
 
 // Split plan of one decode call: pages_per_split consecutive pages per work

@@ -118,11 +118,14 @@ constexpr float kRaise = 8.f;           // lazy-rescale threshold (log2 units)
 //          the softmax's vector instructions interleaved between the products,
 //          3 as 1 with the step's loads issued after the products, 4 as 2
 //          with the step's loads interleaved between the products too
-template <int H, int RK, int RV, int G, int MQ, int NW, int PPS, int DEPTH, int SCHED, bool KLDS>
+template <int H, int RK, int RV, int G, int MQ, int NW, int PPS, int DEPTH, int SCHED, bool KLDS,
+          int QG>
 __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   static_assert(DEPTH >= 2 && DEPTH <= 3, "register ring of 2 or 3 steps");
   static_assert(PPS == 1 || PPS == 2, "one or two pages per step");
+  static_assert(H % QG == 0, "query heads per key/value head");
   using C = PrefillCfg<H, RK, RV, G, MQ, NW>;
+  constexpr int HKV = H / QG;  // key/value heads of a key page (query head h reads h / QG)
   typedef _Float16 kvec __attribute__((ext_vector_type(C::KC / 4)));
   constexpr int RING = 2 * kChunk;
   constexpr int TPS = PPS * PBS;  // tokens per step
@@ -135,6 +138,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) int sBlk[RING];
   // KLDS: key pages of three steps, [step % 3][head][page][token][r_k + pad],
   // each loaded once per work group and shared by the head's score waves
+  // (under grouped-query attention each query head's slot holds its key/value
+  // head's page)
   constexpr int LDKV = RK + 8;
   __shared__ __attribute__((aligned(16))) half_t sK[KLDS ? 3 : 1][G][PPS][PBS][LDKV];
 
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   // the loads take a scalar base plus a 32-bit vector offset)
   int k_off[C::SUW];
 #pragma unroll
-  for (int i = 0; i < C::SUW; ++i) k_off[i] = (su_h[i] * PBS + col) * RK + quad * (C::KC / 4);
+  for (int i = 0; i < C::SUW; ++i) k_off[i] = ((su_h[i] / QG) * PBS + col) * RK + quad * (C::KC / 4);
   const int v_off = f_base * PBS + hf * 8;
 
   auto block_of = [&](int page) {
@@ -231,7 +236,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
 #pragma unroll
     for (int pg = 0; pg < PPS; ++pg) {
       const int blk = ids[pg];
-      const half_t* kp = a.k_cache + (size_t)(blk < 0 ? 0 : blk) * (H * PBS * RK);
+      const half_t* kp = a.k_cache + (size_t)(blk < 0 ? 0 : blk) * (HKV * PBS * RK);
 #pragma unroll
       for (int i = 0; i < C::SUW; ++i)
 #pragma unroll
@@ -260,7 +265,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
       const int rc = c % (RK / 8), tok = (c / (RK / 8)) % PBS;
       const int pg = (c / (RK / 8 * PBS)) % PPS, hl = c / (RK / 8 * PBS * PPS);
       const int blk = ids[pg] < 0 ? 0 : ids[pg];
-      kst[j] = *(const half8*)(a.k_cache + (((size_t)blk * H + g * G + hl) * PBS + tok) * RK + rc * 8);
+      kst[j] = *(const half8*)(a.k_cache +
+                               (((size_t)blk * HKV + (g * G + hl) / QG) * PBS + tok) * RK + rc * 8);
     }
   };
   auto kst_store = [&](int kb) {
@@ -613,7 +619,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
 }
 
 template <int H, int D, int RK, int RV, int G, int MQ, int NW, int PPS, int DEPTH, int SCHED,
-          bool KLDS = false>
+          bool KLDS = false, int QG = 1>
 static hipError_t prefill_instance(const void* qt, const int32_t* qsl, int max_query_len,
                                    const void* k_cache, const void* v_cache, const void* W,
                                    const int32_t* block_tables, int max_blocks,
@@ -634,11 +640,12 @@ static hipError_t prefill_instance(const void* qt, const int32_t* qsl, int max_q
   a.n_groups = H / G;
   a.n_tb = (total_q + 31) / 32;
   const long wgs = (long)batch * a.n_qtiles * a.n_groups;
-  launch_hooked(TIME_PREFILL_ATTN, TIME_NONE, prefill_attn_kernel<H, RK, RV, G, MQ, NW, PPS, DEPTH, SCHED, KLDS>,
+  launch_hooked(TIME_PREFILL_ATTN, TIME_NONE,
+                prefill_attn_kernel<H, RK, RV, G, MQ, NW, PPS, DEPTH, SCHED, KLDS, QG>,
                 dim3((unsigned)wgs), dim3(NW * 64), st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_upproj_tiled(ShapeKey{H, D, RK, RV}, W, z, total_q, out, st);
+  return launch_upproj_tiled(ShapeKey{H, D, RK, RV, H / QG}, W, z, total_q, out, st);
 }
 
 // Kernel variant (tuning aid, STARKV_PREFILL_VARIANT): head group, query
@@ -660,7 +667,11 @@ hipError_t launch_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl,
 #define STARKV_PREFILL_ARGS                                                                    \
   qt, qsl, max_query_len, k_cache, v_cache, W, block_tables, max_blocks, seq_lens, num_blocks, \
       batch, total_q, z, out, st
-  if (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) {
+  if (s.H == 32 && s.Hkv == 8 && s.d == 128 && s.rk == 64 && s.rv == 512)
+    return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 3, 4, true, 4>(STARKV_PREFILL_ARGS);
+  if (s.H == 4 && s.Hkv == 2 && s.d == 64 && s.rk == 16 && s.rv == 64)
+    return prefill_instance<4, 64, 16, 64, 4, 16, 2, 2, 2, 1, true, 2>(STARKV_PREFILL_ARGS);
+  if (s.H == 32 && s.Hkv == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) {
     switch (prefill_variant()) {
       case 1: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 2, 1, true>(STARKV_PREFILL_ARGS);
       case 2: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 2, 2, false>(STARKV_PREFILL_ARGS);
@@ -669,7 +680,7 @@ hipError_t launch_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl,
       default: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 3, 4, true>(STARKV_PREFILL_ARGS);
     }
   }
-  if (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64)
+  if (s.H == 4 && s.Hkv == 4 && s.d == 64 && s.rk == 16 && s.rv == 64)
     return prefill_instance<4, 64, 16, 64, 4, 16, 2, 2, 2, 1, true>(STARKV_PREFILL_ARGS);
 #undef STARKV_PREFILL_ARGS
   return hipErrorInvalidValue;

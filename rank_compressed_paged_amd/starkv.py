@@ -40,7 +40,8 @@ EXPORTED = [
 class Dims(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("rank_k", ctypes.c_int32), ("rank_v", ctypes.c_int32),
-                ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32)]
+                ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32)]
 
 
 class StarKVError(RuntimeError):
@@ -108,15 +109,18 @@ def _check(status, where):
         raise StarKVError(status, where)
 
 
-def make_dims(H, d, r_k, r_v, num_blocks, block_size=16):
-    return Dims(H, d, r_k, r_v, block_size, num_blocks)
+def make_dims(H, d, r_k, r_v, num_blocks, block_size=16, num_kv_heads=0):
+    return Dims(H, d, r_k, r_v, block_size, num_blocks, num_kv_heads)
 
 
-def dims_of(k_cache, v_cache, U, W):
-    NB, H, bs, r_k = k_cache.shape
+def dims_of(k_cache, v_cache, U, W, num_heads=None):
+    """Dims of a cache; num_heads = query heads (default: the cache's key/value
+    heads, i.e. multi-head attention)."""
+    NB, Hkv, bs, r_k = k_cache.shape
     d = U.shape[1]
     r_v = v_cache.shape[1]
-    return make_dims(H, d, r_k, r_v, NB, bs)
+    H = Hkv if num_heads is None else int(num_heads)
+    return make_dims(H, d, r_k, r_v, NB, bs, 0 if H == Hkv else Hkv)
 
 
 def shape_supported(dims):
@@ -169,7 +173,7 @@ def alloc_workspace(nbytes, device):
 
 
 def append(k, v, U, W, slot_mapping, k_cache, v_cache, stream=None):
-    """Project k, v [N, H, d] to latents and write them to slot_mapping [N] (int64)."""
+    """Project k, v [N, Hkv, d] to latents and write them to slot_mapping [N] (int64)."""
     dims = dims_of(k_cache, v_cache, U, W)
     N = k.shape[0]
     H, d = dims.num_heads, dims.head_dim
@@ -185,7 +189,7 @@ def append(k, v, U, W, slot_mapping, k_cache, v_cache, stream=None):
 def decode_attn(q, k_cache, v_cache, U, W, block_tables, seq_lens, max_seq_len, scale=None,
                 out=None, workspace=None, stream=None):
     """Decode attention for q [B, H, d]; returns out [B, H, d] fp16."""
-    dims = dims_of(k_cache, v_cache, U, W)
+    dims = dims_of(k_cache, v_cache, U, W, num_heads=q.shape[1])
     B = q.shape[0]
     H, d = dims.num_heads, dims.head_dim
     if scale is None:
@@ -210,7 +214,7 @@ def decode_attn(q, k_cache, v_cache, U, W, block_tables, seq_lens, max_seq_len, 
 def prefill_attn(q, query_start_loc, max_query_len, k_cache, v_cache, U, W, block_tables,
                  seq_lens, max_seq_len, scale=None, out=None, workspace=None, stream=None):
     """Chunked-prefill attention for q [total_q, H, d]; returns out fp16."""
-    dims = dims_of(k_cache, v_cache, U, W)
+    dims = dims_of(k_cache, v_cache, U, W, num_heads=q.shape[1])
     T = q.shape[0]
     B = seq_lens.shape[0]
     H, d = dims.num_heads, dims.head_dim

@@ -31,7 +31,7 @@ def test_exports_match_header():
 
 
 def test_version_and_status_strings():
-    assert sk.abi_version() == 1
+    assert sk.abi_version() == 2
     for s in range(0, 8):
         assert sk.lib().starkv_status_string(s)
     assert sk.lib().starkv_status_string(99) == b"unknown status"
@@ -43,6 +43,12 @@ def _main_dims(nb=8):
 
 def test_shape_support():
     assert sk.shape_supported(_main_dims())
+    assert sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, num_kv_heads=8))
+    assert sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, num_kv_heads=32))
+    assert sk.shape_supported(sk.make_dims(4, 64, 16, 64, 3, num_kv_heads=2))
+    assert not sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, num_kv_heads=16))
+    assert not sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, num_kv_heads=5))  # not a divisor
+    assert not sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, num_kv_heads=-1))
     assert sk.shape_supported(sk.make_dims(4, 64, 16, 64, 3))
     assert not sk.shape_supported(sk.make_dims(32, 128, 64, 256, 3))
     assert not sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, block_size=32))
@@ -80,6 +86,13 @@ def test_append_validation():
     assert f(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None) == 1
     assert f(ctypes.byref(d), FAKE, FAKE, FAKE, MISALIGNED, FAKE, 4, FAKE, FAKE, None) == 5
     assert f(ctypes.byref(d), None, None, None, None, None, 0, None, None, None) == 0
+    # the append only sees key/value heads: the 8-head view of the grouped
+    # shape is accepted, an unknown head count is not
+    kv8 = sk.make_dims(8, 128, 64, 512, 8)
+    assert f(ctypes.byref(kv8), None, None, None, None, None, 0, None, None, None) == 0
+    assert f(ctypes.byref(kv8), FAKE, None, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None) == 1
+    kv16 = sk.make_dims(16, 128, 64, 512, 8)
+    assert f(ctypes.byref(kv16), FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None) == 3
 
 
 def test_prefill_validation():
