@@ -14,8 +14,9 @@ events that take its dispatch's own begin and end timestamps.  `value` is
 latent-KV bytes per step / mean step time.  Beside the headline the line
 carries the step with its append, a streaming-read ceiling, the chunked
 prefill workload (16 requests x 4096 cached + 256 new tokens: attention and
-append, as TFLOP/s against the fp16 MFMA peak), grouped-query decode
-(gqa8_b16: 32 query heads on 8 key/value heads), the bases fit from 16384
+append, as TFLOP/s against the fp16 MFMA peak), decode at two other
+layouts of the same batch (gqa8_b16: 32 query heads on 8 key/value heads;
+lowrank_b16: r_k 32, r_v 256), the bases fit from 16384
 K/V samples (its Gram kernel against the same peak), and the CPU leg, which
 times the fp64 oracle on a bounded sample of the decode workload on the host
 cores.
@@ -99,7 +100,8 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill_b16 leg")
     ap.add_argument("--no-fit", action="store_true", help="skip the bases-fit leg")
-    ap.add_argument("--no-gqa", action="store_true", help="skip the grouped-query decode leg")
+    ap.add_argument("--no-layouts", action="store_true",
+                    help="skip the grouped-query and low-rank decode legs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU sample budget")
     ap.add_argument("--flush", choices=["read", "write"], default="read",
                     help="evict the Infinity Cache by reading (default) or writing 512 MiB")
@@ -263,17 +265,19 @@ def prefill_leg(flush_fn, steps):
     }
 
 
-def gqa_leg(flush_fn, steps):
-    """Decode at gqa8_b16: 16 sequences x 2048 tokens, 32 query heads on 8
-    key/value heads (H d128 r_k64 r_v512), 2048 latent bytes per token.
-    Flushed steps (events around the call) and the split-K kernel (the
-    library's timing events), as latent GB/s against the 8 TB/s peak."""
+def decode_leg(name, flush_fn, steps):
+    """Decode at another layout of the same batch (16 sequences x 2048
+    tokens): gqa8_b16 (32 query heads on 8 key/value heads, r_k 64, r_v 512:
+    2048 latent bytes per token) or lowrank_b16 (32 heads, r_k 32, r_v 256:
+    2560 bytes per token).  Flushed steps (events around the call) and the
+    split-K kernel (the library's timing events), as latent GB/s against the
+    8 TB/s peak."""
     import numpy as np
     import torch
     from rank_compressed_paged_amd import metrics
     from rank_compressed_paged_amd import starkv as sk
     from rank_compressed_paged_amd import workloads as wl
-    case = wl.make_config("gqa8_b16")
+    case = wl.make_config(name)
     sh, c = case.shape, case.cache
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
     q, kc, vc, U, W = dev(case.q), dev(c.k_cache), dev(c.v_cache), dev(case.U), dev(case.W)
@@ -296,7 +300,8 @@ def gqa_leg(flush_fn, steps):
     m = statistics.fmean
     gbs = lambda ms: lat / (ms * 1e-3) / 1e9
     return {
-        "workload": "gqa8_b16", "batch": B, "seq_len": msl, "heads": sh.H, "kv_heads": sh.kv,
+        "workload": name, "batch": B, "seq_len": msl, "heads": sh.H, "kv_heads": sh.kv,
+        "rank_k": sh.r_k, "rank_v": sh.r_v,
         "latent_bytes_per_step": int(lat), "steps": steps,
         "step_ms": round(m(step_ms), 5), "step_gbs": round(gbs(m(step_ms)), 1),
         "split_kernel_ms": round(m(kern_ms), 5),
@@ -475,8 +480,8 @@ def run_bench(args):
     if not args.no_prefill:
         del ceil_sink
         res["prefill"] = prefill_leg(do_flush, args.steps)
-    if not args.no_gqa:
-        res["gqa"] = gqa_leg(do_flush, args.steps)
+    if not args.no_layouts:
+        res["layouts"] = [decode_leg(n, do_flush, args.steps) for n in ("gqa8_b16", "lowrank_b16")]
     if not args.no_fit:
         res["fit"] = fit_leg(args.steps)
     res["device"] = device_info()

@@ -12,8 +12,12 @@ namespace starkv {
 
 TimingHook g_timing;
 
+// Compiled instances: the main shape at two rank profiles (r_k, r_v) =
+// (64, 512) and (32, 256), the former also with 8 key/value heads, and the
+// tiny shape with 4 or 2 key/value heads.
 bool shape_supported(const ShapeKey& s) {
   return (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512 && (s.Hkv == 32 || s.Hkv == 8)) ||
+         (s.H == 32 && s.d == 128 && s.rk == 32 && s.rv == 256 && s.Hkv == 32) ||
          (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64 && (s.Hkv == 4 || s.Hkv == 2));
 }
 
@@ -21,6 +25,7 @@ bool shape_supported(const ShapeKey& s) {
 // (Hkv, d, r_k, r_v) of every supported shape, whatever the query heads.
 static bool kv_shape_supported(const ShapeKey& s) {
   return (s.d == 128 && s.rk == 64 && s.rv == 512 && (s.Hkv == 32 || s.Hkv == 8)) ||
+         (s.d == 128 && s.rk == 32 && s.rv == 256 && s.Hkv == 32) ||
          (s.d == 64 && s.rk == 16 && s.rv == 64 && (s.Hkv == 4 || s.Hkv == 2));
 }
 

@@ -519,6 +519,11 @@ hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const 
                     dim3(512 / 16 + 8), dim3(kSmallWaves * 64), st, a);
       return hipGetLastError();
     }
+    if (s.H == 32 && s.d == 128 && s.rk == 32 && s.rv == 256) {
+      launch_hooked(TIME_APPEND, TIME_NONE, append_small_kernel<32, 128, 32, 256>,
+                    dim3(256 / 16 + 32), dim3(kSmallWaves * 64), st, a);
+      return hipGetLastError();
+    }
   }
   if (s.H == 8 && s.d == 128 && s.rk == 64 && s.rv == 512) {
     const long tiles_m = (n_tokens + TT_M - 1) / TT_M;

@@ -736,6 +736,8 @@ hipError_t launch_upproj_tiled(const ShapeKey& s, const void* W, const void* z_t
     launch_upproj_tiled_t<32, 128, 512, 8, 1>(W, z_tiled, n_tokens, out, st);
   else if (s.H == 32 && s.Hkv == 8 && s.d == 128 && s.rv == 512)
     launch_upproj_tiled_t<32, 128, 512, 8, 4>(W, z_tiled, n_tokens, out, st);
+  else if (s.H == 32 && s.Hkv == 32 && s.d == 128 && s.rv == 256)
+    launch_upproj_tiled_t<32, 128, 256, 8, 1>(W, z_tiled, n_tokens, out, st);
   else if (s.H == 4 && s.Hkv == 4 && s.d == 64 && s.rv == 64)
     launch_upproj_tiled_t<4, 64, 64, 4, 1>(W, z_tiled, n_tokens, out, st);
   else if (s.H == 4 && s.Hkv == 2 && s.d == 64 && s.rv == 64)
@@ -805,6 +807,8 @@ hipError_t launch_qproj(const ShapeKey& s, const void* q, const void* U, int n_t
     if (s.Hkv == 32) return qproj_instance<32, 128, 64, 1>(q, U, n_tokens, scale, qt, precedes, st);
     if (s.Hkv == 8) return qproj_instance<32, 128, 64, 4>(q, U, n_tokens, scale, qt, precedes, st);
   }
+  if (s.H == 32 && s.d == 128 && s.rk == 32 && s.Hkv == 32)
+    return qproj_instance<32, 128, 32, 1>(q, U, n_tokens, scale, qt, precedes, st);
   if (s.H == 4 && s.d == 64 && s.rk == 16) {
     if (s.Hkv == 4) return qproj_instance<4, 64, 16, 1>(q, U, n_tokens, scale, qt, precedes, st);
     if (s.Hkv == 2) return qproj_instance<4, 64, 16, 2>(q, U, n_tokens, scale, qt, precedes, st);
@@ -822,6 +826,8 @@ hipError_t launch_decode(const ShapeKey& s, const DecodePlan& p, const void* qt,
     return decode_instance<32, 128, 64, 512, 16, 2, false, 4>(STARKV_DECODE_ARGS);
   if (s.H == 4 && s.Hkv == 2 && s.d == 64 && s.rk == 16 && s.rv == 64)
     return decode_instance<4, 64, 16, 64, 4, 2, false, 2>(STARKV_DECODE_ARGS);
+  if (s.H == 32 && s.Hkv == 32 && s.d == 128 && s.rk == 32 && s.rv == 256)
+    return decode_instance<32, 128, 32, 256, 16, 2, false>(STARKV_DECODE_ARGS);
   if (s.H == 32 && s.Hkv == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) {
     // kernel variant (tuning aid): waves per group, prefetch depth, non-temporal loads
     switch (p.variant) {

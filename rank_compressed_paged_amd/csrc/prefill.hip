@@ -671,6 +671,10 @@ hipError_t launch_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl,
     return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 3, 4, true, 4>(STARKV_PREFILL_ARGS);
   if (s.H == 4 && s.Hkv == 2 && s.d == 64 && s.rk == 16 && s.rv == 64)
     return prefill_instance<4, 64, 16, 64, 4, 16, 2, 2, 2, 1, true, 2>(STARKV_PREFILL_ARGS);
+  // r_k 32: a step's two key pages of two heads are too few chunks for the
+  // LDS key ring, so the waves load their keys directly
+  if (s.H == 32 && s.Hkv == 32 && s.d == 128 && s.rk == 32 && s.rv == 256)
+    return prefill_instance<32, 128, 32, 256, 2, 64, 8, 2, 2, 2, false>(STARKV_PREFILL_ARGS);
   if (s.H == 32 && s.Hkv == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) {
     switch (prefill_variant()) {
       case 1: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 2, 1, true>(STARKV_PREFILL_ARGS);

@@ -61,6 +61,8 @@ TINY = Shape(H=4, d=64, r_k=16, r_v=64, bs=16)
 # grouped-query layouts: 8 key/value heads for 32 query heads (groups of 4),
 # and a tiny one with groups of 2
 GQA8 = Shape(H=32, d=128, r_k=64, r_v=512, bs=16, Hkv=8)
+# a lower rank profile of the main shape (per-layer ranks may differ)
+LOWRANK = Shape(H=32, d=128, r_k=32, r_v=256, bs=16)
 TINY_GQA = Shape(H=4, d=64, r_k=16, r_v=64, bs=16, Hkv=2)
 
 # Named workloads.  "seq" is ("fixed", L) or ("uniform", lo, hi) inclusive.
@@ -75,6 +77,9 @@ CONFIGS = {
     "gqa8_b64": dict(kind="decode", shape=GQA8, B=64, seq=("uniform", 4096, 8192), seed=7),
     "gqa8_prefill_b16": dict(kind="prefill", shape=GQA8, B=16, cached=4096, chunk=256, seed=8),
     "tiny_gqa": dict(kind="decode", shape=TINY_GQA, B=2, seq=("fixed", 256), seed=9),
+    "lowrank_b16": dict(kind="decode", shape=LOWRANK, B=16, seq=("fixed", 2048), seed=10),
+    "lowrank_prefill_b16": dict(kind="prefill", shape=LOWRANK, B=16, cached=4096, chunk=256,
+                                seed=11),
 }
 
 

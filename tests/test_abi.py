@@ -46,6 +46,8 @@ def test_shape_support():
     assert sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, num_kv_heads=8))
     assert sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, num_kv_heads=32))
     assert sk.shape_supported(sk.make_dims(4, 64, 16, 64, 3, num_kv_heads=2))
+    assert sk.shape_supported(sk.make_dims(32, 128, 32, 256, 3))          # low-rank profile
+    assert not sk.shape_supported(sk.make_dims(32, 128, 32, 512, 3))
     assert not sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, num_kv_heads=16))
     assert not sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, num_kv_heads=5))  # not a divisor
     assert not sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, num_kv_heads=-1))
