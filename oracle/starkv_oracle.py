@@ -49,6 +49,10 @@ __all__ = [
     "prefill",
     "fit_bases",
     "projector",
+    "e4m3_values",
+    "quantize_e4m3",
+    "append_fp8",
+    "dequantize_cache",
 ]
 
 
@@ -126,6 +130,83 @@ def append(k, v, U, W, slot_mapping, k_cache, v_cache):
         for h in range(H):
             kc[blk, h, off, :] = (Uf[h].T @ kf[n, h]).astype(np.float16)
         vc[blk, :, off] = (Wf.T @ vf[n].reshape(-1)).astype(np.float16)
+    return kc, vc
+
+
+# ---------------------------------------------------------------------------
+# FP8 latents (the quantised-latent variant the adjacent pages measure for
+# KV caches).  Format: OCP FP8 E4M3 -- one sign bit, four exponent bits with
+# bias 7, three mantissa bits; exponent 0 holds the subnormals m/8 * 2^-6;
+# S.1111.111 is NaN and there are no infinities, so the largest finite value
+# is 1.75 * 2^8 = 448.  A latent is stored as the code of c / scale with one
+# scale per tensor (keys, values), rounded to nearest with ties to the even
+# mantissa after clamping to +-448 (saturation); it reads back as
+# scale * value(code).
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_values():
+    """Value of each of the 256 E4M3 byte codes (NaN for the two NaN codes)."""
+    vals = np.empty(256)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 0xF, c & 0x7
+        if e == 15 and m == 7:
+            vals[c] = np.nan
+        elif e == 0:
+            vals[c] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            vals[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+def quantize_e4m3(x):
+    """E4M3 codes (uint8) of x: clamp to +-448, then round to the nearest
+    representable value with ties to the even mantissa.  The grid step in
+    the binade [2^e, 2^(e+1)) is 2^(e-3); below the smallest normal 2^-6
+    the step is the subnormal one, 2^-9."""
+    x = np.clip(np.asarray(x, dtype=np.float64), -E4M3_MAX, E4M3_MAX)
+    a = np.abs(x)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    step = 2.0 ** (e - 3)
+    q = np.round(a / step) * step          # numpy rounds half to even
+    codes = np.zeros(a.shape, dtype=np.int64)
+    nz = q > 0
+    eq = np.floor(np.log2(np.where(nz, q, 1.0)))   # binade of the rounded value
+    sub = nz & (eq < -6)
+    nrm = nz & ~sub
+    codes[sub] = np.round(q[sub] / 2.0 ** -9).astype(np.int64)
+    codes[nrm] = (((eq[nrm] + 7).astype(np.int64) << 3)
+                  | np.round((q[nrm] / 2.0 ** eq[nrm] - 1.0) * 8.0).astype(np.int64))
+    codes |= np.where(np.signbit(x), 0x80, 0)
+    return codes.astype(np.uint8)
+
+
+def dequantize_cache(codes, scale):
+    """fp64 latents scale * value(code) of an FP8 cache."""
+    return e4m3_values()[np.asarray(codes, dtype=np.uint8)] * float(scale)
+
+
+def append_fp8(k, v, U, W, slot_mapping, k_scale, v_scale, k_cache8, v_cache8):
+    """append() into FP8 caches (uint8 codes, same layouts): the exact fp64
+    projections divided by the tensor's scale and quantised by
+    quantize_e4m3.  Returns new caches (copies)."""
+    kc = np.array(k_cache8, dtype=np.uint8, copy=True)
+    vc = np.array(v_cache8, dtype=np.uint8, copy=True)
+    NB, H, bs, r_k = kc.shape
+    Uf = _f64(U)
+    Wf = _f64(W)
+    kf = _f64(k)
+    vf = _f64(v)
+    for n, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot >= 0:                  # negative slots are skipped
+            blk, off = int(slot) // bs, int(slot) % bs
+            if blk >= NB:
+                raise IndexError(f"slot {slot} beyond cache")
+            for h in range(H):
+                kc[blk, h, off, :] = quantize_e4m3((Uf[h].T @ kf[n, h]) / k_scale)
+            vc[blk, :, off] = quantize_e4m3((Wf.T @ vf[n].reshape(-1)) / v_scale)
     return kc, vc
 
 

@@ -520,7 +520,73 @@ def check_fit_invariances(orc):
     assert np.abs(orc.projector(W) - orc.projector(W2)).max() < 1e-9
 
 
+# --------------------------------------------------------------------------
+# FP8 latents
+def check_e4m3_table_matches_torch(orc):
+    """The 256 E4M3 code values equal torch's float8_e4m3fn conversion."""
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    v = orc.e4m3_values()
+    assert np.array_equal(np.isnan(v), np.isnan(ref))
+    assert np.array_equal(v[~np.isnan(v)], ref[~np.isnan(ref)])
+
+
+def check_e4m3_rounding_matches_torch(orc):
+    """Rounding to nearest, ties to even, on fp32 inputs inside +-448 (where
+    torch's conversion and the clamped one agree): random values over eight
+    decades, every exact midpoint between neighbouring codes, subnormals."""
+    rng = np.random.default_rng(31)
+    x = np.concatenate([rng.standard_normal(4000) * s for s in (1e-3, 1e-2, 0.1, 1, 10, 100)])
+    vals = np.sort(np.unique(torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn)
+                             .to(torch.float64).numpy()))
+    vals = vals[np.isfinite(vals)]
+    mids = (vals[1:] + vals[:-1]) / 2            # exact in fp32 for this grid
+    x = np.clip(np.concatenate([x, mids, -mids, vals]), -448, 448).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = orc.quantize_e4m3(x)
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, (x[bad[:5]], got[bad[:5]], ref[bad[:5]])
+
+
+def check_e4m3_saturates(orc):
+    """Magnitudes at or beyond the largest finite value clamp to +-448."""
+    x = np.array([448.0, 449.0, 479.0, 480.0, 1e6, -500.0, -1e30])
+    v = orc.e4m3_values()[orc.quantize_e4m3(x)]
+    assert np.array_equal(v, np.array([448, 448, 448, 448, 448, -448, -448], dtype=float))
+
+
+def check_fp8_append_exact_roundtrip(orc):
+    """Signed-permutation bases and inputs that are scale times E4M3 values:
+    the FP8 append stores exactly those values, so dequantising gives back
+    the projections (closed form), with the scales on both sides."""
+    rng = np.random.default_rng(32)
+    sh = Shape(H=2, d=8, r_k=8, r_v=16, bs=4)
+    U = np.stack([signed_permutation(rng, 8) for _ in range(2)])
+    W = signed_permutation(rng, 16)
+    grid = orc.e4m3_values()[:0x70]              # positive finite values up to 1.875 * 2^6
+    ks, vs = 0.5, 4.0
+    n = 6
+    k = (rng.choice(grid, size=(n, 2, 8)) * rng.choice([-1, 1], size=(n, 2, 8)) * ks)
+    v = (rng.choice(grid, size=(n, 2, 8)) * rng.choice([-1, 1], size=(n, 2, 8)) * vs)
+    k, v = k.astype(np.float16), v.astype(np.float16)
+    slots = np.array([3, 9, -1, 0, 15, 6])
+    kc = np.zeros((4, 2, 4, 8), np.uint8)
+    vc = np.zeros((4, 16, 4), np.uint8)
+    kc, vc = orc.append_fp8(k, v, U, W, slots, ks, vs, kc, vc)
+    kd, vd = orc.dequantize_cache(kc, ks), orc.dequantize_cache(vc, vs)
+    for i, s_ in enumerate(slots):
+        if s_ < 0:
+            continue
+        blk, off = divmod(int(s_), 4)
+        for h in range(2):
+            assert np.array_equal(kd[blk, h, off], U[h].T @ k[i, h].astype(np.float64))
+        assert np.array_equal(vd[blk, :, off], W.T @ v[i].astype(np.float64).reshape(-1))
+
+
 ALL_CHECKS = [
+    check_e4m3_table_matches_torch,
+    check_e4m3_rounding_matches_torch,
+    check_e4m3_saturates,
+    check_fp8_append_exact_roundtrip,
     check_fit_planted_subspace,
     check_fit_uncentred,
     check_fit_optimal_against_candidates,

@@ -40,6 +40,13 @@ MUTANTS = {
     "append_truncates": ("kc[blk, h, off, :] = (Uf[h].T @ kf[n, h]).astype(np.float16)",
                          "kc[blk, h, off, :] = np.trunc((Uf[h].T @ kf[n, h]) * 64) / 64"),
     "empty_sequence_nan": ("out[b] = 0.0", "out[b] = np.nan"),
+    "e4m3_wrong_bias": ("vals[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)",
+                        "vals[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 8)"),
+    "e4m3_truncates": ("q = np.round(a / step) * step", "q = np.floor(a / step) * step"),
+    "e4m3_no_saturation": ("x = np.clip(np.asarray(x, dtype=np.float64), -E4M3_MAX, E4M3_MAX)",
+                           "x = np.asarray(x, dtype=np.float64)"),
+    "fp8_append_scale_inverted": ("quantize_e4m3((Uf[h].T @ kf[n, h]) / k_scale)",
+                                  "quantize_e4m3((Uf[h].T @ kf[n, h]) * k_scale)"),
     "gqa_interleaved_groups": ("        for h in range(H):\n            g = h // G\n            o, p = _attend(",
                                "        for h in range(H):\n            g = h % (H // G)\n            o, p = _attend("),
     "gqa_prefill_first_head_only": ("            g = h // G\n            o, _ = _attend(",
