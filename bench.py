@@ -15,8 +15,9 @@ latent-KV bytes per step / mean step time.  Beside the headline the line
 carries the step with its append, a streaming-read ceiling, the chunked
 prefill workload (16 requests x 4096 cached + 256 new tokens: attention and
 append, as TFLOP/s against the fp16 MFMA peak), decode at two other
-layouts of the same batch (gqa8_b16: 32 query heads on 8 key/value heads;
-lowrank_b16: r_k 32, r_v 256), the bases fit from 16384
+layouts (gqa8_b16: 32 query heads on 8 key/value heads; lowrank_b16: r_k
+32, r_v 256; decode_b16_fp8 and decode_b64_fp8: FP8 E4M3 latents), the bases
+fit from 16384
 K/V samples (its Gram kernel against the same peak), and the CPU leg, which
 times the fp64 oracle on a bounded sample of the decode workload on the host
 cores.
@@ -286,9 +287,14 @@ def decode_leg(name, flush_fn, steps):
     dims = sk.dims_of(kc, vc, U, W, num_heads=sh.H)
     ws = sk.alloc_workspace(sk.decode_workspace_size(dims, B, msl), "cuda")
     out = torch.empty((B, sh.H, sh.d), dtype=torch.float16, device="cuda")
+    fp8 = c.k_cache.dtype == np.uint8
 
     def step():
-        sk.decode_attn(q, kc, vc, U, W, bt, sl, msl, case.scale, out=out, workspace=ws)
+        if fp8:
+            sk.decode_attn_fp8(q, kc, vc, U, W, bt, sl, msl, case.k_scale, case.v_scale,
+                               case.scale, out=out, workspace=ws)
+        else:
+            sk.decode_attn(q, kc, vc, U, W, bt, sl, msl, case.scale, out=out, workspace=ws)
 
     for i in range(5):
         flush_fn(i)
@@ -296,12 +302,12 @@ def decode_leg(name, flush_fn, steps):
     torch.cuda.synchronize()
     step_ms, _, _ = timed(step, steps, flush_fn)
     _, kern_ms, _ = timed(step, steps, flush_fn, sk.TIME_DECODE_SPLIT)
-    lat = metrics.decode_latent_bytes(c.seq_lens, sh.kv, sh.r_k, sh.r_v)
+    lat = metrics.decode_latent_bytes(c.seq_lens, sh.kv, sh.r_k, sh.r_v) // (2 if fp8 else 1)
     m = statistics.fmean
     gbs = lambda ms: lat / (ms * 1e-3) / 1e9
     return {
         "workload": name, "batch": B, "seq_len": msl, "heads": sh.H, "kv_heads": sh.kv,
-        "rank_k": sh.r_k, "rank_v": sh.r_v,
+        "rank_k": sh.r_k, "rank_v": sh.r_v, "latent_dtype": "e4m3" if fp8 else "f16",
         "latent_bytes_per_step": int(lat), "steps": steps,
         "step_ms": round(m(step_ms), 5), "step_gbs": round(gbs(m(step_ms)), 1),
         "split_kernel_ms": round(m(kern_ms), 5),
@@ -481,7 +487,8 @@ def run_bench(args):
         del ceil_sink
         res["prefill"] = prefill_leg(do_flush, args.steps)
     if not args.no_layouts:
-        res["layouts"] = [decode_leg(n, do_flush, args.steps) for n in ("gqa8_b16", "lowrank_b16")]
+        res["layouts"] = [decode_leg(n, do_flush, args.steps)
+                          for n in ("gqa8_b16", "lowrank_b16", "decode_b16_fp8", "decode_b64_fp8")]
     if not args.no_fit:
         res["fit"] = fit_leg(args.steps)
     res["device"] = device_info()

@@ -120,6 +120,24 @@ starkv_status starkv_append(const starkv_dims* dims, const void* k, const void* 
                             void* k_cache, void* v_cache, void* stream);
 
 /*
+ * FP8 latents (the quantised-latent variant that adjacent KV-cache work
+ * measures; half the bytes of fp16).  The caches keep the layouts above
+ * with one-byte elements: OCP FP8 E4M3 codes (sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent 0 subnormal; S.1111.111 NaN; largest
+ * value 448).  A latent c is stored as the code of c / scale, clamped to
+ * +-448 and rounded to nearest with ties to the even mantissa, with one
+ * scale per tensor (k_scale for keys, v_scale for values, finite and > 0),
+ * and reads back as scale * value(code).
+ *
+ * starkv_append_fp8: starkv_append writing FP8 codes (the projection is
+ * accumulated in fp32 and divided by the scale in fp32 before rounding).
+ */
+starkv_status starkv_append_fp8(const starkv_dims* dims, const void* k, const void* v,
+                                const void* U, const void* W, const int64_t* slot_mapping,
+                                int32_t num_tokens, float k_scale, float v_scale,
+                                void* k_cache8, void* v_cache8, void* stream);
+
+/*
  * Workspace bytes (host out-parameter *bytes) that starkv_decode_attn needs
  * for `batch` sequences of at most max_seq_len tokens.  Returns a status.
  */
@@ -149,6 +167,23 @@ starkv_status starkv_decode_attn(const starkv_dims* dims, const void* q, const v
                                  const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
                                  float scale, void* out, void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/*
+ * starkv_decode_attn over FP8 caches (see starkv_append_fp8): the same
+ * attention on the latents scale * value(code); k_scale folds into q~ and
+ * v_scale into the split partials, so the kernels do the same work on half
+ * the bytes (codes become fp16 matrix-core operands as they are used).
+ * Instances: (H, d, r_k, r_v) = (32, 128, 64, 512) with Hkv 32 or 8, and
+ * (4, 64, 16, 64); other shapes return STARKV_ERR_UNSUPPORTED.  Workspace as
+ * for starkv_decode_attn (starkv_decode_workspace_size).
+ */
+starkv_status starkv_decode_attn_fp8(const starkv_dims* dims, const void* q,
+                                     const void* k_cache8, const void* v_cache8, const void* U,
+                                     const void* W, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                     int32_t batch, int32_t max_seq_len, float scale,
+                                     float k_scale, float v_scale, void* out, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /*
  * Workspace bytes for starkv_prefill_attn with total_q chunk queries.

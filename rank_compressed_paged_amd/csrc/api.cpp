@@ -23,6 +23,12 @@ bool shape_supported(const ShapeKey& s) {
 
 // The append sees only the key/value heads: it supports the key/value view
 // (Hkv, d, r_k, r_v) of every supported shape, whatever the query heads.
+// Decode over FP8 latents: the main shape (both head layouts) and the tiny one.
+static bool fp8_decode_supported(const ShapeKey& s) {
+  return (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512 && (s.Hkv == 32 || s.Hkv == 8)) ||
+         (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64 && s.Hkv == 4);
+}
+
 static bool kv_shape_supported(const ShapeKey& s) {
   return (s.d == 128 && s.rk == 64 && s.rv == 512 && (s.Hkv == 32 || s.Hkv == 8)) ||
          (s.d == 128 && s.rk == 32 && s.rv == 256 && s.Hkv == 32) ||
@@ -268,7 +274,31 @@ starkv_status starkv_append(const starkv_dims* dims, const void* k, const void* 
   // the append only sees key/value heads
   const ShapeKey kv_key{key.Hkv, key.d, key.rk, key.rv, key.Hkv};
   const hipError_t e = launch_append(kv_key, k, v, U, W, slot_mapping, num_tokens,
-                                     dims->num_blocks, k_cache, v_cache, (hipStream_t)stream);
+                                     dims->num_blocks, k_cache, v_cache, LatentFormat{},
+                                     (hipStream_t)stream);
+  return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
+}
+
+starkv_status starkv_append_fp8(const starkv_dims* dims, const void* k, const void* v,
+                                const void* U, const void* W, const int64_t* slot_mapping,
+                                int32_t num_tokens, float k_scale, float v_scale,
+                                void* k_cache8, void* v_cache8, void* stream) {
+  ShapeKey key;
+  starkv_status st = check_dims(dims, &key, /*kv_view=*/true);
+  if (st != STARKV_OK) return st;
+  if (num_tokens < 0) return STARKV_ERR_DIMS;
+  if (!scale_ok(k_scale) || !scale_ok(v_scale)) return STARKV_ERR_ARG;
+  if (num_tokens == 0) return STARKV_OK;
+  st = check_ptrs({k, v, U, W, slot_mapping, k_cache8, v_cache8});
+  if (st != STARKV_OK) return st;
+  const ShapeKey kv_key{key.Hkv, key.d, key.rk, key.rv, key.Hkv};
+  LatentFormat fmt;
+  fmt.fp8 = true;
+  fmt.k_scale = k_scale;
+  fmt.v_scale = v_scale;
+  const hipError_t e = launch_append(kv_key, k, v, U, W, slot_mapping, num_tokens,
+                                     dims->num_blocks, k_cache8, v_cache8, fmt,
+                                     (hipStream_t)stream);
   return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
 }
 
@@ -321,7 +351,43 @@ starkv_status starkv_decode_attn(const starkv_dims* dims, const void* q, const v
   if (e != hipSuccess) return STARKV_ERR_LAUNCH;
   e = launch_decode(key, p, wb + ws.qt_off, k_cache, v_cache, W, block_tables,
                     max_blocks_per_seq, seq_lens, dims->num_blocks, batch,
-                    (float*)(wb + ws.ml_off), wb + ws.zp_off, out, s);
+                    (float*)(wb + ws.ml_off), wb + ws.zp_off, out, LatentFormat{}, s);
+  return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
+}
+
+starkv_status starkv_decode_attn_fp8(const starkv_dims* dims, const void* q,
+                                     const void* k_cache8, const void* v_cache8, const void* U,
+                                     const void* W, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                     int32_t batch, int32_t max_seq_len, float scale,
+                                     float k_scale, float v_scale, void* out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  ShapeKey key;
+  starkv_status st = check_dims(dims, &key);
+  if (st != STARKV_OK) return st;
+  if (!fp8_decode_supported(key)) return STARKV_ERR_UNSUPPORTED;
+  st = check_paging(batch, max_seq_len, max_blocks_per_seq, dims->block_size);
+  if (st != STARKV_OK) return st;
+  if (!scale_ok(scale) || !scale_ok(k_scale) || !scale_ok(v_scale)) return STARKV_ERR_ARG;
+  if (batch == 0) return STARKV_OK;
+  st = check_ptrs({q, k_cache8, v_cache8, U, W, block_tables, seq_lens, out, workspace});
+  if (st != STARKV_OK) return st;
+  const DecodePlan p = plan_decode(key, batch, max_seq_len, dims->block_size);
+  const DecodeWorkspace ws = decode_workspace_layout(key, batch, p);
+  if (workspace_bytes < ws.total) return STARKV_ERR_WORKSPACE;
+  char* wb = (char*)workspace;
+  const hipStream_t s = (hipStream_t)stream;
+  // the key scale folds into q~, the value scale into the split partials
+  hipError_t e = launch_qproj(key, q, U, batch, scale * k_scale, wb + ws.qt_off,
+                              TIME_DECODE_SPLIT, s);
+  if (e != hipSuccess) return STARKV_ERR_LAUNCH;
+  LatentFormat fmt;
+  fmt.fp8 = true;
+  fmt.k_scale = k_scale;
+  fmt.v_scale = v_scale;
+  e = launch_decode(key, p, wb + ws.qt_off, k_cache8, v_cache8, W, block_tables,
+                    max_blocks_per_seq, seq_lens, dims->num_blocks, batch,
+                    (float*)(wb + ws.ml_off), wb + ws.zp_off, out, fmt, s);
   return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
 }
 

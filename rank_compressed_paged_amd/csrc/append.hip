@@ -12,8 +12,9 @@
 // contiguous fp16 per lane), B is staged through LDS transposed so that each
 // lane again reads 8 contiguous values.  The next K step's loads are issued
 // before the current step's LDS barrier (which waits on LDS only).  The epilogue rounds to fp16
-// (nearest even) and writes slot_mapping[n]; negative or out-of-range slots
-// are skipped.  Layouts: k_cache [NB, H, 16, r_k], v_cache [NB, r_v, 16].
+// (nearest even), or to FP8 E4M3 codes of latent / scale for FP8 caches, and
+// writes slot_mapping[n]; negative or out-of-range slots are skipped.
+// Layouts: k_cache [NB, H, 16, r_k], v_cache [NB, r_v, 16].
 #include <stdlib.h>
 
 #include <type_traits>
@@ -29,11 +30,27 @@ struct AppendArgs {
   const half_t* U;  // [H, d, r_k]
   const half_t* W;  // [H*d, r_v]
   const int64_t* slots;
-  half_t* k_cache;
-  half_t* v_cache;
+  void* k_cache;    // fp16, or FP8 E4M3 codes when fp8
+  void* v_cache;
   int N, H, D, RK, RV, num_blocks;
   int tiles_m, v_tiles_n, k_tiles_n;
+  int fp8;               // store FP8 E4M3 codes of latent / scale
+  float k_scale, v_scale;
 };
+
+// One latent of the epilogue: fp16 rounded to nearest even, or the E4M3
+// code of acc / scale, clamped to +-448 first (saturation) and rounded to
+// nearest even by v_cvt_pk_fp8_f32.
+__device__ __forceinline__ void store_latent(const AppendArgs& a, bool is_v, size_t idx,
+                                             float acc) {
+  void* base = is_v ? a.v_cache : a.k_cache;
+  if (a.fp8) {
+    const float x = fminf(fmaxf(acc / (is_v ? a.v_scale : a.k_scale), -448.f), 448.f);
+    ((uint8_t*)base)[idx] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xff);
+  } else {
+    ((half_t*)base)[idx] = (half_t)acc;
+  }
+}
 
 constexpr int AT_M = 64, AT_N = 64, AT_K = 32, AT_LDS = AT_K + 8;
 
@@ -139,11 +156,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
       for (int nt = 0; nt < 2; ++nt) {
         const int n = n_base + wn * 32 + nt * 16 + col;
         if (n >= Ndim) continue;
-        const half_t val = (half_t)acc[mt][nt][r];
         if (is_v)
-          a.v_cache[((size_t)blk * a.RV + n) * 16 + off] = val;
+          store_latent(a, true, ((size_t)blk * a.RV + n) * 16 + off, acc[mt][nt][r]);
         else
-          a.k_cache[(((size_t)blk * a.H + h) * 16 + off) * a.RK + n] = val;
+          store_latent(a, false, (((size_t)blk * a.H + h) * 16 + off) * a.RK + n, acc[mt][nt][r]);
       }
     }
   }
@@ -280,7 +296,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void append_small_kernel(AppendAr
       if (slot < 0) continue;
       const int64_t blk = slot / 16;
       if (blk >= a.num_blocks) continue;
-      store(blk, (int)(slot % 16), o0 + o, (half_t)sum);
+      store(blk, (int)(slot % 16), o0 + o, sum);
     }
   };
 
@@ -293,14 +309,14 @@ __global__ __launch_bounds__(kSmallWaves * 64) void append_small_kernel(AppendAr
     int job = blockIdx.x;
     if constexpr ((RV / 16) % 32 == 0) job = (blockIdx.x % 8) * (RV / 128) + blockIdx.x / 8;
     const int f0 = job * 16;
-    run(VJ{}, a.v, HD, a.W, RV, f0, [&](int64_t blk, int off, int f, half_t val) {
-      a.v_cache[((size_t)blk * RV + f) * 16 + off] = val;
+    run(VJ{}, a.v, HD, a.W, RV, f0, [&](int64_t blk, int off, int f, float val) {
+      store_latent(a, true, ((size_t)blk * RV + f) * 16 + off, val);
     });
   } else {
     const int h = blockIdx.x - RV / 16;
     run(KJ{}, a.k + (size_t)h * D, HD, a.U + (size_t)h * D * RK, RK, 0,
-        [&](int64_t blk, int off, int r, half_t val) {
-          a.k_cache[(((size_t)blk * H + h) * 16 + off) * RK + r] = val;
+        [&](int64_t blk, int off, int r, float val) {
+          store_latent(a, false, (((size_t)blk * H + h) * 16 + off) * RK + r, val);
         });
   }
 }
@@ -462,11 +478,10 @@ __global__ __launch_bounds__(512) void append_tiled_kernel(AppendArgs a) {
     const int64_t blk = slot / 16;
     const int off = (int)(slot % 16);
     if (blk >= a.num_blocks) continue;
-    const half_t val = (half_t)acc[i];
     if (is_v)
-      a.v_cache[((size_t)blk * RV + nt * TT_N + n) * 16 + off] = val;
+      store_latent(a, true, ((size_t)blk * RV + nt * TT_N + n) * 16 + off, acc[i]);
     else
-      a.k_cache[(((size_t)blk * H + h) * 16 + off) * RK + n] = val;
+      store_latent(a, false, (((size_t)blk * H + h) * 16 + off) * RK + n, acc[i]);
   }
 }
 
@@ -481,16 +496,19 @@ static int append_variant() {
 
 hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const void* U,
                          const void* W, const int64_t* slots, int n_tokens, int num_blocks,
-                         void* k_cache, void* v_cache, hipStream_t st) {
+                         void* k_cache, void* v_cache, const LatentFormat& fmt, hipStream_t st) {
   if (n_tokens <= 0) return hipSuccess;
   AppendArgs a;
+  a.fp8 = fmt.fp8 ? 1 : 0;
+  a.k_scale = fmt.k_scale;
+  a.v_scale = fmt.v_scale;
   a.k = (const half_t*)k;
   a.v = (const half_t*)v;
   a.U = (const half_t*)U;
   a.W = (const half_t*)W;
   a.slots = slots;
-  a.k_cache = (half_t*)k_cache;
-  a.v_cache = (half_t*)v_cache;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
   a.N = n_tokens;
   a.H = s.H;
   a.D = s.d;

@@ -36,6 +36,8 @@
 //   * two register sets ping-pong: page p+1 is loaded while page p is used.
 //   * the main shape runs 16 waves (2 heads and 32 value features each, four
 //     waves per SIMD), which measured 1-1.5% faster than 8 waves.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -158,12 +160,49 @@ struct KeyCfg {
   static_assert(H % QG == 0 && (HPW % QG == 0 || QG % HPW == 0), "query groups must align with waves");
 };
 
-template <int H, int RK, int RV, int NW, int QG>
+// FP8 E4M3 codes to fp16: v_cvt_scalef32_pk_f16_fp8 with scale 1 turns the
+// low or the high two bytes of a word into two fp16 values (every E4M3 value
+// is exactly an fp16 value), two instructions per four codes.
+__device__ __forceinline__ half4 e4m3x4_to_half4(uint32_t w) {
+  typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+  const half2v lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  const half2v hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+  return half4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Page operands of one wave, as loaded: fp16, or FP8 codes (half the bytes,
+// turned into the same fp16 operands when used).
+template <int H, int RK, int RV, int NW, int QG, bool FP8>
 struct PageRegs {
   using C = DecodeCfg<H, RK, RV, NW>;
   typedef _Float16 kvec __attribute__((ext_vector_type(C::KC / 4)));
-  kvec k[KeyCfg<H, RK, RV, NW, QG>::KPW][C::NKC];
-  half4 v[C::FT];
+  typedef uint8_t k8 __attribute__((ext_vector_type(C::KC / 4)));
+  typedef uint8_t v8 __attribute__((ext_vector_type(4)));
+  using kraw = std::conditional_t<FP8, k8, kvec>;
+  using vraw = std::conditional_t<FP8, v8, half4>;
+  kraw k[KeyCfg<H, RK, RV, NW, QG>::KPW][C::NKC];
+  vraw v[C::FT];
+
+  __device__ __forceinline__ kvec key(int kk, int c) const {
+    if constexpr (FP8) {
+      if constexpr (C::KC / 4 == 8) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 w = __builtin_bit_cast(u32x2, k[kk][c]);
+        const half4 a = e4m3x4_to_half4(w[0]), b = e4m3x4_to_half4(w[1]);
+        return kvec{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      } else {
+        return e4m3x4_to_half4(__builtin_bit_cast(uint32_t, k[kk][c]));
+      }
+    } else {
+      return k[kk][c];
+    }
+  }
+  __device__ __forceinline__ half4 val(int ft) const {
+    if constexpr (FP8)
+      return e4m3x4_to_half4(__builtin_bit_cast(uint32_t, v[ft]));
+    else
+      return v[ft];
+  }
 };
 
 template <bool NT, typename T>
@@ -174,27 +213,32 @@ __device__ __forceinline__ T ld_page(const T* p) {
     return *p;
 }
 
-template <int H, int RK, int RV, int NW, int QG, bool NT>
-__device__ __forceinline__ void load_page(PageRegs<H, RK, RV, NW, QG>& pr,
-                                          const half_t* __restrict__ kc,
-                                          const half_t* __restrict__ vc, int blk, int w, int col,
-                                          int quad) {
+// Element type of the caches: fp16, or FP8 codes (same layouts, one byte).
+template <bool FP8>
+using latent_t = std::conditional_t<FP8, uint8_t, half_t>;
+
+template <int H, int RK, int RV, int NW, int QG, bool NT, bool FP8>
+__device__ __forceinline__ void load_page(PageRegs<H, RK, RV, NW, QG, FP8>& pr,
+                                          const latent_t<FP8>* __restrict__ kc,
+                                          const latent_t<FP8>* __restrict__ vc, int blk, int w,
+                                          int col, int quad) {
   using C = DecodeCfg<H, RK, RV, NW>;
   using K = KeyCfg<H, RK, RV, NW, QG>;
-  using kvec = typename PageRegs<H, RK, RV, NW, QG>::kvec;
+  using R = PageRegs<H, RK, RV, NW, QG, FP8>;
   // keys: key/value head (kv0 + kk), token row `col`, k chunk `quad`
   const int kv0 = w * C::HPW / QG;
-  const half_t* kb =
+  const latent_t<FP8>* kb =
       kc + (((size_t)blk * K::HKV + kv0) * BS + col) * RK + quad * (C::KC / 4);
 #pragma unroll
   for (int kk = 0; kk < K::KPW; ++kk)
 #pragma unroll
     for (int c = 0; c < C::NKC; ++c)
-      pr.k[kk][c] = ld_page<NT>((const kvec*)(kb + (size_t)kk * BS * RK + c * C::KC));
+      pr.k[kk][c] = ld_page<NT>((const typename R::kraw*)(kb + (size_t)kk * BS * RK + c * C::KC));
   // values: feature (w*FPW + ft*16 + col), tokens 4*quad .. 4*quad+3
-  const half_t* vb = vc + ((size_t)blk * RV + w * C::FPW + col) * BS + quad * 4;
+  const latent_t<FP8>* vb = vc + ((size_t)blk * RV + w * C::FPW + col) * BS + quad * 4;
 #pragma unroll
-  for (int ft = 0; ft < C::FT; ++ft) pr.v[ft] = ld_page<NT>((const half4*)(vb + (size_t)ft * 16 * BS));
+  for (int ft = 0; ft < C::FT; ++ft)
+    pr.v[ft] = ld_page<NT>((const typename R::vraw*)(vb + (size_t)ft * 16 * BS));
 }
 
 template <int H, int RK, int RV, int NW>
@@ -210,15 +254,15 @@ struct SplitState {
 // weight 0 and a zeroed value operand, so a fully masked page changes
 // nothing.  Keeping every page on the same path lets the compiler count the
 // prefetched loads exactly instead of draining them.
-template <int H, int RK, int RV, int NW, int QG>
+template <int H, int RK, int RV, int NW, int QG, bool FP8>
 __device__ __forceinline__ void process_page(
-    SplitState<H, RK, RV, NW>& st, PageRegs<H, RK, RV, NW, QG>& cur,
-    const typename PageRegs<H, RK, RV, NW, QG>::kvec (&qv)[DecodeCfg<H, RK, RV, NW>::NKC],
+    SplitState<H, RK, RV, NW>& st, PageRegs<H, RK, RV, NW, QG, FP8>& cur,
+    const typename PageRegs<H, RK, RV, NW, QG, FP8>::kvec (&qv)[DecodeCfg<H, RK, RV, NW>::NKC],
     half_t (*sP)[DecodeCfg<H, RK, RV, NW>::R16][BS], float (*sAlpha)[DecodeCfg<H, RK, RV, NW>::R16],
     int* sFlag, int p, int buf, int valid, int w, int col, int quad) {
   using C = DecodeCfg<H, RK, RV, NW>;
   using K = KeyCfg<H, RK, RV, NW, QG>;
-  using kvec = typename PageRegs<H, RK, RV, NW, QG>::kvec;
+  using kvec = typename PageRegs<H, RK, RV, NW, QG, FP8>::kvec;
   const kvec kzero = {};
   // B column col holds q~ of query head w*HPW + col, whose key/value head is
   // the wave's kk-th: the products for key page kk take only those columns
@@ -230,9 +274,9 @@ __device__ __forceinline__ void process_page(
     for (int c = 0; c < C::NKC; ++c) {
       const kvec bq = (my_kk == kk) ? qv[c] : kzero;
       if constexpr (C::KC == 32)
-        sacc = mfma16x16x32(cur.k[kk][c], bq, sacc);
+        sacc = mfma16x16x32(cur.key(kk, c), bq, sacc);
       else
-        sacc = mfma16x16x16(cur.k[kk][c], bq, sacc);
+        sacc = mfma16x16x16(cur.key(kk, c), bq, sacc);
     }
   }
   float sv[4];
@@ -281,7 +325,7 @@ __device__ __forceinline__ void process_page(
 #pragma unroll
   for (int ft = 0; ft < C::FT; ++ft) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    u32x2 bits = __builtin_bit_cast(u32x2, cur.v[ft]);
+    u32x2 bits = __builtin_bit_cast(u32x2, cur.val(ft));
     bits[0] &= m01;
     bits[1] &= m23;
     const half4 av = __builtin_bit_cast(half4, bits);
@@ -290,14 +334,15 @@ __device__ __forceinline__ void process_page(
   }
 }
 
-template <int H, int RK, int RV, int NW, int DEPTH, bool NT, int QG>
+template <int H, int RK, int RV, int NW, int DEPTH, bool NT, int QG, bool FP8>
 __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
-    const half_t* __restrict__ qt, const half_t* __restrict__ k_cache,
-    const half_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const half_t* __restrict__ qt, const latent_t<FP8>* __restrict__ k_cache,
+    const latent_t<FP8>* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ seq_lens, float* __restrict__ ml, half_t* __restrict__ zpart,
-    int max_blocks, int num_blocks, int pages_per_split, int num_splits, int split_stride) {
+    int max_blocks, int num_blocks, int pages_per_split, int num_splits, int split_stride,
+    float v_scale) {
   using C = DecodeCfg<H, RK, RV, NW>;
-  using kvec = typename PageRegs<H, RK, RV, NW, QG>::kvec;
+  using kvec = typename PageRegs<H, RK, RV, NW, QG, FP8>::kvec;
   __shared__ __attribute__((aligned(16))) half_t sP[2][C::R16][BS];
   __shared__ float sAlpha[2][C::R16];
   __shared__ int sFlag[2];  // page index whose softmax step moved a running max
@@ -327,8 +372,8 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
   if (p0 >= n_pages) return;
   const int p1 = min(p0 + pages_per_split, n_pages);
 
-  PageRegs<H, RK, RV, NW, QG> ring[DEPTH];
-  load_page<H, RK, RV, NW, QG, NT>(ring[0], k_cache, v_cache,
+  PageRegs<H, RK, RV, NW, QG, FP8> ring[DEPTH];
+  load_page<H, RK, RV, NW, QG, NT, FP8>(ring[0], k_cache, v_cache,
                                ((unsigned)blk0 < (unsigned)num_blocks) ? blk0 : 0, w, col, quad);
 
   // rows >= H are padding: P stays zero there, alpha one
@@ -372,16 +417,17 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
   // current page's matrix ops (and the waits they need) above that request.
 #pragma unroll
   for (int j = 1; j < DEPTH - 1; ++j)
-    load_page<H, RK, RV, NW, QG, NT>(ring[j], k_cache, v_cache, page_block(p0 + j), w, col, quad);
+    load_page<H, RK, RV, NW, QG, NT, FP8>(ring[j], k_cache, v_cache, page_block(p0 + j), w, col,
+                                          quad);
 
   for (int p = p0; p < p1; p += DEPTH) {
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {
-      load_page<H, RK, RV, NW, QG, NT>(ring[(j + DEPTH - 1) % DEPTH], k_cache, v_cache,
-                                       page_block(p + j + DEPTH - 1), w, col, quad);
+      load_page<H, RK, RV, NW, QG, NT, FP8>(ring[(j + DEPTH - 1) % DEPTH], k_cache, v_cache,
+                                            page_block(p + j + DEPTH - 1), w, col, quad);
       __builtin_amdgcn_sched_barrier(0);
-      process_page<H, RK, RV, NW, QG>(st, ring[j], qv, sP, sAlpha, sFlag, p + j,
-                                      (p + j - p0) & 1, page_valid(p + j), w, col, quad);
+      process_page<H, RK, RV, NW, QG, FP8>(st, ring[j], qv, sP, sAlpha, sFlag, p + j,
+                                           (p + j - p0) & 1, page_valid(p + j), w, col, quad);
     }
   }
 
@@ -402,7 +448,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     const int hr = rt * 16 + col;
     if (hr < H) {  // rows past H are padding
       const float lh = sL[hr];
-      const float inv = lh > 0.f ? 1.f / lh : 0.f;
+      const float inv = lh > 0.f ? v_scale / lh : 0.f;  // v_scale: FP8 value scale, else 1
 #pragma unroll
       for (int ft = 0; ft < C::FT; ++ft) {
         half4 zh;
@@ -750,16 +796,18 @@ hipError_t launch_upproj_tiled(const ShapeKey& s, const void* W, const void* z_t
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-template <int H, int D, int RK, int RV, int NW, int DEPTH, bool NT, int QG = 1>
+template <int H, int D, int RK, int RV, int NW, int DEPTH, bool NT, int QG = 1, bool FP8 = false>
 static hipError_t decode_instance(const DecodePlan& p, const void* qt, const void* k_cache,
                                   const void* v_cache, const void* W, const int32_t* block_tables,
                                   int max_blocks, const int32_t* seq_lens, int num_blocks,
-                                  int batch, float* ml, void* zpart, void* out, hipStream_t st) {
-  launch_hooked(TIME_DECODE_SPLIT, TIME_NONE, decode_split_kernel<H, RK, RV, NW, DEPTH, NT, QG>,
+                                  int batch, float* ml, void* zpart, void* out, float v_scale,
+                                  hipStream_t st) {
+  launch_hooked(TIME_DECODE_SPLIT, TIME_NONE,
+                decode_split_kernel<H, RK, RV, NW, DEPTH, NT, QG, FP8>,
                 dim3(p.num_splits, batch), dim3(NW * 64), st, (const half_t*)qt,
-                (const half_t*)k_cache, (const half_t*)v_cache, block_tables, seq_lens, ml,
-                (half_t*)zpart, max_blocks, num_blocks, p.pages_per_split, p.num_splits,
-                p.split_stride);
+                (const latent_t<FP8>*)k_cache, (const latent_t<FP8>*)v_cache, block_tables,
+                seq_lens, ml, (half_t*)zpart, max_blocks, num_blocks, p.pages_per_split,
+                p.num_splits, p.split_stride, v_scale);
   // merge + up-projection: TB sequences and NT threads per work group, CB
   // splits per request round (the planner picks all three; the split stride
   // is a multiple of CB times the split groups)
@@ -819,9 +867,20 @@ hipError_t launch_qproj(const ShapeKey& s, const void* q, const void* U, int n_t
 hipError_t launch_decode(const ShapeKey& s, const DecodePlan& p, const void* qt, const void* k_cache,
                          const void* v_cache, const void* W, const int32_t* block_tables,
                          int max_blocks, const int32_t* seq_lens, int num_blocks, int batch,
-                         float* ml, void* zpart, void* out, hipStream_t st) {
-#define STARKV_DECODE_ARGS \
-  p, qt, k_cache, v_cache, W, block_tables, max_blocks, seq_lens, num_blocks, batch, ml, zpart, out, st
+                         float* ml, void* zpart, void* out, const LatentFormat& fmt,
+                         hipStream_t st) {
+#define STARKV_DECODE_ARGS                                                                    \
+  p, qt, k_cache, v_cache, W, block_tables, max_blocks, seq_lens, num_blocks, batch, ml, zpart, \
+      out, fmt.fp8 ? fmt.v_scale : 1.f, st
+  if (fmt.fp8) {  // FP8 latents: the main shape (either head layout) and the tiny one
+    if (s.H == 32 && s.Hkv == 32 && s.d == 128 && s.rk == 64 && s.rv == 512)
+      return decode_instance<32, 128, 64, 512, 16, 2, false, 1, true>(STARKV_DECODE_ARGS);
+    if (s.H == 32 && s.Hkv == 8 && s.d == 128 && s.rk == 64 && s.rv == 512)
+      return decode_instance<32, 128, 64, 512, 16, 2, false, 4, true>(STARKV_DECODE_ARGS);
+    if (s.H == 4 && s.Hkv == 4 && s.d == 64 && s.rk == 16 && s.rv == 64)
+      return decode_instance<4, 64, 16, 64, 4, 2, false, 1, true>(STARKV_DECODE_ARGS);
+    return hipErrorInvalidValue;
+  }
   if (s.H == 32 && s.Hkv == 8 && s.d == 128 && s.rk == 64 && s.rv == 512)
     return decode_instance<32, 128, 64, 512, 16, 2, false, 4>(STARKV_DECODE_ARGS);
   if (s.H == 4 && s.Hkv == 2 && s.d == 64 && s.rk == 16 && s.rv == 64)

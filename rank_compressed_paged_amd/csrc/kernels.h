@@ -55,6 +55,13 @@ struct FitWorkspace {
       dv_off, dk_off, total;
 };
 
+// Storage of the latents: fp16, or FP8 E4M3 codes of latent / scale with one
+// scale per tensor (keys, values).
+struct LatentFormat {
+  bool fp8 = false;
+  float k_scale = 1.f, v_scale = 1.f;
+};
+
 bool shape_supported(const ShapeKey& s);
 DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int block_size);
 DecodeWorkspace decode_workspace_layout(const ShapeKey& s, int batch, const DecodePlan& p);
@@ -98,7 +105,7 @@ hipError_t launch_decode(const ShapeKey& s, const DecodePlan& p, const void* qt,
                          const void* k_cache, const void* v_cache, const void* W,
                          const int32_t* block_tables, int max_blocks, const int32_t* seq_lens,
                          int num_blocks, int batch, float* ml, void* zpart, void* out,
-                         hipStream_t st);
+                         const LatentFormat& fmt, hipStream_t st);
 
 // out[n, h, :] = W_h z[n, h, :] for the many tokens of a prefill call: z is
 // fp16, tiled in the A-operand order of the up-projection's 32x32x16
@@ -114,7 +121,7 @@ hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStre
 
 hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const void* U,
                          const void* W, const int64_t* slots, int n_tokens, int num_blocks,
-                         void* k_cache, void* v_cache, hipStream_t st);
+                         void* k_cache, void* v_cache, const LatentFormat& fmt, hipStream_t st);
 
 FitWorkspace fit_workspace_layout(const ShapeKey& s);
 

@@ -34,6 +34,7 @@ EXPORTED = [
     "starkv_prefill_attn", "starkv_set_timing_events", "starkv_decode_plan",
     "starkv_util_stream_read", "starkv_util_event_create", "starkv_util_event_destroy",
     "starkv_util_event_elapsed_ms", "starkv_fit_workspace_size", "starkv_fit_bases",
+    "starkv_append_fp8", "starkv_decode_attn_fp8",
 ]
 
 
@@ -90,6 +91,13 @@ _lib.starkv_fit_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(
 _lib.starkv_fit_bases.restype = _i32
 _lib.starkv_fit_bases.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp,
                                   _vp, _sz, _vp, _vp]
+_f32 = ctypes.c_float
+_lib.starkv_append_fp8.restype = _i32
+_lib.starkv_append_fp8.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _vp, _vp, _vp, _i32, _f32, _f32,
+                                   _vp, _vp, _vp]
+_lib.starkv_decode_attn_fp8.restype = _i32
+_lib.starkv_decode_attn_fp8.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                        _vp, _i32, _i32, _f32, _f32, _f32, _vp, _vp, _sz, _vp]
 _lib.starkv_set_timing_events.restype = _i32
 _lib.starkv_set_timing_events.argtypes = [_vp, _vp, _i32]
 
@@ -184,6 +192,45 @@ def append(k, v, U, W, slot_mapping, k_cache, v_cache, stream=None):
         int(N), _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"),
         _stream(stream))
     _check(st, "starkv_append")
+
+
+def append_fp8(k, v, U, W, slot_mapping, k_scale, v_scale, k_cache8, v_cache8, stream=None):
+    """append() into FP8 E4M3 caches (uint8 codes, same layouts)."""
+    dims = dims_of(k_cache8, v_cache8, U, W)
+    N = k.shape[0]
+    Hkv, d = dims.num_heads, dims.head_dim
+    st = _lib.starkv_append_fp8(
+        ctypes.byref(dims), _dev(k, torch.float16, "k", (N, Hkv, d)),
+        _dev(v, torch.float16, "v", (N, Hkv, d)), _dev(U, torch.float16, "U"),
+        _dev(W, torch.float16, "W"), _dev(slot_mapping, torch.int64, "slot_mapping", (N,)),
+        int(N), float(k_scale), float(v_scale), _dev(k_cache8, torch.uint8, "k_cache8"),
+        _dev(v_cache8, torch.uint8, "v_cache8"), _stream(stream))
+    _check(st, "starkv_append_fp8")
+
+
+def decode_attn_fp8(q, k_cache8, v_cache8, U, W, block_tables, seq_lens, max_seq_len, k_scale,
+                    v_scale, scale=None, out=None, workspace=None, stream=None):
+    """decode_attn() over FP8 E4M3 caches read as scale * value(code)."""
+    dims = dims_of(k_cache8, v_cache8, U, W, num_heads=q.shape[1])
+    B = q.shape[0]
+    H, d = dims.num_heads, dims.head_dim
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.float16, device=q.device)
+    need = decode_workspace_size(dims, B, max_seq_len)
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    st = _lib.starkv_decode_attn_fp8(
+        ctypes.byref(dims), _dev(q, torch.float16, "q", (B, H, d)),
+        _dev(k_cache8, torch.uint8, "k_cache8"), _dev(v_cache8, torch.uint8, "v_cache8"),
+        _dev(U, torch.float16, "U"), _dev(W, torch.float16, "W"),
+        _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
+        _dev(seq_lens, torch.int32, "seq_lens", (B,)), int(B), int(max_seq_len), float(scale),
+        float(k_scale), float(v_scale), _dev(out, torch.float16, "out", (B, H, d)),
+        _dev(workspace, torch.uint8, "workspace"), int(workspace.numel()), _stream(stream))
+    _check(st, "starkv_decode_attn_fp8")
+    return out
 
 
 def decode_attn(q, k_cache, v_cache, U, W, block_tables, seq_lens, max_seq_len, scale=None,

@@ -39,6 +39,16 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 FP16_NAN_BITS = 0x7E00
+E4M3_NAN_CODE = 0x7F   # OCP FP8 E4M3: S.1111.111
+
+
+def draw_e4m3_codes(rng, shape):
+    """Random FP8 E4M3 codes drawn as bit fields (no rounding involved):
+    exponent field 1..9 (magnitudes 2^-6 .. 15), any mantissa, either sign."""
+    exp = rng.integers(1, 10, size=shape)
+    man = rng.integers(0, 8, size=shape)
+    sign = rng.integers(0, 2, size=shape)
+    return ((sign << 7) | (exp << 3) | man).astype(np.uint8)
 
 
 @dataclass(frozen=True)
@@ -77,6 +87,9 @@ CONFIGS = {
     "gqa8_b64": dict(kind="decode", shape=GQA8, B=64, seq=("uniform", 4096, 8192), seed=7),
     "gqa8_prefill_b16": dict(kind="prefill", shape=GQA8, B=16, cached=4096, chunk=256, seed=8),
     "tiny_gqa": dict(kind="decode", shape=TINY_GQA, B=2, seq=("fixed", 256), seed=9),
+    "decode_b16_fp8": dict(kind="decode", shape=MAIN, B=16, seq=("fixed", 2048), seed=12, fp8=True),
+    "decode_b64_fp8": dict(kind="decode", shape=MAIN, B=64, seq=("uniform", 4096, 8192), seed=13,
+                           fp8=True),
     "lowrank_b16": dict(kind="decode", shape=LOWRANK, B=16, seq=("fixed", 2048), seed=10),
     "lowrank_prefill_b16": dict(kind="prefill", shape=LOWRANK, B=16, cached=4096, chunk=256,
                                 seed=11),
@@ -144,20 +157,30 @@ def scatter_tokens(k_cache, v_cache, table_row, t0, ck, cv, bs):
 
 
 def fill_cache(rng, shape: Shape, seq_lens, cache_lens=None, spare_blocks=1,
-               shuffle=True, keep_logical=False, extra_cols=0):
-    """Block tables for seq_lens tokens, latents drawn for the first cache_lens."""
+               shuffle=True, keep_logical=False, extra_cols=0, fp8=False):
+    """Block tables for seq_lens tokens, latents drawn for the first cache_lens
+    (fp16 N(0,1); or, with fp8, FP8 E4M3 codes from draw_e4m3_codes, unused
+    slots holding the NaN code)."""
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     cache_lens = seq_lens if cache_lens is None else np.asarray(cache_lens, dtype=np.int32)
     bs = shape.bs
     nblk = [(int(L) + bs - 1) // bs for L in seq_lens]
     bt, nb = build_block_tables(rng, nblk, spare_blocks, shuffle, extra_cols)
-    kc = _nan_f16((nb, shape.kv, bs, shape.r_k))
-    vc = _nan_f16((nb, shape.r_v, bs))
+    if fp8:
+        kc = np.full((nb, shape.kv, bs, shape.r_k), E4M3_NAN_CODE, dtype=np.uint8)
+        vc = np.full((nb, shape.r_v, bs), E4M3_NAN_CODE, dtype=np.uint8)
+    else:
+        kc = _nan_f16((nb, shape.kv, bs, shape.r_k))
+        vc = _nan_f16((nb, shape.r_v, bs))
     lck, lcv = [], []
     for b, L in enumerate(cache_lens):
         L = int(L)
-        ck = rng.standard_normal((L, shape.kv, shape.r_k), dtype=np.float32).astype(np.float16)
-        cv = rng.standard_normal((L, shape.r_v), dtype=np.float32).astype(np.float16)
+        if fp8:
+            ck = draw_e4m3_codes(rng, (L, shape.kv, shape.r_k))
+            cv = draw_e4m3_codes(rng, (L, shape.r_v))
+        else:
+            ck = rng.standard_normal((L, shape.kv, shape.r_k), dtype=np.float32).astype(np.float16)
+            cv = rng.standard_normal((L, shape.r_v), dtype=np.float32).astype(np.float16)
         if L:
             scatter_tokens(kc, vc, bt[b], 0, ck, cv, bs)
         if keep_logical:
@@ -177,6 +200,8 @@ class DecodeCase:
     scale: float
     seed: int = 0
     name: str = ""
+    k_scale: float = 1.0   # FP8 caches: per-tensor scales of the codes
+    v_scale: float = 1.0
 
     @property
     def B(self):
@@ -214,8 +239,10 @@ def draw_seq_lens(rng, B, seq):
 
 def make_decode_case(shape: Shape, seq_lens=None, B=None, seq=None, seed=0,
                      spare_blocks=1, shuffle=True, keep_logical=False,
-                     bases=None, extra_cols=0, name=""):
-    """One decode step: B sequences of seq_lens tokens, one query each."""
+                     bases=None, extra_cols=0, name="", fp8=False):
+    """One decode step: B sequences of seq_lens tokens, one query each.  With
+    fp8 the caches hold FP8 E4M3 codes read with k_scale 1/4, v_scale 1/8
+    (latent magnitudes up to about 4 and 2)."""
     rng = np.random.default_rng(seed)
     if bases is None:
         U, W = draw_bases(rng, shape)
@@ -224,9 +251,12 @@ def make_decode_case(shape: Shape, seq_lens=None, B=None, seq=None, seed=0,
     if seq_lens is None:
         seq_lens = draw_seq_lens(rng, B, seq)
     cache = fill_cache(rng, shape, seq_lens, spare_blocks=spare_blocks,
-                       shuffle=shuffle, keep_logical=keep_logical, extra_cols=extra_cols)
+                       shuffle=shuffle, keep_logical=keep_logical, extra_cols=extra_cols,
+                       fp8=fp8)
     q = rng.standard_normal((len(cache.seq_lens), shape.H, shape.d),
                             dtype=np.float32).astype(np.float16)
+    if fp8:
+        return DecodeCase(shape, U, W, cache, q, 1.0 / np.sqrt(shape.d), seed, name, 0.25, 0.125)
     return DecodeCase(shape, U, W, cache, q, 1.0 / np.sqrt(shape.d), seed, name)
 
 
@@ -326,7 +356,7 @@ def make_config(name: str, keep_logical=False):
         return make_fit_case(shape, cfg["N"], seed=cfg["seed"], name=name)
     if cfg["kind"] == "decode":
         return make_decode_case(shape, B=cfg["B"], seq=cfg["seq"], seed=cfg["seed"],
-                                keep_logical=keep_logical, name=name)
+                                keep_logical=keep_logical, name=name, fp8=cfg.get("fp8", False))
     B = cfg["B"]
     return make_prefill_case(shape, [cfg["cached"]] * B, [cfg["chunk"]] * B,
                              seed=cfg["seed"], keep_logical=keep_logical, name=name)

@@ -19,7 +19,7 @@ MISALIGNED = 0x10008
 def declared_symbols():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(starkv_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(starkv_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_match_header():
@@ -161,3 +161,24 @@ def test_fit_validation():
     # any shape within the limits, block size and page count unused
     odd = sk.make_dims(3, 192, 40, 100, 0, block_size=7)
     assert sk.fit_workspace_size(odd) >= (3 * 192) ** 2 * 4
+
+
+def test_fp8_validation():
+    d = _main_dims()
+    fa = sk.lib().starkv_append_fp8
+    assert fa(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.0, 1.0, FAKE, FAKE, None) == 7
+    assert fa(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1.0, float("inf"), FAKE, FAKE,
+              None) == 7
+    assert fa(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1.0, 1.0, None, FAKE, None) == 1
+    assert fa(ctypes.byref(d), None, None, None, None, None, 0, 1.0, 1.0, None, None, None) == 0
+    fd = sk.lib().starkv_decode_attn_fp8
+    need = sk.decode_workspace_size(d, 16, 2048)
+
+    def dec(dims=d, ks=0.5, vs=0.5, scale=0.088, wsb=need, q=FAKE):
+        return fd(ctypes.byref(dims), q, FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 16, 2048, scale,
+                  ks, vs, FAKE, FAKE, wsb, None)
+    assert dec(wsb=0) == 4
+    assert dec(ks=-1.0) == 7
+    assert dec(vs=float("nan")) == 7
+    assert dec(q=None) == 1
+    assert dec(dims=sk.make_dims(32, 128, 32, 256, 8)) == 3   # no FP8 instance for this profile
