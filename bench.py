@@ -197,18 +197,20 @@ def device_info():
             "hbm_gib": round(p.total_memory / 2**30, 1)}
 
 
-def prefill_leg(flush_fn, steps):
+def prefill_leg(flush_fn, steps, name="prefill_b16"):
     """Chunked prefill at 16 requests x (4096 cached + 256 new) tokens: the
     chunk's append (4096 tokens), then causal attention for the 4096 chunk
-    queries.  Reports time, algorithmic TFLOP/s and the fraction of the
-    dense fp16 MFMA peak for the attention kernel and for the append."""
+    queries (prefill_b16; prefill_b16_fp8 the same over FP8 caches).
+    Reports time, algorithmic TFLOP/s and the fraction of the dense fp16 MFMA
+    peak for the attention kernel and for the append."""
     import numpy as np
     import torch
     from rank_compressed_paged_amd import metrics
     from rank_compressed_paged_amd import starkv as sk
     from rank_compressed_paged_amd import workloads as wl
-    pc = wl.make_config("prefill_b16")
+    pc = wl.make_config(name)
     sh, c = pc.shape, pc.cache
+    fp8 = c.k_cache.dtype == np.uint8
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
     q, k_new, v_new = dev(pc.q), dev(pc.k_new), dev(pc.v_new)
     U, W = dev(pc.U), dev(pc.W)
@@ -222,11 +224,19 @@ def prefill_leg(flush_fn, steps):
     ws = sk.alloc_workspace(sk.prefill_workspace_size(dims, B, T, msl), "cuda")
     out = torch.empty((T, sh.H, sh.d), dtype=torch.float16, device="cuda")
 
-    def app():
-        sk.append(k_new, v_new, U, W, slots, kc, vc)   # same slots each time: idempotent
+    def app():   # same slots each time: idempotent
+        if fp8:
+            sk.append_fp8(k_new, v_new, U, W, slots, pc.k_scale, pc.v_scale, kc, vc)
+        else:
+            sk.append(k_new, v_new, U, W, slots, kc, vc)
 
     def attn():
-        sk.prefill_attn(q, qsl, mql, kc, vc, U, W, bt, sl, msl, pc.scale, out=out, workspace=ws)
+        if fp8:
+            sk.prefill_attn_fp8(q, qsl, mql, kc, vc, U, W, bt, sl, msl, pc.k_scale, pc.v_scale,
+                                pc.scale, out=out, workspace=ws)
+        else:
+            sk.prefill_attn(q, qsl, mql, kc, vc, U, W, bt, sl, msl, pc.scale, out=out,
+                            workspace=ws)
 
     app()
     for i in range(3):
@@ -247,7 +257,7 @@ def prefill_leg(flush_fn, steps):
     m = statistics.fmean
     tf = lambda f, ms: f / (ms * 1e-3) / 1e12
     return {
-        "workload": "prefill_b16", "requests": B, "cached": int(pc.cached_lens[0]),
+        "workload": name, "requests": B, "cached": int(pc.cached_lens[0]),
         "chunk": int(chunk[0]), "steps": n,
         "attn_call_ms": round(m(attn_ms), 4),
         "attn_call_tflops": round(tf(flops, m(attn_ms)), 1),
@@ -486,6 +496,7 @@ def run_bench(args):
     if not args.no_prefill:
         del ceil_sink
         res["prefill"] = prefill_leg(do_flush, args.steps)
+        res["prefill_fp8"] = prefill_leg(do_flush, args.steps, "prefill_b16_fp8")
     if not args.no_layouts:
         res["layouts"] = [decode_leg(n, do_flush, args.steps)
                           for n in ("gqa8_b16", "lowrank_b16", "decode_b16_fp8", "decode_b64_fp8")]

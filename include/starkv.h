@@ -213,6 +213,23 @@ starkv_status starkv_prefill_attn(const starkv_dims* dims, const void* q,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * starkv_prefill_attn over FP8 caches (see starkv_append_fp8): the same
+ * chunked-prefill attention on the latents scale * value(code), k_scale
+ * folded into q~ and v_scale into z; key codes become fp16 as they enter
+ * the kernel's LDS key ring, value codes before their products.  Instances
+ * and workspace as for starkv_decode_attn_fp8 / starkv_prefill_attn.
+ */
+starkv_status starkv_prefill_attn_fp8(const starkv_dims* dims, const void* q,
+                                      const int32_t* query_start_loc, int32_t total_q,
+                                      int32_t max_query_len, const void* k_cache8,
+                                      const void* v_cache8, const void* U, const void* W,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, int32_t batch,
+                                      int32_t max_seq_len, float scale, float k_scale,
+                                      float v_scale, void* out, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
  * Profiling aid: time one kernel of later calls with the hipEvent_t pair
  * `start` / `stop`.  `stop` is bound to the selected kernel's dispatch and
  * `start` to the dispatch just before it in the same call (the q projection),

@@ -23,7 +23,8 @@ bool shape_supported(const ShapeKey& s) {
 
 // The append sees only the key/value heads: it supports the key/value view
 // (Hkv, d, r_k, r_v) of every supported shape, whatever the query heads.
-// Decode over FP8 latents: the main shape (both head layouts) and the tiny one.
+// Decode and prefill over FP8 latents: the main shape (both head layouts) and
+// the tiny one.
 static bool fp8_decode_supported(const ShapeKey& s) {
   return (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512 && (s.Hkv == 32 || s.Hkv == 8)) ||
          (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64 && s.Hkv == 4);
@@ -430,7 +431,47 @@ starkv_status starkv_prefill_attn(const starkv_dims* dims, const void* q,
   if (e != hipSuccess) return STARKV_ERR_LAUNCH;
   e = launch_prefill(key, wb + ws.qt_off, query_start_loc, total_q, max_query_len, k_cache,
                      v_cache, W, block_tables, max_blocks_per_seq, seq_lens, dims->num_blocks,
-                     batch, (void*)(wb + ws.z_off), out, s);
+                     batch, (void*)(wb + ws.z_off), out, LatentFormat{}, s);
+  return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
+}
+
+starkv_status starkv_prefill_attn_fp8(const starkv_dims* dims, const void* q,
+                                      const int32_t* query_start_loc, int32_t total_q,
+                                      int32_t max_query_len, const void* k_cache8,
+                                      const void* v_cache8, const void* U, const void* W,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, int32_t batch,
+                                      int32_t max_seq_len, float scale, float k_scale,
+                                      float v_scale, void* out, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  ShapeKey key;
+  starkv_status st = check_dims(dims, &key);
+  if (st != STARKV_OK) return st;
+  if (!fp8_decode_supported(key)) return STARKV_ERR_UNSUPPORTED;
+  st = check_paging(batch, max_seq_len, max_blocks_per_seq, dims->block_size);
+  if (st != STARKV_OK) return st;
+  if (total_q < 0 || max_query_len < 0) return STARKV_ERR_DIMS;
+  if (total_q > 0 && max_query_len == 0) return STARKV_ERR_DIMS;
+  if (max_query_len > max_seq_len) return STARKV_ERR_DIMS;
+  if (!scale_ok(scale) || !scale_ok(k_scale) || !scale_ok(v_scale)) return STARKV_ERR_ARG;
+  if (batch == 0 || total_q == 0) return STARKV_OK;
+  st = check_ptrs({q, query_start_loc, k_cache8, v_cache8, U, W, block_tables, seq_lens, out,
+                   workspace});
+  if (st != STARKV_OK) return st;
+  const PrefillWorkspace ws = prefill_workspace_layout(key, total_q);
+  if (workspace_bytes < ws.total) return STARKV_ERR_WORKSPACE;
+  char* wb = (char*)workspace;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_qproj(key, q, U, total_q, scale * k_scale, wb + ws.qt_off,
+                              TIME_PREFILL_ATTN, s);
+  if (e != hipSuccess) return STARKV_ERR_LAUNCH;
+  LatentFormat fmt;
+  fmt.fp8 = true;
+  fmt.k_scale = k_scale;
+  fmt.v_scale = v_scale;
+  e = launch_prefill(key, wb + ws.qt_off, query_start_loc, total_q, max_query_len, k_cache8,
+                     v_cache8, W, block_tables, max_blocks_per_seq, seq_lens, dims->num_blocks,
+                     batch, (void*)(wb + ws.z_off), out, fmt, s);
   return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
 }
 

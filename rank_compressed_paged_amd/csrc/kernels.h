@@ -135,6 +135,6 @@ hipError_t launch_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl,
                           int max_query_len, const void* k_cache, const void* v_cache,
                           const void* W, const int32_t* block_tables, int max_blocks,
                           const int32_t* seq_lens, int num_blocks, int batch, void* z,
-                          void* out, hipStream_t st);
+                          void* out, const LatentFormat& fmt, hipStream_t st);
 
 }  // namespace starkv

@@ -97,8 +97,9 @@ struct PrefillCfg {
 struct PrefillArgs {
   const half_t* qt;  // [total_q, H, RK] fp16, pre-scaled
   const int32_t* qsl;
-  const half_t* k_cache;
-  const half_t* v_cache;
+  const void* k_cache;  // fp16, or FP8 E4M3 codes (same layouts)
+  const void* v_cache;
+  float v_scale;        // FP8: the value scale, folded into z; else 1
   const int32_t* block_tables;
   const int32_t* seq_lens;
   half_t* z;  // fp16, tiled [H][n_tb][RV/16][64][8], see launch_upproj_tiled
@@ -118,12 +119,28 @@ constexpr float kRaise = 8.f;           // lazy-rescale threshold (log2 units)
 //          the softmax's vector instructions interleaved between the products,
 //          3 as 1 with the step's loads issued after the products, 4 as 2
 //          with the step's loads interleaved between the products too
+// FP8 E4M3 codes to fp16 (exact), two codes per instruction.
+__device__ __forceinline__ half8 e4m3x8_to_half8(uint32_t w0, uint32_t w1) {
+  typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+  const half2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const half2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const half2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const half2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  return half8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 template <int H, int RK, int RV, int G, int MQ, int NW, int PPS, int DEPTH, int SCHED, bool KLDS,
-          int QG>
+          int QG, bool FP8>
 __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   static_assert(DEPTH >= 2 && DEPTH <= 3, "register ring of 2 or 3 steps");
   static_assert(PPS == 1 || PPS == 2, "one or two pages per step");
   static_assert(H % QG == 0, "query heads per key/value head");
+  static_assert(!FP8 || KLDS, "FP8 keys go through the LDS key ring");
+  // cache elements: fp16, or FP8 codes turned into fp16 where they are used
+  // (keys as they enter the LDS ring, values before their products)
+  using LT = std::conditional_t<FP8, uint8_t, half_t>;
+  const LT* k_cache = (const LT*)a.k_cache;
+  const LT* v_cache = (const LT*)a.v_cache;
   using C = PrefillCfg<H, RK, RV, G, MQ, NW>;
   constexpr int HKV = H / QG;  // key/value heads of a key page (query head h reads h / QG)
   typedef _Float16 kvec __attribute__((ext_vector_type(C::KC / 4)));
@@ -213,8 +230,26 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
 
   typedef kvec KSet[PPS][C::SUW][C::NKC];
   typedef half8 VSet[PPS][C::FTW];
+  typedef uint8_t v8x8 __attribute__((ext_vector_type(8)));
+  typedef std::conditional_t<FP8, v8x8, half8> VElem;  // one value operand as loaded
+  typedef VElem VRaw[PPS][C::FTW];
   KSet kr[KLDS ? 1 : DEPTH];  // ring of page operands in registers
-  VSet vr[DEPTH];
+  VRaw vr[DEPTH];
+  // value operands of a step as fp16
+  auto to_vset = [&](VSet& dst, const VRaw& src) {
+#pragma unroll
+    for (int pg = 0; pg < PPS; ++pg)
+#pragma unroll
+      for (int ft = 0; ft < C::FTW; ++ft) {
+        if constexpr (FP8) {
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          const u32x2 w = __builtin_bit_cast(u32x2, src[pg][ft]);
+          dst[pg][ft] = e4m3x8_to_half8(w[0], w[1]);
+        } else {
+          dst[pg][ft] = src[pg][ft];
+        }
+      }
+  };
   const int f_base = w * C::FTW * 32 + c32;  // feature of this lane in tile 0
   // per-lane element offsets inside one page (the page base is uniform, so
   // the loads take a scalar base plus a 32-bit vector offset)
@@ -236,28 +271,29 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
 #pragma unroll
     for (int pg = 0; pg < PPS; ++pg) {
       const int blk = ids[pg];
-      const half_t* kp = a.k_cache + (size_t)(blk < 0 ? 0 : blk) * (HKV * PBS * RK);
+      const half_t* kp = (const half_t*)a.k_cache + (size_t)(blk < 0 ? 0 : blk) * (HKV * PBS * RK);
 #pragma unroll
       for (int i = 0; i < C::SUW; ++i)
 #pragma unroll
         for (int c = 0; c < C::NKC; ++c) dst[pg][i][c] = *(const kvec*)(kp + k_off[i] + c * C::KC);
     }
   };
-  auto load_v = [&](VSet& dst, const StepIds& ids) {
+  auto load_v = [&](VRaw& dst, const StepIds& ids) {
 #pragma unroll
     for (int pg = 0; pg < PPS; ++pg) {
       const int blk = ids[pg];
-      const half_t* vp = a.v_cache + (size_t)(blk < 0 ? 0 : blk) * (RV * PBS);
+      const LT* vp = v_cache + (size_t)(blk < 0 ? 0 : blk) * (RV * PBS);
 #pragma unroll
       for (int ft = 0; ft < C::FTW; ++ft)
-        dst[pg][ft] = *(const half8*)(vp + v_off + ft * 32 * PBS);
+        dst[pg][ft] = *(const VElem*)(vp + v_off + ft * 32 * PBS);
     }
   };
 
   // KLDS staging: thread t copies 16-byte chunks of the step's key pages
   constexpr int KCH = G * PPS * PBS * RK / 8 / (NW * 64);  // chunks per thread
   static_assert(!KLDS || (KCH >= 1 && KCH * NW * 64 * 8 == G * PPS * PBS * RK), "key chunks");
-  half8 kst[KLDS ? KCH : 1];
+  typedef std::conditional_t<FP8, v8x8, half8> KElem;  // 8 key values as loaded
+  KElem kst[KLDS ? KCH : 1];
   auto kst_load = [&](const StepIds& ids) {
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
@@ -265,7 +301,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
       const int rc = c % (RK / 8), tok = (c / (RK / 8)) % PBS;
       const int pg = (c / (RK / 8 * PBS)) % PPS, hl = c / (RK / 8 * PBS * PPS);
       const int blk = ids[pg] < 0 ? 0 : ids[pg];
-      kst[j] = *(const half8*)(a.k_cache +
+      kst[j] = *(const KElem*)(k_cache +
                                (((size_t)blk * HKV + (g * G + hl) / QG) * PBS + tok) * RK + rc * 8);
     }
   };
@@ -275,7 +311,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
       const int c = tid + j * NW * 64;
       const int rc = c % (RK / 8), tok = (c / (RK / 8)) % PBS;
       const int pg = (c / (RK / 8 * PBS)) % PPS, hl = c / (RK / 8 * PBS * PPS);
-      *(half8*)&sK[kb][hl][pg][tok][rc * 8] = kst[j];
+      if constexpr (FP8) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 wk = __builtin_bit_cast(u32x2, kst[j]);
+        *(half8*)&sK[kb][hl][pg][tok][rc * 8] = e4m3x8_to_half8(wk[0], wk[1]);
+      } else {
+        *(half8*)&sK[kb][hl][pg][tok][rc * 8] = kst[j];
+      }
     }
   };
   // score products of the step whose keys are in LDS buffer kb
@@ -521,15 +563,17 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
     const bool vmask = !step_plain_values(id_c, s);
     const bool smask = !step_plain_scores(id_s, s + 1);
     if constexpr (SCHED >= 1) __builtin_amdgcn_sched_barrier(0);
+    VSet vcur;
+    to_vset(vcur, vr[PH]);
     if constexpr (SCHED == 4) {  // masks ahead of the interleaved region
-      if (vmask) mask_values(vr[PH], id_c, s);
-      value_products(false, vr[PH], id_c, s, buf);
+      if (vmask) mask_values(vcur, id_c, s);
+      value_products(false, vcur, id_c, s, buf);
       issue_loads();
     } else if constexpr (SCHED == 2) {  // masks ahead of the interleaved region
-      if (vmask) mask_values(vr[PH], id_c, s);
-      value_products(false, vr[PH], id_c, s, buf);
+      if (vmask) mask_values(vcur, id_c, s);
+      value_products(false, vcur, id_c, s, buf);
     } else {
-      value_products(vmask, vr[PH], id_c, s, buf);
+      value_products(vmask, vcur, id_c, s, buf);
     }
     if constexpr (SCHED == 3) {
       // the loads go out behind the products: the per-CU load path is the
@@ -599,7 +643,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
     const int r_j = j0 + row % MQ;
     if (r_j >= Cn) continue;
     const float lr = sL[row];
-    const float inv = lr > 0.f ? 1.f / lr : 0.f;
+    const float inv = lr > 0.f ? a.v_scale / lr : 0.f;
     // z tiled for the up-projection: [head][token / 32][feature / 16][lane][8]
     // with lane = token % 32 + 32 * ((feature / 8) % 2)
     const int tok = q_begin + r_j;
@@ -619,17 +663,19 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
 }
 
 template <int H, int D, int RK, int RV, int G, int MQ, int NW, int PPS, int DEPTH, int SCHED,
-          bool KLDS = false, int QG = 1>
+          bool KLDS = false, int QG = 1, bool FP8 = false>
 static hipError_t prefill_instance(const void* qt, const int32_t* qsl, int max_query_len,
                                    const void* k_cache, const void* v_cache, const void* W,
                                    const int32_t* block_tables, int max_blocks,
                                    const int32_t* seq_lens, int num_blocks, int batch,
-                                   int total_q, void* z, void* out, hipStream_t st) {
+                                   int total_q, void* z, void* out, float v_scale,
+                                   hipStream_t st) {
   PrefillArgs a;
   a.qt = (const half_t*)qt;
   a.qsl = qsl;
-  a.k_cache = (const half_t*)k_cache;
-  a.v_cache = (const half_t*)v_cache;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.v_scale = v_scale;
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.z = (half_t*)z;
@@ -641,7 +687,7 @@ static hipError_t prefill_instance(const void* qt, const int32_t* qsl, int max_q
   a.n_tb = (total_q + 31) / 32;
   const long wgs = (long)batch * a.n_qtiles * a.n_groups;
   launch_hooked(TIME_PREFILL_ATTN, TIME_NONE,
-                prefill_attn_kernel<H, RK, RV, G, MQ, NW, PPS, DEPTH, SCHED, KLDS, QG>,
+                prefill_attn_kernel<H, RK, RV, G, MQ, NW, PPS, DEPTH, SCHED, KLDS, QG, FP8>,
                 dim3((unsigned)wgs), dim3(NW * 64), st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -662,11 +708,20 @@ hipError_t launch_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl,
                           int max_query_len, const void* k_cache, const void* v_cache,
                           const void* W, const int32_t* block_tables, int max_blocks,
                           const int32_t* seq_lens, int num_blocks, int batch, void* z, void* out,
-                          hipStream_t st) {
+                          const LatentFormat& fmt, hipStream_t st) {
   if (batch <= 0 || total_q <= 0) return hipSuccess;
 #define STARKV_PREFILL_ARGS                                                                    \
   qt, qsl, max_query_len, k_cache, v_cache, W, block_tables, max_blocks, seq_lens, num_blocks, \
-      batch, total_q, z, out, st
+      batch, total_q, z, out, fmt.fp8 ? fmt.v_scale : 1.f, st
+  if (fmt.fp8) {  // FP8 latents: the main shape (either head layout) and the tiny one
+    if (s.H == 32 && s.Hkv == 32 && s.d == 128 && s.rk == 64 && s.rv == 512)
+      return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 3, 4, true, 1, true>(STARKV_PREFILL_ARGS);
+    if (s.H == 32 && s.Hkv == 8 && s.d == 128 && s.rk == 64 && s.rv == 512)
+      return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 3, 4, true, 4, true>(STARKV_PREFILL_ARGS);
+    if (s.H == 4 && s.Hkv == 4 && s.d == 64 && s.rk == 16 && s.rv == 64)
+      return prefill_instance<4, 64, 16, 64, 4, 16, 2, 2, 2, 1, true, 1, true>(STARKV_PREFILL_ARGS);
+    return hipErrorInvalidValue;
+  }
   if (s.H == 32 && s.Hkv == 8 && s.d == 128 && s.rk == 64 && s.rv == 512)
     return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 3, 4, true, 4>(STARKV_PREFILL_ARGS);
   if (s.H == 4 && s.Hkv == 2 && s.d == 64 && s.rk == 16 && s.rv == 64)

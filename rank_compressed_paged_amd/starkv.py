@@ -34,7 +34,7 @@ EXPORTED = [
     "starkv_prefill_attn", "starkv_set_timing_events", "starkv_decode_plan",
     "starkv_util_stream_read", "starkv_util_event_create", "starkv_util_event_destroy",
     "starkv_util_event_elapsed_ms", "starkv_fit_workspace_size", "starkv_fit_bases",
-    "starkv_append_fp8", "starkv_decode_attn_fp8",
+    "starkv_append_fp8", "starkv_decode_attn_fp8", "starkv_prefill_attn_fp8",
 ]
 
 
@@ -98,6 +98,10 @@ _lib.starkv_append_fp8.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _vp, _vp, _vp
 _lib.starkv_decode_attn_fp8.restype = _i32
 _lib.starkv_decode_attn_fp8.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                         _vp, _i32, _i32, _f32, _f32, _f32, _vp, _vp, _sz, _vp]
+_lib.starkv_prefill_attn_fp8.restype = _i32
+_lib.starkv_prefill_attn_fp8.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _i32, _i32, _vp, _vp,
+                                         _vp, _vp, _vp, _i32, _vp, _i32, _i32, _f32, _f32, _f32,
+                                         _vp, _vp, _sz, _vp]
 _lib.starkv_set_timing_events.restype = _i32
 _lib.starkv_set_timing_events.argtypes = [_vp, _vp, _i32]
 
@@ -316,6 +320,35 @@ def fit_bases(k, v, r_k, r_v, u0, w0, iters, U=None, W=None, workspace=None, inf
         _stream(stream))
     _check(st, "starkv_fit_bases")
     return U, W
+
+
+def prefill_attn_fp8(q, query_start_loc, max_query_len, k_cache8, v_cache8, U, W, block_tables,
+                     seq_lens, max_seq_len, k_scale, v_scale, scale=None, out=None,
+                     workspace=None, stream=None):
+    """prefill_attn() over FP8 E4M3 caches read as scale * value(code)."""
+    dims = dims_of(k_cache8, v_cache8, U, W, num_heads=q.shape[1])
+    T = q.shape[0]
+    B = seq_lens.shape[0]
+    H, d = dims.num_heads, dims.head_dim
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((T, H, d), dtype=torch.float16, device=q.device)
+    need = prefill_workspace_size(dims, B, T, max_seq_len)
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    st = _lib.starkv_prefill_attn_fp8(
+        ctypes.byref(dims), _dev(q, torch.float16, "q", (T, H, d)),
+        _dev(query_start_loc, torch.int32, "query_start_loc", (B + 1,)), int(T),
+        int(max_query_len), _dev(k_cache8, torch.uint8, "k_cache8"),
+        _dev(v_cache8, torch.uint8, "v_cache8"), _dev(U, torch.float16, "U"),
+        _dev(W, torch.float16, "W"), _dev(block_tables, torch.int32, "block_tables"),
+        int(block_tables.shape[1]), _dev(seq_lens, torch.int32, "seq_lens", (B,)), int(B),
+        int(max_seq_len), float(scale), float(k_scale), float(v_scale),
+        _dev(out, torch.float16, "out", (T, H, d)), _dev(workspace, torch.uint8, "workspace"),
+        int(workspace.numel()), _stream(stream))
+    _check(st, "starkv_prefill_attn_fp8")
+    return out
 
 
 def stream_read(buf, sink, stream=None):

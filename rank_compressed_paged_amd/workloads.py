@@ -90,6 +90,8 @@ CONFIGS = {
     "decode_b16_fp8": dict(kind="decode", shape=MAIN, B=16, seq=("fixed", 2048), seed=12, fp8=True),
     "decode_b64_fp8": dict(kind="decode", shape=MAIN, B=64, seq=("uniform", 4096, 8192), seed=13,
                            fp8=True),
+    "prefill_b16_fp8": dict(kind="prefill", shape=MAIN, B=16, cached=4096, chunk=256, seed=14,
+                            fp8=True),
     "lowrank_b16": dict(kind="decode", shape=LOWRANK, B=16, seq=("fixed", 2048), seed=10),
     "lowrank_prefill_b16": dict(kind="prefill", shape=LOWRANK, B=16, cached=4096, chunk=256,
                                 seed=11),
@@ -223,6 +225,8 @@ class PrefillCase:
     scale: float
     seed: int = 0
     name: str = ""
+    k_scale: float = 1.0            # FP8 caches: per-tensor scales of the codes
+    v_scale: float = 1.0
 
     @property
     def seq_lens(self):
@@ -262,9 +266,11 @@ def make_decode_case(shape: Shape, seq_lens=None, B=None, seq=None, seed=0,
 
 def make_prefill_case(shape: Shape, cached_lens, chunk_lens, seed=0,
                       spare_blocks=1, shuffle=True, keep_logical=False,
-                      bases=None, name=""):
+                      bases=None, name="", fp8=False):
     """One chunked-prefill step: request b has cached_lens[b] latent tokens and
-    appends chunk_lens[b] new full-precision tokens, then attends causally."""
+    appends chunk_lens[b] new full-precision tokens, then attends causally.
+    With fp8 the cached latents are FP8 E4M3 codes (k_scale 1/16, v_scale
+    1/16, so that the chunk's own projections also fit the format)."""
     rng = np.random.default_rng(seed)
     if bases is None:
         U, W = draw_bases(rng, shape)
@@ -275,7 +281,7 @@ def make_prefill_case(shape: Shape, cached_lens, chunk_lens, seed=0,
     total = cached_lens + chunk_lens
     cache = fill_cache(rng, shape, total, cache_lens=cached_lens,
                        spare_blocks=spare_blocks, shuffle=shuffle,
-                       keep_logical=keep_logical)
+                       keep_logical=keep_logical, fp8=fp8)
     T = int(chunk_lens.sum())
     dims = (T, shape.H, shape.d)
     kv_dims = (T, shape.kv, shape.d)
@@ -290,6 +296,9 @@ def make_prefill_case(shape: Shape, cached_lens, chunk_lens, seed=0,
         pos = cached_lens[b] + np.arange(chunk_lens[b])
         slots[qsl[b]:qsl[b + 1]] = (cache.block_tables[b, pos // bs].astype(np.int64) * bs
                                     + pos % bs)
+    if fp8:
+        return PrefillCase(shape, U, W, cache, cached_lens, k_new, v_new, q, slots, qsl,
+                           1.0 / np.sqrt(shape.d), seed, name, 1.0 / 16, 1.0 / 16)
     return PrefillCase(shape, U, W, cache, cached_lens, k_new, v_new, q, slots, qsl,
                        1.0 / np.sqrt(shape.d), seed, name)
 
@@ -359,4 +368,5 @@ def make_config(name: str, keep_logical=False):
                                 keep_logical=keep_logical, name=name, fp8=cfg.get("fp8", False))
     B = cfg["B"]
     return make_prefill_case(shape, [cfg["cached"]] * B, [cfg["chunk"]] * B,
-                             seed=cfg["seed"], keep_logical=keep_logical, name=name)
+                             seed=cfg["seed"], keep_logical=keep_logical, name=name,
+                             fp8=cfg.get("fp8", False))

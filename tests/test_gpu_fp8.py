@@ -145,3 +145,53 @@ def test_fp8_end_to_end_and_loss(sk):
     ma, rl = errors(out8.float().cpu().numpy(), out16.float().cpu().numpy())
     print(f"[loss] fp8 vs fp16 latents: max_abs={ma:.3e} rel_l2={rl:.3e}", flush=True)
     assert rl < 2.0 ** -4
+
+
+def _gpu_prefill_fp8(sk, case):
+    c = case.cache
+    tk, tv = dev(c.k_cache), dev(c.v_cache)
+    U, W = dev(case.U), dev(case.W)
+    sk.append_fp8(dev(case.k_new), dev(case.v_new), U, W, dev(case.slot_mapping), case.k_scale,
+                  case.v_scale, tk, tv)
+    chunk = np.diff(case.query_start_loc)
+    out = sk.prefill_attn_fp8(dev(case.q), dev(case.query_start_loc), int(chunk.max()), tk, tv,
+                              U, W, dev(c.block_tables), dev(c.seq_lens), int(c.seq_lens.max()),
+                              case.k_scale, case.v_scale, case.scale)
+    torch.cuda.synchronize()
+    return out, tk.cpu().numpy(), tv.cpu().numpy()
+
+
+def _oracle_prefill_fp8(case, kc8, vc8, rows=None):
+    return oracle.prefill(case.q, case.query_start_loc, oracle.dequantize_cache(kc8, case.k_scale),
+                          oracle.dequantize_cache(vc8, case.v_scale), case.U, case.W,
+                          case.cache.block_tables, case.cache.seq_lens, case.scale,
+                          request_indices=rows)
+
+
+@pytest.mark.parametrize("shape,cached,chunk", [
+    (wl.TINY, [20, 0, 7], [5, 16, 33]),
+    (wl.MAIN, [0, 15, 64], [1, 17, 70]),
+    (wl.GQA8, [37, 100], [20, 45]),
+], ids=["tiny", "main_edges", "gqa8"])
+def test_prefill_fp8(sk, shape, cached, chunk):
+    case = wl.make_prefill_case(shape, cached, chunk, seed=88, fp8=True)
+    note(f"fp8 prefill {shape} cached={cached} chunk={chunk}")
+    out, kc8, vc8 = _gpu_prefill_fp8(sk, case)
+    # attention over the GPU's caches, and end to end with the oracle's append
+    assert_parity(out, _oracle_prefill_fp8(case, kc8, vc8), "fp8 prefill (gpu caches)")
+    okc, ovc = oracle.append_fp8(case.k_new, case.v_new, case.U, case.W, case.slot_mapping,
+                                 case.k_scale, case.v_scale, case.cache.k_cache,
+                                 case.cache.v_cache)
+    assert_parity(out, _oracle_prefill_fp8(case, okc, ovc), "fp8 prefill (oracle caches)")
+
+
+def test_prefill_fp8_full_size_sampled(sk):
+    case = wl.make_config("prefill_b16_fp8")
+    note("fp8 prefill full config prefill_b16_fp8")
+    out, kc8, vc8 = _gpu_prefill_fp8(sk, case)
+    rows = [0, 15]
+    ref = _oracle_prefill_fp8(case, kc8, vc8, rows=rows)
+    sel = np.concatenate([np.arange(case.query_start_loc[r], case.query_start_loc[r + 1])
+                          for r in rows])
+    assert torch.isfinite(out.float()).all()
+    assert_parity(out[torch.from_numpy(sel).cuda()], ref[sel], "prefill_b16_fp8 sample")
