@@ -16,7 +16,8 @@ carries the step with its append, a streaming-read ceiling, the chunked
 prefill workload (16 requests x 4096 cached + 256 new tokens: attention and
 append, as TFLOP/s against the fp16 MFMA peak), decode at two other
 layouts (gqa8_b16: 32 query heads on 8 key/value heads; lowrank_b16: r_k
-32, r_v 256; decode_b16_fp8 and decode_b64_fp8: FP8 E4M3 latents), the bases
+32, r_v 256; decode_b16_fp8 and decode_b64_fp8: FP8 E4M3 latents), low-batch
+decode latency (batch 1-4: eager calls against a captured HIP graph), the bases
 fit from 16384
 K/V samples (its Gram kernel against the same peak), and the CPU leg, which
 times the fp64 oracle on a bounded sample of the decode workload on the host
@@ -101,6 +102,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill_b16 leg")
     ap.add_argument("--no-fit", action="store_true", help="skip the bases-fit leg")
+    ap.add_argument("--no-low-batch", action="store_true", help="skip the low-batch latency leg")
     ap.add_argument("--no-layouts", action="store_true",
                     help="skip the grouped-query and low-rank decode legs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU sample budget")
@@ -326,6 +328,65 @@ def decode_leg(name, flush_fn, steps):
     }
 
 
+def low_batch_leg(flush_fn, steps):
+    """Low-batch decode latency (batch 1, 2, 4 x 2048 tokens, main shape):
+    per step, after the Infinity-Cache flush and a device synchronisation,
+    host wall time from the call to its completion (synchronise), once with
+    the decode call made eagerly (three kernel launches from the host) and
+    once replaying a HIP graph that captured it; plus the GPU time of the
+    step from events on the stream."""
+    import numpy as np
+    import torch
+    from rank_compressed_paged_amd import starkv as sk
+    from rank_compressed_paged_amd import workloads as wl
+    rows = []
+    n = max(steps, 20)
+    for B in (1, 2, 4):
+        case = wl.make_decode_case(wl.MAIN, seq_lens=[2048] * B, seed=93)
+        c = case.cache
+        dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        q, kc, vc, U, W = dev(case.q), dev(c.k_cache), dev(c.v_cache), dev(case.U), dev(case.W)
+        bt, sl = dev(c.block_tables), dev(c.seq_lens)
+        dims = sk.dims_of(kc, vc, U, W)
+        ws = sk.alloc_workspace(sk.decode_workspace_size(dims, B, 2048), "cuda")
+        out = torch.empty((B, 32, 128), dtype=torch.float16, device="cuda")
+
+        def step():
+            sk.decode_attn(q, kc, vc, U, W, bt, sl, 2048, case.scale, out=out, workspace=ws)
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+
+        def wall(fn):
+            ts = []
+            for i in range(n):
+                flush_fn(i)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                fn()
+                torch.cuda.synchronize()
+                ts.append((time.perf_counter() - t0) * 1e6)
+            return statistics.median(ts)
+        eager_us = wall(step)
+        graph_us = wall(g.replay)
+        gpu_ms, _, _ = timed(step, n, flush_fn)
+        pps, ns = sk.decode_plan(dims, B, 2048)
+        rows.append({"batch": B, "seq_len": 2048, "plan": [pps, ns],
+                     "gpu_step_us": round(statistics.fmean(gpu_ms) * 1e3, 2),
+                     "eager_latency_us": round(eager_us, 2),
+                     "graph_latency_us": round(graph_us, 2)})
+        del g
+    return rows
+
+
 def fit_leg(steps):
     """The bases fit at 16384 K/V samples of the main shape, 8 iterations:
     the whole call, and its Gram-matrix kernel (algorithmic TFLOP/s of the
@@ -497,6 +558,8 @@ def run_bench(args):
         del ceil_sink
         res["prefill"] = prefill_leg(do_flush, args.steps)
         res["prefill_fp8"] = prefill_leg(do_flush, args.steps, "prefill_b16_fp8")
+    if not args.no_low_batch:
+        res["low_batch"] = low_batch_leg(do_flush, args.steps)
     if not args.no_layouts:
         res["layouts"] = [decode_leg(n, do_flush, args.steps)
                           for n in ("gqa8_b16", "lowrank_b16", "decode_b16_fp8", "decode_b64_fp8")]
