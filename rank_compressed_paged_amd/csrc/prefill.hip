@@ -65,11 +65,15 @@ __device__ __forceinline__ float16v mfma32x32x16(half8 a, half8 b, float16v c) {
 // the vector ALU instead of going through LDS.  With both operands equal,
 // permlane16_swap leaves lane l of one result and lane l^16 of the other
 // holding x[l] and x[l^16]; permlane32_swap does the same for l^32.
+// Maxima use the NaN-propagating maximum (v_maximum3_f32), which needs no
+// quieting of its inputs, unlike fmaxf: the scores it sees are finite or
+// -inf (masked), never NaN.
+__device__ __forceinline__ float fmax_nn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float quad_max(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = fmax_nn(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return fmax_nn(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float quad_sum(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -147,8 +151,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   constexpr int RING = 2 * kChunk;
   constexpr int TPS = PPS * PBS;  // tokens per step
   // P in the B-operand order of the 32x32x16 product:
-  // [buffer][page of the step][row tile][token half][row % 32][8 tokens]
-  __shared__ __attribute__((aligned(16))) half_t sP[2][PPS][C::RT][2][32][8];
+  // [buffer][page of the step][row tile][(row % 32) / 16][token half][row % 16][8 tokens].
+  // The softmax's half-waves (token halves 0 and 1 of 16 rows) then write
+  // adjacent 256-byte ranges, which the LDS takes without bank conflicts
+  // (with the halves 512 bytes apart a write took 1.4x as long); a
+  // fragment read stays four contiguous 256-byte ranges.
+  __shared__ __attribute__((aligned(16))) half_t sP[2][PPS][C::RT][2][2][16][8];
   // rescale factor of row rt*32 + r at sAlpha[buffer][r][rt]
   __shared__ __attribute__((aligned(16))) float sAlpha[2][32][C::RT];
   __shared__ float sL[C::R];
@@ -156,8 +164,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   // KLDS: key pages of three steps, [step % 3][head][page][token][r_k + pad],
   // each loaded once per work group and shared by the head's score waves
   // (under grouped-query attention each query head's slot holds its key/value
-  // head's page)
-  constexpr int LDKV = RK + 8;
+  // head's page).  The pad of 16 elements (a 160-byte row at r_k 64) makes
+  // the score products' reads (16 rows x four 16-byte chunks per wave)
+  // conflict-free on the gfx950 LDS; a 144-byte row took twice as long.
+  constexpr int LDKV = RK + 16;
   __shared__ __attribute__((aligned(16))) half_t sK[KLDS ? 3 : 1][G][PPS][PBS][LDKV];
 
   // ---- work decode (XCD-aware when the batch allows it)
@@ -189,12 +199,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   const int c32 = lane & 31, hf = lane >> 5;     // 32x32 layouts
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
 
-  // block id of a page (pages past the tile's range repeat its last page;
-  // ids outside the cache read as -1)
-  auto fetch_block = [&](int page) {
-    const int v = bt[min(page, n_pages - 1)];
-    return ((unsigned)v < (unsigned)a.num_blocks) ? v : -1;
-  };
+  // block id of a page as stored in the table (pages past the tile's range
+  // repeat its last page); the range check is made where an id is read back
+  // from the ring, on the scalar unit
+  auto fetch_block = [&](int page) { return bt[min(page, n_pages - 1)]; };
   if (tid < RING) sBlk[tid] = fetch_block(tid);
 
   // ---- this wave's score units: (head, 16 queries); lane column = query
@@ -258,8 +266,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   for (int i = 0; i < C::SUW; ++i) k_off[i] = ((su_h[i] / QG) * PBS + col) * RK + quad * (C::KC / 4);
   const int v_off = f_base * PBS + hf * 8;
 
+  // block id of a page, read back from the ring; ids outside the cache read
+  // as -1 (uniform, so the check runs on the scalar unit)
   auto block_of = [&](int page) {
-    return __builtin_amdgcn_readfirstlane(sBlk[page & (RING - 1)]);
+    const int v = __builtin_amdgcn_readfirstlane(sBlk[page & (RING - 1)]);
+    return ((unsigned)v < (unsigned)a.num_blocks) ? v : -1;
   };
   // block ids of the PPS pages of a step, read together (one LDS round trip)
   typedef int StepIds[PPS];
@@ -278,31 +289,50 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
         for (int c = 0; c < C::NKC; ++c) dst[pg][i][c] = *(const kvec*)(kp + k_off[i] + c * C::KC);
     }
   };
+  // value pages: a uniform page base plus this lane's fixed 32-bit byte
+  // offset (the scalar-base addressing form, no per-lane 64-bit arithmetic)
+  const uint32_t v_off_b = (uint32_t)v_off * (uint32_t)sizeof(LT);
   auto load_v = [&](VRaw& dst, const StepIds& ids) {
 #pragma unroll
     for (int pg = 0; pg < PPS; ++pg) {
       const int blk = ids[pg];
-      const LT* vp = v_cache + (size_t)(blk < 0 ? 0 : blk) * (RV * PBS);
+      const char* vp = (const char*)v_cache + (size_t)(blk < 0 ? 0 : blk) * (RV * PBS * sizeof(LT));
 #pragma unroll
       for (int ft = 0; ft < C::FTW; ++ft)
-        dst[pg][ft] = *(const VElem*)(vp + v_off + ft * 32 * PBS);
+        dst[pg][ft] = *(const VElem*)(vp + v_off_b + ft * 32 * PBS * sizeof(LT));
     }
   };
 
-  // KLDS staging: thread t copies 16-byte chunks of the step's key pages
+  // KLDS staging: thread t copies 16-byte chunks c = t + j*NW*64 of the
+  // step's key pages, ordered [head][page][token][r_k / 8].  When the chunks
+  // of one (head, page) fill whole waves, every wave's chunks share their
+  // head and page: the page base is then uniform and each lane adds a fixed
+  // offset.
   constexpr int KCH = G * PPS * PBS * RK / 8 / (NW * 64);  // chunks per thread
   static_assert(!KLDS || (KCH >= 1 && KCH * NW * 64 * 8 == G * PPS * PBS * RK), "key chunks");
+  constexpr int CPP = PBS * RK / 8;  // chunks per (head, page)
+  constexpr bool KUNI = (CPP % 64) == 0;
+  const int w_u = __builtin_amdgcn_readfirstlane(w);
   typedef std::conditional_t<FP8, v8x8, half8> KElem;  // 8 key values as loaded
   KElem kst[KLDS ? KCH : 1];
   auto kst_load = [&](const StepIds& ids) {
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
-      const int c = tid + j * NW * 64;
-      const int rc = c % (RK / 8), tok = (c / (RK / 8)) % PBS;
-      const int pg = (c / (RK / 8 * PBS)) % PPS, hl = c / (RK / 8 * PBS * PPS);
-      const int blk = ids[pg] < 0 ? 0 : ids[pg];
-      kst[j] = *(const KElem*)(k_cache +
-                               (((size_t)blk * HKV + (g * G + hl) / QG) * PBS + tok) * RK + rc * 8);
+      if constexpr (KUNI) {
+        const int cw = (w_u + j * NW) * 64;  // the wave's first chunk
+        const int pg = (cw / CPP) % PPS, hl = cw / (CPP * PPS);
+        const int blk = ids[pg] < 0 ? 0 : ids[pg];
+        const char* kp = (const char*)k_cache +
+                         (((size_t)blk * HKV + (g * G + hl) / QG) * PBS * RK) * sizeof(LT);
+        kst[j] = *(const KElem*)(kp + (uint32_t)((cw % CPP + lane) * 8 * sizeof(LT)));
+      } else {
+        const int c = tid + j * NW * 64;
+        const int rc = c % (RK / 8), tok = (c / (RK / 8)) % PBS;
+        const int pg = (c / (RK / 8 * PBS)) % PPS, hl = c / (RK / 8 * PBS * PPS);
+        const int blk = ids[pg] < 0 ? 0 : ids[pg];
+        kst[j] = *(const KElem*)(k_cache +
+                                 (((size_t)blk * HKV + (g * G + hl) / QG) * PBS + tok) * RK + rc * 8);
+      }
     }
   };
   auto kst_store = [&](int kb) {
@@ -356,14 +386,18 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   };
   // online softmax of step s's tokens; P and the rescale factors go to LDS
   // buffer `buf`.  A row's reference max moves only when the step's max
-  // exceeds it by more than kRaise.  `mask`: some token of the step is not
-  // visible to some row of the tile, or a page of the step is invalid.
-  // BRANCHFREE applies the masks with selects on every step (blk_ok: the
-  // step's pages have valid block ids), so the softmax forms one basic block
-  // with the products it is interleaved with.
-  auto softmax = [&](auto branchfree, bool mask, const bool (&blk_ok)[PPS],
-                     const float4v (&sacc)[PPS][C::SUW], int s, int buf) {
-    constexpr bool BRANCHFREE = decltype(branchfree)::value;
+  // exceeds it by more than kRaise.  MASKED: some token of the step may be
+  // invisible to some row of the tile, or a page of the step may have an
+  // invalid block id (blk_ok false); the masks are then applied with
+  // selects.  Each lane keeps its own part of the row sum (its tokens' P,
+  // as rounded to fp16 for the products, summed in fp32 by v_dot2): the four
+  // quads of a row share the reference max and the rescale factor, so their
+  // parts are added once, after the last step.
+  auto softmax = [&](auto masked, const bool (&blk_ok)[PPS], const float4v (&sacc)[PPS][C::SUW],
+                     int s, int buf) {
+    constexpr bool MASKED = decltype(masked)::value;
+    typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+    const half2v ones = {(half_t)1.f, (half_t)1.f};
 #pragma unroll
     for (int i = 0; i < C::SUW; ++i) {
       float sv[PPS][4];
@@ -371,7 +405,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
       for (int pg = 0; pg < PPS; ++pg)
 #pragma unroll
         for (int e = 0; e < 4; ++e) sv[pg][e] = sacc[pg][i][e];
-      auto apply_masks = [&]() {
+      if constexpr (MASKED) {
 #pragma unroll
         for (int pg = 0; pg < PPS; ++pg) {
           const int page = s * PPS + pg;
@@ -379,36 +413,30 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) sv[pg][e] = (e <= d) ? sv[pg][e] : -INFINITY;
         }
-      };
-      if constexpr (BRANCHFREE)
-        apply_masks();
-      else if (mask)  // uniform
-        apply_masks();
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int pg = 0; pg < PPS; ++pg)
-        mx = fmaxf(mx, fmaxf(fmaxf(sv[pg][0], sv[pg][1]), fmaxf(sv[pg][2], sv[pg][3])));
+        mx = fmax_nn(mx, fmax_nn(fmax_nn(sv[pg][0], sv[pg][1]), fmax_nn(sv[pg][2], sv[pg][3])));
       const float pm = quad_max(mx);
       const bool raise = pm > m_run[i] + kRaise;  // false while pm is -inf
       const float m_use = raise ? pm : m_run[i];
       const float alpha = raise ? __builtin_amdgcn_exp2f(m_run[i] - pm) : 1.f;  // 0 on the first raise
-      // m_use is -inf only while no key has been visible; every sv is then -inf
-      const float m_sub = (m_use == -INFINITY) ? 0.f : m_use;
-      float ps = 0.f;
+      // m_use is -inf only while no key has been visible (every sv is then
+      // -inf), which a step without masks never sees
+      const float m_sub = (MASKED && m_use == -INFINITY) ? 0.f : m_use;
+      float ps = l_run[i] * alpha;
       const int row = su_row[i];
 #pragma unroll
       for (int pg = 0; pg < PPS; ++pg) {
         half4 ph;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pr = __builtin_amdgcn_exp2f(sv[pg][e] - m_sub);  // exp2(-inf) = 0
-          ps += pr;
-          ph[e] = (half_t)pr;
-        }
-        *(half4*)&sP[buf][pg][row >> 5][quad >> 1][row & 31][(quad & 1) * 4] = ph;
+        for (int e = 0; e < 4; ++e) ph[e] = (half_t)__builtin_amdgcn_exp2f(sv[pg][e] - m_sub);  // exp2(-inf) = 0
+        ps = __builtin_amdgcn_fdot2(half2v{ph[0], ph[1]}, ones, ps, false);
+        ps = __builtin_amdgcn_fdot2(half2v{ph[2], ph[3]}, ones, ps, false);
+        *(half4*)&sP[buf][pg][row >> 5][(row >> 4) & 1][quad >> 1][row & 15][(quad & 1) * 4] = ph;
       }
-      ps = quad_sum(ps);
-      l_run[i] = l_run[i] * alpha + ps;
+      l_run[i] = ps;
       m_run[i] = m_use;
       sAlpha[buf][row & 31][row >> 5] = alpha;  // the four quads agree
     }
@@ -456,7 +484,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
       // first product, so the page waits for LDS once
       half8 pb[C::RT];
 #pragma unroll
-      for (int rt = 0; rt < C::RT; ++rt) pb[rt] = *(const half8*)&sP[buf][pg][rt][hf][c32][0];
+      for (int rt = 0; rt < C::RT; ++rt) pb[rt] = *(const half8*)&sP[buf][pg][rt][c32 >> 4][hf][c32 & 15][0];
       if constexpr (SCHED != 2) __builtin_amdgcn_sched_barrier(0);  // keep the reads together
 #pragma unroll
       for (int rt = 0; rt < C::RT; ++rt)
@@ -464,20 +492,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
         for (int ft = 0; ft < C::FTW; ++ft) acc[rt][ft] = mfma32x32x16(vv[pg][ft], pb[rt], acc[rt][ft]);
     }
   };
-  // every token of step s visible to every row, and every page valid
-  auto step_plain_scores = [&](const StepIds& ids, int s) {
-    bool ok = (s * PPS + PPS) * PBS - 1 <= lim_min;
-#pragma unroll
-    for (int pg = 0; pg < PPS; ++pg) ok = ok && ids[pg] >= 0;
-    return ok;
-  };
-  auto step_plain_values = [&](const StepIds& ids, int s) {
-    bool ok = (s * PPS + PPS) * PBS <= L;
-#pragma unroll
-    for (int pg = 0; pg < PPS; ++pg) ok = ok && ids[pg] >= 0;
-    return ok;
-  };
-
   // ---- prologue: block ids staged, keys of steps 0..DEPTH-1 and values of
   // steps 0..DEPTH-2 in flight, step 0 scored
   block_sync_lds();
@@ -520,7 +534,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
     bool ok0[PPS];
 #pragma unroll
     for (int pg = 0; pg < PPS; ++pg) ok0[pg] = ids0[pg] >= 0;
-    softmax(std::false_type{}, true, ok0, sacc, 0, 0);
+    softmax(std::true_type{}, ok0, sacc, 0, 0);
   }
   // nothing of the prologue stays in flight into the loop, so the loop's
   // wait counts depend on its own loads only
@@ -528,18 +542,23 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   block_sync_lds();
 
   // step s (register-ring phase PH = s % DEPTH): loads for the keys of step
-  // s+DEPTH and the values of step s+DEPTH-1, scores of step s+1, products of
+  // s+KA and the values of step s+DEPTH-1, scores of step s+1, products of
   // step s.  P and the rescale factors alternate between two LDS buffers.
-  auto step = [&](auto phase, int s) {
+  // win[k] holds the block ids of step s+k (k = 0..KA), carried from step to
+  // step so that each step reads only one new step's ids from the ring.
+  // MASKED: the step needs masks (a token of step s+1 beyond some row's
+  // causal limit or past the sequence, or an invalid block id in step s or
+  // s+1); most steps need none and skip the selects.
+  constexpr int KA = KLDS ? 3 : DEPTH;  // furthest step whose keys a step loads
+  auto step = [&](auto phase, auto masked, int s, const StepIds (&win)[KA + 1]) {
     constexpr int PH = decltype(phase)::value;
+    constexpr bool MASKED = decltype(masked)::value;
     int staged[PPS];
-    // block ids of every step this one touches, read together up front
-    StepIds id_c, id_s, id_v, id_k;  // steps s, s+1, s+DEPTH-1, s+DEPTH (KLDS: s+3)
-    ids_of(id_c, s);
-    ids_of(id_s, s + 1);
-    ids_of(id_v, s + DEPTH - 1);
-    ids_of(id_k, KLDS ? s + 3 : s + DEPTH);
-    // loads for the keys of step s+DEPTH and the values of step s+DEPTH-1
+    const StepIds& id_c = win[0];
+    const StepIds& id_s = win[1];
+    const StepIds& id_v = win[DEPTH - 1];
+    const StepIds& id_k = win[KA];
+    // loads for the keys of step s+KA and the values of step s+DEPTH-1
     // (their ring slots were consumed last step)
     auto issue_loads = [&]() {
 #pragma unroll
@@ -560,20 +579,18 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
       score_products(kr[(PH + 1) % DEPTH], sacc);
     const int buf = s & 1;
     rescale(buf);
-    const bool vmask = !step_plain_values(id_c, s);
-    const bool smask = !step_plain_scores(id_s, s + 1);
     if constexpr (SCHED >= 1) __builtin_amdgcn_sched_barrier(0);
     VSet vcur;
     to_vset(vcur, vr[PH]);
     if constexpr (SCHED == 4) {  // masks ahead of the interleaved region
-      if (vmask) mask_values(vcur, id_c, s);
+      if constexpr (MASKED) mask_values(vcur, id_c, s);
       value_products(false, vcur, id_c, s, buf);
       issue_loads();
     } else if constexpr (SCHED == 2) {  // masks ahead of the interleaved region
-      if (vmask) mask_values(vcur, id_c, s);
+      if constexpr (MASKED) mask_values(vcur, id_c, s);
       value_products(false, vcur, id_c, s, buf);
     } else {
-      value_products(vmask, vcur, id_c, s, buf);
+      value_products(MASKED, vcur, id_c, s, buf);
     }
     if constexpr (SCHED == 3) {
       // the loads go out behind the products: the per-CU load path is the
@@ -586,10 +603,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
     bool ok_s[PPS];
 #pragma unroll
     for (int pg = 0; pg < PPS; ++pg) ok_s[pg] = id_s[pg] >= 0;
-    if constexpr (SCHED == 2 || SCHED == 4)
-      softmax(std::true_type{}, smask, ok_s, sacc, s + 1, buf ^ 1);
-    else
-      softmax(std::false_type{}, smask, ok_s, sacc, s + 1, buf ^ 1);
+    softmax(masked, ok_s, sacc, s + 1, buf ^ 1);
     if constexpr (SCHED == 4) {
       // one P.c_v product, a few vector instructions and, every other
       // product, one of the step's loads: the loads drain through the
@@ -620,21 +634,57 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
     }
     block_sync_lds();
   };
+  // one step, then the id window moves on
+  StepIds win[KA + 1];
+#pragma unroll
+  for (int k = 0; k <= KA; ++k) ids_of(win[k], k);
+  auto run_step = [&](auto phase, auto masked, int s) {
+    StepIds next;
+    ids_of(next, s + KA + 1);
+    step(phase, masked, s, win);
+#pragma unroll
+    for (int k = 0; k < KA; ++k)
+#pragma unroll
+      for (int pg = 0; pg < PPS; ++pg) win[k][pg] = win[k + 1][pg];
+#pragma unroll
+    for (int pg = 0; pg < PPS; ++pg) win[KA][pg] = next[pg];
+  };
   // DEPTH steps per loop trip (a single path through its body, so the wait
-  // counts at its head see only the previous trip's loads); the tail after
+  // counts at its head see only the previous trip's loads).  Trips whose
+  // steps need no masks run first: every token up to step s+DEPTH visible to
+  // every row of the tile, and the ids in the window (steps s..s+KA, which
+  // cover the steps that the trip's steps read) valid.  The rest of the
+  // steps, from the first that may need a mask, run with masks.
+  auto trip_plain = [&](int s) {
+    bool ok = (s + DEPTH + 1) * TPS - 1 <= lim_min;
+#pragma unroll
+    for (int k = 0; k <= KA; ++k)
+#pragma unroll
+      for (int pg = 0; pg < PPS; ++pg) ok = ok && win[k][pg] >= 0;
+    return ok;
+  };
+  static_assert(KA >= DEPTH, "the window covers the scores of a trip's last step");
   int s = 0;
-  for (; s + DEPTH <= n_steps; s += DEPTH) {
-    step(std::integral_constant<int, 0>{}, s);
-    step(std::integral_constant<int, 1>{}, s + 1);
-    if constexpr (DEPTH > 2) step(std::integral_constant<int, 2 % DEPTH>{}, s + 2);
+  for (; s + DEPTH <= n_steps && trip_plain(s); s += DEPTH) {
+    run_step(std::integral_constant<int, 0>{}, std::false_type{}, s);
+    run_step(std::integral_constant<int, 1>{}, std::false_type{}, s + 1);
+    if constexpr (DEPTH > 2) run_step(std::integral_constant<int, 2 % DEPTH>{}, std::false_type{}, s + 2);
   }
-  if (s < n_steps) step(std::integral_constant<int, 0>{}, s);
+  for (; s + DEPTH <= n_steps; s += DEPTH) {
+    run_step(std::integral_constant<int, 0>{}, std::true_type{}, s);
+    run_step(std::integral_constant<int, 1>{}, std::true_type{}, s + 1);
+    if constexpr (DEPTH > 2) run_step(std::integral_constant<int, 2 % DEPTH>{}, std::true_type{}, s + 2);
+  }
+  if (s < n_steps) run_step(std::integral_constant<int, 0>{}, std::true_type{}, s);
   if constexpr (DEPTH > 2)
-    if (s + 1 < n_steps) step(std::integral_constant<int, 1>{}, s + 1);
+    if (s + 1 < n_steps) run_step(std::integral_constant<int, 1>{}, std::true_type{}, s + 1);
 
   // ---- normalise and write z rows of this tile
 #pragma unroll
-  for (int i = 0; i < C::SUW; ++i) sL[su_row[i]] = l_run[i];  // the four quads agree
+  for (int i = 0; i < C::SUW; ++i) {
+    const float l = quad_sum(l_run[i]);  // the four quads' parts
+    sL[su_row[i]] = l;                    // the four quads agree
+  }
   block_sync_lds();
 #pragma unroll
   for (int rt = 0; rt < C::RT; ++rt) {
