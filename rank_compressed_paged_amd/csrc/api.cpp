@@ -348,7 +348,7 @@ starkv_status starkv_decode_attn(const starkv_dims* dims, const void* q, const v
   if (workspace_bytes < ws.total) return STARKV_ERR_WORKSPACE;
   char* wb = (char*)workspace;
   const hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_qproj(key, q, U, batch, scale, wb + ws.qt_off, TIME_DECODE_SPLIT, s);
+  hipError_t e = launch_qproj(key, q, U, batch, scale, wb + ws.qt_off, TIME_DECODE_SPLIT, s, W);
   if (e != hipSuccess) return STARKV_ERR_LAUNCH;
   e = launch_decode(key, p, wb + ws.qt_off, k_cache, v_cache, W, block_tables,
                     max_blocks_per_seq, seq_lens, dims->num_blocks, batch,
@@ -380,7 +380,7 @@ starkv_status starkv_decode_attn_fp8(const starkv_dims* dims, const void* q,
   const hipStream_t s = (hipStream_t)stream;
   // the key scale folds into q~, the value scale into the split partials
   hipError_t e = launch_qproj(key, q, U, batch, scale * k_scale, wb + ws.qt_off,
-                              TIME_DECODE_SPLIT, s);
+                              TIME_DECODE_SPLIT, s, W);
   if (e != hipSuccess) return STARKV_ERR_LAUNCH;
   LatentFormat fmt;
   fmt.fp8 = true;

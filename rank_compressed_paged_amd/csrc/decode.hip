@@ -82,14 +82,37 @@ __device__ __forceinline__ half4 lds_read_tr16(const half_t* p) {
   return __builtin_bit_cast(half4, r);
 }
 
+// Rows y >= token_rows of the grid prefetch the up-projection basis for the
+// merge that ends the step: work group (h, token_rows + p) reads part p of
+// the W block of head h's key/value head.  Work groups are dealt to the 8
+// XCDs round robin, so with H a multiple of 8 it runs on XCD h % 8, where
+// the merge places head h's work groups; the block then waits in that XCD's
+// L2 (the split kernel's page reads are non-temporal) instead of in HBM.
+// The loaded words only feed a value stored through `sink`, which is null.
 template <int H, int D, int RK, int TPW, int QG>
 __global__ __launch_bounds__(256) void qproj_kernel(const half_t* __restrict__ q,
                                                     const half_t* __restrict__ U, int n_tokens,
-                                                    float qscale, half_t* __restrict__ qt) {
+                                                    float qscale, half_t* __restrict__ qt,
+                                                    int token_rows, const char* __restrict__ wpf,
+                                                    int wpf_head_bytes, int wpf_part_bytes,
+                                                    uint32_t* __restrict__ sink) {
   constexpr int LDU = RK + 8;  // halves per LDS row: 4 rows of a read group hit distinct banks
   __shared__ __attribute__((aligned(16))) half_t sU[D][LDU];
   const int h = blockIdx.x;
   const int tid = threadIdx.x;
+  if ((int)blockIdx.y >= token_rows) {  // whole work group, before any barrier
+    const char* p = wpf + (size_t)(h / QG) * wpf_head_bytes +
+                    (size_t)(blockIdx.y - token_rows) * wpf_part_bytes;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    uint32_t x = 0;
+#pragma unroll 8
+    for (int off = tid * 16; off < wpf_part_bytes; off += 256 * 16) {
+      const u32x4 v = *(const u32x4*)(p + off);
+      x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    if (sink) *sink = x;
+    return;
+  }
   const int lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
   auto load_q = [&](half8 (&b)[D / 32], int nb) {
@@ -834,32 +857,41 @@ static hipError_t decode_instance(const DecodePlan& p, const void* qt, const voi
   return hipGetLastError();
 }
 
+// W prefetch rows: each reads kPrefetchPart bytes of one head's W block
+constexpr int kPrefetchPart = 64 * 1024;
+
 template <int H, int D, int RK, int QG>
 static hipError_t qproj_instance(const void* q, const void* U, int n, float scale, void* qt,
-                                 int precedes, hipStream_t st) {
-  if (n >= 1024)  // many tokens: four 64-token tiles per work group
-    launch_hooked(TIME_NONE, precedes, qproj_kernel<H, D, RK, 4, QG>, dim3(H, (n + 255) / 256),
+                                 int precedes, const void* wpf, int rv, hipStream_t st) {
+  const int head_bytes = D * rv * (int)sizeof(half_t);
+  const bool pf = wpf != nullptr && H % 8 == 0 && head_bytes % kPrefetchPart == 0;
+  const int pf_rows = pf ? head_bytes / kPrefetchPart : 0;
+  if (n >= 1024) {  // many tokens: four 64-token tiles per work group
+    const int rows = (n + 255) / 256;
+    launch_hooked(TIME_NONE, precedes, qproj_kernel<H, D, RK, 4, QG>, dim3(H, rows + pf_rows),
                   dim3(256), st, (const half_t*)q, (const half_t*)U, n, scale * kLog2e,
-                  (half_t*)qt);
-  else
-    launch_hooked(TIME_NONE, precedes, qproj_kernel<H, D, RK, 1, QG>, dim3(H, (n + 63) / 64),
+                  (half_t*)qt, rows, (const char*)wpf, head_bytes, kPrefetchPart, (uint32_t*)nullptr);
+  } else {
+    const int rows = (n + 63) / 64;
+    launch_hooked(TIME_NONE, precedes, qproj_kernel<H, D, RK, 1, QG>, dim3(H, rows + pf_rows),
                   dim3(256), st, (const half_t*)q, (const half_t*)U, n, scale * kLog2e,
-                  (half_t*)qt);
+                  (half_t*)qt, rows, (const char*)wpf, head_bytes, kPrefetchPart, (uint32_t*)nullptr);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_qproj(const ShapeKey& s, const void* q, const void* U, int n_tokens, float scale,
-                        void* qt, int precedes, hipStream_t st) {
+                        void* qt, int precedes, hipStream_t st, const void* w_prefetch) {
   if (n_tokens <= 0) return hipSuccess;
   if (s.H == 32 && s.d == 128 && s.rk == 64) {
-    if (s.Hkv == 32) return qproj_instance<32, 128, 64, 1>(q, U, n_tokens, scale, qt, precedes, st);
-    if (s.Hkv == 8) return qproj_instance<32, 128, 64, 4>(q, U, n_tokens, scale, qt, precedes, st);
+    if (s.Hkv == 32) return qproj_instance<32, 128, 64, 1>(q, U, n_tokens, scale, qt, precedes, w_prefetch, s.rv, st);
+    if (s.Hkv == 8) return qproj_instance<32, 128, 64, 4>(q, U, n_tokens, scale, qt, precedes, w_prefetch, s.rv, st);
   }
   if (s.H == 32 && s.d == 128 && s.rk == 32 && s.Hkv == 32)
-    return qproj_instance<32, 128, 32, 1>(q, U, n_tokens, scale, qt, precedes, st);
+    return qproj_instance<32, 128, 32, 1>(q, U, n_tokens, scale, qt, precedes, w_prefetch, s.rv, st);
   if (s.H == 4 && s.d == 64 && s.rk == 16) {
-    if (s.Hkv == 4) return qproj_instance<4, 64, 16, 1>(q, U, n_tokens, scale, qt, precedes, st);
-    if (s.Hkv == 2) return qproj_instance<4, 64, 16, 2>(q, U, n_tokens, scale, qt, precedes, st);
+    if (s.Hkv == 4) return qproj_instance<4, 64, 16, 1>(q, U, n_tokens, scale, qt, precedes, w_prefetch, s.rv, st);
+    if (s.Hkv == 2) return qproj_instance<4, 64, 16, 2>(q, U, n_tokens, scale, qt, precedes, w_prefetch, s.rv, st);
   }
   return hipErrorInvalidValue;
 }

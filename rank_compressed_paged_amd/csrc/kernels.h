@@ -98,8 +98,11 @@ inline void launch_hooked(int which, int precedes, void (*kernel)(KArgs...), dim
 }
 
 // `precedes`: the hooked kernel that follows this launch in the call.
+// w_prefetch: the W that the step's merge will read (decode), fetched into
+// the L2 of the XCD that will use each head's block; null for none
 hipError_t launch_qproj(const ShapeKey& s, const void* q, const void* U, int n_tokens,
-                        float scale, void* qt, int precedes, hipStream_t st);
+                        float scale, void* qt, int precedes, hipStream_t st,
+                        const void* w_prefetch = nullptr);
 
 hipError_t launch_decode(const ShapeKey& s, const DecodePlan& p, const void* qt,
                          const void* k_cache, const void* v_cache, const void* W,
