@@ -473,9 +473,11 @@ def run_bench(args):
     kc_app = torch.zeros((nb_app, sh.H, sh.bs, sh.r_k), dtype=torch.float16, device="cuda")
     vc_app = torch.zeros((nb_app, sh.r_v, sh.bs), dtype=torch.float16, device="cuda")
     slots = torch.arange(B, dtype=torch.int64, device="cuda")
+    ws_app = sk.alloc_workspace(sk.append_workspace_size(sk.dims_of(kc_app, vc_app, t["U"], t["W"]), B),
+                                "cuda")
 
     def append_step():
-        sk.append(k_new, v_new, t["U"], t["W"], slots, kc_app, vc_app)
+        sk.append(k_new, v_new, t["U"], t["W"], slots, kc_app, vc_app, workspace=ws_app)
 
     # warmup (untimed)
     for i in range(args.warmup):

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define STARKV_ABI_VERSION 2
+#define STARKV_ABI_VERSION 3
 
 typedef enum {
   STARKV_OK = 0,
@@ -100,6 +100,16 @@ const char* starkv_status_string(int32_t status);
 int32_t starkv_shape_supported(const starkv_dims* dims);
 
 /*
+ * Workspace bytes (host out-parameter *bytes) that starkv_append and
+ * starkv_append_fp8 need for num_tokens tokens: the fp32 partial products of
+ * the value projection over 64-row slices of W, (Hkv*d/64) * num_tokens *
+ * r_v * 4 bytes, when num_tokens <= 64 (a decode step's tokens), and 0 for
+ * more tokens.  Returns a status.
+ */
+starkv_status starkv_append_workspace_size(const starkv_dims* dims, int32_t num_tokens,
+                                           size_t* bytes /* (host) */);
+
+/*
  * Append (README, "Kernel profiling breakdown": the write kernel's low-rank
  * projection and paged write).  For each n < num_tokens with
  * slot_mapping[n] >= 0, writes
@@ -114,10 +124,17 @@ int32_t starkv_shape_supported(const starkv_dims* dims);
  * (dims with num_heads = Hkv and num_kv_heads 0 describe the same append).
  *   slot_mapping  [num_tokens] int64
  *   k_cache, v_cache  updated in place
+ *   workspace     device scratch of at least starkv_append_workspace_size
+ *                 bytes, 16-byte aligned, owned by the caller; may be NULL
+ *                 (with workspace_bytes 0) when that size is 0.  A missing
+ *                 or short workspace returns STARKV_ERR_NULL or
+ *                 STARKV_ERR_WORKSPACE before anything is launched.  Calls
+ *                 that overlap in time must not share a workspace.
  */
 starkv_status starkv_append(const starkv_dims* dims, const void* k, const void* v, const void* U,
                             const void* W, const int64_t* slot_mapping, int32_t num_tokens,
-                            void* k_cache, void* v_cache, void* stream);
+                            void* k_cache, void* v_cache, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * FP8 latents (the quantised-latent variant that adjacent KV-cache work
@@ -135,7 +152,8 @@ starkv_status starkv_append(const starkv_dims* dims, const void* k, const void* 
 starkv_status starkv_append_fp8(const starkv_dims* dims, const void* k, const void* v,
                                 const void* U, const void* W, const int64_t* slot_mapping,
                                 int32_t num_tokens, float k_scale, float v_scale,
-                                void* k_cache8, void* v_cache8, void* stream);
+                                void* k_cache8, void* v_cache8, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * Workspace bytes (host out-parameter *bytes) that starkv_decode_attn needs

@@ -262,9 +262,33 @@ int32_t starkv_shape_supported(const starkv_dims* dims) {
   return check_dims(dims, &k) == STARKV_OK ? 1 : 0;
 }
 
+starkv_status starkv_append_workspace_size(const starkv_dims* dims, int32_t num_tokens,
+                                           size_t* bytes) {
+  ShapeKey key;
+  starkv_status st = check_dims(dims, &key, /*kv_view=*/true);
+  if (st != STARKV_OK) return st;
+  if (!bytes) return STARKV_ERR_NULL;
+  if (num_tokens < 0) return STARKV_ERR_DIMS;
+  const ShapeKey kv_key{key.Hkv, key.d, key.rk, key.rv, key.Hkv};
+  *bytes = append_workspace_bytes(kv_key, num_tokens);
+  return STARKV_OK;
+}
+
+// the workspace that an append of num_tokens tokens needs is present
+static starkv_status check_append_workspace(const ShapeKey& kv_key, int32_t num_tokens,
+                                            const void* workspace, size_t workspace_bytes) {
+  const size_t need = append_workspace_bytes(kv_key, num_tokens);
+  if (need == 0) return STARKV_OK;
+  if (!workspace) return STARKV_ERR_NULL;
+  if (workspace_bytes < need) return STARKV_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 15) != 0) return STARKV_ERR_ALIGN;
+  return STARKV_OK;
+}
+
 starkv_status starkv_append(const starkv_dims* dims, const void* k, const void* v, const void* U,
                             const void* W, const int64_t* slot_mapping, int32_t num_tokens,
-                            void* k_cache, void* v_cache, void* stream) {
+                            void* k_cache, void* v_cache, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   ShapeKey key;
   starkv_status st = check_dims(dims, &key, /*kv_view=*/true);
   if (st != STARKV_OK) return st;
@@ -274,16 +298,19 @@ starkv_status starkv_append(const starkv_dims* dims, const void* k, const void* 
   if (st != STARKV_OK) return st;
   // the append only sees key/value heads
   const ShapeKey kv_key{key.Hkv, key.d, key.rk, key.rv, key.Hkv};
+  st = check_append_workspace(kv_key, num_tokens, workspace, workspace_bytes);
+  if (st != STARKV_OK) return st;
   const hipError_t e = launch_append(kv_key, k, v, U, W, slot_mapping, num_tokens,
                                      dims->num_blocks, k_cache, v_cache, LatentFormat{},
-                                     (hipStream_t)stream);
+                                     workspace, (hipStream_t)stream);
   return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
 }
 
 starkv_status starkv_append_fp8(const starkv_dims* dims, const void* k, const void* v,
                                 const void* U, const void* W, const int64_t* slot_mapping,
                                 int32_t num_tokens, float k_scale, float v_scale,
-                                void* k_cache8, void* v_cache8, void* stream) {
+                                void* k_cache8, void* v_cache8, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   ShapeKey key;
   starkv_status st = check_dims(dims, &key, /*kv_view=*/true);
   if (st != STARKV_OK) return st;
@@ -293,12 +320,14 @@ starkv_status starkv_append_fp8(const starkv_dims* dims, const void* k, const vo
   st = check_ptrs({k, v, U, W, slot_mapping, k_cache8, v_cache8});
   if (st != STARKV_OK) return st;
   const ShapeKey kv_key{key.Hkv, key.d, key.rk, key.rv, key.Hkv};
+  st = check_append_workspace(kv_key, num_tokens, workspace, workspace_bytes);
+  if (st != STARKV_OK) return st;
   LatentFormat fmt;
   fmt.fp8 = true;
   fmt.k_scale = k_scale;
   fmt.v_scale = v_scale;
   const hipError_t e = launch_append(kv_key, k, v, U, W, slot_mapping, num_tokens,
-                                     dims->num_blocks, k_cache8, v_cache8, fmt,
+                                     dims->num_blocks, k_cache8, v_cache8, fmt, workspace,
                                      (hipStream_t)stream);
   return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
 }

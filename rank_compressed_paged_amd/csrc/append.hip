@@ -36,6 +36,7 @@ struct AppendArgs {
   int tiles_m, v_tiles_n, k_tiles_n;
   int fp8;               // store FP8 E4M3 codes of latent / scale
   float k_scale, v_scale;
+  float* part;           // few-token path: value partials [K / kSliceRows][N][RV] fp32
 };
 
 // One latent of the epilogue: fp16 rounded to nearest even, or the E4M3
@@ -167,17 +168,19 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 
 
 // ---------------------------------------------------------------------------
-// Few tokens (a decode step's append): the work is reading the bases, and a
-// contraction as long as H*d must not run as one serial chain.  One work
-// group per job:
-//   value job: 16 outputs f0..f0+15 of c_v over the whole K = H*d,
-//   key job:   one head, all r_k outputs over K = d.
-// The job's slice of W (or U_h) is staged once in LDS as it is in memory,
-// [k][output], and the B operand of v_mfma_f32_16x16x32_f16 (8 consecutive
-// k of one output per lane) comes through the transposing LDS read; A is 8
-// consecutive features of one token straight from memory.  The K range is split over
-// the waves, and the partial 16x16 tiles are summed through LDS (reusing
-// the staging area) before the fp16 rounding and the paged scatter.
+// Few tokens (a decode step's append): the work is reading the bases (W is
+// 4 MiB at the main shape), so it is spread over many work groups that each
+// read whole rows.  One work group per job:
+//   value slice j: rows kSliceRows*j .. of W (64 KiB at r_v 512), all r_v
+//     outputs: fp32 partial products of those rows go to the workspace, and
+//     append_reduce_kernel sums the slices, rounds and scatters;
+//   key job: one head, all r_k outputs over K = d, rounded and scattered
+//     here (the K range split over the waves, the partial tiles summed
+//     through LDS).
+// The job's rows of W (or U_h) are staged once in LDS as they are in
+// memory, [k][output], and the B operand of v_mfma_f32_16x16x32_f16 (8
+// consecutive k of one output per lane) comes through the transposing LDS
+// read; A is 8 consecutive features of one token straight from memory.
 // ---------------------------------------------------------------------------
 // ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane i
 // receives element i%4 of the 4-element (8-byte) chunk addressed by lane
@@ -193,6 +196,7 @@ __device__ __forceinline__ half4 lds_read_tr16(const half_t* p) {
 }
 
 constexpr int kSmallN = 64;            // tokens handled by the few-token kernel
+constexpr int kSliceRows = 64;         // rows of W per value slice
 constexpr int kSmallWaves = 16;
 
 template <int K, int OUT>
@@ -214,11 +218,11 @@ struct SmallJob {
 
 template <int H, int D, int RK, int RV>
 __global__ __launch_bounds__(kSmallWaves * 64) void append_small_kernel(AppendArgs a) {
-  using VJ = SmallJob<H * D, 16>;
   using KJ = SmallJob<D, RK>;
-  constexpr size_t kLds = VJ::lds_bytes(kSmallN / 16) > KJ::lds_bytes(kSmallN / 16)
-                              ? VJ::lds_bytes(kSmallN / 16)
-                              : KJ::lds_bytes(kSmallN / 16);
+  constexpr int LDW = RV + 16;  // halves per staged row of a value slice
+  constexpr size_t kSliceLds = (size_t)kSliceRows * LDW * 2;
+  constexpr size_t kLds = KJ::lds_bytes(kSmallN / 16) > kSliceLds ? KJ::lds_bytes(kSmallN / 16)
+                                                                   : kSliceLds;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
@@ -301,19 +305,55 @@ __global__ __launch_bounds__(kSmallWaves * 64) void append_small_kernel(AppendAr
   };
 
   const int HD = H * D;
-  if (blockIdx.x < RV / 16) {
-    // A value job reads 32 bytes of every 1 KiB row of W, so the four jobs
-    // of one 64-output group share each cache line.  Work groups are dealt
-    // to the 8 XCDs round robin (blockIdx % 8): give each XCD whole groups,
-    // so every line is fetched into one L2 once instead of into four.
-    int job = blockIdx.x;
-    if constexpr ((RV / 16) % 32 == 0) job = (blockIdx.x % 8) * (RV / 128) + blockIdx.x / 8;
-    const int f0 = job * 16;
-    run(VJ{}, a.v, HD, a.W, RV, f0, [&](int64_t blk, int off, int f, float val) {
-      store_latent(a, true, ((size_t)blk * RV + f) * 16 + off, val);
-    });
+  constexpr int NS = H * D / kSliceRows;  // value slices
+  if ((int)blockIdx.x < NS) {
+    // value slice j: rows kSliceRows*j .. of W staged in LDS as [k][output];
+    // partial[j][n][f] = sum over the slice's k of v[n][k] W[k][f]
+    const int j = blockIdx.x, k0 = j * kSliceRows;
+    half_t* sW = (half_t*)smem;
+    for (int c = tid; c < kSliceRows * (RV / 8); c += kSmallWaves * 64) {
+      const int k = c / (RV / 8), o = (c % (RV / 8)) * 8;
+      *(half8*)&sW[k * LDW + o] = *(const half8*)(a.W + (size_t)(k0 + k) * RV + o);
+    }
+    __syncthreads();
+    constexpr int OTW = RV / 16 / kSmallWaves;  // 16-output tiles per wave
+    static_assert(RV % (16 * kSmallWaves) == 0 || RV / 16 < kSmallWaves, "value tiles over the waves");
+    constexpr int NOT = OTW > 0 ? OTW : 1;
+    const bool active = OTW > 0 || w < RV / 16;
+    const int n_tiles = (a.N + 15) / 16;
+    if (active) {
+      for (int t = 0; t < n_tiles; ++t) {  // uniform
+        const int m = min(t * 16 + col, a.N - 1);
+        half8 av[kSliceRows / 32];
+#pragma unroll
+        for (int c = 0; c < kSliceRows / 32; ++c)
+          av[c] = *(const half8*)(a.v + (size_t)m * HD + k0 + c * 32 + quad * 8);
+#pragma unroll
+        for (int u = 0; u < NOT; ++u) {
+          const int ot = OTW > 0 ? w * OTW + u : w;
+          float4v acc = zero4();
+#pragma unroll
+          for (int c = 0; c < kSliceRows / 32; ++c) {
+            // B fragment: k c*32 + 8*quad .. +7 of output ot*16 + col through
+            // the transposing read (lane col addresses row col/4, outputs
+            // 4*(col%4) .. +3)
+            const half_t* bp = &sW[(c * 32 + quad * 8 + (col >> 2)) * LDW + ot * 16 + 4 * (col & 3)];
+            const half4 b0 = lds_read_tr16(bp);
+            const half4 b1 = lds_read_tr16(bp + 4 * LDW);
+            const half8 bq = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+            acc = mfma16x16x32(av[c], bq, acc);
+          }
+          // D[token 4*quad + r][output ot*16 + col]
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int n = t * 16 + quad * 4 + r;
+            if (n < a.N) a.part[((size_t)j * a.N + n) * RV + ot * 16 + col] = acc[r];
+          }
+        }
+      }
+    }
   } else {
-    const int h = blockIdx.x - RV / 16;
+    const int h = blockIdx.x - NS;
     run(KJ{}, a.k + (size_t)h * D, HD, a.U + (size_t)h * D * RK, RK, 0,
         [&](int64_t blk, int off, int r, float val) {
           store_latent(a, false, (((size_t)blk * H + h) * 16 + off) * RK + r, val);
@@ -321,6 +361,45 @@ __global__ __launch_bounds__(kSmallWaves * 64) void append_small_kernel(AppendAr
   }
 }
 
+// Few-token values, second half: the slices' partials summed, rounded and
+// written to the tokens' slots.  A work group takes 64 groups of four
+// adjacent outputs (16-byte reads, coalesced across threads) and splits the
+// NS slices into four runs of NS/4, one per thread group; the runs' sums
+// are added through LDS in run order, so the result is deterministic.  All
+// of a thread's reads are issued before its sum: one memory round trip.
+template <int RV, int NS>
+__global__ __launch_bounds__(256) void append_reduce_kernel(AppendArgs a) {
+  constexpr int SR = 4;        // slice runs
+  constexpr int RUN = NS / SR;
+  static_assert(NS % SR == 0 && RV % 4 == 0, "slice runs, output quads");
+  __shared__ float4v sSum[SR][64];
+  const int tid = threadIdx.x, sr = tid / 64, oq = tid % 64;
+  const int e4 = blockIdx.x * 64 + oq;  // output quad: token e4 / (RV/4), outputs 4*(e4 % (RV/4)) ..
+  const bool live = e4 < a.N * (RV / 4);
+  if (live) {
+    const float4v* src = (const float4v*)a.part + (size_t)sr * RUN * a.N * (RV / 4) + e4;
+    float4v p[RUN];
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) p[j] = src[(size_t)j * a.N * (RV / 4)];
+    float4v sum = zero4();
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) sum += p[j];
+    sSum[sr][oq] = sum;
+  }
+  __syncthreads();
+  if (!live || sr != 0) return;
+  float4v sum = sSum[0][oq];
+#pragma unroll
+  for (int r = 1; r < SR; ++r) sum += sSum[r][oq];
+  const int n = e4 / (RV / 4), f = 4 * (e4 % (RV / 4));
+  const int64_t slot = a.slots[n];
+  if (slot < 0) return;
+  const int64_t blk = slot / 16;
+  if (blk >= a.num_blocks) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    store_latent(a, true, ((size_t)blk * RV + f + i) * 16 + (int)(slot % 16), sum[i]);
+}
 
 // ---------------------------------------------------------------------------
 // Many tokens (a prefill chunk's append): C = A B with A the token rows (v, or
@@ -494,9 +573,25 @@ static int append_variant() {
   return v;
 }
 
+size_t append_workspace_bytes(const ShapeKey& s, int n_tokens) {
+  if (n_tokens <= 0 || n_tokens > kSmallN) return 0;
+  return (size_t)(s.H * s.d / kSliceRows) * n_tokens * s.rv * sizeof(float);
+}
+
+template <int H, int D, int RK, int RV>
+static void launch_few(const AppendArgs& a, hipStream_t st) {
+  constexpr int NS = H * D / kSliceRows;
+  static_assert((H * D) % kSliceRows == 0, "value slices");
+  launch_hooked(TIME_NONE, TIME_NONE, append_small_kernel<H, D, RK, RV>, dim3(NS + H),
+                dim3(kSmallWaves * 64), st, a);
+  launch_hooked(TIME_APPEND, TIME_NONE, append_reduce_kernel<RV, NS>,
+                dim3((unsigned)((a.N * (RV / 4) + 63) / 64)), dim3(256), st, a);
+}
+
 hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const void* U,
                          const void* W, const int64_t* slots, int n_tokens, int num_blocks,
-                         void* k_cache, void* v_cache, const LatentFormat& fmt, hipStream_t st) {
+                         void* k_cache, void* v_cache, const LatentFormat& fmt, void* workspace,
+                         hipStream_t st) {
   if (n_tokens <= 0) return hipSuccess;
   AppendArgs a;
   a.fp8 = fmt.fp8 ? 1 : 0;
@@ -515,31 +610,28 @@ hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const 
   a.RK = s.rk;
   a.RV = s.rv;
   a.num_blocks = num_blocks;
+  a.part = (float*)workspace;
   a.tiles_m = (n_tokens + AT_M - 1) / AT_M;
   a.v_tiles_n = (s.rv + AT_N - 1) / AT_N;
   a.k_tiles_n = (s.rk + AT_N - 1) / AT_N;
   const long jobs = (long)a.tiles_m * (a.v_tiles_n + (long)s.H * a.k_tiles_n);
   // a single launch: the start event is recorded on the stream just before it
   if (g_timing.which == TIME_APPEND && g_timing.start) hipEventRecord(g_timing.start, st);
-  if (n_tokens <= kSmallN) {
+  if (n_tokens <= kSmallN && workspace != nullptr) {
     if (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) {
-      launch_hooked(TIME_APPEND, TIME_NONE, append_small_kernel<32, 128, 64, 512>,
-                    dim3(512 / 16 + 32), dim3(kSmallWaves * 64), st, a);
+      launch_few<32, 128, 64, 512>(a, st);
       return hipGetLastError();
     }
     if (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64) {
-      launch_hooked(TIME_APPEND, TIME_NONE, append_small_kernel<4, 64, 16, 64>,
-                    dim3(64 / 16 + 4), dim3(kSmallWaves * 64), st, a);
+      launch_few<4, 64, 16, 64>(a, st);
       return hipGetLastError();
     }
     if (s.H == 8 && s.d == 128 && s.rk == 64 && s.rv == 512) {
-      launch_hooked(TIME_APPEND, TIME_NONE, append_small_kernel<8, 128, 64, 512>,
-                    dim3(512 / 16 + 8), dim3(kSmallWaves * 64), st, a);
+      launch_few<8, 128, 64, 512>(a, st);
       return hipGetLastError();
     }
     if (s.H == 32 && s.d == 128 && s.rk == 32 && s.rv == 256) {
-      launch_hooked(TIME_APPEND, TIME_NONE, append_small_kernel<32, 128, 32, 256>,
-                    dim3(256 / 16 + 32), dim3(kSmallWaves * 64), st, a);
+      launch_few<32, 128, 32, 256>(a, st);
       return hipGetLastError();
     }
   }

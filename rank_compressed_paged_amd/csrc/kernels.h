@@ -122,9 +122,14 @@ hipError_t launch_upproj_tiled(const ShapeKey& s, const void* W, const void* z_t
 // fold them into one word per work group, so nothing is optimised away.
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t st);
 
+// Workspace bytes of an append of n_tokens tokens (the few-token path's
+// value partials; 0 above that path's token limit).
+size_t append_workspace_bytes(const ShapeKey& s, int n_tokens);
+
 hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const void* U,
                          const void* W, const int64_t* slots, int n_tokens, int num_blocks,
-                         void* k_cache, void* v_cache, const LatentFormat& fmt, hipStream_t st);
+                         void* k_cache, void* v_cache, const LatentFormat& fmt, void* workspace,
+                         hipStream_t st);
 
 FitWorkspace fit_workspace_layout(const ShapeKey& s);
 

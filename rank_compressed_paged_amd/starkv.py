@@ -30,6 +30,7 @@ STATUS = {
 }
 EXPORTED = [
     "starkv_abi_version", "starkv_status_string", "starkv_shape_supported", "starkv_append",
+    "starkv_append_workspace_size",
     "starkv_decode_workspace_size", "starkv_decode_attn", "starkv_prefill_workspace_size",
     "starkv_prefill_attn", "starkv_set_timing_events", "starkv_decode_plan",
     "starkv_util_stream_read", "starkv_util_event_create", "starkv_util_event_destroy",
@@ -62,7 +63,10 @@ _lib.starkv_status_string.argtypes = [_i32]
 _lib.starkv_shape_supported.restype = _i32
 _lib.starkv_shape_supported.argtypes = [ctypes.POINTER(Dims)]
 _lib.starkv_append.restype = _i32
-_lib.starkv_append.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]
+_lib.starkv_append.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
+                               _sz, _vp]
+_lib.starkv_append_workspace_size.restype = _i32
+_lib.starkv_append_workspace_size.argtypes = [ctypes.POINTER(Dims), _i32, ctypes.POINTER(_sz)]
 _lib.starkv_decode_workspace_size.restype = _i32
 _lib.starkv_decode_workspace_size.argtypes = [ctypes.POINTER(Dims), _i32, _i32, ctypes.POINTER(_sz)]
 _lib.starkv_decode_plan.restype = _i32
@@ -94,7 +98,7 @@ _lib.starkv_fit_bases.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _i32, _vp, _vp
 _f32 = ctypes.c_float
 _lib.starkv_append_fp8.restype = _i32
 _lib.starkv_append_fp8.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _vp, _vp, _vp, _i32, _f32, _f32,
-                                   _vp, _vp, _vp]
+                                   _vp, _vp, _vp, _sz, _vp]
 _lib.starkv_decode_attn_fp8.restype = _i32
 _lib.starkv_decode_attn_fp8.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                         _vp, _i32, _i32, _f32, _f32, _f32, _vp, _vp, _sz, _vp]
@@ -184,31 +188,52 @@ def alloc_workspace(nbytes, device):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def append(k, v, U, W, slot_mapping, k_cache, v_cache, stream=None):
+def append_workspace_size(dims, num_tokens):
+    out = _sz(0)
+    _check(_lib.starkv_append_workspace_size(ctypes.byref(dims), int(num_tokens), ctypes.byref(out)),
+           "starkv_append_workspace_size")
+    return int(out.value)
+
+
+def _append_workspace(dims, N, workspace, device):
+    """(pointer, bytes) of the append workspace: the given one, or a new
+    allocation when the call needs one and none was given."""
+    need = append_workspace_size(dims, N)
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = alloc_workspace(need, device)
+    return _dev(workspace, torch.uint8, "workspace"), int(workspace.numel())
+
+
+def append(k, v, U, W, slot_mapping, k_cache, v_cache, workspace=None, stream=None):
     """Project k, v [N, Hkv, d] to latents and write them to slot_mapping [N] (int64)."""
     dims = dims_of(k_cache, v_cache, U, W)
     N = k.shape[0]
     H, d = dims.num_heads, dims.head_dim
+    ws, ws_bytes = _append_workspace(dims, N, workspace, k.device)
     st = _lib.starkv_append(
         ctypes.byref(dims), _dev(k, torch.float16, "k", (N, H, d)),
         _dev(v, torch.float16, "v", (N, H, d)), _dev(U, torch.float16, "U"),
         _dev(W, torch.float16, "W"), _dev(slot_mapping, torch.int64, "slot_mapping", (N,)),
         int(N), _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"),
-        _stream(stream))
+        ws, ws_bytes, _stream(stream))
     _check(st, "starkv_append")
 
 
-def append_fp8(k, v, U, W, slot_mapping, k_scale, v_scale, k_cache8, v_cache8, stream=None):
+def append_fp8(k, v, U, W, slot_mapping, k_scale, v_scale, k_cache8, v_cache8, workspace=None,
+               stream=None):
     """append() into FP8 E4M3 caches (uint8 codes, same layouts)."""
     dims = dims_of(k_cache8, v_cache8, U, W)
     N = k.shape[0]
     Hkv, d = dims.num_heads, dims.head_dim
+    ws, ws_bytes = _append_workspace(dims, N, workspace, k.device)
     st = _lib.starkv_append_fp8(
         ctypes.byref(dims), _dev(k, torch.float16, "k", (N, Hkv, d)),
         _dev(v, torch.float16, "v", (N, Hkv, d)), _dev(U, torch.float16, "U"),
         _dev(W, torch.float16, "W"), _dev(slot_mapping, torch.int64, "slot_mapping", (N,)),
         int(N), float(k_scale), float(v_scale), _dev(k_cache8, torch.uint8, "k_cache8"),
-        _dev(v_cache8, torch.uint8, "v_cache8"), _stream(stream))
+        _dev(v_cache8, torch.uint8, "v_cache8"), ws, ws_bytes, _stream(stream))
     _check(st, "starkv_append_fp8")
 
 

@@ -31,7 +31,7 @@ def test_exports_match_header():
 
 
 def test_version_and_status_strings():
-    assert sk.abi_version() == 2
+    assert sk.abi_version() == 3
     for s in range(0, 8):
         assert sk.lib().starkv_status_string(s)
     assert sk.lib().starkv_status_string(99) == b"unknown status"
@@ -84,17 +84,41 @@ def test_decode_validation():
 def test_append_validation():
     d = _main_dims()
     f = sk.lib().starkv_append
-    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, FAKE, None) == 2
-    assert f(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None) == 1
-    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, MISALIGNED, FAKE, 4, FAKE, FAKE, None) == 5
-    assert f(ctypes.byref(d), None, None, None, None, None, 0, None, None, None) == 0
+    ws = sk.append_workspace_size(d, 4)
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, FAKE, FAKE, ws, None) == 2
+    assert f(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, ws, None) == 1
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, MISALIGNED, FAKE, 4, FAKE, FAKE, FAKE, ws,
+             None) == 5
+    assert f(ctypes.byref(d), None, None, None, None, None, 0, None, None, None, 0, None) == 0
+    # the few-token path needs its workspace: missing, short or misaligned
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None, 0, None) == 1
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, ws - 1,
+             None) == 4
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, MISALIGNED, ws,
+             None) == 5
     # the append only sees key/value heads: the 8-head view of the grouped
     # shape is accepted, an unknown head count is not
     kv8 = sk.make_dims(8, 128, 64, 512, 8)
-    assert f(ctypes.byref(kv8), None, None, None, None, None, 0, None, None, None) == 0
-    assert f(ctypes.byref(kv8), FAKE, None, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None) == 1
+    assert f(ctypes.byref(kv8), None, None, None, None, None, 0, None, None, None, 0, None) == 0
+    assert f(ctypes.byref(kv8), FAKE, None, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, ws, None) == 1
     kv16 = sk.make_dims(16, 128, 64, 512, 8)
-    assert f(ctypes.byref(kv16), FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None) == 3
+    assert f(ctypes.byref(kv16), FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, ws,
+             None) == 3
+
+
+def test_append_workspace_size():
+    """fp32 partials of the value projection over 64-row slices of W for up to
+    64 tokens, nothing beyond."""
+    d = _main_dims()
+    assert sk.append_workspace_size(d, 16) == (32 * 128 // 64) * 16 * 512 * 4
+    assert sk.append_workspace_size(d, 64) == (32 * 128 // 64) * 64 * 512 * 4
+    assert sk.append_workspace_size(d, 65) == 0
+    assert sk.append_workspace_size(d, 0) == 0
+    # grouped-query caches: only the key/value heads enter
+    assert sk.append_workspace_size(sk.make_dims(32, 128, 64, 512, 8, num_kv_heads=8), 16) == 16 * 16 * 512 * 4
+    assert sk.lib().starkv_append_workspace_size(ctypes.byref(d), 4, None) == 1
+    assert sk.lib().starkv_append_workspace_size(ctypes.byref(d), -1,
+                                                 ctypes.byref(ctypes.c_size_t())) == 2
 
 
 def test_prefill_validation():
@@ -166,11 +190,17 @@ def test_fit_validation():
 def test_fp8_validation():
     d = _main_dims()
     fa = sk.lib().starkv_append_fp8
-    assert fa(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.0, 1.0, FAKE, FAKE, None) == 7
-    assert fa(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1.0, float("inf"), FAKE, FAKE,
+    ws = sk.append_workspace_size(d, 4)
+    assert fa(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.0, 1.0, FAKE, FAKE, FAKE, ws,
               None) == 7
-    assert fa(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1.0, 1.0, None, FAKE, None) == 1
-    assert fa(ctypes.byref(d), None, None, None, None, None, 0, 1.0, 1.0, None, None, None) == 0
+    assert fa(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1.0, float("inf"), FAKE, FAKE,
+              FAKE, ws, None) == 7
+    assert fa(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1.0, 1.0, None, FAKE, FAKE, ws,
+              None) == 1
+    assert fa(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1.0, 1.0, FAKE, FAKE, FAKE, ws - 1,
+              None) == 4
+    assert fa(ctypes.byref(d), None, None, None, None, None, 0, 1.0, 1.0, None, None, None, 0,
+              None) == 0
     fd = sk.lib().starkv_decode_attn_fp8
     need = sk.decode_workspace_size(d, 16, 2048)
 
