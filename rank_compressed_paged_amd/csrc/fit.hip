@@ -24,8 +24,8 @@
 //   symm_f32_kernel    Y = G Q, G stored as its lower tiles (fp32 matrix cores)
 //   syrk_f64_kernel    row slices of S = Y^T Y, lower 64x64 tiles, fp64 sums
 //   sum_slices_kernel  S = sum of the slices
-//   chol_panel_kernel  one wave per problem: factor the 64x64 diagonal block
-//                      of the current panel and invert it (D = L11^-1)
+//   chol_panel_kernel  four waves per problem: factor the 64x64 diagonal
+//                      block of the current panel and invert it (D = L11^-1)
 //   chol_rows_kernel   the panel rows below, L_I = A_Ip D^T
 //   chol_update_kernel the trailing update A_IJ -= L_I L_J^T over the lower
 //                      tiles
@@ -413,77 +413,91 @@ __device__ __forceinline__ double rsqrt_f64(double x) {
   return y;
 }
 
-__global__ __launch_bounds__(64) void chol_panel_kernel(const double* __restrict__ A,
-                                                        double* __restrict__ L,
-                                                        double* __restrict__ Dinv, int r, int p,
-                                                        int* __restrict__ info) {
-  __shared__ double sLt[64][128 + 2];  // row k = column k of L; columns >= 64 stay zero
-  __shared__ double sS[64];            // 1 / L_kk
+__global__ __launch_bounds__(256) void chol_panel_kernel(const double* __restrict__ A,
+                                                         double* __restrict__ L,
+                                                         double* __restrict__ Dinv, int r, int p,
+                                                         int* __restrict__ info) {
+  // Four waves; lane = row of the 64x64 block in every wave.  Factor: wave w
+  // holds columns 16w .. 16w+15 of the row in registers.  At step k the
+  // wave that owns column k takes the pivot from lane k (readlane), scales
+  // the column by its reciprocal square root and publishes it in LDS as row
+  // k of L^T; after one barrier every wave applies the rank-1 update to its
+  // own 16 columns (16 fp64 FMAs per lane instead of up to 63 for one wave).
+  // Updates of columns already factored only touch values never read again.
+  // Inverse D = L^-1: wave w holds rows 16w .. 16w+15 of D (lane = column);
+  // the owner of row k scales it by 1/L_kk and publishes it, and every wave
+  // subtracts L[row][k] times it from its rows below k.
+  __shared__ double sLt[64][64 + 1];  // row k = column k of L (zero above the diagonal)
+  __shared__ double sX[64][64];       // row k of D, published at inverse step k
+  __shared__ double sS[64];           // 1 / L_kk
   const int prob = blockIdx.x;
   const int nbk = ceil_div(r, 64);
   const double* Ap = A + (size_t)prob * r * r;
   double* Lp = L + (size_t)prob * r * r;
   double* Dp = Dinv + ((size_t)prob * nbk + p) * 64 * 64;
   const int j0 = 64 * p, nb = min(64, r - j0);
-  const int lane = threadIdx.x;
-  for (int e = lane; e < 64 * 130; e += 64) (&sLt[0][0])[e] = 0.0;
-  double a[64];
-  // row `lane` of the block (lower part; zero above the diagonal and past nb)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  double a[16];
+  // row `lane`, columns 16w + t (lower part; zero above the diagonal and past nb)
 #pragma unroll
-  for (int t = 0; t < 64; ++t)
-    a[t] = (lane < nb && t <= lane) ? Ap[(size_t)(j0 + lane) * r + j0 + t] : 0.0;
-  wave_sync_lds();
-  for (int k0 = 0; k0 < nb; k0 += 8) {
+  for (int t = 0; t < 16; ++t) {
+    const int c = 16 * w + t;
+    a[t] = (lane < nb && c <= lane) ? Ap[(size_t)(j0 + lane) * r + j0 + c] : 0.0;
+  }
+  for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int k = k0 + kk;
+    for (int tk = 0; tk < 16; ++tk) {
+      const int k = 16 * kb + tk;
       if (k < nb) {  // uniform
-        double dk = readlane_f64(a[kk], k);
-        if (!(dk > 0.0)) {
-          if (lane == 0 && info) atomicAdd(info, 1);
-          dk = 1.0;
+        if (w == kb) {  // uniform: the owner of column k
+          double dk = readlane_f64(a[tk], k);
+          if (!(dk > 0.0)) {
+            if (lane == 0 && info) atomicAdd(info, 1);
+            dk = 1.0;
+          }
+          const double sc = rsqrt_f64(dk);
+          sLt[k][lane] = lane == k ? dk * sc : (lane > k ? a[tk] * sc : 0.0);
+          if (lane == 0) sS[k] = sc;
         }
-        const double s = rsqrt_f64(dk);
-        const double l = lane == k ? dk * s : (lane > k ? a[kk] * s : 0.0);
-        sLt[k][lane] = l;
-        if (lane == 0) sS[k] = s;
-        // all of row k's reads in flight before the updates use them
-        double lr[64];
+        __syncthreads();
+        const double lk = sLt[k][lane];  // L[lane][k]
+        double lc[16];
 #pragma unroll
-        for (int t = kk + 1; t < 64; ++t) lr[t] = sLt[k][k0 + t];
-        __builtin_amdgcn_sched_barrier(0);
+        for (int t = 0; t < 16; ++t) lc[t] = sLt[k][16 * w + t];  // L[16w + t][k]
 #pragma unroll
-        for (int t = kk + 1; t < 64; ++t) a[t] -= l * lr[t];
+        for (int t = 0; t < 16; ++t) a[t] -= lk * lc[t];
       }
     }
-#pragma unroll
-    for (int t = 0; t < 56; ++t) a[t] = a[t + 8];
   }
-  // D = L11^-1, lane c owning column c (a[] is reused as that column)
+  // D = L^-1 by rows: x[t] is row 16w + t of D, lane = column
+  double x[16];
 #pragma unroll
-  for (int t = 0; t < 64; ++t) a[t] = (t == lane && t < nb) ? 1.0 : 0.0;
-  for (int k0 = 0; k0 < 64; k0 += 8) {
+  for (int t = 0; t < 16; ++t) x[t] = (16 * w + t == lane && lane < nb) ? 1.0 : 0.0;
+  for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int k = k0 + kk;
-      if (k < nb) {
-        double lr[64];
+    for (int tk = 0; tk < 16; ++tk) {
+      const int k = 16 * kb + tk;
+      if (k < nb) {  // uniform
+        if (w == kb) {
+          x[tk] *= sS[k];
+          sX[k][lane] = x[tk];
+        }
+        __syncthreads();
+        const double xk = sX[k][lane];
+        double lr[16];
 #pragma unroll
-        for (int t = kk + 1; t < 64; ++t) lr[t] = sLt[k][k0 + t];
-        const double xk = a[kk] * sS[k];
-        __builtin_amdgcn_sched_barrier(0);
-        a[kk] = xk;
+        for (int t = 0; t < 16; ++t) lr[t] = sLt[k][16 * w + t];  // L[16w + t][k], 0 above k
 #pragma unroll
-        for (int t = kk + 1; t < 64; ++t) a[t] -= lr[t] * xk;
+        for (int t = 0; t < 16; ++t)
+          if (16 * w + t > k) x[t] -= lr[t] * xk;  // rows below k
       }
     }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) Dp[(size_t)(k0 + t) * 64 + lane] = a[t];  // zero past nb
-#pragma unroll
-    for (int t = 0; t < 56; ++t) a[t] = a[t + 8];
   }
+#pragma unroll
+  for (int t = 0; t < 16; ++t) Dp[(size_t)(16 * w + t) * 64 + lane] = x[t];  // zero past nb
   // L11: element (i, j) = row j of L^T, column i
-  for (int i = 0; i < nb; ++i)
+  for (int i = w; i < nb; i += 4)
     if (lane < nb) Lp[(size_t)(j0 + i) * r + j0 + lane] = lane <= i ? sLt[lane][i] : 0.0;
 }
 
@@ -789,7 +803,7 @@ hipError_t orth(const OrthProblem& o, const float* Y, float* Q, int* info, hipSt
                        o.A);
   }
   for (int p = 0; p < nbk; ++p) {
-    hipLaunchKernelGGL(chol_panel_kernel, dim3(o.P), dim3(64), 0, st, o.A, o.L, o.D, o.r, p,
+    hipLaunchKernelGGL(chol_panel_kernel, dim3(o.P), dim3(256), 0, st, o.A, o.L, o.D, o.r, p,
                        info);
     const int m = nbk - p - 1;
     if (m > 0) {
