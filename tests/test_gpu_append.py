@@ -127,3 +127,28 @@ def test_prefill_chunk_append_full_size(sk):
     okv, uv, _ = _within(gv[bk, :, ok], rv[bk, :, ok], ATOL_V)
     print(f"[parity] prefill_b16 append sample: k max ulp {uk.max()}, v max ulp {uv.max()}")
     assert okk.all() and okv.all()
+
+
+def test_few_token_append_shared_workspace_deterministic(sk):
+    """The few-token path keeps fp32 partials in the caller's workspace and
+    sums them in a fixed order: one workspace serves consecutive calls of
+    different sizes (a larger call's leftovers never leak into a smaller
+    one), and a repeated call writes the same bits."""
+    sh = wl.MAIN
+    dims = sk.make_dims(sh.H, sh.d, sh.r_k, sh.r_v, 1)
+    ws = sk.alloc_workspace(sk.append_workspace_size(dims, 64), "cuda")
+    ws.fill_(0x7F)  # start from garbage: every partial read must have been written
+    outs = {}
+    for n, seed in ((16, 41), (5, 42), (16, 41)):
+        U, W, k, v, slots, kc, vc = _case(sh, n, seed, 0)
+        note(f"append shared workspace n={n}")
+        tk, tv = dev(kc), dev(vc)
+        sk.append(dev(k), dev(v), dev(U), dev(W), dev(slots), tk, tv, workspace=ws)
+        torch.cuda.synchronize()
+        gk, gv = tk.cpu().numpy(), tv.cpu().numpy()
+        rk, rv = oracle.append(k, v, U, W, slots, kc, vc)
+        _check(gk, gv, rk, rv, f"append shared workspace n={n}")
+        if n in outs:
+            assert np.array_equal(gk.view(np.uint16), outs[n][0].view(np.uint16))
+            assert np.array_equal(gv.view(np.uint16), outs[n][1].view(np.uint16))
+        outs[n] = (gk, gv)
