@@ -106,6 +106,8 @@ def parse_args(argv=None):
     ap.add_argument("--no-layouts", action="store_true",
                     help="skip the grouped-query and low-rank decode legs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU sample budget")
+    ap.add_argument("--cpu-prefill-seconds", type=float, default=5.0,
+                    help="CPU sample budget of the prefill leg's oracle baseline")
     ap.add_argument("--flush", choices=["read", "write"], default="read",
                     help="evict the Infinity Cache by reading (default) or writing 512 MiB")
     ap.add_argument("--profile-run", action="store_true")
@@ -199,7 +201,47 @@ def device_info():
             "hbm_gib": round(p.total_memory / 2**30, 1)}
 
 
-def prefill_leg(flush_fn, steps, name="prefill_b16"):
+def cpu_prefill_baseline(pc, budget_s):
+    """The fp64 oracle, as it stands, on whole requests of the same prefill
+    workload (each request's chunk appended by the oracle first, untimed)
+    until about budget_s seconds of prefill attention are spent; algorithmic
+    TFLOP/s, the unit of the GPU prefill figures."""
+    import numpy as np
+    import oracle
+    from rank_compressed_paged_amd import metrics
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    sh, c = pc.shape, pc.cache
+    qsl = pc.query_start_loc
+    B = len(qsl) - 1
+    done, spent, flops = 0, 0.0, 0
+    kc, vc = c.k_cache, c.v_cache
+    while spent < budget_s or done < 1:
+        b = done % B
+        rows = slice(int(qsl[b]), int(qsl[b + 1]))
+        kc, vc = oracle.append(pc.k_new[rows], pc.v_new[rows], pc.U, pc.W, pc.slot_mapping[rows],
+                               kc, vc)
+        t0 = time.perf_counter()
+        oracle.prefill(pc.q, qsl, kc, vc, pc.U, pc.W, c.block_tables, c.seq_lens, pc.scale,
+                       request_indices=[b])
+        spent += time.perf_counter() - t0
+        flops += metrics.prefill_flops(pc.cached_lens[b:b + 1], np.diff(qsl)[b:b + 1], sh.H, sh.d,
+                                       sh.r_k, sh.r_v)
+        done += 1
+    total = metrics.prefill_flops(pc.cached_lens, np.diff(qsl), sh.H, sh.d, sh.r_k, sh.r_v)
+    return {"value": round(flops / spent / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} whole requests of the {B} of one {pc.name} call "
+                      f"({done / B:.2f} calls' worth), {spent:.1f} s, fp64 numpy "
+                      f"rebuild-then-attend",
+            "ms_per_call_extrapolated": round(spent / flops * total * 1e3, 1)}
+
+
+def prefill_leg(flush_fn, steps, name="prefill_b16", cpu_budget_s=0.0):
     """Chunked prefill at 16 requests x (4096 cached + 256 new) tokens: the
     chunk's append (4096 tokens), then causal attention for the 4096 chunk
     queries (prefill_b16; prefill_b16_fp8 the same over FP8 caches).
@@ -275,6 +317,7 @@ def prefill_leg(flush_fn, steps, name="prefill_b16"):
         "append_kernel_tflops": round(tf(app_flops, m(app_kern_ms)), 1),
         "append_kernel_mfma_frac": round(tf(app_flops, m(app_kern_ms)) / MFMA_F16_PEAK_TFLOPS, 4),
         "append_kernel_gbs": round(app_bytes / (m(app_kern_ms) * 1e-3) / 1e9, 1),
+        "cpu_baseline": cpu_prefill_baseline(pc, cpu_budget_s) if cpu_budget_s > 0 else None,
     }
 
 
@@ -558,7 +601,8 @@ def run_bench(args):
     }
     if not args.no_prefill:
         del ceil_sink
-        res["prefill"] = prefill_leg(do_flush, args.steps)
+        res["prefill"] = prefill_leg(do_flush, args.steps,
+                                     cpu_budget_s=0.0 if args.no_cpu else args.cpu_prefill_seconds)
         res["prefill_fp8"] = prefill_leg(do_flush, args.steps, "prefill_b16_fp8")
     if not args.no_low_batch:
         res["low_batch"] = low_batch_leg(do_flush, args.steps)
