@@ -193,12 +193,40 @@ def timed(fn, n, flush_fn=None, kernel_sel=0):
     return steps_ms, kern_ms, wall
 
 
+def rocminfo_gpu():
+    """Marketing name, maximum engine clock and compute units of the first
+    GPU agent as rocminfo prints them (empty when rocminfo is unavailable)."""
+    import subprocess
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except Exception:
+        return {}
+    for agent in txt.split("*******")[1:]:
+        if "Device Type:             GPU" not in agent and "Device Type: GPU" not in " ".join(agent.split()):
+            continue
+        info = {}
+        for line in agent.splitlines():
+            key, _, val = line.strip().partition(":")
+            val = val.strip()
+            if key == "Marketing Name" and val:
+                info["marketing_name"] = val
+            elif key == "Max Clock Freq. (MHz)" and val.isdigit():
+                info["max_clock_mhz"] = int(val)
+            elif key == "Compute Unit" and val.isdigit():
+                info["rocminfo_compute_units"] = int(val)
+        if info:
+            return info
+    return {}
+
+
 def device_info():
     import torch
     p = torch.cuda.get_device_properties(0)
-    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
-            "compute_units": p.multi_processor_count,
-            "hbm_gib": round(p.total_memory / 2**30, 1)}
+    d = {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
+         "compute_units": p.multi_processor_count,
+         "hbm_gib": round(p.total_memory / 2**30, 1)}
+    d.update(rocminfo_gpu())
+    return d
 
 
 def cpu_prefill_baseline(pc, budget_s):

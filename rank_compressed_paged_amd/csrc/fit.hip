@@ -25,7 +25,8 @@
 //   syrk_f64_kernel    row slices of S = Y^T Y, lower 64x64 tiles, fp64 sums
 //   sum_slices_kernel  S = sum of the slices
 //   chol_panel_kernel  four waves per problem: factor the 64x64 diagonal
-//                      block of the current panel and invert it (D = L11^-1)
+//                      block of the current panel in 16-column sub-blocks
+//                      and invert it in 16x16 blocks (D = L11^-1)
 //   chol_rows_kernel   the panel rows below, L_I = A_Ip D^T
 //   chol_update_kernel the trailing update A_IJ -= L_I L_J^T over the lower
 //                      tiles
@@ -417,19 +418,24 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(const double* __restric
                                                          double* __restrict__ L,
                                                          double* __restrict__ Dinv, int r, int p,
                                                          int* __restrict__ info) {
-  // Four waves; lane = row of the 64x64 block in every wave.  Factor: wave w
-  // holds columns 16w .. 16w+15 of the row in registers.  At step k the
-  // wave that owns column k takes the pivot from lane k (readlane), scales
-  // the column by its reciprocal square root and publishes it in LDS as row
-  // k of L^T; after one barrier every wave applies the rank-1 update to its
-  // own 16 columns (16 fp64 FMAs per lane instead of up to 63 for one wave).
-  // Updates of columns already factored only touch values never read again.
-  // Inverse D = L^-1: wave w holds rows 16w .. 16w+15 of D (lane = column);
-  // the owner of row k scales it by 1/L_kk and publishes it, and every wave
-  // subtracts L[row][k] times it from its rows below k.
+  // Four waves, blocked by 16 columns; lane = row of the 64x64 block.
+  // Factor: wave w holds columns 16w .. 16w+15 of its row in registers.  For
+  // sub-block sb the owning wave factors its 16 columns for all rows alone
+  // (pivot from lane k by readlane, fp64 reciprocal square root, the scaled
+  // column published in LDS as row k of L^T and read back by the same wave,
+  // whose LDS operations complete in order, then the update of the block's
+  // later columns); after one barrier every later wave subtracts the rank-16
+  // product L[:, sb] L[c, sb]^T from its own columns c.  Updates only ever
+  // touch columns not yet factored, and values above the diagonal are never
+  // read as pivots or results.
+  // Inverse D = L^-1 in 16x16 blocks: each wave inverts one diagonal block
+  // by forward substitution (lane = column), then the off-diagonal blocks
+  // follow by distance from the diagonal, D_IJ = -D_II sum_{K=J}^{I-1}
+  // L_IK D_KJ, one block per wave and level, a barrier between levels.
   __shared__ double sLt[64][64 + 1];  // row k = column k of L (zero above the diagonal)
-  __shared__ double sX[64][64];       // row k of D, published at inverse step k
-  __shared__ double sS[64];           // 1 / L_kk
+  __shared__ double sD[64][64 + 1];   // D, row-major, filled block by block
+  __shared__ double sT[4][16][16 + 1];  // per-wave scratch of the off-diagonal blocks
+  __shared__ double sS[64];            // 1 / L_kk
   const int prob = blockIdx.x;
   const int nbk = ceil_div(r, 64);
   const double* Ap = A + (size_t)prob * r * r;
@@ -439,64 +445,110 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(const double* __restric
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   double a[16];
-  // row `lane`, columns 16w + t (lower part; zero above the diagonal and past nb)
 #pragma unroll
   for (int t = 0; t < 16; ++t) {
     const int c = 16 * w + t;
     a[t] = (lane < nb && c <= lane) ? Ap[(size_t)(j0 + lane) * r + j0 + c] : 0.0;
   }
-  for (int kb = 0; kb < 4; ++kb) {
+  for (int sb = 0; sb < 4; ++sb) {
+    const int c0 = 16 * sb;
+    if (c0 >= nb) break;  // uniform
+    if (w == sb) {        // uniform: the owner factors its 16 columns
 #pragma unroll
-    for (int tk = 0; tk < 16; ++tk) {
-      const int k = 16 * kb + tk;
-      if (k < nb) {  // uniform
-        if (w == kb) {  // uniform: the owner of column k
+      for (int tk = 0; tk < 16; ++tk) {
+        const int k = c0 + tk;
+        if (k < nb) {
           double dk = readlane_f64(a[tk], k);
           if (!(dk > 0.0)) {
             if (lane == 0 && info) atomicAdd(info, 1);
             dk = 1.0;
           }
           const double sc = rsqrt_f64(dk);
-          sLt[k][lane] = lane == k ? dk * sc : (lane > k ? a[tk] * sc : 0.0);
+          const double l = lane == k ? dk * sc : (lane > k ? a[tk] * sc : 0.0);
+          sLt[k][lane] = l;
           if (lane == 0) sS[k] = sc;
+          double lr[16];
+#pragma unroll
+          for (int t = tk + 1; t < 16; ++t) lr[t] = sLt[k][c0 + t];  // L[c0 + t][k]
+#pragma unroll
+          for (int t = tk + 1; t < 16; ++t) a[t] -= l * lr[t];
         }
-        __syncthreads();
-        const double lk = sLt[k][lane];  // L[lane][k]
+      }
+    }
+    __syncthreads();
+    if (w > sb) {  // uniform: rank-16 update of this wave's columns
+      double lm[16];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) lm[m] = sLt[c0 + m][lane];  // L[lane][c0 + m]
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
         double lc[16];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) lc[t] = sLt[k][16 * w + t];  // L[16w + t][k]
+        for (int t = 0; t < 16; ++t) lc[t] = sLt[c0 + m][16 * w + t];  // L[16w + t][c0 + m]
 #pragma unroll
-        for (int t = 0; t < 16; ++t) a[t] -= lk * lc[t];
+        for (int t = 0; t < 16; ++t) a[t] -= lm[m] * lc[t];
       }
     }
   }
-  // D = L^-1 by rows: x[t] is row 16w + t of D, lane = column
-  double x[16];
+  __syncthreads();
+  // inverse, diagonal blocks: wave J inverts L_JJ, lane = column (16 lanes)
+  const int nsb = ceil_div(nb, 16);
+  if (w < nsb && lane < 16) {
+    const int c0 = 16 * w;
+    double x[16];
 #pragma unroll
-  for (int t = 0; t < 16; ++t) x[t] = (16 * w + t == lane && lane < nb) ? 1.0 : 0.0;
-  for (int kb = 0; kb < 4; ++kb) {
+    for (int t = 0; t < 16; ++t) x[t] = (t == lane && c0 + t < nb) ? 1.0 : 0.0;
 #pragma unroll
-    for (int tk = 0; tk < 16; ++tk) {
-      const int k = 16 * kb + tk;
-      if (k < nb) {  // uniform
-        if (w == kb) {
-          x[tk] *= sS[k];
-          sX[k][lane] = x[tk];
-        }
-        __syncthreads();
-        const double xk = sX[k][lane];
-        double lr[16];
+    for (int k = 0; k < 16; ++k) {
+      if (c0 + k < nb) {
+        x[k] *= sS[c0 + k];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) lr[t] = sLt[k][16 * w + t];  // L[16w + t][k], 0 above k
-#pragma unroll
-        for (int t = 0; t < 16; ++t)
-          if (16 * w + t > k) x[t] -= lr[t] * xk;  // rows below k
+        for (int t = k + 1; t < 16; ++t) x[t] -= sLt[c0 + k][c0 + t] * x[k];  // L[c0+t][c0+k]
       }
     }
-  }
 #pragma unroll
-  for (int t = 0; t < 16; ++t) Dp[(size_t)(16 * w + t) * 64 + lane] = x[t];  // zero past nb
-  // L11: element (i, j) = row j of L^T, column i
+    for (int t = 0; t < 16; ++t) sD[c0 + t][c0 + lane] = x[t];
+  }
+  // zero the blocks above the diagonal (never written otherwise)
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int i = e / 64, j = e % 64;
+    if (j / 16 > i / 16) sD[i][j] = 0.0;
+  }
+  __syncthreads();
+  // off-diagonal blocks by distance dist = I - J; lane = (row r = lane / 4,
+  // columns 4 (lane % 4) .. +3) of the 16x16 block
+  for (int dist = 1; dist < nsb; ++dist) {
+    const int J = w, I = w + dist;
+    if (I < nsb) {  // uniform
+      const int I0 = 16 * I, J0 = 16 * J, rr = lane >> 2, cc = 4 * (lane & 3);
+      // T = sum_{K=J}^{I-1} L_IK D_KJ
+      double tv[4] = {0.0, 0.0, 0.0, 0.0};
+      for (int m = J0; m < I0; ++m) {
+        const double lim = sLt[m][I0 + rr];  // L[I0 + rr][m]
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tv[q] += lim * sD[m][J0 + cc + q];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sT[w][rr][cc + q] = tv[q];
+      wave_sync_lds();  // this wave's own writes, read back below
+      // D_IJ = -D_II T
+      double dv[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const double dim = sD[I0 + rr][I0 + m];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dv[q] += dim * sT[w][m][cc + q];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sD[I0 + rr][J0 + cc + q] = -dv[q];
+    }
+    __syncthreads();
+  }
+  // D out (zero past nb and above the diagonal), then L11
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int i = e / 64, j = e % 64;
+    Dp[(size_t)i * 64 + j] = (i < nb && j < nb && j <= i) ? sD[i][j] : 0.0;
+  }
   for (int i = w; i < nb; i += 4)
     if (lane < nb) Lp[(size_t)(j0 + i) * r + j0 + lane] = lane <= i ? sLt[lane][i] : 0.0;
 }
