@@ -107,8 +107,17 @@ struct PrefillArgs {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   half_t* z;  // fp16, tiled [H][n_tb][RV/16][64][8], see launch_upproj_tiled
+  const half_t* W;  // fused up-projection: the value basis [Hkv*D][RV]
+  half_t* out;      // fused up-projection: out [total_q][H][D]
   int max_blocks, num_blocks, batch, n_qtiles, n_groups, n_tb;
 };
+
+// Instances whose epilogue applies W_h itself (out = W_h z without z ever
+// leaving the chip): two heads of 64 queries, 8 waves, r_v 512, d 128.
+template <int G, int MQ, int NW, int RV, int D>
+constexpr bool prefill_fused() {
+  return G == 2 && MQ == 64 && NW == 8 && RV == 512 && D == 128;
+}
 
 constexpr int PBS = 16;                 // tokens per page
 constexpr int kChunk = 64;              // block-id ring: 2 * kChunk entries
@@ -134,7 +143,7 @@ __device__ __forceinline__ half8 e4m3x8_to_half8(uint32_t w0, uint32_t w1) {
 }
 
 template <int H, int RK, int RV, int G, int MQ, int NW, int PPS, int DEPTH, int SCHED, bool KLDS,
-          int QG, bool FP8>
+          int QG, bool FP8, int DH>
 __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   static_assert(DEPTH >= 2 && DEPTH <= 3, "register ring of 2 or 3 steps");
   static_assert(PPS == 1 || PPS == 2, "one or two pages per step");
@@ -679,13 +688,89 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
   if constexpr (DEPTH > 2)
     if (s + 1 < n_steps) run_step(std::integral_constant<int, 1>{}, std::true_type{}, s + 1);
 
-  // ---- normalise and write z rows of this tile
+  // ---- normalise: every row's softmax sum
 #pragma unroll
   for (int i = 0; i < C::SUW; ++i) {
     const float l = quad_sum(l_run[i]);  // the four quads' parts
     sL[su_row[i]] = l;                    // the four quads agree
   }
   block_sync_lds();
+  if constexpr (prefill_fused<G, MQ, NW, RV, DH>()) {
+    // ---- out = W_h z in the epilogue.  z (this tile's 128 rows x r_v,
+    // normalised, fp16) is staged in LDS one half of the features at a time
+    // by the waves that hold it; wave w then accumulates out rows of head
+    // w / 4 (64 queries) x 32 of d (block w % 4) with v_mfma_f32_32x32x16_f16:
+    // A = z rows from LDS, B = 8 consecutive features of one row of W_h
+    // straight from memory (a 16-entry register ring runs over both halves,
+    // so the second half's loads go out during the first half's products).
+    constexpr int FH = RV / 2;             // features per half
+    constexpr int LDZ = FH + 72;           // 656-byte rows: conflict-free 16-byte reads of 32 rows
+    constexpr int WPH = NW / G;            // waves per head
+    constexpr int KH = FH / 16;            // 16-feature chunks per half
+    static_assert(DH / WPH == 32 && MQ % 32 == 0 && KH == 16, "fused up-projection tile");
+    __shared__ __attribute__((aligned(16))) half_t sZ[C::R][LDZ];
+    const int hl = w_u / WPH, db = w_u % WPH;
+    const int r_h = g * G + hl;
+    // row d = 32 db + c32 of W_h (its key/value head), features from 8 hf
+    const half_t* Wd = a.W + ((size_t)(r_h / QG) * DH + db * 32 + c32) * RV + 8 * hf;
+    constexpr int WRING = 8;  // W operands in flight
+    half8 wr[WRING];
+#pragma unroll
+    for (int kc = 0; kc < WRING; ++kc) wr[kc] = *(const half8*)(Wd + kc * 16);
+    float inv[C::RT];
+#pragma unroll
+    for (int rt = 0; rt < C::RT; ++rt) {
+      const float lr = sL[rt * 32 + c32];
+      inv[rt] = lr > 0.f ? a.v_scale / lr : 0.f;
+    }
+    float16v oacc[MQ / 32];
+#pragma unroll
+    for (int mt = 0; mt < MQ / 32; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[mt][e] = 0.f;
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      if ((w_u * C::FTW * 32) / FH == ps) {  // uniform: the waves holding this half
+#pragma unroll
+        for (int rt = 0; rt < C::RT; ++rt)
+#pragma unroll
+          for (int ft = 0; ft < C::FTW; ++ft)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              // features w*64 + 32 ft + 8 jj + 4 hf + 0..3 of row 32 rt + c32
+              const int f = w_u * C::FTW * 32 + ft * 32 + 8 * jj + 4 * hf - ps * FH;
+              half4 o;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) o[r] = (half_t)(acc[rt][ft][4 * jj + r] * inv[rt]);
+              *(half4*)&sZ[rt * 32 + c32][f] = o;
+            }
+      }
+      block_sync_lds();
+#pragma unroll
+      for (int kc = 0; kc < KH; ++kc) {
+        const int k = ps * KH + kc;  // chunk over both halves
+        const half8 b = wr[k % WRING];
+        if (k + WRING < 2 * KH) wr[k % WRING] = *(const half8*)(Wd + (k + WRING) * 16);
+#pragma unroll
+        for (int mt = 0; mt < MQ / 32; ++mt) {
+          const half8 av = *(const half8*)&sZ[hl * MQ + mt * 32 + c32][kc * 16 + 8 * hf];
+          oacc[mt] = mfma32x32x16(av, b, oacc[mt]);
+        }
+      }
+      if (ps == 0) block_sync_lds();  // the second half overwrites sZ
+    }
+    // register i of tile mt: row 8 (i/4) + 4 hf + i%4 of the tile, column d = 32 db + c32
+#pragma unroll
+    for (int mt = 0; mt < MQ / 32; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r_j = j0 + mt * 32 + 8 * (i / 4) + 4 * hf + (i % 4);
+        if (r_j < Cn)
+          a.out[((size_t)(q_begin + r_j) * H + r_h) * DH + db * 32 + c32] = (half_t)oacc[mt][i];
+      }
+    return;
+  }
+  // ---- otherwise write z rows of this tile for the up-projection kernel
 #pragma unroll
   for (int rt = 0; rt < C::RT; ++rt) {
     const int row = rt * 32 + c32;
@@ -729,6 +814,8 @@ static hipError_t prefill_instance(const void* qt, const int32_t* qsl, int max_q
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.z = (half_t*)z;
+  a.W = (const half_t*)W;
+  a.out = (half_t*)out;
   a.max_blocks = max_blocks;
   a.num_blocks = num_blocks;
   a.batch = batch;
@@ -737,10 +824,11 @@ static hipError_t prefill_instance(const void* qt, const int32_t* qsl, int max_q
   a.n_tb = (total_q + 31) / 32;
   const long wgs = (long)batch * a.n_qtiles * a.n_groups;
   launch_hooked(TIME_PREFILL_ATTN, TIME_NONE,
-                prefill_attn_kernel<H, RK, RV, G, MQ, NW, PPS, DEPTH, SCHED, KLDS, QG, FP8>,
+                prefill_attn_kernel<H, RK, RV, G, MQ, NW, PPS, DEPTH, SCHED, KLDS, QG, FP8, D>,
                 dim3((unsigned)wgs), dim3(NW * 64), st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if constexpr (prefill_fused<G, MQ, NW, RV, D>()) return hipSuccess;  // out written by the kernel
   return launch_upproj_tiled(ShapeKey{H, D, RK, RV, H / QG}, W, z, total_q, out, st);
 }
 
