@@ -322,7 +322,9 @@ def prefill_leg(flush_fn, steps, name="prefill_b16", cpu_budget_s=0.0):
     _, app_kern_ms, _ = timed(app, n, flush_fn, sk.TIME_APPEND)
     flops = metrics.prefill_flops(pc.cached_lens, chunk, sh.H, sh.d, sh.r_k, sh.r_v)
     pairs = metrics.prefill_pairs(pc.cached_lens, chunk)
-    kern_flops = 2 * sh.H * pairs * (sh.r_k + sh.r_v)     # scores + P.c_v, the kernel's share
+    # the kernel's share: scores + P.c_v, and the up-projection, which the
+    # main-shape kernels apply in their epilogue
+    kern_flops = 2 * sh.H * pairs * (sh.r_k + sh.r_v) + 2 * sh.H * T * sh.r_v * sh.d
     app_flops = metrics.append_flops(T, sh.H, sh.d, sh.r_k, sh.r_v)
     app_bytes = (2 * T * sh.H * sh.d * 2 + T * 8 + metrics.basis_bytes(sh.H, sh.d, sh.r_k, sh.r_v)
                  + T * metrics.latent_bytes_per_token(sh.H, sh.r_k, sh.r_v))
@@ -339,6 +341,7 @@ def prefill_leg(flush_fn, steps, name="prefill_b16", cpu_budget_s=0.0):
         "attn_kernel_mfma_frac": round(tf(kern_flops, m(attn_kern_ms)) / MFMA_F16_PEAK_TFLOPS, 4),
         "algorithmic_gflop_call": round(flops / 1e9, 1),
         "algorithmic_gflop_kernel": round(kern_flops / 1e9, 1),
+        "kernel_includes_upprojection": True,
         "append_tokens": T,
         "append_call_ms": round(m(app_ms), 4),
         "append_kernel_ms": round(m(app_kern_ms), 4),
