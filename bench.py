@@ -162,6 +162,27 @@ def cpu_baseline(case, budget_s):
             "ms_per_step_extrapolated": round(spent / tokens * int(c.seq_lens.sum()) * 1e3, 1)}
 
 
+def settle(fn, flush_fn=None, seconds=0.2):
+    """Run fn (each call after flush_fn) for about `seconds` of GPU time.
+    Matrix-core-heavy kernels start up to about 30% slower and take some tens
+    of milliseconds of sustained load to reach their steady clock (the
+    prefill kernel's per-dispatch durations in a kernel trace fall from about
+    0.85 ms to 0.65 ms over its first ~50 calls); timing starts after that.
+    Memory-bound kernels show no such ramp."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        for _ in range(8):
+            if flush_fn is not None:
+                flush_fn(i)
+            fn()
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return i
+
+
 def timed(fn, n, flush_fn=None, kernel_sel=0):
     """Run fn n times, each optionally after flush_fn (outside the events).
     Returns per-call ms from events around the call on the current stream,
@@ -311,10 +332,7 @@ def prefill_leg(flush_fn, steps, name="prefill_b16", cpu_budget_s=0.0):
                             workspace=ws)
 
     app()
-    for i in range(3):
-        flush_fn(i)
-        attn()
-    torch.cuda.synchronize()
+    settle(attn, flush_fn, 0.25)
     n = max(steps // 2, 10)
     attn_ms, _, _ = timed(attn, n, flush_fn)
     _, attn_kern_ms, _ = timed(attn, n, flush_fn, sk.TIME_PREFILL_ATTN)
@@ -484,8 +502,7 @@ def fit_leg(steps):
     def fit():
         sk.fit_bases(k, v, sh.r_k, sh.r_v, u0, w0, iters, U=U, W=W, workspace=ws)
 
-    fit()
-    torch.cuda.synchronize()
+    settle(fit, None, 0.25)
     n = max(min(steps // 5, 10), 3)
     call_ms, _, _ = timed(fit, n)
     _, gram_ms, _ = timed(fit, n, None, sk.TIME_FIT_GRAM)
