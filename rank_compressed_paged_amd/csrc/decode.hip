@@ -121,38 +121,64 @@ __global__ __launch_bounds__(256) void qproj_kernel(const half_t* __restrict__ q
 #pragma unroll
     for (int k = 0; k < D / 32; ++k) b[k] = *(const half8*)(qrow + k * 32);
   };
-  half8 bq[D / 32];
+  // all of the wave's token sets are requested up front: with two waves per
+  // SIMD, loading them one set at a time left the latency of each exposed
+  half8 bq[TPW][D / 32];
   const int nb0 = blockIdx.y * TPW * 64 + w * 16;
-  if (nb0 < n_tokens) load_q(bq, nb0);
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt)
+    if (nb0 + tt * 64 < n_tokens) load_q(bq[tt], nb0 + tt * 64);
   const half_t* Uh = U + (size_t)(h / QG) * D * RK;  // the head's key/value head
-  for (int c = tid; c < D * RK / 8; c += 256) {
-    const int i = c / (RK / 8), r0 = (c % (RK / 8)) * 8;
-    *(half8*)&sU[i][r0] = *(const half8*)(Uh + (size_t)i * RK + r0);
+  // Ranks are permuted inside the LDS copy: column 16t + 4a + r holds rank
+  // 4NT*a + 4t + r (NT = RK/16 rank tiles, a = the lane's quad).  The four
+  // outputs a lane takes from each of the NT tiles are then 4NT consecutive
+  // ranks of one token, stored whole (a token's row in 16- or 32-byte pieces
+  // instead of 8-byte ones).  Each output keeps its own products and order.
+  constexpr int NT = RK / 16;
+  static_assert(RK % 16 == 0, "whole rank tiles");
+  for (int c = tid; c < D * RK / 4; c += 256) {
+    const int i = c / (RK / 4), g = c % (RK / 4);
+    *(half4*)&sU[i][16 * (g % NT) + 4 * (g / NT)] = *(const half4*)(Uh + (size_t)i * RK + 4 * g);
   }
   __syncthreads();
+#pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     const int nb = nb0 + tt * 64;
     if (nb >= n_tokens) break;  // wave-uniform; no barrier follows
-    if (tt > 0) load_q(bq, nb);
+    float4v acc[NT];
 #pragma unroll
-    for (int rt = 0; rt < RK / 16; ++rt) {
-      float4v acc = zero4();
+    for (int rt = 0; rt < NT; ++rt) {
+      acc[rt] = zero4();
 #pragma unroll
       for (int k = 0; k < D / 32; ++k) {
-        // A fragment: outputs 16*rt + col, d = 32k + 8*quad .. +7
+        // A fragment: LDS columns 16*rt + col, d = 32k + 8*quad .. +7
         const half_t* ap = &sU[k * 32 + quad * 8 + (col >> 2)][rt * 16 + 4 * (col & 3)];
         const half4 a0 = lds_read_tr16(ap);
         const half4 a1 = lds_read_tr16(ap + 4 * LDU);
         const half8 au = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        acc = mfma16x16x32(au, bq[k], acc);
+        acc[rt] = mfma16x16x32(au, bq[tt][k], acc[rt]);
       }
-      // D[output 4*quad + r][token col]: four consecutive outputs of one token
-      const int nt = nb + col;
-      if (nt < n_tokens) {
-        half4 o;
+    }
+    // D[LDS column 16rt + 4*quad + r][token col] = rank 4NT*quad + 4rt + r
+    const int nt = nb + col;
+    if (nt < n_tokens) {
+      half_t* dst = qt + ((size_t)nt * H + h) * RK + quad * 4 * NT;
+      if constexpr (NT % 2 == 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = (half_t)(acc[r] * qscale);
-        *(half4*)(qt + ((size_t)nt * H + h) * RK + rt * 16 + quad * 4) = o;
+        for (int p = 0; p < NT / 2; ++p) {
+          half8 o;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = (half_t)(acc[2 * p + e / 4][e % 4] * qscale);
+          *(half8*)(dst + 8 * p) = o;
+        }
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+          half4 o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = (half_t)(acc[rt][r] * qscale);
+          *(half4*)(dst + 4 * rt) = o;
+        }
       }
     }
   }
