@@ -317,11 +317,14 @@ def prefill_leg(flush_fn, steps, name="prefill_b16", cpu_budget_s=0.0):
     ws = sk.alloc_workspace(sk.prefill_workspace_size(dims, B, T, msl), "cuda")
     out = torch.empty((T, sh.H, sh.d), dtype=torch.float16, device="cuda")
 
+    ws_app = sk.alloc_workspace(sk.append_workspace_size(dims, T), "cuda")
+
     def app():   # same slots each time: idempotent
         if fp8:
-            sk.append_fp8(k_new, v_new, U, W, slots, pc.k_scale, pc.v_scale, kc, vc)
+            sk.append_fp8(k_new, v_new, U, W, slots, pc.k_scale, pc.v_scale, kc, vc,
+                          workspace=ws_app)
         else:
-            sk.append(k_new, v_new, U, W, slots, kc, vc)
+            sk.append(k_new, v_new, U, W, slots, kc, vc, workspace=ws_app)
 
     def attn():
         if fp8:

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define STARKV_ABI_VERSION 3
+#define STARKV_ABI_VERSION 4
 
 typedef enum {
   STARKV_OK = 0,
@@ -101,10 +101,16 @@ int32_t starkv_shape_supported(const starkv_dims* dims);
 
 /*
  * Workspace bytes (host out-parameter *bytes) that starkv_append and
- * starkv_append_fp8 need for num_tokens tokens: the fp32 partial products of
- * the value projection over 64-row slices of W, (Hkv*d/64) * num_tokens *
- * r_v * 4 bytes, when num_tokens <= 64 (a decode step's tokens), and 0 for
- * more tokens.  Returns a status.
+ * starkv_append_fp8 need for num_tokens tokens, all of it fp32 partial
+ * products of the value projection:
+ *   num_tokens <= 64 (a decode step's tokens): over 64-row slices of W,
+ *     (Hkv*d/64) * num_tokens * r_v * 4 bytes;
+ *   65..1792 tokens at 32 key/value heads of d 128 with r_k 64 and r_v 512:
+ *     over four equal parts of the contraction, 4 * num_tokens * r_v * 4
+ *     bytes; 1793..2816 tokens there: two parts, 2 * num_tokens * r_v * 4;
+ *   other token counts and shapes: 0.
+ * The size is not monotonic in num_tokens: a workspace reused for several
+ * token counts takes the largest of their sizes.  Returns a status.
  */
 starkv_status starkv_append_workspace_size(const starkv_dims* dims, int32_t num_tokens,
                                            size_t* bytes /* (host) */);

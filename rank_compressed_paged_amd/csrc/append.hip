@@ -141,14 +141,21 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     buf ^= 1;
   }
 
-  // ---- epilogue: D[token][output], lane holds rows 4*quad + r, column col
+  // ---- epilogue: D[token][output], lane holds rows 4*quad + r, column col;
+  // the lane's 8 slots are requested together (indices clamped into range)
+  int64_t slot_of[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      slot_of[mt][r] = a.slots[min(m_base + wm * 32 + mt * 16 + quad * 4 + r, a.N - 1)];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = m_base + wm * 32 + mt * 16 + quad * 4 + r;
       if (m >= a.N) continue;
-      const int64_t slot = a.slots[m];
+      const int64_t slot = slot_of[mt][r];
       if (slot < 0) continue;
       const int64_t blk = slot / 16;
       const int off = (int)(slot % 16);
@@ -369,13 +376,13 @@ __global__ __launch_bounds__(kSmallWaves * 64) void append_small_kernel(AppendAr
 // of a thread's reads are issued before its sum: one memory round trip.
 template <int RV, int NS>
 __global__ __launch_bounds__(256) void append_reduce_kernel(AppendArgs a) {
-  constexpr int SR = 4;        // slice runs
+  constexpr int SR = NS < 4 ? NS : 4;  // slice runs (one per 64-thread group in use)
   constexpr int RUN = NS / SR;
   static_assert(NS % SR == 0 && RV % 4 == 0, "slice runs, output quads");
   __shared__ float4v sSum[SR][64];
   const int tid = threadIdx.x, sr = tid / 64, oq = tid % 64;
   const int e4 = blockIdx.x * 64 + oq;  // output quad: token e4 / (RV/4), outputs 4*(e4 % (RV/4)) ..
-  const bool live = e4 < a.N * (RV / 4);
+  const bool live = sr < SR && e4 < a.N * (RV / 4);
   if (live) {
     const float4v* src = (const float4v*)a.part + (size_t)sr * RUN * a.N * (RV / 4) + e4;
     float4v p[RUN];
@@ -416,7 +423,7 @@ __global__ __launch_bounds__(256) void append_reduce_kernel(AppendArgs a) {
 constexpr int TT_M = 128, TT_N = 64;
 
 
-template <int H, int D, int RK, int RV, int TK, int RING>
+template <int H, int D, int RK, int RV, int TK, int RING, int VS = 1>
 __global__ __launch_bounds__(512) void append_tiled_kernel(AppendArgs a) {
   static_assert(RV % TT_N == 0 && RK == TT_N && D % TK == 0, "tile shape");
   static_assert(RING >= 1 && RING <= 4, "register ring of 1 to 4 steps");
@@ -439,24 +446,33 @@ __global__ __launch_bounds__(512) void append_tiled_kernel(AppendArgs a) {
   // copy of those token rows instead of fetching them once per XCD.
   constexpr int VT = RV / TT_N;
   const int tiles_m = (a.N + TT_M - 1) / TT_M;
+  // With VS > 1 the value contraction (K = H*d) is split into VS equal parts,
+  // one per job (split js after all output tiles of split js-1); each writes
+  // fp32 partial products to a.part[js][token][output] and
+  // append_reduce_kernel sums the VS parts in split order.  A value job's
+  // time is set by its serial K steps (one 128-token tile alone takes about
+  // as long as the whole chunk), so splitting K shortens the critical path.
   int job = blockIdx.x;
   bool is_v;
-  int mt, nt = 0, h = 0;
-  if (job < tiles_m * VT) {
+  int mt, nt = 0, h = 0, js = 0;
+  if (job < tiles_m * VT * VS) {
     is_v = true;
     mt = job % tiles_m;
-    nt = job / tiles_m;
+    nt = (job / tiles_m) % VT;
+    js = job / (tiles_m * VT);
   } else {
     is_v = false;
-    job -= tiles_m * VT;
+    job -= tiles_m * VT * VS;
     mt = job / H;
     h = job % H;
   }
   constexpr int HD = H * D;
-  const half_t* A = is_v ? a.v : a.k + (size_t)h * D;
-  const half_t* B = is_v ? a.W + nt * TT_N : a.U + (size_t)h * D * RK;
+  constexpr int KS = HD / VS;  // value contraction per split
+  static_assert(KS % TK == 0, "whole K steps per split");
+  const half_t* A = is_v ? a.v + (size_t)js * KS : a.k + (size_t)h * D;
+  const half_t* B = is_v ? a.W + (size_t)js * KS * RV + nt * TT_N : a.U + (size_t)h * D * RK;
   const int ldb = is_v ? RV : RK;
-  const int n_steps = (is_v ? HD : D) / TK;
+  const int n_steps = (is_v ? KS : D) / TK;
   const int m_base = mt * TT_M;
 
   // staging roles: A chunk i is row a_row[i], k offset a_k[i]; B chunk j is
@@ -546,13 +562,31 @@ __global__ __launch_bounds__(512) void append_tiled_kernel(AppendArgs a) {
   if constexpr (RING > 2)
     if (s + 2 < n_steps) iter(std::integral_constant<int, 3 % RING>{}, s + 2);
 
-  // epilogue: register i holds token 8*(i/4) + 4*hf + i%4, output c32
+  // epilogue: register i holds token 8*(i/4) + 4*hf + i%4, output c32.  The
+  // 16 slots are requested together (indices clamped into range): loaded
+  // inside the checks below, each would wait for the one before it, 16
+  // memory round trips at the end of every work group.
   const int n = wn * 32 + c32;
+  if constexpr (VS > 1) {
+    if (is_v) {  // partial products: 32 consecutive outputs of a token per store
+      float* dst = a.part + (size_t)js * a.N * RV + nt * TT_N + n;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m_base + wm * 32 + 8 * (i / 4) + 4 * hf + (i % 4);
+        if (m < a.N) dst[(size_t)m * RV] = acc[i];
+      }
+      return;
+    }
+  }
+  int64_t slot_of[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    slot_of[i] = a.slots[min(m_base + wm * 32 + 8 * (i / 4) + 4 * hf + (i % 4), a.N - 1)];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int m = m_base + wm * 32 + 8 * (i / 4) + 4 * hf + (i % 4);
     if (m >= a.N) continue;
-    const int64_t slot = a.slots[m];
+    const int64_t slot = slot_of[i];
     if (slot < 0) continue;
     const int64_t blk = slot / 16;
     const int off = (int)(slot % 16);
@@ -573,9 +607,25 @@ static int append_variant() {
   return v;
 }
 
+// Splits of the value contraction in the many-token path at the main shape
+// (32 key/value heads, d 128, r_k 64, r_v 512).  Alone, a value job's 64
+// serial K steps take about 42 us whatever the chunk size, so small chunks
+// gain from shorter jobs; from about 3k tokens the chip is busy without the
+// split and the partials' round trip costs more than it saves.  Measured:
+// 512 tokens 41 -> 17 us (four ways), 2048 tokens 44 -> 35 us (two ways),
+// 4096 tokens 49 us unsplit against 60 (two ways).
+constexpr int kSplit4MaxTokens = 1792;
+constexpr int kSplit2MaxTokens = 2816;
+static int tiled_splits(const ShapeKey& s, int n_tokens) {
+  if (!(s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) || n_tokens <= kSmallN) return 1;
+  return n_tokens <= kSplit4MaxTokens ? 4 : n_tokens <= kSplit2MaxTokens ? 2 : 1;
+}
+
 size_t append_workspace_bytes(const ShapeKey& s, int n_tokens) {
-  if (n_tokens <= 0 || n_tokens > kSmallN) return 0;
-  return (size_t)(s.H * s.d / kSliceRows) * n_tokens * s.rv * sizeof(float);
+  if (n_tokens <= 0) return 0;
+  if (n_tokens <= kSmallN) return (size_t)(s.H * s.d / kSliceRows) * n_tokens * s.rv * sizeof(float);
+  const int vs = tiled_splits(s, n_tokens);
+  return vs > 1 ? (size_t)vs * n_tokens * s.rv * sizeof(float) : 0;
 }
 
 template <int H, int D, int RK, int RV>
@@ -657,9 +707,27 @@ hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const 
         launch_hooked(TIME_APPEND, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 128, 3>, grid,
                       dim3(512), st, a);
         break;
-      default:
-        launch_hooked(TIME_APPEND, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 64, 1>, grid,
-                      dim3(512), st, a);
+      default: {
+        // value contraction split VS ways, the partials summed by the
+        // reduction (the workspace holds exactly the chosen split's partials)
+        const int vs = workspace == nullptr ? 1 : tiled_splits(s, n_tokens);
+        const dim3 gridv((unsigned)(tiles_m * (vs * 512 / TT_N + 32)));
+        const dim3 gridr((unsigned)((a.N * (512 / 4) + 63) / 64));
+        if (vs == 4) {
+          launch_hooked(TIME_NONE, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 64, 1, 4>,
+                        gridv, dim3(512), st, a);
+          launch_hooked(TIME_APPEND, TIME_NONE, append_reduce_kernel<512, 4>, gridr, dim3(256),
+                        st, a);
+        } else if (vs == 2) {
+          launch_hooked(TIME_NONE, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 64, 1, 2>,
+                        gridv, dim3(512), st, a);
+          launch_hooked(TIME_APPEND, TIME_NONE, append_reduce_kernel<512, 2>, gridr, dim3(256),
+                        st, a);
+        } else {
+          launch_hooked(TIME_APPEND, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 64, 1>,
+                        grid, dim3(512), st, a);
+        }
+      }
     }
     return hipGetLastError();
   }

@@ -31,7 +31,7 @@ def test_exports_match_header():
 
 
 def test_version_and_status_strings():
-    assert sk.abi_version() == 3
+    assert sk.abi_version() == 4
     for s in range(0, 8):
         assert sk.lib().starkv_status_string(s)
     assert sk.lib().starkv_status_string(99) == b"unknown status"
@@ -107,12 +107,20 @@ def test_append_validation():
 
 
 def test_append_workspace_size():
-    """fp32 partials of the value projection over 64-row slices of W for up to
-    64 tokens, nothing beyond."""
+    """fp32 partials of the value projection: over 64-row slices of W for up to
+    64 tokens; beyond that, at the main shape, over four parts of the
+    contraction up to 1792 tokens, two parts up to 2816, none above; nothing
+    at the other shapes."""
     d = _main_dims()
     assert sk.append_workspace_size(d, 16) == (32 * 128 // 64) * 16 * 512 * 4
     assert sk.append_workspace_size(d, 64) == (32 * 128 // 64) * 64 * 512 * 4
-    assert sk.append_workspace_size(d, 65) == 0
+    assert sk.append_workspace_size(d, 65) == 4 * 65 * 512 * 4
+    assert sk.append_workspace_size(d, 1792) == 4 * 1792 * 512 * 4
+    assert sk.append_workspace_size(d, 1793) == 2 * 1793 * 512 * 4
+    assert sk.append_workspace_size(d, 2816) == 2 * 2816 * 512 * 4
+    assert sk.append_workspace_size(d, 2817) == 0
+    assert sk.append_workspace_size(d, 4096) == 0
+    assert sk.append_workspace_size(sk.make_dims(32, 128, 32, 256, 8), 1024) == 0
     assert sk.append_workspace_size(d, 0) == 0
     # grouped-query caches: only the key/value heads enter
     assert sk.append_workspace_size(sk.make_dims(32, 128, 64, 512, 8, num_kv_heads=8), 16) == 16 * 16 * 512 * 4

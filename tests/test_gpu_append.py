@@ -76,13 +76,17 @@ def _check(gk, gv, rk, rv, what):
     assert okk.all() and okv.all()
 
 
-# token counts on both sides of the few-token kernel's limit (64 tokens)
+# token counts on both sides of the few-token kernel's limit (64 tokens), and
+# at the main shape in each range of the many-token path's contraction split
+# (four ways to 1792 tokens, two ways to 2816, none above: main_2000 and the
+# full-size chunk test below)
 @pytest.mark.parametrize("shape,n,seed,neg", [(wl.MAIN, 16, 31, 0), (wl.MAIN, 300, 32, 7),
                                               (wl.TINY, 5, 33, 2), (wl.TINY, 130, 34, 0),
                                               (wl.MAIN, 1, 37, 0), (wl.MAIN, 64, 38, 5),
-                                              (wl.MAIN, 65, 39, 0), (wl.TINY, 64, 40, 3)],
+                                              (wl.MAIN, 65, 39, 0), (wl.TINY, 64, 40, 3),
+                                              (wl.MAIN, 2000, 41, 9)],
                          ids=["main_decode_step", "main_ragged_300", "tiny_5", "tiny_130",
-                              "main_1", "main_64", "main_65", "tiny_64"])
+                              "main_1", "main_64", "main_65", "tiny_64", "main_2000"])
 def test_append_matches_oracle(sk, shape, n, seed, neg):
     U, W, k, v, slots, kc, vc = _case(shape, n, seed, neg)
     note(f"append {shape} n={n}")
