@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define STARKV_ABI_VERSION 4
+#define STARKV_ABI_VERSION 5
 
 typedef enum {
   STARKV_OK = 0,
@@ -191,6 +191,38 @@ starkv_status starkv_decode_attn(const starkv_dims* dims, const void* q, const v
                                  const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
                                  float scale, void* out, void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/*
+ * Split plan of a decode call (host struct).  The decode step splits each
+ * sequence's pages over work groups (split-K, README "Kernel profiling
+ * breakdown": split-K attention plus a combine) and merges the splits' partial
+ * softmax states; the plan fixes how.  Each field is 0 for the library's
+ * choice (what starkv_decode_attn uses) or a value in range:
+ *   pages_per_split  1..256 consecutive 16-token pages per work group
+ *   merge_seqs       sequences per work group of the merge: 1, 2, 4 or 8
+ * Any plan gives the same attention up to rounding order.
+ */
+typedef struct {
+  int32_t pages_per_split;
+  int32_t merge_seqs;
+} starkv_decode_config;
+
+/*
+ * starkv_decode_workspace_size and starkv_decode_attn with the caller's plan
+ * (cfg may be NULL: the library's plan).  A field out of range returns
+ * STARKV_ERR_ARG.  The workspace must be sized with the same cfg.
+ */
+starkv_status starkv_decode_workspace_size_cfg(const starkv_dims* dims, int32_t batch,
+                                               int32_t max_seq_len,
+                                               const starkv_decode_config* cfg /* (host) */,
+                                               size_t* bytes /* (host) */);
+starkv_status starkv_decode_attn_cfg(const starkv_dims* dims, const void* q, const void* k_cache,
+                                     const void* v_cache, const void* U, const void* W,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* seq_lens, int32_t batch,
+                                     int32_t max_seq_len, float scale,
+                                     const starkv_decode_config* cfg /* (host) */, void* out,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * starkv_decode_attn over FP8 caches (see starkv_append_fp8): the same

@@ -3,7 +3,6 @@
 // so a rejected call enqueues nothing; no C++ exception crosses the ABI.
 #include <cmath>
 #include <initializer_list>
-#include <cstdlib>
 
 #include "../../include/starkv.h"
 #include "kernels.h"
@@ -36,13 +35,6 @@ static bool kv_shape_supported(const ShapeKey& s) {
          (s.d == 64 && s.rk == 16 && s.rv == 64 && (s.Hkv == 4 || s.Hkv == 2));
 }
 
-static int env_int(const char* name, int dflt) {
-  const char* v = std::getenv(name);
-  if (!v || !*v) return dflt;
-  const int x = std::atoi(v);
-  return x > 0 ? x : dflt;
-}
-
 static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
 // Number of compute units of the current device (queried once per device;
@@ -63,15 +55,15 @@ static int device_cus() {
 // The merge + up-projection tile.  TB sequences per work group: 1 when the
 // batch is too small to give every CU a (head, sequence) pair, else the
 // widest of 2, 4, 8 that still gives a work group per CU (each work group
-// reads all of W_h, so wide groups cut that traffic at large batch), or
-// STARKV_DECODE_FINISH_TB.  The merge requests CB splits per round and
+// reads all of W_h, so wide groups cut that traffic at large batch), unless
+// the caller fixes TB.  The merge requests CB splits per round and
 // thread; with many splits (small batch, long sequences) the work group
 // grows to 512 threads whose split groups take disjoint sets of splits, so
 // the partials are requested in fewer rounds (1024 threads would leave 128
 // registers per thread, too few for the operands in flight).
-static DecodePlan with_finish(DecodePlan p, const ShapeKey& s, int batch) {
+static DecodePlan with_finish(DecodePlan p, const ShapeKey& s, int batch, int force_tb) {
   const int cus = device_cus();
-  int tb = env_int("STARKV_DECODE_FINISH_TB", 0);
+  int tb = force_tb;
   if (tb != 1 && tb != 2 && tb != 4 && tb != 8) {
     tb = (long)s.H * batch < cus ? 1 : 2;
     while (tb >= 2 && tb < 8 && (long)s.H * cdiv(batch, 2 * tb) >= cus) tb *= 2;
@@ -101,27 +93,18 @@ static DecodePlan with_finish(DecodePlan p, const ShapeKey& s, int batch) {
 // preferring fewer splits on ties; pages_per_split <= 256 (block ids are
 // staged in LDS).  The weight 6 of the per-split term comes from sweeps at
 // batch 1-64 (2K-32K tokens), where it picks the fastest plan or one within
-// a few percent of it.  Environment overrides (tuning aids):
-// STARKV_DECODE_TARGET_WGS / STARKV_DECODE_MIN_PAGES switch to a fixed
-// target of work groups with a minimum split length, and
-// STARKV_DECODE_SPLIT_COST (in tenths) replaces the weight 6.
-static double split_cost_weight() {
-  const int tenths = env_int("STARKV_DECODE_SPLIT_COST", 0);
-  return tenths > 0 ? tenths / 10.0 : 6.0;
-}
+// a few percent of it.  A caller may fix pages_per_split (force_pps > 0,
+// at most 256) and the merge tile (force_tb in {1, 2, 4, 8}); the plan is
+// otherwise a function of the shape, batch, length bound and device only.
+constexpr double kSplitCost = 6.0;
 
-DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int bs) {
-  const double kSplitCost = split_cost_weight();
+DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int bs, int force_pps,
+                       int force_tb) {
   const int pages = cdiv(max_seq_len, bs);
-  const int variant = env_int("STARKV_DECODE_VARIANT", 0);
-  if (pages <= 0 || batch <= 0) return with_finish(DecodePlan{1, 1, variant, 0, 0, 0, 0}, s, batch);
-  const int target = env_int("STARKV_DECODE_TARGET_WGS", 0);
-  if (target > 0) {
-    const int min_pps = env_int("STARKV_DECODE_MIN_PAGES", 1);
-    int pps = cdiv(pages, cdiv(target, batch));
-    if (pps < min_pps) pps = min_pps;
-    if (pps > 256) pps = 256;
-    return with_finish(DecodePlan{pps, cdiv(pages, pps), variant, 0, 0, 0, 0}, s, batch);
+  if (pages <= 0 || batch <= 0) return with_finish(DecodePlan{1, 1, 0, 0, 0, 0}, s, batch, force_tb);
+  if (force_pps > 0) {
+    const int pps = force_pps < 256 ? force_pps : 256;
+    return with_finish(DecodePlan{pps, cdiv(pages, pps), 0, 0, 0, 0}, s, batch, force_tb);
   }
   const int cus = device_cus();
   double best = 1e300;
@@ -138,7 +121,7 @@ DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int bs) {
     }
     if (ns > 4 * cus) break;
   }
-  return with_finish(DecodePlan{best_pps, cdiv(pages, best_pps), variant, 0, 0, 0, 0}, s, batch);
+  return with_finish(DecodePlan{best_pps, cdiv(pages, best_pps), 0, 0, 0, 0}, s, batch, force_tb);
 }
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -148,7 +131,7 @@ DecodeWorkspace decode_workspace_layout(const ShapeKey& s, int batch, const Deco
   DecodeWorkspace w;
   size_t off = 0;
   w.qt_off = off;
-  off = align256(off + (size_t)batch * s.H * s.rk * 2);
+  off = align256(off + (size_t)batch * s.H * s.rk * 4);  // q~, fp32
   w.ml_off = off;
   off = align256(off + (size_t)batch * p.split_stride * 2 * r16 * 4);
   w.zp_off = off;  // per-split z rows, fp16
@@ -161,7 +144,7 @@ PrefillWorkspace prefill_workspace_layout(const ShapeKey& s, int total_q) {
   PrefillWorkspace w;
   size_t off = 0;
   w.qt_off = off;
-  off = align256(off + (size_t)total_q * s.H * s.rk * 2);
+  off = align256(off + (size_t)total_q * s.H * s.rk * 4);  // q~, fp32
   w.z_off = off;  // fp16 z tiled by 32-token blocks, see launch_upproj_tiled
   off = align256(off + (size_t)((total_q + 31) / 32) * 32 * s.H * s.rv * 2);
   w.total = off;
@@ -332,16 +315,93 @@ starkv_status starkv_append_fp8(const starkv_dims* dims, const void* k, const vo
   return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
 }
 
-starkv_status starkv_decode_workspace_size(const starkv_dims* dims, int32_t batch,
-                                           int32_t max_seq_len, size_t* bytes) {
+}  // extern "C"
+
+namespace {
+
+// A caller's plan override: each field 0 (the planner's choice) or in range.
+starkv_status check_config(const starkv_decode_config* cfg) {
+  if (!cfg) return STARKV_OK;
+  if (cfg->pages_per_split < 0 || cfg->pages_per_split > 256) return STARKV_ERR_ARG;
+  const int m = cfg->merge_seqs;
+  if (m != 0 && m != 1 && m != 2 && m != 4 && m != 8) return STARKV_ERR_ARG;
+  return STARKV_OK;
+}
+
+DecodePlan plan_for(const ShapeKey& key, int batch, int max_seq_len, int bs,
+                    const starkv_decode_config* cfg) {
+  return plan_decode(key, batch, max_seq_len, bs, cfg ? cfg->pages_per_split : 0,
+                     cfg ? cfg->merge_seqs : 0);
+}
+
+starkv_status workspace_size(const starkv_dims* dims, int32_t batch, int32_t max_seq_len,
+                             const starkv_decode_config* cfg, size_t* bytes) {
   ShapeKey key;
   starkv_status st = check_dims(dims, &key);
   if (st != STARKV_OK) return st;
   if (!bytes) return STARKV_ERR_NULL;
   if (batch < 0 || max_seq_len < 0 || batch > 65535) return STARKV_ERR_DIMS;
-  const DecodePlan p = plan_decode(key, batch, max_seq_len, dims->block_size);
-  *bytes = decode_workspace_layout(key, batch, p).total;
+  st = check_config(cfg);
+  if (st != STARKV_OK) return st;
+  *bytes = decode_workspace_layout(key, batch, plan_for(key, batch, max_seq_len, dims->block_size, cfg)).total;
   return STARKV_OK;
+}
+
+// Every decode entry point: host checks, then the q projection (the key
+// scale, FP8 only, folds into q~), the split-K pass and the merge.
+starkv_status decode_common(const starkv_dims* dims, const void* q, const void* k_cache,
+                            const void* v_cache, const void* U, const void* W,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                            float scale, const LatentFormat& fmt, const starkv_decode_config* cfg,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  ShapeKey key;
+  starkv_status st = check_dims(dims, &key);
+  if (st != STARKV_OK) return st;
+  if (fmt.fp8 && !fp8_decode_supported(key)) return STARKV_ERR_UNSUPPORTED;
+  st = check_paging(batch, max_seq_len, max_blocks_per_seq, dims->block_size);
+  if (st != STARKV_OK) return st;
+  if (!scale_ok(scale) || !scale_ok(fmt.k_scale) || !scale_ok(fmt.v_scale)) return STARKV_ERR_ARG;
+  st = check_config(cfg);
+  if (st != STARKV_OK) return st;
+  if (batch == 0) return STARKV_OK;
+  st = check_ptrs({q, k_cache, v_cache, U, W, block_tables, seq_lens, out, workspace});
+  if (st != STARKV_OK) return st;
+  const DecodePlan p = plan_for(key, batch, max_seq_len, dims->block_size, cfg);
+  const DecodeWorkspace ws = decode_workspace_layout(key, batch, p);
+  if (workspace_bytes < ws.total) return STARKV_ERR_WORKSPACE;
+  char* wb = (char*)workspace;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_qproj(key, q, U, batch, scale * (fmt.fp8 ? fmt.k_scale : 1.f),
+                              wb + ws.qt_off, TIME_DECODE_SPLIT, s, W);
+  if (e != hipSuccess) return STARKV_ERR_LAUNCH;
+  e = launch_decode(key, p, wb + ws.qt_off, k_cache, v_cache, W, block_tables,
+                    max_blocks_per_seq, seq_lens, dims->num_blocks, batch,
+                    (float*)(wb + ws.ml_off), wb + ws.zp_off, out, fmt, s);
+  return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
+}
+
+LatentFormat fp8_format(float k_scale, float v_scale) {
+  LatentFormat fmt;
+  fmt.fp8 = true;
+  fmt.k_scale = k_scale;
+  fmt.v_scale = v_scale;
+  return fmt;
+}
+
+}  // namespace
+
+extern "C" {
+
+starkv_status starkv_decode_workspace_size(const starkv_dims* dims, int32_t batch,
+                                           int32_t max_seq_len, size_t* bytes) {
+  return workspace_size(dims, batch, max_seq_len, nullptr, bytes);
+}
+
+starkv_status starkv_decode_workspace_size_cfg(const starkv_dims* dims, int32_t batch,
+                                               int32_t max_seq_len,
+                                               const starkv_decode_config* cfg, size_t* bytes) {
+  return workspace_size(dims, batch, max_seq_len, cfg, bytes);
 }
 
 starkv_status starkv_decode_plan(const starkv_dims* dims, int32_t batch, int32_t max_seq_len,
@@ -363,26 +423,21 @@ starkv_status starkv_decode_attn(const starkv_dims* dims, const void* q, const v
                                  const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
                                  float scale, void* out, void* workspace, size_t workspace_bytes,
                                  void* stream) {
-  ShapeKey key;
-  starkv_status st = check_dims(dims, &key);
-  if (st != STARKV_OK) return st;
-  st = check_paging(batch, max_seq_len, max_blocks_per_seq, dims->block_size);
-  if (st != STARKV_OK) return st;
-  if (!scale_ok(scale)) return STARKV_ERR_ARG;
-  if (batch == 0) return STARKV_OK;
-  st = check_ptrs({q, k_cache, v_cache, U, W, block_tables, seq_lens, out, workspace});
-  if (st != STARKV_OK) return st;
-  const DecodePlan p = plan_decode(key, batch, max_seq_len, dims->block_size);
-  const DecodeWorkspace ws = decode_workspace_layout(key, batch, p);
-  if (workspace_bytes < ws.total) return STARKV_ERR_WORKSPACE;
-  char* wb = (char*)workspace;
-  const hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_qproj(key, q, U, batch, scale, wb + ws.qt_off, TIME_DECODE_SPLIT, s, W);
-  if (e != hipSuccess) return STARKV_ERR_LAUNCH;
-  e = launch_decode(key, p, wb + ws.qt_off, k_cache, v_cache, W, block_tables,
-                    max_blocks_per_seq, seq_lens, dims->num_blocks, batch,
-                    (float*)(wb + ws.ml_off), wb + ws.zp_off, out, LatentFormat{}, s);
-  return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
+  return decode_common(dims, q, k_cache, v_cache, U, W, block_tables, max_blocks_per_seq,
+                       seq_lens, batch, max_seq_len, scale, LatentFormat{}, nullptr, out,
+                       workspace, workspace_bytes, stream);
+}
+
+starkv_status starkv_decode_attn_cfg(const starkv_dims* dims, const void* q, const void* k_cache,
+                                     const void* v_cache, const void* U, const void* W,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* seq_lens, int32_t batch,
+                                     int32_t max_seq_len, float scale,
+                                     const starkv_decode_config* cfg, void* out, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return decode_common(dims, q, k_cache, v_cache, U, W, block_tables, max_blocks_per_seq,
+                       seq_lens, batch, max_seq_len, scale, LatentFormat{}, cfg, out, workspace,
+                       workspace_bytes, stream);
 }
 
 starkv_status starkv_decode_attn_fp8(const starkv_dims* dims, const void* q,
@@ -392,33 +447,9 @@ starkv_status starkv_decode_attn_fp8(const starkv_dims* dims, const void* q,
                                      int32_t batch, int32_t max_seq_len, float scale,
                                      float k_scale, float v_scale, void* out, void* workspace,
                                      size_t workspace_bytes, void* stream) {
-  ShapeKey key;
-  starkv_status st = check_dims(dims, &key);
-  if (st != STARKV_OK) return st;
-  if (!fp8_decode_supported(key)) return STARKV_ERR_UNSUPPORTED;
-  st = check_paging(batch, max_seq_len, max_blocks_per_seq, dims->block_size);
-  if (st != STARKV_OK) return st;
-  if (!scale_ok(scale) || !scale_ok(k_scale) || !scale_ok(v_scale)) return STARKV_ERR_ARG;
-  if (batch == 0) return STARKV_OK;
-  st = check_ptrs({q, k_cache8, v_cache8, U, W, block_tables, seq_lens, out, workspace});
-  if (st != STARKV_OK) return st;
-  const DecodePlan p = plan_decode(key, batch, max_seq_len, dims->block_size);
-  const DecodeWorkspace ws = decode_workspace_layout(key, batch, p);
-  if (workspace_bytes < ws.total) return STARKV_ERR_WORKSPACE;
-  char* wb = (char*)workspace;
-  const hipStream_t s = (hipStream_t)stream;
-  // the key scale folds into q~, the value scale into the split partials
-  hipError_t e = launch_qproj(key, q, U, batch, scale * k_scale, wb + ws.qt_off,
-                              TIME_DECODE_SPLIT, s, W);
-  if (e != hipSuccess) return STARKV_ERR_LAUNCH;
-  LatentFormat fmt;
-  fmt.fp8 = true;
-  fmt.k_scale = k_scale;
-  fmt.v_scale = v_scale;
-  e = launch_decode(key, p, wb + ws.qt_off, k_cache8, v_cache8, W, block_tables,
-                    max_blocks_per_seq, seq_lens, dims->num_blocks, batch,
-                    (float*)(wb + ws.ml_off), wb + ws.zp_off, out, fmt, s);
-  return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
+  return decode_common(dims, q, k_cache8, v_cache8, U, W, block_tables, max_blocks_per_seq,
+                       seq_lens, batch, max_seq_len, scale, fp8_format(k_scale, v_scale),
+                       nullptr, out, workspace, workspace_bytes, stream);
 }
 
 starkv_status starkv_prefill_workspace_size(const starkv_dims* dims, int32_t batch,

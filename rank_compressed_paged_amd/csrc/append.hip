@@ -15,7 +15,6 @@
 // (nearest even), or to FP8 E4M3 codes of latent / scale for FP8 caches, and
 // writes slot_mapping[n]; negative or out-of-range slots are skipped.
 // Layouts: k_cache [NB, H, 16, r_k], v_cache [NB, r_v, 16].
-#include <stdlib.h>
 
 #include <type_traits>
 
@@ -598,15 +597,6 @@ __global__ __launch_bounds__(512) void append_tiled_kernel(AppendArgs a) {
   }
 }
 
-// Kernel variant of the many-token path (tuning aid, STARKV_APPEND_VARIANT).
-static int append_variant() {
-  static const int v = [] {
-    const char* e = getenv("STARKV_APPEND_VARIANT");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
-}
-
 // Splits of the value contraction in the many-token path at the main shape
 // (32 key/value heads, d 128, r_k 64, r_v 512).  Alone, a value job's 64
 // serial K steps take about 42 us whatever the chunk size, so small chunks
@@ -694,40 +684,22 @@ hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const 
   if (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) {
     const long tiles_m = (n_tokens + TT_M - 1) / TT_M;
     const dim3 grid((unsigned)(tiles_m * (512 / TT_N + 32)));
-    switch (append_variant()) {
-      case 1:
-        launch_hooked(TIME_APPEND, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 64, 4>, grid,
-                      dim3(512), st, a);
-        break;
-      case 2:
-        launch_hooked(TIME_APPEND, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 128, 2>, grid,
-                      dim3(512), st, a);
-        break;
-      case 3:
-        launch_hooked(TIME_APPEND, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 128, 3>, grid,
-                      dim3(512), st, a);
-        break;
-      default: {
-        // value contraction split VS ways, the partials summed by the
-        // reduction (the workspace holds exactly the chosen split's partials)
-        const int vs = workspace == nullptr ? 1 : tiled_splits(s, n_tokens);
-        const dim3 gridv((unsigned)(tiles_m * (vs * 512 / TT_N + 32)));
-        const dim3 gridr((unsigned)((a.N * (512 / 4) + 63) / 64));
-        if (vs == 4) {
-          launch_hooked(TIME_NONE, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 64, 1, 4>,
-                        gridv, dim3(512), st, a);
-          launch_hooked(TIME_APPEND, TIME_NONE, append_reduce_kernel<512, 4>, gridr, dim3(256),
-                        st, a);
-        } else if (vs == 2) {
-          launch_hooked(TIME_NONE, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 64, 1, 2>,
-                        gridv, dim3(512), st, a);
-          launch_hooked(TIME_APPEND, TIME_NONE, append_reduce_kernel<512, 2>, gridr, dim3(256),
-                        st, a);
-        } else {
-          launch_hooked(TIME_APPEND, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 64, 1>,
-                        grid, dim3(512), st, a);
-        }
-      }
+    // value contraction split VS ways, the partials summed by the reduction
+    // (the workspace holds exactly the chosen split's partials)
+    const int vs = workspace == nullptr ? 1 : tiled_splits(s, n_tokens);
+    const dim3 gridv((unsigned)(tiles_m * (vs * 512 / TT_N + 32)));
+    const dim3 gridr((unsigned)((a.N * (512 / 4) + 63) / 64));
+    if (vs == 4) {
+      launch_hooked(TIME_NONE, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 64, 1, 4>, gridv,
+                    dim3(512), st, a);
+      launch_hooked(TIME_APPEND, TIME_NONE, append_reduce_kernel<512, 4>, gridr, dim3(256), st, a);
+    } else if (vs == 2) {
+      launch_hooked(TIME_NONE, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 64, 1, 2>, gridv,
+                    dim3(512), st, a);
+      launch_hooked(TIME_APPEND, TIME_NONE, append_reduce_kernel<512, 2>, gridr, dim3(256), st, a);
+    } else {
+      launch_hooked(TIME_APPEND, TIME_NONE, append_tiled_kernel<32, 128, 64, 512, 64, 1>, grid,
+                    dim3(512), st, a);
     }
     return hipGetLastError();
   }

@@ -52,7 +52,8 @@ struct DecodeCfg {
   static constexpr int FT = FPW / 16;       // 16-feature tiles per wave
   static constexpr int KC = (RK % 32 == 0) ? 32 : 16;
   static constexpr int NKC = RK / KC;
-  static_assert(H % NW == 0 && HPW >= 1 && HPW <= 16, "heads per wave must be 1..16");
+  static_assert(H % NW == 0 && (HPW == 1 || HPW == 2 || HPW == 4 || HPW == 8),
+                "heads per wave: a power of two up to 8 (q~ hi and lo take 2 HPW columns)");
   static_assert(RV % (16 * NW) == 0, "value rank must split into 16-wide tiles per wave");
   static_assert(RK % 16 == 0, "key rank must be a multiple of 16");
 };
@@ -61,8 +62,12 @@ constexpr int BS = 16;  // tokens per page
 constexpr int kMaxSplitPages = 256;  // planner bound on pages per split
 
 // ---------------------------------------------------------------------------
-// 1. q~[n, h, :] = (scale*log2e) * U_g^T q[n, h, :]  -> fp16, g = h / QG the
-//    key/value head of query head h (QG = 1: multi-head attention)
+// 1. q~[n, h, :] = (scale*log2e) * U_g^T q[n, h, :]  -> fp32, g = h / QG the
+//    key/value head of query head h (QG = 1: multi-head attention).  q~ stays
+//    fp32: the attention kernels split it into an fp16 hi/lo pair for their
+//    score products, since one fp16 rounding of q~ moves a score by about
+//    2^-12 of its size, which peaked softmax rows (scores tens of units
+//    apart) turn into output errors above 1e-3.
 // grid (H, ceil(N/(64*TPW))), 4 waves; in token tile tt the wave w owns
 // tokens n0+16w .. n0+16w+15 of that tile's 64.  The product is taken as
 // q~^T = U_h^T q^T, so that each lane ends with 4 consecutive outputs of one
@@ -92,7 +97,7 @@ __device__ __forceinline__ half4 lds_read_tr16(const half_t* p) {
 template <int H, int D, int RK, int TPW, int QG>
 __global__ __launch_bounds__(256) void qproj_kernel(const half_t* __restrict__ q,
                                                     const half_t* __restrict__ U, int n_tokens,
-                                                    float qscale, half_t* __restrict__ qt,
+                                                    float qscale, float* __restrict__ qt,
                                                     int token_rows, const char* __restrict__ wpf,
                                                     int wpf_head_bytes, int wpf_part_bytes,
                                                     uint32_t* __restrict__ sink) {
@@ -159,27 +164,13 @@ __global__ __launch_bounds__(256) void qproj_kernel(const half_t* __restrict__ q
         acc[rt] = mfma16x16x32(au, bq[tt][k], acc[rt]);
       }
     }
-    // D[LDS column 16rt + 4*quad + r][token col] = rank 4NT*quad + 4rt + r
+    // D[LDS column 16rt + 4*quad + r][token col] = rank 4NT*quad + 4rt + r,
+    // so the lane's NT tiles are 4NT consecutive ranks of its token
     const int nt = nb + col;
     if (nt < n_tokens) {
-      half_t* dst = qt + ((size_t)nt * H + h) * RK + quad * 4 * NT;
-      if constexpr (NT % 2 == 0) {
+      float* dst = qt + ((size_t)nt * H + h) * RK + quad * 4 * NT;
 #pragma unroll
-        for (int p = 0; p < NT / 2; ++p) {
-          half8 o;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = (half_t)(acc[2 * p + e / 4][e % 4] * qscale);
-          *(half8*)(dst + 8 * p) = o;
-        }
-      } else {
-#pragma unroll
-        for (int rt = 0; rt < NT; ++rt) {
-          half4 o;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (half_t)(acc[rt][r] * qscale);
-          *(half4*)(dst + 4 * rt) = o;
-        }
-      }
+      for (int rt = 0; rt < NT; ++rt) *(float4v*)(dst + 4 * rt) = acc[rt] * qscale;
     }
   }
 }
@@ -313,9 +304,11 @@ __device__ __forceinline__ void process_page(
   using K = KeyCfg<H, RK, RV, NW, QG>;
   using kvec = typename PageRegs<H, RK, RV, NW, QG, FP8>::kvec;
   const kvec kzero = {};
-  // B column col holds q~ of query head w*HPW + col, whose key/value head is
-  // the wave's kk-th: the products for key page kk take only those columns
-  const int my_kk = col < C::HPW ? (w * C::HPW + col) / QG - w * C::HPW / QG : -1;
+  // B column col < HPW holds the fp16 hi part of q~ of query head
+  // w*HPW + col, column col + HPW its lo part; that head's key/value head is
+  // the wave's kk-th, and the products for key page kk take only its columns
+  const int hsel = col < C::HPW ? col : col - C::HPW;
+  const int my_kk = col < 2 * C::HPW ? (w * C::HPW + hsel) / QG - w * C::HPW / QG : -1;
   float4v sacc = zero4();
 #pragma unroll
   for (int kk = 0; kk < K::KPW; ++kk) {
@@ -328,6 +321,10 @@ __device__ __forceinline__ void process_page(
         sacc = mfma16x16x16(cur.key(kk, c), bq, sacc);
     }
   }
+  // score = hi product + lo product: the lo column of head col sits HPW
+  // lanes away in the same row of 16 (HPW is a power of two below 16)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) sacc[r] += __shfl_xor(sacc[r], C::HPW);
   float sv[4];
   float pm = -INFINITY;
 #pragma unroll
@@ -385,7 +382,7 @@ __device__ __forceinline__ void process_page(
 
 template <int H, int RK, int RV, int NW, int DEPTH, bool NT, int QG, bool FP8>
 __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
-    const half_t* __restrict__ qt, const latent_t<FP8>* __restrict__ k_cache,
+    const float* __restrict__ qt, const latent_t<FP8>* __restrict__ k_cache,
     const latent_t<FP8>* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ seq_lens, float* __restrict__ ml, half_t* __restrict__ zpart,
     int max_blocks, int num_blocks, int pages_per_split, int num_splits, int split_stride,
@@ -431,13 +428,26 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
   if (tid < 2) sFlag[tid] = -1;
   if (tid < p1 - p0) sBlk[tid] = ((unsigned)bid < (unsigned)num_blocks) ? bid : -1;
 
-  // q~ of head (w*HPW + col) for this lane's k chunks; B column col
+  // B column col: the fp16 hi part of q~ of head w*HPW + col (col < HPW) or
+  // the lo part of head w*HPW + col - HPW (HPW <= col < 2 HPW), for this
+  // lane's k chunks; hi + lo carries q~ to about 2^-22 of its size
   kvec qv[C::NKC];
   {
-    const int hq = w * C::HPW + (col < C::HPW ? col : 0);
-    const half_t* qp = qt + ((size_t)b * H + hq) * RK + quad * (C::KC / 4);
+    const int hsel = col < C::HPW ? col : (col < 2 * C::HPW ? col - C::HPW : 0);
+    const bool lo_part = col >= C::HPW;
+    const float* qp = qt + ((size_t)b * H + w * C::HPW + hsel) * RK + quad * (C::KC / 4);
 #pragma unroll
-    for (int c = 0; c < C::NKC; ++c) qv[c] = *(const kvec*)(qp + c * C::KC);
+    for (int c = 0; c < C::NKC; ++c) {
+#pragma unroll
+      for (int e4 = 0; e4 < C::KC / 16; ++e4) {
+        const float4v x = *(const float4v*)(qp + c * C::KC + 4 * e4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const half_t hi = (half_t)x[e];
+          qv[c][4 * e4 + e] = lo_part ? (half_t)(x[e] - (float)hi) : hi;
+        }
+      }
+    }
   }
 
   SplitState<H, RK, RV, NW> st;
@@ -853,7 +863,7 @@ static hipError_t decode_instance(const DecodePlan& p, const void* qt, const voi
                                   hipStream_t st) {
   launch_hooked(TIME_DECODE_SPLIT, TIME_NONE,
                 decode_split_kernel<H, RK, RV, NW, DEPTH, NT, QG, FP8>,
-                dim3(p.num_splits, batch), dim3(NW * 64), st, (const half_t*)qt,
+                dim3(p.num_splits, batch), dim3(NW * 64), st, (const float*)qt,
                 (const latent_t<FP8>*)k_cache, (const latent_t<FP8>*)v_cache, block_tables,
                 seq_lens, ml, (half_t*)zpart, max_blocks, num_blocks, p.pages_per_split,
                 p.num_splits, p.split_stride, v_scale);
@@ -896,12 +906,12 @@ static hipError_t qproj_instance(const void* q, const void* U, int n, float scal
     const int rows = (n + 255) / 256;
     launch_hooked(TIME_NONE, precedes, qproj_kernel<H, D, RK, 4, QG>, dim3(H, rows + pf_rows),
                   dim3(256), st, (const half_t*)q, (const half_t*)U, n, scale * kLog2e,
-                  (half_t*)qt, rows, (const char*)wpf, head_bytes, kPrefetchPart, (uint32_t*)nullptr);
+                  (float*)qt, rows, (const char*)wpf, head_bytes, kPrefetchPart, (uint32_t*)nullptr);
   } else {
     const int rows = (n + 63) / 64;
     launch_hooked(TIME_NONE, precedes, qproj_kernel<H, D, RK, 1, QG>, dim3(H, rows + pf_rows),
                   dim3(256), st, (const half_t*)q, (const half_t*)U, n, scale * kLog2e,
-                  (half_t*)qt, rows, (const char*)wpf, head_bytes, kPrefetchPart, (uint32_t*)nullptr);
+                  (float*)qt, rows, (const char*)wpf, head_bytes, kPrefetchPart, (uint32_t*)nullptr);
   }
   return hipGetLastError();
 }
@@ -945,18 +955,8 @@ hipError_t launch_decode(const ShapeKey& s, const DecodePlan& p, const void* qt,
     return decode_instance<4, 64, 16, 64, 4, 2, false, 2>(STARKV_DECODE_ARGS);
   if (s.H == 32 && s.Hkv == 32 && s.d == 128 && s.rk == 32 && s.rv == 256)
     return decode_instance<32, 128, 32, 256, 16, 2, false>(STARKV_DECODE_ARGS);
-  if (s.H == 32 && s.Hkv == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) {
-    // kernel variant (tuning aid): waves per group, prefetch depth, non-temporal loads
-    switch (p.variant) {
-      case 1: return decode_instance<32, 128, 64, 512, 4, 2, false>(STARKV_DECODE_ARGS);
-      case 2: return decode_instance<32, 128, 64, 512, 8, 3, false>(STARKV_DECODE_ARGS);
-      case 3: return decode_instance<32, 128, 64, 512, 8, 2, true>(STARKV_DECODE_ARGS);
-      case 4: return decode_instance<32, 128, 64, 512, 8, 2, false>(STARKV_DECODE_ARGS);
-      case 5: return decode_instance<32, 128, 64, 512, 8, 4, false>(STARKV_DECODE_ARGS);
-      case 6: return decode_instance<32, 128, 64, 512, 16, 3, false>(STARKV_DECODE_ARGS);
-      default: return decode_instance<32, 128, 64, 512, 16, 2, false>(STARKV_DECODE_ARGS);
-    }
-  }
+  if (s.H == 32 && s.Hkv == 32 && s.d == 128 && s.rk == 64 && s.rv == 512)
+    return decode_instance<32, 128, 64, 512, 16, 2, false>(STARKV_DECODE_ARGS);
   if (s.H == 4 && s.Hkv == 4 && s.d == 64 && s.rk == 16 && s.rv == 64)
     return decode_instance<4, 64, 16, 64, 4, 2, false>(STARKV_DECODE_ARGS);
 #undef STARKV_DECODE_ARGS

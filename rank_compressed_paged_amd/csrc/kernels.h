@@ -21,7 +21,6 @@ struct ShapeKey {
 struct DecodePlan {
   int pages_per_split;
   int num_splits;
-  int variant;    // split-kernel variant (0 = default)
   int finish_tb;     // sequences per work group of the merge + up-projection (1, 2, 4, 8)
   int finish_cb;     // splits per request round of each merging thread (4, 8, 16)
   int finish_nt;     // threads per work group of the merge (256, 512)
@@ -63,7 +62,10 @@ struct LatentFormat {
 };
 
 bool shape_supported(const ShapeKey& s);
-DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int block_size);
+// force_pps > 0 fixes the pages per split, force_tb in {1, 2, 4, 8} the
+// sequences per merge work group; 0 leaves either to the planner
+DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int block_size,
+                       int force_pps = 0, int force_tb = 0);
 DecodeWorkspace decode_workspace_layout(const ShapeKey& s, int batch, const DecodePlan& p);
 PrefillWorkspace prefill_workspace_layout(const ShapeKey& s, int total_q);
 

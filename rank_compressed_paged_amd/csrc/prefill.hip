@@ -43,8 +43,6 @@
 //     per step, so no block-table load sits on the critical path.
 //   * work groups of one request are placed on one XCD when the batch is a
 //     multiple of 8, so the request's latents are shared through that L2.
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "common.h"
@@ -99,7 +97,7 @@ struct PrefillCfg {
 };
 
 struct PrefillArgs {
-  const half_t* qt;  // [total_q, H, RK] fp16, pre-scaled
+  const float* qt;  // [total_q, H, RK] fp32, pre-scaled
   const int32_t* qsl;
   const void* k_cache;  // fp16, or FP8 E4M3 codes (same layouts)
   const void* v_cache;
@@ -216,7 +214,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
 
   // ---- this wave's score units: (head, 16 queries); lane column = query
   int su_h[C::SUW], su_row[C::SUW], su_lim[C::SUW];
-  kvec qv[C::SUW][C::NKC];
+  // q~ as an fp16 hi/lo pair (hi + lo = q~ to about 2^-22 of its size): the
+  // score products take both, so a score keeps fp32 accuracy in q~
+  kvec qv[C::SUW][C::NKC], ql[C::SUW][C::NKC];
 #pragma unroll
   for (int i = 0; i < C::SUW; ++i) {
     const int unit = w * C::SUW + i;
@@ -225,9 +225,19 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
     su_h[i] = g * G + hl;
     su_row[i] = hl * MQ + qb * 16 + col;
     su_lim[i] = min(L - 1, P0 + jq);                 // last visible key
-    const half_t* qp = a.qt + ((size_t)(q_begin + jq) * H + su_h[i]) * RK + quad * (C::KC / 4);
+    const float* qp = a.qt + ((size_t)(q_begin + jq) * H + su_h[i]) * RK + quad * (C::KC / 4);
 #pragma unroll
-    for (int c = 0; c < C::NKC; ++c) qv[i][c] = *(const kvec*)(qp + c * C::KC);
+    for (int c = 0; c < C::NKC; ++c)
+#pragma unroll
+      for (int e4 = 0; e4 < C::KC / 16; ++e4) {
+        const float4v x = *(const float4v*)(qp + c * C::KC + 4 * e4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const half_t hi = (half_t)x[e];
+          qv[i][c][4 * e4 + e] = hi;
+          ql[i][c][4 * e4 + e] = (half_t)(x[e] - (float)hi);
+        }
+      }
   }
   float m_run[C::SUW], l_run[C::SUW];
 #pragma unroll
@@ -370,10 +380,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
 #pragma unroll
         for (int c = 0; c < C::NKC; ++c) {
           const kvec kk = *(const kvec*)&sK[kb][hl][pg][col][c * C::KC + quad * (C::KC / 4)];
-          if constexpr (C::KC == 32)
+          if constexpr (C::KC == 32) {
             sacc[pg][i] = mfma16x16x32(kk, qv[i][c], sacc[pg][i]);
-          else
+            sacc[pg][i] = mfma16x16x32(kk, ql[i][c], sacc[pg][i]);
+          } else {
             sacc[pg][i] = mfma16x16x16(kk, qv[i][c], sacc[pg][i]);
+            sacc[pg][i] = mfma16x16x16(kk, ql[i][c], sacc[pg][i]);
+          }
         }
       }
   };
@@ -386,10 +399,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
         sacc[pg][i] = zero4();
 #pragma unroll
         for (int c = 0; c < C::NKC; ++c) {
-          if constexpr (C::KC == 32)
+          if constexpr (C::KC == 32) {
             sacc[pg][i] = mfma16x16x32(kk[pg][i][c], qv[i][c], sacc[pg][i]);
-          else
+            sacc[pg][i] = mfma16x16x32(kk[pg][i][c], ql[i][c], sacc[pg][i]);
+          } else {
             sacc[pg][i] = mfma16x16x16(kk[pg][i][c], qv[i][c], sacc[pg][i]);
+            sacc[pg][i] = mfma16x16x16(kk[pg][i][c], ql[i][c], sacc[pg][i]);
+          }
         }
       }
   };
@@ -806,7 +822,7 @@ static hipError_t prefill_instance(const void* qt, const int32_t* qsl, int max_q
                                    int total_q, void* z, void* out, float v_scale,
                                    hipStream_t st) {
   PrefillArgs a;
-  a.qt = (const half_t*)qt;
+  a.qt = (const float*)qt;
   a.qsl = qsl;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
@@ -830,16 +846,6 @@ static hipError_t prefill_instance(const void* qt, const int32_t* qsl, int max_q
   if (e != hipSuccess) return e;
   if constexpr (prefill_fused<G, MQ, NW, RV, D>()) return hipSuccess;  // out written by the kernel
   return launch_upproj_tiled(ShapeKey{H, D, RK, RV, H / QG}, W, z, total_q, out, st);
-}
-
-// Kernel variant (tuning aid, STARKV_PREFILL_VARIANT): head group, query
-// tile and instruction schedule of the main shape.
-static int prefill_variant() {
-  static const int v = [] {
-    const char* e = getenv("STARKV_PREFILL_VARIANT");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
 }
 
 hipError_t launch_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl, int total_q,
@@ -868,15 +874,8 @@ hipError_t launch_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl,
   // LDS key ring, so the waves load their keys directly
   if (s.H == 32 && s.Hkv == 32 && s.d == 128 && s.rk == 32 && s.rv == 256)
     return prefill_instance<32, 128, 32, 256, 2, 64, 8, 2, 2, 2, false>(STARKV_PREFILL_ARGS);
-  if (s.H == 32 && s.Hkv == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) {
-    switch (prefill_variant()) {
-      case 1: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 2, 1, true>(STARKV_PREFILL_ARGS);
-      case 2: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 2, 2, false>(STARKV_PREFILL_ARGS);
-      case 3: return prefill_instance<32, 128, 64, 512, 4, 32, 8, 2, 2, 2, true>(STARKV_PREFILL_ARGS);
-      case 4: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 2, 2, true>(STARKV_PREFILL_ARGS);
-      default: return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 3, 4, true>(STARKV_PREFILL_ARGS);
-    }
-  }
+  if (s.H == 32 && s.Hkv == 32 && s.d == 128 && s.rk == 64 && s.rv == 512)
+    return prefill_instance<32, 128, 64, 512, 2, 64, 8, 2, 3, 4, true>(STARKV_PREFILL_ARGS);
   if (s.H == 4 && s.Hkv == 4 && s.d == 64 && s.rk == 16 && s.rv == 64)
     return prefill_instance<4, 64, 16, 64, 4, 16, 2, 2, 2, 1, true>(STARKV_PREFILL_ARGS);
 #undef STARKV_PREFILL_ARGS

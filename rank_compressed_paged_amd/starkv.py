@@ -36,6 +36,7 @@ EXPORTED = [
     "starkv_util_stream_read", "starkv_util_event_create", "starkv_util_event_destroy",
     "starkv_util_event_elapsed_ms", "starkv_fit_workspace_size", "starkv_fit_bases",
     "starkv_append_fp8", "starkv_decode_attn_fp8", "starkv_prefill_attn_fp8",
+    "starkv_decode_workspace_size_cfg", "starkv_decode_attn_cfg",
 ]
 
 
@@ -44,6 +45,10 @@ class Dims(ctypes.Structure):
                 ("rank_k", ctypes.c_int32), ("rank_v", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32)]
+
+
+class DecodeConfig(ctypes.Structure):
+    _fields_ = [("pages_per_split", ctypes.c_int32), ("merge_seqs", ctypes.c_int32)]
 
 
 class StarKVError(RuntimeError):
@@ -75,6 +80,13 @@ _lib.starkv_decode_plan.argtypes = [ctypes.POINTER(Dims), _i32, _i32, ctypes.POI
 _lib.starkv_decode_attn.restype = _i32
 _lib.starkv_decode_attn.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                                     _i32, _i32, ctypes.c_float, _vp, _vp, _sz, _vp]
+_lib.starkv_decode_workspace_size_cfg.restype = _i32
+_lib.starkv_decode_workspace_size_cfg.argtypes = [ctypes.POINTER(Dims), _i32, _i32,
+                                                  ctypes.POINTER(DecodeConfig), ctypes.POINTER(_sz)]
+_lib.starkv_decode_attn_cfg.restype = _i32
+_lib.starkv_decode_attn_cfg.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                        _vp, _i32, _i32, ctypes.c_float,
+                                        ctypes.POINTER(DecodeConfig), _vp, _vp, _sz, _vp]
 _lib.starkv_prefill_workspace_size.restype = _i32
 _lib.starkv_prefill_workspace_size.argtypes = [ctypes.POINTER(Dims), _i32, _i32, _i32,
                                                ctypes.POINTER(_sz)]
@@ -162,10 +174,24 @@ def _stream(stream):
     return _vp(s.cuda_stream)
 
 
-def decode_workspace_size(dims, batch, max_seq_len):
+def _config(pages_per_split, merge_seqs):
+    """Plan override, or None for the library's plan."""
+    if not pages_per_split and not merge_seqs:
+        return None
+    return DecodeConfig(int(pages_per_split or 0), int(merge_seqs or 0))
+
+
+def decode_workspace_size(dims, batch, max_seq_len, pages_per_split=0, merge_seqs=0):
     out = _sz(0)
-    _check(_lib.starkv_decode_workspace_size(ctypes.byref(dims), int(batch), int(max_seq_len),
-                                             ctypes.byref(out)), "starkv_decode_workspace_size")
+    cfg = _config(pages_per_split, merge_seqs)
+    if cfg is None:
+        _check(_lib.starkv_decode_workspace_size(ctypes.byref(dims), int(batch), int(max_seq_len),
+                                                 ctypes.byref(out)), "starkv_decode_workspace_size")
+    else:
+        _check(_lib.starkv_decode_workspace_size_cfg(ctypes.byref(dims), int(batch),
+                                                     int(max_seq_len), ctypes.byref(cfg),
+                                                     ctypes.byref(out)),
+               "starkv_decode_workspace_size_cfg")
     return int(out.value)
 
 
@@ -263,8 +289,9 @@ def decode_attn_fp8(q, k_cache8, v_cache8, U, W, block_tables, seq_lens, max_seq
 
 
 def decode_attn(q, k_cache, v_cache, U, W, block_tables, seq_lens, max_seq_len, scale=None,
-                out=None, workspace=None, stream=None):
-    """Decode attention for q [B, H, d]; returns out [B, H, d] fp16."""
+                out=None, workspace=None, stream=None, pages_per_split=0, merge_seqs=0):
+    """Decode attention for q [B, H, d]; returns out [B, H, d] fp16.
+    pages_per_split / merge_seqs: a plan override (0 = the library's plan)."""
     dims = dims_of(k_cache, v_cache, U, W, num_heads=q.shape[1])
     B = q.shape[0]
     H, d = dims.num_heads, dims.head_dim
@@ -272,18 +299,22 @@ def decode_attn(q, k_cache, v_cache, U, W, block_tables, seq_lens, max_seq_len, 
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, H, d), dtype=torch.float16, device=q.device)
-    need = decode_workspace_size(dims, B, max_seq_len)
+    need = decode_workspace_size(dims, B, max_seq_len, pages_per_split, merge_seqs)
     if workspace is None:
         workspace = alloc_workspace(need, q.device)
-    st = _lib.starkv_decode_attn(
-        ctypes.byref(dims), _dev(q, torch.float16, "q", (B, H, d)),
-        _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"),
-        _dev(U, torch.float16, "U"), _dev(W, torch.float16, "W"),
-        _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
-        _dev(seq_lens, torch.int32, "seq_lens", (B,)), int(B), int(max_seq_len), float(scale),
-        _dev(out, torch.float16, "out", (B, H, d)), _dev(workspace, torch.uint8, "workspace"),
-        int(workspace.numel()), _stream(stream))
-    _check(st, "starkv_decode_attn")
+    args = [ctypes.byref(dims), _dev(q, torch.float16, "q", (B, H, d)),
+            _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"),
+            _dev(U, torch.float16, "U"), _dev(W, torch.float16, "W"),
+            _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
+            _dev(seq_lens, torch.int32, "seq_lens", (B,)), int(B), int(max_seq_len), float(scale)]
+    tail = [_dev(out, torch.float16, "out", (B, H, d)), _dev(workspace, torch.uint8, "workspace"),
+            int(workspace.numel()), _stream(stream)]
+    cfg = _config(pages_per_split, merge_seqs)
+    if cfg is None:
+        _check(_lib.starkv_decode_attn(*args, *tail), "starkv_decode_attn")
+    else:
+        _check(_lib.starkv_decode_attn_cfg(*args, ctypes.byref(cfg), *tail),
+               "starkv_decode_attn_cfg")
     return out
 
 

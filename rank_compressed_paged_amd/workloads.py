@@ -241,12 +241,57 @@ def draw_seq_lens(rng, B, seq):
     raise ValueError(seq)
 
 
+def _pow2(mult):
+    m = float(mult)
+    if m <= 0 or 2.0 ** round(np.log2(m)) != m:
+        raise ValueError("q_mult must be a power of two (exact in fp16)")
+    return m
+
+
+def plant_key_pairs(cache: PagedCache, where, factor):
+    """Sharpen the scores without touching the draws' order: in each sequence
+    and each chosen page ("first", "mid", "last"), the key latents of page
+    offsets 3 and 9 become +factor and -factor times offset 3's draw (fp16),
+    so one of the pair scores far above the rest in every head whatever the
+    query's sign.  Pages shorter than 10 tokens are skipped."""
+    bs = cache.shape.bs
+    for b, L in enumerate(cache.seq_lens):
+        n_pages = (int(L) + bs - 1) // bs
+        for w in where:
+            p = {"first": 0, "mid": n_pages // 2, "last": n_pages - 1}[w]
+            if p < 0 or (p + 1) * bs > int(L) and int(L) - p * bs < 10:
+                continue
+            blk = int(cache.block_tables[b, p])
+            base = cache.k_cache[blk, :, 3, :].astype(np.float32)
+            cache.k_cache[blk, :, 3, :] = (base * factor).astype(np.float16)
+            cache.k_cache[blk, :, 9, :] = (-base * factor).astype(np.float16)
+
+
+def ramp_keys(cache: PagedCache, ramp, lens=None):
+    """Key latents of token t scaled by 1 + ramp * t / L (fp16), so scores and
+    their running maximum rise along each sequence (L = lens[b], default the
+    sequence length; only the first L tokens are touched)."""
+    bs = cache.shape.bs
+    lens = cache.seq_lens if lens is None else lens
+    for b, L in enumerate(lens):
+        L = int(L)
+        for t in range(L):
+            blk = int(cache.block_tables[b, t // bs])
+            f = 1.0 + ramp * t / max(int(cache.seq_lens[b]), 1)
+            cache.k_cache[blk, :, t % bs, :] = (
+                cache.k_cache[blk, :, t % bs, :].astype(np.float32) * f).astype(np.float16)
+
+
 def make_decode_case(shape: Shape, seq_lens=None, B=None, seq=None, seed=0,
                      spare_blocks=1, shuffle=True, keep_logical=False,
-                     bases=None, extra_cols=0, name="", fp8=False):
+                     bases=None, extra_cols=0, name="", fp8=False, q_mult=1,
+                     plant=(), plant_factor=12.0, ramp=0.0):
     """One decode step: B sequences of seq_lens tokens, one query each.  With
     fp8 the caches hold FP8 E4M3 codes read with k_scale 1/4, v_scale 1/8
-    (latent magnitudes up to about 4 and 2)."""
+    (latent magnitudes up to about 4 and 2).  Sharper softmax rows, with the
+    same draws: q_mult (a power of two) scales q; plant puts a dominant +/-
+    key pair on the first / middle / last page (fp16 only); ramp makes the
+    scores rise along each sequence (fp16 only)."""
     rng = np.random.default_rng(seed)
     if bases is None:
         U, W = draw_bases(rng, shape)
@@ -259,6 +304,14 @@ def make_decode_case(shape: Shape, seq_lens=None, B=None, seq=None, seed=0,
                        fp8=fp8)
     q = rng.standard_normal((len(cache.seq_lens), shape.H, shape.d),
                             dtype=np.float32).astype(np.float16)
+    if q_mult != 1:
+        q = (q.astype(np.float32) * _pow2(q_mult)).astype(np.float16)
+    if (plant or ramp) and fp8:
+        raise ValueError("planted and ramped keys are fp16-cache options")
+    if plant:
+        plant_key_pairs(cache, plant, plant_factor)
+    if ramp:
+        ramp_keys(cache, ramp)
     if fp8:
         return DecodeCase(shape, U, W, cache, q, 1.0 / np.sqrt(shape.d), seed, name, 0.25, 0.125)
     return DecodeCase(shape, U, W, cache, q, 1.0 / np.sqrt(shape.d), seed, name)
@@ -266,11 +319,15 @@ def make_decode_case(shape: Shape, seq_lens=None, B=None, seq=None, seed=0,
 
 def make_prefill_case(shape: Shape, cached_lens, chunk_lens, seed=0,
                       spare_blocks=1, shuffle=True, keep_logical=False,
-                      bases=None, name="", fp8=False):
+                      bases=None, name="", fp8=False, q_mult=1, ramp=0.0):
     """One chunked-prefill step: request b has cached_lens[b] latent tokens and
     appends chunk_lens[b] new full-precision tokens, then attends causally.
     With fp8 the cached latents are FP8 E4M3 codes (k_scale 1/16, v_scale
-    1/16, so that the chunk's own projections also fit the format)."""
+    1/16, so that the chunk's own projections also fit the format).  Sharper
+    rows with the same draws: q_mult (a power of two) scales q; ramp scales
+    cached key latents and the chunk's new keys by 1 + ramp * t / L at
+    absolute position t (fp16 only), so the scores' maximum rises along the
+    request, also inside the chunk."""
     rng = np.random.default_rng(seed)
     if bases is None:
         U, W = draw_bases(rng, shape)
@@ -290,6 +347,18 @@ def make_prefill_case(shape: Shape, cached_lens, chunk_lens, seed=0,
     q = rng.standard_normal(dims, dtype=np.float32).astype(np.float16)
     qsl = np.zeros(len(chunk_lens) + 1, dtype=np.int32)
     qsl[1:] = np.cumsum(chunk_lens)
+    if q_mult != 1:
+        q = (q.astype(np.float32) * _pow2(q_mult)).astype(np.float16)
+    if ramp:
+        if fp8:
+            raise ValueError("ramped keys are an fp16-cache option")
+        ramp_keys(cache, ramp, lens=cached_lens)
+        for b in range(len(chunk_lens)):
+            L = int(total[b])
+            for j in range(int(chunk_lens[b])):
+                t = int(cached_lens[b]) + j
+                n = qsl[b] + j
+                k_new[n] = (k_new[n].astype(np.float32) * (1.0 + ramp * t / L)).astype(np.float16)
     slots = np.empty(T, dtype=np.int64)
     bs = shape.bs
     for b in range(len(chunk_lens)):

@@ -31,7 +31,7 @@ def test_exports_match_header():
 
 
 def test_version_and_status_strings():
-    assert sk.abi_version() == 4
+    assert sk.abi_version() == 5
     for s in range(0, 8):
         assert sk.lib().starkv_status_string(s)
     assert sk.lib().starkv_status_string(99) == b"unknown status"
@@ -133,8 +133,8 @@ def test_prefill_validation():
     d = _main_dims()
     f = sk.lib().starkv_prefill_attn
     need = sk.prefill_workspace_size(d, 16, 4096, 4352)
-    # q~ (fp16, r_k per head) and z (fp16, r_v per head) of every chunk query
-    assert need >= 4096 * 32 * (64 * 2 + 512 * 2)
+    # q~ (fp32, r_k per head) and z (fp16, r_v per head) of every chunk query
+    assert need >= 4096 * 32 * (64 * 4 + 512 * 2)
     args = lambda **kw: dict(dict(q=FAKE, qsl=FAKE, T=4096, mq=256, kc=FAKE, vc=FAKE, U=FAKE,
                                   W=FAKE, bt=FAKE, mb=272, sl=FAKE, B=16, msl=4352, scale=0.088,
                                   out=FAKE, ws=FAKE, wsb=0), **kw)
@@ -167,6 +167,53 @@ def test_decode_plan_properties():
         pages = -(-L // 16)
         assert ns >= 1 and 1 <= pps <= 256
         assert pps * ns >= pages and pps * (ns - 1) < pages
+
+
+def test_decode_config_validation():
+    """The plan override: fields 0 (the library's choice) or in range; the
+    workspace follows the plan."""
+    d = _main_dims()
+    f = sk.lib().starkv_decode_attn_cfg
+    fs = sk.lib().starkv_decode_workspace_size_cfg
+
+    def size(cfg):
+        out = ctypes.c_size_t(0)
+        st = fs(ctypes.byref(d), 16, 2048, ctypes.byref(cfg) if cfg else None, ctypes.byref(out))
+        return st, out.value
+
+    def call(cfg, wsb):
+        return f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, 16, 2048, 0.088,
+                 ctypes.byref(cfg) if cfg else None, FAKE, FAKE, wsb, None)
+    st, dflt = size(None)
+    assert st == 0 and dflt == sk.decode_workspace_size(d, 16, 2048)
+    assert size(sk.DecodeConfig(0, 0)) == (0, dflt)
+    st, one = size(sk.DecodeConfig(1, 0))                 # 128 splits per sequence
+    assert st == 0 and one > dflt
+    assert size(sk.DecodeConfig(257, 0))[0] == 7
+    assert size(sk.DecodeConfig(-1, 0))[0] == 7
+    assert size(sk.DecodeConfig(0, 3))[0] == 7
+    for m in (1, 2, 4, 8):
+        assert size(sk.DecodeConfig(0, m))[0] == 0
+    assert call(sk.DecodeConfig(0, 5), one) == 7
+    assert call(sk.DecodeConfig(1, 0), one - 1) == 4      # sized for the default plan: too small
+    assert call(None, dflt - 1) == 4
+
+
+def test_decode_plan_ignores_environment(monkeypatch):
+    """The plan is a function of the call's arguments and the device only:
+    the environment variables that tuning builds once read change nothing."""
+    d = _main_dims()
+    before = [sk.decode_plan(d, B, L) for B, L in [(16, 2048), (1, 8192), (64, 6000)]]
+    sizes = [sk.decode_workspace_size(d, B, L) for B, L in [(16, 2048), (1, 8192)]]
+    for name, val in [("STARKV_DECODE_TARGET_WGS", "4096"), ("STARKV_DECODE_MIN_PAGES", "64"),
+                      ("STARKV_DECODE_SPLIT_COST", "5"), ("STARKV_DECODE_FINISH_TB", "8"),
+                      ("STARKV_DECODE_VARIANT", "3")]:
+        monkeypatch.setenv(name, val)
+    assert [sk.decode_plan(d, B, L) for B, L in [(16, 2048), (1, 8192), (64, 6000)]] == before
+    assert [sk.decode_workspace_size(d, B, L) for B, L in [(16, 2048), (1, 8192)]] == sizes
+    text = "".join(open(os.path.join(ROOT, "rank_compressed_paged_amd", "csrc", f)).read()
+                   for f in os.listdir(os.path.join(ROOT, "rank_compressed_paged_amd", "csrc")))
+    assert "getenv" not in text
 
 
 def test_fit_validation():
