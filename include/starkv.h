@@ -225,6 +225,29 @@ starkv_status starkv_decode_attn_cfg(const starkv_dims* dims, const void* q, con
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * starkv_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The call allocates nothing:
+ * its scratch (q~, the split partials) is a device array of the library,
+ * STARKV_NOALLOC_SCRATCH_BYTES per GPU, held from the library's first use on
+ * that GPU until the process ends.  A batch / length whose plan needs more
+ * scratch than that (starkv_decode_workspace_size reports the need) returns
+ * STARKV_ERR_WORKSPACE before anything is launched; e.g. 64 sequences of up
+ * to 8192 tokens, or 20 of 32768, at the main shape fit.  Every call on one
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other host threads) race on it and must be serialised by the
+ * caller.  Nothing in the scratch needs to start at zero.  Same arguments
+ * and result as starkv_decode_attn otherwise (the library's plan).
+ */
+#define STARKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+starkv_status starkv_decode_attn_noalloc(const starkv_dims* dims, const void* q,
+                                         const void* k_cache, const void* v_cache, const void* U,
+                                         const void* W, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                         int32_t batch, int32_t max_seq_len, float scale,
+                                         void* out, void* stream);
+
+/*
  * starkv_decode_attn over FP8 caches (see starkv_append_fp8): the same
  * attention on the latents scale * value(code); k_scale folds into q~ and
  * v_scale into the split partials, so the kernels do the same work on half

@@ -20,7 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libstarkv.so")
-SOURCES = ["api.cpp", "decode.hip", "append.hip", "prefill.hip", "util.hip", "fit.hip"]
+SOURCES = ["api.cpp", "decode.hip", "append.hip", "prefill.hip", "util.hip", "fit.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 

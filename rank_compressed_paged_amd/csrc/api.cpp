@@ -9,6 +9,8 @@
 
 namespace starkv {
 
+static_assert(kNoallocScratchBytes == STARKV_NOALLOC_SCRATCH_BYTES, "one scratch size");
+
 TimingHook g_timing;
 
 // Compiled instances: the main shape at two rank profiles (r_k, r_v) =
@@ -349,12 +351,15 @@ starkv_status workspace_size(const starkv_dims* dims, int32_t batch, int32_t max
 
 // Every decode entry point: host checks, then the q projection (the key
 // scale, FP8 only, folds into q~), the split-K pass and the merge.
+// noalloc: the library's own scratch replaces the caller's workspace (which
+// is then ignored), and a plan whose workspace exceeds it is rejected.
 starkv_status decode_common(const starkv_dims* dims, const void* q, const void* k_cache,
                             const void* v_cache, const void* U, const void* W,
                             const int32_t* block_tables, int32_t max_blocks_per_seq,
                             const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
                             float scale, const LatentFormat& fmt, const starkv_decode_config* cfg,
-                            void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                            void* out, void* workspace, size_t workspace_bytes, void* stream,
+                            bool noalloc = false) {
   ShapeKey key;
   starkv_status st = check_dims(dims, &key);
   if (st != STARKV_OK) return st;
@@ -365,11 +370,17 @@ starkv_status decode_common(const starkv_dims* dims, const void* q, const void* 
   st = check_config(cfg);
   if (st != STARKV_OK) return st;
   if (batch == 0) return STARKV_OK;
-  st = check_ptrs({q, k_cache, v_cache, U, W, block_tables, seq_lens, out, workspace});
+  st = check_ptrs({q, k_cache, v_cache, U, W, block_tables, seq_lens, out,
+                   noalloc ? (const void*)q : workspace});
   if (st != STARKV_OK) return st;
   const DecodePlan p = plan_for(key, batch, max_seq_len, dims->block_size, cfg);
   const DecodeWorkspace ws = decode_workspace_layout(key, batch, p);
-  if (workspace_bytes < ws.total) return STARKV_ERR_WORKSPACE;
+  if (noalloc) {
+    if (ws.total > kNoallocScratchBytes) return STARKV_ERR_WORKSPACE;
+    if (noalloc_scratch(&workspace) != hipSuccess) return STARKV_ERR_LAUNCH;
+  } else if (workspace_bytes < ws.total) {
+    return STARKV_ERR_WORKSPACE;
+  }
   char* wb = (char*)workspace;
   const hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_qproj(key, q, U, batch, scale * (fmt.fp8 ? fmt.k_scale : 1.f),
@@ -438,6 +449,17 @@ starkv_status starkv_decode_attn_cfg(const starkv_dims* dims, const void* q, con
   return decode_common(dims, q, k_cache, v_cache, U, W, block_tables, max_blocks_per_seq,
                        seq_lens, batch, max_seq_len, scale, LatentFormat{}, cfg, out, workspace,
                        workspace_bytes, stream);
+}
+
+starkv_status starkv_decode_attn_noalloc(const starkv_dims* dims, const void* q,
+                                         const void* k_cache, const void* v_cache, const void* U,
+                                         const void* W, const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                         int32_t batch, int32_t max_seq_len, float scale,
+                                         void* out, void* stream) {
+  return decode_common(dims, q, k_cache, v_cache, U, W, block_tables, max_blocks_per_seq,
+                       seq_lens, batch, max_seq_len, scale, LatentFormat{}, nullptr, out, nullptr,
+                       0, stream, /*noalloc=*/true);
 }
 
 starkv_status starkv_decode_attn_fp8(const starkv_dims* dims, const void* q,

@@ -120,6 +120,12 @@ hipError_t launch_decode(const ShapeKey& s, const DecodePlan& p, const void* qt,
 hipError_t launch_upproj_tiled(const ShapeKey& s, const void* W, const void* z_tiled,
                                int n_tokens, void* out, hipStream_t st);
 
+// Scratch of the no-allocation decode entry point: a device array of the
+// library, one per GPU; *ptr receives its device address on the current
+// device (taken once per device).
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Measurement aid: read `bytes` (a multiple of 16) with 16-byte loads and
 // fold them into one word per work group, so nothing is optimised away.
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t st);

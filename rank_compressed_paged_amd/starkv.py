@@ -36,8 +36,9 @@ EXPORTED = [
     "starkv_util_stream_read", "starkv_util_event_create", "starkv_util_event_destroy",
     "starkv_util_event_elapsed_ms", "starkv_fit_workspace_size", "starkv_fit_bases",
     "starkv_append_fp8", "starkv_decode_attn_fp8", "starkv_prefill_attn_fp8",
-    "starkv_decode_workspace_size_cfg", "starkv_decode_attn_cfg",
+    "starkv_decode_workspace_size_cfg", "starkv_decode_attn_cfg", "starkv_decode_attn_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class Dims(ctypes.Structure):
@@ -87,6 +88,9 @@ _lib.starkv_decode_attn_cfg.restype = _i32
 _lib.starkv_decode_attn_cfg.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                         _vp, _i32, _i32, ctypes.c_float,
                                         ctypes.POINTER(DecodeConfig), _vp, _vp, _sz, _vp]
+_lib.starkv_decode_attn_noalloc.restype = _i32
+_lib.starkv_decode_attn_noalloc.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _vp, _vp, _vp, _vp,
+                                            _i32, _vp, _i32, _i32, ctypes.c_float, _vp, _vp]
 _lib.starkv_prefill_workspace_size.restype = _i32
 _lib.starkv_prefill_workspace_size.argtypes = [ctypes.POINTER(Dims), _i32, _i32, _i32,
                                                ctypes.POINTER(_sz)]
@@ -315,6 +319,27 @@ def decode_attn(q, k_cache, v_cache, U, W, block_tables, seq_lens, max_seq_len, 
     else:
         _check(_lib.starkv_decode_attn_cfg(*args, ctypes.byref(cfg), *tail),
                "starkv_decode_attn_cfg")
+    return out
+
+
+def decode_attn_noalloc(q, k_cache, v_cache, U, W, block_tables, seq_lens, max_seq_len, out,
+                        scale=None, stream=None):
+    """decode_attn() through the entry point that allocates nothing: the
+    library's own scratch replaces the workspace; the caller passes out
+    [B, H, d] fp16."""
+    dims = dims_of(k_cache, v_cache, U, W, num_heads=q.shape[1])
+    B = q.shape[0]
+    H, d = dims.num_heads, dims.head_dim
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = _lib.starkv_decode_attn_noalloc(
+        ctypes.byref(dims), _dev(q, torch.float16, "q", (B, H, d)),
+        _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"),
+        _dev(U, torch.float16, "U"), _dev(W, torch.float16, "W"),
+        _dev(block_tables, torch.int32, "block_tables"), int(block_tables.shape[1]),
+        _dev(seq_lens, torch.int32, "seq_lens", (B,)), int(B), int(max_seq_len), float(scale),
+        _dev(out, torch.float16, "out", (B, H, d)), _stream(stream))
+    _check(st, "starkv_decode_attn_noalloc")
     return out
 
 

@@ -199,6 +199,24 @@ def test_decode_config_validation():
     assert call(None, dflt - 1) == 4
 
 
+def test_decode_noalloc_validation():
+    """The entry point without a workspace checks on the host like the others,
+    and refuses a plan that needs more than its 32 MiB scratch."""
+    d = _main_dims()
+    f = sk.lib().starkv_decode_attn_noalloc
+
+    def call(B=16, msl=2048, mb=128, q=FAKE, scale=0.088):
+        return f(ctypes.byref(d), q, FAKE, FAKE, FAKE, FAKE, FAKE, mb, FAKE, B, msl, scale, FAKE,
+                 None)
+    assert sk.decode_workspace_size(d, 256, 4096) > sk.NOALLOC_SCRATCH_BYTES
+    assert call(B=256, msl=4096, mb=256) == 4           # beyond the scratch: refused
+    assert call(q=None) == 1
+    assert call(q=MISALIGNED) == 5
+    assert call(mb=100) == 2
+    assert call(scale=0.0) == 7
+    assert call(B=0) == 0
+
+
 def test_decode_plan_ignores_environment(monkeypatch):
     """The plan is a function of the call's arguments and the device only:
     the environment variables that tuning builds once read change nothing."""
