@@ -14,7 +14,8 @@ events that take its dispatch's own begin and end timestamps.  `value` is
 latent-KV bytes per step / mean step time.  Beside the headline the line
 carries the step with its append, a streaming-read ceiling, the chunked
 prefill workload (16 requests x 4096 cached + 256 new tokens: attention and
-append, as TFLOP/s against the fp16 MFMA peak), decode at two other
+append, as TFLOP/s against the fp16 MFMA peak), the other fp16 decode
+configurations of the same shape (decode_b64, long_b20, tiny), decode at other
 layouts (gqa8_b16: 32 query heads on 8 key/value heads; lowrank_b16: r_k
 32, r_v 256; decode_b16_fp8 and decode_b64_fp8: FP8 E4M3 latents), low-batch
 decode latency (batch 1-4: eager calls against a captured HIP graph), the bases
@@ -103,6 +104,8 @@ def parse_args(argv=None):
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill_b16 leg")
     ap.add_argument("--no-fit", action="store_true", help="skip the bases-fit leg")
     ap.add_argument("--no-low-batch", action="store_true", help="skip the low-batch latency leg")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the decode_b64, long_b20 and tiny legs")
     ap.add_argument("--no-layouts", action="store_true",
                     help="skip the grouped-query and low-rank decode legs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU sample budget")
@@ -183,13 +186,21 @@ def settle(fn, flush_fn=None, seconds=0.2):
             return i
 
 
+# GPU work enqueued ahead of every timed loop (set by run_bench): the host
+# then enqueues the loop's calls while the GPU is still busy with it, so no
+# call's events ever wait for the host to launch its kernels.  Without it a
+# short call (the few-token append: about 9 us of kernels after a 75 us
+# flush) read 35-48 us, the host's Python launch path included.
+HEAD_START = {"fn": None}
+
+
 def timed(fn, n, flush_fn=None, kernel_sel=0):
     """Run fn n times, each optionally after flush_fn (outside the events).
     Returns per-call ms from events around the call on the current stream,
     per-call ms of one kernel through the library's timing hook (when
     kernel_sel selects one: the library's timing events, bound to that
     dispatch and recorded without a system-scope fence), and the wall time of
-    the loop."""
+    the loop (which includes the head start)."""
     import torch
     from rank_compressed_paged_amd import starkv as sk
     stream = torch.cuda.current_stream()
@@ -198,6 +209,8 @@ def timed(fn, n, flush_fn=None, kernel_sel=0):
     kev = [(sk.TimingEvent(), sk.TimingEvent()) for _ in range(n)] if kernel_sel else []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    if HEAD_START["fn"] is not None:
+        HEAD_START["fn"](n)
     for i in range(n):
         if flush_fn is not None:
             flush_fn(i)
@@ -374,12 +387,14 @@ def prefill_leg(flush_fn, steps, name="prefill_b16", cpu_budget_s=0.0):
 
 
 def decode_leg(name, flush_fn, steps):
-    """Decode at another layout of the same batch (16 sequences x 2048
-    tokens): gqa8_b16 (32 query heads on 8 key/value heads, r_k 64, r_v 512:
-    2048 latent bytes per token) or lowrank_b16 (32 heads, r_k 32, r_v 256:
-    2560 bytes per token).  Flushed steps (events around the call) and the
-    split-K kernel (the library's timing events), as latent GB/s against the
-    8 TB/s peak."""
+    """Decode on another workload: the other fp16 configurations of the main
+    shape (decode_b64: 64 x U{4096..8192} tokens; long_b20: 20 x 32768; tiny:
+    the small parity shape), or another layout of 16 x 2048 tokens: gqa8_b16
+    (32 query heads on 8 key/value heads, r_k 64, r_v 512: 2048 latent bytes
+    per token), lowrank_b16 (r_k 32, r_v 256: 2560 bytes per token) and the
+    FP8 caches.  Flushed steps (events around the call) and the split-K
+    kernel (the library's timing events), as latent GB/s against the 8 TB/s
+    peak."""
     import numpy as np
     import torch
     from rank_compressed_paged_amd import metrics
@@ -543,6 +558,12 @@ def run_bench(args):
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     flush_sink = torch.empty((), dtype=torch.float32, device="cuda")
 
+    def head_start(n):
+        # about 150 us of GPU work per call to be timed (two 512 MiB reads)
+        for _ in range(2 * n):
+            torch.sum(flush, dim=0, out=flush_sink)
+    HEAD_START["fn"] = head_start
+
     def do_flush(i):
         # a read-only sweep leaves clean lines behind; a write sweep leaves
         # dirty ones whose write-back competes with the next step's reads
@@ -592,8 +613,8 @@ def run_bench(args):
     both_ms, _, _ = timed(lambda: (append_step(), step()), args.steps, do_flush)
 
     # measured streaming-read ceiling on this machine: the library's plain
-    # 16-byte streaming read over as many bytes as one step's latents, after
-    # the same flush
+    # streaming read (16-byte non-temporal loads, 16 in flight per thread)
+    # over as many bytes as one step's latents, after the same flush
     ceil_buf = torch.ones(lat_bytes, dtype=torch.uint8, device="cuda")
     ceil_sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
     ceil_ms, _, _ = timed(lambda: sk.stream_read(ceil_buf, ceil_sink), max(args.steps, 10),
@@ -638,6 +659,7 @@ def run_bench(args):
         "split_plan": {"pages_per_split": pps, "num_splits": ns},
         "flush": args.flush,
         "stream_read_ceiling_gbs": round(ceiling_gbs, 1),
+        "split_kernel_over_ceiling": round(achieved / ceiling_gbs, 4),
         "roofline": {
             "kernel": DECODE_KERNEL,
             "bound": "hbm",
@@ -657,6 +679,10 @@ def run_bench(args):
         res["prefill_fp8"] = prefill_leg(do_flush, args.steps, "prefill_b16_fp8")
     if not args.no_low_batch:
         res["low_batch"] = low_batch_leg(do_flush, args.steps)
+    if not args.no_configs:
+        # the other fp16 configurations of the metric's shape
+        res["decode_configs"] = [decode_leg(n, do_flush, args.steps)
+                                 for n in ("decode_b64", "long_b20", "tiny")]
     if not args.no_layouts:
         res["layouts"] = [decode_leg(n, do_flush, args.steps)
                           for n in ("gqa8_b16", "lowrank_b16", "decode_b16_fp8", "decode_b64_fp8")]
