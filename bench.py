@@ -685,7 +685,8 @@ def run_bench(args):
                                  for n in ("decode_b64", "long_b20", "tiny")]
     if not args.no_layouts:
         res["layouts"] = [decode_leg(n, do_flush, args.steps)
-                          for n in ("gqa8_b16", "lowrank_b16", "decode_b16_fp8", "decode_b64_fp8")]
+                          for n in ("gqa8_b16", "lowrank_b16", "decode_b16_fp8", "decode_b64_fp8",
+                                    "conservative_b16", "odd_h28_b16")]
     if not args.no_fit:
         res["fit"] = fit_leg(args.steps)
     res["device"] = device_info()

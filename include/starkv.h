@@ -48,11 +48,17 @@
  *   - Contents of device index arrays (block tables, seq_lens, slots,
  *     query_start_loc) are trusted.  Block ids outside [0, num_blocks) and
  *     slots outside the cache are skipped rather than dereferenced.
- *   - Compiled shape instances of the attention and append calls:
- *     (H, d, r_k, r_v) = (32, 128, 64, 512) with Hkv 32 or 8, and
- *     (4, 64, 16, 64) with Hkv 4 or 2; block size 16.  Other shapes return
- *     STARKV_ERR_UNSUPPORTED.  The bases fit takes any shape within the
- *     limits stated at its declaration.
+ *   - Shapes.  Tuned instances of the attention and append calls:
+ *     (H, d, r_k, r_v) = (32, 128, 64, 512) with Hkv 32 or 8,
+ *     (32, 128, 32, 256) with Hkv 32, and (4, 64, 16, 64) with Hkv 4 or 2
+ *     (FP8 caches: the first and the last, Hkv 32/8 and 4).  Every other
+ *     shape within the generic limits -- d a multiple of 32 up to 256, r_k a
+ *     multiple of 8 up to min(d, 256), r_v a multiple of 8 up to
+ *     min(2048, Hkv * d), Hkv dividing H -- runs on generic kernels that take
+ *     the sizes at run time (fp16 and FP8 caches alike: per-layer rank
+ *     profiles, other head counts, sizes and grouped-query groups).  Block
+ *     size 16.  Other shapes return STARKV_ERR_UNSUPPORTED.  The bases fit
+ *     takes any shape within the limits stated at its declaration.
  */
 #ifndef STARKV_H_
 #define STARKV_H_
@@ -162,8 +168,9 @@ starkv_status starkv_append_fp8(const starkv_dims* dims, const void* k, const vo
                                 size_t workspace_bytes, void* stream);
 
 /*
- * Workspace bytes (host out-parameter *bytes) that starkv_decode_attn needs
- * for `batch` sequences of at most max_seq_len tokens.  Returns a status.
+ * Workspace bytes (host out-parameter *bytes) that starkv_decode_attn and
+ * starkv_decode_attn_fp8 need for `batch` sequences of at most max_seq_len
+ * tokens (the larger of the two).  Returns a status.
  */
 starkv_status starkv_decode_workspace_size(const starkv_dims* dims, int32_t batch,
                                            int32_t max_seq_len, size_t* bytes /* (host) */);
@@ -252,9 +259,10 @@ starkv_status starkv_decode_attn_noalloc(const starkv_dims* dims, const void* q,
  * attention on the latents scale * value(code); k_scale folds into q~ and
  * v_scale into the split partials, so the kernels do the same work on half
  * the bytes (codes become fp16 matrix-core operands as they are used).
- * Instances: (H, d, r_k, r_v) = (32, 128, 64, 512) with Hkv 32 or 8, and
- * (4, 64, 16, 64); other shapes return STARKV_ERR_UNSUPPORTED.  Workspace as
- * for starkv_decode_attn (starkv_decode_workspace_size).
+ * Shapes as for starkv_decode_attn (tuned FP8 instances: (32, 128, 64, 512)
+ * with Hkv 32 or 8, and (4, 64, 16, 64); the generic kernels otherwise).
+ * Workspace as for starkv_decode_attn (starkv_decode_workspace_size covers
+ * both caches' needs).
  */
 starkv_status starkv_decode_attn_fp8(const starkv_dims* dims, const void* q,
                                      const void* k_cache8, const void* v_cache8, const void* U,

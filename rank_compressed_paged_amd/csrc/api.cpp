@@ -13,28 +13,38 @@ static_assert(kNoallocScratchBytes == STARKV_NOALLOC_SCRATCH_BYTES, "one scratch
 
 TimingHook g_timing;
 
-// Compiled instances: the main shape at two rank profiles (r_k, r_v) =
+// Tuned instances: the main shape at two rank profiles (r_k, r_v) =
 // (64, 512) and (32, 256), the former also with 8 key/value heads, and the
 // tiny shape with 4 or 2 key/value heads.
-bool shape_supported(const ShapeKey& s) {
+static bool tuned_shape(const ShapeKey& s) {
   return (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512 && (s.Hkv == 32 || s.Hkv == 8)) ||
          (s.H == 32 && s.d == 128 && s.rk == 32 && s.rv == 256 && s.Hkv == 32) ||
          (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64 && (s.Hkv == 4 || s.Hkv == 2));
 }
 
-// The append sees only the key/value heads: it supports the key/value view
-// (Hkv, d, r_k, r_v) of every supported shape, whatever the query heads.
-// Decode and prefill over FP8 latents: the main shape (both head layouts) and
+// Tuned instances over FP8 latents: the main shape (both head layouts) and
 // the tiny one.
-static bool fp8_decode_supported(const ShapeKey& s) {
+static bool tuned_fp8(const ShapeKey& s) {
   return (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512 && (s.Hkv == 32 || s.Hkv == 8)) ||
          (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64 && s.Hkv == 4);
 }
 
+// Every other shape within the generic kernels' limits runs on them (fp16
+// and FP8 alike).
+bool shape_supported(const ShapeKey& s) { return tuned_shape(s) || generic_shape_ok(s); }
+static bool fp8_decode_supported(const ShapeKey& s) { return tuned_fp8(s) || generic_shape_ok(s); }
+static bool use_generic(const ShapeKey& s, bool fp8) {
+  return fp8 ? !tuned_fp8(s) : !tuned_shape(s);
+}
+
+// The append sees only the key/value heads: the key/value view (Hkv, d, r_k,
+// r_v) of a tuned shape, or any view within the generic limits (the tiled
+// append kernel takes every size at run time).
 static bool kv_shape_supported(const ShapeKey& s) {
   return (s.d == 128 && s.rk == 64 && s.rv == 512 && (s.Hkv == 32 || s.Hkv == 8)) ||
          (s.d == 128 && s.rk == 32 && s.rv == 256 && s.Hkv == 32) ||
-         (s.d == 64 && s.rk == 16 && s.rv == 64 && (s.Hkv == 4 || s.Hkv == 2));
+         (s.d == 64 && s.rk == 16 && s.rv == 64 && (s.Hkv == 4 || s.Hkv == 2)) ||
+         generic_shape_ok(ShapeKey{s.Hkv, s.d, s.rk, s.rv, s.Hkv});
 }
 
 static inline int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
@@ -100,8 +110,33 @@ static DecodePlan with_finish(DecodePlan p, const ShapeKey& s, int batch, int fo
 // otherwise a function of the shape, batch, length bound and device only.
 constexpr double kSplitCost = 6.0;
 
+// Split plan of the generic kernels: about two work groups per CU over the
+// batch, its head groups and the splits, at most 4096 splits; a caller's
+// pages_per_split is kept unless it would exceed that.
+static DecodePlan plan_generic(const ShapeKey& s, int batch, int max_seq_len, int bs,
+                               int force_pps) {
+  DecodePlan p{1, 1, 1, 4, 256, 1};
+  p.generic = true;
+  const int pages = cdiv(max_seq_len, bs);
+  if (pages <= 0 || batch <= 0) return p;
+  int pps;
+  if (force_pps > 0) {
+    pps = force_pps;
+  } else {
+    const long per_split = (long)batch * generic_head_groups(s);
+    const int want = cdiv(2L * device_cus(), per_split);
+    pps = cdiv(pages, want < 1 ? 1 : (want > pages ? pages : want));
+  }
+  if (cdiv(pages, pps) > 4096) pps = cdiv(pages, 4096);
+  p.pages_per_split = pps;
+  p.num_splits = cdiv(pages, pps);
+  p.split_stride = p.num_splits;
+  return p;
+}
+
 DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int bs, int force_pps,
-                       int force_tb) {
+                       int force_tb, bool generic) {
+  if (generic) return plan_generic(s, batch, max_seq_len, bs, force_pps);
   const int pages = cdiv(max_seq_len, bs);
   if (pages <= 0 || batch <= 0) return with_finish(DecodePlan{1, 1, 0, 0, 0, 0}, s, batch, force_tb);
   if (force_pps > 0) {
@@ -132,6 +167,16 @@ DecodeWorkspace decode_workspace_layout(const ShapeKey& s, int batch, const Deco
   const size_t r16 = (size_t)((s.H + 15) / 16) * 16;
   DecodeWorkspace w;
   size_t off = 0;
+  if (p.generic) {  // q~ fp32, fp32 statistics [B][H][2][S] and unnormalised z [B][H][S][r_v]
+    w.qt_off = off;
+    off = align256(off + (size_t)batch * s.H * s.rk * 4);
+    w.ml_off = off;
+    off = align256(off + (size_t)batch * s.H * 2 * p.num_splits * 4);
+    w.zp_off = off;
+    off = align256(off + (size_t)batch * s.H * p.num_splits * s.rv * 4);
+    w.total = off;
+    return w;
+  }
   w.qt_off = off;
   off = align256(off + (size_t)batch * s.H * s.rk * 4);  // q~, fp32
   w.ml_off = off;
@@ -331,9 +376,24 @@ starkv_status check_config(const starkv_decode_config* cfg) {
 }
 
 DecodePlan plan_for(const ShapeKey& key, int batch, int max_seq_len, int bs,
-                    const starkv_decode_config* cfg) {
+                    const starkv_decode_config* cfg, bool fp8) {
   return plan_decode(key, batch, max_seq_len, bs, cfg ? cfg->pages_per_split : 0,
-                     cfg ? cfg->merge_seqs : 0);
+                     cfg ? cfg->merge_seqs : 0, use_generic(key, fp8));
+}
+
+// The workspace of a decode call over fp16 latents and of one over FP8
+// latents may differ (one may run on the generic kernels): the size query
+// covers both.
+size_t decode_need(const ShapeKey& key, int batch, int max_seq_len, int bs,
+                   const starkv_decode_config* cfg) {
+  size_t need = decode_workspace_layout(key, batch, plan_for(key, batch, max_seq_len, bs, cfg,
+                                                             false)).total;
+  if (fp8_decode_supported(key)) {
+    const size_t n8 = decode_workspace_layout(key, batch, plan_for(key, batch, max_seq_len, bs,
+                                                                   cfg, true)).total;
+    if (n8 > need) need = n8;
+  }
+  return need;
 }
 
 starkv_status workspace_size(const starkv_dims* dims, int32_t batch, int32_t max_seq_len,
@@ -345,7 +405,7 @@ starkv_status workspace_size(const starkv_dims* dims, int32_t batch, int32_t max
   if (batch < 0 || max_seq_len < 0 || batch > 65535) return STARKV_ERR_DIMS;
   st = check_config(cfg);
   if (st != STARKV_OK) return st;
-  *bytes = decode_workspace_layout(key, batch, plan_for(key, batch, max_seq_len, dims->block_size, cfg)).total;
+  *bytes = decode_need(key, batch, max_seq_len, dims->block_size, cfg);
   return STARKV_OK;
 }
 
@@ -373,7 +433,7 @@ starkv_status decode_common(const starkv_dims* dims, const void* q, const void* 
   st = check_ptrs({q, k_cache, v_cache, U, W, block_tables, seq_lens, out,
                    noalloc ? (const void*)q : workspace});
   if (st != STARKV_OK) return st;
-  const DecodePlan p = plan_for(key, batch, max_seq_len, dims->block_size, cfg);
+  const DecodePlan p = plan_for(key, batch, max_seq_len, dims->block_size, cfg, fmt.fp8);
   const DecodeWorkspace ws = decode_workspace_layout(key, batch, p);
   if (noalloc) {
     if (ws.total > kNoallocScratchBytes) return STARKV_ERR_WORKSPACE;
@@ -383,8 +443,18 @@ starkv_status decode_common(const starkv_dims* dims, const void* q, const void* 
   }
   char* wb = (char*)workspace;
   const hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_qproj(key, q, U, batch, scale * (fmt.fp8 ? fmt.k_scale : 1.f),
-                              wb + ws.qt_off, TIME_DECODE_SPLIT, s, W);
+  const float qscale = scale * (fmt.fp8 ? fmt.k_scale : 1.f);
+  if (p.generic) {
+    hipError_t e = launch_generic_qproj(key, q, U, batch, qscale, wb + ws.qt_off,
+                                        TIME_DECODE_SPLIT, s);
+    if (e != hipSuccess) return STARKV_ERR_LAUNCH;
+    e = launch_generic_attn(key, wb + ws.qt_off, nullptr, batch, k_cache, v_cache, W,
+                            block_tables, max_blocks_per_seq, seq_lens, dims->num_blocks, batch,
+                            p.pages_per_split, p.num_splits, (float*)(wb + ws.ml_off),
+                            (float*)(wb + ws.zp_off), out, fmt, TIME_DECODE_SPLIT, s);
+    return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
+  }
+  hipError_t e = launch_qproj(key, q, U, batch, qscale, wb + ws.qt_off, TIME_DECODE_SPLIT, s, W);
   if (e != hipSuccess) return STARKV_ERR_LAUNCH;
   e = launch_decode(key, p, wb + ws.qt_off, k_cache, v_cache, W, block_tables,
                     max_blocks_per_seq, seq_lens, dims->num_blocks, batch,
@@ -485,22 +555,30 @@ starkv_status starkv_prefill_workspace_size(const starkv_dims* dims, int32_t bat
   return STARKV_OK;
 }
 
-starkv_status starkv_prefill_attn(const starkv_dims* dims, const void* q,
-                                  const int32_t* query_start_loc, int32_t total_q,
-                                  int32_t max_query_len, const void* k_cache, const void* v_cache,
-                                  const void* U, const void* W, const int32_t* block_tables,
-                                  int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                                  int32_t batch, int32_t max_seq_len, float scale, void* out,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both prefill entry points: host checks, the q projection (the key scale,
+// FP8 only, folds into q~), then the chunk attention with the up-projection:
+// the tuned kernels, or the generic ones (one row per chunk query, one split).
+starkv_status prefill_common(const starkv_dims* dims, const void* q,
+                             const int32_t* query_start_loc, int32_t total_q,
+                             int32_t max_query_len, const void* k_cache, const void* v_cache,
+                             const void* U, const void* W, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                             int32_t max_seq_len, float scale, const LatentFormat& fmt, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   ShapeKey key;
   starkv_status st = check_dims(dims, &key);
   if (st != STARKV_OK) return st;
+  if (fmt.fp8 && !fp8_decode_supported(key)) return STARKV_ERR_UNSUPPORTED;
   st = check_paging(batch, max_seq_len, max_blocks_per_seq, dims->block_size);
   if (st != STARKV_OK) return st;
   if (total_q < 0 || max_query_len < 0) return STARKV_ERR_DIMS;
   if (total_q > 0 && max_query_len == 0) return STARKV_ERR_DIMS;
   if (max_query_len > max_seq_len) return STARKV_ERR_DIMS;
-  if (!scale_ok(scale)) return STARKV_ERR_ARG;
+  if (!scale_ok(scale) || !scale_ok(fmt.k_scale) || !scale_ok(fmt.v_scale)) return STARKV_ERR_ARG;
   if (batch == 0 || total_q == 0) return STARKV_OK;
   st = check_ptrs({q, query_start_loc, k_cache, v_cache, U, W, block_tables, seq_lens, out,
                    workspace});
@@ -509,12 +587,39 @@ starkv_status starkv_prefill_attn(const starkv_dims* dims, const void* q,
   if (workspace_bytes < ws.total) return STARKV_ERR_WORKSPACE;
   char* wb = (char*)workspace;
   const hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_qproj(key, q, U, total_q, scale, wb + ws.qt_off, TIME_PREFILL_ATTN, s);
+  const float qscale = scale * (fmt.fp8 ? fmt.k_scale : 1.f);
+  hipError_t e;
+  if (use_generic(key, fmt.fp8)) {
+    e = launch_generic_qproj(key, q, U, total_q, qscale, wb + ws.qt_off, TIME_PREFILL_ATTN, s);
+    if (e != hipSuccess) return STARKV_ERR_LAUNCH;
+    e = launch_generic_attn(key, wb + ws.qt_off, query_start_loc, total_q, k_cache, v_cache, W,
+                            block_tables, max_blocks_per_seq, seq_lens, dims->num_blocks, batch,
+                            max_blocks_per_seq, 1, nullptr, nullptr, out, fmt, TIME_PREFILL_ATTN,
+                            s);
+    return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
+  }
+  e = launch_qproj(key, q, U, total_q, qscale, wb + ws.qt_off, TIME_PREFILL_ATTN, s);
   if (e != hipSuccess) return STARKV_ERR_LAUNCH;
   e = launch_prefill(key, wb + ws.qt_off, query_start_loc, total_q, max_query_len, k_cache,
                      v_cache, W, block_tables, max_blocks_per_seq, seq_lens, dims->num_blocks,
-                     batch, (void*)(wb + ws.z_off), out, LatentFormat{}, s);
+                     batch, (void*)(wb + ws.z_off), out, fmt, s);
   return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+starkv_status starkv_prefill_attn(const starkv_dims* dims, const void* q,
+                                  const int32_t* query_start_loc, int32_t total_q,
+                                  int32_t max_query_len, const void* k_cache, const void* v_cache,
+                                  const void* U, const void* W, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                  int32_t batch, int32_t max_seq_len, float scale, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_common(dims, q, query_start_loc, total_q, max_query_len, k_cache, v_cache, U, W,
+                        block_tables, max_blocks_per_seq, seq_lens, batch, max_seq_len, scale,
+                        LatentFormat{}, out, workspace, workspace_bytes, stream);
 }
 
 starkv_status starkv_prefill_attn_fp8(const starkv_dims* dims, const void* q,
@@ -526,35 +631,9 @@ starkv_status starkv_prefill_attn_fp8(const starkv_dims* dims, const void* q,
                                       int32_t max_seq_len, float scale, float k_scale,
                                       float v_scale, void* out, void* workspace,
                                       size_t workspace_bytes, void* stream) {
-  ShapeKey key;
-  starkv_status st = check_dims(dims, &key);
-  if (st != STARKV_OK) return st;
-  if (!fp8_decode_supported(key)) return STARKV_ERR_UNSUPPORTED;
-  st = check_paging(batch, max_seq_len, max_blocks_per_seq, dims->block_size);
-  if (st != STARKV_OK) return st;
-  if (total_q < 0 || max_query_len < 0) return STARKV_ERR_DIMS;
-  if (total_q > 0 && max_query_len == 0) return STARKV_ERR_DIMS;
-  if (max_query_len > max_seq_len) return STARKV_ERR_DIMS;
-  if (!scale_ok(scale) || !scale_ok(k_scale) || !scale_ok(v_scale)) return STARKV_ERR_ARG;
-  if (batch == 0 || total_q == 0) return STARKV_OK;
-  st = check_ptrs({q, query_start_loc, k_cache8, v_cache8, U, W, block_tables, seq_lens, out,
-                   workspace});
-  if (st != STARKV_OK) return st;
-  const PrefillWorkspace ws = prefill_workspace_layout(key, total_q);
-  if (workspace_bytes < ws.total) return STARKV_ERR_WORKSPACE;
-  char* wb = (char*)workspace;
-  const hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_qproj(key, q, U, total_q, scale * k_scale, wb + ws.qt_off,
-                              TIME_PREFILL_ATTN, s);
-  if (e != hipSuccess) return STARKV_ERR_LAUNCH;
-  LatentFormat fmt;
-  fmt.fp8 = true;
-  fmt.k_scale = k_scale;
-  fmt.v_scale = v_scale;
-  e = launch_prefill(key, wb + ws.qt_off, query_start_loc, total_q, max_query_len, k_cache8,
-                     v_cache8, W, block_tables, max_blocks_per_seq, seq_lens, dims->num_blocks,
-                     batch, (void*)(wb + ws.z_off), out, fmt, s);
-  return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
+  return prefill_common(dims, q, query_start_loc, total_q, max_query_len, k_cache8, v_cache8, U,
+                        W, block_tables, max_blocks_per_seq, seq_lens, batch, max_seq_len, scale,
+                        fp8_format(k_scale, v_scale), out, workspace, workspace_bytes, stream);
 }
 
 starkv_status starkv_fit_workspace_size(const starkv_dims* dims, size_t* bytes) {

@@ -611,9 +611,20 @@ static int tiled_splits(const ShapeKey& s, int n_tokens) {
   return n_tokens <= kSplit4MaxTokens ? 4 : n_tokens <= kSplit2MaxTokens ? 2 : 1;
 }
 
+// Key/value views with a few-token instance (launch_few below); other shapes
+// take the tiled kernel for any token count and need no workspace.
+static bool few_token_instance(const ShapeKey& s) {
+  return (s.H == 32 && s.d == 128 && s.rk == 64 && s.rv == 512) ||
+         (s.H == 4 && s.d == 64 && s.rk == 16 && s.rv == 64) ||
+         (s.H == 8 && s.d == 128 && s.rk == 64 && s.rv == 512) ||
+         (s.H == 32 && s.d == 128 && s.rk == 32 && s.rv == 256);
+}
+
 size_t append_workspace_bytes(const ShapeKey& s, int n_tokens) {
   if (n_tokens <= 0) return 0;
-  if (n_tokens <= kSmallN) return (size_t)(s.H * s.d / kSliceRows) * n_tokens * s.rv * sizeof(float);
+  if (n_tokens <= kSmallN)
+    return few_token_instance(s) ? (size_t)(s.H * s.d / kSliceRows) * n_tokens * s.rv * sizeof(float)
+                                 : 0;
   const int vs = tiled_splits(s, n_tokens);
   return vs > 1 ? (size_t)vs * n_tokens * s.rv * sizeof(float) : 0;
 }

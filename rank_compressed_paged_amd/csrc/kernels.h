@@ -26,6 +26,7 @@ struct DecodePlan {
   int finish_nt;     // threads per work group of the merge (256, 512)
   int split_stride;  // split slots per sequence and head in the workspace: num_splits
                      // rounded up to a multiple of finish_cb times the split groups
+  bool generic = false;  // the generic kernels (generic.hip), which use the first two fields
 };
 
 // Split groups of the merge: when a work group has more threads than
@@ -65,7 +66,7 @@ bool shape_supported(const ShapeKey& s);
 // force_pps > 0 fixes the pages per split, force_tb in {1, 2, 4, 8} the
 // sequences per merge work group; 0 leaves either to the planner
 DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int block_size,
-                       int force_pps = 0, int force_tb = 0);
+                       int force_pps = 0, int force_tb = 0, bool generic = false);
 DecodeWorkspace decode_workspace_layout(const ShapeKey& s, int batch, const DecodePlan& p);
 PrefillWorkspace prefill_workspace_layout(const ShapeKey& s, int total_q);
 
@@ -98,6 +99,37 @@ inline void launch_hooked(int which, int precedes, void (*kernel)(KArgs...), dim
   else
     hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
 }
+
+// launch_hooked with `lds` bytes of dynamic LDS.
+template <typename... KArgs, typename... Args>
+inline void launch_hooked_lds(int which, int precedes, void (*kernel)(KArgs...), dim3 grid,
+                              dim3 block, size_t lds, hipStream_t st, Args... args) {
+  hipEvent_t ev = nullptr;
+  if (g_timing.start && g_timing.stop) {
+    if (g_timing.which == which)
+      ev = g_timing.stop;
+    else if (precedes != TIME_NONE && g_timing.which == precedes)
+      ev = g_timing.start;
+  }
+  if (ev)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, nullptr, ev, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+}
+
+// Generic instances (any shape within their limits; see generic.hip).
+bool generic_shape_ok(const ShapeKey& s);
+int generic_head_groups(const ShapeKey& s);
+hipError_t launch_generic_qproj(const ShapeKey& s, const void* q, const void* U, int n_tokens,
+                                float scale, void* qt, int precedes, hipStream_t st);
+// rows: decode sequences (qsl null) or prefill chunk queries (qsl the
+// query start locations of `batch` requests); num_splits 1 fuses the merge
+hipError_t launch_generic_attn(const ShapeKey& s, const void* qt, const int32_t* qsl, int rows,
+                               const void* k_cache, const void* v_cache, const void* W,
+                               const int32_t* block_tables, int max_blocks,
+                               const int32_t* seq_lens, int num_blocks, int batch,
+                               int pages_per_split, int num_splits, float* ml, float* zpart,
+                               void* out, const LatentFormat& fmt, int which, hipStream_t st);
 
 // `precedes`: the hooked kernel that follows this launch in the call.
 // w_prefetch: the W that the step's merge will read (decode), fetched into

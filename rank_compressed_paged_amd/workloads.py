@@ -74,6 +74,10 @@ GQA8 = Shape(H=32, d=128, r_k=64, r_v=512, bs=16, Hkv=8)
 # a lower rank profile of the main shape (per-layer ranks may differ)
 LOWRANK = Shape(H=32, d=128, r_k=32, r_v=256, bs=16)
 TINY_GQA = Shape(H=4, d=64, r_k=16, r_v=64, bs=16, Hkv=2)
+# shapes without a tuned instance (the generic kernels): a conservative rank
+# profile of the main shape, and an odd head count and head size
+CONSERVATIVE = Shape(H=32, d=128, r_k=128, r_v=1024, bs=16)
+ODD_H28 = Shape(H=28, d=96, r_k=48, r_v=640, bs=16)
 
 # Named workloads.  "seq" is ("fixed", L) or ("uniform", lo, hi) inclusive.
 CONFIGS = {
@@ -95,6 +99,9 @@ CONFIGS = {
     "lowrank_b16": dict(kind="decode", shape=LOWRANK, B=16, seq=("fixed", 2048), seed=10),
     "lowrank_prefill_b16": dict(kind="prefill", shape=LOWRANK, B=16, cached=4096, chunk=256,
                                 seed=11),
+    "conservative_b16": dict(kind="decode", shape=CONSERVATIVE, B=16, seq=("fixed", 2048),
+                             seed=15),
+    "odd_h28_b16": dict(kind="decode", shape=ODD_H28, B=16, seq=("fixed", 2048), seed=16),
 }
 
 

@@ -47,12 +47,22 @@ def test_shape_support():
     assert sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, num_kv_heads=32))
     assert sk.shape_supported(sk.make_dims(4, 64, 16, 64, 3, num_kv_heads=2))
     assert sk.shape_supported(sk.make_dims(32, 128, 32, 256, 3))          # low-rank profile
-    assert not sk.shape_supported(sk.make_dims(32, 128, 32, 512, 3))
-    assert not sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, num_kv_heads=16))
+    assert sk.shape_supported(sk.make_dims(4, 64, 16, 64, 3))
+    # the generic kernels: any shape with d a multiple of 32 up to 256, r_k a
+    # multiple of 8 up to min(d, 256), r_v a multiple of 8 up to
+    # min(2048, Hkv d), Hkv dividing H
+    for dims in [(32, 128, 32, 512), (32, 128, 64, 256), (28, 96, 48, 640), (32, 128, 128, 1024),
+                 (64, 256, 256, 2048), (32, 128, 16, 128), (1, 32, 8, 8)]:
+        assert sk.shape_supported(sk.make_dims(*dims, 3)), dims
+    for hkv in (4, 16):          # r_v 512 needs Hkv d >= 512
+        assert sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, num_kv_heads=hkv))
+    assert not sk.shape_supported(sk.make_dims(32, 100, 64, 512, 3))     # d not a multiple of 32
+    assert not sk.shape_supported(sk.make_dims(32, 288, 64, 512, 3))     # d above 256
+    assert not sk.shape_supported(sk.make_dims(32, 128, 60, 512, 3))     # r_k not a multiple of 8
+    assert not sk.shape_supported(sk.make_dims(32, 128, 64, 4096, 3))    # r_v above 2048
+    assert not sk.shape_supported(sk.make_dims(4, 32, 8, 200, 3, num_kv_heads=1))  # r_v > Hkv d
     assert not sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, num_kv_heads=5))  # not a divisor
     assert not sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, num_kv_heads=-1))
-    assert sk.shape_supported(sk.make_dims(4, 64, 16, 64, 3))
-    assert not sk.shape_supported(sk.make_dims(32, 128, 64, 256, 3))
     assert not sk.shape_supported(sk.make_dims(32, 128, 64, 512, 3, block_size=32))
     assert not sk.shape_supported(sk.make_dims(32, 128, 256, 512, 3))  # r_k > d
     assert not sk.shape_supported(sk.make_dims(32, 128, 64, 512, 0))
@@ -75,7 +85,7 @@ def test_decode_validation():
     assert _decode(d, B=-1) == 2
     assert _decode(d, scale=0.0) == 7
     assert _decode(d, scale=float("nan")) == 7
-    assert _decode(sk.make_dims(32, 128, 64, 256, 8)) == 3   # unsupported shape
+    assert _decode(sk.make_dims(32, 100, 64, 256, 8)) == 3   # unsupported shape
     assert sk.lib().starkv_decode_attn(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, 1, 1,
                                        0.1, FAKE, FAKE, 0, None) == 1
     assert _decode(d, B=0) == 0                              # empty batch: no-op
@@ -101,8 +111,8 @@ def test_append_validation():
     kv8 = sk.make_dims(8, 128, 64, 512, 8)
     assert f(ctypes.byref(kv8), None, None, None, None, None, 0, None, None, None, 0, None) == 0
     assert f(ctypes.byref(kv8), FAKE, None, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, ws, None) == 1
-    kv16 = sk.make_dims(16, 128, 64, 512, 8)
-    assert f(ctypes.byref(kv16), FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, ws,
+    bad = sk.make_dims(16, 100, 64, 512, 8)       # outside every instance's limits
+    assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, ws,
              None) == 3
 
 
@@ -121,6 +131,9 @@ def test_append_workspace_size():
     assert sk.append_workspace_size(d, 2817) == 0
     assert sk.append_workspace_size(d, 4096) == 0
     assert sk.append_workspace_size(sk.make_dims(32, 128, 32, 256, 8), 1024) == 0
+    # shapes without a few-token instance take the tiled kernel: no workspace
+    assert sk.append_workspace_size(sk.make_dims(28, 96, 48, 640, 8), 16) == 0
+    assert sk.append_workspace_size(sk.make_dims(32, 128, 64, 512, 8, num_kv_heads=16), 16) == 0
     assert sk.append_workspace_size(d, 0) == 0
     # grouped-query caches: only the key/value heads enter
     assert sk.append_workspace_size(sk.make_dims(32, 128, 64, 512, 8, num_kv_heads=8), 16) == 16 * 16 * 512 * 4
@@ -284,4 +297,4 @@ def test_fp8_validation():
     assert dec(ks=-1.0) == 7
     assert dec(vs=float("nan")) == 7
     assert dec(q=None) == 1
-    assert dec(dims=sk.make_dims(32, 128, 32, 256, 8)) == 3   # no FP8 instance for this profile
+    assert dec(dims=sk.make_dims(32, 100, 32, 256, 8)) == 3   # outside every instance's limits
