@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define STARKV_ABI_VERSION 5
+#define STARKV_ABI_VERSION 6
 
 typedef enum {
   STARKV_OK = 0,
@@ -367,13 +367,24 @@ starkv_status starkv_decode_plan(const starkv_dims* dims, int32_t batch, int32_t
  *                 the number of non-positive pivots the Cholesky steps met
  *                 (0 on success; > 0 means rank-deficient samples or start,
  *                 and the output is then not orthonormal)
+ *   residual      optional (NULL = not computed), 2 fp32 device words: the
+ *                 convergence of the returned bases (before their fp16
+ *                 rounding) as the relative invariant-subspace residual
+ *                 ||G B - B (B^T G B)||_F / ||G B||_F, G the second-moment
+ *                 matrix; [0] keys (largest over the heads), [1] values.
+ *                 0 for an exact eigenspace.  By the Davis-Kahan sin-theta
+ *                 theorem the sine of the largest angle between span(B) and
+ *                 the top eigenspace is at most residual * ||G B||_F /
+ *                 (lambda_r - lambda_{r+1}) when that gap is positive.  Costs
+ *                 one more product with G per side.
  * Asynchronous on `stream`; about 20 kernels per iteration.
  */
 starkv_status starkv_fit_workspace_size(const starkv_dims* dims, size_t* bytes /* (host) */);
 starkv_status starkv_fit_bases(const starkv_dims* dims, const void* k, const void* v,
                                int32_t num_samples, const float* u0, const float* w0,
                                int32_t iters, void* U, void* W, void* workspace,
-                               size_t workspace_bytes, int32_t* info, void* stream);
+                               size_t workspace_bytes, int32_t* info, float* residual,
+                               void* stream);
 
 /*
  * Measurement utility (not part of the attention path): read `bytes` bytes

@@ -648,7 +648,8 @@ starkv_status starkv_fit_workspace_size(const starkv_dims* dims, size_t* bytes) 
 starkv_status starkv_fit_bases(const starkv_dims* dims, const void* k, const void* v,
                                int32_t num_samples, const float* u0, const float* w0,
                                int32_t iters, void* U, void* W, void* workspace,
-                               size_t workspace_bytes, int32_t* info, void* stream) {
+                               size_t workspace_bytes, int32_t* info, float* residual,
+                               void* stream) {
   ShapeKey key;
   starkv_status st = check_fit_dims(dims, &key);
   if (st != STARKV_OK) return st;
@@ -657,9 +658,10 @@ starkv_status starkv_fit_bases(const starkv_dims* dims, const void* k, const voi
   st = check_ptrs({k, v, u0, w0, U, W, workspace});
   if (st != STARKV_OK) return st;
   if (info && ((uintptr_t)info & 3u) != 0) return STARKV_ERR_ALIGN;
+  if (residual && ((uintptr_t)residual & 3u) != 0) return STARKV_ERR_ALIGN;
   if (workspace_bytes < fit_workspace_layout(key).total) return STARKV_ERR_WORKSPACE;
   const hipError_t e = launch_fit(key, k, v, num_samples, u0, w0, iters, U, W, workspace,
-                                  (int*)info, (hipStream_t)stream);
+                                  (int*)info, residual, (hipStream_t)stream);
   return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
 }
 

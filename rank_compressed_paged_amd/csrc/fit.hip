@@ -285,15 +285,17 @@ __global__ __launch_bounds__(256) void symm_f32_kernel(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Slice s of S_p = Y_p^T Y_p: sum over rows [s*rows, (s+1)*rows) of Y_p
-// (n x r fp32) of the exact fp64 products, lower 64x64 tiles only.
+// Slice s of S_p = X_p^T Y_p: sum over rows [s*rows, (s+1)*rows) of X_p and
+// Y_p (n x r fp32) of the exact fp64 products; lower 64x64 tiles only
+// (X = Y, a symmetric S), or every tile (full).
 // grid (tiles, problems * slices); 256 threads, 4x4 outputs each; 32-row
 // chunks, the next one loaded into registers while the current one is used.
 // Output: S + (p * slices + s) * r * r.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void syrk_f64_kernel(const float* __restrict__ Y, size_t sy,
+__global__ __launch_bounds__(256) void syrk_f64_kernel(const float* __restrict__ X,
+                                                       const float* __restrict__ Y, size_t sy,
                                                        int n, int r, int slices, int rows,
-                                                       double* __restrict__ S) {
+                                                       int full, double* __restrict__ S) {
   __shared__ __attribute__((aligned(16))) float sa[2][32][64 + 4];
   __shared__ __attribute__((aligned(16))) float sb[2][32][64 + 4];
   // the tiles of one row slice (which share its rows of Y) together
@@ -301,7 +303,14 @@ __global__ __launch_bounds__(256) void syrk_f64_kernel(const float* __restrict__
   const int task = xcd_task(blockIdx.y * nt + blockIdx.x, nt * gridDim.y);
   const int p = (task / nt) / slices, s = (task / nt) % slices;
   int I, J;
-  tri_index(task % nt, I, J);
+  if (full) {
+    const int nbk = (r + 63) / 64;
+    I = (task % nt) / nbk;
+    J = (task % nt) % nbk;
+  } else {
+    tri_index(task % nt, I, J);
+  }
+  const float* Xp = X + (size_t)p * sy;
   const float* Yp = Y + (size_t)p * sy;
   const int a0 = I * 64, b0 = J * 64;
   const int i_beg = s * rows, i_end = min(n, i_beg + rows);
@@ -312,7 +321,7 @@ __global__ __launch_bounds__(256) void syrk_f64_kernel(const float* __restrict__
     for (int e = 0; e < 8; ++e) {
       const int idx = tid + e * 256, ii = idx >> 6, c = idx & 63;
       const bool rok = i0 + ii < i_end;
-      ya[e] = (rok && a0 + c < r) ? Yp[(size_t)(i0 + ii) * r + a0 + c] : 0.f;
+      ya[e] = (rok && a0 + c < r) ? Xp[(size_t)(i0 + ii) * r + a0 + c] : 0.f;
       yb[e] = (rok && b0 + c < r) ? Yp[(size_t)(i0 + ii) * r + b0 + c] : 0.f;
     }
   };
@@ -364,16 +373,17 @@ __global__ __launch_bounds__(256) void syrk_f64_kernel(const float* __restrict__
     }
 }
 
-// A_p = sum over s of S_(p*slices + s), entries in the lower 64-tiles only.
+// A_p = sum over s of S_(p*slices + s), entries in the lower 64-tiles only
+// (or all of them: full).
 __global__ __launch_bounds__(256) void sum_slices_kernel(const double* __restrict__ S, int r,
-                                                         int slices, int problems,
+                                                         int slices, int problems, int full,
                                                          double* __restrict__ A) {
   const size_t rr = (size_t)r * r;
   const size_t total = rr * problems;
   for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < total; x += (size_t)gridDim.x * 256) {
     const size_t p = x / rr, e = x % rr;
     const int i = (int)(e / r), j = (int)(e % r);
-    if (j / 64 > i / 64) continue;
+    if (!full && j / 64 > i / 64) continue;
     double s = 0.0;
     for (int k = 0; k < slices; ++k) s += S[(p * slices + k) * rr + e];
     A[x] = s;
@@ -781,6 +791,86 @@ __global__ __launch_bounds__(256) void trsm_kernel(const float* __restrict__ Y, 
   }
 }
 
+// Convergence of the returned basis Q_p (orthonormal n x r) of each problem:
+// with Y_p = G_p Q_p and T_p = Q_p^T Y_p (the Rayleigh matrix, fp64), the
+// invariant-subspace residual R_p = Y_p - Q_p T_p, formed explicitly (the
+// difference of squared norms ||Y||^2 - ||T||^2 would lose it below the
+// square root of Q's fp32 orthonormality error).  Work group (32 rows, p):
+// the rows of Q in LDS, thread j of each round accumulating column j of
+// those 32 rows of Q T in fp64 (T read once per work group); the partial
+// sums of |R|^2 and |Y|^2 go to part[(p * blocks + block) * 2 + {0, 1}].
+constexpr int kResRows = 32;
+__global__ __launch_bounds__(256) void fit_resid_rows_kernel(const float* __restrict__ Q,
+                                                             const float* __restrict__ Y,
+                                                             size_t sq, int n, int r,
+                                                             const double* __restrict__ T,
+                                                             double* __restrict__ part) {
+  __shared__ float sQ[kResRows][512];
+  __shared__ double red[2][256];
+  const int blk = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
+  const int i0 = blk * kResRows;
+  const float* Qp = Q + (size_t)p * sq;
+  const float* Yp = Y + (size_t)p * sq;
+  const double* Tp = T + (size_t)p * r * r;
+  for (int x = tid; x < kResRows * r; x += 256) {
+    const int row = x / r, k = x % r;
+    sQ[row][k] = i0 + row < n ? Qp[(size_t)(i0 + row) * r + k] : 0.f;
+  }
+  __syncthreads();
+  double rr = 0.0, yy = 0.0;
+  for (int j = tid; j < r; j += 256) {
+    double acc[kResRows];
+#pragma unroll
+    for (int row = 0; row < kResRows; ++row) acc[row] = 0.0;
+    for (int k = 0; k < r; ++k) {
+      const double t = Tp[(size_t)k * r + j];
+#pragma unroll
+      for (int row = 0; row < kResRows; ++row) acc[row] = __builtin_fma((double)sQ[row][k], t, acc[row]);
+    }
+#pragma unroll
+    for (int row = 0; row < kResRows; ++row) {
+      if (i0 + row < n) {
+        const double y = (double)Yp[(size_t)(i0 + row) * r + j];
+        const double d = y - acc[row];
+        rr = __builtin_fma(d, d, rr);
+        yy = __builtin_fma(y, y, yy);
+      }
+    }
+  }
+  red[0][tid] = rr;
+  red[1][tid] = yy;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) {
+      red[0][tid] += red[0][tid + w];
+      red[1][tid] += red[1][tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    part[((size_t)p * gridDim.x + blk) * 2] = red[0][0];
+    part[((size_t)p * gridDim.x + blk) * 2 + 1] = red[1][0];
+  }
+}
+
+// *out = max_p sqrt(sum |R_p|^2 / sum |Y_p|^2) (0 when Y_p is zero), summing
+// the row blocks' partials in order.  One work group.
+__global__ __launch_bounds__(64) void fit_resid_final_kernel(const double* __restrict__ part,
+                                                             int blocks, int problems,
+                                                             float* __restrict__ out) {
+  if (threadIdx.x != 0) return;
+  double worst = 0.0;
+  for (int p = 0; p < problems; ++p) {
+    double rr = 0.0, yy = 0.0;
+    for (int b = 0; b < blocks; ++b) {
+      rr += part[((size_t)p * blocks + b) * 2];
+      yy += part[((size_t)p * blocks + b) * 2 + 1];
+    }
+    worst = fmax(worst, yy > 0.0 ? sqrt(rr / yy) : 0.0);
+  }
+  *out = (float)worst;
+}
+
 __global__ __launch_bounds__(256) void to_f16_kernel(const float* __restrict__ src, size_t n,
                                                      half_t* __restrict__ dst) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
@@ -812,10 +902,13 @@ FitWorkspace fit_workspace_layout(const ShapeKey& s) {
   off = align256_(off + (size_t)s.H * nk * rk * 4);
   w.qk_off[1] = off;
   off = align256_(off + (size_t)s.H * nk * rk * 4);
-  w.sv_off = off;  // slices of S_v (unused when one slice)
-  off = align256_(off + (size_t)syrk_slices((int)nv) * rv * rv * 8);
+  // slices of S_v (unused when one slice), and the residual's row-block sums
+  w.sv_off = off;
+  off = align256_(off + std::max<size_t>((size_t)syrk_slices((int)nv) * rv * rv,
+                                         2 * (size_t)ceil_div((int)nv, kResRows)) * 8);
   w.sk_off = off;
-  off = align256_(off + (size_t)s.H * syrk_slices((int)nk) * rk * rk * 8);
+  off = align256_(off + (size_t)s.H * std::max<size_t>((size_t)syrk_slices((int)nk) * rk * rk,
+                                                       2 * (size_t)ceil_div((int)nk, kResRows)) * 8);
   w.av_off = off;
   off = align256_(off + rv * rv * 8);
   w.ak_off = off;
@@ -846,13 +939,13 @@ hipError_t orth(const OrthProblem& o, const float* Y, float* Q, int* info, hipSt
   const int tiles = nbk * (nbk + 1) / 2;
   const size_t sy = (size_t)o.n * o.r;
   double* dst = slices > 1 ? o.S : o.A;
-  hipLaunchKernelGGL(syrk_f64_kernel, dim3(tiles, o.P * slices), dim3(256), 0, st, Y, sy, o.n,
-                     o.r, slices, rows, dst);
+  hipLaunchKernelGGL(syrk_f64_kernel, dim3(tiles, o.P * slices), dim3(256), 0, st, Y, Y, sy, o.n,
+                     o.r, slices, rows, 0, dst);
   if (slices > 1) {
     const size_t total = (size_t)o.P * o.r * o.r;
     const int blocks = (int)std::min<size_t>((total + 255) / 256, 2048);
     hipLaunchKernelGGL(sum_slices_kernel, dim3(blocks), dim3(256), 0, st, o.S, o.r, slices, o.P,
-                       o.A);
+                       0, o.A);
   }
   for (int p = 0; p < nbk; ++p) {
     hipLaunchKernelGGL(chol_panel_kernel, dim3(o.P), dim3(256), 0, st, o.A, o.L, o.D, o.r, p,
@@ -869,11 +962,37 @@ hipError_t orth(const OrthProblem& o, const float* Y, float* Q, int* info, hipSt
   return hipGetLastError();
 }
 
+// The residual of the returned basis Q (see fit_resid_rows_kernel): Y = G Q
+// into Yw, T = Q^T Y (every tile, fp64) into o.A, then the reduction.
+hipError_t residual(const OrthProblem& o, const float* G, int tm, const float* Q, float* Yw,
+                    float* out, hipStream_t st) {
+  const size_t sg = (size_t)o.n * o.n, sq = (size_t)o.n * o.r;
+  hipLaunchKernelGGL(symm_f32_kernel, dim3(ceil_div(o.r, 64), o.n / 64, o.P), dim3(256), 0, st, G,
+                     sg, o.n, tm, Q, sq, Yw, sq, o.r);
+  const int slices = syrk_slices(o.n), rows = ceil_div(o.n, slices);
+  const int nbk = ceil_div(o.r, 64);
+  double* dst = slices > 1 ? o.S : o.A;
+  hipLaunchKernelGGL(syrk_f64_kernel, dim3(nbk * nbk, o.P * slices), dim3(256), 0, st, Q, Yw, sq,
+                     o.n, o.r, slices, rows, 1, dst);
+  if (slices > 1) {
+    const size_t total = (size_t)o.P * o.r * o.r;
+    const int blocks = (int)std::min<size_t>((total + 255) / 256, 2048);
+    hipLaunchKernelGGL(sum_slices_kernel, dim3(blocks), dim3(256), 0, st, o.S, o.r, slices, o.P,
+                       1, o.A);
+  }
+  // the slices of S are free again: they take the row blocks' partial sums
+  const int blocks = ceil_div(o.n, kResRows);
+  hipLaunchKernelGGL(fit_resid_rows_kernel, dim3(blocks, o.P), dim3(256), 0, st, Q, Yw, sq, o.n,
+                     o.r, o.A, o.S);
+  hipLaunchKernelGGL(fit_resid_final_kernel, dim3(1), dim3(64), 0, st, o.S, blocks, o.P, out);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_fit(const ShapeKey& s, const void* k, const void* v, int n_samples,
                       const float* u0, const float* w0, int iters, void* U, void* W,
-                      void* workspace, int* info, hipStream_t st) {
+                      void* workspace, int* info, float* residual_out, hipStream_t st) {
   const FitWorkspace ws = fit_workspace_layout(s);
   char* wb = (char*)workspace;
   float* Gv = (float*)(wb + ws.gv_off);
@@ -926,6 +1045,11 @@ hipError_t launch_fit(const ShapeKey& s, const void* k, const void* v, int n_sam
     }
     e = orth(sd.o, sd.buf[0], sd.buf[1], info, st);  // second round of the last QR
     if (e != hipSuccess) return e;
+    if (residual_out) {  // keys into [0], values into [1]
+      e = residual(sd.o, sd.G, tm, sd.buf[1], sd.buf[0], residual_out + (&sd == &sides[0] ? 1 : 0),
+                   st);
+      if (e != hipSuccess) return e;
+    }
     const size_t cnt = (size_t)sd.P * sq;
     const int blocks = (int)std::min<size_t>((cnt + 255) / 256, 4096);
     hipLaunchKernelGGL(to_f16_kernel, dim3(blocks), dim3(256), 0, st, sd.buf[1], cnt, sd.out);

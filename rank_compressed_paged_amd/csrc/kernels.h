@@ -175,9 +175,11 @@ FitWorkspace fit_workspace_layout(const ShapeKey& s);
 
 // Top-r_k eigenspaces of each head's key second-moment matrix and the top-r_v
 // eigenspace of the joint value one, by subspace iteration from u0 / w0.
+// residual_out (optional, 2 floats): the relative invariant-subspace residual
+// of the returned bases, keys (largest over heads) then values.
 hipError_t launch_fit(const ShapeKey& s, const void* k, const void* v, int n_samples,
                       const float* u0, const float* w0, int iters, void* U, void* W,
-                      void* workspace, int* info, hipStream_t st);
+                      void* workspace, int* info, float* residual_out, hipStream_t st);
 
 hipError_t launch_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl, int total_q,
                           int max_query_len, const void* k_cache, const void* v_cache,

@@ -110,7 +110,7 @@ _lib.starkv_fit_workspace_size.restype = _i32
 _lib.starkv_fit_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(_sz)]
 _lib.starkv_fit_bases.restype = _i32
 _lib.starkv_fit_bases.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp,
-                                  _vp, _sz, _vp, _vp]
+                                  _vp, _sz, _vp, _vp, _vp]
 _f32 = ctypes.c_float
 _lib.starkv_append_fp8.restype = _i32
 _lib.starkv_append_fp8.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _vp, _vp, _vp, _i32, _f32, _f32,
@@ -378,10 +378,12 @@ def fit_workspace_size(dims):
 
 
 def fit_bases(k, v, r_k, r_v, u0, w0, iters, U=None, W=None, workspace=None, info=None,
-              stream=None):
+              residual=None, stream=None):
     """Bases U [H, d, r_k], W [H*d, r_v] (fp16) from samples k, v [N, H, d]
     (fp16), by subspace iteration from u0, w0 (fp32, same shapes).  `info`
-    (int32 [1], optional) receives the count of non-positive pivots."""
+    (int32 [1], optional) receives the count of non-positive pivots;
+    `residual` (float32 [2], optional) the relative invariant-subspace
+    residual of the returned key (largest over heads) and value bases."""
     N, H, d = k.shape
     dims = make_dims(H, d, r_k, r_v, 1)
     if U is None:
@@ -398,6 +400,7 @@ def fit_bases(k, v, r_k, r_v, u0, w0, iters, U=None, W=None, workspace=None, inf
         int(iters), _dev(U, torch.float16, "U", (H, d, r_k)),
         _dev(W, torch.float16, "W", (H * d, r_v)), _dev(workspace, torch.uint8, "workspace"),
         int(workspace.numel()), None if info is None else _dev(info, torch.int32, "info", (1,)),
+        None if residual is None else _dev(residual, torch.float32, "residual", (2,)),
         _stream(stream))
     _check(st, "starkv_fit_bases")
     return U, W

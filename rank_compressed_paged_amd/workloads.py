@@ -391,8 +391,20 @@ class FitCase:
     name: str = ""
 
 
-def make_fit_case(shape: Shape, N, seed=0, noise=0.05, name=""):
-    """Samples with a planted low-rank structure plus isotropic noise.
+def make_fit_case(shape: Shape, N, seed=0, noise=0.05, name="", spectrum="planted"):
+    """K/V samples for the bases fit, with one of three spectra.
+
+    spectrum "power" or "exp" (decaying spectra with no gap at the rank, as
+    real K/V are): per head an orthonormal d x d frame A_h (reduced QR of
+    N(0,1), sign-fixed), then one (H*d) x (H*d) frame B; coefficients z_k ~
+    N(0,1) [N, H, d] and z_v ~ N(0,1) [N, H*d]; then u0, w0 as below.
+    k[n, h] = A_h (s_k * z_k[n, h]) and vec(v[n]) = B (s_v * z_v[n]) with
+    s^2 (the second moment's spectrum up to sampling) falling as (i + 1)^-2
+    ("power") or exp(-4 i / r) ("exp", r the side's rank), scaled to a largest
+    s of 4.  The eigenvalue ratio at the rank is then about (r / (r+1))^2 or
+    exp(-4 / r): subspace iteration needs hundreds of steps.
+
+    spectrum "planted" (the default):
 
     Draw order (numpy PCG64, ``default_rng(seed)``):
       1. per head h: an orthonormal d x r_k frame A_h (reduced QR of N(0,1),
@@ -417,6 +429,23 @@ def make_fit_case(shape: Shape, N, seed=0, noise=0.05, name=""):
         return qm * sgn[None, :]
 
     H, d, rk, rv = shape.H, shape.d, shape.r_k, shape.r_v
+    if spectrum in ("power", "exp"):
+        def scales(m, r):
+            i = np.arange(m, dtype=np.float64)
+            s2 = (i + 1.0) ** -2.0 if spectrum == "power" else np.exp(-4.0 * i / r)
+            return 4.0 * np.sqrt(s2 / s2[0])
+        A = np.stack([frame(d, d) for _ in range(H)])        # [H, d, d]
+        B = frame(H * d, H * d)
+        zk = rng.standard_normal((N, H, d))
+        zv = rng.standard_normal((N, H * d))
+        k = np.einsum("hde,nhe->nhd", A, zk * scales(d, rk))
+        v = (zv * scales(H * d, rv)) @ B.T
+        u0 = rng.standard_normal((H, d, rk), dtype=np.float32)
+        w0 = rng.standard_normal((H * d, rv), dtype=np.float32)
+        return FitCase(shape, k.astype(np.float16), v.reshape(N, H, d).astype(np.float16),
+                       u0, w0, seed, name)
+    if spectrum != "planted":
+        raise ValueError(spectrum)
     A = np.stack([frame(d, rk) for _ in range(H)])          # [H, d, rk]
     B = frame(H * d, rv)                                     # [H*d, rv]
     zk = rng.standard_normal((N, H, rk))

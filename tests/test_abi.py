@@ -31,7 +31,7 @@ def test_exports_match_header():
 
 
 def test_version_and_status_strings():
-    assert sk.abi_version() == 5
+    assert sk.abi_version() == 6
     for s in range(0, 8):
         assert sk.lib().starkv_status_string(s)
     assert sk.lib().starkv_status_string(99) == b"unknown status"
@@ -254,20 +254,21 @@ def test_fit_validation():
     # the fp32 value Gram matrix alone is (H*d)^2 * 4 bytes
     assert need >= (32 * 128) ** 2 * 4
 
-    def call(dims=d, N=4096, iters=4, k=FAKE, info=None, wsb=need):
+    def call(dims=d, N=4096, iters=4, k=FAKE, info=None, wsb=need, res=None):
         return f(ctypes.byref(dims), k, FAKE, N, FAKE, FAKE, iters, FAKE, FAKE, FAKE, wsb, info,
-                 None)
+                 res, None)
     assert call(wsb=need - 1) == 4                               # workspace too small
     assert call(k=None) == 1                                     # null pointer
     assert call(k=MISALIGNED) == 5
     assert call(info=FAKE + 2) == 5                              # info must be 4-byte aligned
+    assert call(res=FAKE + 2) == 5                               # so must the residual
     assert call(N=511) == 2                                      # fewer samples than r_v
     assert call(iters=0) == 7
     assert call(iters=1001) == 7
     assert call(dims=sk.make_dims(32, 96, 64, 512, 8)) == 3      # d not a multiple of 64
     assert call(dims=sk.make_dims(32, 128, 64, 1024, 8)) == 3    # r_v > 512
     assert call(dims=sk.make_dims(32, 128, 129, 512, 8)) == 2    # r_k > d
-    assert f(None, FAKE, FAKE, 1, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, None, None) == 1
+    assert f(None, FAKE, FAKE, 1, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 0, None, None, None) == 1
     # any shape within the limits, block size and page count unused
     odd = sk.make_dims(3, 192, 40, 100, 0, block_size=7)
     assert sk.fit_workspace_size(odd) >= (3 * 192) ** 2 * 4

@@ -55,13 +55,15 @@ def check_basis(B16, ref, what):
     assert orth <= ORTHO_TOL, f"{what}: orthonormality {orth:.3e}"
 
 
-def run_fit(sk, case, iters):
+def run_fit(sk, case, iters, with_residual=False):
     info = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    res = torch.full((2,), -1.0, dtype=torch.float32, device="cuda") if with_residual else None
     sh = case.shape
     U, W = sk.fit_bases(dev(case.k), dev(case.v), sh.r_k, sh.r_v, dev(case.u0), dev(case.w0),
-                        iters, info=info)
+                        iters, info=info, residual=res)
     torch.cuda.synchronize()
-    return U.float().cpu().numpy(), W.float().cpu().numpy(), int(info.item())
+    out = (U.float().cpu().numpy(), W.float().cpu().numpy(), int(info.item()))
+    return out + (res.cpu().numpy(),) if with_residual else out
 
 
 def compare(case, U, W):
@@ -129,3 +131,72 @@ def test_fit_full_size(sk):
     U, W, info = run_fit(sk, case, iters=8)
     assert info == 0
     compare(case, U, W)
+
+
+def dk_bound(res, ev, r, n_samples):
+    """Davis-Kahan: sin of the largest angle between a basis B and the top-r
+    eigenspace of G is at most ||G B - B (B^T G B)||_F / (lambda_r -
+    lambda_{r+1}).  The GPU reports that residual relative to ||G B||_F
+    (sqrt of the sum of the top r eigenvalues squared for a converged basis)
+    against its own fp32 Gram matrix, which differs from the exact one by
+    about 2^-24 sqrt(N) ||G||_F (fp32 sums of N products); that perturbation
+    enters the same bound."""
+    ev = np.asarray(ev, np.float64)
+    gap = ev[r - 1] - ev[r]
+    resid = float(res) * float(np.sqrt(np.sum(ev[:r] ** 2)))
+    gram = 2.0 ** -24 * np.sqrt(n_samples) * float(np.sqrt(np.sum(ev ** 2)))
+    return (resid + gram) / gap
+
+
+DECAY_SHAPES = [wl.Shape(H=4, d=64, r_k=16, r_v=32), wl.Shape(H=3, d=128, r_k=24, r_v=48)]
+
+
+@pytest.mark.parametrize("spectrum", ["power", "exp"])
+@pytest.mark.parametrize("shape", DECAY_SHAPES, ids=["h4_d64", "h3_d128"])
+def test_fit_decaying_spectrum(sk, shape, spectrum):
+    """Spectra with no planted gap (sample eigenvalue ratio at the rank
+    0.80-0.97 with these shapes and 16384 samples): 600 iterations; the
+    reported residual must be small, and the GPU basis must lie within the
+    Davis-Kahan bound that residual implies (plus the fp16 rounding of the
+    exact basis) of the oracle's eigenspace."""
+    iters = 600
+    case = wl.make_fit_case(shape, 16384, seed=16, spectrum=spectrum,
+                            name=f"{spectrum} H{shape.H} d{shape.d}")
+    note(f"fit {spectrum} spectrum H{shape.H} d{shape.d} iters={iters}")
+    U, W, info, res = run_fit(sk, case, iters, with_residual=True)
+    assert info == 0
+    Uo, Wo, ek, ev = oracle.fit_bases(case.k, case.v, shape.r_k, shape.r_v)
+    ratio_k = max(ek[h][shape.r_k] / ek[h][shape.r_k - 1] for h in range(shape.H))
+    ratio_v = ev[shape.r_v] / ev[shape.r_v - 1]
+    print(f"[fit] {spectrum} H{shape.H} d{shape.d}: {iters} iterations, residual keys "
+          f"{res[0]:.3e} values {res[1]:.3e}; eigenvalue ratio at the rank keys {ratio_k:.3f} "
+          f"values {ratio_v:.3f}", flush=True)
+    assert 0.0 <= res[0] < 1e-3 and 0.0 <= res[1] < 1e-3
+    for h in range(shape.H):
+        b = dk_bound(res[0], ek[h], shape.r_k, 16384)
+        d16 = sin_theta(Uo[h].astype(np.float16), Uo[h])
+        st = sin_theta(U[h], Uo[h])
+        print(f"[parity] {case.name} U[{h}]: sin_theta={st:.3e} bound {b + 2 * d16 + 2e-4:.3e}",
+              flush=True)
+        assert st <= b + 2 * d16 + 2e-4
+    b = dk_bound(res[1], ev, shape.r_v, 16384)
+    d16 = sin_theta(Wo.astype(np.float16), Wo)
+    st = sin_theta(W, Wo)
+    print(f"[parity] {case.name} W: sin_theta={st:.3e} bound {b + 2 * d16 + 2e-4:.3e}", flush=True)
+    assert st <= b + 2 * d16 + 2e-4
+
+
+def test_fit_residual_falls_with_iterations(sk):
+    """The residual is a convergence measure: on a decaying spectrum it falls
+    as the iterations grow, and it is near zero on the planted one."""
+    case = wl.make_fit_case(DECAY_SHAPES[0], 16384, seed=17, spectrum="exp", name="exp h4")
+    note("fit residual vs iterations")
+    rs = [run_fit(sk, case, it, with_residual=True)[3] for it in (2, 20, 200)]
+    print(f"[fit] residual after 2 / 20 / 200 iterations: keys "
+          f"{[f'{r[0]:.2e}' for r in rs]} values {[f'{r[1]:.2e}' for r in rs]}", flush=True)
+    for side in (0, 1):
+        assert rs[0][side] > rs[1][side] > rs[2][side]
+    planted = wl.make_fit_case(wl.TINY, 4096, seed=18, name="planted tiny")
+    r = run_fit(sk, planted, 8, with_residual=True)[3]
+    print(f"[fit] planted spectrum, 8 iterations: residual {r[0]:.2e} {r[1]:.2e}", flush=True)
+    assert r[0] < 1e-3 and r[1] < 1e-3
