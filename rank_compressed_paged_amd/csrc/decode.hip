@@ -9,8 +9,10 @@
 // README's "Per-decode-step attention" notes), W_h being rows h*d..h*d+d-1.
 //
 // One decode step is three launches on the caller's stream:
-//   1. qproj        q~ = U_h^T q, pre-scaled by scale*log2(e), fp16, on the
-//                   matrix cores (U_h read through the transposing LDS read)
+//   1. qproj        q~ = U_h^T q, pre-scaled by scale*log2(e), fp32, on the
+//                   matrix cores (U_h read through the transposing LDS read);
+//                   the split kernel feeds it to the score products as an
+//                   fp16 hi/lo pair in otherwise unused B columns
 //   2. decode_split split-K pass over the pages (README, "Kernel profiling
 //                   breakdown": split-K attention plus a combine); one work
 //                   group owns all heads of a run of pages so the joint value

@@ -7,9 +7,12 @@
 //   S^T[t, j] = c_k[t, h] . q~[j, h]          (q~ pre-scaled by scale*log2 e)
 //   P = causal softmax over t <= P0 + j, P0 = seq_len - chunk_len
 //   Z^T[f, j] = sum_t c_v[t, f] P[j, t]        (normalised at the end)
-// and writes z as fp16 (tiled by 32-token blocks in the operand order of the
-// up-projection); the up-projection out_h = W_h z_h runs afterwards on the
-// matrix cores (decode.hip, many-token variant).
+// then applies the up-projection out_h = W_h z_h: in the kernel's epilogue
+// for the main-shape instances (z staged in LDS, W_h rows through a register
+// ring), or, for the other instances, by writing z as fp16 tiled by 32-token
+// blocks in the operand order of the many-token up-projection kernel
+// (decode.hip), which runs afterwards.  q~ arrives in fp32 and enters the
+// score products as an fp16 hi/lo pair (two products per key chunk).
 //
 // Work group = (request, tile of MQ queries, group of G heads), NW waves;
 // the main shape runs G = 2 heads x MQ = 64 queries = 128 (head, query) rows
