@@ -488,9 +488,14 @@ def low_batch_leg(flush_fn, steps):
         eager_us = wall(step)
         graph_us = wall(g.replay)
         gpu_ms, _, _ = timed(step, n, flush_fn)
+        ws2 = sk.alloc_workspace(sk.decode_workspace_size(dims, B, 2048, launches=2), "cuda")
+        fused_ms, _, _ = timed(lambda: sk.decode_attn(q, kc, vc, U, W, bt, sl, 2048, case.scale,
+                                                      out=out, workspace=ws2, launches=2),
+                               n, flush_fn)
         pps, ns = sk.decode_plan(dims, B, 2048)
         rows.append({"batch": B, "seq_len": 2048, "plan": [pps, ns],
                      "gpu_step_us": round(statistics.fmean(gpu_ms) * 1e3, 2),
+                     "fused_gpu_step_us": round(statistics.fmean(fused_ms) * 1e3, 2),
                      "eager_latency_us": round(eager_us, 2),
                      "graph_latency_us": round(graph_us, 2)})
         del g
@@ -611,6 +616,16 @@ def run_bench(args):
     _, app_kern_ms, _ = timed(append_step, max(args.steps, 10), do_flush, sk.TIME_APPEND)
     # the step with its append in front (second row)
     both_ms, _, _ = timed(lambda: (append_step(), step()), args.steps, do_flush)
+    # the same step with the split pass and the merge fused into one kernel
+    # (the q projection, then that kernel) instead of three kernels
+    ws2 = sk.alloc_workspace(sk.decode_workspace_size(dims, B, msl, launches=2), "cuda")
+
+    def step2():
+        sk.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["U"], t["W"], t["block_tables"],
+                       t["seq_lens"], msl, case.scale, out=out, workspace=ws2, launches=2)
+    fused_ms, _, _ = timed(step2, args.steps, do_flush)
+    _, fused_kern_ms, _ = timed(step2, args.steps, do_flush, sk.TIME_DECODE_SPLIT)
+    del ws2
 
     # measured streaming-read ceiling on this machine: the library's plain
     # streaming read (16-byte non-temporal loads, 16 in flight per thread)
@@ -655,6 +670,8 @@ def run_bench(args):
         "append_step_ms": round(statistics.fmean(app_ms), 5),
         "append_kernel_ms": round(statistics.fmean(app_kern_ms), 5),
         "step_with_append_ms": round(statistics.fmean(both_ms), 5),
+        "fused_step_ms": round(statistics.fmean(fused_ms), 5),
+        "fused_kernel_ms": round(statistics.fmean(fused_kern_ms), 5),
         "wall_s_timed_loop_incl_flush": round(wall, 4),
         "split_plan": {"pages_per_split": pps, "num_splits": ns},
         "flush": args.flush,

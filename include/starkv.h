@@ -207,11 +207,16 @@ starkv_status starkv_decode_attn(const starkv_dims* dims, const void* q, const v
  * choice (what starkv_decode_attn uses) or a value in range:
  *   pages_per_split  1..256 consecutive 16-token pages per work group
  *   merge_seqs       sequences per work group of the merge: 1, 2, 4 or 8
+ *   launches         3: q projection, split pass and merge as three kernels
+ *                    (the library's choice); 2: the split pass and the merge
+ *                    in one kernel whose work groups merge once their
+ *                    sequences' splits have signalled (tuned shapes only)
  * Any plan gives the same attention up to rounding order.
  */
 typedef struct {
   int32_t pages_per_split;
   int32_t merge_seqs;
+  int32_t launches;
 } starkv_decode_config;
 
 /*

@@ -73,12 +73,24 @@ static int device_cus() {
 // grows to 512 threads whose split groups take disjoint sets of splits, so
 // the partials are requested in fewer rounds (1024 threads would leave 128
 // registers per thread, too few for the operands in flight).
-static DecodePlan with_finish(DecodePlan p, const ShapeKey& s, int batch, int force_tb) {
+static DecodePlan with_finish(DecodePlan p, const ShapeKey& s, int batch, int force_tb,
+                              bool fused) {
   const int cus = device_cus();
   int tb = force_tb;
   if (tb != 1 && tb != 2 && tb != 4 && tb != 8) {
     tb = (long)s.H * batch < cus ? 1 : 2;
     while (tb >= 2 && tb < 8 && (long)s.H * cdiv(batch, 2 * tb) >= cus) tb *= 2;
+  }
+  if (fused) {
+    // the merge runs in the split kernel's work groups: their thread count,
+    // four splits per request round
+    p.fused = true;
+    p.finish_tb = tb;
+    p.finish_cb = 4;
+    p.finish_nt = decode_threads(s);
+    const int per_round = 4 * finish_split_groups(p.finish_nt, tb, s.rv);
+    p.split_stride = cdiv(p.num_splits, per_round) * per_round;
+    return p;
   }
   int nt = 256, cb = 4;
   if (tb >= 4) {
@@ -135,13 +147,15 @@ static DecodePlan plan_generic(const ShapeKey& s, int batch, int max_seq_len, in
 }
 
 DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int bs, int force_pps,
-                       int force_tb, bool generic) {
+                       int force_tb, bool generic, int launches) {
   if (generic) return plan_generic(s, batch, max_seq_len, bs, force_pps);
+  const bool fused = launches == 2;
   const int pages = cdiv(max_seq_len, bs);
-  if (pages <= 0 || batch <= 0) return with_finish(DecodePlan{1, 1, 0, 0, 0, 0}, s, batch, force_tb);
+  if (pages <= 0 || batch <= 0)
+    return with_finish(DecodePlan{1, 1, 0, 0, 0, 0}, s, batch, force_tb, fused);
   if (force_pps > 0) {
     const int pps = force_pps < 256 ? force_pps : 256;
-    return with_finish(DecodePlan{pps, cdiv(pages, pps), 0, 0, 0, 0}, s, batch, force_tb);
+    return with_finish(DecodePlan{pps, cdiv(pages, pps), 0, 0, 0, 0}, s, batch, force_tb, fused);
   }
   const int cus = device_cus();
   double best = 1e300;
@@ -158,7 +172,8 @@ DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int bs, in
     }
     if (ns > 4 * cus) break;
   }
-  return with_finish(DecodePlan{best_pps, cdiv(pages, best_pps), 0, 0, 0, 0}, s, batch, force_tb);
+  return with_finish(DecodePlan{best_pps, cdiv(pages, best_pps), 0, 0, 0, 0}, s, batch, force_tb,
+                     fused);
 }
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -174,6 +189,7 @@ DecodeWorkspace decode_workspace_layout(const ShapeKey& s, int batch, const Deco
     off = align256(off + (size_t)batch * s.H * 2 * p.num_splits * 4);
     w.zp_off = off;
     off = align256(off + (size_t)batch * s.H * p.num_splits * s.rv * 4);
+    w.sync_off = off;
     w.total = off;
     return w;
   }
@@ -183,6 +199,8 @@ DecodeWorkspace decode_workspace_layout(const ShapeKey& s, int batch, const Deco
   off = align256(off + (size_t)batch * p.split_stride * 2 * r16 * 4);
   w.zp_off = off;  // per-split z rows, fp16
   off = align256(off + (size_t)batch * p.split_stride * r16 * s.rv * 2);
+  w.sync_off = off;  // the fused step's counters: one per sequence, then an error word
+  if (p.fused) off = align256(off + ((size_t)batch + 1) * 4);
   w.total = off;
   return w;
 }
@@ -372,13 +390,14 @@ starkv_status check_config(const starkv_decode_config* cfg) {
   if (cfg->pages_per_split < 0 || cfg->pages_per_split > 256) return STARKV_ERR_ARG;
   const int m = cfg->merge_seqs;
   if (m != 0 && m != 1 && m != 2 && m != 4 && m != 8) return STARKV_ERR_ARG;
+  if (cfg->launches != 0 && cfg->launches != 2 && cfg->launches != 3) return STARKV_ERR_ARG;
   return STARKV_OK;
 }
 
 DecodePlan plan_for(const ShapeKey& key, int batch, int max_seq_len, int bs,
                     const starkv_decode_config* cfg, bool fp8) {
   return plan_decode(key, batch, max_seq_len, bs, cfg ? cfg->pages_per_split : 0,
-                     cfg ? cfg->merge_seqs : 0, use_generic(key, fp8));
+                     cfg ? cfg->merge_seqs : 0, use_generic(key, fp8), cfg ? cfg->launches : 0);
 }
 
 // The workspace of a decode call over fp16 latents and of one over FP8
@@ -454,11 +473,13 @@ starkv_status decode_common(const starkv_dims* dims, const void* q, const void* 
                             (float*)(wb + ws.zp_off), out, fmt, TIME_DECODE_SPLIT, s);
     return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
   }
-  hipError_t e = launch_qproj(key, q, U, batch, qscale, wb + ws.qt_off, TIME_DECODE_SPLIT, s, W);
+  uint32_t* sync = (uint32_t*)(wb + ws.sync_off);
+  hipError_t e = launch_qproj(key, q, U, batch, qscale, wb + ws.qt_off, TIME_DECODE_SPLIT, s, W,
+                              p.fused ? sync : nullptr, p.fused ? batch + 1 : 0);
   if (e != hipSuccess) return STARKV_ERR_LAUNCH;
   e = launch_decode(key, p, wb + ws.qt_off, k_cache, v_cache, W, block_tables,
                     max_blocks_per_seq, seq_lens, dims->num_blocks, batch,
-                    (float*)(wb + ws.ml_off), wb + ws.zp_off, out, fmt, s);
+                    (float*)(wb + ws.ml_off), wb + ws.zp_off, out, fmt, sync, s);
   return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
 }
 

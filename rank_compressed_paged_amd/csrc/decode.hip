@@ -102,11 +102,15 @@ __global__ __launch_bounds__(256) void qproj_kernel(const half_t* __restrict__ q
                                                     float qscale, float* __restrict__ qt,
                                                     int token_rows, const char* __restrict__ wpf,
                                                     int wpf_head_bytes, int wpf_part_bytes,
-                                                    uint32_t* __restrict__ sink) {
+                                                    uint32_t* __restrict__ sink,
+                                                    uint32_t* __restrict__ zero, int n_zero) {
   constexpr int LDU = RK + 8;  // halves per LDS row: 4 rows of a read group hit distinct banks
   __shared__ __attribute__((aligned(16))) half_t sU[D][LDU];
   const int h = blockIdx.x;
   const int tid = threadIdx.x;
+  // the counters the fused decode step that follows waits on start at zero
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = tid; i < n_zero; i += 256) zero[i] = 0u;
   if ((int)blockIdx.y >= token_rows) {  // whole work group, before any barrier
     const char* p = wpf + (size_t)(h / QG) * wpf_head_bytes +
                     (size_t)(blockIdx.y - token_rows) * wpf_part_bytes;
@@ -382,22 +386,55 @@ __device__ __forceinline__ void process_page(
   }
 }
 
-template <int H, int RK, int RV, int NW, int DEPTH, bool NT, int QG, bool FP8>
-__global__ __launch_bounds__(NW * 64) void decode_split_kernel(
-    const float* __restrict__ qt, const latent_t<FP8>* __restrict__ k_cache,
-    const latent_t<FP8>* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ seq_lens, float* __restrict__ ml, half_t* __restrict__ zpart,
-    int max_blocks, int num_blocks, int pages_per_split, int num_splits, int split_stride,
-    float v_scale) {
+// Stores and loads of the data that the fused step passes between work
+// groups (split partials): device-scope relaxed atomics, which gfx950 issues
+// as ordinary global stores / loads with the sc1 bit, so they write through to
+// and read from the device-coherent level instead of an XCD's own L2.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(half_t* p, half4 v) {
+  __hip_atomic_store((uint64_t*)p, __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ half4 ld_dev(const half_t* p) {
+  return __builtin_bit_cast(half4, __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// LDS of one split work item.
+template <int H, int RK, int RV, int NW>
+struct SplitLds {
+  using C = DecodeCfg<H, RK, RV, NW>;
+  __attribute__((aligned(16))) half_t sP[2][C::R16][BS];
+  float sAlpha[2][C::R16];
+  int sFlag[2];              // page index whose softmax step moved a running max
+  int sBlk[kMaxSplitPages];  // block ids of this split, loadable
+  float sL[C::R16];          // final softmax sums, by head
+};
+
+// One split work item: pages [s * pages_per_split, ...) of sequence b.
+// FUSED: the partials are written with device-coherent stores and, once all
+// of the work group's stores have completed, seq_done[b] is incremented with
+// release semantics (the merge waits for it).
+template <int H, int RK, int RV, int NW, int DEPTH, bool NT, int QG, bool FP8, bool FUSED>
+__device__ __forceinline__ void split_body(
+    SplitLds<H, RK, RV, NW>& lds, const int s, const int b, const float* __restrict__ qt,
+    const latent_t<FP8>* __restrict__ k_cache, const latent_t<FP8>* __restrict__ v_cache,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
+    float* __restrict__ ml, half_t* __restrict__ zpart, int max_blocks, int num_blocks,
+    int pages_per_split, int num_splits, int split_stride, float v_scale,
+    uint32_t* __restrict__ seq_done) {
   using C = DecodeCfg<H, RK, RV, NW>;
   using kvec = typename PageRegs<H, RK, RV, NW, QG, FP8>::kvec;
-  __shared__ __attribute__((aligned(16))) half_t sP[2][C::R16][BS];
-  __shared__ float sAlpha[2][C::R16];
-  __shared__ int sFlag[2];  // page index whose softmax step moved a running max
-  __shared__ int sBlk[kMaxSplitPages];  // block ids of this split, loadable
-  __shared__ float sL[C::R16];          // final softmax sums, by head
-
-  const int s = blockIdx.x, b = blockIdx.y;
+  auto& sP = lds.sP;
+  auto& sAlpha = lds.sAlpha;
+  auto& sFlag = lds.sFlag;
+  auto& sBlk = lds.sBlk;
+  auto& sL = lds.sL;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
@@ -498,8 +535,13 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
   // contiguous features.  The sums move to the value layout through LDS.
   if (col < C::HPW && quad == 0) {
     float* mp = ml + ((size_t)b * C::R16 + w * C::HPW + col) * 2 * split_stride + s;
-    mp[0] = st.m_run;
-    mp[split_stride] = st.l_run;
+    if constexpr (FUSED) {
+      st_dev(mp, st.m_run);
+      st_dev(mp + split_stride, st.l_run);
+    } else {
+      mp[0] = st.m_run;
+      mp[split_stride] = st.l_run;
+    }
     sL[w * C::HPW + col] = st.l_run;
   }
   block_sync_lds();
@@ -515,10 +557,35 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
         half4 zh;
 #pragma unroll
         for (int r = 0; r < 4; ++r) zh[r] = (half_t)(st.acc[rt][ft][r] * inv);
-        *(half4*)(pz + (size_t)hr * split_stride * RV + ft * 16) = zh;
+        if constexpr (FUSED)
+          st_dev(pz + (size_t)hr * split_stride * RV + ft * 16, zh);
+        else
+          *(half4*)(pz + (size_t)hr * split_stride * RV + ft * 16) = zh;
       }
     }
   }
+  if constexpr (FUSED) {
+    // Every store of the work group has completed at the device-coherent
+    // level (sc1 stores, vmcnt(0)) before the barrier, so a relaxed increment
+    // publishes the partials.  A release increment would add an L2
+    // write-back (buffer_wbl2) per work group: 3 us more per decode_b16 step.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (tid == 0) __hip_atomic_fetch_add(seq_done + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <int H, int RK, int RV, int NW, int DEPTH, bool NT, int QG, bool FP8>
+__global__ __launch_bounds__(NW * 64) void decode_split_kernel(
+    const float* __restrict__ qt, const latent_t<FP8>* __restrict__ k_cache,
+    const latent_t<FP8>* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ seq_lens, float* __restrict__ ml, half_t* __restrict__ zpart,
+    int max_blocks, int num_blocks, int pages_per_split, int num_splits, int split_stride,
+    float v_scale) {
+  __shared__ SplitLds<H, RK, RV, NW> lds;
+  split_body<H, RK, RV, NW, DEPTH, NT, QG, FP8, false>(
+      lds, blockIdx.x, blockIdx.y, qt, k_cache, v_cache, block_tables, seq_lens, ml, zpart,
+      max_blocks, num_blocks, pages_per_split, num_splits, split_stride, v_scale, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -548,48 +615,85 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
 // the products avoid per-element conversions in their unrolled bodies.
 // ---------------------------------------------------------------------------
 template <int H, int D, int RV, int TB, int CB, int NT, int QG>
-__global__ __launch_bounds__(NT) void finish_kernel(const float* __restrict__ ml,
-                                                    const half_t* __restrict__ zpart,
-                                                    const int32_t* __restrict__ seq_lens,
-                                                    const half_t* __restrict__ W, int batch,
-                                                    int max_blocks, int pages_per_split,
-                                                    int num_splits, int split_stride,
-                                                    half_t* __restrict__ out) {
-  constexpr int R16 = ((H + 15) / 16) * 16;
-  constexpr int F4 = RV / 4;
-  constexpr int UG = TB * F4;                  // four-feature units of the work group
-  constexpr int SG = finish_split_groups(NT, TB, RV);  // split groups (1: one)
+struct FinishCfg {
+  static constexpr int R16 = ((H + 15) / 16) * 16;
+  static constexpr int F4 = RV / 4;
+  static constexpr int UG = TB * F4;                  // four-feature units of the work group
+  static constexpr int SG = finish_split_groups(NT, TB, RV);  // split groups (1: one)
+  static constexpr int LDZ = RV + 8;                  // halves per LDS row
+  // 256-thread tiles stage W_h in LDS by whole rows (each load instruction
+  // covers one contiguous 1 KiB row), which moves it faster than loading the
+  // product operands directly (16 rows x 64 bytes per instruction); the
+  // wider tiles have no LDS left for it.
+  static constexpr bool WL = NT == 256;
+};
+
+// LDS of one merge unit.
+template <int H, int D, int RV, int TB, int CB, int NT, int QG>
+struct FinishLds {
+  using F = FinishCfg<H, D, RV, TB, CB, NT, QG>;
+  // hi and lo parts of z by sequence; row TB stays zero
+  __attribute__((aligned(16))) half_t sZ[2][TB + 1][F::LDZ];
+  __attribute__((aligned(16))) half_t sW[F::WL ? D : 1][F::WL ? RV + 8 : 8];
+  // per split group: running max, sum and four weighted features of a unit
+  float sMerge[F::SG > 1 ? F::SG : 1][F::SG > 1 ? F::UG : 1][6];
+};
+
+// Bounded wait for *p >= target (device-coherent loads); after about a
+// second of polling it records the failure in *err and returns, so the
+// kernel always ends.
+constexpr int kSpinLimit = 1 << 20;
+__device__ __forceinline__ void wait_count(const uint32_t* p, uint32_t target, uint32_t* err) {
+  for (int it = 0; it < kSpinLimit; ++it) {
+    if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One merge unit (head h, sequence group g), placed by `unit` as the
+// launch's block index.  FUSED: the unit first waits until every non-empty
+// split of its sequences has signalled seq_done, then reads their partials
+// with device-coherent loads.
+template <int H, int D, int RV, int TB, int CB, int NT, int QG, bool FUSED>
+__device__ __forceinline__ void finish_body(FinishLds<H, D, RV, TB, CB, NT, QG>& lds,
+                                            const int unit, const float* __restrict__ ml,
+                                            const half_t* __restrict__ zpart,
+                                            const int32_t* __restrict__ seq_lens,
+                                            const half_t* __restrict__ W, int batch,
+                                            int max_blocks, int pages_per_split, int num_splits,
+                                            int split_stride, half_t* __restrict__ out,
+                                            const uint32_t* __restrict__ seq_done,
+                                            uint32_t* __restrict__ err) {
+  using F = FinishCfg<H, D, RV, TB, CB, NT, QG>;
+  constexpr int R16 = F::R16;
+  constexpr int F4 = F::F4;
+  constexpr int UG = F::UG;
+  constexpr int SG = F::SG;
   constexpr int NU = SG > 1 ? 1 : (UG + NT - 1) / NT;  // units per thread
   constexpr int NWV = NT / 64;
   constexpr int MW = NWV < D / 16 ? NWV : D / 16;  // waves on the products
   constexpr int RTW = D / (16 * MW);           // 16-row tiles of W_h per product wave
   constexpr int KS = RV / 32;                  // 32-feature steps
-  constexpr int LDZ = RV + 8;                  // halves per LDS row
   constexpr bool UNIFORM_SEQ = F4 % 64 == 0;   // a wave's units share one sequence
   static_assert(D % (16 * MW) == 0 && RV % 32 == 0 && TB >= 1 && TB <= 8, "finish tile shape");
   static_assert(SG == 1 || SG * UG <= NT, "split groups must fit the work group");
-  // hi and lo parts of z by sequence; row TB stays zero
-  __shared__ __attribute__((aligned(16))) half_t sZ[2][TB + 1][LDZ];
-  // 256-thread tiles stage W_h in LDS by whole rows (each load instruction
-  // covers one contiguous 1 KiB row), which moves it faster than loading the
-  // product operands directly (16 rows x 64 bytes per instruction); the
-  // 512-thread tiles have no LDS left for it.
-  constexpr bool WL = NT == 256;
+  constexpr bool WL = F::WL;
   constexpr int WCH = WL ? D * RV / 8 / NT : 1;  // 16-byte chunks per thread
-  __shared__ __attribute__((aligned(16))) half_t sW[WL ? D : 1][WL ? RV + 8 : 8];
+  auto& sZ = lds.sZ;
+  auto& sW = lds.sW;
+  auto& sMerge = lds.sMerge;
   half8 wst[WCH];
-  // per split group: running max, sum and four weighted features of a unit
-  __shared__ float sMerge[SG > 1 ? SG : 1][SG > 1 ? UG : 1][6];
 
   const int groups = (batch + TB - 1) / TB;
   int h, g;
   if constexpr (H % 8 == 0) {
-    const int x = blockIdx.x % 8, y = blockIdx.x / 8;
+    const int x = unit % 8, y = unit / 8;
     h = x + 8 * (y / groups);
     g = y % groups;
   } else {
-    h = blockIdx.x / groups;
-    g = blockIdx.x % groups;
+    h = unit / groups;
+    g = unit % groups;
   }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
@@ -619,6 +723,20 @@ __global__ __launch_bounds__(NT) void finish_kernel(const float* __restrict__ ml
     const half4 hz = {};
     *(half4*)&sZ[i / (RV / 4)][TB][(i % (RV / 4)) * 4] = hz;
   }
+  if constexpr (FUSED) {
+    // W_h in flight first; then every non-empty split of the group's
+    // sequences must have signalled before any partial is read
+    if (WL || w < MW) load_w();
+    if (tid == 0) {
+      for (int t = 0; t < TB; ++t) {
+        const int bb = g * TB + t;
+        if (bb >= batch) break;
+        const int np = min(min((seq_lens[bb] + BS - 1) / BS, max_blocks), num_splits * pages_per_split);
+        wait_count(seq_done + bb, (uint32_t)((np + pages_per_split - 1) / pages_per_split), err);
+      }
+    }
+    __syncthreads();
+  }
 
 #pragma unroll
   for (int j = 0; j < NU; ++j) {
@@ -638,13 +756,19 @@ __global__ __launch_bounds__(NT) void finish_kernel(const float* __restrict__ ml
     auto request = [&](int q0) {
 #pragma unroll
       for (int i = 0; i < CB; ++i) {
-        m[i] = mp[(q0 + i) * SG];
-        l[i] = mp[split_stride + (q0 + i) * SG];
-        a[i] = *(const half4*)(zp + (size_t)(q0 + i) * SG * RV);
+        if constexpr (FUSED) {
+          m[i] = ld_dev(mp + (q0 + i) * SG);
+          l[i] = ld_dev(mp + split_stride + (q0 + i) * SG);
+          a[i] = ld_dev(zp + (size_t)(q0 + i) * SG * RV);
+        } else {
+          m[i] = mp[(q0 + i) * SG];
+          l[i] = mp[split_stride + (q0 + i) * SG];
+          a[i] = *(const half4*)(zp + (size_t)(q0 + i) * SG * RV);
+        }
       }
     };
     if (merger) request(0);
-    if (j == 0 && (WL || w < MW)) load_w();
+    if (!FUSED && j == 0 && (WL || w < MW)) load_w();
     __builtin_amdgcn_sched_barrier(0);  // the sequence length is read after these requests
     const int n_pages =
         min(min((seq_lens[b] + BS - 1) / BS, max_blocks), num_splits * pages_per_split);
@@ -756,6 +880,58 @@ __global__ __launch_bounds__(NT) void finish_kernel(const float* __restrict__ ml
   }
 }
 
+template <int H, int D, int RV, int TB, int CB, int NT, int QG>
+__global__ __launch_bounds__(NT) void finish_kernel(const float* __restrict__ ml,
+                                                    const half_t* __restrict__ zpart,
+                                                    const int32_t* __restrict__ seq_lens,
+                                                    const half_t* __restrict__ W, int batch,
+                                                    int max_blocks, int pages_per_split,
+                                                    int num_splits, int split_stride,
+                                                    half_t* __restrict__ out) {
+  __shared__ FinishLds<H, D, RV, TB, CB, NT, QG> lds;
+  finish_body<H, D, RV, TB, CB, NT, QG, false>(lds, blockIdx.x, ml, zpart, seq_lens, W, batch,
+                                               max_blocks, pages_per_split, num_splits,
+                                               split_stride, out, nullptr, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// 3'. the split pass and the merge in one launch.  Work group w runs split
+// items w, w + G, ... (item = sequence * num_splits + split, as the split
+// kernel's grid), then merge units w, w + G, ... (unit as the merge kernel's
+// block index, so a head's units keep their XCD).  A merge unit waits for its
+// sequences' non-empty splits through seq_done (zeroed by the q projection
+// launch before this one).  Split items never wait, and the host caps G at
+// the number of work groups that can be resident at once, so every split
+// item is run by a work group that is or will be resident and every wait
+// ends; the wait is bounded all the same.
+// ---------------------------------------------------------------------------
+template <int H, int D, int RK, int RV, int NW, int DEPTH, int QG, bool FP8, int TB, int CB>
+__global__ __launch_bounds__(NW * 64) void decode_fused_kernel(
+    const float* __restrict__ qt, const latent_t<FP8>* __restrict__ k_cache,
+    const latent_t<FP8>* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ seq_lens, float* __restrict__ ml, half_t* __restrict__ zpart,
+    const half_t* __restrict__ W, half_t* __restrict__ out, uint32_t* __restrict__ sync,
+    int batch, int max_blocks, int num_blocks, int pages_per_split, int num_splits,
+    int split_stride, float v_scale, int n_items, int n_units) {
+  __shared__ SplitLds<H, RK, RV, NW> ls;
+  __shared__ FinishLds<H, D, RV, TB, CB, NW * 64, QG> lf;
+  uint32_t* seq_done = sync;
+  uint32_t* err = sync + batch;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    split_body<H, RK, RV, NW, DEPTH, false, QG, FP8, true>(
+        ls, item % num_splits, item / num_splits, qt, k_cache, v_cache, block_tables, seq_lens,
+        ml, zpart, max_blocks, num_blocks, pages_per_split, num_splits, split_stride, v_scale,
+        seq_done);
+    __syncthreads();
+  }
+  for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+    finish_body<H, D, RV, TB, CB, NW * 64, QG, true>(lf, unit, ml, zpart, seq_lens, W, batch,
+                                                     max_blocks, pages_per_split, num_splits,
+                                                     split_stride, out, seq_done, err);
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 4. up-projection of many tokens (prefill), out[n, h, :] = W_h z[n, h, :]:
 // grid (H, ceil(N / (32*NW))).  W_h (D x RV
@@ -857,12 +1033,60 @@ hipError_t launch_upproj_tiled(const ShapeKey& s, const void* W, const void* z_t
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
+// Compute units the stream's kernels may use: those set in its CU mask (the
+// device's count when the mask cannot be read).
+static int stream_cus(hipStream_t st) {
+  uint32_t mask[16] = {};
+  if (hipExtStreamGetCUMask(st, 16, mask) == hipSuccess) {
+    int n = 0;
+    for (uint32_t m : mask) n += __builtin_popcount(m);
+    if (n > 0) return n;
+  }
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+    return n;
+  return 0;
+}
+
 template <int H, int D, int RK, int RV, int NW, int DEPTH, bool NT, int QG = 1, bool FP8 = false>
 static hipError_t decode_instance(const DecodePlan& p, const void* qt, const void* k_cache,
                                   const void* v_cache, const void* W, const int32_t* block_tables,
                                   int max_blocks, const int32_t* seq_lens, int num_blocks,
                                   int batch, float* ml, void* zpart, void* out, float v_scale,
-                                  hipStream_t st) {
+                                  uint32_t* sync, hipStream_t st) {
+  if (p.fused) {
+    // the split pass and the merge in one launch, grid capped at the work
+    // groups that can be resident at once
+    const int n_items = batch * p.num_splits;
+    const int n_units = H * ((batch + p.finish_tb - 1) / p.finish_tb);
+    const int want = n_items > n_units ? n_items : n_units;
+#define STARKV_FUSED(TB_)                                                                          \
+  {                                                                                                \
+    auto kern = decode_fused_kernel<H, D, RK, RV, NW, DEPTH, QG, FP8, TB_, 4>;                     \
+    static const int occ = [&] {                                                                   \
+      int n = 0;                                                                                   \
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, NW * 64, 0) == hipSuccess ? n  \
+                                                                                              : 0; \
+    }();                                                                                           \
+    const int slots = occ * stream_cus(st);                                                        \
+    if (slots <= 0) return hipErrorInvalidConfiguration;                                           \
+    launch_hooked(TIME_DECODE_SPLIT, TIME_NONE, kern, dim3(want < slots ? want : slots),           \
+                  dim3(NW * 64), st, (const float*)qt, (const latent_t<FP8>*)k_cache,              \
+                  (const latent_t<FP8>*)v_cache, block_tables, seq_lens, ml, (half_t*)zpart,       \
+                  (const half_t*)W, (half_t*)out, sync, batch, max_blocks, num_blocks,             \
+                  p.pages_per_split, p.num_splits, p.split_stride, v_scale, n_items, n_units);     \
+  }
+    switch (p.finish_tb) {
+      case 1: STARKV_FUSED(1) break;
+      case 2: STARKV_FUSED(2) break;
+      case 4: STARKV_FUSED(4) break;
+      case 8: STARKV_FUSED(8) break;
+      default: return hipErrorInvalidValue;
+    }
+#undef STARKV_FUSED
+    return hipGetLastError();
+  }
   launch_hooked(TIME_DECODE_SPLIT, TIME_NONE,
                 decode_split_kernel<H, RK, RV, NW, DEPTH, NT, QG, FP8>,
                 dim3(p.num_splits, batch), dim3(NW * 64), st, (const float*)qt,
@@ -900,7 +1124,8 @@ constexpr int kPrefetchPart = 64 * 1024;
 
 template <int H, int D, int RK, int QG>
 static hipError_t qproj_instance(const void* q, const void* U, int n, float scale, void* qt,
-                                 int precedes, const void* wpf, int rv, hipStream_t st) {
+                                 int precedes, const void* wpf, int rv, uint32_t* zero,
+                                 int n_zero, hipStream_t st) {
   const int head_bytes = D * rv * (int)sizeof(half_t);
   const bool pf = wpf != nullptr && H % 8 == 0 && head_bytes % kPrefetchPart == 0;
   const int pf_rows = pf ? head_bytes / kPrefetchPart : 0;
@@ -908,40 +1133,48 @@ static hipError_t qproj_instance(const void* q, const void* U, int n, float scal
     const int rows = (n + 255) / 256;
     launch_hooked(TIME_NONE, precedes, qproj_kernel<H, D, RK, 4, QG>, dim3(H, rows + pf_rows),
                   dim3(256), st, (const half_t*)q, (const half_t*)U, n, scale * kLog2e,
-                  (float*)qt, rows, (const char*)wpf, head_bytes, kPrefetchPart, (uint32_t*)nullptr);
+                  (float*)qt, rows, (const char*)wpf, head_bytes, kPrefetchPart, (uint32_t*)nullptr,
+                  zero, n_zero);
   } else {
     const int rows = (n + 63) / 64;
     launch_hooked(TIME_NONE, precedes, qproj_kernel<H, D, RK, 1, QG>, dim3(H, rows + pf_rows),
                   dim3(256), st, (const half_t*)q, (const half_t*)U, n, scale * kLog2e,
-                  (float*)qt, rows, (const char*)wpf, head_bytes, kPrefetchPart, (uint32_t*)nullptr);
+                  (float*)qt, rows, (const char*)wpf, head_bytes, kPrefetchPart, (uint32_t*)nullptr,
+                  zero, n_zero);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_qproj(const ShapeKey& s, const void* q, const void* U, int n_tokens, float scale,
-                        void* qt, int precedes, hipStream_t st, const void* w_prefetch) {
+                        void* qt, int precedes, hipStream_t st, const void* w_prefetch,
+                        uint32_t* zero, int n_zero) {
   if (n_tokens <= 0) return hipSuccess;
+#define STARKV_QPROJ(H_, D_, RK_, QG_) \
+  return qproj_instance<H_, D_, RK_, QG_>(q, U, n_tokens, scale, qt, precedes, w_prefetch, s.rv, \
+                                          zero, n_zero, st)
   if (s.H == 32 && s.d == 128 && s.rk == 64) {
-    if (s.Hkv == 32) return qproj_instance<32, 128, 64, 1>(q, U, n_tokens, scale, qt, precedes, w_prefetch, s.rv, st);
-    if (s.Hkv == 8) return qproj_instance<32, 128, 64, 4>(q, U, n_tokens, scale, qt, precedes, w_prefetch, s.rv, st);
+    if (s.Hkv == 32) STARKV_QPROJ(32, 128, 64, 1);
+    if (s.Hkv == 8) STARKV_QPROJ(32, 128, 64, 4);
   }
-  if (s.H == 32 && s.d == 128 && s.rk == 32 && s.Hkv == 32)
-    return qproj_instance<32, 128, 32, 1>(q, U, n_tokens, scale, qt, precedes, w_prefetch, s.rv, st);
+  if (s.H == 32 && s.d == 128 && s.rk == 32 && s.Hkv == 32) STARKV_QPROJ(32, 128, 32, 1);
   if (s.H == 4 && s.d == 64 && s.rk == 16) {
-    if (s.Hkv == 4) return qproj_instance<4, 64, 16, 1>(q, U, n_tokens, scale, qt, precedes, w_prefetch, s.rv, st);
-    if (s.Hkv == 2) return qproj_instance<4, 64, 16, 2>(q, U, n_tokens, scale, qt, precedes, w_prefetch, s.rv, st);
+    if (s.Hkv == 4) STARKV_QPROJ(4, 64, 16, 1);
+    if (s.Hkv == 2) STARKV_QPROJ(4, 64, 16, 2);
   }
+#undef STARKV_QPROJ
   return hipErrorInvalidValue;
 }
+
+int decode_threads(const ShapeKey& s) { return s.H == 4 ? 4 * 64 : 16 * 64; }
 
 hipError_t launch_decode(const ShapeKey& s, const DecodePlan& p, const void* qt, const void* k_cache,
                          const void* v_cache, const void* W, const int32_t* block_tables,
                          int max_blocks, const int32_t* seq_lens, int num_blocks, int batch,
                          float* ml, void* zpart, void* out, const LatentFormat& fmt,
-                         hipStream_t st) {
+                         uint32_t* sync, hipStream_t st) {
 #define STARKV_DECODE_ARGS                                                                    \
   p, qt, k_cache, v_cache, W, block_tables, max_blocks, seq_lens, num_blocks, batch, ml, zpart, \
-      out, fmt.fp8 ? fmt.v_scale : 1.f, st
+      out, fmt.fp8 ? fmt.v_scale : 1.f, sync, st
   if (fmt.fp8) {  // FP8 latents: the main shape (either head layout) and the tiny one
     if (s.H == 32 && s.Hkv == 32 && s.d == 128 && s.rk == 64 && s.rv == 512)
       return decode_instance<32, 128, 64, 512, 16, 2, false, 1, true>(STARKV_DECODE_ARGS);

@@ -27,6 +27,8 @@ struct DecodePlan {
   int split_stride;  // split slots per sequence and head in the workspace: num_splits
                      // rounded up to a multiple of finish_cb times the split groups
   bool generic = false;  // the generic kernels (generic.hip), which use the first two fields
+  bool fused = false;    // the split pass and the merge in one launch (finish_cb is then 4
+                         // and finish_nt the split kernel's thread count)
 };
 
 // Split groups of the merge: when a work group has more threads than
@@ -38,8 +40,11 @@ constexpr int finish_split_groups(int nt, int tb, int rv) {
 
 // Byte offsets of the decode workspace regions.
 struct DecodeWorkspace {
-  size_t qt_off, ml_off, zp_off, total;
+  size_t qt_off, ml_off, zp_off, sync_off, total;
 };
+
+// Threads per work group of the tuned decode split kernel of a shape.
+int decode_threads(const ShapeKey& s);
 
 struct PrefillWorkspace {
   size_t qt_off, z_off, total;
@@ -65,8 +70,11 @@ struct LatentFormat {
 bool shape_supported(const ShapeKey& s);
 // force_pps > 0 fixes the pages per split, force_tb in {1, 2, 4, 8} the
 // sequences per merge work group; 0 leaves either to the planner
+// launches: 2 fuses the split pass and the merge into one kernel; anything
+// else (the library's choice) keeps them in launches of their own
 DecodePlan plan_decode(const ShapeKey& s, int batch, int max_seq_len, int block_size,
-                       int force_pps = 0, int force_tb = 0, bool generic = false);
+                       int force_pps = 0, int force_tb = 0, bool generic = false,
+                       int launches = 0);
 DecodeWorkspace decode_workspace_layout(const ShapeKey& s, int batch, const DecodePlan& p);
 PrefillWorkspace prefill_workspace_layout(const ShapeKey& s, int total_q);
 
@@ -134,15 +142,18 @@ hipError_t launch_generic_attn(const ShapeKey& s, const void* qt, const int32_t*
 // `precedes`: the hooked kernel that follows this launch in the call.
 // w_prefetch: the W that the step's merge will read (decode), fetched into
 // the L2 of the XCD that will use each head's block; null for none
+// zero / n_zero: words that the launch clears (the fused decode step's
+// counters), or none
 hipError_t launch_qproj(const ShapeKey& s, const void* q, const void* U, int n_tokens,
                         float scale, void* qt, int precedes, hipStream_t st,
-                        const void* w_prefetch = nullptr);
+                        const void* w_prefetch = nullptr, uint32_t* zero = nullptr,
+                        int n_zero = 0);
 
 hipError_t launch_decode(const ShapeKey& s, const DecodePlan& p, const void* qt,
                          const void* k_cache, const void* v_cache, const void* W,
                          const int32_t* block_tables, int max_blocks, const int32_t* seq_lens,
                          int num_blocks, int batch, float* ml, void* zpart, void* out,
-                         const LatentFormat& fmt, hipStream_t st);
+                         const LatentFormat& fmt, uint32_t* sync, hipStream_t st);
 
 // out[n, h, :] = W_h z[n, h, :] for the many tokens of a prefill call: z is
 // fp16, tiled in the A-operand order of the up-projection's 32x32x16

@@ -49,7 +49,8 @@ class Dims(ctypes.Structure):
 
 
 class DecodeConfig(ctypes.Structure):
-    _fields_ = [("pages_per_split", ctypes.c_int32), ("merge_seqs", ctypes.c_int32)]
+    _fields_ = [("pages_per_split", ctypes.c_int32), ("merge_seqs", ctypes.c_int32),
+                ("launches", ctypes.c_int32)]
 
 
 class StarKVError(RuntimeError):
@@ -178,16 +179,16 @@ def _stream(stream):
     return _vp(s.cuda_stream)
 
 
-def _config(pages_per_split, merge_seqs):
+def _config(pages_per_split, merge_seqs, launches=0):
     """Plan override, or None for the library's plan."""
-    if not pages_per_split and not merge_seqs:
+    if not pages_per_split and not merge_seqs and not launches:
         return None
-    return DecodeConfig(int(pages_per_split or 0), int(merge_seqs or 0))
+    return DecodeConfig(int(pages_per_split or 0), int(merge_seqs or 0), int(launches or 0))
 
 
-def decode_workspace_size(dims, batch, max_seq_len, pages_per_split=0, merge_seqs=0):
+def decode_workspace_size(dims, batch, max_seq_len, pages_per_split=0, merge_seqs=0, launches=0):
     out = _sz(0)
-    cfg = _config(pages_per_split, merge_seqs)
+    cfg = _config(pages_per_split, merge_seqs, launches)
     if cfg is None:
         _check(_lib.starkv_decode_workspace_size(ctypes.byref(dims), int(batch), int(max_seq_len),
                                                  ctypes.byref(out)), "starkv_decode_workspace_size")
@@ -293,9 +294,12 @@ def decode_attn_fp8(q, k_cache8, v_cache8, U, W, block_tables, seq_lens, max_seq
 
 
 def decode_attn(q, k_cache, v_cache, U, W, block_tables, seq_lens, max_seq_len, scale=None,
-                out=None, workspace=None, stream=None, pages_per_split=0, merge_seqs=0):
+                out=None, workspace=None, stream=None, pages_per_split=0, merge_seqs=0,
+                launches=0):
     """Decode attention for q [B, H, d]; returns out [B, H, d] fp16.
-    pages_per_split / merge_seqs: a plan override (0 = the library's plan)."""
+    pages_per_split / merge_seqs / launches: a plan override (0 = the
+    library's plan; launches 2 fuses the split pass and the merge, 3 keeps
+    three kernels)."""
     dims = dims_of(k_cache, v_cache, U, W, num_heads=q.shape[1])
     B = q.shape[0]
     H, d = dims.num_heads, dims.head_dim
@@ -303,7 +307,7 @@ def decode_attn(q, k_cache, v_cache, U, W, block_tables, seq_lens, max_seq_len, 
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, H, d), dtype=torch.float16, device=q.device)
-    need = decode_workspace_size(dims, B, max_seq_len, pages_per_split, merge_seqs)
+    need = decode_workspace_size(dims, B, max_seq_len, pages_per_split, merge_seqs, launches)
     if workspace is None:
         workspace = alloc_workspace(need, q.device)
     args = [ctypes.byref(dims), _dev(q, torch.float16, "q", (B, H, d)),
@@ -313,7 +317,7 @@ def decode_attn(q, k_cache, v_cache, U, W, block_tables, seq_lens, max_seq_len, 
             _dev(seq_lens, torch.int32, "seq_lens", (B,)), int(B), int(max_seq_len), float(scale)]
     tail = [_dev(out, torch.float16, "out", (B, H, d)), _dev(workspace, torch.uint8, "workspace"),
             int(workspace.numel()), _stream(stream)]
-    cfg = _config(pages_per_split, merge_seqs)
+    cfg = _config(pages_per_split, merge_seqs, launches)
     if cfg is None:
         _check(_lib.starkv_decode_attn(*args, *tail), "starkv_decode_attn")
     else:

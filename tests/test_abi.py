@@ -207,7 +207,12 @@ def test_decode_config_validation():
     assert size(sk.DecodeConfig(0, 3))[0] == 7
     for m in (1, 2, 4, 8):
         assert size(sk.DecodeConfig(0, m))[0] == 0
+    assert size(sk.DecodeConfig(0, 0, 1))[0] == 7         # launches: 0, 2 or 3
+    assert size(sk.DecodeConfig(0, 0, 3)) == (0, dflt)    # the default: three launches
+    st, two = size(sk.DecodeConfig(0, 0, 2))
+    assert st == 0 and two > dflt                         # the fused step's counters
     assert call(sk.DecodeConfig(0, 5), one) == 7
+    assert call(sk.DecodeConfig(0, 0, 4), one) == 7
     assert call(sk.DecodeConfig(1, 0), one - 1) == 4      # sized for the default plan: too small
     assert call(None, dflt - 1) == 4
 

@@ -83,20 +83,23 @@ def _run_planned(sk, case, **plan):
     return out
 
 
+@pytest.mark.parametrize("launches", [2, 3])
 @pytest.mark.parametrize("pps", [1, 3, 64, 256])
-def test_split_plan_invariance(sk, pps):
+def test_split_plan_invariance(sk, pps, launches):
     """Any split plan (here fixed through the plan-override entry point) gives
-    the same attention within the parity bars."""
+    the same attention within the parity bars, with the split pass and the
+    merge fused into one kernel (2 launches) or as separate kernels (3)."""
     case = wl.make_decode_case(wl.MAIN, seq_lens=[1500, 700, 33], seed=25)
     ref = _oracle(case)
-    note(f"decode split plan pages_per_split={pps}")
-    out = _run_planned(sk, case, pages_per_split=pps)
-    assert_parity(out, ref, f"plan pps={pps}")
+    note(f"decode split plan pages_per_split={pps} launches={launches}")
+    out = _run_planned(sk, case, pages_per_split=pps, launches=launches)
+    assert_parity(out, ref, f"plan pps={pps} launches={launches}")
 
 
+@pytest.mark.parametrize("launches", [2, 3])
 @pytest.mark.parametrize("tb", [1, 2, 4, 8])
 @pytest.mark.parametrize("shape", ["main", "tiny"])
-def test_finish_tiles(sk, tb, shape):
+def test_finish_tiles(sk, tb, shape, launches):
     """The merge of the splits and the up-projection with 1, 2, 4 or 8
     sequences per work group (and so split groups, 16, 8 or 4 splits per
     request round, several rounds where the plan has more splits), on a batch
@@ -105,9 +108,9 @@ def test_finish_tiles(sk, tb, shape):
     cfg = wl.MAIN if shape == "main" else wl.TINY
     case = wl.make_decode_case(cfg, seq_lens=[1500, 0, 33, 700, 5], seed=27)
     ref = _oracle(case)
-    note(f"decode finish tile tb={tb} shape={shape}")
-    out = _run_planned(sk, case, merge_seqs=tb)
-    assert_parity(out, ref, f"finish tb={tb} {shape}")
+    note(f"decode finish tile tb={tb} shape={shape} launches={launches}")
+    out = _run_planned(sk, case, merge_seqs=tb, launches=launches)
+    assert_parity(out, ref, f"finish tb={tb} {shape} launches={launches}")
     assert torch.count_nonzero(out[1]).item() == 0
 
 
@@ -144,3 +147,46 @@ def test_full_size_config_sampled(sk, name, rows):
     sel = list(range(case.B)) if rows is None else rows
     assert torch.isfinite(out.float()).all()
     assert_parity(out[sel], ref[sel], f"{name} rows={rows}")
+
+
+@pytest.mark.parametrize("name,rows", [("decode_b16", None), ("tiny", None),
+                                       ("decode_b64", [0, 31, 63]), ("long_b20", [7])])
+def test_fused_path_full_size(sk, name, rows):
+    """The fused split + merge kernel on full workloads (its grid capped at
+    the resident work groups), all or sampled rows."""
+    case = wl.make_config(name)
+    t = decode_tensors(case)
+    msl = int(case.cache.seq_lens.max())
+    note(f"decode fused step {name}")
+    out = sk.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["U"], t["W"], t["block_tables"],
+                         t["seq_lens"], msl, case.scale, launches=2)
+    torch.cuda.synchronize()
+    sel = list(range(case.B)) if rows is None else rows
+    assert_parity(out[sel], _oracle(case, rows)[sel], f"fused {name}")
+
+
+def test_fused_step_repeats_and_resets(sk):
+    """The fused step's counters are cleared by each call's q projection: many
+    calls in a row on one workspace, with batches of different sizes, stay
+    bit-identical to the first call of each batch."""
+    a = wl.make_decode_case(wl.MAIN, seq_lens=[900, 33, 2048, 5], seed=29)
+    b = wl.make_decode_case(wl.MAIN, seq_lens=[4000], seed=30)
+    ta, tb_ = decode_tensors(a), decode_tensors(b)
+    dims = sk.dims_of(ta["k_cache"], ta["v_cache"], ta["U"], ta["W"])
+    need = max(sk.decode_workspace_size(dims, 4, 2048, launches=2),
+               sk.decode_workspace_size(dims, 1, 4000, launches=2))
+    ws = torch.full((need,), 0xAB, dtype=torch.uint8, device="cuda")   # garbage to start
+    note("decode fused step repeated with one workspace")
+    outs_a, outs_b = [], []
+    for i in range(6):
+        for case, t, outs in ((a, ta, outs_a), (b, tb_, outs_b)):
+            o = sk.decode_attn(t["q"], t["k_cache"], t["v_cache"], t["U"], t["W"],
+                               t["block_tables"], t["seq_lens"], int(case.cache.seq_lens.max()),
+                               case.scale, workspace=ws, launches=2)
+            outs.append(o.clone())
+    torch.cuda.synchronize()
+    for outs in (outs_a, outs_b):
+        for o in outs[1:]:
+            assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    assert_parity(outs_a[0], _oracle(a), "fused repeat a")
+    assert_parity(outs_b[0], _oracle(b), "fused repeat b")
