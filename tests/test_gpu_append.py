@@ -49,11 +49,14 @@ def _run(sk, U, W, k, v, slots, kc, vc):
 
 # The GPU accumulates the projections in fp32 on the matrix cores, so a value
 # may round to the other fp16 neighbour of the exact result (1 ulp), and
-# values near zero carry the fp32 summation error in absolute terms: about
-# sqrt(K) * 2^-24 per unit of partial-sum size for K products, K = d = 128
-# for keys and K = H*d = 4096 for values; 8x that is the allowance below.
-ATOL_K = 8 * np.sqrt(128) * 2.0**-24
-ATOL_V = 8 * np.sqrt(4096) * 2.0**-24
+# values near zero (where an fp16 ulp is tiny) carry the fp32 summation error
+# in absolute terms.  Measured over every append case here and in the
+# grouped-query, rank-profile and generic tests (K = d for keys, Hkv*d up to
+# 4096 for values): at most 2.4e-7 for keys and 2.4e-6 for values (the
+# 2000-token split-contraction case) among latents more than one ulp off.
+# The allowances are twice those, under the 1e-5 the design set.
+ATOL_K = 5e-7
+ATOL_V = 5e-6
 
 
 def _within(g, r, atol):
@@ -72,7 +75,8 @@ def _check(gk, gv, rk, rv, what):
     okv, uv, av = _within(gv[mv], rv[mv], ATOL_V)
     print(f"[parity] {what}: k max ulp {uk.max(initial=0)} max abs {ak.max(initial=0):.2e}; "
           f"v max ulp {uv.max(initial=0)} max abs {av.max(initial=0):.2e}; "
-          f"v >1ulp {(uv > 1).sum()} of {uv.size}", flush=True)
+          f"v >1ulp {(uv > 1).sum()} of {uv.size}; beyond 1 ulp: k max abs "
+          f"{ak[uk > 1].max(initial=0):.3e} v max abs {av[uv > 1].max(initial=0):.3e}", flush=True)
     assert okk.all() and okv.all()
 
 

@@ -135,8 +135,10 @@ def test_max_seq_len_bound_larger_than_lengths(sk):
     assert_parity(o2, ref, "loose bound")
 
 
-@pytest.mark.parametrize("name,rows", [("decode_b16", None), ("decode_b64", [0, 17, 63]),
-                                       ("long_b20", [0, 19])])
+@pytest.mark.parametrize("name,rows", [("decode_b16", None),
+                                       ("decode_b64", [0, 3, 9, 17, 22, 28, 31, 35, 40, 44, 47,
+                                                       51, 55, 58, 61, 63]),
+                                       ("long_b20", [0, 2, 5, 8, 11, 14, 17, 19])])
 def test_full_size_config_sampled(sk, name, rows):
     """Full-size workload in the benchmark's launch configuration; the oracle
     checks all sequences (b16) or a fixed sample of them."""

@@ -286,7 +286,8 @@ def test_generic_append(sk, name, n):
         m = ~np.isnan(r)
         u = _ulp_diff(g[m], r[m])
         a = np.abs(g[m].astype(np.float64) - r[m].astype(np.float64))
-        atol = 8 * np.sqrt(K) * 2.0**-24
+        atol = 5e-7 if what == "k" else 5e-6   # as the tuned append's allowances
         print(f"[parity] generic append {name} n={n} {what}: max ulp {u.max(initial=0)} "
-              f"max abs {a.max(initial=0):.2e}", flush=True)
+              f"max abs {a.max(initial=0):.2e}; beyond 1 ulp: max abs "
+              f"{a[u > 1].max(initial=0):.3e} (K {K})", flush=True)
         assert ((u <= 1) | (a <= atol)).all()

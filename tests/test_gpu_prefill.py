@@ -82,7 +82,7 @@ def test_prefill_full_size_sampled(sk):
     case = wl.make_config("prefill_b16")
     note("prefill full config prefill_b16")
     out, kc, vc = _gpu_prefill(sk, case)
-    rows = [0, 9, 15]
+    rows = [0, 2, 5, 7, 9, 11, 13, 15]
     ref = _oracle(case, kc, vc, rows=rows)
     sel = np.concatenate([np.arange(case.query_start_loc[r], case.query_start_loc[r + 1])
                           for r in rows])
