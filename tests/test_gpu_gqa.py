@@ -171,12 +171,12 @@ def test_append_gqa(sk, shape, n, seed):
     rk, rv = oracle.append(k, v, U, W, slots, kc, vc)
     assert np.array_equal(np.isnan(gk), np.isnan(rk))
     assert np.array_equal(np.isnan(gv), np.isnan(rv))
-    atol_k = 8 * np.sqrt(shape.d) * 2.0**-24
-    atol_v = 8 * np.sqrt(shape.kv * shape.d) * 2.0**-24
-    for g, r, atol, what in ((gk, rk, atol_k, "k"), (gv, rv, atol_v, "v")):
+    # the tuned append's allowances (twice the measured fp32 summation error)
+    for g, r, atol, what in ((gk, rk, 5e-7, "k"), (gv, rv, 5e-6, "v")):
         m = ~np.isnan(r)
         u = _ulp_diff(g[m], r[m])
         a = np.abs(g[m].astype(np.float64) - r[m].astype(np.float64))
         print(f"[parity] gqa append {what}: max ulp {u.max(initial=0)} max abs "
-              f"{a.max(initial=0):.2e}", flush=True)
+              f"{a.max(initial=0):.2e}; beyond 1 ulp: max abs {a[u > 1].max(initial=0):.3e}",
+              flush=True)
         assert ((u <= 1) | (a <= atol)).all()

@@ -110,11 +110,12 @@ def test_append_lowrank(sk, n, seed):
     rk, rv = oracle.append(k, v, U, W, slots, kc, vc)
     assert np.array_equal(np.isnan(gk), np.isnan(rk))
     assert np.array_equal(np.isnan(gv), np.isnan(rv))
-    for g, r, atol, what in ((gk, rk, 8 * np.sqrt(shape.d) * 2.0**-24, "k"),
-                             (gv, rv, 8 * np.sqrt(shape.kv * shape.d) * 2.0**-24, "v")):
+    # the tuned append's allowances (twice the measured fp32 summation error)
+    for g, r, atol, what in ((gk, rk, 5e-7, "k"), (gv, rv, 5e-6, "v")):
         m = ~np.isnan(r)
         u = _ulp_diff(g[m], r[m])
         a = np.abs(g[m].astype(np.float64) - r[m].astype(np.float64))
         print(f"[parity] lowrank append {what}: max ulp {u.max(initial=0)} max abs "
-              f"{a.max(initial=0):.2e}", flush=True)
+              f"{a.max(initial=0):.2e}; beyond 1 ulp: max abs {a[u > 1].max(initial=0):.3e}",
+              flush=True)
         assert ((u <= 1) | (a <= atol)).all()
