@@ -28,6 +28,9 @@ Other modes:
     --profile-run             a few steps plus a 256 MiB copy, for rocprofv3
     --summarize-pmc F W OUT   turn FETCH_SIZE / WRITE_SIZE counter CSVs into
                               the traffic summary the benchmark reads back
+    --plan-sweep              decode step and split kernel at forced split
+                              plans (pages per split) beside the planner's own,
+                              one JSON line per plan
 """
 from __future__ import annotations
 
@@ -117,6 +120,12 @@ def parse_args(argv=None):
     ap.add_argument("--profile-fit", action="store_true",
                     help="a few bases fits (fit_n16384, 8 iterations), for rocprofv3")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"))
+    ap.add_argument("--plan-sweep", action="store_true",
+                    help="decode steps at forced pages_per_split values (JSON line per plan)")
+    ap.add_argument("--sweep-workloads", default="decode_b16,decode_b64,long_b20",
+                    help="workloads of --plan-sweep")
+    ap.add_argument("--sweep-pps", default="4,6,8,9,12,16,32,64,128",
+                    help="pages_per_split values of --plan-sweep (0 = the planner's)")
     return ap.parse_args(argv)
 
 
@@ -763,6 +772,56 @@ def profile_run(args):
           flush=True)
 
 
+def plan_sweep(args):
+    """Decode steps and the split-K kernel (flushed, as in the benchmark) at
+    the planner's split plan and at forced pages_per_split values: the
+    evidence for the planner's choice, one JSON line per (workload, plan)."""
+    import numpy as np
+    import torch
+    from rank_compressed_paged_amd import metrics
+    from rank_compressed_paged_amd import starkv as sk
+    from rank_compressed_paged_amd import workloads as wl
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    fl = lambda i: torch.sum(flush, dim=0, out=sink)
+    HEAD_START["fn"] = lambda n: [torch.sum(flush, dim=0, out=sink) for _ in range(2 * n)]
+    for name in args.sweep_workloads.split(","):
+        case = wl.make_config(name)
+        sh, c = case.shape, case.cache
+        dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        q, kc, vc, U, W = dev(case.q), dev(c.k_cache), dev(c.v_cache), dev(case.U), dev(case.W)
+        bt, sl = dev(c.block_tables), dev(c.seq_lens)
+        B, msl = case.B, int(c.seq_lens.max())
+        dims = sk.dims_of(kc, vc, U, W, num_heads=sh.H)
+        lat = metrics.decode_latent_bytes(c.seq_lens, sh.kv, sh.r_k, sh.r_v)
+        out = torch.empty((B, sh.H, sh.d), dtype=torch.float16, device="cuda")
+        pages = (msl + sh.bs - 1) // sh.bs
+        for pps in [0] + [int(x) for x in args.sweep_pps.split(",")]:
+            if pps > pages:
+                continue
+            ws = sk.alloc_workspace(sk.decode_workspace_size(dims, B, msl, pages_per_split=pps),
+                                    "cuda")
+
+            def step():
+                sk.decode_attn(q, kc, vc, U, W, bt, sl, msl, case.scale, out=out, workspace=ws,
+                               pages_per_split=pps)
+            for i in range(5):
+                fl(i)
+                step()
+            torch.cuda.synchronize()
+            s_ms, _, _ = timed(step, args.steps, fl)
+            _, k_ms, _ = timed(step, args.steps, fl, sk.TIME_DECODE_SPLIT)
+            sm, km = statistics.fmean(s_ms), statistics.fmean(k_ms)
+            plan = sk.decode_plan(dims, B, msl) if pps == 0 else (pps, (pages + pps - 1) // pps)
+            print(json.dumps({"workload": name, "pages_per_split": plan[0], "num_splits": plan[1],
+                              "planner": pps == 0, "work_groups": B * plan[1],
+                              "step_us": round(sm * 1e3, 2), "split_kernel_us": round(km * 1e3, 2),
+                              "split_kernel_hbm_frac": round(lat / (km * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "step_hbm_frac": round(lat / (sm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}),
+                  flush=True)
+            del ws
+
+
 def _pmc_rows(path):
     with open(path) as f:
         return list(csv.DictReader(f))
@@ -835,6 +894,9 @@ def main():
         return 0
     if args.profile_fit:
         profile_fit(args)
+        return 0
+    if args.plan_sweep:
+        plan_sweep(args)
         return 0
     run_bench(args)
     return 0
