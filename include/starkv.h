@@ -42,6 +42,13 @@
  *     memory, including workspaces; the library allocates nothing and keeps
  *     no per-call state.  `stream` is a hipStream_t (NULL = default stream).
  *     Calls are asynchronous on `stream`; nothing synchronises the host.
+ *   - Workspaces (decode, prefill, append).  Their first 256 bytes are
+ *     reserved: the few-token append keeps arrival counters there.  They
+ *     must be zero when a workspace is first used (allocate it zero-filled
+ *     or clear it once); every call leaves them zero and no call writes
+ *     anything else there, so one buffer may serve all three kinds of call.
+ *     The rest of a workspace needs no initialisation.  Calls that overlap in
+ *     time must not share a workspace.
  *   - Arguments are validated on the host BEFORE any HIP call: on failure the
  *     call returns a non-zero status and enqueues nothing.  Device pointers
  *     must be 16-byte aligned.  A launch failure maps to STARKV_ERR_LAUNCH.
@@ -70,7 +77,7 @@
 extern "C" {
 #endif
 
-#define STARKV_ABI_VERSION 6
+#define STARKV_ABI_VERSION 7
 
 typedef enum {
   STARKV_OK = 0,
@@ -107,13 +114,17 @@ int32_t starkv_shape_supported(const starkv_dims* dims);
 
 /*
  * Workspace bytes (host out-parameter *bytes) that starkv_append and
- * starkv_append_fp8 need for num_tokens tokens, all of it fp32 partial
- * products of the value projection:
- *   num_tokens <= 64 (a decode step's tokens): over 64-row slices of W,
- *     (Hkv*d/64) * num_tokens * r_v * 4 bytes;
+ * starkv_append_fp8 need for num_tokens tokens: 0, or the reserved 256
+ * bytes (the arrival counters, see the workspace convention above) followed
+ * by fp32 partial products of the value projection:
+ *   num_tokens <= 64 (a decode step's tokens) at the tuned shapes: over
+ *     S slices of W's Hkv*d rows, S = Hkv*d / R with
+ *     R = max(64, Hkv*d * (r_v/32) / 256) rows per slice,
+ *     256 + S * num_tokens * r_v * 4 bytes (S = 16 at 32 key/value heads of
+ *     d 128 with r_v 512);
  *   65..1792 tokens at 32 key/value heads of d 128 with r_k 64 and r_v 512:
- *     over four equal parts of the contraction, 4 * num_tokens * r_v * 4
- *     bytes; 1793..2816 tokens there: two parts, 2 * num_tokens * r_v * 4;
+ *     over four equal parts of the contraction, 256 + 4 * num_tokens * r_v * 4
+ *     bytes; 1793..2816 tokens there: two parts, 256 + 2 * num_tokens * r_v * 4;
  *   other token counts and shapes: 0.
  * The size is not monotonic in num_tokens: a workspace reused for several
  * token counts takes the largest of their sizes.  Returns a status.
@@ -137,11 +148,15 @@ starkv_status starkv_append_workspace_size(const starkv_dims* dims, int32_t num_
  *   slot_mapping  [num_tokens] int64
  *   k_cache, v_cache  updated in place
  *   workspace     device scratch of at least starkv_append_workspace_size
- *                 bytes, 16-byte aligned, owned by the caller; may be NULL
+ *                 bytes, 16-byte aligned, owned by the caller, its first 256
+ *                 bytes zero (workspace convention above); may be NULL
  *                 (with workspace_bytes 0) when that size is 0.  A missing
  *                 or short workspace returns STARKV_ERR_NULL or
- *                 STARKV_ERR_WORKSPACE before anything is launched.  Calls
- *                 that overlap in time must not share a workspace.
+ *                 STARKV_ERR_WORKSPACE before anything is launched.
+ * Up to 64 tokens (tuned shapes) run as one launch: slices of the value
+ * projection write their partial products to the workspace and the last
+ * slice of each block of 32 outputs to finish sums them in slice order,
+ * rounds and writes the slots (nothing waits on another work group).
  */
 starkv_status starkv_append(const starkv_dims* dims, const void* k, const void* v, const void* U,
                             const void* W, const int64_t* slot_mapping, int32_t num_tokens,
@@ -188,7 +203,8 @@ starkv_status starkv_decode_workspace_size(const starkv_dims* dims, int32_t batc
  *   scale         (host) softmax scale, normally 1/sqrt(d); finite, > 0
  *   out           [batch][H][d] fp16
  *   workspace     >= starkv_decode_workspace_size(...) bytes, 256-byte aligned
- *                 preferred; contents need no initialisation
+ *                 preferred; its first 256 bytes zero (workspace convention
+ *                 above), the rest needs no initialisation
  * Three kernels run on `stream`: q projection, split-K latent attention,
  * and the merge of the splits fused with the W_h up-projection.
  */

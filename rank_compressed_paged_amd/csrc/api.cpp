@@ -181,7 +181,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 DecodeWorkspace decode_workspace_layout(const ShapeKey& s, int batch, const DecodePlan& p) {
   const size_t r16 = (size_t)((s.H + 15) / 16) * 16;
   DecodeWorkspace w;
-  size_t off = 0;
+  size_t off = kWorkspaceHeaderBytes;
   if (p.generic) {  // q~ fp32, fp32 statistics [B][H][2][S] and unnormalised z [B][H][S][r_v]
     w.qt_off = off;
     off = align256(off + (size_t)batch * s.H * s.rk * 4);
@@ -207,7 +207,7 @@ DecodeWorkspace decode_workspace_layout(const ShapeKey& s, int batch, const Deco
 
 PrefillWorkspace prefill_workspace_layout(const ShapeKey& s, int total_q) {
   PrefillWorkspace w;
-  size_t off = 0;
+  size_t off = kWorkspaceHeaderBytes;
   w.qt_off = off;
   off = align256(off + (size_t)total_q * s.H * s.rk * 4);  // q~, fp32
   w.z_off = off;  // fp16 z tiled by 32-token blocks, see launch_upproj_tiled

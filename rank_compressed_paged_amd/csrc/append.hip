@@ -6,14 +6,17 @@
 //   c_v[n, :]    = W^T vec(v[n])           (one [N x H*d] x [H*d x r_v] product)
 //
 // Both products are C = A B with A row-major (contraction contiguous) and B
-// row-major (outputs contiguous), so one tiled matrix-core kernel serves both.
-// A 256-thread work group computes a 64 (tokens) x 64 (outputs) tile with
-// v_mfma_f32_16x16x32_f16; A operands come straight from memory (8
-// contiguous fp16 per lane), B is staged through LDS transposed so that each
-// lane again reads 8 contiguous values.  The next K step's loads are issued
-// before the current step's LDS barrier (which waits on LDS only).  The epilogue rounds to fp16
-// (nearest even), or to FP8 E4M3 codes of latent / scale for FP8 caches, and
-// writes slot_mapping[n]; negative or out-of-range slots are skipped.
+// row-major (outputs contiguous).  Three forms, all on the matrix cores:
+//   * few tokens (a decode step): append_few_kernel, one launch of about 256
+//     work groups that split the value contraction and finish it with a
+//     last-arriver sum (below);
+//   * many tokens at the tuned shapes: append_tiled_kernel, 128 x 64 tiles
+//     with both operand tiles staged through LDS, optionally with the value
+//     contraction split over work groups and summed by append_reduce_kernel;
+//   * any other shape: append_kernel, 64 x 64 tiles, A straight from memory.
+// The epilogues round to fp16 (nearest even), or to FP8 E4M3 codes of
+// latent / scale for FP8 caches, and write slot_mapping[n]; negative or
+// out-of-range slots are skipped.
 // Layouts: k_cache [NB, H, 16, r_k], v_cache [NB, r_v, 16].
 
 #include <type_traits>
@@ -35,7 +38,8 @@ struct AppendArgs {
   int tiles_m, v_tiles_n, k_tiles_n;
   int fp8;               // store FP8 E4M3 codes of latent / scale
   float k_scale, v_scale;
-  float* part;           // few-token path: value partials [K / kSliceRows][N][RV] fp32
+  uint32_t* counters;    // few-token path: arrival counter per value column block
+  float* part;           // value partials [slice][N][RV] fp32 (few-token path, split tiled path)
 };
 
 // One latent of the epilogue: fp16 rounded to nearest even, or the E4M3
@@ -54,6 +58,11 @@ __device__ __forceinline__ void store_latent(const AppendArgs& a, bool is_v, siz
 
 constexpr int AT_M = 64, AT_N = 64, AT_K = 32, AT_LDS = AT_K + 8;
 
+// Generic form: a 256-thread work group computes a 64 (tokens) x 64 (outputs)
+// tile with v_mfma_f32_16x16x32_f16; A operands come straight from memory (8
+// contiguous fp16 per lane), B is staged through LDS transposed so that each
+// lane again reads 8 contiguous values.  The next K step's loads are issued
+// before the current step's LDS barrier.
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   __shared__ __attribute__((aligned(16))) half_t sB[2][AT_N][AT_LDS];
   const int tid = threadIdx.x;
@@ -173,21 +182,6 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 }
 
 
-// ---------------------------------------------------------------------------
-// Few tokens (a decode step's append): the work is reading the bases (W is
-// 4 MiB at the main shape), so it is spread over many work groups that each
-// read whole rows.  One work group per job:
-//   value slice j: rows kSliceRows*j .. of W (64 KiB at r_v 512), all r_v
-//     outputs: fp32 partial products of those rows go to the workspace, and
-//     append_reduce_kernel sums the slices, rounds and scatters;
-//   key job: one head, all r_k outputs over K = d, rounded and scattered
-//     here (the K range split over the waves, the partial tiles summed
-//     through LDS).
-// The job's rows of W (or U_h) are staged once in LDS as they are in
-// memory, [k][output], and the B operand of v_mfma_f32_16x16x32_f16 (8
-// consecutive k of one output per lane) comes through the transposing LDS
-// read; A is 8 consecutive features of one token straight from memory.
-// ---------------------------------------------------------------------------
 // ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane i
 // receives element i%4 of the 4-element (8-byte) chunk addressed by lane
 // 4e + i/4, for e = 0..3.  So if lane q of a group addresses row k0 + q/4,
@@ -201,170 +195,204 @@ __device__ __forceinline__ half4 lds_read_tr16(const half_t* p) {
   return __builtin_bit_cast(half4, r);
 }
 
-constexpr int kSmallN = 64;            // tokens handled by the few-token kernel
-constexpr int kSliceRows = 64;         // rows of W per value slice
-constexpr int kSmallWaves = 16;
+// ---------------------------------------------------------------------------
+// Few tokens (a decode step's append), one launch.  The work is reading the
+// bases (W is 4 MiB at the main shape), so it is spread over about 256 work
+// groups of four waves:
+//   value job (slice s, column block cb): rows R*s .. R*s+R-1 of W and its
+//     CB outputs cb*CB ..; the fp32 partial products of the slice's rows,
+//     [N][CB], go to the workspace with device-coherent stores, then the
+//     block's arrival counter is incremented.  The work group that arrives
+//     last sums the S slices' partials in slice order (so the result does
+//     not depend on arrival order), rounds, writes the tokens' slots and
+//     sets the counter back to zero: nothing waits, and every call leaves
+//     the counters zero;
+//   key job (head h): U_h staged in LDS, one 16-output tile of c_k per
+//     wave over the whole contraction d, rounded and written directly.
+// The B operand of v_mfma_f32_16x16x32_f16 (8 consecutive k of one output
+// per lane) comes from the basis staged [k][output] through the transposing
+// LDS read; A is 8 consecutive features of one token straight from memory.
+// ---------------------------------------------------------------------------
+constexpr int kSmallN = 64;  // tokens handled by the few-token kernel
 
-template <int K, int OUT>
-struct SmallJob {
-  static constexpr int OT = OUT / 16;                      // output tiles
-  static constexpr int KS0 = kSmallWaves / OT;             // wanted K splits
-  static constexpr int KS = (K / 32 < KS0) ? K / 32 : KS0;  // K splits (>= 32 each)
-  static constexpr int KPW = K / KS;                       // K per wave
-  // staged [k][output] as in memory; rows of 16 outputs are read without
-  // bank conflicts unpadded, wider rows get 8 halves of padding
-  static constexpr int LDB = (OUT == 16) ? 16 : OUT + 8;
-  static constexpr size_t lds_bytes(int nt) {
-    const size_t stage = (size_t)K * LDB * 2;
-    const size_t red = (size_t)OT * KS * nt * 256 * 4;
-    return stage > red ? stage : red;
-  }
-  static_assert(OUT % 16 == 0 && K % 32 == 0 && K % KS == 0 && KPW % 32 == 0, "job shape");
+// Rows of W per value slice: about 256 value jobs over (slices x column
+// blocks of 32 outputs), at least 64 rows each.
+constexpr int few_slice_rows(int K, int RV) {
+  return K * (RV / 32) / 256 < 64 ? 64 : K * (RV / 32) / 256;
+}
+
+template <int H, int D, int RK, int RV>
+struct FewCfg {
+  static constexpr int K = H * D;           // value contraction
+  static constexpr int CB = 32;             // outputs per column block
+  static constexpr int NCB = RV / CB;       // column blocks (one counter each)
+  static constexpr int R = few_slice_rows(K, RV);
+  static constexpr int S = K / R;           // slices
+  static constexpr int VJ = S * NCB;        // value jobs
+  static constexpr int KCW = R / 64;        // 32-row chunks per wave (two waves per tile)
+  static constexpr int LDW = CB + 16;       // halves per staged row of a W slice
+  static constexpr int LDU = RK + 16;       // halves per staged row of U_h
+  static constexpr int LDS_HALVES = (R * LDW > D * LDU) ? R * LDW : D * LDU;
+  static_assert(RV % CB == 0 && K % R == 0 && R % 64 == 0, "few-token value tiling");
+  static_assert(RK % 16 == 0 && RK <= 64 && D % 32 == 0, "few-token key tiling");
+  static_assert(NCB * 4 <= (int)kWorkspaceHeaderBytes, "arrival counters");
 };
 
 template <int H, int D, int RK, int RV>
-__global__ __launch_bounds__(kSmallWaves * 64) void append_small_kernel(AppendArgs a) {
-  using KJ = SmallJob<D, RK>;
-  constexpr int LDW = RV + 16;  // halves per staged row of a value slice
-  constexpr size_t kSliceLds = (size_t)kSliceRows * LDW * 2;
-  constexpr size_t kLds = KJ::lds_bytes(kSmallN / 16) > kSliceLds ? KJ::lds_bytes(kSmallN / 16)
-                                                                   : kSliceLds;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
+__global__ __launch_bounds__(256) void append_few_kernel(AppendArgs a) {
+  using F = FewCfg<H, D, RK, RV>;
+  __shared__ __attribute__((aligned(16))) half_t sT[F::LDS_HALVES];
+  __shared__ float4v sRed[2][kSmallN / 16][64];  // upper k half of each (tile, token tile)
+  __shared__ int sLast;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 15, quad = lane >> 4;
   const int n_tiles = (a.N + 15) / 16;  // <= kSmallN / 16
+  uint32_t* const counters = a.counters;
+  float* const part = a.part;
 
-  auto run = [&](auto job, const half_t* A, int lda, const half_t* B, int ldb, int o0,
-                 auto store) {
-    using J = decltype(job);
-    constexpr int K = J::KPW * J::KS, OUT = J::OT * 16;
-    half_t* sT = (half_t*)smem;  // [K][LDB]
-    const bool active = w < J::OT * J::KS;
-    const int ot = w % J::OT, ks = w / J::OT;
-    // A fragments of a token tile (8 consecutive features of one token per
-    // chunk); tile 0's are requested before the staging so the two memory
-    // round trips overlap
-    auto load_a = [&](half8 (&av)[J::KPW / 32], int t) {
+  if ((int)blockIdx.x >= F::VJ) {
+    // ---- key job: head h, c_k = U_h^T k over d, one output tile per wave
+    const int h = blockIdx.x - F::VJ;
+    const half_t* Uh = a.U + (size_t)h * D * RK;
+    constexpr int KC = D / 32;
+    const bool active = w < RK / 16;
+    auto load_k = [&](half8 (&av)[KC], int t) {
       const int m = min(t * 16 + col, a.N - 1);
 #pragma unroll
-      for (int c = 0; c < J::KPW / 32; ++c)
-        av[c] = *(const half8*)(A + (size_t)m * lda + ks * J::KPW + c * 32 + quad * 8);
+      for (int c = 0; c < KC; ++c)
+        av[c] = *(const half8*)(a.k + ((size_t)m * H + h) * D + c * 32 + quad * 8);
     };
-    half8 av[J::KPW / 32];
-    if (active) load_a(av, 0);
-    // stage B[k][o0 .. o0+OUT): a thread takes 8 outputs of one k
-    for (int c = tid; c < K * (OUT / 8); c += kSmallWaves * 64) {
-      const int k = c / (OUT / 8), o = (c % (OUT / 8)) * 8;
-      *(half8*)&sT[k * J::LDB + o] = *(const half8*)(B + (size_t)k * ldb + o0 + o);
+    half8 av[KC];
+    if (active) load_k(av, 0);
+    for (int c = tid; c < D * (RK / 8); c += 256) {
+      const int k = c / (RK / 8), o = (c % (RK / 8)) * 8;
+      *(half8*)&sT[k * F::LDU + o] = *(const half8*)(Uh + (size_t)k * RK + o);
     }
     __syncthreads();
-    float4v acc[kSmallN / 16];
+    if (!active) return;  // no barrier follows
+    for (int t = 0; t < n_tiles; ++t) {  // uniform
+      if (t > 0) load_k(av, t);
+      float4v acc = zero4();
 #pragma unroll
-    for (int t = 0; t < kSmallN / 16; ++t) acc[t] = zero4();
-    if (active) {
-      // token tiles outermost; all A fragments of a tile are requested
-      // before its first product, so a tile costs one memory round trip
-      for (int t = 0; t < n_tiles; ++t) {  // uniform
-        if (t > 0) load_a(av, t);
-        float4v acc_t = zero4();
+      for (int c = 0; c < KC; ++c) {
+        // B fragment: k c*32 + 8*quad .. +7 of output 16w + col (lane col
+        // addresses row col/4, outputs 4*(col%4) .. +3)
+        const half_t* bp = &sT[(c * 32 + quad * 8 + (col >> 2)) * F::LDU + w * 16 + 4 * (col & 3)];
+        const half4 b0 = lds_read_tr16(bp);
+        const half4 b1 = lds_read_tr16(bp + 4 * F::LDU);
+        const half8 bq = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        acc = mfma16x16x32(av[c], bq, acc);
+      }
+      // D[token 4*quad + r][output 16w + col]
 #pragma unroll
-        for (int c = 0; c < J::KPW / 32; ++c) {
-          const int k0 = ks * J::KPW + c * 32 + quad * 8;
-          // B fragment (k0 .. k0+7 of output ot*16 + col) through the
-          // transposing read: lane col of the group addresses row col/4,
-          // outputs 4*(col%4) .. +3
-          const half_t* bp = &sT[(k0 + (col >> 2)) * J::LDB + ot * 16 + 4 * (col & 3)];
-          const half4 b0 = lds_read_tr16(bp);
-          const half4 b1 = lds_read_tr16(bp + 4 * J::LDB);
-          const half8 bq = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-          acc_t = mfma16x16x32(av[c], bq, acc_t);
-        }
-#pragma unroll
-        for (int t2 = 0; t2 < kSmallN / 16; ++t2)
-          if (t2 == t) acc[t2] = acc_t;
+      for (int r = 0; r < 4; ++r) {
+        const int n = t * 16 + quad * 4 + r;
+        if (n >= a.N) continue;
+        const int64_t slot = a.slots[n];
+        if (slot < 0 || slot / 16 >= a.num_blocks) continue;
+        store_latent(a, false, (((size_t)(slot / 16) * H + h) * 16 + slot % 16) * RK + w * 16 + col,
+                     acc[r]);
       }
     }
-    __syncthreads();  // staging area becomes the reduction area
-    float* sR = (float*)smem;  // [OT][KS][tile][16 tokens][16 outputs]
-    if (active) {
-#pragma unroll
-      for (int t = 0; t < kSmallN / 16; ++t)
-        if (t < n_tiles)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            sR[(((ot * J::KS + ks) * (kSmallN / 16) + t) * 16 + quad * 4 + r) * 16 + col] = acc[t][r];
-    }
-    __syncthreads();
-    for (int e = tid; e < a.N * OUT; e += kSmallWaves * 64) {
-      const int m = e / OUT, o = e % OUT;
-      const int t = m / 16, tok = m % 16, ot2 = o / 16, oc = o % 16;
-      float sum = 0.f;
-#pragma unroll
-      for (int k2 = 0; k2 < J::KS; ++k2)
-        sum += sR[(((ot2 * J::KS + k2) * (kSmallN / 16) + t) * 16 + tok) * 16 + oc];
-      const int64_t slot = a.slots[m];
-      if (slot < 0) continue;
-      const int64_t blk = slot / 16;
-      if (blk >= a.num_blocks) continue;
-      store(blk, (int)(slot % 16), o0 + o, sum);
-    }
-  };
-
-  const int HD = H * D;
-  constexpr int NS = H * D / kSliceRows;  // value slices
-  if ((int)blockIdx.x < NS) {
-    // value slice j: rows kSliceRows*j .. of W staged in LDS as [k][output];
-    // partial[j][n][f] = sum over the slice's k of v[n][k] W[k][f]
-    const int j = blockIdx.x, k0 = j * kSliceRows;
-    half_t* sW = (half_t*)smem;
-    for (int c = tid; c < kSliceRows * (RV / 8); c += kSmallWaves * 64) {
-      const int k = c / (RV / 8), o = (c % (RV / 8)) * 8;
-      *(half8*)&sW[k * LDW + o] = *(const half8*)(a.W + (size_t)(k0 + k) * RV + o);
-    }
-    __syncthreads();
-    constexpr int OTW = RV / 16 / kSmallWaves;  // 16-output tiles per wave
-    static_assert(RV % (16 * kSmallWaves) == 0 || RV / 16 < kSmallWaves, "value tiles over the waves");
-    constexpr int NOT = OTW > 0 ? OTW : 1;
-    const bool active = OTW > 0 || w < RV / 16;
-    const int n_tiles = (a.N + 15) / 16;
-    if (active) {
-      for (int t = 0; t < n_tiles; ++t) {  // uniform
-        const int m = min(t * 16 + col, a.N - 1);
-        half8 av[kSliceRows / 32];
-#pragma unroll
-        for (int c = 0; c < kSliceRows / 32; ++c)
-          av[c] = *(const half8*)(a.v + (size_t)m * HD + k0 + c * 32 + quad * 8);
-#pragma unroll
-        for (int u = 0; u < NOT; ++u) {
-          const int ot = OTW > 0 ? w * OTW + u : w;
-          float4v acc = zero4();
-#pragma unroll
-          for (int c = 0; c < kSliceRows / 32; ++c) {
-            // B fragment: k c*32 + 8*quad .. +7 of output ot*16 + col through
-            // the transposing read (lane col addresses row col/4, outputs
-            // 4*(col%4) .. +3)
-            const half_t* bp = &sW[(c * 32 + quad * 8 + (col >> 2)) * LDW + ot * 16 + 4 * (col & 3)];
-            const half4 b0 = lds_read_tr16(bp);
-            const half4 b1 = lds_read_tr16(bp + 4 * LDW);
-            const half8 bq = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-            acc = mfma16x16x32(av[c], bq, acc);
-          }
-          // D[token 4*quad + r][output ot*16 + col]
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int n = t * 16 + quad * 4 + r;
-            if (n < a.N) a.part[((size_t)j * a.N + n) * RV + ot * 16 + col] = acc[r];
-          }
-        }
-      }
-    }
-  } else {
-    const int h = blockIdx.x - NS;
-    run(KJ{}, a.k + (size_t)h * D, HD, a.U + (size_t)h * D * RK, RK, 0,
-        [&](int64_t blk, int off, int r, float val) {
-          store_latent(a, false, (((size_t)blk * H + h) * 16 + off) * RK + r, val);
-        });
+    return;
   }
+
+  // ---- value job.  Work groups are dealt to the XCDs round robin; ids b and
+  // b + 8 share an XCD, so they take the two column blocks of one 128-byte
+  // line of W rows, which that XCD's L2 then fetches once.
+  int cb, s;
+  const int b = blockIdx.x;
+  if constexpr (F::VJ % 16 == 0 && F::NCB % 2 == 0) {
+    const int t = (b / 16) * 8 + b % 8;
+    cb = 2 * (t % (F::NCB / 2)) + (b / 8) % 2;
+    s = t / (F::NCB / 2);
+  } else {
+    cb = b % F::NCB;
+    s = b / F::NCB;
+  }
+  const int k0 = s * F::R, o0 = cb * F::CB;
+  const int ot = w & 1, kh = w >> 1;  // output tile, k half of the slice
+  auto load_v = [&](half8 (&av)[F::KCW], int t) {
+    const int m = min(t * 16 + col, a.N - 1);
+#pragma unroll
+    for (int c = 0; c < F::KCW; ++c)
+      av[c] = *(const half8*)(a.v + (size_t)m * F::K + k0 + (kh * F::KCW + c) * 32 + quad * 8);
+  };
+  half8 av[F::KCW];
+  load_v(av, 0);
+  for (int c = tid; c < F::R * (F::CB / 8); c += 256) {
+    const int k = c / (F::CB / 8), o = (c % (F::CB / 8)) * 8;
+    *(half8*)&sT[k * F::LDW + o] = *(const half8*)(a.W + (size_t)(k0 + k) * RV + o0 + o);
+  }
+  __syncthreads();
+  float4v acc[kSmallN / 16];
+#pragma unroll
+  for (int t = 0; t < kSmallN / 16; ++t) acc[t] = zero4();
+  for (int t = 0; t < n_tiles; ++t) {  // uniform
+    if (t > 0) load_v(av, t);
+    float4v acc_t = zero4();
+#pragma unroll
+    for (int c = 0; c < F::KCW; ++c) {
+      const int kr = (kh * F::KCW + c) * 32 + quad * 8;
+      const half_t* bp = &sT[(kr + (col >> 2)) * F::LDW + ot * 16 + 4 * (col & 3)];
+      const half4 b0 = lds_read_tr16(bp);
+      const half4 b1 = lds_read_tr16(bp + 4 * F::LDW);
+      const half8 bq = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      acc_t = mfma16x16x32(av[c], bq, acc_t);
+    }
+#pragma unroll
+    for (int t2 = 0; t2 < kSmallN / 16; ++t2)
+      if (t2 == t) acc[t2] = acc_t;
+  }
+  // the upper k half's sums join the lower half's through LDS
+  if (kh == 1)
+#pragma unroll
+    for (int t = 0; t < kSmallN / 16; ++t)
+      if (t < n_tiles) sRed[ot][t][lane] = acc[t];
+  block_sync_lds();
+  if (kh == 0) {
+#pragma unroll
+    for (int t = 0; t < kSmallN / 16; ++t) {
+      if (t >= n_tiles) break;
+      const float4v sum = acc[t] + sRed[ot][t][lane];
+      // D[token 4*quad + r][output 16*ot + col]
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = t * 16 + quad * 4 + r;
+        if (n < a.N) st_dev(part + ((size_t)s * a.N + n) * RV + o0 + ot * 16 + col, sum[r]);
+      }
+    }
+  }
+  // every partial store of the work group has completed at the device-coherent
+  // level before the arrival is counted
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t before =
+        __hip_atomic_fetch_add(counters + cb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sLast = before == (uint32_t)(F::S - 1);
+  }
+  __syncthreads();
+  if (!sLast) return;
+  // ---- the last slice of column block cb: sums, rounding, slots
+  for (int u = tid; u < a.N * (F::CB / 2); u += 256) {
+    const int n = u / (F::CB / 2), o = o0 + 2 * (u % (F::CB / 2));
+    float2 p[F::S];
+#pragma unroll
+    for (int j = 0; j < F::S; ++j) p[j] = ld_dev2(part + ((size_t)j * a.N + n) * RV + o);
+    float x = 0.f, y = 0.f;
+#pragma unroll
+    for (int j = 0; j < F::S; ++j) {
+      x += p[j].x;
+      y += p[j].y;
+    }
+    const int64_t slot = a.slots[n];
+    if (slot < 0 || slot / 16 >= a.num_blocks) continue;
+    const size_t base = ((size_t)(slot / 16) * RV + o) * 16 + slot % 16;
+    store_latent(a, true, base, x);
+    store_latent(a, true, base + 16, y);
+  }
+  if (tid == 0) __hip_atomic_store(counters + cb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Few-token values, second half: the slices' partials summed, rounded and
@@ -620,23 +648,25 @@ static bool few_token_instance(const ShapeKey& s) {
          (s.H == 32 && s.d == 128 && s.rk == 32 && s.rv == 256);
 }
 
+// Workspace of an append: none, or the arrival counters (kWorkspaceHeaderBytes,
+// zero between calls) followed by the value partials of the few-token path
+// or of the split tiled path.
 size_t append_workspace_bytes(const ShapeKey& s, int n_tokens) {
   if (n_tokens <= 0) return 0;
-  if (n_tokens <= kSmallN)
-    return few_token_instance(s) ? (size_t)(s.H * s.d / kSliceRows) * n_tokens * s.rv * sizeof(float)
-                                 : 0;
+  if (n_tokens <= kSmallN) {
+    if (!few_token_instance(s)) return 0;
+    const int K = s.H * s.d;
+    return kWorkspaceHeaderBytes + (size_t)(K / few_slice_rows(K, s.rv)) * n_tokens * s.rv * sizeof(float);
+  }
   const int vs = tiled_splits(s, n_tokens);
-  return vs > 1 ? (size_t)vs * n_tokens * s.rv * sizeof(float) : 0;
+  return vs > 1 ? kWorkspaceHeaderBytes + (size_t)vs * n_tokens * s.rv * sizeof(float) : 0;
 }
 
 template <int H, int D, int RK, int RV>
 static void launch_few(const AppendArgs& a, hipStream_t st) {
-  constexpr int NS = H * D / kSliceRows;
-  static_assert((H * D) % kSliceRows == 0, "value slices");
-  launch_hooked(TIME_NONE, TIME_NONE, append_small_kernel<H, D, RK, RV>, dim3(NS + H),
-                dim3(kSmallWaves * 64), st, a);
-  launch_hooked(TIME_APPEND, TIME_NONE, append_reduce_kernel<RV, NS>,
-                dim3((unsigned)((a.N * (RV / 4) + 63) / 64)), dim3(256), st, a);
+  using F = FewCfg<H, D, RK, RV>;
+  launch_hooked(TIME_APPEND, TIME_NONE, append_few_kernel<H, D, RK, RV>, dim3(F::VJ + H),
+                dim3(256), st, a);
 }
 
 hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const void* U,
@@ -661,7 +691,8 @@ hipError_t launch_append(const ShapeKey& s, const void* k, const void* v, const 
   a.RK = s.rk;
   a.RV = s.rv;
   a.num_blocks = num_blocks;
-  a.part = (float*)workspace;
+  a.counters = (uint32_t*)workspace;
+  a.part = workspace ? (float*)((char*)workspace + kWorkspaceHeaderBytes) : nullptr;
   a.tiles_m = (n_tokens + AT_M - 1) / AT_M;
   a.v_tiles_n = (s.rv + AT_N - 1) / AT_N;
   a.k_tiles_n = (s.rk + AT_N - 1) / AT_N;

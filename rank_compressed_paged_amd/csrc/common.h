@@ -81,4 +81,30 @@ __device__ __forceinline__ void wave_sync_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// Stores and loads of data that work groups of one launch pass to each
+// other (split partials): device-scope relaxed atomics, which gfx950 issues
+// as ordinary global stores / loads with the sc1 bit, so they write through to
+// and read from the device-coherent level instead of an XCD's own L2.  The
+// writer waits for its stores (vmcnt(0)) before it publishes them with an
+// atomic counter; the reader loads them after it has seen the count.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(half_t* p, half4 v) {
+  __hip_atomic_store((uint64_t*)p, __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ half4 ld_dev(const half_t* p) {
+  return __builtin_bit_cast(half4, __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+}
+
+__device__ __forceinline__ float2 ld_dev2(const float* p) {
+  return __builtin_bit_cast(float2, __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT));
+}
+
 }  // namespace starkv

@@ -38,6 +38,12 @@ constexpr int finish_split_groups(int nt, int tb, int rv) {
   return (tb * rv / 4 >= nt) ? 1 : (nt / (tb * rv / 4) > 8 ? 8 : nt / (tb * rv / 4));
 }
 
+// The first bytes of every decode, prefill and append workspace are
+// reserved: the few-token append keeps its arrival counters there, which
+// must be zero when a workspace is first used and which every call leaves
+// zero (no other call writes them).
+constexpr size_t kWorkspaceHeaderBytes = 256;
+
 // Byte offsets of the decode workspace regions.
 struct DecodeWorkspace {
   size_t qt_off, ml_off, zp_off, sync_off, total;

@@ -216,7 +216,9 @@ def prefill_workspace_size(dims, batch, total_q, max_seq_len):
 
 
 def alloc_workspace(nbytes, device):
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    """A zero-filled workspace: its first 256 bytes (arrival counters of the
+    few-token append) must start at zero, and every call leaves them zero."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
 def append_workspace_size(dims, num_tokens):

@@ -31,7 +31,7 @@ def test_exports_match_header():
 
 
 def test_version_and_status_strings():
-    assert sk.abi_version() == 6
+    assert sk.abi_version() == 7
     for s in range(0, 8):
         assert sk.lib().starkv_status_string(s)
     assert sk.lib().starkv_status_string(99) == b"unknown status"
@@ -117,29 +117,43 @@ def test_append_validation():
 
 
 def test_append_workspace_size():
-    """fp32 partials of the value projection: over 64-row slices of W for up to
-    64 tokens; beyond that, at the main shape, over four parts of the
-    contraction up to 1792 tokens, two parts up to 2816, none above; nothing
-    at the other shapes."""
+    """The reserved 256 bytes (arrival counters) and fp32 partials of the value
+    projection: up to 64 tokens over S slices of W's Hkv*d rows (S = Hkv*d / R,
+    R = max(64, Hkv*d * (r_v/32) / 256)); beyond that, at the main shape,
+    over four parts of the contraction up to 1792 tokens, two parts up to
+    2816, none above; nothing at the shapes without a tuned instance."""
     d = _main_dims()
-    assert sk.append_workspace_size(d, 16) == (32 * 128 // 64) * 16 * 512 * 4
-    assert sk.append_workspace_size(d, 64) == (32 * 128 // 64) * 64 * 512 * 4
-    assert sk.append_workspace_size(d, 65) == 4 * 65 * 512 * 4
-    assert sk.append_workspace_size(d, 1792) == 4 * 1792 * 512 * 4
-    assert sk.append_workspace_size(d, 1793) == 2 * 1793 * 512 * 4
-    assert sk.append_workspace_size(d, 2816) == 2 * 2816 * 512 * 4
+    H = 256  # reserved header
+    assert sk.append_workspace_size(d, 16) == H + 16 * 16 * 512 * 4      # S 16 (R 256)
+    assert sk.append_workspace_size(d, 64) == H + 16 * 64 * 512 * 4
+    assert sk.append_workspace_size(d, 65) == H + 4 * 65 * 512 * 4
+    assert sk.append_workspace_size(d, 1792) == H + 4 * 1792 * 512 * 4
+    assert sk.append_workspace_size(d, 1793) == H + 2 * 1793 * 512 * 4
+    assert sk.append_workspace_size(d, 2816) == H + 2 * 2816 * 512 * 4
     assert sk.append_workspace_size(d, 2817) == 0
     assert sk.append_workspace_size(d, 4096) == 0
     assert sk.append_workspace_size(sk.make_dims(32, 128, 32, 256, 8), 1024) == 0
+    assert sk.append_workspace_size(sk.make_dims(32, 128, 32, 256, 8), 16) == H + 32 * 16 * 256 * 4
+    assert sk.append_workspace_size(sk.make_dims(4, 64, 16, 64, 8), 5) == H + 4 * 5 * 64 * 4
     # shapes without a few-token instance take the tiled kernel: no workspace
     assert sk.append_workspace_size(sk.make_dims(28, 96, 48, 640, 8), 16) == 0
     assert sk.append_workspace_size(sk.make_dims(32, 128, 64, 512, 8, num_kv_heads=16), 16) == 0
     assert sk.append_workspace_size(d, 0) == 0
-    # grouped-query caches: only the key/value heads enter
-    assert sk.append_workspace_size(sk.make_dims(32, 128, 64, 512, 8, num_kv_heads=8), 16) == 16 * 16 * 512 * 4
+    # grouped-query caches: only the key/value heads enter (Hkv*d = 1024: R 64, S 16)
+    assert sk.append_workspace_size(sk.make_dims(32, 128, 64, 512, 8, num_kv_heads=8), 16) == \
+        H + 16 * 16 * 512 * 4
     assert sk.lib().starkv_append_workspace_size(ctypes.byref(d), 4, None) == 1
     assert sk.lib().starkv_append_workspace_size(ctypes.byref(d), -1,
                                                  ctypes.byref(ctypes.c_size_t())) == 2
+
+
+def test_workspace_header_reserved():
+    """Every decode and prefill layout starts after the reserved 256 bytes, so
+    a workspace is never smaller than that."""
+    d = _main_dims()
+    assert sk.decode_workspace_size(d, 0, 2048) >= 256
+    assert sk.decode_workspace_size(d, 1, 16) >= 256 + 32 * 64 * 4
+    assert sk.prefill_workspace_size(d, 1, 1, 16) >= 256 + 32 * 64 * 4
 
 
 def test_prefill_validation():

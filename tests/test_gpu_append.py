@@ -138,21 +138,26 @@ def test_prefill_chunk_append_full_size(sk):
 
 
 def test_few_token_append_shared_workspace_deterministic(sk):
-    """The few-token path keeps fp32 partials in the caller's workspace and
-    sums them in a fixed order: one workspace serves consecutive calls of
-    different sizes (a larger call's leftovers never leak into a smaller
-    one), and a repeated call writes the same bits."""
+    """The few-token path is one launch: value slices write fp32 partials to
+    the caller's workspace and the last slice of each output block sums them
+    in a fixed order, then sets the block's arrival counter (in the reserved
+    first 256 bytes) back to zero.  One workspace serves consecutive calls of
+    different sizes (a larger call's leftovers never leak into a smaller one),
+    the counters are zero after every call, and a repeated call writes the
+    same bits."""
     sh = wl.MAIN
     dims = sk.make_dims(sh.H, sh.d, sh.r_k, sh.r_v, 1)
     ws = sk.alloc_workspace(sk.append_workspace_size(dims, 64), "cuda")
-    ws.fill_(0x7F)  # start from garbage: every partial read must have been written
+    ws.fill_(0x7F)  # partials start as garbage: every one read must have been written
+    ws[:256].zero_()  # the reserved counters start at zero
     outs = {}
-    for n, seed in ((16, 41), (5, 42), (16, 41)):
+    for n, seed in ((16, 41), (5, 42), (64, 43), (16, 41)):
         U, W, k, v, slots, kc, vc = _case(sh, n, seed, 0)
         note(f"append shared workspace n={n}")
         tk, tv = dev(kc), dev(vc)
         sk.append(dev(k), dev(v), dev(U), dev(W), dev(slots), tk, tv, workspace=ws)
         torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws[:256])) == 0, "arrival counters left non-zero"
         gk, gv = tk.cpu().numpy(), tv.cpu().numpy()
         rk, rv = oracle.append(k, v, U, W, slots, kc, vc)
         _check(gk, gv, rk, rv, f"append shared workspace n={n}")
@@ -160,3 +165,54 @@ def test_few_token_append_shared_workspace_deterministic(sk):
             assert np.array_equal(gk.view(np.uint16), outs[n][0].view(np.uint16))
             assert np.array_equal(gv.view(np.uint16), outs[n][1].view(np.uint16))
         outs[n] = (gk, gv)
+
+
+@pytest.mark.parametrize("shape", [wl.TINY, wl.LOWRANK, wl.GQA8], ids=["tiny", "lowrank", "gqa8"])
+def test_few_token_append_counters_reset(sk, shape):
+    """Every few-token instance leaves the reserved counters zero, also with
+    FP8 caches, so a second call on the same workspace is right again."""
+    dims = sk.make_dims(shape.kv, shape.d, shape.r_k, shape.r_v, 1)
+    ws = sk.alloc_workspace(sk.append_workspace_size(dims, 33), "cuda")
+    for rep in range(2):
+        rng = np.random.default_rng(90 + rep)
+        U, W = wl.draw_bases(rng, shape)
+        n = 33
+        nb = (n + shape.bs - 1) // shape.bs + 1
+        slots = rng.permutation(nb * shape.bs)[:n].astype(np.int64)
+        k = rng.standard_normal((n, shape.kv, shape.d), dtype=np.float32).astype(np.float16)
+        v = rng.standard_normal((n, shape.kv, shape.d), dtype=np.float32).astype(np.float16)
+        kc = wl._nan_f16((nb, shape.kv, shape.bs, shape.r_k))
+        vc = wl._nan_f16((nb, shape.r_v, shape.bs))
+        note(f"few-token counters {shape} rep {rep}")
+        tk, tv = dev(kc), dev(vc)
+        sk.append(dev(k), dev(v), dev(U), dev(W), dev(slots), tk, tv, workspace=ws)
+        tk8 = torch.zeros((nb, shape.kv, shape.bs, shape.r_k), dtype=torch.uint8, device="cuda")
+        tv8 = torch.zeros((nb, shape.r_v, shape.bs), dtype=torch.uint8, device="cuda")
+        sk.append_fp8(dev(k), dev(v), dev(U), dev(W), dev(slots), 0.05, 0.05, tk8, tv8,
+                      workspace=ws)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws[:256])) == 0, "arrival counters left non-zero"
+        rk, rv = oracle.append(k, v, U, W, slots, kc, vc)
+        _check(tk.cpu().numpy(), tv.cpu().numpy(), rk, rv, f"few-token {shape} rep {rep}")
+
+
+def test_workspace_shared_by_decode_and_append(sk):
+    """One zero-filled buffer serves a decode call and then an append: the
+    decode never writes the reserved first 256 bytes."""
+    case = wl.make_config("tiny")
+    sh, c = case.shape, case.cache
+    dims = sk.make_dims(sh.H, sh.d, sh.r_k, sh.r_v, c.k_cache.shape[0])
+    msl = int(c.seq_lens.max())
+    need = max(sk.decode_workspace_size(dims, case.B, msl), sk.append_workspace_size(dims, 16))
+    ws = sk.alloc_workspace(need, "cuda")
+    note("decode then append on one workspace")
+    sk.decode_attn(dev(case.q), dev(c.k_cache), dev(c.v_cache), dev(case.U), dev(case.W),
+                   dev(c.block_tables), dev(c.seq_lens), msl, case.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws[:256])) == 0
+    U, W, k, v, slots, kc, vc = _case(sh, 16, 44, 0)
+    tk, tv = dev(kc), dev(vc)
+    sk.append(dev(k), dev(v), dev(U), dev(W), dev(slots), tk, tv, workspace=ws)
+    torch.cuda.synchronize()
+    rk, rv = oracle.append(k, v, U, W, slots, kc, vc)
+    _check(tk.cpu().numpy(), tv.cpu().numpy(), rk, rv, "append after decode on one workspace")
