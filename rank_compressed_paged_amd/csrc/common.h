@@ -34,18 +34,6 @@ __device__ __forceinline__ float4v mfma16x16x32(half8 a, half8 b, float4v c) {
 
 __device__ __forceinline__ float4v zero4() { return float4v{0.f, 0.f, 0.f, 0.f}; }
 
-// Butterfly over the four lanes that share l%16 (l, l^16, l^32, l^48).
-__device__ __forceinline__ float max_over_quads(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-__device__ __forceinline__ float sum_over_quads(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
-
 // fp32 -> (hi, lo) fp16 pairs with hi + lo == x to about 2^-22 relative.
 __device__ __forceinline__ void split_f16x8(float4v a, float4v b, half8& hi, half8& lo) {
 #pragma unroll
@@ -65,6 +53,38 @@ __device__ __forceinline__ void split_f16x4(float4v a, half4& hi, half4& lo) {
     hi[e] = ha;
     lo[e] = (half_t)(a[e] - (float)ha);
   }
+}
+
+// Reductions over the four lanes l, l^16, l^32, l^48 (the four 4-row
+// slices of one column of a 16x16 product) with the cross-row lane swaps,
+// which stay in the vector ALU instead of going through the LDS pipe as
+// __shfl_xor does.  With both operands equal,
+// permlane16_swap leaves lane l of one result and lane l^16 of the other
+// holding x[l] and x[l^16]; permlane32_swap does the same for l^32.
+// Maxima use the NaN-propagating maximum (v_maximum3_f32), which needs no
+// quieting of its inputs, unlike fmaxf: the scores it sees are finite or
+// -inf (masked), never NaN.
+__device__ __forceinline__ float fmax_nn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float quad_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmax_nn(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmax_nn(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// x of lane l ^ X for X = 1 or 2 (within each group of four lanes), through
+// a DPP quad permutation: one vector instruction, no LDS.
+template <int X>
+__device__ __forceinline__ float xor_lane_small(float x) {
+  static_assert(X == 1 || X == 2, "quad permutations only");
+  constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, false));
 }
 
 // Work-group barrier that orders LDS only: waits for this wave's LDS (and

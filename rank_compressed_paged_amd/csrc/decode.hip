@@ -328,28 +328,36 @@ __device__ __forceinline__ void process_page(
     }
   }
   // score = hi product + lo product: the lo column of head col sits HPW
-  // lanes away in the same row of 16 (HPW is a power of two below 16)
-#pragma unroll
-  for (int r = 0; r < 4; ++r) sacc[r] += __shfl_xor(sacc[r], C::HPW);
-  float sv[4];
-  float pm = -INFINITY;
+  // lanes away in the same row of 16 (HPW is a power of two below 16; a DPP
+  // quad permutation for HPW <= 2)
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    sv[r] = (quad * 4 + r < valid) ? sacc[r] : -INFINITY;
-    pm = fmaxf(pm, sv[r]);
+    if constexpr (C::HPW <= 2)
+      sacc[r] += xor_lane_small<C::HPW>(sacc[r]);
+    else
+      sacc[r] += __shfl_xor(sacc[r], C::HPW);
   }
-  pm = max_over_quads(pm);
+  // `valid` is uniform: pages wholly inside the sequence skip every mask
+  const bool full = valid >= BS;
+  float sv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) sv[r] = (full || quad * 4 + r < valid) ? sacc[r] : -INFINITY;
+  const float pm = quad_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
   const float m_new = fmaxf(st.m_run, pm);
-  const float alpha = (m_new == st.m_run) ? 1.f : exp2f(st.m_run - m_new);
+  // weights are 2^(s - m_ref): m_ref is the new running max, or 0 while every
+  // score so far is masked (all s are then -inf); v_exp_f32 gives
+  // 2^-inf = 0, so masked scores need no test
+  const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = (m_new == st.m_run) ? 1.f : __builtin_amdgcn_exp2f(st.m_run - m_ref);
   float ps = 0.f;
   half4 ph;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const float pr = (sv[r] == -INFINITY) ? 0.f : exp2f(sv[r] - m_new);
+    const float pr = __builtin_amdgcn_exp2f(sv[r] - m_ref);
     ps += pr;
     ph[r] = (half_t)pr;
   }
-  ps = sum_over_quads(ps);
+  ps = quad_sum(ps);
   st.l_run = st.l_run * alpha + ps;
   st.m_run = m_new;
   if (col < C::HPW) {
@@ -369,6 +377,15 @@ __device__ __forceinline__ void process_page(
 #pragma unroll
       for (int ft = 0; ft < C::FT; ++ft) st.acc[rt][ft] *= al;
     }
+  }
+  if (full) {
+#pragma unroll
+    for (int ft = 0; ft < C::FT; ++ft) {
+      const half4 av = cur.val(ft);
+#pragma unroll
+      for (int rt = 0; rt < C::RT; ++rt) st.acc[rt][ft] = mfma16x16x16(av, pb[rt], st.acc[rt][ft]);
+    }
+    return;
   }
   // value slots past the sequence may hold anything (NaN): zero them
   const int t0 = quad * 4;

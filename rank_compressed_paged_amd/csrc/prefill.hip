@@ -61,28 +61,6 @@ __device__ __forceinline__ float16v mfma32x32x16(half8 a, half8 b, float16v c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// Reductions over the four lanes l, l^16, l^32, l^48 (the four 4-token
-// slices of one query's scores) with the cross-row lane swaps, which stay in
-// the vector ALU instead of going through LDS.  With both operands equal,
-// permlane16_swap leaves lane l of one result and lane l^16 of the other
-// holding x[l] and x[l^16]; permlane32_swap does the same for l^32.
-// Maxima use the NaN-propagating maximum (v_maximum3_f32), which needs no
-// quieting of its inputs, unlike fmaxf: the scores it sees are finite or
-// -inf (masked), never NaN.
-__device__ __forceinline__ float fmax_nn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
-__device__ __forceinline__ float quad_max(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmax_nn(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmax_nn(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float quad_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 template <int H, int RK, int RV, int G, int MQ, int NW>
 struct PrefillCfg {
   static constexpr int R = G * MQ;           // (head, query) rows
