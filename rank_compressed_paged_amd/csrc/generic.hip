@@ -314,35 +314,68 @@ __global__ __launch_bounds__(kGenThreads) void generic_merge_kernel(GenArgs a) {
 }
 
 // q~[n, h, :] = qscale * U_g^T q[n, h, :] (fp32): work group (16 tokens, h);
-// the tokens' q rows are staged in LDS as fp32, thread r accumulates rank r
-// of all 16 tokens (U read along its rows: consecutive threads, consecutive
-// ranks).
+// the tokens' q rows are staged in LDS as fp32 and U_g in chunks of 32 rows
+// (16-byte loads, the next chunk in flight), thread r accumulates rank r of
+// all 16 tokens over d in order.
 __global__ __launch_bounds__(kGenThreads) void generic_qproj_kernel(
     const half_t* __restrict__ q, const half_t* __restrict__ U, int n_tokens, int H, int QG,
     int D, int RK, float qscale, float* __restrict__ qt) {
-  constexpr int TT = 16;
+  constexpr int TT = 16;  // tokens per work group
+  constexpr int KC = 32;  // rows of U_g per staged chunk
   __shared__ float sq[TT][256];
+  __shared__ __attribute__((aligned(16))) half_t sU[2][KC][256];
+  const int tid = threadIdx.x;
   const int h = blockIdx.y, n0 = blockIdx.x * TT;
   const int g = h / QG;
-  for (int i = threadIdx.x; i < TT * D; i += kGenThreads) {
+  for (int i = tid; i < TT * D; i += kGenThreads) {
     const int tt = i / D, k = i % D;
     const int n = n0 + tt;
     sq[tt][k] = n < n_tokens ? (float)q[((size_t)n * H + h) * D + k] : 0.f;
   }
-  __syncthreads();
+  // U_g moves through LDS in chunks of KC rows, the next chunk's 16-byte
+  // pieces in flight while the current one is used (at most 4 per thread)
   const half_t* Ug = U + (size_t)g * D * RK;
-  for (int r = threadIdx.x; r < RK; r += kGenThreads) {
-    float acc[TT];
+  const int pieces = KC * (RK / 8);
+  half8 pre[4];
+  auto fetch = [&](int c) {
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) acc[tt] = 0.f;
-    for (int k = 0; k < D; ++k) {
-      const float u = (float)Ug[(size_t)k * RK + r];
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) acc[tt] = __builtin_fmaf(sq[tt][k], u, acc[tt]);
+    for (int j = 0; j < 4; ++j) {
+      const int idx = tid + j * kGenThreads;
+      if (idx < pieces)
+        pre[j] = *(const half8*)(Ug + (size_t)(c * KC + idx / (RK / 8)) * RK + (idx % (RK / 8)) * 8);
     }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = tid + j * kGenThreads;
+      if (idx < pieces) *(half8*)&sU[buf][idx / (RK / 8)][(idx % (RK / 8)) * 8] = pre[j];
+    }
+  };
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  const int nc = D / KC;
+  float acc[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) acc[tt] = 0.f;
+  for (int c = 0; c < nc; ++c) {
+    if (c + 1 < nc) fetch(c + 1);
+    if (tid < RK) {  // thread r = tid accumulates rank r of the 16 tokens
+#pragma unroll 4
+      for (int k = 0; k < KC; ++k) {
+        const float u = (float)sU[c & 1][k][tid];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) acc[tt] = __builtin_fmaf(sq[tt][c * KC + k], u, acc[tt]);
+      }
+    }
+    if (c + 1 < nc) stage((c + 1) & 1);
+    __syncthreads();
+  }
+  if (tid < RK) {
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
-      if (n0 + tt < n_tokens) qt[((size_t)(n0 + tt) * H + h) * RK + r] = acc[tt] * qscale;
+      if (n0 + tt < n_tokens) qt[((size_t)(n0 + tt) * H + h) * RK + tid] = acc[tt] * qscale;
   }
 }
 
