@@ -14,7 +14,8 @@ events that take its dispatch's own begin and end timestamps.  `value` is
 latent-KV bytes per step / mean step time.  Beside the headline the line
 carries the step with its append, a streaming-read ceiling, the chunked
 prefill workload (16 requests x 4096 cached + 256 new tokens: attention and
-append, as TFLOP/s against the fp16 MFMA peak), the other fp16 decode
+append, as TFLOP/s against the fp16 MFMA peak), the append at 16 to 4096
+tokens, the other fp16 decode
 configurations of the same shape (decode_b64, long_b20, tiny), decode at other
 layouts (gqa8_b16: 32 query heads on 8 key/value heads; lowrank_b16: r_k
 32, r_v 256; decode_b16_fp8 and decode_b64_fp8: FP8 E4M3 latents), low-batch
@@ -236,6 +237,25 @@ def timed(fn, n, flush_fn=None, kernel_sel=0):
     return steps_ms, kern_ms, wall
 
 
+def stream_ceiling_gbs(nbytes, flush_fn, steps):
+    """The streaming-read ceiling at nbytes: a plain read (16-byte
+    non-temporal loads, 16 in flight per thread) of that many bytes after the
+    same flush, timed like the split kernel (the library's events, from the
+    end of the dispatch before it to the end of its own)."""
+    import torch
+    from rank_compressed_paged_amd import starkv as sk
+    buf = torch.ones(int(nbytes) // 16 * 16, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    for i in range(3):
+        flush_fn(i)
+        sk.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    _, kern_ms, _ = timed(lambda: sk.stream_read(buf, sink), steps, flush_fn, sk.TIME_STREAM_READ)
+    gbs = buf.numel() / (statistics.fmean(kern_ms) * 1e-3) / 1e9
+    del buf
+    return gbs
+
+
 def rocminfo_gpu():
     """Marketing name, maximum engine clock and compute units of the first
     GPU agent as rocminfo prints them (empty when rocminfo is unavailable)."""
@@ -436,6 +456,8 @@ def decode_leg(name, flush_fn, steps):
     lat = metrics.decode_latent_bytes(c.seq_lens, sh.kv, sh.r_k, sh.r_v) // (2 if fp8 else 1)
     m = statistics.fmean
     gbs = lambda ms: lat / (ms * 1e-3) / 1e9
+    del q, kc, vc, ws
+    ceiling = stream_ceiling_gbs(lat, flush_fn, steps)
     return {
         "workload": name, "batch": B, "seq_len": msl, "heads": sh.H, "kv_heads": sh.kv,
         "rank_k": sh.r_k, "rank_v": sh.r_v, "latent_dtype": "e4m3" if fp8 else "f16",
@@ -444,6 +466,8 @@ def decode_leg(name, flush_fn, steps):
         "split_kernel_ms": round(m(kern_ms), 5),
         "split_kernel_gbs": round(gbs(m(kern_ms)), 1),
         "split_kernel_hbm_frac": round(gbs(m(kern_ms)) / HBM_PEAK_GBS, 4),
+        "stream_read_ceiling_gbs": round(ceiling, 1),
+        "split_kernel_over_ceiling": round(gbs(m(kern_ms)) / ceiling, 4),
     }
 
 
@@ -509,6 +533,52 @@ def low_batch_leg(flush_fn, steps):
                      "graph_latency_us": round(graph_us, 2)})
         del g
     return rows
+
+
+def append_sizes_leg(flush_fn, steps):
+    """The append at the main shape over a range of token counts (a decode
+    step's 16 tokens up to a prefill chunk's 4096), flushed: events around the
+    call and the library's timing events around its kernels, with the
+    workspace the call needs (few-token path up to 64 tokens, the tiled
+    kernel with its contraction split in four or two parts up to 2816, the
+    unsplit tiled kernel above)."""
+    import numpy as np
+    import torch
+    from rank_compressed_paged_amd import metrics
+    from rank_compressed_paged_amd import starkv as sk
+    from rank_compressed_paged_amd import workloads as wl
+    sh = wl.MAIN
+    rng = np.random.default_rng(321)
+    U, W = wl.draw_bases(rng, sh)
+    U, W = torch.from_numpy(U).cuda(), torch.from_numpy(W).cuda()
+    out = []
+    for n in (16, 64, 128, 512, 1024, 2048, 4096):
+        k = torch.from_numpy(rng.standard_normal((n, sh.H, sh.d), dtype=np.float32)
+                             .astype(np.float16)).cuda()
+        v = torch.from_numpy(rng.standard_normal((n, sh.H, sh.d), dtype=np.float32)
+                             .astype(np.float16)).cuda()
+        nb = (n + sh.bs - 1) // sh.bs
+        kc = torch.zeros((nb, sh.H, sh.bs, sh.r_k), dtype=torch.float16, device="cuda")
+        vc = torch.zeros((nb, sh.r_v, sh.bs), dtype=torch.float16, device="cuda")
+        slots = torch.arange(n, dtype=torch.int64, device="cuda")
+        dims = sk.dims_of(kc, vc, U, W)
+        need = sk.append_workspace_size(dims, n)
+        ws = sk.alloc_workspace(need, "cuda") if need else None
+
+        def app():   # same slots each time: idempotent
+            sk.append(k, v, U, W, slots, kc, vc, workspace=ws)
+        for i in range(3):
+            flush_fn(i)
+            app()
+        torch.cuda.synchronize()
+        call_ms, _, _ = timed(app, steps, flush_fn)
+        _, kern_ms, _ = timed(app, steps, flush_fn, sk.TIME_APPEND)
+        kern = statistics.fmean(kern_ms)
+        flops = metrics.append_flops(n, sh.H, sh.d, sh.r_k, sh.r_v)
+        out.append({"tokens": n, "call_us": round(statistics.fmean(call_ms) * 1e3, 2),
+                    "kernel_us": round(kern * 1e3, 2), "workspace_bytes": int(need),
+                    "kernel_tflops": round(flops / (kern * 1e-3) / 1e12, 1)})
+    return out
 
 
 def fit_leg(steps):
@@ -636,15 +706,8 @@ def run_bench(args):
     _, fused_kern_ms, _ = timed(step2, args.steps, do_flush, sk.TIME_DECODE_SPLIT)
     del ws2
 
-    # measured streaming-read ceiling on this machine: the library's plain
-    # streaming read (16-byte non-temporal loads, 16 in flight per thread)
-    # over as many bytes as one step's latents, after the same flush
-    ceil_buf = torch.ones(lat_bytes, dtype=torch.uint8, device="cuda")
-    ceil_sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
-    ceil_ms, _, _ = timed(lambda: sk.stream_read(ceil_buf, ceil_sink), max(args.steps, 10),
-                          do_flush)
-    ceiling_gbs = lat_bytes / (statistics.fmean(ceil_ms) * 1e-3) / 1e9
-    del ceil_buf
+    # the streaming-read ceiling measured on this machine at this step's size
+    ceiling_gbs = stream_ceiling_gbs(lat_bytes, do_flush, max(args.steps, 10))
 
     ms = statistics.fmean(step_ms)
     kern = statistics.fmean(kern_ms)
@@ -699,10 +762,10 @@ def run_bench(args):
         },
     }
     if not args.no_prefill:
-        del ceil_sink
         res["prefill"] = prefill_leg(do_flush, args.steps,
                                      cpu_budget_s=0.0 if args.no_cpu else args.cpu_prefill_seconds)
         res["prefill_fp8"] = prefill_leg(do_flush, args.steps, "prefill_b16_fp8")
+        res["append_sizes"] = append_sizes_leg(do_flush, args.steps)
     if not args.no_low_batch:
         res["low_batch"] = low_batch_leg(do_flush, args.steps)
     if not args.no_configs:

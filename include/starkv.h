@@ -347,7 +347,9 @@ starkv_status starkv_prefill_attn_fp8(const starkv_dims* dims, const void* q,
  * `start` is recorded on the stream just before their launch.
  *   which = 0 none (clears), 1 decode split-K attention, 2 prefill attention,
  *   3 append, 4 the Gram-matrix kernel of the bases fit (no predecessor
- *   either).  Events are owned by the caller and must outlive the calls.
+ *   either), 5 the streaming read of starkv_util_stream_read (which then
+ *   launches an empty one-wave kernel first, for `start`).  Events are owned
+ *   by the caller and must outlive the calls.
  * Process-wide setting; not for concurrent use from several threads.
  */
 starkv_status starkv_set_timing_events(void* start, void* stop, int32_t which);

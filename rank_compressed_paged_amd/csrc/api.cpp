@@ -695,7 +695,7 @@ starkv_status starkv_util_stream_read(const void* src, size_t bytes, void* sink,
 }
 
 starkv_status starkv_set_timing_events(void* start, void* stop, int32_t which) {
-  if (which < 0 || which > 4) return STARKV_ERR_ARG;
+  if (which < 0 || which > 5) return STARKV_ERR_ARG;
   if (which != 0 && (!start || !stop)) return STARKV_ERR_NULL;
   g_timing.start = (hipEvent_t)start;
   g_timing.stop = (hipEvent_t)stop;

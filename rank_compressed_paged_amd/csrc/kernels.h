@@ -90,7 +90,14 @@ struct TimingHook {
   int which = 0;
 };
 extern TimingHook g_timing;
-enum { TIME_NONE = 0, TIME_DECODE_SPLIT = 1, TIME_PREFILL_ATTN = 2, TIME_APPEND = 3, TIME_FIT_GRAM = 4 };
+enum {
+  TIME_NONE = 0,
+  TIME_DECODE_SPLIT = 1,
+  TIME_PREFILL_ATTN = 2,
+  TIME_APPEND = 3,
+  TIME_FIT_GRAM = 4,
+  TIME_STREAM_READ = 5
+};
 
 // Launch `kernel` on `st`.  Timing hook: when the hook selects `which`, its
 // stop event is bound to this dispatch (hipExtLaunchKernelGGL), so it takes

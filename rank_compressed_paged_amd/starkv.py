@@ -126,7 +126,8 @@ _lib.starkv_prefill_attn_fp8.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _i32, _
 _lib.starkv_set_timing_events.restype = _i32
 _lib.starkv_set_timing_events.argtypes = [_vp, _vp, _i32]
 
-TIME_NONE, TIME_DECODE_SPLIT, TIME_PREFILL_ATTN, TIME_APPEND, TIME_FIT_GRAM = 0, 1, 2, 3, 4
+TIME_NONE, TIME_DECODE_SPLIT, TIME_PREFILL_ATTN, TIME_APPEND, TIME_FIT_GRAM, TIME_STREAM_READ = \
+    0, 1, 2, 3, 4, 5
 
 
 def lib():

@@ -184,7 +184,9 @@ def test_timing_event_validation():
     assert f(None, None, 0) == 0
     assert f(None, None, 1) == 1
     assert f(FAKE, FAKE, 9) == 7
-    assert f(FAKE, FAKE, 5) == 7
+    assert f(FAKE, FAKE, 6) == 7
+    assert f(None, None, 5) == 1   # the streaming-read selector needs both events
+    assert f(None, None, 0) == 0
 
 
 def test_decode_plan_properties():
