@@ -30,7 +30,8 @@ Other modes:
     --summarize-pmc F W OUT   turn FETCH_SIZE / WRITE_SIZE counter CSVs into
                               the traffic summary the benchmark reads back
     --plan-sweep              decode step and split kernel at forced split
-                              plans (pages per split) beside the planner's own,
+                              plans (pages per split, and with --sweep-merge
+                              finish-kernel tiles) beside the planner's own,
                               one JSON line per plan
 """
 from __future__ import annotations
@@ -127,6 +128,9 @@ def parse_args(argv=None):
                     help="workloads of --plan-sweep")
     ap.add_argument("--sweep-pps", default="4,6,8,9,12,16,32,64,128",
                     help="pages_per_split values of --plan-sweep (0 = the planner's)")
+    ap.add_argument("--sweep-merge", default="",
+                    help="merge_seqs values of --plan-sweep, each at the planner's split plan "
+                         "(0 = the planner's)")
     return ap.parse_args(argv)
 
 
@@ -837,8 +841,9 @@ def profile_run(args):
 
 def plan_sweep(args):
     """Decode steps and the split-K kernel (flushed, as in the benchmark) at
-    the planner's split plan and at forced pages_per_split values: the
-    evidence for the planner's choice, one JSON line per (workload, plan)."""
+    the planner's split plan, at forced pages_per_split values and at forced
+    finish-kernel tiles (merge_seqs, rows per work group): the evidence for
+    the planner's choices, one JSON line per (workload, plan)."""
     import numpy as np
     import torch
     from rank_compressed_paged_amd import metrics
@@ -859,15 +864,17 @@ def plan_sweep(args):
         lat = metrics.decode_latent_bytes(c.seq_lens, sh.kv, sh.r_k, sh.r_v)
         out = torch.empty((B, sh.H, sh.d), dtype=torch.float16, device="cuda")
         pages = (msl + sh.bs - 1) // sh.bs
-        for pps in [0] + [int(x) for x in args.sweep_pps.split(",")]:
+        plans = [(pps, 0) for pps in [0] + [int(x) for x in args.sweep_pps.split(",") if x]]
+        plans += [(0, m) for m in [int(x) for x in args.sweep_merge.split(",") if x]]
+        for pps, merge in plans:
             if pps > pages:
                 continue
-            ws = sk.alloc_workspace(sk.decode_workspace_size(dims, B, msl, pages_per_split=pps),
-                                    "cuda")
+            ws = sk.alloc_workspace(sk.decode_workspace_size(dims, B, msl, pages_per_split=pps,
+                                                             merge_seqs=merge), "cuda")
 
             def step():
                 sk.decode_attn(q, kc, vc, U, W, bt, sl, msl, case.scale, out=out, workspace=ws,
-                               pages_per_split=pps)
+                               pages_per_split=pps, merge_seqs=merge)
             for i in range(5):
                 fl(i)
                 step()
@@ -877,7 +884,8 @@ def plan_sweep(args):
             sm, km = statistics.fmean(s_ms), statistics.fmean(k_ms)
             plan = sk.decode_plan(dims, B, msl) if pps == 0 else (pps, (pages + pps - 1) // pps)
             print(json.dumps({"workload": name, "pages_per_split": plan[0], "num_splits": plan[1],
-                              "planner": pps == 0, "work_groups": B * plan[1],
+                              "merge_seqs": merge or "planner",
+                              "planner": pps == 0 and merge == 0, "work_groups": B * plan[1],
                               "step_us": round(sm * 1e3, 2), "split_kernel_us": round(km * 1e3, 2),
                               "split_kernel_hbm_frac": round(lat / (km * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                               "step_hbm_frac": round(lat / (sm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}),
