@@ -54,7 +54,8 @@
  *     must be 16-byte aligned.  A launch failure maps to STARKV_ERR_LAUNCH.
  *   - Contents of device index arrays (block tables, seq_lens, slots,
  *     query_start_loc) are trusted.  Block ids outside [0, num_blocks) and
- *     slots outside the cache are skipped rather than dereferenced.
+ *     slots outside the cache are skipped rather than dereferenced;
+ *     starkv_check_indices reports them on request.
  *   - Shapes.  Tuned instances of the attention and append calls:
  *     (H, d, r_k, r_v) = (32, 128, 64, 512) with Hkv 32 or 8,
  *     (32, 128, 32, 256) with Hkv 32, and (4, 64, 16, 64) with Hkv 4 or 2
@@ -77,7 +78,7 @@
 extern "C" {
 #endif
 
-#define STARKV_ABI_VERSION 7
+#define STARKV_ABI_VERSION 8
 
 typedef enum {
   STARKV_OK = 0,
@@ -408,6 +409,39 @@ starkv_status starkv_fit_bases(const starkv_dims* dims, const void* k, const voi
                                int32_t iters, void* U, void* W, void* workspace,
                                size_t workspace_bytes, int32_t* info, float* residual,
                                void* stream);
+
+/*
+ * Index checks (a debugging aid, not part of the attention path).  Decode,
+ * prefill and append trust the contents of their device index arrays: they
+ * skip block ids outside [0, num_blocks) and slots outside the cache, and
+ * plan the split-K work for lengths up to max_seq_len, so a bad index shows
+ * up as silently missing tokens rather than as an error.  This call scans the
+ * arrays those calls would read (the paged cache of README "KV-cache
+ * capacity": 16-token blocks reached through a block table, and the slots of
+ * the new tokens) and reports what lies outside those ranges:
+ *   block_tables  [batch][max_blocks_per_seq] int32; entry (b, j) is checked
+ *                 for j < ceil(min(max(seq_lens[b], 0), max_seq_len) / 16)
+ *   seq_lens      [batch] int32, each expected in [0, max_seq_len]
+ *   slot_mapping  [num_tokens] int64 (may be NULL when num_tokens is 0);
+ *                 each expected below num_blocks * 16 (negative = padding)
+ *   report        [4] uint32 (device, 16-byte aligned), written by the call:
+ *                 report[0]  bit 0: a block id out of range,
+ *                            bit 1: a length out of range,
+ *                            bit 2: a slot at or beyond the cache
+ *                 report[1]  the first sequence with a bad block id,
+ *                 report[2]  the first sequence with a bad length,
+ *                 report[3]  the first token with a bad slot
+ *                 (0xFFFFFFFF where there is none)
+ * dims supplies num_blocks and block_size (16); its other fields are not
+ * used.  Host checks as for decode (batch, max_seq_len, max_blocks_per_seq),
+ * num_tokens >= 0.  One work group scans everything, so the call takes time
+ * linear in batch * max_blocks_per_seq + num_tokens; asynchronous on stream.
+ */
+starkv_status starkv_check_indices(const starkv_dims* dims, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                   int32_t batch, int32_t max_seq_len,
+                                   const int64_t* slot_mapping, int32_t num_tokens,
+                                   uint32_t* report, void* stream);
 
 /*
  * Measurement utility (not part of the attention path): read `bytes` bytes

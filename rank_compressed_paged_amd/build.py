@@ -21,7 +21,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libstarkv.so")
 SOURCES = ["api.cpp", "decode.hip", "append.hip", "prefill.hip", "util.hip", "fit.hip",
-           "noalloc.hip", "generic.hip"]
+           "noalloc.hip", "generic.hip", "check.hip"]
 ARCH = "gfx950"
 
 

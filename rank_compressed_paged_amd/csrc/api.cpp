@@ -686,6 +686,27 @@ starkv_status starkv_fit_bases(const starkv_dims* dims, const void* k, const voi
   return e == hipSuccess ? STARKV_OK : STARKV_ERR_LAUNCH;
 }
 
+starkv_status starkv_check_indices(const starkv_dims* dims, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                   int32_t batch, int32_t max_seq_len,
+                                   const int64_t* slot_mapping, int32_t num_tokens,
+                                   uint32_t* report, void* stream) {
+  if (!dims || !report) return STARKV_ERR_NULL;
+  if (dims->block_size != 16 || dims->num_blocks < 0 || num_tokens < 0) return STARKV_ERR_DIMS;
+  starkv_status st = check_paging(batch, max_seq_len, max_blocks_per_seq, dims->block_size);
+  if (st != STARKV_OK) return st;
+  if (batch > 0 && (!seq_lens || (max_blocks_per_seq > 0 && !block_tables))) return STARKV_ERR_NULL;
+  if (num_tokens > 0 && !slot_mapping) return STARKV_ERR_NULL;
+  for (const void* p : {(const void*)block_tables, (const void*)seq_lens,
+                        (const void*)slot_mapping, (const void*)report})
+    if (p && !aligned16(p)) return STARKV_ERR_ALIGN;
+  return launch_check_indices(block_tables, max_blocks_per_seq, seq_lens, batch, max_seq_len,
+                              dims->num_blocks, slot_mapping, num_tokens, report,
+                              (hipStream_t)stream) == hipSuccess
+             ? STARKV_OK
+             : STARKV_ERR_LAUNCH;
+}
+
 starkv_status starkv_util_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
   if (bytes == 0) return STARKV_OK;
   if (!src || !sink) return STARKV_ERR_NULL;

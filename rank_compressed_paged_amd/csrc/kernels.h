@@ -182,6 +182,13 @@ hipError_t launch_upproj_tiled(const ShapeKey& s, const void* W, const void* z_t
 constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
 hipError_t noalloc_scratch(void** ptr);
 
+// Index checks (debugging aid): scan block tables, lengths and slots, write
+// the four-word report described with starkv_check_indices.
+hipError_t launch_check_indices(const int32_t* block_tables, int max_blocks,
+                                const int32_t* seq_lens, int batch, int max_seq_len,
+                                int num_blocks, const int64_t* slots, int n_slots,
+                                uint32_t* report, hipStream_t st);
+
 // Measurement aid: read `bytes` (a multiple of 16) with 16-byte loads and
 // fold them into one word per work group, so nothing is optimised away.
 hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t st);

@@ -37,6 +37,7 @@ EXPORTED = [
     "starkv_util_event_elapsed_ms", "starkv_fit_workspace_size", "starkv_fit_bases",
     "starkv_append_fp8", "starkv_decode_attn_fp8", "starkv_prefill_attn_fp8",
     "starkv_decode_workspace_size_cfg", "starkv_decode_attn_cfg", "starkv_decode_attn_noalloc",
+    "starkv_check_indices",
 ]
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -99,6 +100,9 @@ _lib.starkv_prefill_attn.restype = _i32
 _lib.starkv_prefill_attn.argtypes = [ctypes.POINTER(Dims), _vp, _vp, _i32, _i32, _vp, _vp, _vp,
                                      _vp, _vp, _i32, _vp, _i32, _i32, ctypes.c_float, _vp, _vp,
                                      _sz, _vp]
+_lib.starkv_check_indices.restype = _i32
+_lib.starkv_check_indices.argtypes = [ctypes.POINTER(Dims), _vp, _i32, _vp, _i32, _i32, _vp, _i32,
+                                      _vp, _vp]
 _lib.starkv_util_stream_read.restype = _i32
 _lib.starkv_util_stream_read.argtypes = [_vp, _sz, _vp, _vp]
 _lib.starkv_util_event_create.restype = _i32
@@ -440,6 +444,26 @@ def prefill_attn_fp8(q, query_start_loc, max_query_len, k_cache8, v_cache8, U, W
         int(workspace.numel()), _stream(stream))
     _check(st, "starkv_prefill_attn_fp8")
     return out
+
+
+def check_indices(block_tables, seq_lens, max_seq_len, num_blocks, slot_mapping=None,
+                  report=None, stream=None):
+    """Index checks (debugging aid): returns the [4] device report of
+    starkv_check_indices as int32 (flags; first sequence with a bad block id;
+    first with a bad length; first token with a bad slot; -1, the uint32
+    0xFFFFFFFF, for none)."""
+    B = int(seq_lens.shape[0])
+    dims = make_dims(1, 32, 8, 8, int(num_blocks))
+    if report is None:
+        report = torch.empty(4, dtype=torch.int32, device=seq_lens.device)
+    n = 0 if slot_mapping is None else int(slot_mapping.shape[0])
+    slots = None if slot_mapping is None else _dev(slot_mapping, torch.int64, "slot_mapping")
+    _check(_lib.starkv_check_indices(
+        ctypes.byref(dims), _dev(block_tables, torch.int32, "block_tables"),
+        int(block_tables.shape[1]), _dev(seq_lens, torch.int32, "seq_lens", (B,)), B,
+        int(max_seq_len), slots, n, _dev(report, torch.int32, "report", (4,)), _stream(stream)),
+        "starkv_check_indices")
+    return report
 
 
 def stream_read(buf, sink, stream=None):

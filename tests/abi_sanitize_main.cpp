@@ -175,6 +175,19 @@ int main() {
                           nullptr, (float*)((char*)F + 2), nullptr),
          STARKV_ERR_ALIGN);
 
+  // index checks
+  const int64_t* Fs = (const int64_t*)F;
+  uint32_t* Fu = (uint32_t*)F;
+  starkv_dims nb100 = dims(1, 32, 8, 8, 100);
+  EXPECT(starkv_check_indices(&nb100, Fi, 8, Fi, 4, 128, Fs, 16, nullptr, nullptr), STARKV_ERR_NULL);
+  EXPECT(starkv_check_indices(nullptr, Fi, 8, Fi, 4, 128, Fs, 16, Fu, nullptr), STARKV_ERR_NULL);
+  EXPECT(starkv_check_indices(&nb100, Fi, 8, Fi, 4, 129, Fs, 16, Fu, nullptr), STARKV_ERR_DIMS);
+  EXPECT(starkv_check_indices(&nb100, Fi, 8, Fi, 4, 128, nullptr, 16, Fu, nullptr),
+         STARKV_ERR_NULL);
+  EXPECT(starkv_check_indices(&nb100, Fi, 8, Fi, 4, 128, Fs, -3, Fu, nullptr), STARKV_ERR_DIMS);
+  EXPECT(starkv_check_indices(&nb100, Fi, 8, Fi, 4, 128, Fs, 16, (uint32_t*)M, nullptr),
+         STARKV_ERR_ALIGN);
+
   // measurement hooks
   EXPECT(starkv_set_timing_events(nullptr, nullptr, 0), STARKV_OK);
   EXPECT(starkv_set_timing_events(nullptr, nullptr, 1), STARKV_ERR_NULL);

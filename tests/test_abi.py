@@ -31,7 +31,7 @@ def test_exports_match_header():
 
 
 def test_version_and_status_strings():
-    assert sk.abi_version() == 7
+    assert sk.abi_version() == 8
     for s in range(0, 8):
         assert sk.lib().starkv_status_string(s)
     assert sk.lib().starkv_status_string(99) == b"unknown status"
@@ -154,6 +154,24 @@ def test_workspace_header_reserved():
     assert sk.decode_workspace_size(d, 0, 2048) >= 256
     assert sk.decode_workspace_size(d, 1, 16) >= 256 + 32 * 64 * 4
     assert sk.prefill_workspace_size(d, 1, 1, 16) >= 256 + 32 * 64 * 4
+
+
+def test_check_indices_validation():
+    """Host checks of the index scan, all before any launch."""
+    f = sk.lib().starkv_check_indices
+    d = sk.make_dims(1, 32, 8, 8, 100)
+    assert f(ctypes.byref(d), FAKE, 8, FAKE, 4, 128, FAKE, 16, None, None) == 1   # no report
+    assert f(None, FAKE, 8, FAKE, 4, 128, FAKE, 16, FAKE, None) == 1
+    assert f(ctypes.byref(d), None, 8, FAKE, 4, 128, FAKE, 16, FAKE, None) == 1   # no table
+    assert f(ctypes.byref(d), FAKE, 8, None, 4, 128, FAKE, 16, FAKE, None) == 1   # no lengths
+    assert f(ctypes.byref(d), FAKE, 8, FAKE, 4, 128, None, 16, FAKE, None) == 1   # no slots
+    assert f(ctypes.byref(d), FAKE, 8, FAKE, 4, 129, FAKE, 16, FAKE, None) == 2   # table too short
+    assert f(ctypes.byref(d), FAKE, 8, FAKE, 4, 128, FAKE, -1, FAKE, None) == 2
+    assert f(ctypes.byref(d), FAKE, 8, FAKE, -1, 128, FAKE, 16, FAKE, None) == 2
+    d17 = sk.make_dims(1, 32, 8, 8, 100, block_size=17)
+    assert f(ctypes.byref(d17), FAKE, 8, FAKE, 4, 128, FAKE, 16, FAKE, None) == 2
+    assert f(ctypes.byref(d), FAKE, 8, FAKE, 4, 128, FAKE, 16, FAKE + 4, None) == 5
+    assert f(ctypes.byref(d), FAKE + 8, 8, FAKE, 4, 128, FAKE, 16, FAKE, None) == 5
 
 
 def test_prefill_validation():
