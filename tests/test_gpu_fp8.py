@@ -79,9 +79,14 @@ def _code_rank(c):
 
 
 @pytest.mark.parametrize("shape,n,seed", [(wl.MAIN, 16, 82), (wl.MAIN, 300, 83),
+                                          (wl.MAIN, 2000, 86), (wl.MAIN, 3000, 87),
                                           (wl.TINY, 40, 84), (wl.GQA8, 100, 85)],
-                         ids=["main_16", "main_300", "tiny_40", "gqa8_100"])
+                         ids=["main_16", "main_300_split4", "main_2000_split2",
+                              "main_3000_unsplit", "tiny_40", "gqa8_100"])
 def test_append_fp8(sk, shape, n, seed):
+    """FP8 codes from every append form: one launch (16 tokens), the tiled
+    kernel with its value contraction split four ways (300), two ways (2000)
+    or not at all (3000), and the smaller shapes."""
     rng = np.random.default_rng(seed)
     U, W = wl.draw_bases(rng, shape)
     nb = (n + shape.bs - 1) // shape.bs + 2
