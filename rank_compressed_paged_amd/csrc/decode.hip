@@ -94,7 +94,7 @@ __device__ __forceinline__ half4 lds_read_tr16(const half_t* p) {
 // the W block of head h's key/value head.  Work groups are dealt to the 8
 // XCDs round robin, so with H a multiple of 8 it runs on XCD h % 8, where
 // the merge places head h's work groups; the block then waits in that XCD's
-// L2 (the split kernel's page reads are non-temporal) instead of in HBM.
+// L2 instead of in HBM.
 // The loaded words only feed a value stored through `sink`, which is null.
 template <int H, int D, int RK, int TPW, int QG>
 __global__ __launch_bounds__(256) void qproj_kernel(const half_t* __restrict__ q,
