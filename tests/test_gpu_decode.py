@@ -192,3 +192,26 @@ def test_fused_step_repeats_and_resets(sk):
             assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
     assert_parity(outs_a[0], _oracle(a), "fused repeat a")
     assert_parity(outs_b[0], _oracle(b), "fused repeat b")
+
+
+def test_decode_one_million_tokens(sk):
+    """One sequence of 2^20 tokens (65536 pages: the planner's largest split,
+    256 pages, and 256 splits merged by the wide merge tiles), tiny shape;
+    a planted key pair in the middle page keeps the output away from zero."""
+    case = wl.make_decode_case(wl.TINY, seq_lens=[1 << 20], seed=33, plant=("mid",), q_mult=4)
+    note("decode 2^20 tokens, tiny shape")
+    out = run_decode(sk, case)
+    assert_parity(out, _oracle(case), "2^20 tokens")
+
+
+def test_decode_4096_short_sequences(sk):
+    """4096 sequences of 0-299 tokens in one call (tiny shape): a grid 4096
+    rows tall, empty sequences among them."""
+    rng = np.random.default_rng(34)
+    lens = rng.integers(0, 300, size=4096).tolist()
+    case = wl.make_decode_case(wl.TINY, seq_lens=lens, seed=34)
+    note("decode 4096 short sequences, tiny shape")
+    out = run_decode(sk, case)
+    assert_parity(out, _oracle(case), "4096 sequences")
+    empty = [b for b, L in enumerate(lens) if L == 0]
+    assert empty and torch.count_nonzero(out[empty]).item() == 0
