@@ -88,3 +88,22 @@ def test_prefill_full_size_sampled(sk):
                           for r in rows])
     assert torch.isfinite(out.float()).all()
     assert_parity(out[torch.from_numpy(sel).cuda()], ref[sel], "prefill_b16 sample")
+
+
+@pytest.mark.parametrize("shape", [wl.TINY, wl.MAIN], ids=["tiny", "main"])
+def test_prefill_long_prefix_and_many_requests(sk, shape):
+    """A request with a long cached prefix beside an empty-prefix one and a
+    single-token chunk (tiny shape: 131072 cached tokens; main shape: 16384),
+    then 64 requests of mixed lengths in one call."""
+    long = 131072 if shape is wl.TINY else 16384
+    case = wl.make_prefill_case(shape, [long, 0, 5000], [64, 300, 1], seed=44)
+    note(f"prefill long prefix {shape}")
+    out, kc, vc = _gpu_prefill(sk, case)
+    assert_parity(out, _oracle(case, kc, vc), "long prefix (gpu caches)")
+    rng = np.random.default_rng(45)
+    cached = rng.integers(0, 600, size=64).tolist()
+    chunk = rng.integers(1, 90, size=64).tolist()
+    case = wl.make_prefill_case(shape, cached, chunk, seed=45)
+    note(f"prefill 64 requests {shape}")
+    out, kc, vc = _gpu_prefill(sk, case)
+    assert_parity(out, _oracle(case, kc, vc), "64 requests (gpu caches)")
