@@ -60,3 +60,68 @@ def test_decode_graph_replays(sk, lens):
         ref = oracle.decode(qn, c.k_cache, c.v_cache, case.U, case.W, c.block_tables,
                             c.seq_lens, case.scale)
         assert_parity(got, ref, f"graph replay {rep}")
+
+
+@pytest.mark.parametrize("chunk", [16, 300], ids=["few_token_append", "tiled_append"])
+def test_serving_step_graph_replays(sk, chunk):
+    """A whole serving step captured as one graph: the append of the step's
+    new tokens (the few-token form, whose arrival counters must return to
+    zero, or the tiled form with its split contraction) and then decode over
+    the grown sequences.  Each replay gets new q, k, v written in place;
+    every replay must equal the eager step bit for bit and the oracle's
+    append-then-decode within the bars."""
+    shape = wl.MAIN
+    B = 4 if chunk == 16 else 1
+    per = chunk // B
+    lens0 = [600, 33, 1500, 0][:B] if B > 1 else [900]
+    case = wl.make_decode_case(shape, seq_lens=[L + per for L in lens0], seed=93)
+    c = case.cache
+    # the step's tokens: the last `per` positions of every sequence
+    slots = np.concatenate([c.block_tables[b, (lens0[b] + j) // 16] * 16 + (lens0[b] + j) % 16
+                            for b in range(B) for j in [np.arange(per)]]).astype(np.int64)
+    kc0, vc0 = c.k_cache.copy(), c.v_cache.copy()
+    q, U, W = dev(case.q), dev(case.U), dev(case.W)
+    kc, vc = dev(kc0), dev(vc0)
+    bt, sl = dev(c.block_tables), dev(c.seq_lens)
+    ts = dev(slots)
+    msl = int(c.seq_lens.max())
+    rng = np.random.default_rng(94)
+    kn = torch.zeros((chunk, shape.kv, shape.d), dtype=torch.float16, device="cuda")
+    vn = torch.zeros_like(kn)
+    dims = sk.dims_of(kc, vc, U, W)
+    ws_a = sk.alloc_workspace(sk.append_workspace_size(dims, chunk), "cuda")
+    ws_d = sk.alloc_workspace(sk.decode_workspace_size(dims, B, msl), "cuda")
+    out = torch.empty((B, shape.H, shape.d), dtype=torch.float16, device="cuda")
+    note(f"graph capture of append ({chunk} tokens) + decode")
+
+    def step(o):
+        sk.append(kn, vn, U, W, ts, kc, vc, workspace=ws_a)
+        sk.decode_attn(q, kc, vc, U, W, bt, sl, msl, case.scale, out=o, workspace=ws_d)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(out)
+    for rep in range(4):
+        qn = rng.standard_normal(case.q.shape, dtype=np.float32).astype(np.float16)
+        knn = rng.standard_normal(tuple(kn.shape), dtype=np.float32).astype(np.float16)
+        vnn = rng.standard_normal(tuple(vn.shape), dtype=np.float32).astype(np.float16)
+        q.copy_(torch.from_numpy(qn))
+        kn.copy_(torch.from_numpy(knn))
+        vn.copy_(torch.from_numpy(vnn))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        assert int(torch.count_nonzero(ws_a[:256]).item()) == 0
+        eager = torch.empty_like(out)
+        step(eager)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        okc, ovc = oracle.append(knn, vnn, case.U, case.W, slots, kc0, vc0)
+        ref = oracle.decode(qn, okc, ovc, case.U, case.W, c.block_tables, c.seq_lens, case.scale)
+        assert_parity(got, ref, f"step graph replay {rep}")
