@@ -1,4 +1,4 @@
-"""Low-batch decode captured in a HIP graph: the decode call launches kernels
+"""Decode, serving and prefill steps captured in HIP graphs: the calls launch kernels
 only (no allocation, no memset, no host synchronisation), so a caller can
 capture one step on its stream and replay it.  The test replays the graph
 several times, with eager work and synchronisations between the replays and
@@ -125,3 +125,63 @@ def test_serving_step_graph_replays(sk, chunk):
         okc, ovc = oracle.append(knn, vnn, case.U, case.W, slots, kc0, vc0)
         ref = oracle.decode(qn, okc, ovc, case.U, case.W, c.block_tables, c.seq_lens, case.scale)
         assert_parity(got, ref, f"step graph replay {rep}")
+
+
+@pytest.mark.parametrize("shape", [wl.MAIN, wl.LOWRANK], ids=["main_fused_upprojection", "lowrank_upprojection_kernel"])
+def test_prefill_step_graph_replays(sk, shape):
+    """A chunked-prefill step (append of the chunks, then attention; the main
+    shape applies W_h in the attention epilogue, the lower rank profile in a
+    launch of its own) captured as one graph and replayed with new chunk
+    tokens: each replay bit-identical to the eager step and within the bars."""
+    case = wl.make_prefill_case(shape, [100, 700], [40, 90], seed=95)
+    c = case.cache
+    kc0, vc0 = c.k_cache.copy(), c.v_cache.copy()
+    U, W = dev(case.U), dev(case.W)
+    kc, vc = dev(kc0), dev(vc0)
+    bt, sl, qsl = dev(c.block_tables), dev(c.seq_lens), dev(case.query_start_loc)
+    ts = dev(case.slot_mapping)
+    T = int(case.query_start_loc[-1])
+    mq = int(np.diff(case.query_start_loc).max())
+    msl = int(c.seq_lens.max())
+    q = torch.zeros(tuple(case.q.shape), dtype=torch.float16, device="cuda")
+    kn = torch.zeros(tuple(case.k_new.shape), dtype=torch.float16, device="cuda")
+    vn = torch.zeros_like(kn)
+    dims = sk.dims_of(kc, vc, U, W, num_heads=shape.H)
+    ws_a = sk.alloc_workspace(sk.append_workspace_size(dims, T), "cuda")
+    ws_p = sk.alloc_workspace(sk.prefill_workspace_size(dims, len(case.query_start_loc) - 1, T,
+                                                        msl), "cuda")
+    out = torch.empty((T, shape.H, shape.d), dtype=torch.float16, device="cuda")
+    note(f"graph capture of append + prefill {shape}")
+
+    def step(o):
+        sk.append(kn, vn, U, W, ts, kc, vc, workspace=ws_a)
+        sk.prefill_attn(q, qsl, mq, kc, vc, U, W, bt, sl, msl, case.scale, out=o, workspace=ws_p)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(out)
+    rng = np.random.default_rng(96)
+    for rep in range(3):
+        qn = rng.standard_normal(tuple(q.shape), dtype=np.float32).astype(np.float16)
+        knn = rng.standard_normal(tuple(kn.shape), dtype=np.float32).astype(np.float16)
+        vnn = rng.standard_normal(tuple(vn.shape), dtype=np.float32).astype(np.float16)
+        q.copy_(torch.from_numpy(qn))
+        kn.copy_(torch.from_numpy(knn))
+        vn.copy_(torch.from_numpy(vnn))
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        eager = torch.empty_like(out)
+        step(eager)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        okc, ovc = oracle.append(knn, vnn, case.U, case.W, case.slot_mapping, kc0, vc0)
+        ref = oracle.prefill(qn, case.query_start_loc, okc, ovc, case.U, case.W, c.block_tables,
+                             c.seq_lens, case.scale)
+        assert_parity(got, ref, f"prefill step graph replay {rep}")
