@@ -102,15 +102,15 @@ constexpr int PBS = 16;                 // tokens per page
 constexpr int kChunk = 64;              // block-id ring: 2 * kChunk entries
 constexpr float kRaise = 8.f;           // lazy-rescale threshold (log2 units)
 
-// Template knobs (tuning aids):
+// Template parameters chosen per instance:
 //   PPS    pages per step: one LDS barrier, one block-id read and one
 //          rescale check per PPS pages
 //   DEPTH  steps of page operands held in the register ring (2 or 3)
-//   SCHED  instruction order inside a step: 0 left to the compiler, 1 score
-//          products, then the P.c_v products, then the softmax, 2 as 1 with
-//          the softmax's vector instructions interleaved between the products,
-//          3 as 1 with the step's loads issued after the products, 4 as 2
-//          with the step's loads interleaved between the products too
+//   SCHED  instruction order inside a step: 1 score products, then the P.c_v
+//          products, then the softmax (the tiny shape); 2 as 1 with the
+//          softmax's vector instructions interleaved between the products
+//          (the lower rank profile); 4 as 2 with the step's loads interleaved
+//          between the products too (the main shape)
 // FP8 E4M3 codes to fp16 (exact), two codes per instruction.
 __device__ __forceinline__ half8 e4m3x8_to_half8(uint32_t w0, uint32_t w1) {
   typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -577,7 +577,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
       }
       load_v(vr[(PH + DEPTH - 1) % DEPTH], id_v);
     };
-    if constexpr (SCHED != 3 && SCHED != 4) issue_loads();
+    static_assert(SCHED == 1 || SCHED == 2 || SCHED == 4, "instruction orders 1, 2 and 4");
+    if constexpr (SCHED != 4) issue_loads();
     float4v sacc[PPS][C::SUW];
     if constexpr (KLDS)
       score_products_lds((s + 1) % 3, sacc);
@@ -585,7 +586,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
       score_products(kr[(PH + 1) % DEPTH], sacc);
     const int buf = s & 1;
     rescale(buf);
-    if constexpr (SCHED >= 1) __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_sched_barrier(0);
     VSet vcur;
     to_vset(vcur, vr[PH]);
     if constexpr (SCHED == 4) {  // masks ahead of the interleaved region
@@ -598,14 +599,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
     } else {
       value_products(MASKED, vcur, id_c, s, buf);
     }
-    if constexpr (SCHED == 3) {
-      // the loads go out behind the products: the per-CU load path is the
-      // busiest resource, and its back-pressure then stalls the wave while
-      // the matrix cores are busy rather than before they start
-      __builtin_amdgcn_sched_barrier(0);
-      issue_loads();
-    }
-    if constexpr (SCHED == 1 || SCHED == 3) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SCHED == 1) __builtin_amdgcn_sched_barrier(0);
     bool ok_s[PPS];
 #pragma unroll
     for (int pg = 0; pg < PPS; ++pg) ok_s[pg] = id_s[pg] >= 0;
