@@ -40,6 +40,7 @@ constexpr int kGenThreads = 256;
 constexpr int kGenHG = 8;   // heads per work group
 constexpr int kGenFJ = 8;   // feature slots per thread: r_v <= 2048
 constexpr int kGenBS = 16;  // tokens per page
+constexpr int kGenSB = 8;   // key-row chunks a thread requests together
 
 struct GenArgs {
   int H, Hkv, D, RK, RV, QG;
@@ -78,28 +79,36 @@ __device__ __forceinline__ void gen_row(const GenArgs& a, int row, int& tb, int&
   L = a.seq_lens[lo] - (a.qsl[lo + 1] - row) + 1;
 }
 
-// One latent as float: fp16, or an E4M3 code (exact in fp16).
+// Eight latents as loaded (fp16, or E4M3 codes), and their float values:
+// the loads of a batch are requested as raw registers and widened when used.
 template <bool FP8>
-__device__ __forceinline__ void load8(const void* base, size_t idx, float (&x)[8]) {
-  if constexpr (FP8) {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 w = *(const u32x2*)((const uint8_t*)base + idx);
-    typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const half2v lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[k], 1.0f, false);
-      const half2v hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[k], 1.0f, true);
-      x[4 * k + 0] = (float)lo[0];
-      x[4 * k + 1] = (float)lo[1];
-      x[4 * k + 2] = (float)hi[0];
-      x[4 * k + 3] = (float)hi[1];
-    }
-  } else {
-    const half8 h = *(const half8*)((const half_t*)base + idx);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (float)h[e];
+struct Raw8 {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  std::conditional_t<FP8, u32x2, half8> r;
+  __device__ __forceinline__ void load(const void* base, size_t idx) {
+    if constexpr (FP8)
+      r = *(const u32x2*)((const uint8_t*)base + idx);
+    else
+      r = *(const half8*)((const half_t*)base + idx);
   }
-}
+  __device__ __forceinline__ void widen(float (&x)[8]) const {
+    if constexpr (FP8) {
+      typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const half2v lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[k], 1.0f, false);
+        const half2v hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[k], 1.0f, true);
+        x[4 * k + 0] = (float)lo[0];
+        x[4 * k + 1] = (float)lo[1];
+        x[4 * k + 2] = (float)hi[0];
+        x[4 * k + 3] = (float)hi[1];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (float)r[e];
+    }
+  }
+};
 
 // z of one head (LDS, fp32, RV values) -> out[row, h, :] = scale * W_g z,
 // one output per thread and round.
@@ -158,20 +167,36 @@ __global__ __launch_bounds__(kGenThreads) void generic_split_kernel(GenArgs a) {
     const int blk = bt[p];
     const int nv = ((unsigned)blk < (unsigned)a.num_blocks) ? min(kGenBS, L - p * kGenBS) : 0;
     if (nv <= 0) continue;  // uniform: an invalid block id masks its page
-    // scores of (head hh, token t)
-    if (tid < nh * kGenBS) {
-      const int hh = tid / kGenBS, t = tid % kGenBS;
-      const int g = (h0 + hh) / a.QG;
+    // scores of (head hh, token t): two neighbouring threads per pair, each
+    // taking every other 8-rank chunk of the key row.  A batch's chunks are
+    // requested together (addresses clamped into the row, so no branch
+    // separates the loads) and summed afterwards, one memory round trip per
+    // kGenSB chunks instead of one per chunk.
+    {
+      const int pair = tid >> 1, half = tid & 1;
+      const int hh = min(pair / kGenBS, kGenHG - 1), t = pair % kGenBS;
+      const int g = min(h0 + hh, a.H - 1) / a.QG;
       const size_t kb = (((size_t)blk * a.Hkv + g) * kGenBS + t) * a.RK;
       const float* qv = sq + hh * a.RK;
+      const int nch = a.RK / 8;
       float sc = 0.f;
-      for (int r = 0; r < a.RK; r += 8) {
-        float x[8];
-        load8<FP8>(a.k_cache, kb + r, x);
+      for (int c0 = 0; c0 < nch; c0 += 2 * kGenSB) {  // uniform
+        Raw8<FP8> x[kGenSB];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sc = __builtin_fmaf(qv[r + e], x[e], sc);
+        for (int i = 0; i < kGenSB; ++i) x[i].load(a.k_cache, kb + (size_t)min(c0 + half + 2 * i, nch - 1) * 8);
+#pragma unroll
+        for (int i = 0; i < kGenSB; ++i) {
+          const int c = c0 + half + 2 * i;
+          if (c < nch) {
+            float xf[8];
+            x[i].widen(xf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sc = __builtin_fmaf(qv[c * 8 + e], xf[e], sc);
+          }
+        }
       }
-      sS[hh * kGenBS + t] = t < nv ? sc : -INFINITY;
+      sc += __shfl_xor(sc, 1);
+      if (half == 0 && pair < nh * kGenBS) sS[hh * kGenBS + t] = t < nv ? sc : -INFINITY;
     }
     __syncthreads();
     // online softmax of each head (log2 domain)
@@ -191,19 +216,26 @@ __global__ __launch_bounds__(kGenThreads) void generic_split_kernel(GenArgs a) {
       sA[tid] = alpha;
     }
     __syncthreads();
-    // P.c_v: this thread's features of every head of the group
+    // P.c_v: this thread's features of every head of the group.  The value
+    // columns of all its features are requested first (feature indices
+    // clamped into range, so no branch separates the loads), then used.
+    {
+      Raw8<FP8> xv[kGenFJ][2];
 #pragma unroll
-    for (int j = 0; j < kGenFJ; ++j) {
-      const int f = tid + kGenThreads * j;
-      if (f < a.RV) {
-        float cv[kGenBS];
-        float x[8];
-        load8<FP8>(a.v_cache, ((size_t)blk * a.RV + f) * kGenBS, x);
+      for (int j = 0; j < kGenFJ; ++j) {
+        const int f = min(tid + kGenThreads * j, a.RV - 1);
+        xv[j][0].load(a.v_cache, ((size_t)blk * a.RV + f) * kGenBS);
+        xv[j][1].load(a.v_cache, ((size_t)blk * a.RV + f) * kGenBS + 8);
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cv[e] = e < nv ? x[e] : 0.f;  // slots past the end may be NaN
-        load8<FP8>(a.v_cache, ((size_t)blk * a.RV + f) * kGenBS + 8, x);
+      for (int j = 0; j < kGenFJ; ++j) {
+        if (tid + kGenThreads * j >= a.RV) continue;
+        float cv[kGenBS], c0[8], c1[8];
+        xv[j][0].widen(c0);
+        xv[j][1].widen(c1);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cv[8 + e] = 8 + e < nv ? x[e] : 0.f;
+        for (int t = 0; t < kGenBS; ++t)  // slots past the end may be NaN
+          cv[t] = t < nv ? (t < 8 ? c0[t] : c1[t - 8]) : 0.f;
 #pragma unroll
         for (int hh = 0; hh < kGenHG; ++hh) {
           if (hh < nh) {
