@@ -6,7 +6,9 @@ d = 128, r_k = 64 per head, joint r_v = 512, 16-token pages, fp16 storage.
 
     python bench.py [--steps K] [--warmup W] [--workload decode_b16] [--no-cpu]
 
-Prints ONE JSON line.  Timing: every step is preceded (outside the timed
+Prints ONE JSON line.  By default 20 untimed warm-up steps, then 200 timed
+ones (the median, p10 and p90 are reported beside the mean).  Timing: every
+step is preceded (outside the timed
 events) by a 512 MiB read sweep that evicts the 256 MB Infinity Cache, so
 each step reads its latents from HBM; each step is bracketed by HIP events on
 the stream the library launches on.  The split-K kernel alone is timed by
@@ -101,8 +103,8 @@ def read_traffic(per_launch_algorithmic_bytes):
 def parse_args(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_b16",
                     choices=["decode_b16", "decode_b64", "long_b20", "tiny"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
@@ -146,18 +148,39 @@ def make_inputs(name):
     return case, t
 
 
+def host_cpu_info():
+    """The host the CPU oracle runs on: the cores this process may use, the
+    CPU model, and numpy's BLAS library with its thread count (the oracle's
+    matrix products run there)."""
+    info = {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": None,
+            "blas": None, "blas_threads": int(os.environ.get("OMP_NUM_THREADS", "1"))}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+            info["blas_threads"] = int(max(p.get("num_threads", 1) for p in blas))
+    except Exception:
+        pass
+    return info
+
+
 def cpu_baseline(case, budget_s):
     """The fp64 oracle, as it stands, on the first sequences of the same
     workload until about budget_s seconds of CPU work are spent."""
     import numpy as np
     import oracle
     from rank_compressed_paged_amd import metrics
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                       if p.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    host = host_cpu_info()
+    threads = host["blas_threads"]
     c = case.cache
     sh = case.shape
     done, spent, tokens = 0, 0.0, 0
@@ -172,7 +195,7 @@ def cpu_baseline(case, budget_s):
         done += 1
     lat = tokens * metrics.latent_bytes_per_token(sh.H, sh.r_k, sh.r_v)
     return {"value": round(lat / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "host": host,
             "sample": f"{done} sequence decodes cycling over the {case.B} sequences of one "
                       f"{case.name} step ({tokens} cached tokens, {done / case.B:.1f} steps' "
                       f"worth), {spent:.1f} s, fp64 numpy rebuild-then-attend",
@@ -304,12 +327,8 @@ def cpu_prefill_baseline(pc, budget_s):
     import numpy as np
     import oracle
     from rank_compressed_paged_amd import metrics
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                       if p.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    host = host_cpu_info()
+    threads = host["blas_threads"]
     sh, c = pc.shape, pc.cache
     qsl = pc.query_start_loc
     B = len(qsl) - 1
@@ -329,7 +348,7 @@ def cpu_prefill_baseline(pc, budget_s):
         done += 1
     total = metrics.prefill_flops(pc.cached_lens, np.diff(qsl), sh.H, sh.d, sh.r_k, sh.r_v)
     return {"value": round(flops / spent / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "host": host,
             "sample": f"{done} whole requests of the {B} of one {pc.name} call "
                       f"({done / B:.2f} calls' worth), {spent:.1f} s, fp64 numpy "
                       f"rebuild-then-attend",
