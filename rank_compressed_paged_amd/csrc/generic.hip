@@ -9,10 +9,12 @@
 // These kernels take every size at run time, so a model whose layers use
 // other ranks (the README's rank profiles and learned per-layer ranks), other
 // head counts or head sizes, or other grouped-query groups, runs without a
-// compiled instance of its own.  They are written for clarity over speed:
-// scores and P.c_v run on the vector ALU in fp32, each work group covers at
-// most 8 heads (so a value page is read once per group of 8 heads), and a
-// prefill query is a row of its own that walks its causal prefix.
+// compiled instance of its own.  The attention itself is written for
+// clarity over speed: scores and P.c_v run on the vector ALU in fp32, each
+// work group covers at most 8 heads (so a value page is read once per group
+// of 8 heads), and a prefill query is a row of its own that walks its causal
+// prefix.  The q projection and the merge's up-projection run on the matrix
+// cores.
 //
 // Limits (checked on the host): d a multiple of 32 up to 256; r_k a multiple
 // of 8 up to min(d, 256); r_v a multiple of 8 up to min(2048, Hkv * d).
@@ -110,20 +112,58 @@ struct Raw8 {
   }
 };
 
-// z of one head (LDS, fp32, RV values) -> out[row, h, :] = scale * W_g z,
-// one output per thread and round.
+// Sum over the 64 lanes of a wave.
+__device__ __forceinline__ float gen_wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+__device__ __forceinline__ float gen_wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+
+// z of one head (LDS, fp32, RV values) -> out[row, h, :] = scale * W_g z.
+// Wave w takes output rows w, w + 4, ...; its lanes split each W row into
+// 16-byte pieces (lane l: features 8l + 512j), so a load instruction reads
+// 1 KiB of one row, and a row's products are summed across the wave.  Four
+// rows' loads are requested together; z stays in registers (zero past RV).
+constexpr int kGenUpRows = 4;   // rows whose loads are in flight together
+constexpr int kGenUpParts = 4;  // 512-feature parts of a row: RV <= 2048
 __device__ __forceinline__ void gen_upproject(const GenArgs& a, const float* z, int row, int h,
                                               float scale) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int NWV = kGenThreads / 64;
   const int g = h / a.QG;
-  for (int i = threadIdx.x; i < a.D; i += kGenThreads) {
-    const half_t* wr = a.W + ((size_t)g * a.D + i) * a.RV;
-    float o = 0.f;
-    for (int f = 0; f < a.RV; f += 8) {
-      const half8 w8 = *(const half8*)(wr + f);
+  float zr[kGenUpParts][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o = __builtin_fmaf((float)w8[e], z[f + e], o);
+  for (int j = 0; j < kGenUpParts; ++j) {
+    const int f = 8 * lane + 512 * j;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zr[j][e] = f < a.RV ? z[f + e] : 0.f;
+  }
+  const half_t* Wg = a.W + (size_t)g * a.D * a.RV;
+  for (int i0 = w; i0 < a.D; i0 += NWV * kGenUpRows) {  // uniform
+    half8 wv[kGenUpRows][kGenUpParts];
+#pragma unroll
+    for (int k = 0; k < kGenUpRows; ++k) {
+      const int i = min(i0 + NWV * k, a.D - 1);
+#pragma unroll
+      for (int j = 0; j < kGenUpParts; ++j)
+        wv[k][j] = *(const half8*)(Wg + (size_t)i * a.RV + min(8 * lane + 512 * j, a.RV - 8));
     }
-    a.out[((size_t)row * a.H + h) * a.D + i] = (half_t)(o * scale);
+#pragma unroll
+    for (int k = 0; k < kGenUpRows; ++k) {
+      float o = 0.f;
+#pragma unroll
+      for (int j = 0; j < kGenUpParts; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o = __builtin_fmaf((float)wv[k][j][e], zr[j][e], o);
+      o = gen_wave_sum(o);
+      const int i = i0 + NWV * k;
+      if (lane == 0 && i < a.D) a.out[((size_t)row * a.H + h) * a.D + i] = (half_t)(o * scale);
+    }
   }
 }
 
@@ -290,124 +330,261 @@ __global__ __launch_bounds__(kGenThreads) void generic_split_kernel(GenArgs a) {
   }
 }
 
-// Merge of the splits and the up-projection, one work group per (row, head):
-// z = sum_s w_s z_s / sum_s w_s l_s with w_s = 2^(m_s - M), M the largest
-// running max of the row's splits (splits past the row's pages are never
-// written and never read), then out = v_scale * W_g z.
-__global__ __launch_bounds__(kGenThreads) void generic_merge_kernel(GenArgs a) {
+// Merge of the splits and the up-projection for TB rows (TB <= kGenMT) of one
+// head, so each W_g row is fetched once per TB rows:
+//  1. wave t < TB takes row t: M = max_s m_s and the weights w_s = 2^(m_s -
+//     M) of its written splits (splits past the row's pages are never written
+//     and never read), the denominator sum_s w_s l_s, by cross-lane sums;
+//  2. z[t, f] = sum_s w_s z_s[f] / denominator into LDS (fp32), kGenSB
+//     splits' values of four (row, feature) pairs requested together;
+//  3. out[t, h, :] = v_scale * W_g z[t] on the matrix cores:
+//     v_mfma_f32_16x16x32_f16 with A = 16 rows of W_g x 32 features (16
+//     contiguous bytes per lane, straight from memory) and B column 2t + e =
+//     part e of an fp16 hi/lo split of z[t] (hi + lo = z to about 2^-22);
+//     the two parts' sums are added by a neighbour-lane exchange.  Wave w
+//     owns output tiles w, w + 8, ... (TPW of them); W moves in batches of
+//     8 / TPW chunks of each tile, double-buffered in registers, and the
+//     first batch is requested before step 1, so W is in flight during the
+//     merge.
+constexpr int kGenMT = 4;          // rows per merge work group, at most
+constexpr int kGenMergeThreads = 512;  // eight waves
+template <int TPW>
+__global__ __launch_bounds__(kGenMergeThreads) void generic_merge_kernel(GenArgs a, int tb) {
+  static_assert(TPW == 1 || TPW == 2, "output tiles per wave");
+  constexpr int KB = 8 / TPW;  // chunks per batch
   extern __shared__ __attribute__((aligned(16))) float gsm[];
-  const int row = blockIdx.x, h = blockIdx.y;
-  const int tid = threadIdx.x;
-  int tb, L;
-  gen_row(a, row, tb, L);
-  const int n_pages = min((L + kGenBS - 1) / kGenBS, a.max_blocks);
-  const int ns = (n_pages + a.pages_per_split - 1) / a.pages_per_split;  // splits written
   const int S = a.num_splits;
-  float* sw = gsm;              // [S] weights
-  float* sred = sw + S;         // [kGenThreads] reduction
-  float* sZ = sred + kGenThreads;  // [RV]
-  const float* mp = a.ml + ((size_t)row * a.H + h) * 2 * S;
-  // M = max_s m_s
-  float mx = -INFINITY;
-  for (int s = tid; s < ns; s += kGenThreads) mx = fmaxf(mx, mp[s]);
-  sred[tid] = mx;
-  __syncthreads();
-  for (int w = kGenThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) sred[tid] = fmaxf(sred[tid], sred[tid + w]);
-    __syncthreads();
-  }
-  const float M = sred[0];
-  __syncthreads();
-  float den = 0.f;
-  for (int s = tid; s < ns; s += kGenThreads) {
-    const float m = mp[s];
-    const float w = m == -INFINITY ? 0.f : exp2f(m - M);
-    sw[s] = w;
-    den += w * mp[S + s];
-  }
-  sred[tid] = den;
-  __syncthreads();
-  for (int w = kGenThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) sred[tid] += sred[tid + w];
-    __syncthreads();
-  }
-  const float inv = sred[0] > 0.f ? 1.f / sred[0] : 0.f;
-  const float* zp = a.zpart + ((size_t)row * a.H + h) * S * a.RV;
-  for (int f = tid; f < a.RV; f += kGenThreads) {
-    float z = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float w = sw[s];
-      if (w != 0.f) z = __builtin_fmaf(w, zp[(size_t)s * a.RV + f], z);
+  float* sZ = gsm;                  // [tb][RV]
+  float* sw = sZ + tb * a.RV;       // [tb][S]
+  float* sInv = sw + tb * S;        // [tb]
+  int* sNs = (int*)(sInv + tb);     // [tb]
+  const int r0 = blockIdx.x * tb, h = blockIdx.y;
+  const int nt = min(tb, a.rows - r0);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, quad = lane >> 4;
+  const int ntiles = a.D / 16, nck = (a.RV + 31) / 32, nb = (nck + KB - 1) / KB;
+  const half_t* Wg = a.W + (size_t)(h / a.QG) * a.D * a.RV;
+  // W batch b: chunks KB*b .. of this wave's tiles (rows and features
+  // clamped into W_g; the products ignore what lies past them)
+  auto load_batch = [&](half8 (&dst)[TPW][KB], int b) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int orow = min((w + 8 * i) * 16 + col, a.D - 1);
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int f = min(32 * (KB * b + k) + 8 * quad, a.RV - 8);
+        dst[i][k] = *(const half8*)(Wg + (size_t)orow * a.RV + f);
+      }
     }
-    sZ[f] = z * inv;
+  };
+  half8 wa0[TPW][KB], wa1[TPW][KB];
+  load_batch(wa0, 0);
+  // 1. weights
+  if (w < nt) {  // uniform per wave
+    const int row = r0 + w;
+    int tbx, L;
+    gen_row(a, row, tbx, L);
+    const int n_pages = min((L + kGenBS - 1) / kGenBS, a.max_blocks);
+    // a length past the call's bound must not reach past the row's splits
+    const int ns = min((n_pages + a.pages_per_split - 1) / a.pages_per_split, S);
+    const float* mp = a.ml + ((size_t)row * a.H + h) * 2 * S;
+    float mx = -INFINITY;
+    for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, mp[s]);
+    mx = gen_wave_max(mx);
+    float den = 0.f;
+    for (int s = lane; s < ns; s += 64) {
+      const float m = mp[s];
+      const float ws = m == -INFINITY ? 0.f : exp2f(m - mx);
+      sw[w * S + s] = ws;
+      den += ws * mp[S + s];
+    }
+    den = gen_wave_sum(den);
+    if (lane == 0) {
+      sInv[w] = den > 0.f ? 1.f / den : 0.f;
+      sNs[w] = ns;
+    }
   }
   __syncthreads();
-  gen_upproject(a, sZ, row, h, a.v_scale);
+  // 2. z of the rows
+  int ns_max = 0;
+  for (int t = 0; t < nt; ++t) ns_max = max(ns_max, sNs[t]);
+  const int pairs = nt * a.RV;
+  for (int p0 = tid; p0 < pairs; p0 += 4 * kGenMergeThreads) {  // uniform trip count
+    float x[4][kGenSB], z[4];
+    int t4[4], f4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pp = min(p0 + u * kGenMergeThreads, pairs - 1);
+      t4[u] = pp / a.RV;
+      f4[u] = pp % a.RV;
+      z[u] = 0.f;
+    }
+    for (int s0 = 0; s0 < ns_max; s0 += kGenSB) {  // uniform
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int ns = sNs[t4[u]];
+        const float* zp = a.zpart + ((size_t)(r0 + t4[u]) * a.H + h) * S * a.RV + f4[u];
+#pragma unroll
+        for (int i = 0; i < kGenSB; ++i)
+          x[u][i] = zp[(size_t)max(min(s0 + i, ns - 1), 0) * a.RV];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int ns = sNs[t4[u]];
+#pragma unroll
+        for (int i = 0; i < kGenSB; ++i) {
+          const float ws = s0 + i < ns ? sw[t4[u] * S + s0 + i] : 0.f;
+          if (ws != 0.f) z[u] = __builtin_fmaf(ws, x[u][i], z[u]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (p0 + u * kGenMergeThreads < pairs) sZ[t4[u] * a.RV + f4[u]] = z[u] * sInv[t4[u]];
+  }
+  __syncthreads();
+  // 3. up-projection
+  const int tcol = col >> 1, part = col & 1;
+  float4v acc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) acc[i] = zero4();
+  auto compute_batch = [&](const half8 (&src)[TPW][KB], int b) {
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int c = KB * b + k;
+      const int f = 32 * c + 8 * quad;
+      half8 bz = {};
+      if (tcol < nt && f < a.RV) {
+        const float4v z0 = *(const float4v*)&sZ[tcol * a.RV + f];
+        const float4v z1 = *(const float4v*)&sZ[tcol * a.RV + f + 4];
+        half8 hi, lo;
+        split_f16x8(z0, z1, hi, lo);
+        bz = part ? lo : hi;
+      }
+#pragma unroll
+      for (int i = 0; i < TPW; ++i)  // features past RV: B is zero there
+        if (w + 8 * i < ntiles && c < nck) acc[i] = mfma16x16x32(src[i][k], bz, acc[i]);
+    }
+  };
+  for (int b = 0; b < nb; b += 2) {  // uniform
+    if (b + 1 < nb) load_batch(wa1, b + 1);
+    compute_batch(wa0, b);
+    if (b + 1 < nb) {
+      if (b + 2 < nb) load_batch(wa0, b + 2);
+      compute_batch(wa1, b + 1);
+    }
+  }
+  // lanes 2t and 2t+1 hold the hi and lo sums of row t
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int tile = w + 8 * i;
+    if (tile >= ntiles) break;  // uniform
+    float4v o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] = acc[i][r] + xor_lane_small<1>(acc[i][r]);
+    if (part == 0 && tcol < nt) {
+      half4 hv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hv[r] = (half_t)(o[r] * a.v_scale);
+      *(half4*)(a.out + ((size_t)(r0 + tcol) * a.H + h) * a.D + tile * 16 + 4 * quad) = hv;
+    }
+  }
 }
 
-// q~[n, h, :] = qscale * U_g^T q[n, h, :] (fp32): work group (16 tokens, h);
-// the tokens' q rows are staged in LDS as fp32 and U_g in chunks of 32 rows
-// (16-byte loads, the next chunk in flight), thread r accumulates rank r of
-// all 16 tokens over d in order.
+// ds_read_b64_tr_b16: within each 16-lane group, lane q addresses row
+// r0 + q/4, columns c0 + 4*(q%4); lane i then receives rows r0 .. r0+3 of
+// column c0 + i.
+typedef short gen_short4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ half4 gen_tr16(const half_t* p) {
+  typedef __attribute__((address_space(3))) gen_short4v lds_short4v;
+  const gen_short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)p);
+  return __builtin_bit_cast(half4, r);
+}
+
+// q~[n, h, :] = qscale * U_g^T q[n, h, :] (fp32) on the matrix cores:
+// v_mfma_f32_16x16x32_f16 with A = U_g^T (16 ranks x 32 of d, read from LDS
+// through the transposing read) and B = q^T (32 of d x 16 tokens, 16
+// contiguous bytes of a q row per lane); the fp16 products are exact and the
+// sums fp32.  Work group (TW*16 tokens, head h), four waves: wave w takes
+// token group w % TW and the rank tiles w / TW, w / TW + 4/TW, ...  U_g
+// passes through LDS in 32-row chunks (ranks padded to a multiple of 16 with
+// zeros), the next chunk in flight while the current one is used.
+constexpr int kGenQK = 32;                   // rows of U_g per chunk
+constexpr int kGenQLd = 256 + 8;             // LDS row stride (halves)
+template <int TW>
 __global__ __launch_bounds__(kGenThreads) void generic_qproj_kernel(
     const half_t* __restrict__ q, const half_t* __restrict__ U, int n_tokens, int H, int QG,
     int D, int RK, float qscale, float* __restrict__ qt) {
-  constexpr int TT = 16;  // tokens per work group
-  constexpr int KC = 32;  // rows of U_g per staged chunk
-  __shared__ float sq[TT][256];
-  __shared__ __attribute__((aligned(16))) half_t sU[2][KC][256];
-  const int tid = threadIdx.x;
-  const int h = blockIdx.y, n0 = blockIdx.x * TT;
-  const int g = h / QG;
-  for (int i = tid; i < TT * D; i += kGenThreads) {
-    const int tt = i / D, k = i % D;
-    const int n = n0 + tt;
-    sq[tt][k] = n < n_tokens ? (float)q[((size_t)n * H + h) * D + k] : 0.f;
-  }
-  // U_g moves through LDS in chunks of KC rows, the next chunk's 16-byte
-  // pieces in flight while the current one is used (at most 4 per thread)
+  static_assert(TW == 1 || TW == 4, "one or four 16-token groups per work group");
+  constexpr int RP = 4 / TW;        // waves per token group
+  constexpr int SLOTS = 16 / RP;    // rank tiles per wave: r_k <= 256
+  __shared__ __attribute__((aligned(16))) half_t sU[2][kGenQK][kGenQLd];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, quad = lane >> 4;
+  const int h = blockIdx.y, g = h / QG;
+  const int tg = w % TW, rp = w / TW;
+  const int n = blockIdx.x * TW * 16 + tg * 16 + col;  // this lane's token (B column)
+  const int ntile = (RK + 15) / 16, nc = D / kGenQK;
+  // the q rows of this wave's tokens, all chunks (rows past the end mirror
+  // the last token and are not stored)
+  half8 bq[256 / kGenQK];
+  const half_t* qrow = q + ((size_t)min(n, n_tokens - 1) * H + h) * D + quad * 8;
+#pragma unroll
+  for (int c = 0; c < 256 / kGenQK; ++c)
+    if (c < nc) bq[c] = *(const half8*)(qrow + c * kGenQK);
+  // U_g chunk staging: 16-byte pieces of RK/8 per row; ranks RK .. 16*ntile
+  // are zero
   const half_t* Ug = U + (size_t)g * D * RK;
-  const int pieces = KC * (RK / 8);
+  const int ppr = 2 * ntile;              // pieces per staged row
+  const int pieces = kGenQK * ppr;        // <= 1024: four per thread
   half8 pre[4];
   auto fetch = [&](int c) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int idx = tid + j * kGenThreads;
-      if (idx < pieces)
-        pre[j] = *(const half8*)(Ug + (size_t)(c * KC + idx / (RK / 8)) * RK + (idx % (RK / 8)) * 8);
+      const int r = idx / ppr, pc = idx % ppr;
+      const half8 z = {};
+      pre[j] = (idx < pieces && 8 * pc < RK) ? *(const half8*)(Ug + (size_t)(c * kGenQK + r) * RK + 8 * pc) : z;
     }
   };
   auto stage = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int idx = tid + j * kGenThreads;
-      if (idx < pieces) *(half8*)&sU[buf][idx / (RK / 8)][(idx % (RK / 8)) * 8] = pre[j];
+      if (idx < pieces) *(half8*)&sU[buf][idx / ppr][8 * (idx % ppr)] = pre[j];
     }
   };
+  float4v acc[SLOTS];
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) acc[i] = zero4();
   fetch(0);
   stage(0);
   __syncthreads();
-  const int nc = D / KC;
-  float acc[TT];
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) acc[tt] = 0.f;
-  for (int c = 0; c < nc; ++c) {
+  for (int c = 0; c < 256 / kGenQK; ++c) {
+    if (c >= nc) break;  // uniform
     if (c + 1 < nc) fetch(c + 1);
-    if (tid < RK) {  // thread r = tid accumulates rank r of the 16 tokens
-#pragma unroll 4
-      for (int k = 0; k < KC; ++k) {
-        const float u = (float)sU[c & 1][k][tid];
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) acc[tt] = __builtin_fmaf(sq[tt][c * KC + k], u, acc[tt]);
+    for (int i = 0; i < SLOTS; ++i) {
+      const int rt = rp + RP * i;
+      if (rt < ntile) {  // uniform
+        const half_t* ap = &sU[c & 1][quad * 8 + (col >> 2)][rt * 16 + 4 * (col & 3)];
+        const half4 a0 = gen_tr16(ap), a1 = gen_tr16(ap + 4 * kGenQLd);
+        const half8 au = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        acc[i] = mfma16x16x32(au, bq[c], acc[i]);
       }
     }
     if (c + 1 < nc) stage((c + 1) & 1);
     __syncthreads();
   }
-  if (tid < RK) {
+  // D[4*quad + e][col] = rank 16 rt + 4 quad + e of token col
+  if (n < n_tokens) {
+    float* dst = qt + ((size_t)n * H + h) * RK;
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-      if (n0 + tt < n_tokens) qt[((size_t)(n0 + tt) * H + h) * RK + tid] = acc[tt] * qscale;
+    for (int i = 0; i < SLOTS; ++i) {
+      const int r0 = 16 * (rp + RP * i) + 4 * quad;
+      if (r0 < RK) *(float4v*)(dst + r0) = acc[i] * qscale;
+    }
   }
 }
 
@@ -422,9 +599,16 @@ int generic_head_groups(const ShapeKey& s) { return (s.H + kGenHG - 1) / kGenHG;
 hipError_t launch_generic_qproj(const ShapeKey& s, const void* q, const void* U, int n_tokens,
                                 float scale, void* qt, int precedes, hipStream_t st) {
   if (n_tokens <= 0) return hipSuccess;
-  launch_hooked(TIME_NONE, precedes, generic_qproj_kernel, dim3((n_tokens + 15) / 16, s.H),
-                dim3(kGenThreads), st, (const half_t*)q, (const half_t*)U, n_tokens, s.H,
-                s.H / s.Hkv, s.d, s.rk, scale * kLog2e, (float*)qt);
+  // few tokens (a decode step): a work group per 16 tokens and head, its
+  // waves sharing the rank tiles; many: 64 tokens per work group
+  if (n_tokens < 256)
+    launch_hooked(TIME_NONE, precedes, generic_qproj_kernel<1>, dim3((n_tokens + 15) / 16, s.H),
+                  dim3(kGenThreads), st, (const half_t*)q, (const half_t*)U, n_tokens, s.H,
+                  s.H / s.Hkv, s.d, s.rk, scale * kLog2e, (float*)qt);
+  else
+    launch_hooked(TIME_NONE, precedes, generic_qproj_kernel<4>, dim3((n_tokens + 63) / 64, s.H),
+                  dim3(kGenThreads), st, (const half_t*)q, (const half_t*)U, n_tokens, s.H,
+                  s.H / s.Hkv, s.d, s.rk, scale * kLog2e, (float*)qt);
   return hipGetLastError();
 }
 
@@ -477,8 +661,22 @@ hipError_t launch_generic_attn(const ShapeKey& s, const void* qt, const int32_t*
                       dim3(kGenThreads), lds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || fused) return e;
-  const size_t mlds = sizeof(float) * ((size_t)num_splits + kGenThreads + s.rv);
-  hipLaunchKernelGGL(generic_merge_kernel, dim3(rows, s.H), dim3(kGenThreads), mlds, st, a);
+  // rows per merge work group: several rows share each fetch of W_g once
+  // there are enough (row, head) pairs to keep the CUs busy, as long as
+  // their z and weights fit 64 KiB of LDS
+  const long pairs = (long)rows * s.H;
+  int tb = pairs >= 1024 ? kGenMT : (pairs >= 256 ? 2 : 1);
+  auto merge_lds = [&](int t) {
+    return sizeof(float) * ((size_t)t * s.rv + (size_t)t * num_splits + 2 * (size_t)t);
+  };
+  while (tb > 1 && merge_lds(tb) > 65536) tb /= 2;
+  const size_t mlds = merge_lds(tb);
+  const dim3 mgrid((rows + tb - 1) / tb, s.H);
+  const int tiles = s.d / 16;  // output tiles of 16 over the 8 waves: d <= 256
+  if (tiles <= 8)
+    hipLaunchKernelGGL(generic_merge_kernel<1>, mgrid, dim3(kGenMergeThreads), mlds, st, a, tb);
+  else
+    hipLaunchKernelGGL(generic_merge_kernel<2>, mgrid, dim3(kGenMergeThreads), mlds, st, a, tb);
   return hipGetLastError();
 }
 
