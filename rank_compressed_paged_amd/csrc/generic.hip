@@ -43,6 +43,7 @@ constexpr int kGenHG = 8;   // heads per work group
 constexpr int kGenFJ = 8;   // feature slots per thread: r_v <= 2048
 constexpr int kGenBS = 16;  // tokens per page
 constexpr int kGenSB = 8;   // key-row chunks a thread requests together
+constexpr int kGenVH = 4;   // feature slots whose value columns are requested at a page's top
 
 struct GenArgs {
   int H, Hkv, D, RK, RV, QG;
@@ -188,12 +189,18 @@ __global__ __launch_bounds__(kGenThreads) void generic_split_kernel(GenArgs a) {
   float* sS = sq + kGenHG * a.RK;    // [kGenHG][16] scores of the page
   float* sP = sS + kGenHG * kGenBS;  // [kGenHG][16] weights of the page
   float* sA = sP + kGenHG * kGenBS;  // [kGenHG] rescale factors, then sums
-  float* sZ = sA + kGenHG;           // [RV] normalised z of one head (one split only)
+  int* sBlk = (int*)(sA + kGenHG);   // [kGenThreads] block ids of the split
+  float* sZ = (float*)(sBlk + kGenThreads);  // [RV] normalised z of one head (one split only)
 
   for (int i = tid; i < kGenHG * a.RK; i += kGenThreads) {
     const int hh = i / a.RK, r = i % a.RK;
     sq[i] = hh < nh ? a.qt[((size_t)row * a.H + h0 + hh) * a.RK + r] : 0.f;
   }
+  // the split's block ids, staged once when they fit (one vector load per
+  // thread); longer splits read the table page by page
+  const int32_t* bt = a.block_tables + (size_t)tb * a.max_blocks;
+  const bool ids_lds = a.pages_per_split <= kGenThreads;  // uniform
+  if (ids_lds) sBlk[tid] = p0 + tid < p1 ? bt[p0 + tid] : 0;
   float m_run = -INFINITY, l_run = 0.f;  // thread hh < nh: head hh's softmax state
   float acc[kGenHG][kGenFJ];
 #pragma unroll
@@ -202,92 +209,125 @@ __global__ __launch_bounds__(kGenThreads) void generic_split_kernel(GenArgs a) {
     for (int j = 0; j < kGenFJ; ++j) acc[hh][j] = 0.f;
   __syncthreads();
 
-  const int32_t* bt = a.block_tables + (size_t)tb * a.max_blocks;
+  // Pages run as a software pipeline: while page p is processed, the first
+  // 2*kGenSB key chunks of page p+1 are requested (once p's scores are
+  // formed), p's value columns at its top, and the barriers inside the loop
+  // order LDS only, so these requests stay in flight across them.  An
+  // invalid block id reads block 0 and masks its page.
+  auto block_at = [&](int p) {
+    const int v = ids_lds ? __builtin_amdgcn_readfirstlane(sBlk[p - p0]) : bt[p];
+    return v;
+  };
+  // scores of (head hh, token t): two neighbouring threads per pair, each
+  // taking every other 8-rank chunk of the key row; a batch's chunks are
+  // requested together (addresses clamped into the row, so no branch
+  // separates the loads) and summed afterwards
+  const int pair = tid >> 1, half = tid & 1;
+  const int hh_s = min(pair / kGenBS, kGenHG - 1), t_s = pair % kGenBS;
+  const int g_s = min(h0 + hh_s, a.H - 1) / a.QG;
+  const int nch = a.RK / 8;
+  const float* qv = sq + hh_s * a.RK;
+  auto load_keys = [&](Raw8<FP8> (&x)[kGenSB], int blk, int c0) {
+    const size_t kb = (((size_t)blk * a.Hkv + g_s) * kGenBS + t_s) * a.RK;
+#pragma unroll
+    for (int i = 0; i < kGenSB; ++i) x[i].load(a.k_cache, kb + (size_t)min(c0 + half + 2 * i, nch - 1) * 8);
+  };
+  auto dot_keys = [&](const Raw8<FP8> (&x)[kGenSB], int c0, float sc) {
+#pragma unroll
+    for (int i = 0; i < kGenSB; ++i) {
+      const int c = c0 + half + 2 * i;
+      if (c < nch) {
+        float xf[8];
+        x[i].widen(xf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc = __builtin_fmaf(qv[c * 8 + e], xf[e], sc);
+      }
+    }
+    return sc;
+  };
+  auto loadable = [&](int blk) { return (unsigned)blk < (unsigned)a.num_blocks ? blk : 0; };
+  Raw8<FP8> kc[kGenSB], kn[kGenSB];
+  int blk_c = p0 < p1 ? block_at(p0) : 0;
+  if (p0 < p1) load_keys(kc, loadable(blk_c), 0);
   for (int p = p0; p < p1; ++p) {
-    const int blk = bt[p];
-    const int nv = ((unsigned)blk < (unsigned)a.num_blocks) ? min(kGenBS, L - p * kGenBS) : 0;
-    if (nv <= 0) continue;  // uniform: an invalid block id masks its page
-    // scores of (head hh, token t): two neighbouring threads per pair, each
-    // taking every other 8-rank chunk of the key row.  A batch's chunks are
-    // requested together (addresses clamped into the row, so no branch
-    // separates the loads) and summed afterwards, one memory round trip per
-    // kGenSB chunks instead of one per chunk.
-    {
-      const int pair = tid >> 1, half = tid & 1;
-      const int hh = min(pair / kGenBS, kGenHG - 1), t = pair % kGenBS;
-      const int g = min(h0 + hh, a.H - 1) / a.QG;
-      const size_t kb = (((size_t)blk * a.Hkv + g) * kGenBS + t) * a.RK;
-      const float* qv = sq + hh * a.RK;
-      const int nch = a.RK / 8;
-      float sc = 0.f;
-      for (int c0 = 0; c0 < nch; c0 += 2 * kGenSB) {  // uniform
-        Raw8<FP8> x[kGenSB];
+    const int nv = ((unsigned)blk_c < (unsigned)a.num_blocks) ? min(kGenBS, L - p * kGenBS) : 0;
+    const int blk = loadable(blk_c);
+    const int blk_n = p + 1 < p1 ? block_at(p + 1) : 0;
+    // this page's value columns, feature slots 0 .. kGenVH-1 (indices
+    // clamped into range; slots wholly past RV are not requested); slots
+    // from kGenVH on (RV > kGenVH * 256) are loaded where they are used
+    Raw8<FP8> xv[kGenVH][2];
+    auto load_values = [&](int jb) {
 #pragma unroll
-        for (int i = 0; i < kGenSB; ++i) x[i].load(a.k_cache, kb + (size_t)min(c0 + half + 2 * i, nch - 1) * 8);
-#pragma unroll
-        for (int i = 0; i < kGenSB; ++i) {
-          const int c = c0 + half + 2 * i;
-          if (c < nch) {
-            float xf[8];
-            x[i].widen(xf);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sc = __builtin_fmaf(qv[c * 8 + e], xf[e], sc);
-          }
+      for (int j = 0; j < kGenVH; ++j) {
+        if (kGenThreads * (jb + j) < a.RV) {  // uniform
+          const int f = min(tid + kGenThreads * (jb + j), a.RV - 1);
+          xv[j][0].load(a.v_cache, ((size_t)blk * a.RV + f) * kGenBS);
+          xv[j][1].load(a.v_cache, ((size_t)blk * a.RV + f) * kGenBS + 8);
         }
       }
+    };
+    load_values(0);
+    float sc = dot_keys(kc, 0, 0.f);
+    for (int c0 = 2 * kGenSB; c0 < nch; c0 += 2 * kGenSB) {  // r_k > 128: the rest in place
+      Raw8<FP8> x[kGenSB];
+      load_keys(x, blk, c0);
+      sc = dot_keys(x, c0, sc);
+    }
+    if (p + 1 < p1) load_keys(kn, loadable(blk_n), 0);
+    if (nv > 0) {  // uniform: an invalid block id masks its page
       sc += __shfl_xor(sc, 1);
-      if (half == 0 && pair < nh * kGenBS) sS[hh * kGenBS + t] = t < nv ? sc : -INFINITY;
-    }
-    __syncthreads();
-    // online softmax of each head (log2 domain)
-    if (tid < nh) {
-      float mx = m_run;
-      for (int t = 0; t < kGenBS; ++t) mx = fmaxf(mx, sS[tid * kGenBS + t]);
-      const float alpha = (mx == m_run) ? 1.f : exp2f(m_run - mx);  // 0 on the first page
-      float ps = 0.f;
-      for (int t = 0; t < kGenBS; ++t) {
-        const float sc = sS[tid * kGenBS + t];
-        const float pt = sc == -INFINITY ? 0.f : exp2f(sc - mx);
-        sP[tid * kGenBS + t] = pt;
-        ps += pt;
+      if (half == 0 && pair < nh * kGenBS) sS[hh_s * kGenBS + t_s] = t_s < nv ? sc : -INFINITY;
+      block_sync_lds();
+      // online softmax of each head (log2 domain)
+      if (tid < nh) {
+        float mx = m_run;
+        for (int t = 0; t < kGenBS; ++t) mx = fmaxf(mx, sS[tid * kGenBS + t]);
+        const float alpha = (mx == m_run) ? 1.f : exp2f(m_run - mx);  // 0 on the first page
+        float ps = 0.f;
+        for (int t = 0; t < kGenBS; ++t) {
+          const float sv = sS[tid * kGenBS + t];
+          const float pt = sv == -INFINITY ? 0.f : exp2f(sv - mx);
+          sP[tid * kGenBS + t] = pt;
+          ps += pt;
+        }
+        l_run = l_run * alpha + ps;
+        m_run = mx;
+        sA[tid] = alpha;
       }
-      l_run = l_run * alpha + ps;
-      m_run = mx;
-      sA[tid] = alpha;
-    }
-    __syncthreads();
-    // P.c_v: this thread's features of every head of the group.  The value
-    // columns of all its features are requested first (feature indices
-    // clamped into range, so no branch separates the loads), then used.
-    {
-      Raw8<FP8> xv[kGenFJ][2];
+      block_sync_lds();
+      // P.c_v: this thread's features of every head of the group
 #pragma unroll
-      for (int j = 0; j < kGenFJ; ++j) {
-        const int f = min(tid + kGenThreads * j, a.RV - 1);
-        xv[j][0].load(a.v_cache, ((size_t)blk * a.RV + f) * kGenBS);
-        xv[j][1].load(a.v_cache, ((size_t)blk * a.RV + f) * kGenBS + 8);
-      }
+      for (int jb = 0; jb < kGenFJ; jb += kGenVH) {
+        if (kGenThreads * jb >= a.RV) break;  // uniform
+        if (jb > 0) load_values(jb);
 #pragma unroll
-      for (int j = 0; j < kGenFJ; ++j) {
-        if (tid + kGenThreads * j >= a.RV) continue;
-        float cv[kGenBS], c0[8], c1[8];
-        xv[j][0].widen(c0);
-        xv[j][1].widen(c1);
+        for (int jj = 0; jj < kGenVH; ++jj) {
+          const int j = jb + jj;
+          if (kGenThreads * j >= a.RV) break;  // uniform
+          if (tid + kGenThreads * j >= a.RV) continue;
+          float cv[kGenBS], c0[8], c1[8];
+          xv[jj][0].widen(c0);
+          xv[jj][1].widen(c1);
 #pragma unroll
-        for (int t = 0; t < kGenBS; ++t)  // slots past the end may be NaN
-          cv[t] = t < nv ? (t < 8 ? c0[t] : c1[t - 8]) : 0.f;
+          for (int t = 0; t < kGenBS; ++t)  // slots past the end may be NaN
+            cv[t] = t < nv ? (t < 8 ? c0[t] : c1[t - 8]) : 0.f;
 #pragma unroll
-        for (int hh = 0; hh < kGenHG; ++hh) {
-          if (hh < nh) {
-            float v = acc[hh][j] * sA[hh];
+          for (int hh = 0; hh < kGenHG; ++hh) {
+            if (hh < nh) {
+              float v = acc[hh][j] * sA[hh];
 #pragma unroll
-            for (int t = 0; t < kGenBS; ++t) v = __builtin_fmaf(sP[hh * kGenBS + t], cv[t], v);
-            acc[hh][j] = v;
+              for (int t = 0; t < kGenBS; ++t) v = __builtin_fmaf(sP[hh * kGenBS + t], cv[t], v);
+              acc[hh][j] = v;
+            }
           }
         }
       }
+      block_sync_lds();  // the next page rewrites sS, sP, sA
     }
-    __syncthreads();  // the next page rewrites sS, sP, sA
+#pragma unroll
+    for (int i = 0; i < kGenSB; ++i) kc[i] = kn[i];
+    blk_c = blk_n;
   }
 
   if (!fused) {
@@ -613,9 +653,9 @@ hipError_t launch_generic_qproj(const ShapeKey& s, const void* q, const void* U,
 }
 
 // LDS of the split kernel: q~, scores, weights, factors, and one head's z
-// when fused (at most 17.4 KiB within the limits).
+// when fused, and the split's block ids (at most 18.4 KiB within the limits).
 static size_t split_lds(const ShapeKey& s, bool fused) {
-  return sizeof(float) * ((size_t)kGenHG * s.rk + 2 * kGenHG * kGenBS + kGenHG +
+  return sizeof(float) * ((size_t)kGenHG * s.rk + 2 * kGenHG * kGenBS + kGenHG + kGenThreads +
                           (fused ? (size_t)s.rv : 0));
 }
 
