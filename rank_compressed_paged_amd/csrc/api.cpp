@@ -122,9 +122,9 @@ static DecodePlan with_finish(DecodePlan p, const ShapeKey& s, int batch, int fo
 // otherwise a function of the shape, batch, length bound and device only.
 constexpr double kSplitCost = 6.0;
 
-// Split plan of the generic kernels: about two work groups per CU over the
-// batch, its head groups and the splits, at most 4096 splits; a caller's
-// pages_per_split is kept unless it would exceed that.
+// Split plan of the generic kernels: about one work group (eight waves) per
+// CU over the batch, its head groups and the splits, at most 4096 splits; a
+// caller's pages_per_split is kept unless it would exceed that.
 static DecodePlan plan_generic(const ShapeKey& s, int batch, int max_seq_len, int bs,
                                int force_pps) {
   DecodePlan p{1, 1, 1, 4, 256, 1};
@@ -136,7 +136,7 @@ static DecodePlan plan_generic(const ShapeKey& s, int batch, int max_seq_len, in
     pps = force_pps;
   } else {
     const long per_split = (long)batch * generic_head_groups(s);
-    const int want = cdiv(2L * device_cus(), per_split);
+    const int want = cdiv((long)device_cus(), per_split);
     pps = cdiv(pages, want < 1 ? 1 : (want > pages ? pages : want));
   }
   if (cdiv(pages, pps) > 4096) pps = cdiv(pages, 4096);

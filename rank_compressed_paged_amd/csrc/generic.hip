@@ -9,12 +9,12 @@
 // These kernels take every size at run time, so a model whose layers use
 // other ranks (the README's rank profiles and learned per-layer ranks), other
 // head counts or head sizes, or other grouped-query groups, runs without a
-// compiled instance of its own.  The attention itself is written for
-// clarity over speed: scores and P.c_v run on the vector ALU in fp32, each
-// work group covers at most 8 heads (so a value page is read once per group
-// of 8 heads), and a prefill query is a row of its own that walks its causal
-// prefix.  The q projection and the merge's up-projection run on the matrix
-// cores.
+// compiled instance of its own.  They trade speed for generality where
+// the tuned kernels do not: scores run on the vector ALU in fp32, each work
+// group covers at most 16 heads (so a value page is read once per group of
+// 16 heads), and a prefill query is a row of its own that walks its causal
+// prefix.  P.c_v, the q projection and the merge's up-projection run on the
+// matrix cores.
 //
 // Limits (checked on the host): d a multiple of 32 up to 256; r_k a multiple
 // of 8 up to min(d, 256); r_v a multiple of 8 up to min(2048, Hkv * d).
@@ -24,13 +24,17 @@
 // query_start_loc[b+1]), which sees the first P0 + j + 1 tokens of request b,
 // j = n - query_start_loc[b], P0 = seq_lens[b] - C_b.
 //
-// Work group (split s, row, head group): it streams its pages one at a time.
-// Per 16-token page, thread (head hh, token t) forms one score; thread hh runs
-// the online-softmax update of its head (running max, rescale factor, sum)
-// and writes the page's weights to LDS; every thread then updates its own
-// (head, feature) accumulators, features tid + 256 j.  With one split the
-// work group also normalises z and applies W_g; otherwise it writes its
-// running max and sum (fp32) and its unnormalised z (fp32) for the merge.
+// Work group (split s, row, group of 16 heads), eight waves: it streams its
+// pages one at a time.  Per 16-token page, two neighbouring threads per
+// (head hh, token t) form one score from fp32 q~ in LDS and the key row; the
+// 16 lanes of head h run its online-softmax update (running max, rescale
+// factor, sum) with cross-lane reductions and write the page's weights to
+// LDS in fp16; then P.c_v runs as v_mfma_f32_16x16x16_f16 with the
+// feature-major value page as A (4 tokens of one feature per lane) and the
+// weights as B (tokens x heads), wave w owning feature tiles w, w + 8, ...
+// With one split the work group also normalises z and applies W_g;
+// otherwise it writes its running max and sum (fp32) and its unnormalised z
+// (fp32) for the merge.
 #include <type_traits>
 
 #include "common.h"
@@ -39,11 +43,11 @@
 namespace starkv {
 
 constexpr int kGenThreads = 256;
-constexpr int kGenHG = 8;   // heads per work group
-constexpr int kGenFJ = 8;   // feature slots per thread: r_v <= 2048
+constexpr int kGenSHG = 16;        // heads per split work group
+constexpr int kGenSThreads = 512;  // split work group: eight waves
+constexpr int kGenFT = 16;         // 16-feature tiles per wave of the split: r_v <= 2048
 constexpr int kGenBS = 16;  // tokens per page
 constexpr int kGenSB = 8;   // key-row chunks a thread requests together
-constexpr int kGenVH = 4;   // feature slots whose value columns are requested at a page's top
 
 struct GenArgs {
   int H, Hkv, D, RK, RV, QG;
@@ -135,7 +139,7 @@ constexpr int kGenUpParts = 4;  // 512-feature parts of a row: RV <= 2048
 __device__ __forceinline__ void gen_upproject(const GenArgs& a, const float* z, int row, int h,
                                               float scale) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  constexpr int NWV = kGenThreads / 64;
+  constexpr int NWV = kGenSThreads / 64;  // called by the split kernel's work groups
   const int g = h / a.QG;
   float zr[kGenUpParts][8];
 #pragma unroll
@@ -168,15 +172,17 @@ __device__ __forceinline__ void gen_upproject(const GenArgs& a, const float* z, 
   }
 }
 
-template <bool FP8>
-__global__ __launch_bounds__(kGenThreads) void generic_split_kernel(GenArgs a) {
+template <bool FP8, int NFT>
+__global__ __launch_bounds__(kGenSThreads) void generic_split_kernel(GenArgs a) {
+  static_assert(NFT == kGenFT || NFT == kGenFT / 2, "feature tiles per wave: r_v <= 128 * NFT");
   extern __shared__ __attribute__((aligned(16))) float gsm[];
-  const int n_hg = (a.H + kGenHG - 1) / kGenHG;
+  const int n_hg = (a.H + kGenSHG - 1) / kGenSHG;
   const int row = blockIdx.x / n_hg, hg = blockIdx.x % n_hg;
   const int s = blockIdx.y;
-  const int h0 = hg * kGenHG;
-  const int nh = min(kGenHG, a.H - h0);
-  const int tid = threadIdx.x;
+  const int h0 = hg * kGenSHG;
+  const int nh = min(kGenSHG, a.H - h0);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, quad = lane >> 4;
   int tb, L;
   gen_row(a, row, tb, L);
   const int n_pages = min((L + kGenBS - 1) / kGenBS, a.max_blocks);
@@ -185,45 +191,42 @@ __global__ __launch_bounds__(kGenThreads) void generic_split_kernel(GenArgs a) {
   const bool fused = a.num_splits == 1;
   if (!fused && p0 >= n_pages) return;  // whole work group, before any barrier
 
-  float* sq = gsm;                   // [kGenHG][RK] q~ of the group's heads
-  float* sS = sq + kGenHG * a.RK;    // [kGenHG][16] scores of the page
-  float* sP = sS + kGenHG * kGenBS;  // [kGenHG][16] weights of the page
-  float* sA = sP + kGenHG * kGenBS;  // [kGenHG] rescale factors, then sums
-  int* sBlk = (int*)(sA + kGenHG);   // [kGenThreads] block ids of the split
-  float* sZ = (float*)(sBlk + kGenThreads);  // [RV] normalised z of one head (one split only)
+  float* sq = gsm;                           // [16][RK] q~ of the group's heads
+  float* sS = sq + kGenSHG * a.RK;           // [2][16 heads][16 tokens] scores
+  float* sA = sS + 2 * kGenSHG * kGenBS;     // [2][16] rescale factors
+  half_t* sPh = (half_t*)(sA + 2 * kGenSHG);  // [2][16 heads][16 tokens] weights, fp16
+  int* sBlk = (int*)(sPh + 2 * kGenSHG * kGenBS);  // [kGenSThreads] block ids of the split
+  float* sZ = (float*)(sBlk + kGenSThreads);  // [RV] normalised z of one head (one split only)
 
-  for (int i = tid; i < kGenHG * a.RK; i += kGenThreads) {
+  for (int i = tid; i < kGenSHG * a.RK; i += kGenSThreads) {
     const int hh = i / a.RK, r = i % a.RK;
     sq[i] = hh < nh ? a.qt[((size_t)row * a.H + h0 + hh) * a.RK + r] : 0.f;
   }
   // the split's block ids, staged once when they fit (one vector load per
   // thread); longer splits read the table page by page
   const int32_t* bt = a.block_tables + (size_t)tb * a.max_blocks;
-  const bool ids_lds = a.pages_per_split <= kGenThreads;  // uniform
+  const bool ids_lds = a.pages_per_split <= kGenSThreads;  // uniform
   if (ids_lds) sBlk[tid] = p0 + tid < p1 ? bt[p0 + tid] : 0;
-  float m_run = -INFINITY, l_run = 0.f;  // thread hh < nh: head hh's softmax state
-  float acc[kGenHG][kGenFJ];
+  // softmax state of head sh = 4w + lane/16 (waves 0-3), kept by its 16 lanes
+  const int sh = 4 * w + (lane >> 4), st = lane & 15;
+  float m_run = -INFINITY, l_run = 0.f;
+  // z^T accumulators: feature tile ft = w + 8i holds features 16 ft + 4 quad
+  // .. +3 of head col (the 16x16 product's layout)
+  const int ntv = (a.RV + 15) / 16;
+  float4v acc[NFT];
 #pragma unroll
-  for (int hh = 0; hh < kGenHG; ++hh)
-#pragma unroll
-    for (int j = 0; j < kGenFJ; ++j) acc[hh][j] = 0.f;
+  for (int i = 0; i < NFT; ++i) acc[i] = zero4();
   __syncthreads();
 
-  // Pages run as a software pipeline: while page p is processed, the first
-  // 2*kGenSB key chunks of page p+1 are requested (once p's scores are
-  // formed), p's value columns at its top, and the barriers inside the loop
-  // order LDS only, so these requests stay in flight across them.  An
-  // invalid block id reads block 0 and masks its page.
   auto block_at = [&](int p) {
-    const int v = ids_lds ? __builtin_amdgcn_readfirstlane(sBlk[p - p0]) : bt[p];
-    return v;
+    return ids_lds ? __builtin_amdgcn_readfirstlane(sBlk[p - p0]) : bt[p];
   };
   // scores of (head hh, token t): two neighbouring threads per pair, each
   // taking every other 8-rank chunk of the key row; a batch's chunks are
   // requested together (addresses clamped into the row, so no branch
   // separates the loads) and summed afterwards
   const int pair = tid >> 1, half = tid & 1;
-  const int hh_s = min(pair / kGenBS, kGenHG - 1), t_s = pair % kGenBS;
+  const int hh_s = pair / kGenBS, t_s = pair % kGenBS;
   const int g_s = min(h0 + hh_s, a.H - 1) / a.QG;
   const int nch = a.RK / 8;
   const float* qv = sq + hh_s * a.RK;
@@ -246,123 +249,149 @@ __global__ __launch_bounds__(kGenThreads) void generic_split_kernel(GenArgs a) {
     return sc;
   };
   auto loadable = [&](int blk) { return (unsigned)blk < (unsigned)a.num_blocks ? blk : 0; };
+  // a lane's value operand: tokens 4 quad .. +3 of feature 16 ft + col
+  typedef std::conditional_t<FP8, uint32_t, half4> VRaw;
+  auto load_val = [&](int blk, int ft) {
+    const int f = min(16 * ft + col, a.RV - 1);
+    const size_t idx = ((size_t)blk * a.RV + f) * kGenBS + 4 * quad;
+    if constexpr (FP8)
+      return *(const uint32_t*)((const uint8_t*)a.v_cache + idx);
+    else
+      return *(const half4*)((const half_t*)a.v_cache + idx);
+  };
+  auto to_half4 = [&](VRaw v) {
+    if constexpr (FP8) {
+      typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+      const half2v lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
+      const half2v hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, true);
+      return half4{lo[0], lo[1], hi[0], hi[1]};
+    } else {
+      return v;
+    }
+  };
+
+  // Pages run as a software pipeline: at the top of page p, the first
+  // 2*kGenSB key chunks and the value operands of page p+1 are requested,
+  // and the barriers order LDS only, so these requests stay in flight while
+  // page p is processed.  Scores, weights and
+  // factors alternate between two LDS buffers, so two barriers a page
+  // suffice.  An invalid block id reads block 0 and masks its page.
+  // page p's first key chunks and value operands (kc, vc), and page p+1's
+  // (kn, vn), requested at the top of page p
+  // (fp16 values at r_v > 1024 have no registers for two pages: they are
+  // requested at their own page's top)
+  constexpr bool VLA = FP8 || NFT < kGenFT;
   Raw8<FP8> kc[kGenSB], kn[kGenSB];
+  VRaw vc[NFT], vn[VLA ? NFT : 1];
+  auto load_vals = [&](auto& dst, int blk) {
+#pragma unroll
+    for (int i = 0; i < NFT; ++i)
+      if (w + 8 * i < ntv) dst[i] = load_val(blk, w + 8 * i);  // uniform
+  };
   int blk_c = p0 < p1 ? block_at(p0) : 0;
-  if (p0 < p1) load_keys(kc, loadable(blk_c), 0);
+  if (p0 < p1) {
+    load_keys(kc, loadable(blk_c), 0);
+    if constexpr (VLA) load_vals(vc, loadable(blk_c));
+  }
   for (int p = p0; p < p1; ++p) {
+    const int buf = (p - p0) & 1;
     const int nv = ((unsigned)blk_c < (unsigned)a.num_blocks) ? min(kGenBS, L - p * kGenBS) : 0;
     const int blk = loadable(blk_c);
     const int blk_n = p + 1 < p1 ? block_at(p + 1) : 0;
-    // this page's value columns, feature slots 0 .. kGenVH-1 (indices
-    // clamped into range; slots wholly past RV are not requested); slots
-    // from kGenVH on (RV > kGenVH * 256) are loaded where they are used
-    Raw8<FP8> xv[kGenVH][2];
-    auto load_values = [&](int jb) {
-#pragma unroll
-      for (int j = 0; j < kGenVH; ++j) {
-        if (kGenThreads * (jb + j) < a.RV) {  // uniform
-          const int f = min(tid + kGenThreads * (jb + j), a.RV - 1);
-          xv[j][0].load(a.v_cache, ((size_t)blk * a.RV + f) * kGenBS);
-          xv[j][1].load(a.v_cache, ((size_t)blk * a.RV + f) * kGenBS + 8);
-        }
-      }
-    };
-    load_values(0);
+    if constexpr (!VLA) load_vals(vc, blk);
+    if (p + 1 < p1) {  // uniform
+      load_keys(kn, loadable(blk_n), 0);
+      if constexpr (VLA) load_vals(vn, loadable(blk_n));
+    }
     float sc = dot_keys(kc, 0, 0.f);
     for (int c0 = 2 * kGenSB; c0 < nch; c0 += 2 * kGenSB) {  // r_k > 128: the rest in place
       Raw8<FP8> x[kGenSB];
       load_keys(x, blk, c0);
       sc = dot_keys(x, c0, sc);
     }
-    if (p + 1 < p1) load_keys(kn, loadable(blk_n), 0);
     if (nv > 0) {  // uniform: an invalid block id masks its page
       sc += __shfl_xor(sc, 1);
-      if (half == 0 && pair < nh * kGenBS) sS[hh_s * kGenBS + t_s] = t_s < nv ? sc : -INFINITY;
+      if (half == 0)
+        sS[(buf * kGenSHG + hh_s) * kGenBS + t_s] = (hh_s < nh && t_s < nv) ? sc : -INFINITY;
       block_sync_lds();
-      // online softmax of each head (log2 domain)
-      if (tid < nh) {
-        float mx = m_run;
-        for (int t = 0; t < kGenBS; ++t) mx = fmaxf(mx, sS[tid * kGenBS + t]);
+      // online softmax (log2 domain): head sh on the 16 lanes of its group,
+      // lane st = token; the weights are rounded to fp16 for the products
+      // and summed as rounded
+      if (w < 4) {  // uniform
+        const float sv = sS[(buf * kGenSHG + sh) * kGenBS + st];
+        float mx = sv;
+#pragma unroll
+        for (int m = 8; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+        mx = fmaxf(mx, m_run);
         const float alpha = (mx == m_run) ? 1.f : exp2f(m_run - mx);  // 0 on the first page
-        float ps = 0.f;
-        for (int t = 0; t < kGenBS; ++t) {
-          const float sv = sS[tid * kGenBS + t];
-          const float pt = sv == -INFINITY ? 0.f : exp2f(sv - mx);
-          sP[tid * kGenBS + t] = pt;
-          ps += pt;
-        }
+        const half_t ph = (half_t)(sv == -INFINITY ? 0.f : exp2f(sv - mx));
+        sPh[(buf * kGenSHG + sh) * kGenBS + st] = ph;
+        float ps = (float)ph;
+#pragma unroll
+        for (int m = 8; m >= 1; m >>= 1) ps += __shfl_xor(ps, m);
         l_run = l_run * alpha + ps;
         m_run = mx;
-        sA[tid] = alpha;
+        if (st == 0) sA[buf * kGenSHG + sh] = alpha;
       }
       block_sync_lds();
-      // P.c_v: this thread's features of every head of the group
+      // P.c_v on the matrix cores: A = value operands (feature x token), B =
+      // weights (token x head), column = head col
+      const half4 pb = *(const half4*)&sPh[(buf * kGenSHG + col) * kGenBS + 4 * quad];
+      const float al = sA[buf * kGenSHG + col];
+      const bool part = nv < kGenBS;  // uniform: tokens past the end may hold NaN
 #pragma unroll
-      for (int jb = 0; jb < kGenFJ; jb += kGenVH) {
-        if (kGenThreads * jb >= a.RV) break;  // uniform
-        if (jb > 0) load_values(jb);
+      for (int i = 0; i < NFT; ++i) {
+        if (w + 8 * i < ntv) {  // uniform
+          half4 av = to_half4(vc[i]);
+          if (part) {
 #pragma unroll
-        for (int jj = 0; jj < kGenVH; ++jj) {
-          const int j = jb + jj;
-          if (kGenThreads * j >= a.RV) break;  // uniform
-          if (tid + kGenThreads * j >= a.RV) continue;
-          float cv[kGenBS], c0[8], c1[8];
-          xv[jj][0].widen(c0);
-          xv[jj][1].widen(c1);
-#pragma unroll
-          for (int t = 0; t < kGenBS; ++t)  // slots past the end may be NaN
-            cv[t] = t < nv ? (t < 8 ? c0[t] : c1[t - 8]) : 0.f;
-#pragma unroll
-          for (int hh = 0; hh < kGenHG; ++hh) {
-            if (hh < nh) {
-              float v = acc[hh][j] * sA[hh];
-#pragma unroll
-              for (int t = 0; t < kGenBS; ++t) v = __builtin_fmaf(sP[hh * kGenBS + t], cv[t], v);
-              acc[hh][j] = v;
-            }
+            for (int e = 0; e < 4; ++e) av[e] = 4 * quad + e < nv ? av[e] : (half_t)0.f;
           }
+          acc[i] = mfma16x16x16(av, pb, acc[i] * al);
         }
       }
-      block_sync_lds();  // the next page rewrites sS, sP, sA
     }
 #pragma unroll
     for (int i = 0; i < kGenSB; ++i) kc[i] = kn[i];
+    if constexpr (VLA) {
+#pragma unroll
+      for (int i = 0; i < NFT; ++i) vc[i] = vn[i];
+    }
     blk_c = blk_n;
   }
+  __syncthreads();  // the loop's LDS buffers are reused below
 
   if (!fused) {
     // partial state of this split: running max and sum per head, and the
     // unnormalised z rows
-    if (tid < nh) {
-      float* mp = a.ml + ((size_t)row * a.H + h0 + tid) * 2 * a.num_splits + s;
+    if (w < 4 && st == 0 && sh < nh) {
+      float* mp = a.ml + ((size_t)row * a.H + h0 + sh) * 2 * a.num_splits + s;
       mp[0] = m_run;
       mp[a.num_splits] = l_run;
     }
+    if (col < nh) {
+      float* zp = a.zpart + (((size_t)row * a.H + h0 + col) * a.num_splits + s) * a.RV;
 #pragma unroll
-    for (int hh = 0; hh < kGenHG; ++hh) {
-      if (hh >= nh) break;
-      float* zp = a.zpart + (((size_t)row * a.H + h0 + hh) * a.num_splits + s) * a.RV;
-#pragma unroll
-      for (int j = 0; j < kGenFJ; ++j) {
-        const int f = tid + kGenThreads * j;
-        if (f < a.RV) zp[f] = acc[hh][j];
+      for (int i = 0; i < NFT; ++i) {
+        const int f0 = 16 * (w + 8 * i) + 4 * quad;
+        if (w + 8 * i < ntv && f0 < a.RV) *(float4v*)(zp + f0) = acc[i];
       }
     }
     return;
   }
   // one split: per head, z = acc / l (zero for an empty row) to LDS, then
   // out = W_g z
-  if (tid < nh) sA[tid] = l_run;
+  if (w < 4 && st == 0) sA[sh] = l_run;
   __syncthreads();
+  for (int hh = 0; hh < nh; ++hh) {  // uniform
+    if (col == hh) {
+      const float l = sA[hh];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-  for (int hh = 0; hh < kGenHG; ++hh) {
-    if (hh >= nh) break;  // uniform
-    const float l = sA[hh];
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-    for (int j = 0; j < kGenFJ; ++j) {
-      const int f = tid + kGenThreads * j;
-      if (f < a.RV) sZ[f] = acc[hh][j] * inv;
+      for (int i = 0; i < NFT; ++i) {
+        const int f0 = 16 * (w + 8 * i) + 4 * quad;
+        if (w + 8 * i < ntv && f0 < a.RV) *(float4v*)(sZ + f0) = acc[i] * inv;
+      }
     }
     __syncthreads();
     gen_upproject(a, sZ, row, h0 + hh, a.v_scale);
@@ -634,7 +663,7 @@ bool generic_shape_ok(const ShapeKey& s) {
          s.H % s.Hkv == 0 && s.H <= 4096;
 }
 
-int generic_head_groups(const ShapeKey& s) { return (s.H + kGenHG - 1) / kGenHG; }
+int generic_head_groups(const ShapeKey& s) { return (s.H + kGenSHG - 1) / kGenSHG; }
 
 hipError_t launch_generic_qproj(const ShapeKey& s, const void* q, const void* U, int n_tokens,
                                 float scale, void* qt, int precedes, hipStream_t st) {
@@ -652,11 +681,12 @@ hipError_t launch_generic_qproj(const ShapeKey& s, const void* q, const void* U,
   return hipGetLastError();
 }
 
-// LDS of the split kernel: q~, scores, weights, factors, and one head's z
-// when fused, and the split's block ids (at most 18.4 KiB within the limits).
+// LDS of the split kernel: q~, two buffers of scores, factors and fp16
+// weights, the split's block ids, and one head's z when fused (at most
+// 28.3 KiB within the limits).
 static size_t split_lds(const ShapeKey& s, bool fused) {
-  return sizeof(float) * ((size_t)kGenHG * s.rk + 2 * kGenHG * kGenBS + kGenHG + kGenThreads +
-                          (fused ? (size_t)s.rv : 0));
+  return sizeof(float) * ((size_t)kGenSHG * s.rk + 2 * kGenSHG * kGenBS + 2 * kGenSHG +
+                          kGenSHG * kGenBS + kGenSThreads + (fused ? (size_t)s.rv : 0));
 }
 
 hipError_t launch_generic_attn(const ShapeKey& s, const void* qt, const int32_t* qsl, int rows,
@@ -693,12 +723,23 @@ hipError_t launch_generic_attn(const ShapeKey& s, const void* qt, const int32_t*
   const bool fused = num_splits == 1;
   const dim3 grid((unsigned)((long)rows * generic_head_groups(s)), (unsigned)num_splits);
   const size_t lds = split_lds(s, fused);
-  if (fmt.fp8)
-    launch_hooked_lds(which, TIME_NONE, generic_split_kernel<true>, grid,
-                      dim3(kGenThreads), lds, st, a);
-  else
-    launch_hooked_lds(which, TIME_NONE, generic_split_kernel<false>, grid,
-                      dim3(kGenThreads), lds, st, a);
+  // feature tiles per wave: 8 cover r_v <= 1024, 16 the rest
+  const bool wide = s.rv > 8 * 16 * (kGenFT / 2);
+  if (fmt.fp8) {
+    if (wide)
+      launch_hooked_lds(which, TIME_NONE, generic_split_kernel<true, kGenFT>, grid,
+                        dim3(kGenSThreads), lds, st, a);
+    else
+      launch_hooked_lds(which, TIME_NONE, generic_split_kernel<true, kGenFT / 2>, grid,
+                        dim3(kGenSThreads), lds, st, a);
+  } else {
+    if (wide)
+      launch_hooked_lds(which, TIME_NONE, generic_split_kernel<false, kGenFT>, grid,
+                        dim3(kGenSThreads), lds, st, a);
+    else
+      launch_hooked_lds(which, TIME_NONE, generic_split_kernel<false, kGenFT / 2>, grid,
+                        dim3(kGenSThreads), lds, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || fused) return e;
   // rows per merge work group: several rows share each fetch of W_g once

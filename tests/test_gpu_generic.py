@@ -2,7 +2,7 @@
 limits at run time (d a multiple of 32 up to 256; r_k a multiple of 8 up to
 min(d, 256); r_v a multiple of 8 up to min(2048, Hkv d); Hkv dividing H):
 odd head counts and head sizes, per-layer rank profiles from r_k 16 to 128 and
-r_v 128 to 1024 (the README's learned per-layer ranks and its three profiles),
+r_v 128 to 2048 (the README's learned per-layer ranks and its three profiles),
 grouped-query groups of 2 and 8, and FP8 caches on profiles without a tuned FP8
 instance.  Same bars as the tuned kernels: max-abs 2e-3 and rel-L2 1e-3
 against the fp64 oracle, per (row, head) rel-L2 1e-3, bit-identical output
@@ -29,9 +29,11 @@ SHAPES = {
     "conservative_128_1024": S(H=32, d=128, r_k=128, r_v=1024),
     "d256": S(H=8, d=256, r_k=128, r_v=1024),
     "h3_d32_gqa": S(H=6, d=32, r_k=8, r_v=40, Hkv=3),
+    # r_v past 1024: the split kernel's wide instances (16 feature tiles per wave)
+    "wide_v_2048": S(H=16, d=128, r_k=32, r_v=2048),
 }
 # the profiles that also run FP8 caches on the generic kernels
-FP8_SHAPES = ["odd_h28_d96", "rank_96_768", "gqa_g2"]
+FP8_SHAPES = ["odd_h28_d96", "rank_96_768", "gqa_g2", "wide_v_2048"]
 
 
 @pytest.fixture(scope="module")
