@@ -127,6 +127,25 @@ def test_generic_decode_small_batch_long(sk):
     assert_parity(out, _dec_oracle(case), "generic b1 long")
 
 
+@pytest.mark.parametrize("name,batch", [("odd_h28_d96", 42), ("conservative_128_1024", 9)],
+                         ids=["rows_of_4", "rows_of_2"])
+def test_generic_decode_merge_row_tiles(sk, name, batch):
+    """Batches whose (row, head) pairs reach 1024 (odd_h28 x 42: the merge
+    takes four rows per work group, the last block two) or 256
+    (conservative x 9: two rows, the last block one), ragged lengths
+    including empty rows."""
+    rng = np.random.default_rng(120 + batch)
+    lens = [int(x) for x in rng.integers(0, 200, size=batch)]
+    lens[3] = 0
+    case = wl.make_decode_case(SHAPES[name], seq_lens=lens, seed=121)
+    note(f"generic decode merge rows {name} B={batch}")
+    out = _run_dec(sk, case)
+    ref = _dec_oracle(case)
+    assert_parity(out, ref, f"generic merge rows {name}")
+    per_head(out, ref, f"generic merge rows {name}")
+    assert torch.count_nonzero(out[3]).item() == 0
+
+
 def test_generic_block_table_permutation_is_bit_identical(sk):
     lens = [40, 513, 7]
     sh = SHAPES["gqa_g2"]
@@ -204,6 +223,19 @@ def test_generic_prefill(sk, name):
     okc, ovc = oracle.append(case.k_new, case.v_new, case.U, case.W, case.slot_mapping,
                              case.cache.k_cache, case.cache.v_cache)
     assert_parity(out, _pre_oracle(case, okc, ovc), f"generic prefill {name} (oracle caches)")
+
+
+def test_generic_prefill_long_prefix_reads_table(sk):
+    """A prefill row is one split over its whole table row; past 512 pages
+    (here 9000 cached tokens) the split kernel reads the block ids from the
+    table page by page instead of staging them."""
+    case = wl.make_prefill_case(SHAPES["h3_d32_gqa"], [9000, 40], [20, 9], seed=122)
+    assert case.cache.block_tables.shape[1] > 512
+    note("generic prefill over 9000 cached tokens")
+    out, kc, vc = _gpu_prefill(sk, case)
+    ref = _pre_oracle(case, kc, vc)
+    assert_parity(out, ref, "generic prefill long prefix")
+    per_head(out, ref, "generic prefill long prefix")
 
 
 @pytest.mark.parametrize("name", ["odd_h28_d96", "gqa_g8"])
