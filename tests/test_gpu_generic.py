@@ -225,6 +225,16 @@ def test_generic_prefill(sk, name):
     assert_parity(out, _pre_oracle(case, okc, ovc), f"generic prefill {name} (oracle caches)")
 
 
+def test_generic_prefill_many_chunk_tokens(sk):
+    """290 chunk tokens: the q projection takes 64 tokens per work group."""
+    case = wl.make_prefill_case(SHAPES["odd_h28_d96"], [30, 7], [200, 90], seed=123)
+    note("generic prefill 290 chunk tokens")
+    out, kc, vc = _gpu_prefill(sk, case)
+    ref = _pre_oracle(case, kc, vc)
+    assert_parity(out, ref, "generic prefill 290 tokens")
+    per_head(out, ref, "generic prefill 290 tokens")
+
+
 def test_generic_prefill_long_prefix_reads_table(sk):
     """A prefill row is one split over its whole table row; past 512 pages
     (here 9000 cached tokens) the split kernel reads the block ids from the
