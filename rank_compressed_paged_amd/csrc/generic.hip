@@ -415,7 +415,7 @@ __global__ __launch_bounds__(kGenSThreads) void generic_split_kernel(GenArgs a) 
 //     8 / TPW chunks of each tile, double-buffered in registers, and the
 //     first batch is requested before step 1, so W is in flight during the
 //     merge.
-constexpr int kGenMT = 4;          // rows per merge work group, at most
+constexpr int kGenMT = 8;          // rows per merge work group, at most (one per wave)
 constexpr int kGenMergeThreads = 512;  // eight waves
 template <int TPW>
 __global__ __launch_bounds__(kGenMergeThreads) void generic_merge_kernel(GenArgs a, int tb) {
@@ -560,6 +560,237 @@ __global__ __launch_bounds__(kGenMergeThreads) void generic_merge_kernel(GenArgs
   }
 }
 
+// Chunked prefill for the shapes without a tuned instance, r_k <= 128 and
+// r_v <= 1024: a work group takes 32 chunk queries of one request and one
+// head, so every
+// page it streams serves 32 query rows (the split kernel's prefill rows each
+// walk their own prefix).  Eight waves:
+//   * waves 0 and 1 form the scores of query block w (16 queries) on the
+//     matrix cores, v_mfma_f32_16x16x32_f16 with the key page as A (token x
+//     32 ranks, 16 contiguous bytes per lane) and q~ as B, split into an fp16
+//     hi/lo pair (two products per rank chunk), then the online softmax per
+//     query (log2 domain, the quad-lane reductions); the weights go to LDS in
+//     fp16 and are summed as rounded, the rescale factors beside them;
+//   * every wave then runs P.c_v for both query blocks over its feature tiles
+//     w, w + 8, ... (v_mfma_f32_16x16x16_f16, value operands as in the split
+//     kernel), so each value operand feeds two products;
+//   * page p+1's value operands (and, in the score waves, its key chunks) are
+//     requested at the top of page p;
+//   * weights and factors alternate between two LDS buffers: one LDS-only
+//     barrier per page.
+// The causal limit (query j sees keys up to P0 + j), the sequence end and
+// invalid block ids mask scores (-inf); value operands past the sequence end
+// or on an invalid page are zeroed by select, so NaN sentinels never enter a
+// product.  Each chunk query row ends as one split's partials (running max,
+// sum, unnormalised z, fp32), which the merge kernel turns into out = W_g z.
+constexpr int kGPThreads = 512;  // eight waves
+constexpr int kGPQ = 32;         // chunk queries per work group: two blocks of 16
+constexpr int kGPKC = 4;         // 32-rank chunks of a key row: r_k <= 128
+
+template <bool FP8>
+__global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, int n_qb) {
+  constexpr int NFT = kGenFT / 2;  // feature tiles per wave: r_v <= 1024
+  __shared__ __attribute__((aligned(16))) half_t sPh[2][2][16][16];  // [buf][block][query][token]
+  __shared__ float sAl[2][2][16];                                     // [buf][block][query]
+  __shared__ int sBlk[kGPThreads];
+  const int h = blockIdx.y;
+  const int b = blockIdx.x / n_qb, qbk = blockIdx.x % n_qb;
+  const int q_begin = a.qsl[b];
+  const int Cn = a.qsl[b + 1] - q_begin;
+  const int j0 = qbk * kGPQ;
+  if (j0 >= Cn) return;  // whole work group, before any barrier
+  const int L = a.seq_lens[b];
+  const int P0 = L - Cn;
+  const int nq = min(kGPQ, Cn - j0);
+  const int last_key = min(L - 1, P0 + j0 + nq - 1);
+  const int n_pages = last_key < 0 ? 0 : min(last_key / kGenBS + 1, a.max_blocks);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, quad = lane >> 4;
+  const int g = h / a.QG;
+  const int ntv = (a.RV + 15) / 16;
+  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
+  // the pages' block ids, staged once when they fit
+  const bool ids_lds = n_pages <= kGPThreads;  // uniform
+  if (ids_lds) sBlk[tid] = tid < n_pages ? bt[tid] : 0;
+
+  // score waves: query block w & 1, lane column = query
+  const bool scorer = w < 2;  // uniform per wave
+  const int jq = j0 + 16 * (w & 1) + col;
+  const int jqc = min(jq, Cn - 1);         // rows past the chunk mirror its last query
+  const int lim = min(L - 1, P0 + jqc);    // the last key this query sees
+  const int nkc = (a.RK + 31) / 32;
+  half8 qh[kGPKC], ql[kGPKC];
+  if (scorer) {
+    const float* qp = a.qt + ((size_t)(q_begin + jqc) * a.H + h) * a.RK;
+#pragma unroll
+    for (int c = 0; c < kGPKC; ++c) {
+      const int r0 = 32 * c + 8 * quad;
+      if (c < nkc && r0 < a.RK) {
+        const float4v x0 = *(const float4v*)(qp + r0);
+        const float4v x1 = *(const float4v*)(qp + r0 + 4);
+        split_f16x8(x0, x1, qh[c], ql[c]);
+      } else {
+        qh[c] = half8{};
+        ql[c] = half8{};
+      }
+    }
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+  float4v acc[NFT][2];
+#pragma unroll
+  for (int i = 0; i < NFT; ++i) {
+    acc[i][0] = zero4();
+    acc[i][1] = zero4();
+  }
+  __syncthreads();
+
+  typedef std::conditional_t<FP8, uint32_t, half4> VRaw;
+  auto load_val = [&](int blk, int ft) {
+    const int f = min(16 * ft + col, a.RV - 1);
+    const size_t idx = ((size_t)blk * a.RV + f) * kGenBS + 4 * quad;
+    if constexpr (FP8)
+      return *(const uint32_t*)((const uint8_t*)a.v_cache + idx);
+    else
+      return *(const half4*)((const half_t*)a.v_cache + idx);
+  };
+  auto to_half4 = [&](VRaw v) {
+    if constexpr (FP8) {
+      typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+      const half2v lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
+      const half2v hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, true);
+      return half4{lo[0], lo[1], hi[0], hi[1]};
+    } else {
+      return v;
+    }
+  };
+  auto to_half8 = [&](const Raw8<FP8>& k) {
+    if constexpr (FP8) {
+      typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+      half8 o;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const half2v lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k.r[e], 1.0f, false);
+        const half2v hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k.r[e], 1.0f, true);
+        o[4 * e + 0] = lo[0];
+        o[4 * e + 1] = lo[1];
+        o[4 * e + 2] = hi[0];
+        o[4 * e + 3] = hi[1];
+      }
+      return o;
+    } else {
+      return k.r;
+    }
+  };
+
+  auto block_at = [&](int p) {
+    return ids_lds ? __builtin_amdgcn_readfirstlane(sBlk[p]) : bt[p];
+  };
+  auto loadable = [&](int blk) { return (unsigned)blk < (unsigned)a.num_blocks ? blk : 0; };
+  // page operands: value operands (every wave) and key chunks of token col,
+  // ranks 32 c + 8 quad .. +7 (score waves); kc/vc this page's, kn/vn the
+  // next page's
+  VRaw vc[NFT], vn[NFT];
+  Raw8<FP8> kc[kGPKC], kn[kGPKC];
+  auto load_page = [&](VRaw (&v)[NFT], Raw8<FP8> (&k)[kGPKC], int blk) {
+#pragma unroll
+    for (int i = 0; i < NFT; ++i)
+      if (w + 8 * i < ntv) v[i] = load_val(blk, w + 8 * i);  // uniform
+    if (scorer) {
+      const size_t kb = (((size_t)blk * a.Hkv + g) * kGenBS + col) * a.RK;
+#pragma unroll
+      for (int c = 0; c < kGPKC; ++c)
+        if (c < nkc) k[c].load(a.k_cache, kb + min(32 * c + 8 * quad, a.RK - 8));
+    }
+  };
+  int blk_c = n_pages > 0 ? block_at(0) : 0;
+  if (n_pages > 0) load_page(vc, kc, loadable(blk_c));
+  for (int p = 0; p < n_pages; ++p) {
+    const int buf = p & 1;
+    const bool valid = (unsigned)blk_c < (unsigned)a.num_blocks;  // uniform
+    const int nv = valid ? min(kGenBS, L - p * kGenBS) : 0;  // tokens of the page that exist
+    const int blk_n = p + 1 < n_pages ? block_at(p + 1) : 0;
+    if (p + 1 < n_pages) load_page(vn, kn, loadable(blk_n));  // uniform
+    if (scorer) {
+      float4v sc = zero4();
+#pragma unroll
+      for (int c = 0; c < kGPKC; ++c) {
+        if (c < nkc) {  // uniform; ranks past r_k have zero q~
+          const half8 ka = to_half8(kc[c]);
+          sc = mfma16x16x32(ka, qh[c], sc);
+          sc = mfma16x16x32(ka, ql[c], sc);
+        }
+      }
+      // sc[i]: token 16 p + 4 quad + i, query col
+      float sv[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * quad + i;
+        const bool ok = t < nv && p * kGenBS + t <= lim;
+        sv[i] = ok ? sc[i] : -INFINITY;
+        mx = fmax_nn(mx, sv[i]);
+      }
+      mx = quad_max(mx);
+      const float m_new = fmax_nn(m_run, mx);
+      const float alpha = m_new == m_run ? 1.f : exp2f(m_run - m_new);  // 0 on the first page
+      half4 ph;
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ph[i] = (half_t)(sv[i] == -INFINITY ? 0.f : exp2f(sv[i] - m_new));
+        ps += (float)ph[i];
+      }
+      ps = quad_sum(ps);
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+      *(half4*)&sPh[buf][w][col][4 * quad] = ph;
+      if (quad == 0) sAl[buf][w][col] = alpha;
+    }
+    block_sync_lds();
+    const half4 pb0 = *(const half4*)&sPh[buf][0][col][4 * quad];
+    const half4 pb1 = *(const half4*)&sPh[buf][1][col][4 * quad];
+    const float al0 = sAl[buf][0][col], al1 = sAl[buf][1][col];
+    const bool part = nv < kGenBS;  // uniform: tokens past the end may hold NaN
+#pragma unroll
+    for (int i = 0; i < NFT; ++i) {
+      if (w + 8 * i < ntv) {  // uniform
+        half4 av = to_half4(vc[i]);
+        if (part) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) av[e] = 4 * quad + e < nv ? av[e] : (half_t)0.f;
+        }
+        acc[i][0] = mfma16x16x16(av, pb0, acc[i][0] * al0);
+        acc[i][1] = mfma16x16x16(av, pb1, acc[i][1] * al1);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NFT; ++i) vc[i] = vn[i];
+#pragma unroll
+    for (int c = 0; c < kGPKC; ++c) kc[c] = kn[c];
+    blk_c = blk_n;
+  }
+
+  // one split's partials per chunk query row: max and sum from the score
+  // waves, unnormalised z from every wave
+  if (scorer && quad == 0 && jq < Cn) {
+    float* mp = a.ml + ((size_t)(q_begin + jq) * a.H + h) * 2;
+    mp[0] = m_run;
+    mp[1] = l_run;
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int j = j0 + 16 * k + col;
+    if (j < Cn) {
+      float* zp = a.zpart + ((size_t)(q_begin + j) * a.H + h) * a.RV;
+#pragma unroll
+      for (int i = 0; i < NFT; ++i) {
+        const int f0 = 16 * (w + 8 * i) + 4 * quad;
+        if (w + 8 * i < ntv && f0 < a.RV) *(float4v*)(zp + f0) = acc[i][k];
+      }
+    }
+  }
+}
+
 // ds_read_b64_tr_b16: within each 16-lane group, lane q addresses row
 // r0 + q/4, columns c0 + 4*(q%4); lane i then receives rows r0 .. r0+3 of
 // column c0 + i.
@@ -689,13 +920,11 @@ static size_t split_lds(const ShapeKey& s, bool fused) {
                           kGenSHG * kGenBS + kGenSThreads + (fused ? (size_t)s.rv : 0));
 }
 
-hipError_t launch_generic_attn(const ShapeKey& s, const void* qt, const int32_t* qsl, int rows,
-                               const void* k_cache, const void* v_cache, const void* W,
-                               const int32_t* block_tables, int max_blocks,
-                               const int32_t* seq_lens, int num_blocks, int batch,
-                               int pages_per_split, int num_splits, float* ml, float* zpart,
-                               void* out, const LatentFormat& fmt, int which, hipStream_t st) {
-  if (rows <= 0) return hipSuccess;
+static GenArgs gen_args(const ShapeKey& s, const void* qt, const int32_t* qsl, int rows,
+                        const void* k_cache, const void* v_cache, const void* W,
+                        const int32_t* block_tables, int max_blocks, const int32_t* seq_lens,
+                        int num_blocks, int batch, int pages_per_split, int num_splits,
+                        float* ml, float* zpart, void* out, const LatentFormat& fmt) {
   GenArgs a;
   a.H = s.H;
   a.Hkv = s.Hkv;
@@ -720,6 +949,41 @@ hipError_t launch_generic_attn(const ShapeKey& s, const void* qt, const int32_t*
   a.ml = ml;
   a.zpart = zpart;
   a.out = (half_t*)out;
+  return a;
+}
+
+// The merge and up-projection over `rows` rows of num_splits splits each.
+static hipError_t launch_generic_merge(const ShapeKey& s, const GenArgs& a, int rows,
+                                       int num_splits, hipStream_t st) {
+  // rows per merge work group: several rows share each fetch of W_g once
+  // there are enough (row, head) pairs to keep the CUs busy, as long as
+  // their z and weights fit 64 KiB of LDS
+  const long pairs = (long)rows * s.H;
+  int tb = pairs >= 4096 ? kGenMT : (pairs >= 1024 ? 4 : (pairs >= 256 ? 2 : 1));
+  auto merge_lds = [&](int t) {
+    return sizeof(float) * ((size_t)t * s.rv + (size_t)t * num_splits + 2 * (size_t)t);
+  };
+  while (tb > 1 && merge_lds(tb) > 65536) tb /= 2;
+  const size_t mlds = merge_lds(tb);
+  const dim3 mgrid((rows + tb - 1) / tb, s.H);
+  const int tiles = s.d / 16;  // output tiles of 16 over the 8 waves: d <= 256
+  if (tiles <= 8)
+    hipLaunchKernelGGL(generic_merge_kernel<1>, mgrid, dim3(kGenMergeThreads), mlds, st, a, tb);
+  else
+    hipLaunchKernelGGL(generic_merge_kernel<2>, mgrid, dim3(kGenMergeThreads), mlds, st, a, tb);
+  return hipGetLastError();
+}
+
+hipError_t launch_generic_attn(const ShapeKey& s, const void* qt, const int32_t* qsl, int rows,
+                               const void* k_cache, const void* v_cache, const void* W,
+                               const int32_t* block_tables, int max_blocks,
+                               const int32_t* seq_lens, int num_blocks, int batch,
+                               int pages_per_split, int num_splits, float* ml, float* zpart,
+                               void* out, const LatentFormat& fmt, int which, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const GenArgs a = gen_args(s, qt, qsl, rows, k_cache, v_cache, W, block_tables, max_blocks,
+                             seq_lens, num_blocks, batch, pages_per_split, num_splits, ml, zpart,
+                             out, fmt);
   const bool fused = num_splits == 1;
   const dim3 grid((unsigned)((long)rows * generic_head_groups(s)), (unsigned)num_splits);
   const size_t lds = split_lds(s, fused);
@@ -742,23 +1006,35 @@ hipError_t launch_generic_attn(const ShapeKey& s, const void* qt, const int32_t*
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || fused) return e;
-  // rows per merge work group: several rows share each fetch of W_g once
-  // there are enough (row, head) pairs to keep the CUs busy, as long as
-  // their z and weights fit 64 KiB of LDS
-  const long pairs = (long)rows * s.H;
-  int tb = pairs >= 1024 ? kGenMT : (pairs >= 256 ? 2 : 1);
-  auto merge_lds = [&](int t) {
-    return sizeof(float) * ((size_t)t * s.rv + (size_t)t * num_splits + 2 * (size_t)t);
-  };
-  while (tb > 1 && merge_lds(tb) > 65536) tb /= 2;
-  const size_t mlds = merge_lds(tb);
-  const dim3 mgrid((rows + tb - 1) / tb, s.H);
-  const int tiles = s.d / 16;  // output tiles of 16 over the 8 waves: d <= 256
-  if (tiles <= 8)
-    hipLaunchKernelGGL(generic_merge_kernel<1>, mgrid, dim3(kGenMergeThreads), mlds, st, a, tb);
+  return launch_generic_merge(s, a, rows, num_splits, st);
+}
+
+bool generic_prefill_tiled(const ShapeKey& s) {
+  return s.rk <= 32 * kGPKC && s.rv <= 8 * 16 * (kGenFT / 2);
+}
+
+hipError_t launch_generic_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl,
+                                  int total_q, int max_query_len, const void* k_cache,
+                                  const void* v_cache, const void* W,
+                                  const int32_t* block_tables, int max_blocks,
+                                  const int32_t* seq_lens, int num_blocks, int batch, float* ml,
+                                  float* zpart, void* out, const LatentFormat& fmt, int which,
+                                  hipStream_t st) {
+  if (total_q <= 0 || batch <= 0 || max_query_len <= 0) return hipSuccess;
+  // one split per row, covering the whole table row
+  const GenArgs a = gen_args(s, qt, qsl, total_q, k_cache, v_cache, W, block_tables, max_blocks,
+                             seq_lens, num_blocks, batch, max_blocks, 1, ml, zpart, out, fmt);
+  const int n_qb = (max_query_len + kGPQ - 1) / kGPQ;
+  const dim3 grid((unsigned)((long)batch * n_qb), (unsigned)s.H);
+  if (fmt.fp8)
+    launch_hooked_lds(which, TIME_NONE, generic_prefill_kernel<true>, grid, dim3(kGPThreads), 0,
+                      st, a, n_qb);
   else
-    hipLaunchKernelGGL(generic_merge_kernel<2>, mgrid, dim3(kGenMergeThreads), mlds, st, a, tb);
-  return hipGetLastError();
+    launch_hooked_lds(which, TIME_NONE, generic_prefill_kernel<false>, grid, dim3(kGPThreads),
+                      0, st, a, n_qb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_generic_merge(s, a, total_q, 1, st);
 }
 
 }  // namespace starkv
