@@ -16,7 +16,8 @@ events that take its dispatch's own begin and end timestamps.  `value` is
 latent-KV bytes per step / mean step time.  Beside the headline the line
 carries the step with its append, a streaming-read ceiling, the chunked
 prefill workload (16 requests x 4096 cached + 256 new tokens: attention and
-append, as TFLOP/s against the fp16 MFMA peak), the append at 16 to 4096
+append, as TFLOP/s against the fp16 MFMA peak; also over FP8 caches, and at
+the conservative ranks r_k 128, r_v 1024 on the generic kernels), the append at 16 to 4096
 tokens, the other fp16 decode
 configurations of the same shape (decode_b64, long_b20, tiny), decode at other
 layouts (gqa8_b16: 32 query heads on 8 key/value heads; lowrank_b16: r_k
@@ -355,12 +356,15 @@ def cpu_prefill_baseline(pc, budget_s):
             "ms_per_call_extrapolated": round(spent / flops * total * 1e3, 1)}
 
 
-def prefill_leg(flush_fn, steps, name="prefill_b16", cpu_budget_s=0.0):
+def prefill_leg(flush_fn, steps, name="prefill_b16", cpu_budget_s=0.0, upproj_in_kernel=True):
     """Chunked prefill at 16 requests x (4096 cached + 256 new) tokens: the
     chunk's append (4096 tokens), then causal attention for the 4096 chunk
-    queries (prefill_b16; prefill_b16_fp8 the same over FP8 caches).
-    Reports time, algorithmic TFLOP/s and the fraction of the dense fp16 MFMA
-    peak for the attention kernel and for the append."""
+    queries (prefill_b16; prefill_b16_fp8 the same over FP8 caches;
+    conservative_prefill_b16 at r_k 128, r_v 1024 on the generic kernels,
+    whose attention kernel leaves the up-projection to the merge launch:
+    upproj_in_kernel False).  Reports time, algorithmic TFLOP/s and the
+    fraction of the dense fp16 MFMA peak for the attention kernel and for
+    the append."""
     import numpy as np
     import torch
     from rank_compressed_paged_amd import metrics
@@ -408,9 +412,11 @@ def prefill_leg(flush_fn, steps, name="prefill_b16", cpu_budget_s=0.0):
     _, app_kern_ms, _ = timed(app, n, flush_fn, sk.TIME_APPEND)
     flops = metrics.prefill_flops(pc.cached_lens, chunk, sh.H, sh.d, sh.r_k, sh.r_v)
     pairs = metrics.prefill_pairs(pc.cached_lens, chunk)
-    # the kernel's share: scores + P.c_v, and the up-projection, which the
-    # main-shape kernels apply in their epilogue
-    kern_flops = 2 * sh.H * pairs * (sh.r_k + sh.r_v) + 2 * sh.H * T * sh.r_v * sh.d
+    # the kernel's share: scores + P.c_v, and the up-projection when the
+    # kernel applies it in its epilogue (the main-shape instances)
+    kern_flops = 2 * sh.H * pairs * (sh.r_k + sh.r_v)
+    if upproj_in_kernel:
+        kern_flops += 2 * sh.H * T * sh.r_v * sh.d
     app_flops = metrics.append_flops(T, sh.H, sh.d, sh.r_k, sh.r_v)
     app_bytes = (2 * T * sh.H * sh.d * 2 + T * 8 + metrics.basis_bytes(sh.H, sh.d, sh.r_k, sh.r_v)
                  + T * metrics.latent_bytes_per_token(sh.H, sh.r_k, sh.r_v))
@@ -427,7 +433,7 @@ def prefill_leg(flush_fn, steps, name="prefill_b16", cpu_budget_s=0.0):
         "attn_kernel_mfma_frac": round(tf(kern_flops, m(attn_kern_ms)) / MFMA_F16_PEAK_TFLOPS, 4),
         "algorithmic_gflop_call": round(flops / 1e9, 1),
         "algorithmic_gflop_kernel": round(kern_flops / 1e9, 1),
-        "kernel_includes_upprojection": True,
+        "kernel_includes_upprojection": bool(upproj_in_kernel),
         "append_tokens": T,
         "append_call_ms": round(m(app_ms), 4),
         "append_kernel_ms": round(m(app_kern_ms), 4),
@@ -788,6 +794,8 @@ def run_bench(args):
         res["prefill"] = prefill_leg(do_flush, args.steps,
                                      cpu_budget_s=0.0 if args.no_cpu else args.cpu_prefill_seconds)
         res["prefill_fp8"] = prefill_leg(do_flush, args.steps, "prefill_b16_fp8")
+        res["prefill_generic"] = prefill_leg(do_flush, args.steps, "conservative_prefill_b16",
+                                             upproj_in_kernel=False)
         res["append_sizes"] = append_sizes_leg(do_flush, args.steps)
     if not args.no_low_batch:
         res["low_batch"] = low_batch_leg(do_flush, args.steps)

@@ -561,19 +561,19 @@ __global__ __launch_bounds__(kGenMergeThreads) void generic_merge_kernel(GenArgs
 }
 
 // Chunked prefill for the shapes without a tuned instance, r_k <= 128 and
-// r_v <= 1024: a work group takes 32 chunk queries of one request and one
-// head, so every
-// page it streams serves 32 query rows (the split kernel's prefill rows each
-// walk their own prefix).  Eight waves:
-//   * waves 0 and 1 form the scores of query block w (16 queries) on the
+// r_v <= 1024: a work group takes 64 chunk queries of one request and one
+// head, so every page it streams serves 64 query rows (the split kernel's
+// prefill rows each walk their own prefix).  Eight waves:
+//   * waves 0 to 3 form the scores of query block w (16 queries) on the
 //     matrix cores, v_mfma_f32_16x16x32_f16 with the key page as A (token x
 //     32 ranks, 16 contiguous bytes per lane) and q~ as B, split into an fp16
 //     hi/lo pair (two products per rank chunk), then the online softmax per
-//     query (log2 domain, the quad-lane reductions); the weights go to LDS in
-//     fp16 and are summed as rounded, the rescale factors beside them;
-//   * every wave then runs P.c_v for both query blocks over its feature tiles
-//     w, w + 8, ... (v_mfma_f32_16x16x16_f16, value operands as in the split
-//     kernel), so each value operand feeds two products;
+//     query (log2 domain, the quad-lane reductions); q~ waits in LDS as hi/lo
+//     fragments; the weights go to LDS in fp16 and are summed as rounded, the
+//     rescale factors beside them;
+//   * every wave then runs P.c_v for the four query blocks over its feature
+//     tiles w, w + 8, ... (v_mfma_f32_16x16x16_f16, value operands as in the split
+//     kernel), so each value operand feeds four products;
 //   * page p+1's value operands (and, in the score waves, its key chunks) are
 //     requested at the top of page p;
 //   * weights and factors alternate between two LDS buffers: one LDS-only
@@ -584,14 +584,18 @@ __global__ __launch_bounds__(kGenMergeThreads) void generic_merge_kernel(GenArgs
 // product.  Each chunk query row ends as one split's partials (running max,
 // sum, unnormalised z, fp32), which the merge kernel turns into out = W_g z.
 constexpr int kGPThreads = 512;  // eight waves
-constexpr int kGPQ = 32;         // chunk queries per work group: two blocks of 16
+constexpr int kGPQB = 4;         // 16-query blocks per work group
+constexpr int kGPQ = 16 * kGPQB; // chunk queries per work group
 constexpr int kGPKC = 4;         // 32-rank chunks of a key row: r_k <= 128
 
 template <bool FP8>
 __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, int n_qb) {
   constexpr int NFT = kGenFT / 2;  // feature tiles per wave: r_v <= 1024
-  __shared__ __attribute__((aligned(16))) half_t sPh[2][2][16][16];  // [buf][block][query][token]
-  __shared__ float sAl[2][2][16];                                     // [buf][block][query]
+  __shared__ __attribute__((aligned(16))) half_t sPh[2][kGPQB][16][16];  // [buf][block][query][token]
+  __shared__ float sAl[2][kGPQB][16];                                     // [buf][block][query]
+  // q~ of the work group's queries as fp16 hi/lo B fragments:
+  // [block][chunk][hi, lo][quad][query] 16-byte pieces
+  __shared__ __attribute__((aligned(16))) half8 sQ[kGPQB][kGPKC][2][4][16];
   __shared__ int sBlk[kGPThreads];
   const int h = blockIdx.y;
   const int b = blockIdx.x / n_qb, qbk = blockIdx.x % n_qb;
@@ -613,35 +617,33 @@ __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, 
   const bool ids_lds = n_pages <= kGPThreads;  // uniform
   if (ids_lds) sBlk[tid] = tid < n_pages ? bt[tid] : 0;
 
-  // score waves: query block w & 1, lane column = query
-  const bool scorer = w < 2;  // uniform per wave
-  const int jq = j0 + 16 * (w & 1) + col;
+  // score waves: query block w (w < kGPQB), lane column = query
+  const bool scorer = w < kGPQB;  // uniform per wave
+  const int jq = j0 + 16 * (w % kGPQB) + col;
   const int jqc = min(jq, Cn - 1);         // rows past the chunk mirror its last query
   const int lim = min(L - 1, P0 + jqc);    // the last key this query sees
   const int nkc = (a.RK + 31) / 32;
-  half8 qh[kGPKC], ql[kGPKC];
   if (scorer) {
     const float* qp = a.qt + ((size_t)(q_begin + jqc) * a.H + h) * a.RK;
 #pragma unroll
     for (int c = 0; c < kGPKC; ++c) {
       const int r0 = 32 * c + 8 * quad;
+      half8 hi = {}, lo = {};
       if (c < nkc && r0 < a.RK) {
         const float4v x0 = *(const float4v*)(qp + r0);
         const float4v x1 = *(const float4v*)(qp + r0 + 4);
-        split_f16x8(x0, x1, qh[c], ql[c]);
-      } else {
-        qh[c] = half8{};
-        ql[c] = half8{};
+        split_f16x8(x0, x1, hi, lo);
       }
+      sQ[w][c][0][quad][col] = hi;
+      sQ[w][c][1][quad][col] = lo;
     }
   }
   float m_run = -INFINITY, l_run = 0.f;
-  float4v acc[NFT][2];
+  float4v acc[NFT][kGPQB];
 #pragma unroll
-  for (int i = 0; i < NFT; ++i) {
-    acc[i][0] = zero4();
-    acc[i][1] = zero4();
-  }
+  for (int i = 0; i < NFT; ++i)
+#pragma unroll
+    for (int k = 0; k < kGPQB; ++k) acc[i][k] = zero4();
   __syncthreads();
 
   typedef std::conditional_t<FP8, uint32_t, half4> VRaw;
@@ -711,13 +713,17 @@ __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, 
     const int blk_n = p + 1 < n_pages ? block_at(p + 1) : 0;
     if (p + 1 < n_pages) load_page(vn, kn, loadable(blk_n));  // uniform
     if (scorer) {
+      // q~ from LDS at every page (the block index passes through an empty
+      // asm, so the compiler does not keep the fragments in registers)
+      int qw = w;
+      asm volatile("" : "+v"(qw));
       float4v sc = zero4();
 #pragma unroll
       for (int c = 0; c < kGPKC; ++c) {
         if (c < nkc) {  // uniform; ranks past r_k have zero q~
           const half8 ka = to_half8(kc[c]);
-          sc = mfma16x16x32(ka, qh[c], sc);
-          sc = mfma16x16x32(ka, ql[c], sc);
+          sc = mfma16x16x32(ka, sQ[qw][c][0][quad][col], sc);
+          sc = mfma16x16x32(ka, sQ[qw][c][1][quad][col], sc);
         }
       }
       // sc[i]: token 16 p + 4 quad + i, query col
@@ -747,9 +753,13 @@ __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, 
       if (quad == 0) sAl[buf][w][col] = alpha;
     }
     block_sync_lds();
-    const half4 pb0 = *(const half4*)&sPh[buf][0][col][4 * quad];
-    const half4 pb1 = *(const half4*)&sPh[buf][1][col][4 * quad];
-    const float al0 = sAl[buf][0][col], al1 = sAl[buf][1][col];
+    half4 pb[kGPQB];
+    float al[kGPQB];
+#pragma unroll
+    for (int k = 0; k < kGPQB; ++k) {
+      pb[k] = *(const half4*)&sPh[buf][k][col][4 * quad];
+      al[k] = sAl[buf][k][col];
+    }
     const bool part = nv < kGenBS;  // uniform: tokens past the end may hold NaN
 #pragma unroll
     for (int i = 0; i < NFT; ++i) {
@@ -759,8 +769,8 @@ __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, 
 #pragma unroll
           for (int e = 0; e < 4; ++e) av[e] = 4 * quad + e < nv ? av[e] : (half_t)0.f;
         }
-        acc[i][0] = mfma16x16x16(av, pb0, acc[i][0] * al0);
-        acc[i][1] = mfma16x16x16(av, pb1, acc[i][1] * al1);
+#pragma unroll
+        for (int k = 0; k < kGPQB; ++k) acc[i][k] = mfma16x16x16(av, pb[k], acc[i][k] * al[k]);
       }
     }
 #pragma unroll
@@ -778,7 +788,7 @@ __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, 
     mp[1] = l_run;
   }
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < kGPQB; ++k) {
     const int j = j0 + 16 * k + col;
     if (j < Cn) {
       float* zp = a.zpart + ((size_t)(q_begin + j) * a.H + h) * a.RV;

@@ -156,7 +156,7 @@ hipError_t launch_generic_attn(const ShapeKey& s, const void* qt, const int32_t*
                                void* out, const LatentFormat& fmt, int which, hipStream_t st);
 
 // Chunked prefill on the generic kernels for r_k up to 128 and r_v up to 1024
-// (generic_prefill_tiled): 32 chunk queries of one head per work group, each
+// (generic_prefill_tiled): 64 chunk queries of one head per work group, each
 // chunk query row ending as one split's partials in ml [total_q][H][2] and
 // zpart [total_q][H][r_v] (fp32), then the merge with the up-projection.
 bool generic_prefill_tiled(const ShapeKey& s);

@@ -102,6 +102,8 @@ CONFIGS = {
     "conservative_b16": dict(kind="decode", shape=CONSERVATIVE, B=16, seq=("fixed", 2048),
                              seed=15),
     "odd_h28_b16": dict(kind="decode", shape=ODD_H28, B=16, seq=("fixed", 2048), seed=16),
+    "conservative_prefill_b16": dict(kind="prefill", shape=CONSERVATIVE, B=16, cached=4096,
+                                     chunk=256, seed=17),
 }
 
 
