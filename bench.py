@@ -360,11 +360,11 @@ def prefill_leg(flush_fn, steps, name="prefill_b16", cpu_budget_s=0.0, upproj_in
     """Chunked prefill at 16 requests x (4096 cached + 256 new) tokens: the
     chunk's append (4096 tokens), then causal attention for the 4096 chunk
     queries (prefill_b16; prefill_b16_fp8 the same over FP8 caches;
-    conservative_prefill_b16 at r_k 128, r_v 1024 on the generic kernels,
-    whose attention kernel leaves the up-projection to the merge launch:
-    upproj_in_kernel False).  Reports time, algorithmic TFLOP/s and the
-    fraction of the dense fp16 MFMA peak for the attention kernel and for
-    the append."""
+    conservative_prefill_b16 at r_k 128, r_v 1024 on the generic kernels).
+    upproj_in_kernel: the attention kernel applies the up-projection in its
+    epilogue, so its algorithmic flops include it.  Reports time, algorithmic
+    TFLOP/s and the fraction of the dense fp16 MFMA peak for the attention
+    kernel and for the append."""
     import numpy as np
     import torch
     from rank_compressed_paged_amd import metrics
@@ -794,8 +794,7 @@ def run_bench(args):
         res["prefill"] = prefill_leg(do_flush, args.steps,
                                      cpu_budget_s=0.0 if args.no_cpu else args.cpu_prefill_seconds)
         res["prefill_fp8"] = prefill_leg(do_flush, args.steps, "prefill_b16_fp8")
-        res["prefill_generic"] = prefill_leg(do_flush, args.steps, "conservative_prefill_b16",
-                                             upproj_in_kernel=False)
+        res["prefill_generic"] = prefill_leg(do_flush, args.steps, "conservative_prefill_b16")
         res["append_sizes"] = append_sizes_leg(do_flush, args.steps)
     if not args.no_low_batch:
         res["low_batch"] = low_batch_leg(do_flush, args.steps)

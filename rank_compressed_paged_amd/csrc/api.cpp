@@ -212,13 +212,6 @@ PrefillWorkspace prefill_workspace_layout(const ShapeKey& s, int total_q) {
   off = align256(off + (size_t)total_q * s.H * s.rk * 4);  // q~, fp32
   w.z_off = off;  // fp16 z tiled by 32-token blocks, see launch_upproj_tiled
   off = align256(off + (size_t)((total_q + 31) / 32) * 32 * s.H * s.rv * 2);
-  if ((!tuned_shape(s) || !tuned_fp8(s)) && generic_shape_ok(s) && generic_prefill_tiled(s)) {
-    // one split's partials per chunk query row: (max, sum) and z, fp32
-    w.gml_off = off;
-    off = align256(off + (size_t)total_q * s.H * 2 * 4);
-    w.gzp_off = off;
-    off = align256(off + (size_t)total_q * s.H * s.rv * 4);
-  }
   w.total = off;
   return w;
 }
@@ -620,11 +613,10 @@ starkv_status prefill_common(const starkv_dims* dims, const void* q,
   if (use_generic(key, fmt.fp8)) {
     e = launch_generic_qproj(key, q, U, total_q, qscale, wb + ws.qt_off, TIME_PREFILL_ATTN, s);
     if (e != hipSuccess) return STARKV_ERR_LAUNCH;
-    if (generic_prefill_tiled(key))  // 32 chunk queries per work group, then the merge
+    if (generic_prefill_tiled(key))  // 64 chunk queries per work group
       e = launch_generic_prefill(key, wb + ws.qt_off, query_start_loc, total_q, max_query_len,
                                  k_cache, v_cache, W, block_tables, max_blocks_per_seq, seq_lens,
-                                 dims->num_blocks, batch, (float*)(wb + ws.gml_off),
-                                 (float*)(wb + ws.gzp_off), out, fmt, TIME_PREFILL_ATTN, s);
+                                 dims->num_blocks, batch, out, fmt, TIME_PREFILL_ATTN, s);
     else  // r_v > 1024: one row per chunk query, one split
       e = launch_generic_attn(key, wb + ws.qt_off, query_start_loc, total_q, k_cache, v_cache,
                               W, block_tables, max_blocks_per_seq, seq_lens, dims->num_blocks,

@@ -581,8 +581,7 @@ __global__ __launch_bounds__(kGenMergeThreads) void generic_merge_kernel(GenArgs
 // The causal limit (query j sees keys up to P0 + j), the sequence end and
 // invalid block ids mask scores (-inf); value operands past the sequence end
 // or on an invalid page are zeroed by select, so NaN sentinels never enter a
-// product.  Each chunk query row ends as one split's partials (running max,
-// sum, unnormalised z, fp32), which the merge kernel turns into out = W_g z.
+// product.  The epilogue applies W_g to the 64 rows' normalised z (below).
 constexpr int kGPThreads = 512;  // eight waves
 constexpr int kGPQB = 4;         // 16-query blocks per work group
 constexpr int kGPQ = 16 * kGPQB; // chunk queries per work group
@@ -596,6 +595,8 @@ __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, 
   // q~ of the work group's queries as fp16 hi/lo B fragments:
   // [block][chunk][hi, lo][quad][query] 16-byte pieces
   __shared__ __attribute__((aligned(16))) half8 sQ[kGPQB][kGPKC][2][4][16];
+  __shared__ float sL[kGPQB][16];                                   // final sums
+  __shared__ __attribute__((aligned(16))) float4v sRed[kGPQB][8][64];  // epilogue partials
   __shared__ int sBlk[kGPThreads];
   const int h = blockIdx.y;
   const int b = blockIdx.x / n_qb, qbk = blockIdx.x % n_qb;
@@ -780,24 +781,78 @@ __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, 
     blk_c = blk_n;
   }
 
-  // one split's partials per chunk query row: max and sum from the score
-  // waves, unnormalised z from every wave
-  if (scorer && quad == 0 && jq < Cn) {
-    float* mp = a.ml + ((size_t)(q_begin + jq) * a.H + h) * 2;
-    mp[0] = m_run;
-    mp[1] = l_run;
-  }
+  // Epilogue: out = v_scale * W_g z for the 64 rows, z = acc / l rounded to
+  // fp16.  A lane's accumulator tile is the B operand of a 16x16x16 product
+  // as it stands (feature 16 ft + 4 quad + e of query col), so wave w forms
+  // the partial outputs over its own feature tiles, output tile by output
+  // tile (A = 16 rows of W_g x 16 features, 8 contiguous bytes per lane), and
+  // the eight waves' partials are summed through LDS.  W_g is read once per
+  // work group; the next output tile's rows are requested before the sums.
+  __syncthreads();  // the loop's LDS buffers are free
+  if (scorer && quad == 0) sL[w][col] = l_run;
+  __syncthreads();
+  half4 z16[NFT][kGPQB];
 #pragma unroll
   for (int k = 0; k < kGPQB; ++k) {
-    const int j = j0 + 16 * k + col;
-    if (j < Cn) {
-      float* zp = a.zpart + ((size_t)(q_begin + j) * a.H + h) * a.RV;
+    const float l = sL[k][col];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-      for (int i = 0; i < NFT; ++i) {
-        const int f0 = 16 * (w + 8 * i) + 4 * quad;
-        if (w + 8 * i < ntv && f0 < a.RV) *(float4v*)(zp + f0) = acc[i][k];
+    for (int i = 0; i < NFT; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z16[i][k][e] = (half_t)(acc[i][k][e] * inv);
+    }
+  }
+  const half_t* Wg = a.W + (size_t)g * a.D * a.RV;
+  const int n_ot = a.D / 16;
+  auto load_w = [&](half4 (&wa)[NFT], int ot) {
+#pragma unroll
+    for (int i = 0; i < NFT; ++i) {
+      const int f0 = 16 * (w + 8 * i) + 4 * quad;
+      // features past RV (the last tile's upper half) have no W column
+      wa[i] = (w + 8 * i < ntv && f0 < a.RV)
+                  ? *(const half4*)(Wg + (size_t)(16 * ot + col) * a.RV + f0)
+                  : half4{};
+    }
+  };
+  half4 wc[NFT], wn[NFT];
+  load_w(wc, 0);
+  for (int ot = 0; ot < n_ot; ++ot) {  // uniform
+    float4v part[kGPQB];
+#pragma unroll
+    for (int k = 0; k < kGPQB; ++k) part[k] = zero4();
+#pragma unroll
+    for (int i = 0; i < NFT; ++i) {
+      if (w + 8 * i < ntv) {  // uniform
+#pragma unroll
+        for (int k = 0; k < kGPQB; ++k) part[k] = mfma16x16x16(wc[i], z16[i][k], part[k]);
       }
     }
+    if (ot + 1 < n_ot) load_w(wn, ot + 1);
+#pragma unroll
+    for (int k = 0; k < kGPQB; ++k) sRed[k][w][lane] = part[k];
+    block_sync_lds();
+    // thread t sums outputs 16 ot + 4 (l / 16) + 2 hf .. +1 of query l % 16
+    // of block k over the eight waves (t = 128 k + 2 l + hf)
+    {
+      const int k = tid >> 7, l = (tid >> 1) & 63, hf = tid & 1;
+      float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+      for (int wv = 0; wv < 8; ++wv) {
+        const float4v v = sRed[k][wv][l];
+        o0 += v[2 * hf];
+        o1 += v[2 * hf + 1];
+      }
+      const int j = j0 + 16 * k + (l & 15);
+      if (j < Cn) {
+        typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+        const int d = 16 * ot + 4 * (l >> 4) + 2 * hf;
+        *(half2v*)(a.out + ((size_t)(q_begin + j) * a.H + h) * a.D + d) =
+            half2v{(half_t)(o0 * a.v_scale), (half_t)(o1 * a.v_scale)};
+      }
+    }
+    block_sync_lds();  // sRed is rewritten by the next output tile
+#pragma unroll
+    for (int i = 0; i < NFT; ++i) wc[i] = wn[i];
   }
 }
 
@@ -1027,13 +1082,12 @@ hipError_t launch_generic_prefill(const ShapeKey& s, const void* qt, const int32
                                   int total_q, int max_query_len, const void* k_cache,
                                   const void* v_cache, const void* W,
                                   const int32_t* block_tables, int max_blocks,
-                                  const int32_t* seq_lens, int num_blocks, int batch, float* ml,
-                                  float* zpart, void* out, const LatentFormat& fmt, int which,
-                                  hipStream_t st) {
+                                  const int32_t* seq_lens, int num_blocks, int batch, void* out,
+                                  const LatentFormat& fmt, int which, hipStream_t st) {
   if (total_q <= 0 || batch <= 0 || max_query_len <= 0) return hipSuccess;
-  // one split per row, covering the whole table row
   const GenArgs a = gen_args(s, qt, qsl, total_q, k_cache, v_cache, W, block_tables, max_blocks,
-                             seq_lens, num_blocks, batch, max_blocks, 1, ml, zpart, out, fmt);
+                             seq_lens, num_blocks, batch, max_blocks, 1, nullptr, nullptr, out,
+                             fmt);
   const int n_qb = (max_query_len + kGPQ - 1) / kGPQ;
   const dim3 grid((unsigned)((long)batch * n_qb), (unsigned)s.H);
   if (fmt.fp8)
@@ -1042,9 +1096,7 @@ hipError_t launch_generic_prefill(const ShapeKey& s, const void* qt, const int32
   else
     launch_hooked_lds(which, TIME_NONE, generic_prefill_kernel<false>, grid, dim3(kGPThreads),
                       0, st, a, n_qb);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_generic_merge(s, a, total_q, 1, st);
+  return hipGetLastError();
 }
 
 }  // namespace starkv

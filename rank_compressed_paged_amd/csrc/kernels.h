@@ -54,9 +54,6 @@ int decode_threads(const ShapeKey& s);
 
 struct PrefillWorkspace {
   size_t qt_off, z_off, total;
-  // generic prefill partials (shapes that may run on the generic kernels
-  // with r_v <= 1024, in either cache format), else 0
-  size_t gml_off = 0, gzp_off = 0;
 };
 
 // Byte offsets of the workspace of the bases fit: the Gram matrices (fp32),
@@ -156,17 +153,15 @@ hipError_t launch_generic_attn(const ShapeKey& s, const void* qt, const int32_t*
                                void* out, const LatentFormat& fmt, int which, hipStream_t st);
 
 // Chunked prefill on the generic kernels for r_k up to 128 and r_v up to 1024
-// (generic_prefill_tiled): 64 chunk queries of one head per work group, each
-// chunk query row ending as one split's partials in ml [total_q][H][2] and
-// zpart [total_q][H][r_v] (fp32), then the merge with the up-projection.
+// (generic_prefill_tiled): 64 chunk queries of one head per work group, the
+// up-projection in the kernel's epilogue.
 bool generic_prefill_tiled(const ShapeKey& s);
 hipError_t launch_generic_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl,
                                   int total_q, int max_query_len, const void* k_cache,
                                   const void* v_cache, const void* W,
                                   const int32_t* block_tables, int max_blocks,
-                                  const int32_t* seq_lens, int num_blocks, int batch, float* ml,
-                                  float* zpart, void* out, const LatentFormat& fmt, int which,
-                                  hipStream_t st);
+                                  const int32_t* seq_lens, int num_blocks, int batch, void* out,
+                                  const LatentFormat& fmt, int which, hipStream_t st);
 
 // `precedes`: the hooked kernel that follows this launch in the call.
 // w_prefetch: the W that the step's merge will read (decode), fetched into
