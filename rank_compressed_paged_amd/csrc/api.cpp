@@ -613,11 +613,11 @@ starkv_status prefill_common(const starkv_dims* dims, const void* q,
   if (use_generic(key, fmt.fp8)) {
     e = launch_generic_qproj(key, q, U, total_q, qscale, wb + ws.qt_off, TIME_PREFILL_ATTN, s);
     if (e != hipSuccess) return STARKV_ERR_LAUNCH;
-    if (generic_prefill_tiled(key))  // 64 chunk queries per work group
+    if (generic_prefill_tiled(key, max_blocks_per_seq))  // 64 chunk queries per work group
       e = launch_generic_prefill(key, wb + ws.qt_off, query_start_loc, total_q, max_query_len,
                                  k_cache, v_cache, W, block_tables, max_blocks_per_seq, seq_lens,
                                  dims->num_blocks, batch, out, fmt, TIME_PREFILL_ATTN, s);
-    else  // r_v > 1024: one row per chunk query, one split
+    else  // r_k > 128, r_v > 1024 or table rows past 8192 pages: one row per chunk query
       e = launch_generic_attn(key, wb + ws.qt_off, query_start_loc, total_q, k_cache, v_cache,
                               W, block_tables, max_blocks_per_seq, seq_lens, dims->num_blocks,
                               batch, max_blocks_per_seq, 1, nullptr, nullptr, out, fmt,

@@ -574,8 +574,9 @@ __global__ __launch_bounds__(kGenMergeThreads) void generic_merge_kernel(GenArgs
 //   * every wave then runs P.c_v for the four query blocks over its feature
 //     tiles w, w + 8, ... (v_mfma_f32_16x16x16_f16, value operands as in the split
 //     kernel), so each value operand feeds four products;
-//   * page p+1's value operands (and, in the score waves, its key chunks) are
-//     requested at the top of page p;
+//   * page p+1's value operands and key chunks are requested at the top of
+//     page p, into the other of two operand slots (no copies), with no branch
+//     around any request, so every use waits only for its own page;
 //   * weights and factors alternate between two LDS buffers: one LDS-only
 //     barrier per page.
 // The causal limit (query j sees keys up to P0 + j), the sequence end and
@@ -586,6 +587,7 @@ constexpr int kGPThreads = 512;  // eight waves
 constexpr int kGPQB = 4;         // 16-query blocks per work group
 constexpr int kGPQ = 16 * kGPQB; // chunk queries per work group
 constexpr int kGPKC = 4;         // 32-rank chunks of a key row: r_k <= 128
+constexpr int kGPIds = 8192;     // pages of a request's table: 131072 tokens
 
 template <bool FP8>
 __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, int n_qb) {
@@ -597,7 +599,7 @@ __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, 
   __shared__ __attribute__((aligned(16))) half8 sQ[kGPQB][kGPKC][2][4][16];
   __shared__ float sL[kGPQB][16];                                   // final sums
   __shared__ __attribute__((aligned(16))) float4v sRed[kGPQB][8][64];  // epilogue partials
-  __shared__ int sBlk[kGPThreads];
+  __shared__ int sBlk[kGPIds];
   const int h = blockIdx.y;
   const int b = blockIdx.x / n_qb, qbk = blockIdx.x % n_qb;
   const int q_begin = a.qsl[b];
@@ -614,9 +616,9 @@ __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, 
   const int g = h / a.QG;
   const int ntv = (a.RV + 15) / 16;
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
-  // the pages' block ids, staged once when they fit
-  const bool ids_lds = n_pages <= kGPThreads;  // uniform
-  if (ids_lds) sBlk[tid] = tid < n_pages ? bt[tid] : 0;
+  // the pages' block ids, staged once (the host keeps the table's row length
+  // within kGPIds)
+  for (int i = tid; i < n_pages; i += kGPThreads) sBlk[i] = bt[i];
 
   // score waves: query block w (w < kGPQB), lane column = query
   const bool scorer = w < kGPQB;  // uniform per wave
@@ -685,34 +687,38 @@ __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, 
     }
   };
 
-  auto block_at = [&](int p) {
-    return ids_lds ? __builtin_amdgcn_readfirstlane(sBlk[p]) : bt[p];
-  };
+  auto block_at = [&](int p) { return __builtin_amdgcn_readfirstlane(sBlk[p]); };
   auto loadable = [&](int blk) { return (unsigned)blk < (unsigned)a.num_blocks ? blk : 0; };
   // page operands: value operands (every wave) and key chunks of token col,
   // ranks 32 c + 8 quad .. +7 (score waves); kc/vc this page's, kn/vn the
   // next page's
-  VRaw vc[NFT], vn[NFT];
-  Raw8<FP8> kc[kGPKC], kn[kGPKC];
+  // page operands in two slots, page p in slot p % 2 (the loop is unrolled
+  // by two, so no operand is copied).  Every wave issues the same loads on
+  // every page, with addresses clamped into the page (tiles past r_v re-read
+  // the last feature, the waves that form no scores read the page's first
+  // key bytes, the last page requests itself again): with no branch around
+  // a load, each use waits only for its own page's requests.
+  VRaw vr[2][NFT];
+  Raw8<FP8> kr[2][kGPKC];
   auto load_page = [&](VRaw (&v)[NFT], Raw8<FP8> (&k)[kGPKC], int blk) {
 #pragma unroll
-    for (int i = 0; i < NFT; ++i)
-      if (w + 8 * i < ntv) v[i] = load_val(blk, w + 8 * i);  // uniform
-    if (scorer) {
-      const size_t kb = (((size_t)blk * a.Hkv + g) * kGenBS + col) * a.RK;
+    for (int i = 0; i < NFT; ++i) v[i] = load_val(blk, w + 8 * i);
+    const size_t kb = ((size_t)blk * a.Hkv + g) * kGenBS * a.RK;
 #pragma unroll
-      for (int c = 0; c < kGPKC; ++c)
-        if (c < nkc) k[c].load(a.k_cache, kb + min(32 * c + 8 * quad, a.RK - 8));
-    }
+    for (int c = 0; c < kGPKC; ++c)
+      k[c].load(a.k_cache,
+                kb + (scorer ? (size_t)col * a.RK + min(32 * c + 8 * quad, a.RK - 8) : 0));
   };
-  int blk_c = n_pages > 0 ? block_at(0) : 0;
-  if (n_pages > 0) load_page(vc, kc, loadable(blk_c));
-  for (int p = 0; p < n_pages; ++p) {
+  if (n_pages > 0) load_page(vr[0], kr[0], loadable(block_at(0)));
+  auto page = [&](auto phase, int p) {
+    constexpr int PH = decltype(phase)::value;
+    VRaw (&vc)[NFT] = vr[PH];
+    Raw8<FP8> (&kc)[kGPKC] = kr[PH];
+    load_page(vr[PH ^ 1], kr[PH ^ 1], loadable(block_at(min(p + 1, n_pages - 1))));
+    const int blk_c = block_at(p);
     const int buf = p & 1;
     const bool valid = (unsigned)blk_c < (unsigned)a.num_blocks;  // uniform
     const int nv = valid ? min(kGenBS, L - p * kGenBS) : 0;  // tokens of the page that exist
-    const int blk_n = p + 1 < n_pages ? block_at(p + 1) : 0;
-    if (p + 1 < n_pages) load_page(vn, kn, loadable(blk_n));  // uniform
     if (scorer) {
       // q~ from LDS at every page (the block index passes through an empty
       // asm, so the compiler does not keep the fragments in registers)
@@ -774,12 +780,13 @@ __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, 
         for (int k = 0; k < kGPQB; ++k) acc[i][k] = mfma16x16x16(av, pb[k], acc[i][k] * al[k]);
       }
     }
-#pragma unroll
-    for (int i = 0; i < NFT; ++i) vc[i] = vn[i];
-#pragma unroll
-    for (int c = 0; c < kGPKC; ++c) kc[c] = kn[c];
-    blk_c = blk_n;
+  };
+  int p = 0;
+  for (; p + 2 <= n_pages; p += 2) {
+    page(std::integral_constant<int, 0>{}, p);
+    page(std::integral_constant<int, 1>{}, p + 1);
   }
+  if (p < n_pages) page(std::integral_constant<int, 0>{}, p);
 
   // Epilogue: out = v_scale * W_g z for the 64 rows, z = acc / l rounded to
   // fp16.  A lane's accumulator tile is the B operand of a 16x16x16 product
@@ -1074,8 +1081,8 @@ hipError_t launch_generic_attn(const ShapeKey& s, const void* qt, const int32_t*
   return launch_generic_merge(s, a, rows, num_splits, st);
 }
 
-bool generic_prefill_tiled(const ShapeKey& s) {
-  return s.rk <= 32 * kGPKC && s.rv <= 8 * 16 * (kGenFT / 2);
+bool generic_prefill_tiled(const ShapeKey& s, int max_blocks) {
+  return s.rk <= 32 * kGPKC && s.rv <= 8 * 16 * (kGenFT / 2) && max_blocks <= kGPIds;
 }
 
 hipError_t launch_generic_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl,
@@ -1085,6 +1092,7 @@ hipError_t launch_generic_prefill(const ShapeKey& s, const void* qt, const int32
                                   const int32_t* seq_lens, int num_blocks, int batch, void* out,
                                   const LatentFormat& fmt, int which, hipStream_t st) {
   if (total_q <= 0 || batch <= 0 || max_query_len <= 0) return hipSuccess;
+  if (max_blocks > kGPIds) return hipErrorInvalidValue;  // the staged block ids fit in LDS
   const GenArgs a = gen_args(s, qt, qsl, total_q, k_cache, v_cache, W, block_tables, max_blocks,
                              seq_lens, num_blocks, batch, max_blocks, 1, nullptr, nullptr, out,
                              fmt);

@@ -153,9 +153,10 @@ hipError_t launch_generic_attn(const ShapeKey& s, const void* qt, const int32_t*
                                void* out, const LatentFormat& fmt, int which, hipStream_t st);
 
 // Chunked prefill on the generic kernels for r_k up to 128 and r_v up to 1024
-// (generic_prefill_tiled): 64 chunk queries of one head per work group, the
+// (generic_prefill_tiled; table rows of at most 8192 pages, whose block ids
+// the kernel stages in LDS): 64 chunk queries of one head per work group, the
 // up-projection in the kernel's epilogue.
-bool generic_prefill_tiled(const ShapeKey& s);
+bool generic_prefill_tiled(const ShapeKey& s, int max_blocks);
 hipError_t launch_generic_prefill(const ShapeKey& s, const void* qt, const int32_t* qsl,
                                   int total_q, int max_query_len, const void* k_cache,
                                   const void* v_cache, const void* W,

@@ -236,9 +236,8 @@ def test_generic_prefill_many_chunk_tokens(sk):
 
 
 def test_generic_prefill_long_prefix_reads_table(sk):
-    """A prefill row is one split over its whole table row; past 512 pages
-    (here 9000 cached tokens) the split kernel reads the block ids from the
-    table page by page instead of staging them."""
+    """9000 cached tokens (more than 512 pages): the tiled prefill kernel
+    stages all of a request's block ids in LDS, up to 8192 pages."""
     case = wl.make_prefill_case(SHAPES["h3_d32_gqa"], [9000, 40], [20, 9], seed=122)
     assert case.cache.block_tables.shape[1] > 512
     note("generic prefill over 9000 cached tokens")
@@ -246,6 +245,19 @@ def test_generic_prefill_long_prefix_reads_table(sk):
     ref = _pre_oracle(case, kc, vc)
     assert_parity(out, ref, "generic prefill long prefix")
     per_head(out, ref, "generic prefill long prefix")
+
+
+def test_generic_prefill_table_past_lds_ids(sk):
+    """A table row longer than 8192 pages (132000 cached tokens) does not fit
+    the tiled kernel's staged block ids: the call runs on the row kernel,
+    which reads the block ids from the table page by page."""
+    case = wl.make_prefill_case(SHAPES["h3_d32_gqa"], [132000, 40], [20, 9], seed=124)
+    assert case.cache.block_tables.shape[1] > 8192
+    note("generic prefill over 132000 cached tokens")
+    out, kc, vc = _gpu_prefill(sk, case)
+    ref = _pre_oracle(case, kc, vc)
+    assert_parity(out, ref, "generic prefill table past 8192 pages")
+    per_head(out, ref, "generic prefill table past 8192 pages")
 
 
 @pytest.mark.parametrize("name", ["odd_h28_d96", "gqa_g8"])
