@@ -172,7 +172,7 @@ __device__ __forceinline__ void gen_upproject(const GenArgs& a, const float* z, 
   }
 }
 
-template <bool FP8, int NFT>
+template <bool FP8, int NFT, bool IDS, bool RKW>
 __global__ __launch_bounds__(kGenSThreads) void generic_split_kernel(GenArgs a) {
   static_assert(NFT == kGenFT || NFT == kGenFT / 2, "feature tiles per wave: r_v <= 128 * NFT");
   extern __shared__ __attribute__((aligned(16))) float gsm[];
@@ -202,11 +202,11 @@ __global__ __launch_bounds__(kGenSThreads) void generic_split_kernel(GenArgs a) 
     const int hh = i / a.RK, r = i % a.RK;
     sq[i] = hh < nh ? a.qt[((size_t)row * a.H + h0 + hh) * a.RK + r] : 0.f;
   }
-  // the split's block ids, staged once when they fit (one vector load per
-  // thread); longer splits read the table page by page
+  // the split's block ids: staged once (one vector load per thread) when a
+  // split has at most kGenSThreads pages (IDS), else read from the table page
+  // by page
   const int32_t* bt = a.block_tables + (size_t)tb * a.max_blocks;
-  const bool ids_lds = a.pages_per_split <= kGenSThreads;  // uniform
-  if (ids_lds) sBlk[tid] = p0 + tid < p1 ? bt[p0 + tid] : 0;
+  if constexpr (IDS) sBlk[tid] = p0 + tid < p1 ? bt[p0 + tid] : 0;
   // softmax state of head sh = 4w + lane/16 (waves 0-3), kept by its 16 lanes
   const int sh = 4 * w + (lane >> 4), st = lane & 15;
   float m_run = -INFINITY, l_run = 0.f;
@@ -219,7 +219,10 @@ __global__ __launch_bounds__(kGenSThreads) void generic_split_kernel(GenArgs a) 
   __syncthreads();
 
   auto block_at = [&](int p) {
-    return ids_lds ? __builtin_amdgcn_readfirstlane(sBlk[p - p0]) : bt[p];
+    if constexpr (IDS)
+      return __builtin_amdgcn_readfirstlane(sBlk[p - p0]);
+    else
+      return bt[p];
   };
   // scores of (head hh, token t): two neighbouring threads per pair, each
   // taking every other 8-rank chunk of the key row; a batch's chunks are
@@ -271,45 +274,50 @@ __global__ __launch_bounds__(kGenSThreads) void generic_split_kernel(GenArgs a) 
   };
 
   // Pages run as a software pipeline: at the top of page p, the first
-  // 2*kGenSB key chunks and the value operands of page p+1 are requested,
-  // and the barriers order LDS only, so these requests stay in flight while
-  // page p is processed.  Scores, weights and
-  // factors alternate between two LDS buffers, so two barriers a page
-  // suffice.  An invalid block id reads block 0 and masks its page.
-  // page p's first key chunks and value operands (kc, vc), and page p+1's
-  // (kn, vn), requested at the top of page p
-  // (fp16 values at r_v > 1024 have no registers for two pages: they are
-  // requested at their own page's top)
+  // 2*kGenSB key chunks and the value operands of page p+1 are requested
+  // into the other of two operand slots (the loop is unrolled by two, so no
+  // operand is copied), and the barriers order LDS only, so these requests
+  // stay in flight while page p is processed.  Every page issues the same
+  // requests with no branch around them (addresses clamped into the page,
+  // the last page requests itself again), so each use waits only for its own
+  // page.  Scores, weights and factors alternate between two LDS buffers, so
+  // two barriers a page suffice.  An invalid block id reads block 0 and
+  // masks its page.  (fp16 values at r_v > 1024 have no registers for two
+  // pages: they are requested at their own page's top.)
   constexpr bool VLA = FP8 || NFT < kGenFT;
-  Raw8<FP8> kc[kGenSB], kn[kGenSB];
-  VRaw vc[NFT], vn[VLA ? NFT : 1];
-  auto load_vals = [&](auto& dst, int blk) {
+  Raw8<FP8> kr[2][kGenSB];
+  VRaw vr[VLA ? 2 : 1][NFT];
+  auto load_vals = [&](VRaw (&dst)[NFT], int blk) {
 #pragma unroll
-    for (int i = 0; i < NFT; ++i)
-      if (w + 8 * i < ntv) dst[i] = load_val(blk, w + 8 * i);  // uniform
+    for (int i = 0; i < NFT; ++i) dst[i] = load_val(blk, w + 8 * i);
   };
-  int blk_c = p0 < p1 ? block_at(p0) : 0;
   if (p0 < p1) {
-    load_keys(kc, loadable(blk_c), 0);
-    if constexpr (VLA) load_vals(vc, loadable(blk_c));
+    const int blk0 = loadable(block_at(p0));
+    load_keys(kr[0], blk0, 0);
+    if constexpr (VLA) load_vals(vr[0], blk0);
   }
-  for (int p = p0; p < p1; ++p) {
+  auto page = [&](auto phase, int p) {
+    constexpr int PH = decltype(phase)::value;
+    VRaw (&vc)[NFT] = vr[VLA ? PH : 0];
     const int buf = (p - p0) & 1;
+    const int blk_c = block_at(p);
     const int nv = ((unsigned)blk_c < (unsigned)a.num_blocks) ? min(kGenBS, L - p * kGenBS) : 0;
     const int blk = loadable(blk_c);
-    const int blk_n = p + 1 < p1 ? block_at(p + 1) : 0;
+    const int blk_n = loadable(block_at(min(p + 1, p1 - 1)));
     if constexpr (!VLA) load_vals(vc, blk);
-    if (p + 1 < p1) {  // uniform
-      load_keys(kn, loadable(blk_n), 0);
-      if constexpr (VLA) load_vals(vn, loadable(blk_n));
+    load_keys(kr[PH ^ 1], blk_n, 0);
+    if constexpr (VLA) load_vals(vr[PH ^ 1], blk_n);
+    float sc = dot_keys(kr[PH], 0, 0.f);
+    if constexpr (RKW) {  // r_k > 128: the rest of the key row in place
+      for (int c0 = 2 * kGenSB; c0 < nch; c0 += 2 * kGenSB) {
+        Raw8<FP8> x[kGenSB];
+        load_keys(x, blk, c0);
+        sc = dot_keys(x, c0, sc);
+      }
     }
-    float sc = dot_keys(kc, 0, 0.f);
-    for (int c0 = 2 * kGenSB; c0 < nch; c0 += 2 * kGenSB) {  // r_k > 128: the rest in place
-      Raw8<FP8> x[kGenSB];
-      load_keys(x, blk, c0);
-      sc = dot_keys(x, c0, sc);
-    }
-    if (nv > 0) {  // uniform: an invalid block id masks its page
+    // an invalid block id masks its page: no scores (-inf), zero value
+    // operands; the page still runs, so each page waits the same way
+    {
       sc += __shfl_xor(sc, 1);
       if (half == 0)
         sS[(buf * kGenSHG + hh_s) * kGenBS + t_s] = (hh_s < nh && t_s < nv) ? sc : -INFINITY;
@@ -351,14 +359,13 @@ __global__ __launch_bounds__(kGenSThreads) void generic_split_kernel(GenArgs a) 
         }
       }
     }
-#pragma unroll
-    for (int i = 0; i < kGenSB; ++i) kc[i] = kn[i];
-    if constexpr (VLA) {
-#pragma unroll
-      for (int i = 0; i < NFT; ++i) vc[i] = vn[i];
-    }
-    blk_c = blk_n;
+  };
+  int p = p0;
+  for (; p + 2 <= p1; p += 2) {
+    page(std::integral_constant<int, 0>{}, p);
+    page(std::integral_constant<int, 1>{}, p + 1);
   }
+  if (p < p1) page(std::integral_constant<int, 0>{}, p);
   __syncthreads();  // the loop's LDS buffers are reused below
 
   if (!fused) {
@@ -1046,6 +1053,29 @@ static hipError_t launch_generic_merge(const ShapeKey& s, const GenArgs& a, int 
   return hipGetLastError();
 }
 
+// the split kernel instance for a call: FP8 caches or not, 8 or 16
+// feature tiles per wave, block ids staged in LDS or read from the table,
+// key rows of more than 128 ranks or not
+template <bool IDS, bool RKW>
+static void launch_split(bool wide, bool fp8, dim3 grid, size_t lds, const GenArgs& a, int which,
+                         hipStream_t st) {
+  if (fp8) {
+    if (wide)
+      launch_hooked_lds(which, TIME_NONE, generic_split_kernel<true, kGenFT, IDS, RKW>, grid,
+                        dim3(kGenSThreads), lds, st, a);
+    else
+      launch_hooked_lds(which, TIME_NONE, generic_split_kernel<true, kGenFT / 2, IDS, RKW>, grid,
+                        dim3(kGenSThreads), lds, st, a);
+  } else {
+    if (wide)
+      launch_hooked_lds(which, TIME_NONE, generic_split_kernel<false, kGenFT, IDS, RKW>, grid,
+                        dim3(kGenSThreads), lds, st, a);
+    else
+      launch_hooked_lds(which, TIME_NONE, generic_split_kernel<false, kGenFT / 2, IDS, RKW>,
+                        grid, dim3(kGenSThreads), lds, st, a);
+  }
+}
+
 hipError_t launch_generic_attn(const ShapeKey& s, const void* qt, const int32_t* qsl, int rows,
                                const void* k_cache, const void* v_cache, const void* W,
                                const int32_t* block_tables, int max_blocks,
@@ -1061,21 +1091,15 @@ hipError_t launch_generic_attn(const ShapeKey& s, const void* qt, const int32_t*
   const size_t lds = split_lds(s, fused);
   // feature tiles per wave: 8 cover r_v <= 1024, 16 the rest
   const bool wide = s.rv > 8 * 16 * (kGenFT / 2);
-  if (fmt.fp8) {
-    if (wide)
-      launch_hooked_lds(which, TIME_NONE, generic_split_kernel<true, kGenFT>, grid,
-                        dim3(kGenSThreads), lds, st, a);
-    else
-      launch_hooked_lds(which, TIME_NONE, generic_split_kernel<true, kGenFT / 2>, grid,
-                        dim3(kGenSThreads), lds, st, a);
-  } else {
-    if (wide)
-      launch_hooked_lds(which, TIME_NONE, generic_split_kernel<false, kGenFT>, grid,
-                        dim3(kGenSThreads), lds, st, a);
-    else
-      launch_hooked_lds(which, TIME_NONE, generic_split_kernel<false, kGenFT / 2>, grid,
-                        dim3(kGenSThreads), lds, st, a);
-  }
+  const bool ids = pages_per_split <= kGenSThreads, rkw = s.rk > 16 * kGenSB;
+  if (ids && !rkw)
+    launch_split<true, false>(wide, fmt.fp8, grid, lds, a, which, st);
+  else if (ids)
+    launch_split<true, true>(wide, fmt.fp8, grid, lds, a, which, st);
+  else if (!rkw)
+    launch_split<false, false>(wide, fmt.fp8, grid, lds, a, which, st);
+  else
+    launch_split<false, true>(wide, fmt.fp8, grid, lds, a, which, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || fused) return e;
   return launch_generic_merge(s, a, rows, num_splits, st);
