@@ -566,14 +566,15 @@ __global__ __launch_bounds__(512) void append_tiled_kernel(AppendArgs a) {
   if constexpr (RING > 3) fetch(std::integral_constant<int, 4 % RING>{}, min(4, n_steps - 1));
   __syncthreads();
   // step s: products of step s from LDS buffer s&1, step s+1 from the ring
-  // into the other buffer, step s+1+RING into the freed ring slot
+  // into the other buffer, step s+1+RING into the freed ring slot.  The last
+  // step stages and requests too (a repeat of the last step, into a buffer
+  // nothing reads again): with no branch around the requests, each stage
+  // waits only for its own step's
   auto iter = [&](auto phase, int s) {
     constexpr int P = decltype(phase)::value;  // (s + 1) % RING
     compute(acc, s & 1);
-    if (s + 1 < n_steps) {  // uniform
-      stage(std::integral_constant<int, P>{}, (s + 1) & 1);
-      fetch(std::integral_constant<int, P>{}, min(s + 1 + RING, n_steps - 1));
-    }
+    stage(std::integral_constant<int, P>{}, (s + 1) & 1);
+    fetch(std::integral_constant<int, P>{}, min(s + 1 + RING, n_steps - 1));
     __syncthreads();
   };
   int s = 0;

@@ -581,8 +581,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_attn_kernel(PrefillArgs a) {
     if constexpr (SCHED != 4) issue_loads();
     float4v sacc[PPS][C::SUW];
     // a wave in its score products gets issue priority over the CU's waves in
-    // their value products or softmax (about 1.5% off the kernel time at
-    // 16 x (4096 cached + 256 new) tokens)
+    // their value products or softmax, so the step's score chain is not the
+    // last thing to finish before the barrier
     __builtin_amdgcn_s_setprio(1);
     if constexpr (KLDS)
       score_products_lds((s + 1) % 3, sacc);
