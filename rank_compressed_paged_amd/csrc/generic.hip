@@ -10,11 +10,13 @@
 // other ranks (the README's rank profiles and learned per-layer ranks), other
 // head counts or head sizes, or other grouped-query groups, runs without a
 // compiled instance of its own.  They trade speed for generality where
-// the tuned kernels do not: scores run on the vector ALU in fp32, each work
-// group covers at most 16 heads (so a value page is read once per group of
-// 16 heads), and a prefill query is a row of its own that walks its causal
-// prefix.  P.c_v, the q projection and the merge's up-projection run on the
-// matrix cores.
+// the tuned kernels do not: the decode scores run on the vector ALU in fp32,
+// a decode work group covers at most 16 heads (so a value page is read once
+// per group of 16 heads), a prefill work group 64 queries of one head, and a
+// prefill beyond the tiled kernel's limits (r_k > 128, r_v > 1024) runs each
+// chunk query as a row of its own that walks its causal prefix.  P.c_v, the
+// prefill scores, the q projection and the up-projections run on the matrix
+// cores.
 //
 // Limits (checked on the host): d a multiple of 32 up to 256; r_k a multiple
 // of 8 up to min(d, 256); r_v a multiple of 8 up to min(2048, Hkv * d).
@@ -25,7 +27,7 @@
 // j = n - query_start_loc[b], P0 = seq_lens[b] - C_b.
 //
 // Work group (split s, row, group of 16 heads), eight waves: it streams its
-// pages one at a time.  Per 16-token page, two neighbouring threads per
+// pages one at a time, the next page's requests in flight.  Per 16-token page, two neighbouring threads per
 // (head hh, token t) form one score from fp32 q~ in LDS and the key row; the
 // 16 lanes of head h run its online-softmax update (running max, rescale
 // factor, sum) with cross-lane reductions and write the page's weights to
