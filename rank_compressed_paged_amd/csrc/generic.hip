@@ -579,7 +579,10 @@ __global__ __launch_bounds__(kGenMergeThreads) void generic_merge_kernel(GenArgs
 //     hi/lo pair (two products per rank chunk), then the online softmax per
 //     query (log2 domain, the quad-lane reductions); q~ waits in LDS as hi/lo
 //     fragments; the weights go to LDS in fp16 and are summed as rounded, the
-//     rescale factors beside them;
+//     rescale factors beside them; a row's reference max moves only when a
+//     page's max passes it by more than 2^8 (P <= 256 in fp16), so the
+//     accumulators are rescaled on few pages, by a branch the whole wave
+//     takes or skips;
 //   * every wave then runs P.c_v for the four query blocks over its feature
 //     tiles w, w + 8, ... (v_mfma_f32_16x16x16_f16, value operands as in the split
 //     kernel), so each value operand feeds four products;
@@ -597,6 +600,7 @@ constexpr int kGPQB = 4;         // 16-query blocks per work group
 constexpr int kGPQ = 16 * kGPQB; // chunk queries per work group
 constexpr int kGPKC = 4;         // 32-rank chunks of a key row: r_k <= 128
 constexpr int kGPIds = 8192;     // pages of a request's table: 131072 tokens
+constexpr float kGPRaise = 8.f;  // lazy-rescale threshold (log2 units)
 
 template <bool FP8>
 __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, int n_qb) {
@@ -753,7 +757,11 @@ __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, 
         mx = fmax_nn(mx, sv[i]);
       }
       mx = quad_max(mx);
-      const float m_new = fmax_nn(m_run, mx);
+      // lazy reference: a row's reference max moves only when the page's
+      // max passes it by more than 2^kGPRaise, so P <= 2^kGPRaise stays
+      // well inside fp16 and the accumulators are rescaled on few pages
+      // (the softmax is invariant to the reference)
+      const float m_new = mx > m_run + kGPRaise ? mx : m_run;
       const float alpha = m_new == m_run ? 1.f : exp2f(m_run - m_new);  // 0 on the first page
       half4 ph;
       float ps = 0.f;
@@ -771,10 +779,18 @@ __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, 
     block_sync_lds();
     half4 pb[kGPQB];
     float al[kGPQB];
+    bool moved = false;
 #pragma unroll
     for (int k = 0; k < kGPQB; ++k) {
       pb[k] = *(const half4*)&sPh[buf][k][col][4 * quad];
       al[k] = sAl[buf][k][col];
+      moved |= al[k] != 1.f;
+    }
+    if (__builtin_amdgcn_ballot_w64(moved) != 0) {  // uniform; no request inside
+#pragma unroll
+      for (int i = 0; i < NFT; ++i)
+#pragma unroll
+        for (int k = 0; k < kGPQB; ++k) acc[i][k] = acc[i][k] * al[k];
     }
     const bool part = nv < kGenBS;  // uniform: tokens past the end may hold NaN
 #pragma unroll
@@ -786,7 +802,7 @@ __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, 
           for (int e = 0; e < 4; ++e) av[e] = 4 * quad + e < nv ? av[e] : (half_t)0.f;
         }
 #pragma unroll
-        for (int k = 0; k < kGPQB; ++k) acc[i][k] = mfma16x16x16(av, pb[k], acc[i][k] * al[k]);
+        for (int k = 0; k < kGPQB; ++k) acc[i][k] = mfma16x16x16(av, pb[k], acc[i][k]);
       }
     }
   };
