@@ -50,6 +50,7 @@ constexpr int kGenSThreads = 512;  // split work group: eight waves
 constexpr int kGenFT = 16;         // 16-feature tiles per wave of the split: r_v <= 2048
 constexpr int kGenBS = 16;  // tokens per page
 constexpr int kGenSB = 8;   // key-row chunks a thread requests together
+constexpr float kGPRaise = 8.f;  // lazy softmax reference: threshold (log2 units)
 
 struct GenArgs {
   int H, Hkv, D, RK, RV, QG;
@@ -329,10 +330,13 @@ __global__ __launch_bounds__(kGenSThreads) void generic_split_kernel(GenArgs a) 
       // and summed as rounded
       if (w < 4) {  // uniform
         const float sv = sS[(buf * kGenSHG + sh) * kGenBS + st];
-        float mx = sv;
+        float pm = sv;
 #pragma unroll
-        for (int m = 8; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
-        mx = fmaxf(mx, m_run);
+        for (int m = 8; m >= 1; m >>= 1) pm = fmaxf(pm, __shfl_xor(pm, m));
+        // lazy reference: it moves only when the page's max passes it by
+        // more than 2^kGPRaise (P <= 2^kGPRaise in fp16); the merge combines
+        // the splits' (reference, sum, z) whatever each reference is
+        const float mx = pm > m_run + kGPRaise ? pm : m_run;
         const float alpha = (mx == m_run) ? 1.f : exp2f(m_run - mx);  // 0 on the first page
         const half_t ph = (half_t)(sv == -INFINITY ? 0.f : exp2f(sv - mx));
         sPh[(buf * kGenSHG + sh) * kGenBS + st] = ph;
@@ -348,6 +352,10 @@ __global__ __launch_bounds__(kGenSThreads) void generic_split_kernel(GenArgs a) 
       // weights (token x head), column = head col
       const half4 pb = *(const half4*)&sPh[(buf * kGenSHG + col) * kGenBS + 4 * quad];
       const float al = sA[buf * kGenSHG + col];
+      if (__builtin_amdgcn_ballot_w64(al != 1.f) != 0) {  // uniform; no request inside
+#pragma unroll
+        for (int i = 0; i < NFT; ++i) acc[i] = acc[i] * al;
+      }
       const bool part = nv < kGenBS;  // uniform: tokens past the end may hold NaN
 #pragma unroll
       for (int i = 0; i < NFT; ++i) {
@@ -357,7 +365,7 @@ __global__ __launch_bounds__(kGenSThreads) void generic_split_kernel(GenArgs a) 
 #pragma unroll
             for (int e = 0; e < 4; ++e) av[e] = 4 * quad + e < nv ? av[e] : (half_t)0.f;
           }
-          acc[i] = mfma16x16x16(av, pb, acc[i] * al);
+          acc[i] = mfma16x16x16(av, pb, acc[i]);
         }
       }
     }
@@ -600,7 +608,6 @@ constexpr int kGPQB = 4;         // 16-query blocks per work group
 constexpr int kGPQ = 16 * kGPQB; // chunk queries per work group
 constexpr int kGPKC = 4;         // 32-rank chunks of a key row: r_k <= 128
 constexpr int kGPIds = 8192;     // pages of a request's table: 131072 tokens
-constexpr float kGPRaise = 8.f;  // lazy-rescale threshold (log2 units)
 
 template <bool FP8>
 __global__ __launch_bounds__(kGPThreads) void generic_prefill_kernel(GenArgs a, int n_qb) {
